@@ -1,0 +1,220 @@
+/*
+ * CPU oracle for the MSA forward path — TEST INFRASTRUCTURE ONLY (see header).
+ *
+ * Written from the definitions, one step per function, in double precision:
+ *   Eq. 4  block partition           -> block_of()
+ *   Eq. 6  index scores + max-pool   -> score_row()
+ *   Eq. 7  Top-k, local block forced -> topk_row()
+ *   Eq. 8  softmax over the chosen   -> attn_row()
+ * (page "MiniMax Sparse Attention (MSA)" paper review, section 3; page
+ * "papers.chlience.com" reading notes, section 5.1 and 5.1.1.)
+ * No blocking, fusion or reordering beyond the definitions; OpenMP only
+ * splits independent query rows across threads.
+ */
+#include "msa_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static double bf16(uint16_t h) {
+  uint32_t u = ((uint32_t)h) << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* Eq. 4 (0-based): token j lies in block j / B_k. */
+static int64_t block_of(int64_t j, int B_k) { return j / B_k; }
+
+int64_t msa_oracle_num_blocks(int64_t N, int B_k) { return (N + B_k - 1) / B_k; }
+
+int msa_oracle_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/*
+ * Eq. 6 for one query vector qv at position i against keys kidx[0..i]:
+ * S_j = <qv, kidx[j]> / sqrt(d_idx), M[b] = max over visible j in block b.
+ * Invisible blocks stay -inf (reading notes 5.1.1: invisible tokens are -inf).
+ */
+static void score_row(const uint16_t* qv, const uint16_t* kidx, int64_t i, int d_idx, int B_k,
+                      int64_t B, double* Mrow) {
+  double scale = 1.0 / sqrt((double)d_idx);
+  for (int64_t b = 0; b < B; ++b) Mrow[b] = -INFINITY;
+  for (int64_t j = 0; j <= i; ++j) {
+    double s = 0.0;
+    for (int d = 0; d < d_idx; ++d) s += bf16(qv[d]) * bf16(kidx[j * d_idx + d]);
+    s *= scale;
+    int64_t b = block_of(j, B_k);
+    if (s > Mrow[b]) Mrow[b] = s;
+  }
+}
+
+/*
+ * Eq. 7 for one (query, group) row.  The local block is always chosen and uses
+ * one of the k slots (reading notes 5.1.1); the remaining slots are filled one
+ * at a time with the best unchosen earlier block: largest M, and on equal M the
+ * lower block index (scan ascending, replace only on strictly greater).
+ */
+static void topk_row(const double* Mrow, int64_t i, int B_k, int k, int32_t* out, char* chosen) {
+  int64_t bl = block_of(i, B_k);
+  memset(chosen, 0, (size_t)(bl + 1));
+  chosen[bl] = 1;
+  int count = 1;
+  while (count < k) {
+    int64_t best = -1;
+    for (int64_t b = 0; b < bl; ++b) {
+      if (chosen[b]) continue;
+      if (best < 0 || Mrow[b] > Mrow[best]) best = b;
+    }
+    if (best < 0) break; /* fewer than k causal blocks: all are chosen */
+    chosen[best] = 1;
+    ++count;
+  }
+  int n = 0;
+  for (int64_t b = 0; b <= bl; ++b)
+    if (chosen[b]) out[n++] = (int32_t)b;
+  while (n < k) out[n++] = -1;
+}
+
+/*
+ * Eq. 8 for one head: softmax of scale * <qv, k_j> over the token set
+ * T = { j <= i : block_of(j) in the chosen set }, then the weighted sum of v_j.
+ * kbase/vbase point at token 0 of this head's group, consecutive tokens are
+ * `stride` elements apart.
+ */
+static void attn_row(const uint16_t* qv, const uint16_t* kbase, const uint16_t* vbase,
+                     int64_t stride, int64_t i, int64_t N, int d_h, int B_k, const char* inset,
+                     double scale, double* orow, double* lse_out, double* s_buf) {
+  int64_t nt = 0;
+  double m = -INFINITY;
+  int64_t jmax = i < N - 1 ? i : N - 1;
+  for (int64_t j = 0; j <= jmax; ++j) {
+    if (!inset[block_of(j, B_k)]) continue;
+    double s = 0.0;
+    for (int d = 0; d < d_h; ++d) s += bf16(qv[d]) * bf16(kbase[j * stride + d]);
+    s *= scale;
+    s_buf[j] = s;
+    if (s > m) m = s;
+    ++nt;
+  }
+  for (int d = 0; d < d_h; ++d) orow[d] = 0.0;
+  if (nt == 0) {
+    *lse_out = -INFINITY;
+    return;
+  }
+  double l = 0.0;
+  for (int64_t j = 0; j <= jmax; ++j) {
+    if (!inset[block_of(j, B_k)]) continue;
+    double p = exp(s_buf[j] - m);
+    l += p;
+    for (int d = 0; d < d_h; ++d) orow[d] += p * bf16(vbase[j * stride + d]);
+  }
+  for (int d = 0; d < d_h; ++d) orow[d] /= l;
+  *lse_out = m + log(l);
+}
+
+void msa_oracle_block_scores(const uint16_t* q_idx, const uint16_t* k_idx, int64_t N, int H_kv,
+                             int d_idx, int B_k, const int64_t* rows, int64_t nrows, double* M) {
+  int64_t B = msa_oracle_num_blocks(N, B_k);
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t n = 0; n < nrows; ++n) {
+    int64_t i = rows ? rows[n] : n;
+    for (int r = 0; r < H_kv; ++r)
+      score_row(q_idx + (i * H_kv + r) * d_idx, k_idx, i, d_idx, B_k, B, M + (n * H_kv + r) * B);
+  }
+}
+
+void msa_oracle_topk(const double* M, const int64_t* rows, int64_t nrows, int H_kv, int64_t B,
+                     int B_k, int k, int32_t* block_idx) {
+#pragma omp parallel
+  {
+    char* chosen = (char*)malloc((size_t)B + 1);
+#pragma omp for schedule(dynamic, 16)
+    for (int64_t n = 0; n < nrows; ++n) {
+      int64_t i = rows ? rows[n] : n;
+      for (int r = 0; r < H_kv; ++r)
+        topk_row(M + (n * H_kv + r) * B, i, B_k, k, block_idx + (n * H_kv + r) * k, chosen);
+    }
+    free(chosen);
+  }
+}
+
+void msa_oracle_sparse_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                            const int32_t* block_idx, int64_t N, int H_q, int H_kv, int d_h,
+                            int B_k, int kk, double scale, const int64_t* rows, int64_t nrows,
+                            double* o, double* lse) {
+  int64_t B = msa_oracle_num_blocks(N, B_k);
+  int G = H_q / H_kv;
+#pragma omp parallel
+  {
+    char* inset = (char*)malloc((size_t)B);
+    double* s_buf = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t n = 0; n < nrows; ++n) {
+      int64_t i = rows ? rows[n] : n;
+      for (int h = 0; h < H_q; ++h) {
+        int r = h / G;
+        memset(inset, 0, (size_t)B);
+        const int32_t* sel = block_idx + (n * H_kv + r) * kk;
+        for (int s = 0; s < kk; ++s)
+          if (sel[s] >= 0 && sel[s] < B) inset[sel[s]] = 1;
+        attn_row(q + (i * H_q + h) * d_h, k + (int64_t)r * d_h, v + (int64_t)r * d_h,
+                 (int64_t)H_kv * d_h, i, N, d_h, B_k, inset, scale, o + (n * H_q + h) * d_h,
+                 lse + n * H_q + h, s_buf);
+      }
+    }
+    free(s_buf);
+    free(inset);
+  }
+}
+
+void msa_oracle_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_t* k_cache,
+                       const uint16_t* v_cache, const uint16_t* k_idx_cache,
+                       const int64_t* cu_seqlens, int batch, int H_q, int H_kv, int d_h,
+                       int d_idx, int B_k, int kk, double scale, int32_t* block_idx, double* o,
+                       double* lse, double* M, int64_t Bmax) {
+  int G = H_q / H_kv;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int s = 0; s < batch; ++s) {
+    int64_t j0 = cu_seqlens[s];
+    int64_t L = cu_seqlens[s + 1] - j0;
+    if (L <= 0) continue;
+    int64_t i = L - 1; /* the new token is the last cache entry */
+    int64_t B = msa_oracle_num_blocks(L, B_k);
+    double* Mrow = (double*)malloc(sizeof(double) * (size_t)B);
+    char* chosen = (char*)malloc((size_t)B + 1);
+    double* s_buf = (double*)malloc(sizeof(double) * (size_t)L);
+    for (int r = 0; r < H_kv; ++r) {
+      score_row(q_idx + ((int64_t)s * H_kv + r) * d_idx, k_idx_cache + j0 * d_idx, i, d_idx, B_k,
+                B, Mrow);
+      if (M) {
+        double* Mo = M + ((int64_t)s * H_kv + r) * Bmax;
+        for (int64_t b = 0; b < Bmax; ++b) Mo[b] = b < B ? Mrow[b] : -INFINITY;
+      }
+      int32_t* sel = block_idx + ((int64_t)s * H_kv + r) * kk;
+      topk_row(Mrow, i, B_k, kk, sel, chosen);
+      memset(chosen, 0, (size_t)B);
+      for (int t = 0; t < kk; ++t)
+        if (sel[t] >= 0) chosen[sel[t]] = 1;
+      for (int g = 0; g < G; ++g) {
+        int h = r * G + g;
+        attn_row(q + ((int64_t)s * H_q + h) * d_h, k_cache + j0 * H_kv * d_h + (int64_t)r * d_h,
+                 v_cache + j0 * H_kv * d_h + (int64_t)r * d_h, (int64_t)H_kv * d_h, i, L, d_h,
+                 B_k, chosen, scale, o + ((int64_t)s * H_q + h) * d_h, lse + (int64_t)s * H_q + h,
+                 s_buf);
+      }
+    }
+    free(s_buf);
+    free(chosen);
+    free(Mrow);
+  }
+}

@@ -1,0 +1,286 @@
+"""Pins of the CPU oracle to facts fixed by the pages and by mathematics.
+
+None of these re-types the oracle's formula: each compares it with a closed
+form, an invariant, a special case that reduces to a textbook routine, a
+brute-force enumeration on a tiny input, or a hand-derived golden value.
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def bf16(x):
+    return torch.as_tensor(x, dtype=torch.float32).to(torch.bfloat16)
+
+
+def rand_bf16(shape, seed, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g) * scale).to(torch.bfloat16)
+
+
+# --- Eq. 4: block partition ---------------------------------------------------------------
+
+def test_partition_counts_match_workloads():
+    # Block counts printed for the workloads: 32 / 256 / 1024 / 8192 blocks.
+    for name, B in (("c0", 32), ("c1", 256), ("c2", 1024), ("c4", 8192)):
+        c = synth.CONFIGS[name]
+        assert oracle.num_blocks(c.N, c.B_k) == B == c.B
+    assert oracle.num_blocks(129, 128) == 2
+    assert oracle.num_blocks(128, 128) == 1
+    assert oracle.num_blocks(1, 128) == 1
+
+
+# --- Eq. 6: index scores and causal block max-pool ----------------------------------------
+
+def test_block_scores_one_hot_closed_form():
+    """K_idx[j] = c_j e_0, Q_idx[i, r] = a_r e_0  =>  S_ij = a_r c_j / sqrt(d_idx)."""
+    N, H_kv, d_idx, B_k = 11, 2, 64, 4
+    c = [0.5, -1.0, 2.0, 0.25, -3.0, 1.5, 0.75, -0.5, 4.0, 1.0, -2.5]
+    a = [1.5, -2.0]
+    k_idx = torch.zeros(N, d_idx)
+    k_idx[:, 0] = torch.tensor(c)
+    q_idx = torch.zeros(N, H_kv, d_idx)
+    for r in range(H_kv):
+        q_idx[:, r, 0] = a[r]
+    M = oracle.block_scores(bf16(q_idx), bf16(k_idx), B_k)
+    B = 3
+    assert M.shape == (N, H_kv, B)
+    for i in range(N):
+        for r in range(H_kv):
+            for b in range(B):
+                visible = [j for j in range(b * B_k, min((b + 1) * B_k, N)) if j <= i]
+                if not visible:
+                    assert M[i, r, b] == -math.inf
+                else:
+                    assert M[i, r, b] == max(a[r] * c[j] for j in visible) / 8.0
+
+
+def test_block_scores_scale_does_not_change_ranking():
+    """Multiplying every index key by 2 doubles M exactly (power-of-two scaling)."""
+    q = rand_bf16((40, 2, 64), 1)
+    kk = rand_bf16((40, 64), 2)
+    M1 = oracle.block_scores(q, kk, 8)
+    M2 = oracle.block_scores(q, (kk.float() * 2).to(torch.bfloat16), 8)
+    fin = np.isfinite(M1)
+    assert np.array_equal(np.isfinite(M2), fin)
+    np.testing.assert_array_equal(M2[fin], 2 * M1[fin])
+
+
+# --- Eq. 7: Top-k with the forced local block ---------------------------------------------
+
+def _golden_topk_cases():
+    cases = []
+    with open(os.path.join(GOLDEN, "topk_rules.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            name, params, mvals, exp = [p.strip() for p in line.split("|")]
+            i, B_k, k = map(int, params.split())
+            M = [float(x) for x in mvals.split()]
+            cases.append((name, i, B_k, k, M, [int(x) for x in exp.split()]))
+    return cases
+
+
+@pytest.mark.parametrize("case", _golden_topk_cases(), ids=lambda c: c[0])
+def test_topk_golden(case):
+    name, i, B_k, k, M, expected = case
+    Marr = np.array(M, dtype=np.float64).reshape(1, 1, -1)
+    got = oracle.topk(Marr, k, B_k, rows=[i])
+    assert got[0, 0].tolist() == expected
+
+
+def _brute_topk(Mrow, i, B_k, k):
+    bl = i // B_k
+    if bl + 1 <= k:
+        chosen = list(range(bl + 1))
+    else:
+        order = sorted(range(bl), key=lambda b: (-Mrow[b], b))
+        chosen = sorted(order[:k - 1] + [bl])
+    return chosen + [-1] * (k - len(chosen))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_matches_full_sort(seed):
+    """Brute force: sort every causal block by (score desc, index asc); ties are frequent."""
+    rng = np.random.default_rng(seed)
+    N, H_kv, B_k = 90, 3, 4
+    B = oracle.num_blocks(N, B_k)
+    M = rng.integers(-3, 4, size=(N, H_kv, B)).astype(np.float64) * 0.5  # many exact ties
+    for k in (1, 2, 5, 8, 23, 30):
+        got = oracle.topk(M, k, B_k)
+        for i in range(N):
+            for r in range(H_kv):
+                assert got[i, r].tolist() == _brute_topk(M[i, r], i, B_k, k), (k, i, r)
+
+
+def test_local_block_always_selected_and_exp_free():
+    inp = synth.small_prefill(N=700, H_q=4, H_kv=2, k=4, seed=5, B_k=32)
+    M = oracle.block_scores(inp.q_idx, inp.k_idx, 32)
+    bi = oracle.topk(M, 4, 32)
+    for i in range(700):
+        for r in range(2):
+            assert i // 32 in bi[i, r]
+            row = [b for b in bi[i, r] if b >= 0]
+            assert row == sorted(row) and len(set(row)) == len(row)
+            assert max(row) == i // 32
+    # Exp-free selection: softmax over the causal blocks is order-preserving, so
+    # selecting on exp(M) / sum exp(M) gives the same blocks.
+    P = np.exp(M - np.nanmax(np.where(np.isfinite(M), M, np.nan), axis=2, keepdims=True))
+    P = P / P.sum(axis=2, keepdims=True)
+    np.testing.assert_array_equal(oracle.topk(P, 4, 32), bi)
+
+
+def test_fewer_than_k_blocks_padding():
+    inp = synth.small_prefill(N=300, H_q=2, H_kv=1, k=8, seed=9, B_k=64)
+    M = oracle.block_scores(inp.q_idx, inp.k_idx, 64)
+    bi = oracle.topk(M, 8, 64)
+    for i in range(300):
+        bl = i // 64
+        assert bi[i, 0].tolist() == list(range(bl + 1)) + [-1] * (8 - bl - 1)
+
+
+# --- Eq. 8: attention over the chosen blocks ---------------------------------------------
+
+def _dense_causal_gqa(q, k, v, scale):
+    """Textbook causal GQA (Eq. 1) in float64 with torch: adjacent heads share a KV head."""
+    qd, kd, vd = q.double(), k.double(), v.double()
+    N, H_q, _ = qd.shape
+    G = H_q // kd.shape[1]
+    kr = kd.repeat_interleave(G, dim=1)
+    vr = vd.repeat_interleave(G, dim=1)
+    s = torch.einsum("ihd,jhd->hij", qd, kr) * scale
+    mask = torch.triu(torch.ones(N, N, dtype=torch.bool), diagonal=1)
+    s = s.masked_fill(mask, -math.inf)
+    lse = torch.logsumexp(s, dim=-1)
+    p = torch.softmax(s, dim=-1)
+    o = torch.einsum("hij,jhd->ihd", p, vr)
+    return o.numpy(), lse.T.numpy()
+
+
+@pytest.mark.parametrize("N,H_q,H_kv,B_k,d_h", [(37, 4, 2, 8, 16), (64, 6, 3, 16, 32), (50, 8, 1, 4, 8)])
+def test_k_covering_all_blocks_is_dense_gqa(N, H_q, H_kv, B_k, d_h):
+    q = rand_bf16((N, H_q, d_h), 11)
+    k = rand_bf16((N, H_kv, d_h), 12)
+    v = rand_bf16((N, H_kv, d_h), 13)
+    q_idx = rand_bf16((N, H_kv, 16), 14)
+    k_idx = rand_bf16((N, 16), 15)
+    B = oracle.num_blocks(N, B_k)
+    M = oracle.block_scores(q_idx, k_idx, B_k)
+    bi = oracle.topk(M, B, B_k)  # k = B: every causal block
+    scale = 1.0 / math.sqrt(d_h)
+    o, lse = oracle.sparse_attn(q, k, v, bi, B_k, scale)
+    o_ref, lse_ref = _dense_causal_gqa(q, k, v, scale)
+    np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_ref, rtol=0, atol=1e-12)
+
+
+def test_softmax_rows_sum_to_one():
+    """With V = 1 the output is the sum of the softmax weights."""
+    inp = synth.small_prefill(N=500, H_q=4, H_kv=2, k=3, seed=21, B_k=32, d_h=32)
+    v = torch.ones_like(inp.v)
+    M = oracle.block_scores(inp.q_idx, inp.k_idx, 32)
+    bi = oracle.topk(M, 3, 32)
+    o, _ = oracle.sparse_attn(inp.q, inp.k, v, bi, 32)
+    np.testing.assert_allclose(o, 1.0, rtol=0, atol=1e-12)
+
+
+def test_uniform_scores_closed_form():
+    """q = 0: every score is 0, so lse = ln|T| and o is the mean of V over T."""
+    N, H_q, H_kv, d_h, B_k = 45, 2, 1, 8, 8
+    q = torch.zeros(N, H_q, d_h, dtype=torch.bfloat16)
+    k = rand_bf16((N, H_kv, d_h), 31)
+    v = rand_bf16((N, H_kv, d_h), 32)
+    rows = [3, 17, 44, 40]
+    sets = [[0, -1, -1], [0, 2, -1], [1, 3, 5], [5, 0, 2]]
+    bi = np.array(sets, dtype=np.int32).reshape(4, 1, 3)
+    o, lse = oracle.sparse_attn(q, k, v, bi, B_k, rows=rows)
+    vd = v.double().numpy()
+    for n, i in enumerate(rows):
+        T = [j for j in range(N) if j <= i and (j // B_k) in sets[n]]
+        for h in range(H_q):
+            assert lse[n, h] == pytest.approx(math.log(len(T)), abs=1e-12)
+            np.testing.assert_allclose(o[n, h], vd[T, 0].mean(0), atol=1e-12)
+
+
+def test_lse_merge_of_disjoint_partials():
+    """Two-phase combine identity: attention over A u B equals the LSE merge of A and B."""
+    inp = synth.small_prefill(N=600, H_q=4, H_kv=2, k=6, seed=41, B_k=32, d_h=32)
+    rows = [599, 450, 333, 100]
+    A = np.array([[0, 3, 7, -1], [1, 2, 5, 9], [2, 4, -1, -1], [0, 1, -1, -1]], np.int32)
+    Bs = np.array([[9, 12, 18, -1], [11, 13, 14, -1], [6, 8, 10, -1], [3, -1, -1, -1]], np.int32)
+    A = np.repeat(A[:, None, :], 2, axis=1)
+    Bs = np.repeat(Bs[:, None, :], 2, axis=1)
+    U = np.concatenate([A, Bs], axis=2)
+    oA, lA = oracle.sparse_attn(inp.q, inp.k, inp.v, A, 32, rows=rows)
+    oB, lB = oracle.sparse_attn(inp.q, inp.k, inp.v, Bs, 32, rows=rows)
+    oU, lU = oracle.sparse_attn(inp.q, inp.k, inp.v, U, 32, rows=rows)
+    l = np.logaddexp(lA, lB)
+    o = np.exp(lA - l)[..., None] * oA + np.exp(lB - l)[..., None] * oB
+    np.testing.assert_allclose(lU, l, atol=1e-12)
+    np.testing.assert_allclose(oU, o, atol=1e-12)
+
+
+def test_block_order_and_empty_sets():
+    inp = synth.small_prefill(N=300, H_q=2, H_kv=1, k=4, seed=51, B_k=16, d_h=16)
+    rows = [299, 150]
+    bi = np.array([[[0, 5, 9, 18]], [[1, 2, 9, -1]]], np.int32)
+    perm = bi[:, :, ::-1].copy()
+    o1, l1 = oracle.sparse_attn(inp.q, inp.k, inp.v, bi, 16, rows=rows)
+    o2, l2 = oracle.sparse_attn(inp.q, inp.k, inp.v, perm, 16, rows=rows)
+    np.testing.assert_array_equal(l1, l2)
+    np.testing.assert_allclose(o1, o2, atol=1e-15)
+    # A set holding only future blocks (or nothing) has no visible token.
+    empty = np.array([[[-1, -1, -1, -1]], [[10, 12, -1, -1]]], np.int32)
+    o3, l3 = oracle.sparse_attn(inp.q, inp.k, inp.v, empty, 16, rows=rows)
+    assert np.all(l3 == -np.inf) and np.all(o3 == 0)
+
+
+# --- Decode --------------------------------------------------------------------------------
+
+def test_decode_equals_last_prefill_row():
+    lengths = [130, 64, 257]
+    d = synth.make_decode(synth.DecodeConfig("t", batch=3, H_q=4, H_kv=2, k=3, len_lo_blocks=1,
+                                             len_hi_blocks=1, B_k=32, d_h=32, d_idx=16, seed=7),
+                          lengths=lengths)
+    bi, o, lse, M = oracle.decode(d.q, d.q_idx, d.k_cache, d.v_cache, d.k_idx_cache, d.cu_seqlens, 3, 32,
+                                  want_scores=True)
+    cu = d.cu_seqlens.tolist()
+    for s, L in enumerate(lengths):
+        sl = slice(cu[s], cu[s + 1])
+        q_idx = d.k_idx_cache.new_zeros((L, 2, 16))
+        q_idx[L - 1] = d.q_idx[s]
+        q = d.k_cache.new_zeros((L, 4, 32))
+        q[L - 1] = d.q[s]
+        Mp = oracle.block_scores(q_idx, d.k_idx_cache[sl], 32, rows=[L - 1])
+        bp = oracle.topk(Mp, 3, 32, rows=[L - 1])
+        op, lp = oracle.sparse_attn(q, d.k_cache[sl], d.v_cache[sl], bp, 32, rows=[L - 1])
+        B = Mp.shape[2]
+        np.testing.assert_array_equal(M[s, :, :B], Mp[0])
+        np.testing.assert_array_equal(bi[s], bp[0])
+        np.testing.assert_array_equal(o[s], op[0])
+        np.testing.assert_array_equal(lse[s], lp[0])
+
+
+# --- Eq. 12: FLOP accounting used by the benchmark ----------------------------------------
+
+def test_eq12_ratio_matches_printed_28_4():
+    import bench
+    with open(os.path.join(GOLDEN, "eq12_flops.txt")) as f:
+        lines = [l for l in f if l.strip() and not l.startswith("#")]
+    for line in lines:
+        params, printed, exact = [p.strip() for p in line.split("|")]
+        N, H_q, H_kv, d_h, d_idx, B_k, k = map(int, params.split())
+        num = bench.flops_gqa_eq12(N, H_q, d_h)
+        den = bench.flops_msa_eq12(N, H_q, H_kv, d_h, d_idx, B_k, k)
+        assert Fraction(num, den) == Fraction(exact)
+        assert round(num / den, 1) == float(printed)
