@@ -1,0 +1,242 @@
+// Index Branch kernels: index scoring on MFMA with a fused causal mask and block
+// max-pool, and the exp-free Top-k with the forced local block.
+//
+// Method: page "MiniMax Sparse Attention (MSA)" paper review, section 3, Eq. 6
+// (token scores and causal block max-pool) and Eq. 7 (Top-k, local block kept);
+// reading notes page, section 5.1.1 (local block takes one slot, invisible
+// tokens are -inf) and section 5.4 (selection on raw scores, no softmax).
+//
+// Layout of the work: the (query, group) pairs are flattened into "columns"
+// c = i * H_kv + r (the natural row order of q_idx and block_idx).  A workgroup
+// owns a run of consecutive columns and sweeps the key blocks 0..b_last in order.
+// Each key block (128 keys x 64 dims, 16 KB) is staged once in LDS and shared by
+// every wave.  A wave computes S^T = K_block * Q^T with 32x32x16 bf16 MFMAs, so
+// each lane owns one column and holds 16 of the 32 keys of a tile: the max-pool is
+// a per-lane running max plus one swap between the two lane halves.  The block
+// score then goes straight into a per-lane Top-L register list (Top-k fused) or,
+// for the split entry point, to memory.  The token scores never leave registers.
+#include "msa_device.h"
+#include "msa_kernels.h"
+
+namespace msa {
+
+namespace {
+
+constexpr int kIdxWaves = 4;
+constexpr int kIdxThreads = kIdxWaves * kWave;
+
+// Stage key block b of k_idx into LDS: 128 rows x 8 chunks of 16 B, chunk c of row
+// j stored at chunk position c ^ (j & 7) (spreads a 32-row column read over banks).
+__device__ __forceinline__ void idx_load_block(const uint16_t* __restrict__ k_idx, int64_t N,
+                                               int64_t b, int tid, uint4 (&r)[4]) {
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int cidx = tid + kIdxThreads * m;
+    const int key = cidx >> 3, c = cidx & 7;
+    const int64_t j = b * kBk + key;
+    r[m] = j < N ? *reinterpret_cast<const uint4*>(k_idx + j * kDidx + c * 8) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void idx_store_block(uint8_t* buf, int tid, const uint4 (&r)[4]) {
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int cidx = tid + kIdxThreads * m;
+    const int key = cidx >> 3, c = cidx & 7;
+    *reinterpret_cast<uint4*>(buf + key * 128 + ((c ^ (key & 7)) << 4)) = r[m];
+  }
+}
+
+// LIST: register list length (>= k-1); CT: 32-column tiles per wave.
+// WRITE_M: emit block scores M[c][b] (scaled) instead of selecting.
+template <int LIST, int CT, bool WRITE_M>
+__global__ __launch_bounds__(kIdxThreads, 2) void index_topk_kernel(
+    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, int64_t N, int H_kv,
+    int k, int64_t B, int32_t* __restrict__ block_idx, float* __restrict__ M) {
+  constexpr int kColsPerWave = 32 * CT;
+  constexpr int kCols = kIdxWaves * kColsPerWave;
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][kBk * kDidx * 2];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int64_t total = N * H_kv;
+  // Longest sweeps (largest query positions) are dispatched first.
+  const int64_t tile = (int64_t)gridDim.x - 1 - blockIdx.x;
+  const int64_t c0 = tile * kCols;
+  const int64_t c_end = (c0 + kCols < total ? c0 + kCols : total);
+  const int64_t b_last = ((c_end - 1) / H_kv) / kBk;
+  const int64_t wave_c0 = c0 + wave * kColsPerWave;
+  const int64_t i_min_wave = wave_c0 / H_kv;
+
+  int64_t col[CT], qi[CT];
+  uint4 qop[CT][4];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    col[ct] = wave_c0 + ct * 32 + l32;
+    const bool ok = col[ct] < total;
+    qi[ct] = ok ? col[ct] / H_kv : -1;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      qop[ct][ks] = ok ? *reinterpret_cast<const uint4*>(q_idx + col[ct] * kDidx + ks * 16 + 8 * h)
+                       : make_uint4(0, 0, 0, 0);
+  }
+
+  TopList<LIST> list[CT];
+  if constexpr (!WRITE_M) {
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) list[ct].init();
+  }
+
+  uint4 pre[4];
+  idx_load_block(k_idx, N, 0, tid, pre);
+  for (int64_t b = 0; b <= b_last; ++b) {
+    uint8_t* buf = kbuf[b & 1];
+    idx_store_block(buf, tid, pre);
+    __syncthreads();
+    if (b < b_last) idx_load_block(k_idx, N, b + 1, tid, pre);
+    const bool need_mask = b * kBk + (kBk - 1) > i_min_wave;
+    float runmax[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) runmax[ct] = -__builtin_inff();
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const int key = kt * 32 + l32;
+      uint4 a[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int c = ks * 2 + h;
+        a[ks] = *reinterpret_cast<const uint4*>(buf + key * 128 + ((c ^ (key & 7)) << 4));
+      }
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        f32x16_t acc = {};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) acc = mfma_32x32x16(as_bf16x8(a[ks]), as_bf16x8(qop[ct][ks]), acc);
+        if (need_mask) {
+          const int64_t jbase = b * kBk + kt * 32 + 4 * h;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int64_t j = jbase + 8 * (v >> 2) + (v & 3);
+            runmax[ct] = fmaxf(runmax[ct], j <= qi[ct] ? acc[v] : -__builtin_inff());
+          }
+        } else {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) runmax[ct] = fmaxf(runmax[ct], acc[v]);
+        }
+      }
+    }
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const float m = fmaxf(runmax[ct], __shfl_xor(runmax[ct], 32));
+      if constexpr (WRITE_M) {
+        if (h == 0 && qi[ct] >= 0) M[col[ct] * B + b] = m * 0.125f;  // 1/sqrt(64), exact
+      } else {
+        // Blocks before the local one compete; the local block is forced later.
+        if (b < qi[ct] / kBk) list[ct].offer(m, (int)b);
+      }
+    }
+  }
+
+  if constexpr (!WRITE_M) {
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      if (qi[ct] < 0) continue;
+      // Lanes l and l+32 hold identical lists; each writes half of the row.
+      int cand[LIST + 1];
+#pragma unroll
+      for (int j = 0; j < LIST; ++j) cand[j] = (j < k - 1 && list[ct].b[j] >= 0) ? list[ct].b[j] : 0x7fffffff;
+      cand[LIST] = 0x7fffffff;
+      int32_t out[LIST + 1];
+      write_selection<LIST + 1>(cand, k, (int)(qi[ct] / kBk), out);
+      int32_t* row = block_idx + col[ct] * k;
+      const int half = (k + 1) >> 1;
+#pragma unroll
+      for (int t = 0; t <= LIST; ++t) {
+        if (t < k && ((t < half) == (h == 0))) row[t] = out[t];
+      }
+    }
+  }
+}
+
+template <int LIST>
+__global__ __launch_bounds__(256) void topk_from_scores_kernel(const float* __restrict__ M, int64_t N,
+                                                                int H_kv, int64_t B, int k,
+                                                                int32_t* __restrict__ block_idx) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= N * H_kv) return;
+  const int64_t i = c / H_kv;
+  const int64_t bl = i / kBk;
+  TopList<LIST> list;
+  list.init();
+  const float* row = M + c * B;
+  for (int64_t b = 0; b < bl; ++b) list.offer(row[b], (int)b);
+  int cand[LIST + 1];
+#pragma unroll
+  for (int j = 0; j < LIST; ++j) cand[j] = (j < k - 1 && list.b[j] >= 0) ? list.b[j] : 0x7fffffff;
+  cand[LIST] = 0x7fffffff;
+  int32_t out[LIST + 1];
+  write_selection<LIST + 1>(cand, k, (int)bl, out);
+  int32_t* orow = block_idx + c * k;
+#pragma unroll
+  for (int t = 0; t <= LIST; ++t)
+    if (t < k) orow[t] = out[t];
+}
+
+__global__ void fill_f32_kernel(float* __restrict__ p, int64_t n, float val) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += stride) p[e] = val;
+}
+
+}  // namespace
+
+hipError_t launch_index_topk(const uint16_t* q_idx, const uint16_t* k_idx, int64_t N, int H_kv, int k,
+                             int32_t* block_idx, hipStream_t stream) {
+  const int64_t total = N * H_kv;
+  if (k <= 8) {
+    constexpr int CT = 2;
+    const int64_t grid = (total + kIdxWaves * 32 * CT - 1) / (kIdxWaves * 32 * CT);
+    index_topk_kernel<7, CT, false><<<dim3((unsigned)grid), dim3(kIdxThreads), 0, stream>>>(
+        q_idx, k_idx, N, H_kv, k, 0, block_idx, nullptr);
+  } else if (k <= 16) {
+    constexpr int CT = 2;
+    const int64_t grid = (total + kIdxWaves * 32 * CT - 1) / (kIdxWaves * 32 * CT);
+    index_topk_kernel<15, CT, false><<<dim3((unsigned)grid), dim3(kIdxThreads), 0, stream>>>(
+        q_idx, k_idx, N, H_kv, k, 0, block_idx, nullptr);
+  } else {
+    constexpr int CT = 1;
+    const int64_t grid = (total + kIdxWaves * 32 * CT - 1) / (kIdxWaves * 32 * CT);
+    index_topk_kernel<31, CT, false><<<dim3((unsigned)grid), dim3(kIdxThreads), 0, stream>>>(
+        q_idx, k_idx, N, H_kv, k, 0, block_idx, nullptr);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_index_block_scores(const uint16_t* q_idx, const uint16_t* k_idx, int64_t N, int H_kv,
+                                     float* M, hipStream_t stream) {
+  const int64_t B = (N + kBk - 1) / kBk;
+  const int64_t nM = N * H_kv * B;
+  fill_f32_kernel<<<dim3(1024), dim3(256), 0, stream>>>(M, nM, -__builtin_inff());
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  constexpr int CT = 2;
+  const int64_t total = N * H_kv;
+  const int64_t grid = (total + kIdxWaves * 32 * CT - 1) / (kIdxWaves * 32 * CT);
+  index_topk_kernel<1, CT, true><<<dim3((unsigned)grid), dim3(kIdxThreads), 0, stream>>>(
+      q_idx, k_idx, N, H_kv, 1, B, nullptr, M);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_from_scores(const float* M, int64_t N, int H_kv, int64_t B, int k, int32_t* block_idx,
+                                   hipStream_t stream) {
+  const int64_t grid = (N * H_kv + 255) / 256;
+  if (k <= 8)
+    topk_from_scores_kernel<7><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(M, N, H_kv, B, k, block_idx);
+  else if (k <= 16)
+    topk_from_scores_kernel<15><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(M, N, H_kv, B, k, block_idx);
+  else
+    topk_from_scores_kernel<31><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(M, N, H_kv, B, k, block_idx);
+  return hipGetLastError();
+}
+
+}  // namespace msa

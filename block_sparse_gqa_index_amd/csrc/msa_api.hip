@@ -1,0 +1,248 @@
+// C ABI of the MSA forward path: argument checks, workspace sizing and launches.
+// Every entry point validates on the host, then enqueues asynchronously on the
+// caller's stream; nothing here synchronises or allocates device memory.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "msa.h"
+#include "msa_kernels.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+msa_status_t fail(msa_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+msa_status_t ok() {
+  g_last_error[0] = '\0';
+  return MSA_OK;
+}
+
+msa_status_t hip_fail(hipError_t e, const char* where) {
+  return fail(MSA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+constexpr int64_t kMaxN = (int64_t)1 << 24;
+constexpr int64_t kMaxBlocks = 8192;  // inverse-index passes keep 2 x B counters in LDS
+// Default cap on the KV-outer partial buffers; larger inputs run in query windows.
+constexpr size_t kDefaultAttnWorkspace = (size_t)8 << 30;
+
+msa_status_t check_common(int64_t N, int d, int expect_d, const char* dname, int B_k, int k) {
+  if (N < 0) return fail(MSA_ERR_INVALID_ARG, "N must be >= 0 (got %lld)", (long long)N);
+  if (d != expect_d) return fail(MSA_ERR_UNSUPPORTED, "%s must be %d (got %d)", dname, expect_d, d);
+  if (B_k != msa::kBlockKeys) return fail(MSA_ERR_UNSUPPORTED, "B_k must be 128 (got %d)", B_k);
+  if (k < 1 || k > 32) return fail(MSA_ERR_UNSUPPORTED, "k must be in [1, 32] (got %d)", k);
+  if (N >= kMaxN) return fail(MSA_ERR_UNSUPPORTED, "N must be < 2^24 (got %lld)", (long long)N);
+  if ((N + B_k - 1) / B_k > kMaxBlocks) return fail(MSA_ERR_UNSUPPORTED, "too many blocks");
+  return MSA_OK;
+}
+
+int num_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+int64_t window_for_bytes(int64_t N, int H_q, int H_kv, int k, size_t ws_bytes) {
+  const int64_t B = (N + msa::kBlockKeys - 1) / msa::kBlockKeys;
+  // Windows are whole blocks of queries; the largest that fits wins.
+  int64_t lo = 0, hi = B;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) / 2;
+    const int64_t W = mid * msa::kBlockKeys < N ? mid * msa::kBlockKeys : N;
+    if (msa::attn_workspace_layout(W, H_q, H_kv, k, B).total <= ws_bytes)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo * msa::kBlockKeys < N ? lo * msa::kBlockKeys : N;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* msa_status_string(msa_status_t s) {
+  switch (s) {
+    case MSA_OK: return "MSA_OK";
+    case MSA_ERR_INVALID_ARG: return "MSA_ERR_INVALID_ARG";
+    case MSA_ERR_UNSUPPORTED: return "MSA_ERR_UNSUPPORTED";
+    case MSA_ERR_WORKSPACE: return "MSA_ERR_WORKSPACE";
+    case MSA_ERR_HIP: return "MSA_ERR_HIP";
+  }
+  return "MSA_ERR_UNKNOWN";
+}
+
+const char* msa_last_error(void) { return g_last_error; }
+
+size_t msa_index_topk_workspace(int64_t, int, int, int, int) { return 0; }
+
+msa_status_t msa_index_topk(const void* q_idx, const void* k_idx, int64_t N, int H_kv, int d_idx, int B_k, int k,
+                            int32_t* block_idx, void*, size_t, void* hip_stream) {
+  msa_status_t st = check_common(N, d_idx, msa::kIndexDim, "d_idx", B_k, k);
+  if (st != MSA_OK) return st;
+  if (H_kv < 1) return fail(MSA_ERR_INVALID_ARG, "H_kv must be >= 1");
+  if (N == 0) return ok();
+  if (!q_idx || !k_idx || !block_idx) return fail(MSA_ERR_INVALID_ARG, "null pointer");
+  if (!aligned(q_idx, 16) || !aligned(k_idx, 16) || !aligned(block_idx, 4))
+    return fail(MSA_ERR_INVALID_ARG, "misaligned pointer (q_idx/k_idx need 16 B, block_idx 4 B)");
+  if (N * H_kv >= ((int64_t)1 << 31)) return fail(MSA_ERR_UNSUPPORTED, "N * H_kv too large");
+  hipError_t e = msa::launch_index_topk(static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx),
+                                        N, H_kv, k, block_idx, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "index_topk launch");
+  return ok();
+}
+
+msa_status_t msa_index_block_scores(const void* q_idx, const void* k_idx, int64_t N, int H_kv, int d_idx, int B_k,
+                                    float* M, void* hip_stream) {
+  msa_status_t st = check_common(N, d_idx, msa::kIndexDim, "d_idx", B_k, 1);
+  if (st != MSA_OK) return st;
+  if (H_kv < 1) return fail(MSA_ERR_INVALID_ARG, "H_kv must be >= 1");
+  if (N == 0) return ok();
+  if (!q_idx || !k_idx || !M) return fail(MSA_ERR_INVALID_ARG, "null pointer");
+  if (!aligned(q_idx, 16) || !aligned(k_idx, 16) || !aligned(M, 4))
+    return fail(MSA_ERR_INVALID_ARG, "misaligned pointer");
+  hipError_t e = msa::launch_index_block_scores(static_cast<const uint16_t*>(q_idx),
+                                                static_cast<const uint16_t*>(k_idx), N, H_kv, M,
+                                                static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "index_block_scores launch");
+  return ok();
+}
+
+msa_status_t msa_topk_from_scores(const float* M, int64_t N, int H_kv, int64_t B, int B_k, int k, int32_t* block_idx,
+                                  void* hip_stream) {
+  msa_status_t st = check_common(N, msa::kIndexDim, msa::kIndexDim, "d_idx", B_k, k);
+  if (st != MSA_OK) return st;
+  if (H_kv < 1) return fail(MSA_ERR_INVALID_ARG, "H_kv must be >= 1");
+  if (B < (N + B_k - 1) / B_k) return fail(MSA_ERR_INVALID_ARG, "B must be >= ceil(N / B_k)");
+  if (N == 0) return ok();
+  if (!M || !block_idx) return fail(MSA_ERR_INVALID_ARG, "null pointer");
+  if (!aligned(M, 4) || !aligned(block_idx, 4)) return fail(MSA_ERR_INVALID_ARG, "misaligned pointer");
+  hipError_t e = msa::launch_topk_from_scores(M, N, H_kv, B, k, block_idx, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "topk_from_scores launch");
+  return ok();
+}
+
+static msa_status_t check_attn_shape(int64_t N, int H_q, int H_kv, int d_h, int B_k, int k) {
+  msa_status_t st = check_common(N, d_h, msa::kHeadDim, "d_h", B_k, k);
+  if (st != MSA_OK) return st;
+  if (H_kv < 1 || H_q < 1 || H_q % H_kv != 0)
+    return fail(MSA_ERR_INVALID_ARG, "H_q must be a positive multiple of H_kv");
+  const int G = H_q / H_kv;
+  if (!is_pow2(G) || G > 128) return fail(MSA_ERR_UNSUPPORTED, "H_q / H_kv must be a power of two <= 128");
+  return MSA_OK;
+}
+
+size_t msa_sparse_attn_fwd_workspace(int64_t N, int H_q, int H_kv, int d_h, int B_k, int k) {
+  if (check_attn_shape(N, H_q, H_kv, d_h, B_k, k) != MSA_OK || N == 0) return 0;
+  const int64_t W = window_for_bytes(N, H_q, H_kv, k, kDefaultAttnWorkspace);
+  const int64_t B = (N + B_k - 1) / B_k;
+  const int64_t Wmin = N < B_k ? N : B_k;
+  return msa::attn_workspace_layout(W > Wmin ? W : Wmin, H_q, H_kv, k, B).total;
+}
+
+size_t msa_sparse_attn_fwd_workspace_min(int64_t N, int H_q, int H_kv, int d_h, int B_k, int k) {
+  if (check_attn_shape(N, H_q, H_kv, d_h, B_k, k) != MSA_OK || N == 0) return 0;
+  const int64_t B = (N + B_k - 1) / B_k;
+  return msa::attn_workspace_layout(N < B_k ? N : B_k, H_q, H_kv, k, B).total;
+}
+
+msa_status_t msa_sparse_attn_fwd(const void* q, const void* k, const void* v, const int32_t* block_idx, int64_t N,
+                                 int H_q, int H_kv, int d_h, int B_k, int k_sel, float scale, float* o, float* lse,
+                                 void* ws, size_t ws_bytes, void* hip_stream) {
+  msa_status_t st = check_attn_shape(N, H_q, H_kv, d_h, B_k, k_sel);
+  if (st != MSA_OK) return st;
+  if (!(scale > 0.f) || scale != scale) return fail(MSA_ERR_INVALID_ARG, "scale must be a positive number");
+  if (N == 0) return ok();
+  if (!q || !k || !v || !block_idx || !o || !lse) return fail(MSA_ERR_INVALID_ARG, "null pointer");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(block_idx, 4) || !aligned(o, 16) ||
+      !aligned(lse, 4))
+    return fail(MSA_ERR_INVALID_ARG, "misaligned pointer (q/k/v/o need 16 B)");
+  const size_t need = msa_sparse_attn_fwd_workspace_min(N, H_q, H_kv, d_h, B_k, k_sel);
+  if (!ws || ws_bytes < need)
+    return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes is below the minimum %zu", ws ? ws_bytes : 0, need);
+  if (!aligned(ws, 256)) return fail(MSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const int64_t B = (N + B_k - 1) / B_k;
+  int64_t W = window_for_bytes(N, H_q, H_kv, k_sel, ws_bytes);
+  const int64_t Wmin = N < B_k ? N : B_k;
+  if (W < Wmin) W = Wmin;
+  const msa::AttnWorkspace L = msa::attn_workspace_layout(W, H_q, H_kv, k_sel, B);
+  const int cus = num_cus();
+  for (int64_t w0 = 0; w0 < N; w0 += W) {
+    const int64_t Wn = (N - w0 < W) ? N - w0 : W;
+    hipError_t e = msa::launch_sparse_attn_window(
+        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), block_idx,
+        N, H_q, H_kv, k_sel, scale, w0, Wn, cus, o, lse, static_cast<uint8_t*>(ws), L,
+        static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return hip_fail(e, "sparse_attn launch");
+  }
+  return ok();
+}
+
+static msa_status_t check_decode_shape(int batch, int64_t max_len, int H_q, int H_kv, int d_h, int d_idx, int B_k,
+                                       int k) {
+  if (batch < 0) return fail(MSA_ERR_INVALID_ARG, "batch must be >= 0");
+  if (max_len < 0) return fail(MSA_ERR_INVALID_ARG, "max_len must be >= 0");
+  msa_status_t st = check_common(max_len, d_h, msa::kHeadDim, "d_h", B_k, k);
+  if (st != MSA_OK) return st;
+  if (d_idx != msa::kIndexDim) return fail(MSA_ERR_UNSUPPORTED, "d_idx must be 64 (got %d)", d_idx);
+  if (H_kv < 1 || H_q < 1 || H_q % H_kv != 0)
+    return fail(MSA_ERR_INVALID_ARG, "H_q must be a positive multiple of H_kv");
+  if (H_kv > 16) return fail(MSA_ERR_UNSUPPORTED, "decode supports H_kv <= 16");
+  const int G = H_q / H_kv;
+  if (!is_pow2(G) || G > 16) return fail(MSA_ERR_UNSUPPORTED, "decode supports H_q / H_kv in {1,2,4,8,16}");
+  return MSA_OK;
+}
+
+size_t msa_decode_workspace(int batch, int H_q, int H_kv, int d_h, int d_idx, int B_k, int k, int64_t max_len) {
+  if (check_decode_shape(batch, max_len, H_q, H_kv, d_h, d_idx, B_k, k) != MSA_OK) return 0;
+  const int64_t Bmax = (max_len + B_k - 1) / B_k;
+  return msa::decode_workspace_layout(batch, H_q, H_kv, k, Bmax > 0 ? Bmax : 1).total;
+}
+
+msa_status_t msa_decode(const void* q, const void* q_idx, const void* k_cache, const void* v_cache,
+                        const void* k_idx_cache, const int64_t* cu_seqlens, int batch, int64_t max_len, int H_q,
+                        int H_kv, int d_h, int d_idx, int B_k, int k, float scale, int32_t* block_idx, float* o,
+                        float* lse, void* ws, size_t ws_bytes, void* hip_stream) {
+  msa_status_t st = check_decode_shape(batch, max_len, H_q, H_kv, d_h, d_idx, B_k, k);
+  if (st != MSA_OK) return st;
+  if (!(scale > 0.f) || scale != scale) return fail(MSA_ERR_INVALID_ARG, "scale must be a positive number");
+  if (batch == 0) return ok();
+  if (max_len == 0) return fail(MSA_ERR_INVALID_ARG, "max_len must be >= 1 when batch > 0");
+  if (!q || !q_idx || !k_cache || !v_cache || !k_idx_cache || !cu_seqlens || !block_idx || !o || !lse)
+    return fail(MSA_ERR_INVALID_ARG, "null pointer");
+  if (!aligned(q, 16) || !aligned(q_idx, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(k_idx_cache, 16) || !aligned(cu_seqlens, 8) || !aligned(block_idx, 4) || !aligned(o, 16) ||
+      !aligned(lse, 4))
+    return fail(MSA_ERR_INVALID_ARG, "misaligned pointer");
+  const size_t need = msa_decode_workspace(batch, H_q, H_kv, d_h, d_idx, B_k, k, max_len);
+  if (!ws || ws_bytes < need)
+    return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes is below the required %zu", ws ? ws_bytes : 0, need);
+  if (!aligned(ws, 256)) return fail(MSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const int64_t Bmax = (max_len + B_k - 1) / B_k;
+  const msa::DecodeWorkspace L = msa::decode_workspace_layout(batch, H_q, H_kv, k, Bmax);
+  hipError_t e = msa::launch_decode(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_cache),
+      static_cast<const uint16_t*>(v_cache), static_cast<const uint16_t*>(k_idx_cache), cu_seqlens, batch, Bmax, H_q,
+      H_kv, k, scale, block_idx, o, lse, static_cast<uint8_t*>(ws), L, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return ok();
+}
+
+}  // extern "C"

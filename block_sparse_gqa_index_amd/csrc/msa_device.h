@@ -1,0 +1,141 @@
+// Device-side helpers shared by the MSA kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+constexpr int kDh = 128;    // head dim of the main branch
+constexpr int kDidx = 64;   // index head dim
+constexpr int kBk = 128;    // keys per block
+constexpr int kWave = 64;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+// D(32x32) += A(32x16) * B(16x32), bf16 in, fp32 accumulate.
+// Lane l supplies A[l%32][8*(l/32) .. +7] and B[8*(l/32) .. +7][l%32]; it receives
+// D[8*(v/4) + 4*(l/32) + v%4][l%32] in element v.
+__device__ __forceinline__ f32x16_t mfma_32x32x16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// D(16x16) += A(16x32) * B(32x16).  Lane l supplies A[l%16][8*(l/16) .. +7] and
+// B[8*(l/16) .. +7][l%16]; it receives D[4*(l/16) + v][l%16] in element v.
+__device__ __forceinline__ f32x4_t mfma_16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Two fp32 -> packed bf16x2 with round-to-nearest-even (inputs are finite).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+  bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+// ---------------------------------------------------------------------------------
+// Streaming Top-L list kept in registers by one lane: values descending, and among
+// equal values the lower block index first.  Blocks must be offered in increasing
+// index order, so a newcomer ranks below every kept entry of equal value.
+template <int L>
+struct TopList {
+  float v[L];
+  int b[L];
+
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+      v[j] = -__builtin_inff();
+      b[j] = -1;
+    }
+  }
+
+  __device__ __forceinline__ void offer(float x, int blk) {
+    if (x > v[L - 1]) {
+      // position p = #{j : v[j] >= x}; entries from p move down by one.
+#pragma unroll
+      for (int j = L - 1; j >= 1; --j) {
+        const bool keep = v[j] >= x;
+        const bool prev = v[j - 1] >= x;
+        const float nv = keep ? v[j] : (prev ? x : v[j - 1]);
+        const int nb = keep ? b[j] : (prev ? blk : b[j - 1]);
+        v[j] = nv;
+        b[j] = nb;
+      }
+      if (!(v[0] >= x)) {
+        v[0] = x;
+        b[0] = blk;
+      }
+    }
+  }
+
+  // Remove the head (used when merging lists across lanes).
+  __device__ __forceinline__ void pop() {
+#pragma unroll
+    for (int j = 0; j < L - 1; ++j) {
+      v[j] = v[j + 1];
+      b[j] = b[j + 1];
+    }
+    v[L - 1] = -__builtin_inff();
+    b[L - 1] = -1;
+  }
+};
+
+template <int N>
+__device__ __forceinline__ void bitonic_sort_asc(int (&a)[N]) {
+#pragma unroll
+  for (int size = 2; size <= N; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const bool asc = (i & size) == 0;
+          const int x = a[i], y = a[j];
+          const int lo = x < y ? x : y, hi = x < y ? y : x;
+          a[i] = asc ? lo : hi;
+          a[j] = asc ? hi : lo;
+        }
+      }
+    }
+  }
+}
+
+// Final selection for one (query, group): the first k-1 kept blocks plus the local
+// block b_loc, ascending, then -1 padding.  `cand` holds N >= k entries, with
+// INT_MAX for "no block".  Writes k ints to out.
+template <int N>
+__device__ __forceinline__ void write_selection(int (&cand)[N], int k, int b_loc, int32_t* out) {
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < N; ++j) cnt += cand[j] != 0x7fffffff;
+  bitonic_sort_asc<N>(cand);
+#pragma unroll
+  for (int t = 0; t < N; ++t) {
+    if (t < k) out[t] = t < cnt ? cand[t] : (t == cnt ? b_loc : -1);
+  }
+}
+
+}  // namespace msa

@@ -1,0 +1,47 @@
+// Host-side launchers of the MSA kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace msa {
+
+// Shapes of the fast path (head dim, index head dim, keys per block).
+constexpr int kHeadDim = 128;
+constexpr int kIndexDim = 64;
+constexpr int kBlockKeys = 128;
+
+// Chunks (of 128 MFMA rows) per work item of the KV-outer kernel.
+constexpr int kItemChunks = 4;
+
+struct AttnWorkspace {
+  size_t counts, cursor, n_items, items, pairs, opart, lpart, total;
+  int64_t max_items;
+  int item_q;  // queries per work item
+};
+
+struct DecodeWorkspace {
+  size_t M, opart, lpart, total;
+};
+
+hipError_t launch_index_topk(const uint16_t* q_idx, const uint16_t* k_idx, int64_t N, int H_kv, int k,
+                             int32_t* block_idx, hipStream_t stream);
+hipError_t launch_index_block_scores(const uint16_t* q_idx, const uint16_t* k_idx, int64_t N, int H_kv,
+                                     float* M, hipStream_t stream);
+hipError_t launch_topk_from_scores(const float* M, int64_t N, int H_kv, int64_t B, int k, int32_t* block_idx,
+                                   hipStream_t stream);
+
+AttnWorkspace attn_workspace_layout(int64_t W, int H_q, int H_kv, int kk, int64_t B);
+hipError_t launch_sparse_attn_window(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                     const int32_t* block_idx, int64_t N, int H_q, int H_kv, int kk,
+                                     float scale, int64_t w0, int64_t W, int num_cus, float* o, float* lse,
+                                     uint8_t* ws, const AttnWorkspace& L, hipStream_t stream);
+
+DecodeWorkspace decode_workspace_layout(int batch, int H_q, int H_kv, int kk, int64_t Bmax);
+hipError_t launch_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_t* k_cache,
+                         const uint16_t* v_cache, const uint16_t* k_idx_cache, const int64_t* cu, int batch,
+                         int64_t Bmax, int H_q, int H_kv, int kk, float scale, int32_t* block_idx, float* o,
+                         float* lse, uint8_t* ws, const DecodeWorkspace& L, hipStream_t stream);
+
+}  // namespace msa

@@ -1,0 +1,137 @@
+/*
+ * msa.h — C ABI of the MSA (MiniMax Sparse Attention) forward path on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The method (page "MiniMax Sparse Attention (MSA)" paper review, section 3):
+ *   Index Branch  — Eq. 6: every causal token j <= i is scored per GQA group r
+ *                   with one index-query head against one shared index-key
+ *                   head, S = <Q_idx[i,r], K_idx[j]> / sqrt(d_idx); the scores
+ *                   are max-pooled per block of B_k keys (Eq. 4 partition);
+ *                 — Eq. 7: the k best blocks are kept per (query, group) without
+ *                   any exponential; the query's own (local) block is always
+ *                   kept and uses one of the k slots (reading notes page,
+ *                   section 5.1.1).
+ *   Main Branch   — Eq. 8: exact softmax attention of every head of group r over
+ *                   the tokens of the kept blocks, causal inside the local block.
+ *
+ * Conventions for every call
+ *   - All tensors live in device memory, row-major and contiguous, and must be
+ *     16-byte aligned.  bf16 tensors are passed as raw device pointers.
+ *   - The caller owns every buffer, including the workspace whose size the
+ *     matching *_workspace() query returns.  The library keeps no device memory
+ *     between calls, holds no state and is re-entrant per stream.
+ *   - Calls are asynchronous on `hip_stream` (a hipStream_t passed as void*;
+ *     NULL = the default stream) and never synchronise.
+ *   - Arguments are checked on the host before anything is launched; a bad call
+ *     returns a status and writes nothing.  No call aborts or throws.  A failed
+ *     launch returns MSA_ERR_HIP.  msa_last_error() describes the last failure
+ *     on the calling thread.
+ *   - Blocks are numbered from 0: block b holds tokens [b*B_k, min((b+1)*B_k, N)).
+ *     Head h belongs to group h / (H_q / H_kv) (adjacent heads share a KV head).
+ *   - Supported shapes: d_h = 128, d_idx = 64, B_k = 128, 1 <= k <= 32,
+ *     H_q / H_kv a power of two <= 128 and ceil(N / B_k) <= 8192 (N <= 2^20).
+ *     Other shapes return MSA_ERR_UNSUPPORTED.  N = 0 (or batch = 0) is a valid
+ *     empty call that launches nothing.
+ *   - Same inputs give bitwise-identical outputs (no atomics touch results).
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MSA_OK = 0,
+  MSA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, negative size, inconsistent shape */
+  MSA_ERR_UNSUPPORTED = 2, /* shape outside the supported set above */
+  MSA_ERR_WORKSPACE = 3,   /* workspace pointer null or smaller than required */
+  MSA_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} msa_status_t;
+
+const char* msa_status_string(msa_status_t status);
+const char* msa_last_error(void);
+
+/* ------------------------------------------------------------------ Index Branch
+ * msa_index_topk — Eq. 6 + Eq. 7 with the forced local block.
+ *   q_idx     bf16 [N, H_kv, d_idx]   index queries (one head per group)
+ *   k_idx     bf16 [N, d_idx]         shared index keys
+ *   block_idx int32 [N, H_kv, k]      out: per (query, group) the chosen blocks,
+ *             ascending, padded with -1 when fewer than k blocks are causal
+ *             (b_loc + 1 < k).  Ties in block score go to the lower block index.
+ * The N x N token scores and the block scores are never written to memory.
+ * Needs no workspace (msa_index_topk_workspace returns 0; ws may be NULL).
+ */
+size_t msa_index_topk_workspace(int64_t N, int H_kv, int d_idx, int B_k, int k);
+msa_status_t msa_index_topk(const void* q_idx, const void* k_idx, int64_t N, int H_kv, int d_idx,
+                            int B_k, int k, int32_t* block_idx, void* ws, size_t ws_bytes,
+                            void* hip_stream);
+
+/* ------------------------------------------------------------------ Main Branch
+ * msa_sparse_attn_fwd — Eq. 8 over the blocks listed in block_idx.
+ *   q         bf16 [N, H_q, d_h];  k, v  bf16 [N, H_kv, d_h]
+ *   block_idx int32 [N, H_kv, k]  entries < 0 or >= ceil(N/B_k) are ignored;
+ *             entries past the query's local block add no token (causal);
+ *             each block may appear at most once per row (repeats are counted
+ *             once per occurrence).
+ *   scale     softmax scale applied to <q, k> (the pages use 1/sqrt(d_h))
+ *   o         fp32 [N, H_q, d_h]   out: normalised attention output
+ *   lse       fp32 [N, H_q]        out: natural-log sum of exp(scale * <q,k>)
+ *             over the attended tokens; a row with no token gets o = 0,
+ *             lse = -inf.
+ * Work runs KV-block-outer (pages: "KV-outer sparse attention" with query
+ * gather and a two-phase LSE combine), in query windows whose size follows
+ * from ws_bytes: the workspace query returns the size for the default window;
+ * any ws_bytes >= msa_sparse_attn_fwd_workspace_min() works (smaller windows).
+ */
+size_t msa_sparse_attn_fwd_workspace(int64_t N, int H_q, int H_kv, int d_h, int B_k, int k);
+size_t msa_sparse_attn_fwd_workspace_min(int64_t N, int H_q, int H_kv, int d_h, int B_k, int k);
+msa_status_t msa_sparse_attn_fwd(const void* q, const void* k, const void* v,
+                                 const int32_t* block_idx, int64_t N, int H_q, int H_kv, int d_h,
+                                 int B_k, int k_sel, float scale, float* o, float* lse, void* ws,
+                                 size_t ws_bytes, void* hip_stream);
+
+/* ------------------------------------------------------------------ Decode
+ * msa_decode — one new token per sequence against packed variable-length caches.
+ * The new token's K/V and index key are already the last cache entry of its
+ * sequence (position L_s - 1), so its local block is block (L_s - 1) / B_k.
+ *   q            bf16 [batch, H_q, d_h];  q_idx  bf16 [batch, H_kv, d_idx]
+ *   k_cache, v_cache bf16 [T, H_kv, d_h]; k_idx_cache bf16 [T, d_idx]
+ *   cu_seqlens   int64 [batch + 1], device memory, cu[0] = 0, cu[s+1] - cu[s] = L_s
+ *   max_len      host-side bound on every L_s (sizes the launch and workspace; a
+ *                longer sequence is only scored over its first max_len tokens)
+ *   block_idx    int32 [batch, H_kv, k]  out (as for msa_index_topk)
+ *   o            fp32 [batch, H_q, d_h]; lse fp32 [batch, H_q]  out
+ */
+size_t msa_decode_workspace(int batch, int H_q, int H_kv, int d_h, int d_idx, int B_k, int k,
+                            int64_t max_len);
+msa_status_t msa_decode(const void* q, const void* q_idx, const void* k_cache, const void* v_cache,
+                        const void* k_idx_cache, const int64_t* cu_seqlens, int batch,
+                        int64_t max_len, int H_q, int H_kv, int d_h, int d_idx, int B_k, int k,
+                        float scale, int32_t* block_idx, float* o, float* lse, void* ws,
+                        size_t ws_bytes, void* hip_stream);
+
+/* ------------------------------------------------------------------ Split entry points
+ * The pages' open interface separates a pass that emits per-block max scores from
+ * the Top-k select (reading notes page, section 5.4).  These two calls expose the
+ * same split for testing; msa_index_topk fuses them.
+ *
+ * msa_index_block_scores — Eq. 6: M fp32 [N, H_kv, B] with B = ceil(N / B_k),
+ *   M[i][r][b] = max_{j in block b, j <= i} <q_idx[i,r], k_idx[j]> / sqrt(d_idx);
+ *   -inf where block b has no visible token.
+ * msa_topk_from_scores — Eq. 7 on given scores: M fp32 [N, H_kv, B] (row stride B,
+ *   B >= ceil(N / B_k)); only M[i][r][b] for b < i / B_k is read.  Output as for
+ *   msa_index_topk.
+ */
+msa_status_t msa_index_block_scores(const void* q_idx, const void* k_idx, int64_t N, int H_kv,
+                                    int d_idx, int B_k, float* M, void* hip_stream);
+msa_status_t msa_topk_from_scores(const float* M, int64_t N, int H_kv, int64_t B, int B_k, int k,
+                                  int32_t* block_idx, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MSA_H */

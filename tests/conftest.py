@@ -16,3 +16,13 @@ def pytest_configure(config):
 def pytest_collection_modifyitems(config, items):
     # Full-size workloads run last so that a failure there hides nothing else.
     items.sort(key=lambda it: 1 if it.get_closest_marker("slow") else 0)
+
+
+def pytest_runtest_logstart(nodeid, location):
+    # On GPU runs, name each case in a progress file before it starts, so that a
+    # run cut short still says which case was running.
+    path = os.environ.get("MSA_PROGRESS_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(nodeid + "\n")
+            f.flush()

@@ -1,0 +1,133 @@
+"""The C ABI: the library loads, exports every declared symbol, and rejects bad calls
+on the host before anything is launched (no GPU is touched by these tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa.h")
+LIB = os.path.join(ROOT, "block_sparse_gqa_index_amd", "libmsa.so")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(msa_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from block_sparse_gqa_index_amd.build import build
+        build()
+    import block_sparse_gqa_index_amd as m
+    return m
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert {"msa_index_topk", "msa_sparse_attn_fwd", "msa_decode"} <= set(names)
+    raw = ctypes.CDLL(LIB)
+    for n in names:
+        assert hasattr(raw, n), n
+    assert set(names) == set(lib.EXPORTED)
+
+
+def test_no_oracle_or_torch_in_library():
+    # The product path is the HIP library alone: it must not link the oracle.
+    data = open(LIB, "rb").read() if os.path.exists(LIB) else b""
+    assert b"msa_oracle_" not in data
+
+
+def test_status_strings(lib):
+    raw = lib.raw()
+    for s, name in enumerate(["MSA_OK", "MSA_ERR_INVALID_ARG", "MSA_ERR_UNSUPPORTED", "MSA_ERR_WORKSPACE",
+                              "MSA_ERR_HIP"]):
+        assert raw.msa_status_string(s).decode() == name
+
+
+def test_index_topk_rejects_bad_arguments(lib):
+    raw = lib.raw()
+    fake = 0x10000  # never dereferenced: every call below fails validation first
+    call = lambda N=4096, H_kv=1, d_idx=64, B_k=128, k=8, q=fake, kk=fake, out=fake: raw.msa_index_topk(
+        q, kk, N, H_kv, d_idx, B_k, k, out, None, 0, None)
+    assert call(d_idx=32) == lib.MSA_ERR_UNSUPPORTED
+    assert call(B_k=64) == lib.MSA_ERR_UNSUPPORTED
+    assert call(k=0) == lib.MSA_ERR_UNSUPPORTED
+    assert call(k=33) == lib.MSA_ERR_UNSUPPORTED
+    assert call(N=-1) == lib.MSA_ERR_INVALID_ARG
+    assert call(N=1 << 24) == lib.MSA_ERR_UNSUPPORTED
+    assert call(H_kv=0) == lib.MSA_ERR_INVALID_ARG
+    assert call(q=None) == lib.MSA_ERR_INVALID_ARG
+    assert call(out=fake + 2) == lib.MSA_ERR_INVALID_ARG
+    assert call(q=fake + 8) == lib.MSA_ERR_INVALID_ARG
+    assert "misaligned" in raw.msa_last_error().decode()
+    assert call(N=0, q=None, kk=None, out=None) == lib.MSA_OK  # empty call: nothing to do
+
+
+def test_sparse_attn_rejects_bad_arguments(lib):
+    raw = lib.raw()
+    f = 0x10000
+
+    def call(N=4096, H_q=8, H_kv=2, d_h=128, B_k=128, k=8, scale=0.088, ws=f, ws_bytes=1 << 40, o=f):
+        return raw.msa_sparse_attn_fwd(f, f, f, f, N, H_q, H_kv, d_h, B_k, k, scale, o, f, ws, ws_bytes, None)
+
+    assert call(d_h=64) == lib.MSA_ERR_UNSUPPORTED
+    assert call(H_q=6, H_kv=4) == lib.MSA_ERR_INVALID_ARG
+    assert call(H_q=24, H_kv=8) == lib.MSA_ERR_UNSUPPORTED  # G = 3
+    assert call(scale=0.0) == lib.MSA_ERR_INVALID_ARG
+    assert call(scale=float("nan")) == lib.MSA_ERR_INVALID_ARG
+    assert call(ws=None) == lib.MSA_ERR_WORKSPACE
+    need = raw.msa_sparse_attn_fwd_workspace_min(4096, 8, 2, 128, 128, 8)
+    assert need > 0
+    assert call(ws_bytes=need - 1) == lib.MSA_ERR_WORKSPACE
+    assert call(ws=f + 16) == lib.MSA_ERR_INVALID_ARG  # workspace must be 256-byte aligned
+    assert call(o=f + 4) == lib.MSA_ERR_INVALID_ARG
+    assert call(N=0) == lib.MSA_OK
+
+
+def test_workspace_sizes(lib):
+    raw = lib.raw()
+    assert raw.msa_index_topk_workspace(131072, 8, 64, 128, 16) == 0
+    full = raw.msa_sparse_attn_fwd_workspace(131072, 64, 8, 128, 128, 16)
+    small = raw.msa_sparse_attn_fwd_workspace_min(131072, 64, 8, 128, 128, 16)
+    assert 0 < small < full <= (8 << 30)
+    # one query window of 128 queries: partial rows of 128 bf16 + one fp32 lse each
+    assert small >= 128 * 64 * 16 * (128 * 2 + 4)
+    assert raw.msa_sparse_attn_fwd_workspace(131072, 64, 8, 64, 128, 16) == 0  # unsupported d_h
+    assert raw.msa_decode_workspace(64, 64, 8, 128, 64, 128, 16, 131072) >= 64 * 8 * 1024 * 4
+    assert raw.msa_decode_workspace(64, 64, 32, 128, 64, 128, 16, 131072) == 0  # H_kv > 16
+
+
+def test_decode_rejects_bad_arguments(lib):
+    raw = lib.raw()
+    f = 0x10000
+
+    def call(batch=4, max_len=1024, H_q=16, H_kv=2, d_h=128, d_idx=64, B_k=128, k=4, ws=f, ws_bytes=1 << 40,
+             cu=f):
+        return raw.msa_decode(f, f, f, f, f, cu, batch, max_len, H_q, H_kv, d_h, d_idx, B_k, k, 0.088, f, f, f,
+                              ws, ws_bytes, None)
+
+    assert call(d_idx=128) == lib.MSA_ERR_UNSUPPORTED
+    assert call(H_q=64, H_kv=2) == lib.MSA_ERR_UNSUPPORTED  # G = 32 > 16
+    assert call(batch=-1) == lib.MSA_ERR_INVALID_ARG
+    assert call(max_len=0) == lib.MSA_ERR_INVALID_ARG
+    assert call(cu=None) == lib.MSA_ERR_INVALID_ARG
+    assert call(cu=f + 4) == lib.MSA_ERR_INVALID_ARG
+    assert call(ws_bytes=16) == lib.MSA_ERR_WORKSPACE
+    assert call(batch=0) == lib.MSA_OK
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    # Importing the binding from a copy without libmsa.so must raise, not fall back.
+    import shutil
+    import subprocess
+    import sys
+    pkg = tmp_path / "block_sparse_gqa_index_amd"
+    pkg.mkdir()
+    shutil.copy(os.path.join(ROOT, "block_sparse_gqa_index_amd", "__init__.py"), pkg / "__init__.py")
+    r = subprocess.run([sys.executable, "-c", "import block_sparse_gqa_index_amd"], cwd=tmp_path,
+                       capture_output=True, text=True)
+    assert r.returncode != 0 and "libmsa.so is missing" in r.stderr
