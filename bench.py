@@ -1,5 +1,27 @@
-"""Benchmark of the MSA forward path on one MI355X (filled in below)."""
+"""Benchmark of the MSA forward path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode literal|structured]
+
+A prefill step is one pass of the whole prefill path over the 128K workload
+(N = 131072, H_q = 64, H_kv = 8, d_h = 128, d_idx = 64, B_k = 128, k = 16):
+msa_index_topk (index scoring, causal max-pool, Top-k) then msa_sparse_attn_fwd
+(inverse index, KV-outer attention, LSE combine).  A decode step is msa_decode for
+64 sequences with 128K-token caches.  Inputs are synthetic (seeded, resident in
+HBM before timing starts).  One JSON line is printed.
+
+FLOP accounting (exact, from the work the method must do): index
+d_idx * H_kv * N (N + 1) (every causal (query, key) pair per group, 2 FLOP per
+multiply-add) plus main 4 * d_h * H_q * (attended (query, key) pairs); the
+nominal count of Eq. 12 (MSA paper review, section 3) is reported beside it.
+"""
 from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
 
 
 def flops_gqa_eq12(N: int, H_q: int, d_h: int) -> int:
@@ -10,3 +32,196 @@ def flops_gqa_eq12(N: int, H_q: int, d_h: int) -> int:
 def flops_msa_eq12(N: int, H_q: int, H_kv: int, d_h: int, d_idx: int, B_k: int, k: int) -> int:
     """MSA FLOPs as counted by Eq. 12: index branch H_kv d_idx N^2 + main branch 4 H_q d_h N k B_k."""
     return H_kv * d_idx * N * N + 4 * H_q * d_h * N * k * B_k
+
+
+def flops_index_exact(N: int, H_kv: int, d_idx: int) -> int:
+    """2 FLOP x d_idx per causal (query, key) pair and group: d_idx * H_kv * N (N + 1)."""
+    return d_idx * H_kv * N * (N + 1)
+
+
+def attended_pairs(block_idx, B_k: int, G: int) -> int:
+    """Sum over (query, head) of the tokens attended: sum over chosen blocks of |block ∩ [0, i]|."""
+    import torch
+    N = block_idx.shape[0]
+    i = torch.arange(N, device=block_idx.device, dtype=torch.int64).view(N, 1, 1)
+    b = block_idx.to(torch.int64)
+    valid = (b >= 0) & (b <= i // B_k)
+    n = torch.clamp(torch.minimum(i - b * B_k + 1, torch.full_like(b, B_k)), min=0)
+    return int((n * valid).sum().item()) * G
+
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--mode", default="literal", choices=["literal", "structured"])
+    ap.add_argument("--workload", default="c2")
+    ap.add_argument("--decode-workload", default="c3_128k")
+    ap.add_argument("--cpu-rows", type=int, default=192, help="query rows in the oracle's timed sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the MSA path here has no multi-GPU mode "
+              "(each GPU would own a share of the KV groups and run the same kernels).", file=sys.stderr)
+        return 2
+
+    import torch
+    import block_sparse_gqa_index_amd as msa
+    import synth
+
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    cfg = synth.CONFIGS[args.workload]
+    N, H_q, H_kv, k, B_k = cfg.N, cfg.H_q, cfg.H_kv, cfg.k, cfg.B_k
+    G = H_q // H_kv
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    log(f"generating {cfg.name} ({args.mode}) inputs")
+    inp = synth.make_prefill(cfg, args.mode, device=dev)
+    block_idx = torch.empty((N, H_kv, k), dtype=torch.int32, device=dev)
+    o = torch.empty((N, H_q, cfg.d_h), dtype=torch.float32, device=dev)
+    lse = torch.empty((N, H_q), dtype=torch.float32, device=dev)
+    ws = torch.empty(msa.msa_sparse_attn_fwd_workspace(N, H_q, H_kv, k), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def prefill_step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        msa.msa_index_topk(inp.q_idx, inp.k_idx, k, block_idx=block_idx)
+        if ev is not None:
+            ev[1].record(stream)
+        msa.msa_sparse_attn_fwd(inp.q, inp.k, inp.v, block_idx, o=o, lse=lse, workspace=ws)
+        if ev is not None:
+            ev[2].record(stream)
+
+    log("prefill warmup")
+    for _ in range(args.warmup):
+        prefill_step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    log(f"prefill timed: {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        prefill_step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_index = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    t_attn = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    ms_step = wall * 1e3 / args.steps
+
+    pairs = attended_pairs(block_idx, B_k, G)
+    f_index = flops_index_exact(N, H_kv, cfg.d_idx)
+    f_main = 4 * cfg.d_h * pairs
+    f_total = f_index + f_main
+    f_eq12 = flops_msa_eq12(N, H_q, H_kv, cfg.d_h, cfg.d_idx, B_k, k)
+    prefill_tps = N / (ms_step / 1e3)
+    tflops = f_total / (ms_step / 1e3) / 1e12
+    r_off = torch.arange(H_kv, device=dev).view(1, H_kv, 1) * cfg.B
+    ids = (block_idx.to(torch.int64) + r_off)[block_idx >= 0]
+    fan = torch.bincount(ids, minlength=H_kv * cfg.B).view(H_kv, cfg.B)
+    result = {
+        "metric": "MSA prefill tokens/s + TFLOP/s at 128K; decode tokens/s at 128K KV (1 GPU)",
+        "value": round(prefill_tps, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": f"synthetic ({args.mode} mode, seeded)",
+        "config": {"workload": f"prefill N={N} H_q={H_q} H_kv={H_kv} d_h={cfg.d_h} d_idx={cfg.d_idx} "
+                               f"B_k={B_k} k={k}", "mode": args.mode, "seq_len": N, "batch": 1},
+        "prefill": {
+            "tflops": round(tflops, 2),
+            "tflops_eq12_nominal": round(f_eq12 / (ms_step / 1e3) / 1e12, 2),
+            "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "flop_index": f_index, "flop_main": f_main, "flop_eq12": f_eq12,
+            "ms_index_topk": round(t_index, 4), "ms_sparse_attn_fwd": round(t_attn, 4),
+            "block0_fanin_per_group": int(fan[:, 0].float().mean().item()), "max_fanin": int(fan.max().item()),
+            "median_fanin": float(fan.float().median().item()),
+        },
+    }
+    # Roofline of the index-scoring kernel (a single launch inside msa_index_topk).
+    idx_tflops = f_index / (t_index / 1e3) / 1e12
+    result["roofline"] = {"kernel": "index_topk_kernel", "bound": "mfma", "achieved": round(idx_tflops, 2),
+                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                          "frac": round(idx_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None}
+
+    if not args.no_decode:
+        dcfg = synth.CONFIGS[args.decode_workload]
+        log(f"generating {dcfg.name} decode inputs")
+        d = synth.make_decode(dcfg, args.mode, device=dev)
+        max_len = max(d.lengths)
+        dbi = torch.empty((dcfg.batch, dcfg.H_kv, dcfg.k), dtype=torch.int32, device=dev)
+        do = torch.empty((dcfg.batch, dcfg.H_q, dcfg.d_h), dtype=torch.float32, device=dev)
+        dl = torch.empty((dcfg.batch, dcfg.H_q), dtype=torch.float32, device=dev)
+        dws = torch.empty(msa.msa_decode_workspace(dcfg.batch, dcfg.H_q, dcfg.H_kv, dcfg.k, max_len),
+                          dtype=torch.uint8, device=dev)
+
+        def decode_step():
+            msa.msa_decode(d.q, d.q_idx, d.k_cache, d.v_cache, d.k_idx_cache, d.cu_seqlens, max_len, dcfg.k,
+                           block_idx=dbi, o=do, lse=dl, workspace=dws)
+
+        for _ in range(args.warmup):
+            decode_step()
+        torch.cuda.synchronize()
+        dsteps = max(args.steps, 50)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(dsteps):
+            decode_step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dms = e0.elapsed_time(e1) / dsteps
+        T = int(d.cu_seqlens[-1].item())
+        # algorithmic bytes: every cached index key (d_idx bf16) + K and V of the chosen blocks
+        chosen = int((dbi >= 0).sum().item())
+        dbytes = T * dcfg.d_idx * 2 + chosen * B_k * dcfg.d_h * 2 * 2
+        result["decode"] = {
+            "workload": f"decode batch={dcfg.batch} L={min(d.lengths)}..{max_len} H_q={dcfg.H_q} H_kv={dcfg.H_kv} "
+                        f"k={dcfg.k}",
+            "ms_per_step": round(dms, 4), "tokens_per_s": round(dcfg.batch / (dms / 1e3), 1),
+            "algorithmic_bytes": dbytes, "GB_s": round(dbytes / (dms / 1e3) / 1e9, 1),
+            "hbm_peak_frac": round(dbytes / (dms / 1e3) / 1e9 / PEAK_HBM_GBS, 4), "steps": dsteps,
+        }
+        del d
+
+    if not args.no_cpu_baseline:
+        import numpy as np
+        import oracle
+        log(f"cpu baseline: oracle on {args.cpu_rows} sampled query rows")
+        g = np.random.default_rng(cfg.seed)
+        rows = np.sort(g.choice(N, size=args.cpu_rows, replace=False))
+        qi_h, ki_h = inp.q_idx.cpu(), inp.k_idx.cpu()
+        q_h, k_h, v_h = inp.q.cpu(), inp.k.cpu(), inp.v.cpu()
+        t0 = time.perf_counter()
+        M = oracle.block_scores(qi_h, ki_h, B_k, rows=rows)
+        bi = oracle.topk(M, k, B_k, rows=rows)
+        oracle.sparse_attn(q_h, k_h, v_h, bi, B_k, rows=rows)
+        tc = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": round(len(rows) / tc, 3), "unit": "tokens/s", "cores": oracle.threads(),
+                                  "kind": "oracle",
+                                  "sample": f"{len(rows)} uniformly drawn query rows of the same 128K prefill "
+                                            f"(all groups and heads; index scoring, Top-k and attention) in "
+                                            f"{tc:.1f} s"}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

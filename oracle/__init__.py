@@ -60,6 +60,7 @@ def _load():
     lib.msa_oracle_sparse_attn.argtypes = [P, P, P, P, i64, i32, i32, i32, i32, i32, dbl, P, i64, P, P]
     lib.msa_oracle_decode.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, dbl,
                                       P, P, P, P, i64]
+    lib.msa_oracle_decode_attn.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, dbl, P, P, P]
     _lib = lib
     return lib
 
@@ -179,3 +180,26 @@ def decode(q, q_idx, k_cache, v_cache, k_idx_cache, cu_seqlens, k: int, B_k: int
     if want_scores:
         return bi, o, lse, M
     return bi, o, lse
+
+
+def decode_attn(q, k_cache, v_cache, cu_seqlens, block_idx, B_k: int, scale: float | None = None):
+    """Attention of each sequence's last token on a given selection block_idx [batch, H_kv, kk]."""
+    qq, kc, vc = _u16(q), _u16(k_cache), _u16(v_cache)
+    try:
+        import torch
+        if isinstance(cu_seqlens, torch.Tensor):
+            cu_seqlens = cu_seqlens.cpu().numpy()
+    except ImportError:
+        pass
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    batch, H_q, d_h = qq.shape
+    H_kv = kc.shape[1]
+    bi = np.ascontiguousarray(np.asarray(block_idx), dtype=np.int32)
+    kk = bi.shape[2]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d_h)
+    o = np.empty((batch, H_q, d_h), dtype=np.float64)
+    lse = np.empty((batch, H_q), dtype=np.float64)
+    _load().msa_oracle_decode_attn(_ptr(qq), _ptr(kc), _ptr(vc), _ptr(cu), batch, H_q, H_kv, d_h, B_k, kk,
+                                   float(scale), _ptr(bi), _ptr(o), _ptr(lse))
+    return o, lse

@@ -218,3 +218,34 @@ void msa_oracle_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_t*
     free(Mrow);
   }
 }
+
+void msa_oracle_decode_attn(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                            const int64_t* cu_seqlens, int batch, int H_q, int H_kv, int d_h,
+                            int B_k, int kk, double scale, const int32_t* block_idx_in, double* o,
+                            double* lse) {
+  int G = H_q / H_kv;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int s = 0; s < batch; ++s) {
+    int64_t j0 = cu_seqlens[s];
+    int64_t L = cu_seqlens[s + 1] - j0;
+    if (L <= 0) continue;
+    int64_t i = L - 1;
+    int64_t B = msa_oracle_num_blocks(L, B_k);
+    char* inset = (char*)malloc((size_t)B);
+    double* s_buf = (double*)malloc(sizeof(double) * (size_t)L);
+    for (int r = 0; r < H_kv; ++r) {
+      memset(inset, 0, (size_t)B);
+      const int32_t* sel = block_idx_in + ((int64_t)s * H_kv + r) * kk;
+      for (int t = 0; t < kk; ++t)
+        if (sel[t] >= 0 && sel[t] < B) inset[sel[t]] = 1;
+      for (int g = 0; g < G; ++g) {
+        int h = r * G + g;
+        attn_row(q + ((int64_t)s * H_q + h) * d_h, k_cache + j0 * H_kv * d_h + (int64_t)r * d_h,
+                 v_cache + j0 * H_kv * d_h + (int64_t)r * d_h, (int64_t)H_kv * d_h, i, L, d_h, B_k,
+                 inset, scale, o + ((int64_t)s * H_q + h) * d_h, lse + (int64_t)s * H_q + h, s_buf);
+      }
+    }
+    free(s_buf);
+    free(inset);
+  }
+}

@@ -78,6 +78,15 @@ void msa_oracle_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_t*
                        int d_idx, int B_k, int kk, double scale, int32_t* block_idx, double* o,
                        double* lse, double* M, int64_t Bmax);
 
+/*
+ * Decode attention only (Eq. 8 for the last token of each sequence) on a given
+ * selection block_idx_in [batch][H_kv][kk] (entries < 0 ignored; a set).
+ */
+void msa_oracle_decode_attn(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                            const int64_t* cu_seqlens, int batch, int H_q, int H_kv, int d_h,
+                            int B_k, int kk, double scale, const int32_t* block_idx_in, double* o,
+                            double* lse);
+
 #ifdef __cplusplus
 }
 #endif

@@ -284,3 +284,13 @@ def test_eq12_ratio_matches_printed_28_4():
         den = bench.flops_msa_eq12(N, H_q, H_kv, d_h, d_idx, B_k, k)
         assert Fraction(num, den) == Fraction(exact)
         assert round(num / den, 1) == float(printed)
+
+
+def test_decode_attn_on_given_selection_equals_decode():
+    lengths = [300, 1000]
+    d = synth.make_decode(synth.DecodeConfig("t", batch=2, H_q=4, H_kv=2, k=3, len_lo_blocks=1,
+                                             len_hi_blocks=1, seed=9), lengths=lengths)
+    bi, o, lse = oracle.decode(d.q, d.q_idx, d.k_cache, d.v_cache, d.k_idx_cache, d.cu_seqlens, 3, 128)
+    o2, l2 = oracle.decode_attn(d.q, d.k_cache, d.v_cache, d.cu_seqlens, bi, 128)
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(lse, l2)
