@@ -26,7 +26,8 @@ constexpr int kIdxWaves = 4;
 constexpr int kIdxThreads = kIdxWaves * kWave;
 
 // Stage key block b of k_idx into LDS: 128 rows x 8 chunks of 16 B, chunk c of row
-// j stored at chunk position c ^ (j & 7) (spreads a 32-row column read over banks).
+// j stored at chunk position c ^ ((j >> 1) & 7): the 16 rows a 16-lane LDS pass
+// reads then fall on 16 different 16-byte bank groups.
 __device__ __forceinline__ void idx_load_block(const uint16_t* __restrict__ k_idx, int64_t N,
                                                int64_t b, int tid, uint4 (&r)[4]) {
 #pragma unroll
@@ -43,19 +44,64 @@ __device__ __forceinline__ void idx_store_block(uint8_t* buf, int tid, const uin
   for (int m = 0; m < 4; ++m) {
     const int cidx = tid + kIdxThreads * m;
     const int key = cidx >> 3, c = cidx & 7;
-    *reinterpret_cast<uint4*>(buf + key * 128 + ((c ^ (key & 7)) << 4)) = r[m];
+    *reinterpret_cast<uint4*>(buf + key * 128 + ((c ^ ((key >> 1) & 7)) << 4)) = r[m];
   }
+}
+
+// Block maxima of one staged key block for the lane's CT column tiles (raw dot
+// products; the 1/sqrt(d_idx) scale is applied by the caller when needed).
+template <int CT>
+__device__ __forceinline__ void idx_block_max(const uint8_t* buf, const uint4 (&qop)[CT][4], const int64_t (&qi)[CT],
+                                              int64_t b, bool need_mask, int h, int l32, float (&bmax)[CT]) {
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) bmax[ct] = -__builtin_inff();
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    const int key = kt * 32 + l32;
+    uint4 a[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int c = ks * 2 + h;
+      a[ks] = *reinterpret_cast<const uint4*>(buf + key * 128 + ((c ^ ((key >> 1) & 7)) << 4));
+    }
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      f32x16_t acc = {};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) acc = mfma_32x32x16(as_bf16x8(a[ks]), as_bf16x8(qop[ct][ks]), acc);
+      if (need_mask) {
+        // key b*128 + kt*32 + 8*(v/4) + 4h + v%4 is visible iff its offset <= lim
+        int64_t lim64 = qi[ct] - (b * kBk + kt * 32 + 4 * h);
+        lim64 = lim64 < -1 ? -1 : (lim64 > 64 ? 64 : lim64);
+        const int lim = (int)lim64;
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          bmax[ct] = fmaxf(bmax[ct], (8 * (v >> 2) + (v & 3)) <= lim ? acc[v] : -__builtin_inff());
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) bmax[ct] = fmaxf(bmax[ct], acc[v]);
+      }
+    }
+  }
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) bmax[ct] = fmaxf(bmax[ct], __shfl_xor(bmax[ct], 32));
 }
 
 // LIST: register list length (>= k-1); CT: 32-column tiles per wave.
 // WRITE_M: emit block scores M[c][b] (scaled) instead of selecting.
+//
+// Selection: key blocks are swept in pairs (b, b+1).  After the pair, both lane
+// halves hold both block maxima of their column; the lower half offers block b to
+// its list and the upper half block b+1 to its own, so one insertion sequence
+// serves two blocks.  The two lists (even / odd blocks) are merged at the end.
 template <int LIST, int CT, bool WRITE_M>
 __global__ __launch_bounds__(kIdxThreads, 2) void index_topk_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, int64_t N, int H_kv,
     int k, int64_t B, int32_t* __restrict__ block_idx, float* __restrict__ M) {
   constexpr int kColsPerWave = 32 * CT;
   constexpr int kCols = kIdxWaves * kColsPerWave;
-  __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][kBk * kDidx * 2];
+  constexpr int kBlkBytes = kBk * kDidx * 2;
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][2][kBlkBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -88,52 +134,40 @@ __global__ __launch_bounds__(kIdxThreads, 2) void index_topk_kernel(
     for (int ct = 0; ct < CT; ++ct) list[ct].init();
   }
 
-  uint4 pre[4];
-  idx_load_block(k_idx, N, 0, tid, pre);
-  for (int64_t b = 0; b <= b_last; ++b) {
-    uint8_t* buf = kbuf[b & 1];
-    idx_store_block(buf, tid, pre);
+  uint4 pre[2][4];
+  idx_load_block(k_idx, N, 0, tid, pre[0]);
+  if (b_last >= 1) idx_load_block(k_idx, N, 1, tid, pre[1]);
+  int step = 0;
+  for (int64_t b = 0; b <= b_last; b += 2, ++step) {
+    const bool two = b + 1 <= b_last;
+    uint8_t* buf0 = kbuf[step & 1][0];
+    uint8_t* buf1 = kbuf[step & 1][1];
+    idx_store_block(buf0, tid, pre[0]);
+    if (two) idx_store_block(buf1, tid, pre[1]);
     __syncthreads();
-    if (b < b_last) idx_load_block(k_idx, N, b + 1, tid, pre);
-    const bool need_mask = b * kBk + (kBk - 1) > i_min_wave;
-    float runmax[CT];
+    if (b + 2 <= b_last) idx_load_block(k_idx, N, b + 2, tid, pre[0]);
+    if (b + 3 <= b_last) idx_load_block(k_idx, N, b + 3, tid, pre[1]);
+
+    float m0[CT], m1[CT];
+    idx_block_max<CT>(buf0, qop, qi, b, b * kBk + (kBk - 1) > i_min_wave, h, l32, m0);
+    if (two) {
+      idx_block_max<CT>(buf1, qop, qi, b + 1, (b + 1) * kBk + (kBk - 1) > i_min_wave, h, l32, m1);
+    } else {
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) runmax[ct] = -__builtin_inff();
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const int key = kt * 32 + l32;
-      uint4 a[4];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int c = ks * 2 + h;
-        a[ks] = *reinterpret_cast<const uint4*>(buf + key * 128 + ((c ^ (key & 7)) << 4));
-      }
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        f32x16_t acc = {};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) acc = mfma_32x32x16(as_bf16x8(a[ks]), as_bf16x8(qop[ct][ks]), acc);
-        if (need_mask) {
-          const int64_t jbase = b * kBk + kt * 32 + 4 * h;
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int64_t j = jbase + 8 * (v >> 2) + (v & 3);
-            runmax[ct] = fmaxf(runmax[ct], j <= qi[ct] ? acc[v] : -__builtin_inff());
-          }
-        } else {
-#pragma unroll
-          for (int v = 0; v < 16; ++v) runmax[ct] = fmaxf(runmax[ct], acc[v]);
-        }
-      }
+      for (int ct = 0; ct < CT; ++ct) m1[ct] = -__builtin_inff();
     }
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
-      const float m = fmaxf(runmax[ct], __shfl_xor(runmax[ct], 32));
       if constexpr (WRITE_M) {
-        if (h == 0 && qi[ct] >= 0) M[col[ct] * B + b] = m * 0.125f;  // 1/sqrt(64), exact
+        if (qi[ct] >= 0) {
+          if (h == 0) M[col[ct] * B + b] = m0[ct] * 0.125f;  // 1/sqrt(64), exact
+          if (h == 1 && two) M[col[ct] * B + b + 1] = m1[ct] * 0.125f;
+        }
       } else {
         // Blocks before the local one compete; the local block is forced later.
-        if (b < qi[ct] / kBk) list[ct].offer(m, (int)b);
+        const int64_t blk = b + h;
+        const float x = h ? m1[ct] : m0[ct];
+        if (blk < qi[ct] / kBk) list[ct].offer(x, (int)blk);
       }
     }
   }
@@ -141,11 +175,28 @@ __global__ __launch_bounds__(kIdxThreads, 2) void index_topk_kernel(
   if constexpr (!WRITE_M) {
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
+      // Merge the even-block list (lower half) with the odd-block list (upper half):
+      // own run descending, partner's run reversed, one bitonic merge.
+      uint64_t key[2 * (LIST + 1)];
+#pragma unroll
+      for (int j = 0; j < LIST; ++j) {
+        const uint64_t mine = rank_key(list[ct].v[j], list[ct].b[j]);
+        const float ov = __shfl_xor(list[ct].v[j], 32);
+        const int ob = __shfl_xor(list[ct].b[j], 32);
+        key[j] = mine;
+        key[2 * (LIST + 1) - 1 - j] = rank_key(ov, ob);
+      }
+      key[LIST] = 0ull;
+      key[LIST + 1] = 0ull;
+      bitonic_merge_desc<2 * (LIST + 1)>(key);
       if (qi[ct] < 0) continue;
-      // Lanes l and l+32 hold identical lists; each writes half of the row.
+      // Lanes l and l+32 now hold identical merged runs; each writes half of the row.
       int cand[LIST + 1];
 #pragma unroll
-      for (int j = 0; j < LIST; ++j) cand[j] = (j < k - 1 && list[ct].b[j] >= 0) ? list[ct].b[j] : 0x7fffffff;
+      for (int j = 0; j < LIST; ++j) {
+        const int blk = rank_key_block(key[j]);
+        cand[j] = (j < k - 1 && blk >= 0) ? blk : 0x7fffffff;
+      }
       cand[LIST] = 0x7fffffff;
       int32_t out[LIST + 1];
       write_selection<LIST + 1>(cand, k, (int)(qi[ct] / kBk), out);

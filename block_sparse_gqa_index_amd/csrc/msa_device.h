@@ -9,6 +9,10 @@ namespace msa {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+// Native 16- and 8-byte integer vectors (HIP's uint4/uint2 are structs whose
+// copies can block promotion of local arrays to registers).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kDh = 128;    // head dim of the main branch
 constexpr int kDidx = 64;   // index head dim
@@ -19,6 +23,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t u) { return __builtin_bit_cast(bf16x8_t, u); }
 
 // D(32x32) += A(32x16) * B(16x32), bf16 in, fp32 accumulate.
 // Lane l supplies A[l%32][8*(l/32) .. +7] and B[8*(l/32) .. +7][l%32]; it receives
@@ -101,6 +106,37 @@ struct TopList {
     b[L - 1] = -1;
   }
 };
+
+// (value, block) packed so that a larger key means a better entry: value
+// descending, then block ascending; empty entries (block < 0) get key 0.
+__device__ __forceinline__ uint64_t rank_key(float v, int blk) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return blk < 0 ? 0ull : ((uint64_t)ord << 32) | (uint32_t)(0x7fffffff - blk);
+}
+
+__device__ __forceinline__ int rank_key_block(uint64_t key) {
+  return key == 0ull ? -1 : 0x7fffffff - (int)(uint32_t)key;
+}
+
+// Merge two descending runs a[0..N/2) and a[N/2..N) (the second stored reversed,
+// i.e. ascending) into one descending run: the bitonic merge network.
+template <int N>
+__device__ __forceinline__ void bitonic_merge_desc(uint64_t (&a)[N]) {
+#pragma unroll
+  for (int stride = N >> 1; stride > 0; stride >>= 1) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int j = i ^ stride;
+      if (j > i) {
+        const uint64_t x = a[i], y = a[j];
+        const bool sw = y > x;
+        a[i] = sw ? y : x;
+        a[j] = sw ? x : y;
+      }
+    }
+  }
+}
 
 template <int N>
 __device__ __forceinline__ void bitonic_sort_asc(int (&a)[N]) {

@@ -145,33 +145,38 @@ __global__ __launch_bounds__(256) void inv_scatter_kernel(const int32_t* __restr
 
 // --------------------------------------------------------------------- phase 1
 constexpr int kAttnThreads = 256;
-constexpr int kVtStride = kBk * 2 + 8;  // bytes per d-row of V^T (padding spreads banks)
 
-// K block -> LDS, row j (256 B = 16 chunks of 16 B), chunk c at position c ^ (j & 15).
-// V block -> LDS transposed: Vt[d][key] with rows of kVtStride bytes.
-// kb/vb point at (token b*128, group r); rows past `nvalid` read as zero.
+// LDS row rho of the staged K tile holds key swap23(rho) (bits 2 and 3 of the row
+// index exchanged).  With that order the 32x32 MFMA leaves, in each lane half, the
+// probabilities of 8 consecutive keys per PV step, so V^T is read 16 B at a time.
+__device__ __forceinline__ int swap23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
+
+// K block -> LDS: row rho (256 B = 16 chunks of 16 B) holds key swap23(rho), chunk c
+// at position c ^ (rho & 15).  V block -> LDS transposed: Vt[d] (256 B) holds keys
+// in natural order, 8-key chunk kc at position kc ^ (d & 15).  kb/vb point at
+// (token b*128, group r); keys past `nvalid` read as zero.
 __device__ __forceinline__ void stage_kv(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ vb,
                                          int row_stride, int nvalid, uint8_t* Ks, uint8_t* Vt, int tid) {
-  // K: 2048 chunks, 8 per thread (rows tid/16 + 16m, chunk tid%16).
   const int c = tid & 15;
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
-    const int key = (tid >> 4) + 16 * m;
+    const int rho = (tid >> 4) + 16 * m;
+    const int key = swap23(rho);
     const int kr = key < nvalid ? key : nvalid - 1;  // branch-free: clamp, then zero
-    uint4 val = *reinterpret_cast<const uint4*>(kb + kr * row_stride + c * 8);
-    if (key >= nvalid) val = make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(Ks + key * 256 + ((c ^ (key & 15)) << 4)) = val;
+    u32x4_t val = *reinterpret_cast<const u32x4_t*>(kb + kr * row_stride + c * 8);
+    if (key >= nvalid) val = u32x4_t{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4_t*>(Ks + rho * 256 + ((c ^ (rho & 15)) << 4)) = val;
   }
-  // V: thread owns an 8-key x 8-dim tile, transposed in registers.
-  const int dc = tid & 15;   // dims dc*8 .. +7
-  const int kg = tid >> 4;   // keys kg*8 .. +7
+  // V: thread owns keys kg*8 .. +7 x dims dc*8 .. +7, transposed in registers.
+  const int kg = tid & 15;
+  const int dc = tid >> 4;
   uint32_t w[8][4];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int key = kg * 8 + e;
     const int kr = key < nvalid ? key : nvalid - 1;
-    uint4 val = *reinterpret_cast<const uint4*>(vb + kr * row_stride + dc * 8);
-    if (key >= nvalid) val = make_uint4(0, 0, 0, 0);
+    u32x4_t val = *reinterpret_cast<const u32x4_t*>(vb + kr * row_stride + dc * 8);
+    if (key >= nvalid) val = u32x4_t{0u, 0u, 0u, 0u};
     w[e][0] = val.x;
     w[e][1] = val.y;
     w[e][2] = val.z;
@@ -179,16 +184,15 @@ __device__ __forceinline__ void stage_kv(const uint16_t* __restrict__ kb, const 
   }
 #pragma unroll
   for (int f = 0; f < 8; ++f) {
-    // dim dc*8+f for keys kg*8 .. +7: 4 dwords of (key 2m, key 2m+1)
-    uint32_t o4[4];
+    // dim d = dc*8+f for keys kg*8 .. +7: 4 dwords of (key 2m, key 2m+1)
+    u32x4_t o4;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const uint32_t a = w[2 * m][f >> 1], cc = w[2 * m + 1][f >> 1];
       o4[m] = (f & 1) ? ((a >> 16) | (cc & 0xffff0000u)) : ((a & 0xffffu) | (cc << 16));
     }
-    uint8_t* dst = Vt + (dc * 8 + f) * kVtStride + kg * 16;
-    *reinterpret_cast<uint2*>(dst) = make_uint2(o4[0], o4[1]);
-    *reinterpret_cast<uint2*>(dst + 8) = make_uint2(o4[2], o4[3]);
+    const int d = dc * 8 + f;
+    *reinterpret_cast<u32x4_t*>(Vt + d * 256 + ((kg ^ (d & 15)) << 4)) = o4;
   }
 }
 
@@ -197,10 +201,11 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
     const int4* __restrict__ items, const int32_t* __restrict__ n_items_ptr, const int32_t* __restrict__ pairs,
     int64_t N, int H_kv, int64_t B, int kk, int64_t w0, float scale_log2, uint16_t* __restrict__ Opart,
-    float* __restrict__ Lpart) {
+    float2* __restrict__ Lpart) {
   constexpr int kQC = 128 / G;         // gathered queries per chunk
   __shared__ __attribute__((aligned(16))) uint8_t Ks[kBk * 256];
-  __shared__ __attribute__((aligned(16))) uint8_t Vt[kDh * kVtStride];
+  __shared__ __attribute__((aligned(16))) uint8_t Vt[kDh * 256];
+  __shared__ __attribute__((aligned(16))) uint8_t Ostage[4][16 * 256];  // per wave: 16 rows
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -222,79 +227,117 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
 
     __syncthreads();  // previous item's LDS reads are done
     {
+      // Recompute the staging addresses per item rather than keeping ~40 loop-
+      // invariant address registers live across the whole kernel.
+      int stid = tid;
+      asm volatile("" : "+v"(stid));
       const int64_t tok0 = b * kBk;
       const int row_stride = H_kv * kDh;
       const int nvalid = (N - tok0 < kBk) ? (int)(N - tok0) : kBk;
       const int64_t base = tok0 * row_stride + r * kDh;
-      stage_kv(kp + base, vp + base, row_stride, nvalid, Ks, Vt, tid);
+      stage_kv(kp + base, vp + base, row_stride, nvalid, Ks, Vt, stid);
     }
     __syncthreads();
 
+    const int qrow = wave * 32 + l32;
+    const int qs = qrow / G, g = qrow % G;
+    // Chunk 0's gather; later chunks are prefetched one chunk ahead.  Rows past the
+    // end of the item re-read the item's first pair (a valid address); their
+    // results are discarded.
+    //
+    // The gather is coalesced: load t of lane j fetches 16-byte chunk j%16 of the
+    // wave's row 4t + j/16 (16 lanes read one 256-byte head row).  At the start of
+    // a chunk the rows are moved to the MFMA operand layout (lane l32 holds row l32)
+    // through the wave's LDS buffer, 16 rows per pass, chunk c of row rho at
+    // position c ^ rho.
+    uint8_t* ost = Ostage[wave];
+    int pr = pairs[start + (qs < cnt ? qs : 0)];
+    u32x4_t qraw[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int rho = 4 * t + (lane >> 4);
+      const int pr_row = __shfl(pr, rho);
+      const int qrow_r = wave * 32 + rho;
+      const uint16_t* qp = q + ((w0 + (pr_row >> 5)) * H_q + r * G + qrow_r % G) * kDh + (lane & 15) * 8;
+      qraw[t] = *reinterpret_cast<const u32x4_t*>(qp);
+    }
     for (int cb = 0; cb < cnt; cb += kQC) {
       // Keep the LDS operand reads inside the chunk loop: hoisting them (they do
       // not change across chunks) would need 256 registers per lane.
       asm volatile("" ::: "memory");
-      const int qrow = wave * 32 + l32;
-      const int qs = qrow / G, g = qrow % G;
+      u32x4_t qop[8];
+#pragma unroll
+      for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          const int rho = 4 * tt + (lane >> 4);
+          *reinterpret_cast<u32x4_t*>(ost + rho * 256 + (((lane & 15) ^ rho) << 4)) = qraw[4 * pass + tt];
+        }
+        if ((l32 >> 4) == pass) {
+          const int rho = l32 & 15;
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+            qop[t] = *reinterpret_cast<const u32x4_t*>(ost + rho * 256 + (((8 * h + t) ^ rho) << 4));
+        }
+      }
       const bool valid = cb + qs < cnt;
-      // Rows past the end of the item re-read the item's first pair (a valid
-      // address); their results are discarded.
-      const int pr = pairs[start + (valid ? cb + qs : 0)];
       const int64_t i_local = pr >> 5;
       const int s = pr & 31;
       const int64_t i = w0 + i_local;
 
-      uint4 qop[8];
-      const uint16_t* qrow_p = q + (i * H_q + r * G + g) * kDh + 64 * h;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) qop[t] = *reinterpret_cast<const uint4*>(qrow_p + 8 * t);
-
-      // S^T[key][qrow]: k-slot (h, e) of step t is dim 64h + 8t + e in both operands.
+      // S^T[row][qrow] with row -> key swap23(row): k-slot (h, e) of step t is dim
+      // 64h + 8t + e in both operands.
       f32x16_t sacc[4];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
+        asm volatile("" ::: "memory");  // bound the K-operand reads in flight
         sacc[kt] = f32x16_t{};
-        const int key = kt * 32 + l32;
+        const int row = kt * 32 + l32;
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
           const int c = 8 * h + t;
-          const uint4 a = *reinterpret_cast<const uint4*>(Ks + key * 256 + ((c ^ (key & 15)) << 4));
+          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(Ks + row * 256 + ((c ^ (row & 15)) << 4));
           sacc[kt] = mfma_32x32x16(as_bf16x8(a), as_bf16x8(qop[t]), sacc[kt]);
         }
       }
 
-      // Softmax over this block's keys, base-2 with the scale folded in.
-      const bool need_mask = b * kBk + (kBk - 1) > i;
+      // Causal mask, only where a lane's block reaches past its query: element v of
+      // tile kt is key kt*32 + 16*(v/8) + 4*((v/4)%2) + v%4 + 8h of the block.
+      const int lim = (int)(i - b * kBk) - 8 * h;
+      if (__any(b * kBk + (kBk - 1) > i)) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int off = kt * 32 + 16 * (v >> 3) + 4 * ((v >> 2) & 1) + (v & 3);
+            sacc[kt][v] = off <= lim ? sacc[kt][v] : -__builtin_inff();
+          }
+        }
+      }
+      // Softmax over this block's keys in base 2 with the scale folded into one FMA.
       float mx = -__builtin_inff();
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          float x = sacc[kt][v] * scale_log2;
-          if (need_mask) {
-            const int64_t j = b * kBk + kt * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-            x = j <= i ? x : -__builtin_inff();
-          }
-          sacc[kt][v] = x;
-          mx = fmaxf(mx, x);
-        }
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kt][v]);
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const bool empty = mx == -__builtin_inff();
+      const float m2 = empty ? 0.f : mx * scale_log2;
       float l = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const float p = empty ? 0.f : exp2f(sacc[kt][v] - mx);
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kt][v], scale_log2, -m2));
           sacc[kt][v] = p;
           l += p;
         }
       }
       l += __shfl_xor(l, 32);
 
-      // P in bf16 as the B operand of step u (8 keys per lane half).
-      uint4 pb[8];
+      // P in bf16 as the B operand of step u: keys 32*(u/2) + 16*(u%2) + 8h + e.
+      u32x4_t pb[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int kt = u >> 1, hf = u & 1;
@@ -304,89 +347,177 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
         pb[u].w = pack_bf16x2(sacc[kt][8 * hf + 6], sacc[kt][8 * hf + 7]);
       }
 
-      // O^T[d][qrow] = V^T[d][key] * P^T[key][qrow].  Step u covers keys of tile u/2;
-      // k-slot (h, e) is key 32*(u/2) + 16*(u%2) + 4h + (e%4) + 8*(e/4).
+      // Prefetch the next chunk's pair and q rows while this chunk finishes.
+      // (After the item's last chunk this re-reads the item's first pair: a valid
+      // address, and it keeps the current q registers dead after the MFMAs.)
+      const int pr_n = pairs[start + (cb + kQC + qs < cnt ? cb + kQC + qs : 0)];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int rho = 4 * t + (lane >> 4);
+        const int pr_row = __shfl(pr_n, rho);
+        const int qrow_r = wave * 32 + rho;
+        const uint16_t* qp = q + ((w0 + (pr_row >> 5)) * H_q + r * G + qrow_r % G) * kDh + (lane & 15) * 8;
+        qraw[t] = *reinterpret_cast<const u32x4_t*>(qp);
+      }
+
+      // O^T[d][qrow] = V^T[d][key] * P^T[key][qrow]; lane (l32, h) reads the 8-key
+      // chunk 4*(u/2) + 2*(u%2) + h of row d = 32*dt + l32.
       f32x16_t oacc[4];
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x16_t{};
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         asm volatile("" ::: "memory");  // issue this step's V^T reads just in time
-        const int kt = u >> 1, hf = u & 1;
-        const int key0 = kt * 32 + 16 * hf + 4 * h;
+        const int kc = 2 * u + h;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          const uint8_t* vrow = Vt + (dt * 32 + l32) * kVtStride;
-          const uint2 v0 = *reinterpret_cast<const uint2*>(vrow + key0 * 2);
-          const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + (key0 + 8) * 2);
-          oacc[dt] = mfma_32x32x16(as_bf16x8(make_uint4(v0.x, v0.y, v1.x, v1.y)), as_bf16x8(pb[u]), oacc[dt]);
+          const int d = dt * 32 + l32;
+          const u32x4_t va = *reinterpret_cast<const u32x4_t*>(Vt + d * 256 + ((kc ^ (d & 15)) << 4));
+          oacc[dt] = mfma_32x32x16(as_bf16x8(va), as_bf16x8(pb[u]), oacc[dt]);
         }
       }
 
-      if (valid) {
-        const float inv_l = l > 0.f ? 1.f / l : 0.f;
-        const int64_t prow = ((i_local * H_kv + r) * kk + s) * G + g;
-        uint16_t* op = Opart + prow * kDh;
+      // Unnormalised partial (bf16) plus its base-2 max and sum for the combine.
+      // The O^T tile leaves the MFMA with each row split over two lanes; it goes
+      // through a wave-private LDS buffer (two passes of 16 rows, 16-byte chunk c of
+      // row rho at position c ^ rho) so that every store instruction writes four
+      // whole 256-byte partial rows.
+      const int64_t prow = ((i_local * H_kv + r) * kk + s) * G + g;
+      if (valid && h == 0) Lpart[prow] = make_float2(empty ? -__builtin_inff() : m2, l);
+      u32x2_t opk[16];
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
+      for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const int d0 = dt * 32 + 8 * c + 4 * h;
-            uint2 pk;
-            pk.x = pack_bf16x2(oacc[dt][4 * c + 0] * inv_l, oacc[dt][4 * c + 1] * inv_l);
-            pk.y = pack_bf16x2(oacc[dt][4 * c + 2] * inv_l, oacc[dt][4 * c + 3] * inv_l);
-            *reinterpret_cast<uint2*>(op + d0) = pk;
+        for (int c = 0; c < 4; ++c) {
+          opk[4 * dt + c].x = pack_bf16x2(oacc[dt][4 * c + 0], oacc[dt][4 * c + 1]);
+          opk[4 * dt + c].y = pack_bf16x2(oacc[dt][4 * c + 2], oacc[dt][4 * c + 3]);
+        }
+      }
+#pragma unroll
+      for (int pass = 0; pass < 2; ++pass) {
+        if ((l32 >> 4) == pass) {
+          const int rho = l32 & 15;
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            *reinterpret_cast<u32x2_t*>(ost + rho * 256 + ((j ^ rho) << 4) + 8 * h) = opk[j];
+        }
+        // Row rho of this pass is qrow wave*32 + 16*pass + rho; lane -> (row, chunk).
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int rho = 4 * u + (lane >> 4), ch = lane & 15;
+          const u32x4_t val = *reinterpret_cast<const u32x4_t*>(ost + rho * 256 + ((ch ^ rho) << 4));
+          const int src = 16 * pass + rho;                 // l32 of the row's owner
+          const int pr_row = __shfl(pr, src);
+          const int qs_row = (wave * 32 + src) / G, g_row = (wave * 32 + src) % G;
+          if (cb + qs_row < cnt) {
+            const int64_t prow_r = ((((int64_t)(pr_row >> 5)) * H_kv + r) * kk + (pr_row & 31)) * G + g_row;
+            *reinterpret_cast<u32x4_t*>(Opart + prow_r * kDh + ch * 8) = val;
           }
         }
-        if (h == 0) Lpart[prow] = l > 0.f ? (mx + __log2f(l)) * kLn2 : -__builtin_inff();
       }
+      pr = pr_n;
     }
   }
 }
 
 // --------------------------------------------------------------------- phase 2
-// One wave per (query, head): LSE merge of the valid slots' normalised partials.
+// LSE merge of the valid slots' normalised partials.  One wave per (query, group,
+// run of GW heads): lane -> (head, run of 2*GW dims); all slots' loads are issued
+// before any arithmetic so that a wave keeps 16 x (4*GW) bytes per lane in flight.
+template <int G, int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ Opart,
-                                                      const float* __restrict__ Lpart,
+                                                      const float2* __restrict__ Lpart,
                                                       const int32_t* __restrict__ block_idx, int64_t w0,
-                                                      int64_t W, int H_kv, int G, int kk, int64_t B,
+                                                      int64_t W, int H_kv, int kk, int64_t B,
                                                       float* __restrict__ o, float* __restrict__ lse) {
+  constexpr int GW = G < 32 ? G : 32;       // heads per wave
+  constexpr int LPH = 64 / GW;               // lanes per head
+  constexpr int DPL = kDh / LPH;             // dims per lane (2*GW)
+  constexpr int HPW = G / GW;                // waves per (query, group)
   const int lane = threadIdx.x & 63;
   const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int H_q = H_kv * G;
-  if (gw >= W * H_q) return;
-  const int64_t i_local = gw / H_q;
-  const int hh = (int)(gw % H_q);
-  const int r = hh / G, g = hh % G;
+  if (gw >= W * H_kv * HPW) return;
+  const int hw = (int)(gw % HPW);
+  const int64_t ir = gw / HPW;               // (i_local, r)
+  const int64_t i_local = ir / H_kv;
+  const int r = (int)(ir % H_kv);
   const int64_t i = w0 + i_local;
+  const int g = hw * GW + lane / LPH;
+  const int d0 = (lane % LPH) * DPL;
+  const int H_q = H_kv * G;
   const int32_t* sel = block_idx + (i * H_kv + r) * kk;
-  const int64_t pbase = (i_local * H_kv + r) * kk;
+  const int64_t pbase = ir * kk;             // partial row of slot 0 (times G)
 
-  float mstar = -__builtin_inff();
-  for (int s = 0; s < kk; ++s) {
-    if (pair_valid(sel[s], i, B)) mstar = fmaxf(mstar, Lpart[(pbase + s) * G + g]);
+  // Slot s: unnormalised partial o_s with base-2 max m_s and sum l_s;
+  // o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, lse = (M + log2 L) ln 2.
+  // Slot validity is the same for the whole wave.  Invalid slots re-read the first
+  // valid slot's row with weight 0, so every slot's load can be in flight at once.
+  bool valid[KMAX];
+  int first = -1;
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s) {
+    valid[s] = s < kk && pair_valid(sel[s < kk ? s : 0], i, B);
+    if (valid[s] && first < 0) first = s;
   }
-  float* orow = o + (i * H_q + hh) * kDh;
-  if (mstar == -__builtin_inff()) {
-    *reinterpret_cast<float2*>(orow + 2 * lane) = make_float2(0.f, 0.f);
-    if (lane == 0) lse[i * H_q + hh] = -__builtin_inff();
+  float* orow = o + (i * H_q + r * G + g) * kDh + d0;
+  if (first < 0) {
+#pragma unroll
+    for (int d = 0; d < DPL; ++d) orow[d] = 0.f;
+    if (lane % LPH == 0) lse[i * H_q + r * G + g] = -__builtin_inff();
     return;
   }
-  float a0 = 0.f, a1 = 0.f, L = 0.f;
-  for (int s = 0; s < kk; ++s) {
-    if (!pair_valid(sel[s], i, B)) continue;
-    const int64_t prow = (pbase + s) * G + g;
-    const float ls = Lpart[prow];
-    if (ls == -__builtin_inff()) continue;
-    const float wgt = __expf(ls - mstar);
-    const uint32_t pv = *reinterpret_cast<const uint32_t*>(Opart + prow * kDh + 2 * lane);
-    a0 += wgt * __uint_as_float(pv << 16);
-    a1 += wgt * __uint_as_float(pv & 0xffff0000u);
-    L += wgt;
+  float ms[KMAX], ls[KMAX];
+  float mstar = -__builtin_inff();
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s) {
+    const float2 ml = Lpart[(pbase + (valid[s] ? s : first)) * G + g];
+    ms[s] = valid[s] ? ml.x : -__builtin_inff();
+    ls[s] = ml.y;
+    mstar = fmaxf(mstar, ms[s]);
+  }
+  float acc[DPL];
+#pragma unroll
+  for (int d = 0; d < DPL; ++d) acc[d] = 0.f;
+  float L = 0.f;
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s) {
+    const float wgt = valid[s] ? __builtin_amdgcn_exp2f(ms[s] - mstar) : 0.f;
+    L += wgt * ls[s];
+    const uint16_t* src = Opart + ((pbase + (valid[s] ? s : first)) * G + g) * kDh + d0;
+    // DPL bf16 values = DPL/2 dwords, read with the widest aligned vector.
+    uint32_t w[DPL / 2];
+    if constexpr (DPL >= 8) {
+#pragma unroll
+      for (int d = 0; d < DPL; d += 8) {
+        const uint4 u = *reinterpret_cast<const uint4*>(src + d);
+        w[d / 2] = u.x;
+        w[d / 2 + 1] = u.y;
+        w[d / 2 + 2] = u.z;
+        w[d / 2 + 3] = u.w;
+      }
+    } else if constexpr (DPL == 4) {
+      const uint2 u = *reinterpret_cast<const uint2*>(src);
+      w[0] = u.x;
+      w[1] = u.y;
+    } else {
+      w[0] = *reinterpret_cast<const uint32_t*>(src);
+    }
+#pragma unroll
+    for (int m = 0; m < DPL / 2; ++m) {
+      acc[2 * m] += wgt * __uint_as_float(w[m] << 16);
+      acc[2 * m + 1] += wgt * __uint_as_float(w[m] & 0xffff0000u);
+    }
   }
   const float invL = 1.f / L;
-  *reinterpret_cast<float2*>(orow + 2 * lane) = make_float2(a0 * invL, a1 * invL);
-  if (lane == 0) lse[i * H_q + hh] = mstar + __logf(L);
+  if constexpr (DPL >= 4) {
+#pragma unroll
+    for (int d = 0; d < DPL; d += 4)
+      *reinterpret_cast<float4*>(orow + d) =
+          make_float4(acc[d] * invL, acc[d + 1] * invL, acc[d + 2] * invL, acc[d + 3] * invL);
+  } else {
+    *reinterpret_cast<float2*>(orow) = make_float2(acc[0] * invL, acc[1] * invL);
+  }
+  if (lane % LPH == 0) lse[i * H_q + r * G + g] = (mstar + __log2f(L)) * kLn2;
 }
 
 __global__ void fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t val) {
@@ -415,7 +546,7 @@ AttnWorkspace attn_workspace_layout(int64_t W, int H_q, int H_kv, int kk, int64_
   L.items = take(sizeof(int4) * max_items);
   L.pairs = take(sizeof(int32_t) * max_pairs);
   L.opart = take(sizeof(uint16_t) * max_pairs * G * kDh);
-  L.lpart = take(sizeof(float) * max_pairs * G);
+  L.lpart = take(sizeof(float2) * max_pairs * G);
   L.total = off;
   L.max_items = max_items;
   L.item_q = item_q;
@@ -435,7 +566,7 @@ hipError_t launch_sparse_attn_window(const uint16_t* q, const uint16_t* k, const
   int4* items = reinterpret_cast<int4*>(ws + L.items);
   int32_t* pairs = reinterpret_cast<int32_t*>(ws + L.pairs);
   uint16_t* opart = reinterpret_cast<uint16_t*>(ws + L.opart);
-  float* lpart = reinterpret_cast<float*>(ws + L.lpart);
+  float2* lpart = reinterpret_cast<float2*>(ws + L.lpart);
 
   fill_i32_kernel<<<dim3(256), dim3(256), 0, stream>>>(counts, lists, 0);
   hipError_t e = hipGetLastError();
@@ -477,9 +608,28 @@ hipError_t launch_sparse_attn_window(const uint16_t* q, const uint16_t* k, const
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
-  const int64_t waves = W * H_q;
-  combine_kernel<<<dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream>>>(opart, lpart, block_idx, w0, W,
-                                                                               H_kv, G, kk, B, o, lse);
+  const int64_t waves = W * H_kv * (G > 32 ? G / 32 : 1);
+  const dim3 cgrid((unsigned)((waves + 3) / 4));
+  switch (G) {
+#define MSA_COMBINE_CASE(GG)                                                                          \
+  case GG:                                                                                           \
+    if (kk <= 16)                                                                                    \
+      combine_kernel<GG, 16><<<cgrid, dim3(256), 0, stream>>>(opart, lpart, block_idx, w0, W, H_kv, kk, B, o, lse); \
+    else                                                                                             \
+      combine_kernel<GG, 32><<<cgrid, dim3(256), 0, stream>>>(opart, lpart, block_idx, w0, W, H_kv, kk, B, o, lse); \
+    break;
+    MSA_COMBINE_CASE(1)
+    MSA_COMBINE_CASE(2)
+    MSA_COMBINE_CASE(4)
+    MSA_COMBINE_CASE(8)
+    MSA_COMBINE_CASE(16)
+    MSA_COMBINE_CASE(32)
+    MSA_COMBINE_CASE(64)
+    MSA_COMBINE_CASE(128)
+#undef MSA_COMBINE_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
