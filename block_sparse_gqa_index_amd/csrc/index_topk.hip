@@ -50,38 +50,55 @@ __device__ __forceinline__ void idx_store_block(uint8_t* buf, int tid, const uin
 
 // Block maxima of one staged key block for the lane's CT column tiles (raw dot
 // products; the 1/sqrt(d_idx) scale is applied by the caller when needed).
+// The 4 x CT output tiles are software-pipelined over two accumulators: the four
+// MFMAs of tile j+1 are issued before tile j is max-reduced, so the VALU reduction
+// of one tile runs under the matrix work of the next.
+template <int CT>
+__device__ __forceinline__ void idx_tile_reduce(const f32x16_t& acc, int64_t qi, int64_t b, int kt, bool need_mask,
+                                                int h, float& bmax) {
+  if (need_mask) {
+    // key b*128 + kt*32 + 8*(v/4) + 4h + v%4 is visible iff its offset <= lim
+    int64_t lim64 = qi - (b * kBk + kt * 32 + 4 * h);
+    lim64 = lim64 < -1 ? -1 : (lim64 > 64 ? 64 : lim64);
+    const int lim = (int)lim64;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) bmax = fmaxf(bmax, (8 * (v >> 2) + (v & 3)) <= lim ? acc[v] : -__builtin_inff());
+  } else {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) bmax = fmaxf(bmax, acc[v]);
+  }
+}
+
 template <int CT>
 __device__ __forceinline__ void idx_block_max(const uint8_t* buf, const uint4 (&qop)[CT][4], const int64_t (&qi)[CT],
                                               int64_t b, bool need_mask, int h, int l32, float (&bmax)[CT]) {
+  constexpr int kTiles = 4 * CT;
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) bmax[ct] = -__builtin_inff();
+  u32x4_t a[4];
+  f32x16_t acc[2];
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-    const int key = kt * 32 + l32;
-    uint4 a[4];
+  for (int j = 0; j < kTiles; ++j) {
+    const int kt = j / CT, ct = j % CT;
+    if (ct == 0) {
+      const int key = kt * 32 + l32;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int c = ks * 2 + h;
-      a[ks] = *reinterpret_cast<const uint4*>(buf + key * 128 + ((c ^ ((key >> 1) & 7)) << 4));
-    }
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      f32x16_t acc = {};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) acc = mfma_32x32x16(as_bf16x8(a[ks]), as_bf16x8(qop[ct][ks]), acc);
-      if (need_mask) {
-        // key b*128 + kt*32 + 8*(v/4) + 4h + v%4 is visible iff its offset <= lim
-        int64_t lim64 = qi[ct] - (b * kBk + kt * 32 + 4 * h);
-        lim64 = lim64 < -1 ? -1 : (lim64 > 64 ? 64 : lim64);
-        const int lim = (int)lim64;
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-          bmax[ct] = fmaxf(bmax[ct], (8 * (v >> 2) + (v & 3)) <= lim ? acc[v] : -__builtin_inff());
-      } else {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) bmax[ct] = fmaxf(bmax[ct], acc[v]);
+      for (int ks = 0; ks < 4; ++ks) {
+        const int c = ks * 2 + h;
+        a[ks] = *reinterpret_cast<const u32x4_t*>(buf + key * 128 + ((c ^ ((key >> 1) & 7)) << 4));
       }
     }
+    acc[j & 1] = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) acc[j & 1] = mfma_32x32x16(as_bf16x8(a[ks]), as_bf16x8(qop[ct][ks]), acc[j & 1]);
+    if (j > 0) {
+      const int pj = j - 1, pkt = pj / CT, pct = pj % CT;
+      idx_tile_reduce<CT>(acc[pj & 1], qi[pct], b, pkt, need_mask, h, bmax[pct]);
+    }
+  }
+  {
+    constexpr int pj = kTiles - 1, pkt = pj / CT, pct = pj % CT;
+    idx_tile_reduce<CT>(acc[pj & 1], qi[pct], b, pkt, need_mask, h, bmax[pct]);
   }
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) bmax[ct] = fmaxf(bmax[ct], __shfl_xor(bmax[ct], 32));

@@ -35,7 +35,7 @@ bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 constexpr int64_t kMaxN = (int64_t)1 << 24;
 constexpr int64_t kMaxBlocks = 8192;  // inverse-index passes keep 2 x B counters in LDS
 // Default cap on the KV-outer partial buffers; larger inputs run in query windows.
-constexpr size_t kDefaultAttnWorkspace = (size_t)8 << 30;
+constexpr size_t kDefaultAttnWorkspace = (size_t)40 << 30;
 
 msa_status_t check_common(int64_t N, int d, int expect_d, const char* dname, int B_k, int k) {
   if (N < 0) return fail(MSA_ERR_INVALID_ARG, "N must be >= 0 (got %lld)", (long long)N);

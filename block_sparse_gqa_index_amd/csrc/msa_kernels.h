@@ -13,12 +13,14 @@ constexpr int kIndexDim = 64;
 constexpr int kBlockKeys = 128;
 
 // Chunks (of 128 MFMA rows) per work item of the KV-outer kernel.
-constexpr int kItemChunks = 4;
+constexpr int kItemChunks = 8;
 
 struct AttnWorkspace {
   size_t counts, cursor, n_items, items, pairs, opart, lpart, total;
   int64_t max_items;
   int item_q;  // queries per work item
+  int64_t WQ;  // queries per q-locality window
+  int nW;      // q-locality windows per call window
 };
 
 struct DecodeWorkspace {

@@ -30,12 +30,17 @@ __device__ __forceinline__ bool pair_valid(int b, int64_t i, int64_t B) {
   return b >= 0 && (int64_t)b < B && (int64_t)b <= i / kBk;
 }
 
+// Lists are keyed (group r, query window w, block b): list (r * nW + w) * B + b holds
+// the pairs of queries in window w (WQ queries) that chose block b for group r.
+// Processing lists in key order keeps the q rows being gathered (one window of one
+// group) and the K/V blocks being staged (one group) small enough to stay cached.
 __global__ __launch_bounds__(256) void inv_count_kernel(const int32_t* __restrict__ block_idx, int64_t w0,
                                                         int64_t W, int H_kv, int kk, int64_t B, int TQ,
-                                                        int32_t* __restrict__ counts) {
+                                                        int64_t WQ, int nW, int32_t* __restrict__ counts) {
   extern __shared__ int32_t hist[];
   const int r = blockIdx.y;
   const int64_t q0 = w0 + (int64_t)blockIdx.x * TQ;
+  const int64_t lbase = ((int64_t)r * nW + (q0 - w0) / WQ) * B;
   const int64_t q1 = (q0 + TQ < w0 + W) ? q0 + TQ : w0 + W;
   const int64_t bmax = ((q1 - 1) / kBk < B - 1) ? (q1 - 1) / kBk : B - 1;
   for (int64_t b = threadIdx.x; b <= bmax; b += 256) hist[b] = 0;
@@ -50,7 +55,7 @@ __global__ __launch_bounds__(256) void inv_count_kernel(const int32_t* __restric
   __syncthreads();
   for (int64_t b = threadIdx.x; b <= bmax; b += 256) {
     const int c = hist[b];
-    if (c) atomicAdd(&counts[r * B + b], c);
+    if (c) atomicAdd(&counts[lbase + b], c);
   }
 }
 
@@ -102,13 +107,14 @@ __global__ __launch_bounds__(1024) void inv_scan_kernel(const int32_t* __restric
 template <int PPT>
 __global__ __launch_bounds__(256) void inv_scatter_kernel(const int32_t* __restrict__ block_idx, int64_t w0,
                                                           int64_t W, int H_kv, int kk, int64_t B, int TQ,
-                                                          int32_t* __restrict__ cursor,
+                                                          int64_t WQ, int nW, int32_t* __restrict__ cursor,
                                                           int32_t* __restrict__ pairs) {
   extern __shared__ int32_t sh[];
   int32_t* hist = sh;
   int32_t* base = sh + B;
   const int r = blockIdx.y;
   const int64_t q0 = w0 + (int64_t)blockIdx.x * TQ;
+  const int64_t lbase = ((int64_t)r * nW + (q0 - w0) / WQ) * B;
   const int64_t q1 = (q0 + TQ < w0 + W) ? q0 + TQ : w0 + W;
   const int64_t bmax = ((q1 - 1) / kBk < B - 1) ? (q1 - 1) / kBk : B - 1;
   for (int64_t b = threadIdx.x; b <= bmax; b += 256) hist[b] = 0;
@@ -129,7 +135,7 @@ __global__ __launch_bounds__(256) void inv_scatter_kernel(const int32_t* __restr
   __syncthreads();
   for (int64_t b = threadIdx.x; b <= bmax; b += 256) {
     const int c = hist[b];
-    if (c) base[b] = atomicAdd(&cursor[r * B + b], c);
+    if (c) base[b] = atomicAdd(&cursor[lbase + b], c);
   }
   __syncthreads();
 #pragma unroll
@@ -145,6 +151,12 @@ __global__ __launch_bounds__(256) void inv_scatter_kernel(const int32_t* __restr
 
 // --------------------------------------------------------------------- phase 1
 constexpr int kAttnThreads = 256;
+
+__device__ __forceinline__ const uint8_t* shfl_ptr(const uint8_t* p, int src) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __shfl((uint32_t)v, src), hi = __shfl((uint32_t)(v >> 32), src);
+  return reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
+}
 
 // LDS row rho of the staged K tile holds key swap23(rho) (bits 2 and 3 of the row
 // index exchanged).  With that order the 32x32 MFMA leaves, in each lane half, the
@@ -200,7 +212,7 @@ template <int G>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
     const int4* __restrict__ items, const int32_t* __restrict__ n_items_ptr, const int32_t* __restrict__ pairs,
-    int64_t N, int H_kv, int64_t B, int kk, int64_t w0, float scale_log2, uint16_t* __restrict__ Opart,
+    int64_t N, int H_kv, int64_t B, int nW, int kk, int64_t w0, float scale_log2, uint16_t* __restrict__ Opart,
     float2* __restrict__ Lpart) {
   constexpr int kQC = 128 / G;         // gathered queries per chunk
   __shared__ __attribute__((aligned(16))) uint8_t Ks[kBk * 256];
@@ -222,7 +234,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
     const int64_t item = round * grid + (int64_t)xcd * per_xcd + slot_in_xcd;
     if (item >= n_items) break;
     const int4 it = items[item];
-    const int64_t r = it.x / B, b = it.x % B;
+    const int64_t b = it.x % B, r = (it.x / B) / nW;
     const int start = it.y, cnt = it.z;
 
     __syncthreads();  // previous item's LDS reads are done
@@ -251,15 +263,17 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
     // through the wave's LDS buffer, 16 rows per pass, chunk c of row rho at
     // position c ^ rho.
     uint8_t* ost = Ostage[wave];
+    // Byte address of this lane's q row for pair pr (query w0 + pr/32, head r*G + g).
+    auto q_row = [&](int prv) {
+      return reinterpret_cast<const uint8_t*>(q + ((w0 + (prv >> 5)) * H_q + r * G + g) * kDh);
+    };
     int pr = pairs[start + (qs < cnt ? qs : 0)];
     u32x4_t qraw[8];
+    {
+      const uint8_t* qa = q_row(pr);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int rho = 4 * t + (lane >> 4);
-      const int pr_row = __shfl(pr, rho);
-      const int qrow_r = wave * 32 + rho;
-      const uint16_t* qp = q + ((w0 + (pr_row >> 5)) * H_q + r * G + qrow_r % G) * kDh + (lane & 15) * 8;
-      qraw[t] = *reinterpret_cast<const u32x4_t*>(qp);
+      for (int t = 0; t < 8; ++t)
+        qraw[t] = *reinterpret_cast<const u32x4_t*>(shfl_ptr(qa, 4 * t + (lane >> 4)) + (lane & 15) * 16);
     }
     for (int cb = 0; cb < cnt; cb += kQC) {
       // Keep the LDS operand reads inside the chunk loop: hoisting them (they do
@@ -280,6 +294,17 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
             qop[t] = *reinterpret_cast<const u32x4_t*>(ost + rho * 256 + (((8 * h + t) ^ rho) << 4));
         }
       }
+      // Prefetch the next chunk's pair and q rows while this chunk finishes.
+      // (After the item's last chunk this re-reads the item's first pair: a valid
+      // address, and it keeps the current q registers dead after the MFMAs.)
+      const int pr_n = pairs[start + (cb + kQC + qs < cnt ? cb + kQC + qs : 0)];
+      {
+        const uint8_t* qa = q_row(pr_n);
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          qraw[t] = *reinterpret_cast<const u32x4_t*>(shfl_ptr(qa, 4 * t + (lane >> 4)) + (lane & 15) * 16);
+      }
+
       const bool valid = cb + qs < cnt;
       const int64_t i_local = pr >> 5;
       const int s = pr & 31;
@@ -347,19 +372,6 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
         pb[u].w = pack_bf16x2(sacc[kt][8 * hf + 6], sacc[kt][8 * hf + 7]);
       }
 
-      // Prefetch the next chunk's pair and q rows while this chunk finishes.
-      // (After the item's last chunk this re-reads the item's first pair: a valid
-      // address, and it keeps the current q registers dead after the MFMAs.)
-      const int pr_n = pairs[start + (cb + kQC + qs < cnt ? cb + kQC + qs : 0)];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int rho = 4 * t + (lane >> 4);
-        const int pr_row = __shfl(pr_n, rho);
-        const int qrow_r = wave * 32 + rho;
-        const uint16_t* qp = q + ((w0 + (pr_row >> 5)) * H_q + r * G + qrow_r % G) * kDh + (lane & 15) * 8;
-        qraw[t] = *reinterpret_cast<const u32x4_t*>(qp);
-      }
-
       // O^T[d][qrow] = V^T[d][key] * P^T[key][qrow]; lane (l32, h) reads the 8-key
       // chunk 4*(u/2) + 2*(u%2) + h of row d = 32*dt + l32.
       f32x16_t oacc[4];
@@ -384,6 +396,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
       // whole 256-byte partial rows.
       const int64_t prow = ((i_local * H_kv + r) * kk + s) * G + g;
       if (valid && h == 0) Lpart[prow] = make_float2(empty ? -__builtin_inff() : m2, l);
+      const uint8_t* prow_addr = reinterpret_cast<const uint8_t*>(Opart + prow * kDh);
       u32x2_t opk[16];
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
@@ -406,13 +419,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
         for (int u = 0; u < 4; ++u) {
           const int rho = 4 * u + (lane >> 4), ch = lane & 15;
           const u32x4_t val = *reinterpret_cast<const u32x4_t*>(ost + rho * 256 + ((ch ^ rho) << 4));
-          const int src = 16 * pass + rho;                 // l32 of the row's owner
-          const int pr_row = __shfl(pr, src);
-          const int qs_row = (wave * 32 + src) / G, g_row = (wave * 32 + src) % G;
-          if (cb + qs_row < cnt) {
-            const int64_t prow_r = ((((int64_t)(pr_row >> 5)) * H_kv + r) * kk + (pr_row & 31)) * G + g_row;
-            *reinterpret_cast<u32x4_t*>(Opart + prow_r * kDh + ch * 8) = val;
-          }
+          const int src = 16 * pass + rho;  // l32 of the row's owner
+          const uint8_t* dst = shfl_ptr(prow_addr, src);
+          if (__shfl((int)valid, src)) *reinterpret_cast<u32x4_t*>(const_cast<uint8_t*>(dst) + ch * 16) = val;
         }
       }
       pr = pr_n;
@@ -527,9 +536,22 @@ __global__ void fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t val)
 
 }  // namespace
 
+// Query tile of the inverse-index passes: a power of two with at most 4096 pairs.
+static int inv_tile_queries(int kk) {
+  int tq = 1;
+  while (tq * 2 * kk <= 4096) tq *= 2;
+  return tq;
+}
+
 AttnWorkspace attn_workspace_layout(int64_t W, int H_q, int H_kv, int kk, int64_t B) {
   AttnWorkspace L{};
-  const int64_t lists = (int64_t)H_kv * B;
+  // q-locality window: about 128 pairs per (group, window, block) list on average,
+  // a multiple of 4096 queries (so every inverse-index tile lies in one window).
+  int64_t WQ = ((8 * B + 4095) / 4096) * 4096;
+  if (WQ > W) WQ = ((W + 4095) / 4096) * 4096;
+  L.WQ = WQ;
+  L.nW = (int)((W + WQ - 1) / WQ);
+  const int64_t lists = (int64_t)H_kv * L.nW * B;
   const int64_t max_pairs = W * H_kv * kk;
   const int G = H_q / H_kv;
   const int item_q = kItemChunks * (128 / G);
@@ -558,7 +580,7 @@ hipError_t launch_sparse_attn_window(const uint16_t* q, const uint16_t* k, const
                                      float scale, int64_t w0, int64_t W, int num_cus, float* o, float* lse,
                                      uint8_t* ws, const AttnWorkspace& L, hipStream_t stream) {
   const int64_t B = (N + kBk - 1) / kBk;
-  const int64_t lists = (int64_t)H_kv * B;
+  const int64_t lists = (int64_t)H_kv * L.nW * B;
   const int G = H_q / H_kv;
   int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
   int32_t* cursor = reinterpret_cast<int32_t*>(ws + L.cursor);
@@ -572,16 +594,17 @@ hipError_t launch_sparse_attn_window(const uint16_t* q, const uint16_t* k, const
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  // Query tiles of the inverse-index passes hold 4096 pairs (16 per thread).
-  const int TQ = 4096 / kk > 0 ? 4096 / kk : 1;
+  // Query tiles of the inverse-index passes hold at most 4096 pairs (16 per thread).
+  const int TQ = inv_tile_queries(kk);
   const dim3 igrid((unsigned)((W + TQ - 1) / TQ), (unsigned)H_kv);
   const size_t lds_count = sizeof(int32_t) * B;
-  inv_count_kernel<<<igrid, dim3(256), lds_count, stream>>>(block_idx, w0, W, H_kv, kk, B, TQ, counts);
+  inv_count_kernel<<<igrid, dim3(256), lds_count, stream>>>(block_idx, w0, W, H_kv, kk, B, TQ, L.WQ, L.nW,
+                                                             counts);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   inv_scan_kernel<<<dim3(1), dim3(1024), 0, stream>>>(counts, lists, L.item_q, cursor, items, n_items);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  inv_scatter_kernel<16><<<igrid, dim3(256), 2 * lds_count, stream>>>(block_idx, w0, W, H_kv, kk, B, TQ,
-                                                                      cursor, pairs);
+  inv_scatter_kernel<16><<<igrid, dim3(256), 2 * lds_count, stream>>>(block_idx, w0, W, H_kv, kk, B, TQ, L.WQ,
+                                                                      L.nW, cursor, pairs);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
   int64_t grid = (int64_t)num_cus * 2;
@@ -592,7 +615,7 @@ hipError_t launch_sparse_attn_window(const uint16_t* q, const uint16_t* k, const
 #define MSA_ATTN_CASE(GG)                                                                            \
   case GG:                                                                                           \
     attn_kvouter_kernel<GG><<<dim3((unsigned)grid), dim3(kAttnThreads), 0, stream>>>(                \
-        q, k, v, items, n_items, pairs, N, H_kv, B, kk, w0, scale_log2, opart, lpart);               \
+        q, k, v, items, n_items, pairs, N, H_kv, B, L.nW, kk, w0, scale_log2, opart, lpart);         \
     break;
     MSA_ATTN_CASE(1)
     MSA_ATTN_CASE(2)

@@ -93,7 +93,7 @@ def test_workspace_sizes(lib):
     assert raw.msa_index_topk_workspace(131072, 8, 64, 128, 16) == 0
     full = raw.msa_sparse_attn_fwd_workspace(131072, 64, 8, 128, 128, 16)
     small = raw.msa_sparse_attn_fwd_workspace_min(131072, 64, 8, 128, 128, 16)
-    assert 0 < small < full <= (8 << 30)
+    assert 0 < small < full <= (40 << 30)
     # one query window of 128 queries: partial rows of 128 bf16 + one fp32 lse each
     assert small >= 128 * 64 * 16 * (128 * 2 + 4)
     assert raw.msa_sparse_attn_fwd_workspace(131072, 64, 8, 64, 128, 16) == 0  # unsupported d_h
