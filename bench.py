@@ -7,7 +7,10 @@ A prefill step is one pass of the whole prefill path over the 128K workload
 msa_index_topk (index scoring, causal max-pool, Top-k) then msa_sparse_attn_fwd
 (inverse index, KV-outer attention, LSE combine).  A decode step is msa_decode for
 64 sequences with 128K-token caches.  Inputs are synthetic (seeded, resident in
-HBM before timing starts).  One JSON line is printed.
+HBM before timing starts); the headline figures use one input mode and the other
+mode is reported beside them.  One JSON line is printed, with the roofline of the
+dominant kernel (KV-outer phase 1, timed by events the library records around it)
+and the CPU oracle timed on a sample of query rows.
 
 FLOP accounting (exact, from the work the method must do): index
 d_idx * H_kv * N (N + 1) (every causal (query, key) pair per group, 2 FLOP per
@@ -53,19 +56,268 @@ def attended_pairs(block_idx, B_k: int, G: int) -> int:
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+# Sources the KV-outer kernel is compiled from: a recorded traffic figure holds only
+# while their hash is unchanged.
+ATTN_SOURCES = ("block_sparse_gqa_index_amd/csrc/sparse_attn.hip", "block_sparse_gqa_index_amd/csrc/msa_device.h",
+                "block_sparse_gqa_index_amd/csrc/msa_kernels.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kvouter_kernel_128k_traffic.txt")
+
+
+def attn_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(mode: str):
+    """HBM bytes per launch of the KV-outer kernel from the committed counter summary,
+    or None when the kernel's sources changed since the counters were taken."""
+    try:
+        rec = {}
+        with open(TRAFFIC_FILE) as fh:
+            for line in fh:
+                if ":" in line and not line.startswith("#"):
+                    key, val = line.split(":", 1)
+                    rec[key.strip()] = val.strip()
+        if rec.get("source_sha256") != attn_source_hash() or rec.get("mode") != mode:
+            return None
+        return int(float(rec["hbm_bytes_per_launch"]))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def write_traffic_summary(fetch_csv: str, write_csv: str, mode: str, command: str) -> str:
+    """Turn two rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) into
+    HBM bytes per launch of the KV-outer kernel, each counter scaled by what it reads
+    for the calibration copies of COPY_BYTES made at the start of the profiled run."""
+    import csv
+    per = {}
+    for path, counter in ((fetch_csv, "FETCH_SIZE"), (write_csv, "WRITE_SIZE")):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]][:COPY_REPS]
+        attn = [float(r["Counter_Value"]) for r in rows if "attn_kvouter_kernel" in r["Kernel_Name"]]
+        if len(copies) < COPY_REPS or not attn:
+            raise SystemExit(f"{path}: calibration copies or KV-outer dispatches missing")
+        kib_copy = sum(copies) / len(copies)
+        factor = COPY_BYTES / (kib_copy * 1024.0)
+        kib = sum(attn) / len(attn)
+        per[counter] = (kib, kib_copy, factor, kib * 1024.0 * factor, len(attn))
+    total = per["FETCH_SIZE"][3] + per["WRITE_SIZE"][3]
+    lines = [
+        "# HBM traffic of attn_kvouter_kernel<8> (KV-outer phase 1), 128K prefill",
+        "# (N=131072 H_q=64 H_kv=8 d_h=128 B_k=128 k=16), one launch per step.",
+        "# Counters in KiB per dispatch; each scaled by the ratio of the true size of a",
+        f"# plain device copy ({COPY_BYTES} bytes read and written) to what the counter reads for it.",
+        f"# command: {command}",
+        f"kernel: attn_kvouter_kernel",
+        f"mode: {mode}",
+        f"source_sha256: {attn_source_hash()}",
+    ]
+    for c, (kib, kib_copy, factor, b, n) in per.items():
+        lines += [f"{c.lower()}_kib_per_dispatch: {kib:.1f}", f"{c.lower()}_dispatches: {n}",
+                  f"{c.lower()}_copy_kib: {kib_copy:.1f}", f"{c.lower()}_copy_factor: {factor:.4f}",
+                  f"{c.lower()}_bytes_per_launch: {b:.0f}"]
+    lines.append(f"hbm_bytes_per_launch: {total:.0f}")
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return TRAFFIC_FILE
+
+
+COPY_BYTES = 1 << 30
+COPY_REPS = 3
+
+
+def calibration_copies():
+    """Plain device-to-device copies of COPY_BYTES, made before any other GPU work so
+    that a counter run can scale its readings by them."""
+    import torch
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(COPY_REPS):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def run_prefill(msa, synth, cfg, mode, steps, warmup):
+    import torch
+    dev = "cuda"
+    N, H_q, H_kv, k, B_k = cfg.N, cfg.H_q, cfg.H_kv, cfg.k, cfg.B_k
+    G = H_q // H_kv
+    log(f"generating {cfg.name} ({mode}) inputs")
+    inp = synth.make_prefill(cfg, mode, device=dev)
+    block_idx = torch.empty((N, H_kv, k), dtype=torch.int32, device=dev)
+    o = torch.empty((N, H_q, cfg.d_h), dtype=torch.float32, device=dev)
+    lse = torch.empty((N, H_q), dtype=torch.float32, device=dev)
+    ws = torch.empty(msa.msa_sparse_attn_fwd_workspace(N, H_q, H_kv, k), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+            msa.msa_set_profile_events(ev[2:6])
+        msa.msa_index_topk(inp.q_idx, inp.k_idx, k, block_idx=block_idx)
+        if ev is not None:
+            ev[1].record(stream)
+        msa.msa_sparse_attn_fwd(inp.q, inp.k, inp.v, block_idx, o=o, lse=lse, workspace=ws)
+        if ev is not None:
+            msa.msa_set_profile_events(None)
+
+    log(f"prefill {mode}: warmup {warmup}")
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    for e in evs:  # create the event handles before the timed region
+        for x in e:
+            x.record(stream)
+    torch.cuda.synchronize()
+    log(f"prefill {mode}: timed {steps} steps")
+    t0 = time.perf_counter()
+    for s in range(steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    avg = lambda a, b: sum(e[a].elapsed_time(e[b]) for e in evs) / steps
+    t_index, t_attn = avg(0, 1), avg(2, 5)
+    t_inv, t_phase1, t_combine = avg(2, 3), avg(3, 4), avg(4, 5)
+    ms_step = wall * 1e3 / steps
+
+    pairs = attended_pairs(block_idx, B_k, G)
+    f_index = flops_index_exact(N, H_kv, cfg.d_idx)
+    f_main = 4 * cfg.d_h * pairs
+    f_total = f_index + f_main
+    f_eq12 = flops_msa_eq12(N, H_q, H_kv, cfg.d_h, cfg.d_idx, B_k, k)
+    r_off = torch.arange(H_kv, device=dev).view(1, H_kv, 1) * cfg.B
+    ids = (block_idx.to(torch.int64) + r_off)[block_idx >= 0]
+    fan = torch.bincount(ids, minlength=H_kv * cfg.B).view(H_kv, cfg.B)
+    slot_pairs = int((block_idx >= 0).sum().item())     # (query, group, slot) pairs
+    lists = int((fan > 0).sum().item())                  # (group, block) lists with work
+    # KV-outer phase 1, per (query, group, slot) pair: G q rows gathered (bf16), G
+    # unnormalised partial rows written (bf16) and G (max, sum) fp32 pairs; per
+    # (group, block) list: its K and V block (bf16) once.
+    p1_bytes = slot_pairs * G * (cfg.d_h * 2 + cfg.d_h * 2 + 8) + lists * 2 * B_k * cfg.d_h * 2
+    # Combine, per pair: the partial row and (max, sum) read; per (query, head): o and lse written.
+    cb_bytes = slot_pairs * G * (cfg.d_h * 2 + 8) + N * H_q * (cfg.d_h * 4 + 4) + N * H_kv * k * 4
+    res = {
+        "ms_per_step": round(ms_step, 4),
+        "tokens_per_s": round(N / (ms_step / 1e3), 1),
+        "tflops": round(f_total / (ms_step / 1e3) / 1e12, 2),
+        "tflops_eq12_nominal": round(f_eq12 / (ms_step / 1e3) / 1e12, 2),
+        "mfma_peak_frac": round(f_total / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "flop_index": f_index, "flop_main": f_main, "flop_eq12": f_eq12,
+        "ms_index_topk": round(t_index, 4), "ms_sparse_attn_fwd": round(t_attn, 4),
+        "ms_inverse_index": round(t_inv, 4), "ms_kvouter_phase1": round(t_phase1, 4),
+        "ms_combine": round(t_combine, 4),
+        "index_tflops": round(f_index / (t_index / 1e3) / 1e12, 2),
+        "phase1_tflops": round(f_main / (t_phase1 / 1e3) / 1e12, 2),
+        "phase1_algorithmic_bytes": p1_bytes,
+        "combine_GB_s": round(cb_bytes / (t_combine / 1e3) / 1e9, 1),
+        "slot_pairs": slot_pairs, "lists": lists,
+        "block0_fanin_per_group": int(fan[:, 0].float().mean().item()), "max_fanin": int(fan.max().item()),
+        "median_fanin": float(fan.float().median().item()),
+    }
+    del o, lse, ws, block_idx
+    return res, inp
+
+
+def run_decode(msa, synth, dcfg, mode, steps, warmup):
+    import torch
+    dev = "cuda"
+    B_k = dcfg.B_k
+    log(f"generating {dcfg.name} ({mode}) decode inputs")
+    d = synth.make_decode(dcfg, mode, device=dev)
+    max_len = max(d.lengths)
+    dbi = torch.empty((dcfg.batch, dcfg.H_kv, dcfg.k), dtype=torch.int32, device=dev)
+    do = torch.empty((dcfg.batch, dcfg.H_q, dcfg.d_h), dtype=torch.float32, device=dev)
+    dl = torch.empty((dcfg.batch, dcfg.H_q), dtype=torch.float32, device=dev)
+    dws = torch.empty(msa.msa_decode_workspace(dcfg.batch, dcfg.H_q, dcfg.H_kv, dcfg.k, max_len),
+                      dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def decode_step():
+        msa.msa_decode(d.q, d.q_idx, d.k_cache, d.v_cache, d.k_idx_cache, d.cu_seqlens, max_len, dcfg.k,
+                       block_idx=dbi, o=do, lse=dl, workspace=dws)
+
+    for _ in range(warmup):
+        decode_step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        decode_step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dms = e0.elapsed_time(e1) / steps
+    T = int(d.cu_seqlens[-1].item())
+    # every cached index key (d_idx bf16) + K and V of the chosen blocks of every group
+    chosen = int((dbi >= 0).sum().item())
+    dbytes = T * dcfg.d_idx * 2 + chosen * B_k * dcfg.d_h * 2 * 2
+    del d
+    return {
+        "workload": f"decode batch={dcfg.batch} L={min(synth.decode_lengths(dcfg))}..{max_len} H_q={dcfg.H_q} "
+                    f"H_kv={dcfg.H_kv} k={dcfg.k}",
+        "ms_per_step": round(dms, 4), "tokens_per_s": round(dcfg.batch / (dms / 1e3), 1),
+        "algorithmic_bytes": dbytes, "GB_s": round(dbytes / (dms / 1e3) / 1e9, 1),
+        "hbm_peak_frac": round(dbytes / (dms / 1e3) / 1e9 / PEAK_HBM_GBS, 4), "steps": steps,
+    }
+
+
+def cpu_baseline(inp, cfg, n_rows):
+    """The oracle on a uniform sample of query rows of the same prefill (all groups and heads)."""
+    import numpy as np
+    import oracle
+    N, k, B_k = cfg.N, cfg.k, cfg.B_k
+    log(f"cpu baseline: oracle on {n_rows} sampled query rows")
+    g = np.random.default_rng(cfg.seed)
+    rows = np.sort(g.choice(N, size=min(n_rows, N), replace=False))
+    qi_h, ki_h = inp.q_idx.cpu(), inp.k_idx.cpu()
+    q_h, k_h, v_h = inp.q.cpu(), inp.k.cpu(), inp.v.cpu()
+    t0 = time.perf_counter()
+    M = oracle.block_scores(qi_h, ki_h, B_k, rows=rows)
+    bi = oracle.topk(M, k, B_k, rows=rows)
+    oracle.sparse_attn(q_h, k_h, v_h, bi, B_k, rows=rows)
+    tc = time.perf_counter() - t0
+    return {"value": round(len(rows) / tc, 3), "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{len(rows)} uniformly drawn query rows of the same {N}-token prefill (all groups and "
+                      f"heads; index scoring, Top-k and attention), {tc:.1f} s"}
+
 
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--mode", default="literal", choices=["literal", "structured"])
+    ap.add_argument("--mode", default="literal", choices=["literal", "structured"],
+                    help="input mode of the headline figures; the other mode is reported beside them")
     ap.add_argument("--workload", default="c2")
     ap.add_argument("--decode-workload", default="c3_128k")
-    ap.add_argument("--cpu-rows", type=int, default=192, help="query rows in the oracle's timed sample")
+    ap.add_argument("--cpu-rows", type=int, default=4096, help="query rows in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--single-mode", action="store_true", help="skip the second input mode")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="start with plain copies of known size (for counter runs)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the traffic summary from two rocprofv3 counter CSVs and exit")
+    ap.add_argument("--traffic-command", default="", help="the command the counter CSVs came from")
     args = ap.parse_args(argv)
+
+    if args.traffic_from:
+        print(write_traffic_summary(args.traffic_from[0], args.traffic_from[1], args.mode, args.traffic_command))
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the MSA path here has no multi-GPU mode "
@@ -76,69 +328,22 @@ def main(argv=None) -> int:
     import block_sparse_gqa_index_amd as msa
     import synth
 
-    dev = "cuda"
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        calibration_copies()
     cfg = synth.CONFIGS[args.workload]
     N, H_q, H_kv, k, B_k = cfg.N, cfg.H_q, cfg.H_kv, cfg.k, cfg.B_k
-    G = H_q // H_kv
+    other = "structured" if args.mode == "literal" else "literal"
 
-    def log(msg):
-        print(f"[bench] {msg}", file=sys.stderr, flush=True)
-
-    log(f"generating {cfg.name} ({args.mode}) inputs")
-    inp = synth.make_prefill(cfg, args.mode, device=dev)
-    block_idx = torch.empty((N, H_kv, k), dtype=torch.int32, device=dev)
-    o = torch.empty((N, H_q, cfg.d_h), dtype=torch.float32, device=dev)
-    lse = torch.empty((N, H_q), dtype=torch.float32, device=dev)
-    ws = torch.empty(msa.msa_sparse_attn_fwd_workspace(N, H_q, H_kv, k), dtype=torch.uint8, device=dev)
-    torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream()
-
-    def prefill_step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        msa.msa_index_topk(inp.q_idx, inp.k_idx, k, block_idx=block_idx)
-        if ev is not None:
-            ev[1].record(stream)
-        msa.msa_sparse_attn_fwd(inp.q, inp.k, inp.v, block_idx, o=o, lse=lse, workspace=ws)
-        if ev is not None:
-            ev[2].record(stream)
-
-    log("prefill warmup")
-    for _ in range(args.warmup):
-        prefill_step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    log(f"prefill timed: {args.steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        prefill_step(evs[s])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    t_index = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    t_attn = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-    ms_step = wall * 1e3 / args.steps
-
-    pairs = attended_pairs(block_idx, B_k, G)
-    f_index = flops_index_exact(N, H_kv, cfg.d_idx)
-    f_main = 4 * cfg.d_h * pairs
-    f_total = f_index + f_main
-    f_eq12 = flops_msa_eq12(N, H_q, H_kv, cfg.d_h, cfg.d_idx, B_k, k)
-    prefill_tps = N / (ms_step / 1e3)
-    tflops = f_total / (ms_step / 1e3) / 1e12
-    r_off = torch.arange(H_kv, device=dev).view(1, H_kv, 1) * cfg.B
-    ids = (block_idx.to(torch.int64) + r_off)[block_idx >= 0]
-    fan = torch.bincount(ids, minlength=H_kv * cfg.B).view(H_kv, cfg.B)
+    pre, inp = run_prefill(msa, synth, cfg, args.mode, args.steps, args.warmup)
     result = {
         "metric": "MSA prefill tokens/s + TFLOP/s at 128K; decode tokens/s at 128K KV (1 GPU)",
-        "value": round(prefill_tps, 1),
+        "value": pre["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": pre["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -146,79 +351,36 @@ def main(argv=None) -> int:
         "data": f"synthetic ({args.mode} mode, seeded)",
         "config": {"workload": f"prefill N={N} H_q={H_q} H_kv={H_kv} d_h={cfg.d_h} d_idx={cfg.d_idx} "
                                f"B_k={B_k} k={k}", "mode": args.mode, "seq_len": N, "batch": 1},
-        "prefill": {
-            "tflops": round(tflops, 2),
-            "tflops_eq12_nominal": round(f_eq12 / (ms_step / 1e3) / 1e12, 2),
-            "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-            "flop_index": f_index, "flop_main": f_main, "flop_eq12": f_eq12,
-            "ms_index_topk": round(t_index, 4), "ms_sparse_attn_fwd": round(t_attn, 4),
-            "block0_fanin_per_group": int(fan[:, 0].float().mean().item()), "max_fanin": int(fan.max().item()),
-            "median_fanin": float(fan.float().median().item()),
-        },
+        "prefill": pre,
     }
-    # Roofline of the index-scoring kernel (a single launch inside msa_index_topk).
-    idx_tflops = f_index / (t_index / 1e3) / 1e12
-    result["roofline"] = {"kernel": "index_topk_kernel", "bound": "mfma", "achieved": round(idx_tflops, 2),
-                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                          "frac": round(idx_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    # The dominant kernel is the KV-outer phase 1; it is bound by its HBM bytes
+    # (about 126 FLOP per byte, below the bf16 ridge of about 312).
+    gbs = pre["phase1_algorithmic_bytes"] / (pre["ms_kvouter_phase1"] / 1e3) / 1e9
+    traffic = recorded_traffic(args.mode)
+    result["roofline"] = {"kernel": "attn_kvouter_kernel", "bound": "hbm", "achieved": round(gbs, 1),
+                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                          "traffic": traffic,
+                          "algorithmic_bytes": pre["phase1_algorithmic_bytes"],
+                          "mfma_frac": round(pre["phase1_tflops"] / PEAK_BF16_TFLOPS, 4)}
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_rows)
+    del inp
+    torch.cuda.empty_cache()
 
     if not args.no_decode:
         dcfg = synth.CONFIGS[args.decode_workload]
-        log(f"generating {dcfg.name} decode inputs")
-        d = synth.make_decode(dcfg, args.mode, device=dev)
-        max_len = max(d.lengths)
-        dbi = torch.empty((dcfg.batch, dcfg.H_kv, dcfg.k), dtype=torch.int32, device=dev)
-        do = torch.empty((dcfg.batch, dcfg.H_q, dcfg.d_h), dtype=torch.float32, device=dev)
-        dl = torch.empty((dcfg.batch, dcfg.H_q), dtype=torch.float32, device=dev)
-        dws = torch.empty(msa.msa_decode_workspace(dcfg.batch, dcfg.H_q, dcfg.H_kv, dcfg.k, max_len),
-                          dtype=torch.uint8, device=dev)
-
-        def decode_step():
-            msa.msa_decode(d.q, d.q_idx, d.k_cache, d.v_cache, d.k_idx_cache, d.cu_seqlens, max_len, dcfg.k,
-                           block_idx=dbi, o=do, lse=dl, workspace=dws)
-
-        for _ in range(args.warmup):
-            decode_step()
-        torch.cuda.synchronize()
-        dsteps = max(args.steps, 50)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(dsteps):
-            decode_step()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        dms = e0.elapsed_time(e1) / dsteps
-        T = int(d.cu_seqlens[-1].item())
-        # algorithmic bytes: every cached index key (d_idx bf16) + K and V of the chosen blocks
-        chosen = int((dbi >= 0).sum().item())
-        dbytes = T * dcfg.d_idx * 2 + chosen * B_k * dcfg.d_h * 2 * 2
-        result["decode"] = {
-            "workload": f"decode batch={dcfg.batch} L={min(d.lengths)}..{max_len} H_q={dcfg.H_q} H_kv={dcfg.H_kv} "
-                        f"k={dcfg.k}",
-            "ms_per_step": round(dms, 4), "tokens_per_s": round(dcfg.batch / (dms / 1e3), 1),
-            "algorithmic_bytes": dbytes, "GB_s": round(dbytes / (dms / 1e3) / 1e9, 1),
-            "hbm_peak_frac": round(dbytes / (dms / 1e3) / 1e9 / PEAK_HBM_GBS, 4), "steps": dsteps,
-        }
-        del d
-
-    if not args.no_cpu_baseline:
-        import numpy as np
-        import oracle
-        log(f"cpu baseline: oracle on {args.cpu_rows} sampled query rows")
-        g = np.random.default_rng(cfg.seed)
-        rows = np.sort(g.choice(N, size=args.cpu_rows, replace=False))
-        qi_h, ki_h = inp.q_idx.cpu(), inp.k_idx.cpu()
-        q_h, k_h, v_h = inp.q.cpu(), inp.k.cpu(), inp.v.cpu()
-        t0 = time.perf_counter()
-        M = oracle.block_scores(qi_h, ki_h, B_k, rows=rows)
-        bi = oracle.topk(M, k, B_k, rows=rows)
-        oracle.sparse_attn(q_h, k_h, v_h, bi, B_k, rows=rows)
-        tc = time.perf_counter() - t0
-        result["cpu_baseline"] = {"value": round(len(rows) / tc, 3), "unit": "tokens/s", "cores": oracle.threads(),
-                                  "kind": "oracle",
-                                  "sample": f"{len(rows)} uniformly drawn query rows of the same 128K prefill "
-                                            f"(all groups and heads; index scoring, Top-k and attention) in "
-                                            f"{tc:.1f} s"}
+        result["decode"] = run_decode(msa, synth, dcfg, args.mode, max(args.steps, 50), args.warmup)
+        torch.cuda.empty_cache()
+    if not args.single_mode:
+        pre2, inp2 = run_prefill(msa, synth, cfg, other, args.steps, args.warmup)
+        del inp2
+        torch.cuda.empty_cache()
+        result[other] = {"prefill": pre2}
+        if not args.no_decode:
+            result[other]["decode"] = run_decode(msa, synth, synth.CONFIGS[args.decode_workload], other,
+                                                 max(args.steps, 50), args.warmup)
+            torch.cuda.empty_cache()
     print(json.dumps(result), flush=True)
     return 0
 

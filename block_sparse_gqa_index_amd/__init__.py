@@ -41,6 +41,7 @@ _SIGS = {
                     _SZ, _P], _I32),
     "msa_index_block_scores": ([_P, _P, _I64, _I32, _I32, _I32, _P, _P], _I32),
     "msa_topk_from_scores": ([_P, _I64, _I32, _I64, _I32, _I32, _P, _P], _I32),
+    "msa_set_profile_events": ([ctypes.POINTER(_P), _I32], _I32),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -203,6 +204,24 @@ def msa_decode(q: torch.Tensor, q_idx: torch.Tensor, k_cache: torch.Tensor, v_ca
                            batch, max_len, H_q, H_kv, d_h, d_idx, B_k, k, float(scale), _ptr(block_idx), _ptr(o),
                            _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "msa_decode")
     return block_idx, o, lse
+
+
+def msa_set_profile_events(events=None) -> None:
+    """Record 4 caller-owned events at the phase boundaries of later msa_sparse_attn_fwd
+    calls on this thread (inverse index, KV-outer phase 1, combine, end); None clears.
+
+    Takes torch.cuda.Event objects created with enable_timing=True.  Each event is
+    recorded once here on the current stream so that its handle exists."""
+    if events is None:
+        _check(_lib.msa_set_profile_events(None, 0), "msa_set_profile_events")
+        return
+    if len(events) != 4:
+        raise ValueError("msa_set_profile_events takes 4 events")
+    for e in events:
+        if not e.cuda_event:
+            e.record()
+    arr = (_P * 4)(*[e.cuda_event for e in events])
+    _check(_lib.msa_set_profile_events(arr, 4), "msa_set_profile_events")
 
 
 def raw():

@@ -10,6 +10,9 @@
 namespace {
 
 thread_local char g_last_error[512] = "";
+// Caller-owned events recorded at the phase boundaries of msa_sparse_attn_fwd.
+thread_local hipEvent_t g_phase_events[4] = {nullptr, nullptr, nullptr, nullptr};
+thread_local bool g_phase_events_on = false;
 
 msa_status_t fail(msa_status_t st, const char* fmt, ...) {
   va_list ap;
@@ -189,9 +192,22 @@ msa_status_t msa_sparse_attn_fwd(const void* q, const void* k, const void* v, co
     hipError_t e = msa::launch_sparse_attn_window(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), block_idx,
         N, H_q, H_kv, k_sel, scale, w0, Wn, cus, o, lse, static_cast<uint8_t*>(ws), L,
-        static_cast<hipStream_t>(hip_stream));
+        static_cast<hipStream_t>(hip_stream), g_phase_events_on ? g_phase_events : nullptr);
     if (e != hipSuccess) return hip_fail(e, "sparse_attn launch");
   }
+  return ok();
+}
+
+msa_status_t msa_set_profile_events(void* const* events, int n) {
+  if (n == 0) {
+    g_phase_events_on = false;
+    return ok();
+  }
+  if (n != 4 || !events) return fail(MSA_ERR_INVALID_ARG, "msa_set_profile_events takes 0 or 4 events");
+  for (int i = 0; i < 4; ++i)
+    if (!events[i]) return fail(MSA_ERR_INVALID_ARG, "null event handle");
+  for (int i = 0; i < 4; ++i) g_phase_events[i] = static_cast<hipEvent_t>(events[i]);
+  g_phase_events_on = true;
   return ok();
 }
 

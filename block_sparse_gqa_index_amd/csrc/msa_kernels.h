@@ -38,7 +38,8 @@ AttnWorkspace attn_workspace_layout(int64_t W, int H_q, int H_kv, int kk, int64_
 hipError_t launch_sparse_attn_window(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                      const int32_t* block_idx, int64_t N, int H_q, int H_kv, int kk,
                                      float scale, int64_t w0, int64_t W, int num_cus, float* o, float* lse,
-                                     uint8_t* ws, const AttnWorkspace& L, hipStream_t stream);
+                                     uint8_t* ws, const AttnWorkspace& L, hipStream_t stream,
+                                     const hipEvent_t* events);  // 4 phase events or null
 
 DecodeWorkspace decode_workspace_layout(int batch, int H_q, int H_kv, int kk, int64_t Bmax);
 hipError_t launch_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_t* k_cache,

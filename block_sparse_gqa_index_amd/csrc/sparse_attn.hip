@@ -578,7 +578,8 @@ AttnWorkspace attn_workspace_layout(int64_t W, int H_q, int H_kv, int kk, int64_
 hipError_t launch_sparse_attn_window(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                      const int32_t* block_idx, int64_t N, int H_q, int H_kv, int kk,
                                      float scale, int64_t w0, int64_t W, int num_cus, float* o, float* lse,
-                                     uint8_t* ws, const AttnWorkspace& L, hipStream_t stream) {
+                                     uint8_t* ws, const AttnWorkspace& L, hipStream_t stream,
+                                     const hipEvent_t* events) {
   const int64_t B = (N + kBk - 1) / kBk;
   const int64_t lists = (int64_t)H_kv * L.nW * B;
   const int G = H_q / H_kv;
@@ -590,8 +591,10 @@ hipError_t launch_sparse_attn_window(const uint16_t* q, const uint16_t* k, const
   uint16_t* opart = reinterpret_cast<uint16_t*>(ws + L.opart);
   float2* lpart = reinterpret_cast<float2*>(ws + L.lpart);
 
+  hipError_t e;
+  if (events && (e = hipEventRecord(events[0], stream)) != hipSuccess) return e;
   fill_i32_kernel<<<dim3(256), dim3(256), 0, stream>>>(counts, lists, 0);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
 
   // Query tiles of the inverse-index passes hold at most 4096 pairs (16 per thread).
@@ -611,6 +614,7 @@ hipError_t launch_sparse_attn_window(const uint16_t* q, const uint16_t* k, const
   if (grid > L.max_items) grid = L.max_items;
   grid = ((grid + 7) / 8) * 8;
   const float scale_log2 = scale * kLog2e;
+  if (events && (e = hipEventRecord(events[1], stream)) != hipSuccess) return e;
   switch (G) {
 #define MSA_ATTN_CASE(GG)                                                                            \
   case GG:                                                                                           \
@@ -631,6 +635,7 @@ hipError_t launch_sparse_attn_window(const uint16_t* q, const uint16_t* k, const
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
+  if (events && (e = hipEventRecord(events[2], stream)) != hipSuccess) return e;
   const int64_t waves = W * H_kv * (G > 32 ? G / 32 : 1);
   const dim3 cgrid((unsigned)((waves + 3) / 4));
   switch (G) {
@@ -653,7 +658,9 @@ hipError_t launch_sparse_attn_window(const uint16_t* q, const uint16_t* k, const
     default:
       return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (events && (e = hipEventRecord(events[3], stream)) != hipSuccess) return e;
+  return hipSuccess;
 }
 
 }  // namespace msa

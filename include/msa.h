@@ -131,6 +131,17 @@ msa_status_t msa_index_block_scores(const void* q_idx, const void* k_idx, int64_
 msa_status_t msa_topk_from_scores(const float* M, int64_t N, int H_kv, int64_t B, int B_k, int k,
                                   int32_t* block_idx, void* hip_stream);
 
+/* Measurement hook, not part of the method: while set, each msa_sparse_attn_fwd call
+ * made on this host thread records, on its stream and for every query window,
+ * events[0] before the inverse index (counts, scan, scatter), events[1] before the
+ * KV-outer phase-1 kernel, events[2] before the combine and events[3] after it.
+ * After a call the events therefore bracket the phases of its last window.
+ *   events  n hipEvent_t handles owned by the caller; they must stay valid while set.
+ *   n       4 to set, 0 to clear (events is then ignored).
+ * Returns MSA_ERR_INVALID_ARG for any other n or a null handle (the previous setting
+ * is kept).  Host-only; no device work. */
+msa_status_t msa_set_profile_events(void* const* events, int n);
+
 #ifdef __cplusplus
 }
 #endif

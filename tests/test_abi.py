@@ -120,6 +120,16 @@ def test_decode_rejects_bad_arguments(lib):
     assert call(batch=0) == lib.MSA_OK
 
 
+def test_profile_events_hook_validates(lib):
+    raw = lib.raw()
+    assert raw.msa_set_profile_events(None, 3) == lib.MSA_ERR_INVALID_ARG
+    assert raw.msa_set_profile_events(None, 4) == lib.MSA_ERR_INVALID_ARG
+    import ctypes as C
+    arr = (C.c_void_p * 4)(0x10, 0x20, None, 0x40)
+    assert raw.msa_set_profile_events(arr, 4) == lib.MSA_ERR_INVALID_ARG  # null handle
+    assert raw.msa_set_profile_events(None, 0) == lib.MSA_OK
+
+
 def test_binding_fails_loudly_without_library(tmp_path):
     # Importing the binding from a copy without libmsa.so must raise, not fall back.
     import shutil
