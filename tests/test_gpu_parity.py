@@ -111,6 +111,7 @@ ATTN_SHAPES = [  # N, H_q, H_kv, k
     (129, 32, 1, 2),
     (2600, 16, 1, 5),
     (512, 64, 4, 4),
+    (3000, 8, 1, 16),  # one GPU's share of the 128K workload when the 8 groups are split
 ]
 
 
