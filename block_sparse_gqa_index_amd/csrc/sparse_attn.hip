@@ -11,9 +11,9 @@
 //
 // Work decomposition on gfx950.  For each (group r, KV block b) the inverse index
 // lists the (query, slot) pairs that chose it.  Lists are cut into fixed items of
-// kItemChunks chunks; a chunk is 128 MFMA rows = (128 / G) gathered queries x G
+// at most kItemChunks chunks and 128 pairs; a chunk is 128 MFMA rows = (128 / G) gathered queries x G
 // heads (query concatenation).  A workgroup stages the block's K (32 KB) and V^T
-// (33 KB) in LDS once per item, then for each chunk every wave computes 32 rows:
+// (32 KB) in LDS once per item, then for each chunk every wave computes 32 rows:
 // S^T = K * Q^T and O^T = V^T * P^T on 32x32x16 bf16 MFMAs, with the softmax in
 // fp32 in between.  Every pair owns its partial slot [query][group][slot], so the
 // partials of hot (sink) blocks spread over many workgroups without atomics.
@@ -152,10 +152,47 @@ __global__ __launch_bounds__(256) void inv_scatter_kernel(const int32_t* __restr
 // --------------------------------------------------------------------- phase 1
 constexpr int kAttnThreads = 256;
 
-__device__ __forceinline__ const uint8_t* shfl_ptr(const uint8_t* p, int src) {
-  const uint64_t v = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __shfl((uint32_t)v, src), hi = __shfl((uint32_t)(v >> 32), src);
-  return reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
+// The pairs of a work item (at most 128) live in two registers per lane: lane j
+// holds pair j in `ia` and pair 64 + j in `ib`.  A uniform index reads one lane
+// (scalar result); a per-lane index uses two lane shuffles.  Either way no memory
+// access is made, so no wait on earlier stores is needed inside the chunk loop.
+__device__ __forceinline__ int item_pair_u(int ia, int ib, int idx) {
+  const int a = __builtin_amdgcn_readlane(ia, idx & 63), b = __builtin_amdgcn_readlane(ib, idx & 63);
+  return idx < 64 ? a : b;
+}
+__device__ __forceinline__ int item_pair_v(int ia, int ib, int idx) {
+  const int a = __shfl(ia, idx & 63), b = __shfl(ib, idx & 63);
+  return idx < 64 ? a : b;
+}
+
+// Gather of one chunk's q rows, coalesced: load t of lane j fetches 16-byte chunk
+// j%16 of the wave's row 4t + j/16 (16 lanes read one 256-byte head row).  Row rho
+// of the wave is MFMA row wave*32 + rho = (pair cbase + (wave*32 + rho) / G, head
+// (wave*32 + rho) % G); pairs past the item's end re-read pair 0 (a valid address,
+// results discarded).  With G >= 4 the 4 rows of a load are 4 consecutive heads of
+// one pair, i.e. one contiguous 1 KB run: its base is uniform and the lane only
+// adds lane*16 bytes.  Addresses are formed from the kernel's global pointer, so
+// the loads stay global, not flat.
+template <int G>
+__device__ __forceinline__ void gather_q(u32x4_t (&qraw)[8], const uint16_t* __restrict__ q, int ia, int ib,
+                                         int cbase, int cnt, int wave, int lane, int64_t w0, int H_q,
+                                         int64_t r) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    if constexpr (G >= 4) {
+      const int row0 = wave * 32 + 4 * t;
+      const int idx = cbase + row0 / G;
+      const int pr = item_pair_u(ia, ib, idx < cnt ? idx : 0);
+      const int64_t off = ((w0 + (pr >> 5)) * H_q + r * G + row0 % G) * kDh;
+      qraw[t] = *reinterpret_cast<const u32x4_t*>(q + off + lane * 8);
+    } else {
+      const int row = wave * 32 + 4 * t + (lane >> 4);
+      const int idx = cbase + row / G;
+      const int pr = item_pair_v(ia, ib, idx < cnt ? idx : 0);
+      const int64_t off = ((w0 + (pr >> 5)) * H_q + r * G + row % G) * kDh;
+      qraw[t] = *reinterpret_cast<const u32x4_t*>(q + off + (lane & 15) * 8);
+    }
+  }
 }
 
 // LDS row rho of the staged K tile holds key swap23(rho) (bits 2 and 3 of the row
@@ -237,6 +274,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
     const int64_t b = it.x % B, r = (it.x / B) / nW;
     const int start = it.y, cnt = it.z;
 
+    // The item's pairs (at most 128): lane j holds pair j and pair 64 + j.  Entries
+    // past the end repeat pair 0.
+    const int ia = pairs[start + (lane < cnt ? lane : 0)];
+    const int ib = pairs[start + (64 + lane < cnt ? 64 + lane : 0)];
     __syncthreads();  // previous item's LDS reads are done
     {
       // Recompute the staging addresses per item rather than keeping ~40 loop-
@@ -251,35 +292,15 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
     }
     __syncthreads();
 
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     const int qrow = wave * 32 + l32;
     const int qs = qrow / G, g = qrow % G;
-    // Chunk 0's gather; later chunks are prefetched one chunk ahead.  Rows past the
-    // end of the item re-read the item's first pair (a valid address); their
-    // results are discarded.
-    //
-    // The gather is coalesced: load t of lane j fetches 16-byte chunk j%16 of the
-    // wave's row 4t + j/16 (16 lanes read one 256-byte head row).  At the start of
-    // a chunk the rows are moved to the MFMA operand layout (lane l32 holds row l32)
-    // through the wave's LDS buffer, 16 rows per pass, chunk c of row rho at
-    // position c ^ rho.
+    // Chunk 0's gather; later chunks are prefetched one chunk ahead.  Gathered rows
+    // are moved to the MFMA operand layout (lane l32 holds row l32) through the
+    // wave's LDS buffer, 16 rows per pass, chunk c of row rho at position c ^ rho.
     uint8_t* ost = Ostage[wave];
-    // Byte address of this lane's q row for pair pr (query w0 + pr/32, head r*G + g).
-    auto q_row = [&](int prv) {
-      return reinterpret_cast<const uint8_t*>(q + ((w0 + (prv >> 5)) * H_q + r * G + g) * kDh);
-    };
-    int pr = pairs[start + (qs < cnt ? qs : 0)];
-    u32x4_t qraw[8];
-    {
-      const uint8_t* qa = q_row(pr);
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-        qraw[t] = *reinterpret_cast<const u32x4_t*>(shfl_ptr(qa, 4 * t + (lane >> 4)) + (lane & 15) * 16);
-    }
-    for (int cb = 0; cb < cnt; cb += kQC) {
-      // Keep the LDS operand reads inside the chunk loop: hoisting them (they do
-      // not change across chunks) would need 256 registers per lane.
-      asm volatile("" ::: "memory");
-      u32x4_t qop[8];
+    u32x4_t qraw[8], qop[8];
+    auto to_operands = [&]() {
 #pragma unroll
       for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
@@ -294,18 +315,19 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
             qop[t] = *reinterpret_cast<const u32x4_t*>(ost + rho * 256 + (((8 * h + t) ^ rho) << 4));
         }
       }
+    };
+    gather_q<G>(qraw, q, ia, ib, 0, cnt, wave_u, lane, w0, H_q, r);
+    to_operands();
+    for (int cb = 0; cb < cnt; cb += kQC) {
+      // Keep the LDS operand reads inside the chunk loop: hoisting them (they do
+      // not change across chunks) would need 256 registers per lane.
+      asm volatile("" ::: "memory");
       // Prefetch the next chunk's pair and q rows while this chunk finishes.
       // (After the item's last chunk this re-reads the item's first pair: a valid
       // address, and it keeps the current q registers dead after the MFMAs.)
-      const int pr_n = pairs[start + (cb + kQC + qs < cnt ? cb + kQC + qs : 0)];
-      {
-        const uint8_t* qa = q_row(pr_n);
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-          qraw[t] = *reinterpret_cast<const u32x4_t*>(shfl_ptr(qa, 4 * t + (lane >> 4)) + (lane & 15) * 16);
-      }
 
       const bool valid = cb + qs < cnt;
+      const int pr = item_pair_v(ia, ib, valid ? cb + qs : 0);  // the lane's own row
       const int64_t i_local = pr >> 5;
       const int s = pr & 31;
       const int64_t i = w0 + i_local;
@@ -315,7 +337,6 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
       f32x16_t sacc[4];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        asm volatile("" ::: "memory");  // bound the K-operand reads in flight
         sacc[kt] = f32x16_t{};
         const int row = kt * 32 + l32;
 #pragma unroll
@@ -325,6 +346,21 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
           sacc[kt] = mfma_32x32x16(as_bf16x8(a), as_bf16x8(qop[t]), sacc[kt]);
         }
       }
+      // Keep 8 K-operand reads in flight ahead of the MFMAs that consume them.
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int j = 0; j < 24; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+
+      // Prefetch of the next chunk's q rows once the q operands are consumed: they
+      // land while the softmax, PV and stores run.  (After the item's last chunk
+      // this re-reads pair 0: valid addresses.)
+      __builtin_amdgcn_sched_barrier(0);
+      gather_q<G>(qraw, q, ia, ib, cb + kQC, cnt, wave_u, lane, w0, H_q, r);
+      __builtin_amdgcn_sched_barrier(0);
 
       // Causal mask, only where a lane's block reaches past its query: element v of
       // tile kt is key kt*32 + 16*(v/8) + 4*((v/4)%2) + v%4 + 8h of the block.
@@ -372,59 +408,78 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
         pb[u].w = pack_bf16x2(sacc[kt][8 * hf + 6], sacc[kt][8 * hf + 7]);
       }
 
-      // O^T[d][qrow] = V^T[d][key] * P^T[key][qrow]; lane (l32, h) reads the 8-key
-      // chunk 4*(u/2) + 2*(u%2) + h of row d = 32*dt + l32.
-      f32x16_t oacc[4];
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x16_t{};
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        asm volatile("" ::: "memory");  // issue this step's V^T reads just in time
-        const int kc = 2 * u + h;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const int d = dt * 32 + l32;
-          const u32x4_t va = *reinterpret_cast<const u32x4_t*>(Vt + d * 256 + ((kc ^ (d & 15)) << 4));
-          oacc[dt] = mfma_32x32x16(as_bf16x8(va), as_bf16x8(pb[u]), oacc[dt]);
-        }
-      }
-
+      // The softmax is complete before PV starts (its fp32 scores are dead), which
+      // leaves registers for V^T reads in flight.
+      __builtin_amdgcn_sched_barrier(0);
       // Unnormalised partial (bf16) plus its base-2 max and sum for the combine.
-      // The O^T tile leaves the MFMA with each row split over two lanes; it goes
-      // through a wave-private LDS buffer (two passes of 16 rows, 16-byte chunk c of
-      // row rho at position c ^ rho) so that every store instruction writes four
-      // whole 256-byte partial rows.
+      // Stores are unconditional: a row past the item's end computed pair 0's q
+      // against the same block, so it writes pair 0's partial again with the same
+      // bits (and both lane halves write their row's identical (m, l)).
       const int64_t prow = ((i_local * H_kv + r) * kk + s) * G + g;
-      if (valid && h == 0) Lpart[prow] = make_float2(empty ? -__builtin_inff() : m2, l);
-      const uint8_t* prow_addr = reinterpret_cast<const uint8_t*>(Opart + prow * kDh);
-      u32x2_t opk[16];
+      Lpart[prow] = make_float2(empty ? -__builtin_inff() : m2, l);
+
+      // O^T[d][qrow] = V^T[d][key] * P^T[key][qrow] in two halves of 64 dims, each
+      // stored before the next starts (half the accumulators live at a time).  Lane
+      // (l32, h) reads the 8-key chunk 2u + h of V^T row d = 32*dt + l32.
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
+      for (int hd = 0; hd < 2; ++hd) {
+        f32x16_t oacc[2] = {f32x16_t{}, f32x16_t{}};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          opk[4 * dt + c].x = pack_bf16x2(oacc[dt][4 * c + 0], oacc[dt][4 * c + 1]);
-          opk[4 * dt + c].y = pack_bf16x2(oacc[dt][4 * c + 2], oacc[dt][4 * c + 3]);
+        for (int u = 0; u < 8; ++u) {
+          const int kc = 2 * u + h;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int d = (2 * hd + j) * 32 + l32;
+            const u32x4_t va = *reinterpret_cast<const u32x4_t*>(Vt + d * 256 + ((kc ^ (d & 15)) << 4));
+            oacc[j] = mfma_32x32x16(as_bf16x8(va), as_bf16x8(pb[u]), oacc[j]);
+          }
         }
-      }
+        // V^T-operand reads run 8 ahead of their MFMAs.
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
 #pragma unroll
-      for (int pass = 0; pass < 2; ++pass) {
-        if ((l32 >> 4) == pass) {
-          const int rho = l32 & 15;
-#pragma unroll
-          for (int j = 0; j < 16; ++j)
-            *reinterpret_cast<u32x2_t*>(ost + rho * 256 + ((j ^ rho) << 4) + 8 * h) = opk[j];
+        for (int j = 0; j < 8; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
         }
-        // Row rho of this pass is qrow wave*32 + 16*pass + rho; lane -> (row, chunk).
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);
+
+        // The half tile leaves the MFMA with lane (l32, h) holding dims 32j + 8c +
+        // 4h .. +3 (c = 0..3) of row l32.  Through the wave's LDS buffer (half-row
+        // rho at rho*128, 16-byte chunk x at position x ^ (rho & 7)) it is
+        // re-read as 8 half-rows of 128 bytes per instruction.
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            u32x2_t pk;
+            pk.x = pack_bf16x2(oacc[j][4 * c + 0], oacc[j][4 * c + 1]);
+            pk.y = pack_bf16x2(oacc[j][4 * c + 2], oacc[j][4 * c + 3]);
+            *reinterpret_cast<u32x2_t*>(ost + l32 * 128 + (((4 * j + c) ^ (l32 & 7)) << 4) + 8 * h) = pk;
+          }
+        }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const int rho = 4 * u + (lane >> 4), ch = lane & 15;
-          const u32x4_t val = *reinterpret_cast<const u32x4_t*>(ost + rho * 256 + ((ch ^ rho) << 4));
-          const int src = 16 * pass + rho;  // l32 of the row's owner
-          const uint8_t* dst = shfl_ptr(prow_addr, src);
-          if (__shfl((int)valid, src)) *reinterpret_cast<u32x4_t*>(const_cast<uint8_t*>(dst) + ch * 16) = val;
+          const int rho = 8 * u + (lane >> 3), ch = lane & 7;
+          const u32x4_t val = *reinterpret_cast<const u32x4_t*>(ost + rho * 128 + ((ch ^ (rho & 7)) << 4));
+          if constexpr (G >= 8) {
+            // Half-rows 8u..8u+7 are heads g0..g0+7 of one pair: uniform base.
+            const int row0 = wave_u * 32 + 8 * u;
+            const int qs0 = row0 / G, g0 = row0 % G;
+            const int pu = item_pair_u(ia, ib, cb + qs0 < cnt ? cb + qs0 : 0);
+            const int64_t prow0 = (((int64_t)(pu >> 5) * H_kv + r) * kk + (pu & 31)) * G + g0;
+            *reinterpret_cast<u32x4_t*>(Opart + prow0 * kDh + 64 * hd + (lane >> 3) * kDh + ch * 8) = val;
+          } else {
+            const int row = wave * 32 + rho;
+            const int pu = item_pair_v(ia, ib, cb + row / G < cnt ? cb + row / G : 0);
+            const int64_t prow_s = (((int64_t)(pu >> 5) * H_kv + r) * kk + (pu & 31)) * G + row % G;
+            *reinterpret_cast<u32x4_t*>(Opart + prow_s * kDh + 64 * hd + ch * 8) = val;
+          }
         }
       }
-      pr = pr_n;
+      // The next chunk's q rows to the operand layout here, after this chunk's
+      // stores, so that the wait for them counts those stores as still in flight.
+      to_operands();
+
     }
   }
 }
@@ -554,7 +609,9 @@ AttnWorkspace attn_workspace_layout(int64_t W, int H_q, int H_kv, int kk, int64_
   const int64_t lists = (int64_t)H_kv * L.nW * B;
   const int64_t max_pairs = W * H_kv * kk;
   const int G = H_q / H_kv;
-  const int item_q = kItemChunks * (128 / G);
+  // At most 128 pairs per item: the attention kernel keeps an item's pairs in two
+  // registers per lane.
+  const int item_q = kItemChunks * (128 / G) < 128 ? kItemChunks * (128 / G) : 128;
   const int64_t max_items = (max_pairs + item_q - 1) / item_q + lists;
   size_t off = 0;
   auto take = [&](size_t bytes) {
