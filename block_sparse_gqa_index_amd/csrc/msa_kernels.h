@@ -13,7 +13,7 @@ constexpr int kIndexDim = 64;
 constexpr int kBlockKeys = 128;
 
 // Chunks (of 128 MFMA rows) per work item of the KV-outer kernel.
-constexpr int kItemChunks = 8;
+constexpr int kItemChunks = 16;
 
 struct AttnWorkspace {
   size_t counts, cursor, n_items, items, pairs, opart, lpart, total;

@@ -11,7 +11,7 @@
 //
 // Work decomposition on gfx950.  For each (group r, KV block b) the inverse index
 // lists the (query, slot) pairs that chose it.  Lists are cut into fixed items of
-// at most kItemChunks chunks and 128 pairs; a chunk is 128 MFMA rows = (128 / G) gathered queries x G
+// at most kItemChunks chunks and 256 pairs; a chunk is 128 MFMA rows = (128 / G) gathered queries x G
 // heads (query concatenation).  A workgroup stages the block's K (32 KB) and V^T
 // (32 KB) in LDS once per item, then for each chunk every wave computes 32 rows:
 // S^T = K * Q^T and O^T = V^T * P^T on 32x32x16 bf16 MFMAs, with the softmax in
@@ -152,43 +152,68 @@ __global__ __launch_bounds__(256) void inv_scatter_kernel(const int32_t* __restr
 // --------------------------------------------------------------------- phase 1
 constexpr int kAttnThreads = 256;
 
-// The pairs of a work item (at most 128) live in two registers per lane: lane j
-// holds pair j in `ia` and pair 64 + j in `ib`.  A uniform index reads one lane
-// (scalar result); a per-lane index uses two lane shuffles.  Either way no memory
-// access is made, so no wait on earlier stores is needed inside the chunk loop.
-__device__ __forceinline__ int item_pair_u(int ia, int ib, int idx) {
-  const int a = __builtin_amdgcn_readlane(ia, idx & 63), b = __builtin_amdgcn_readlane(ib, idx & 63);
-  return idx < 64 ? a : b;
+// The pairs of a work item live in kPairRegs<G> registers per lane: register j of
+// lane l holds pair 64j + l (entries past the end repeat the last pair).  Reading
+// them needs no memory access, so nothing inside the chunk loop waits on earlier
+// stores.  An item holds at most 64 * kPairRegs<G> pairs.
+template <int G>
+constexpr int kPairRegs = G >= 4 ? 4 : 2;
+
+// Chunk c covers the item's pairs [c*kQC, (c+1)*kQC); with G >= 4, kQC = 128/G
+// divides 64, so one register holds all of them (pairs past the end are replaced
+// by the last pair, which lies in the last chunk).
+// (A select chain here gets turned into an indexed load from a stack copy of ip;
+// a blend with an opaque uniform mask keeps ip in registers.)
+template <int NR>
+__device__ __forceinline__ int pick_reg(const int (&ip)[NR], int j) {
+  int v = 0;
+#pragma unroll
+  for (int k = 0; k < NR; ++k) {
+    int m = -(int)(j == k);
+    asm volatile("" : "+v"(m));
+    v |= ip[k] & m;
+  }
+  return v;
 }
-__device__ __forceinline__ int item_pair_v(int ia, int ib, int idx) {
-  const int a = __shfl(ia, idx & 63), b = __shfl(ib, idx & 63);
-  return idx < 64 ? a : b;
+
+// Per-lane pair index (any register): one lane shuffle per register.
+template <int NR>
+__device__ __forceinline__ int item_pair_v(const int (&ip)[NR], int idx) {
+  int v = 0;
+#pragma unroll
+  for (int k = 0; k < NR; ++k) {
+    const int x = __shfl(ip[k], idx & 63);
+    v = (idx >> 6) == k ? x : v;
+  }
+  return v;
 }
 
 // Gather of one chunk's q rows, coalesced: load t of lane j fetches 16-byte chunk
 // j%16 of the wave's row 4t + j/16 (16 lanes read one 256-byte head row).  Row rho
 // of the wave is MFMA row wave*32 + rho = (pair cbase + (wave*32 + rho) / G, head
-// (wave*32 + rho) % G); pairs past the item's end re-read pair 0 (a valid address,
-// results discarded).  With G >= 4 the 4 rows of a load are 4 consecutive heads of
-// one pair, i.e. one contiguous 1 KB run: its base is uniform and the lane only
-// adds lane*16 bytes.  Addresses are formed from the kernel's global pointer, so
-// the loads stay global, not flat.
+// (wave*32 + rho) % G); pairs past the item's end take the item's last pair (a
+// valid address; see the stores for why its results may be written).  With G >= 4
+// the 4 rows of a load are 4 consecutive heads of one pair, i.e. one contiguous
+// 1 KB run: its base is uniform (pair read from one lane of the chunk's register
+// `cur` into prs[t]) and the lane only adds lane*16 bytes.  Addresses are formed
+// from the kernel's global pointer, so the loads stay global, not flat.
 template <int G>
-__device__ __forceinline__ void gather_q(u32x4_t (&qraw)[8], const uint16_t* __restrict__ q, int ia, int ib,
-                                         int cbase, int cnt, int wave, int lane, int64_t w0, int H_q,
-                                         int64_t r) {
+__device__ __forceinline__ void gather_q(u32x4_t (&qraw)[8], int (&prs)[8], const uint16_t* __restrict__ q,
+                                         const int (&ip)[kPairRegs<G>], int cur, int cbase, int cnt, int wave,
+                                         int lane, int64_t w0, int H_q, int64_t r) {
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     if constexpr (G >= 4) {
       const int row0 = wave * 32 + 4 * t;
       const int idx = cbase + row0 / G;
-      const int pr = item_pair_u(ia, ib, idx < cnt ? idx : 0);
+      const int pr = __builtin_amdgcn_readlane(cur, (idx < cnt ? idx : cnt - 1) & 63);
+      prs[t] = pr;
       const int64_t off = ((w0 + (pr >> 5)) * H_q + r * G + row0 % G) * kDh;
       qraw[t] = *reinterpret_cast<const u32x4_t*>(q + off + lane * 8);
     } else {
       const int row = wave * 32 + 4 * t + (lane >> 4);
       const int idx = cbase + row / G;
-      const int pr = item_pair_v(ia, ib, idx < cnt ? idx : 0);
+      const int pr = item_pair_v(ip, idx < cnt ? idx : cnt - 1);
       const int64_t off = ((w0 + (pr >> 5)) * H_q + r * G + row % G) * kDh;
       qraw[t] = *reinterpret_cast<const u32x4_t*>(q + off + (lane & 15) * 8);
     }
@@ -274,10 +299,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
     const int64_t b = it.x % B, r = (it.x / B) / nW;
     const int start = it.y, cnt = it.z;
 
-    // The item's pairs (at most 128): lane j holds pair j and pair 64 + j.  Entries
-    // past the end repeat pair 0.
-    const int ia = pairs[start + (lane < cnt ? lane : 0)];
-    const int ib = pairs[start + (64 + lane < cnt ? 64 + lane : 0)];
+    constexpr int NR = kPairRegs<G>;
+    int ip[NR];
+#pragma unroll
+    for (int k = 0; k < NR; ++k) ip[k] = pairs[start + (64 * k + lane < cnt ? 64 * k + lane : cnt - 1)];
     __syncthreads();  // previous item's LDS reads are done
     {
       // Recompute the staging addresses per item rather than keeping ~40 loop-
@@ -316,18 +341,22 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
         }
       }
     };
-    gather_q<G>(qraw, q, ia, ib, 0, cnt, wave_u, lane, w0, H_q, r);
+    // Register holding chunk cbase's pairs (G >= 4).
+    auto chunk_reg = [&](int cbase) { return pick_reg(ip, (cbase < cnt ? cbase : cnt - 1) >> 6); };
+    int cur = chunk_reg(0), cur_n = cur;
+    int prs[8], prs_n[8];
+    gather_q<G>(qraw, prs, q, ip, cur, 0, cnt, wave_u, lane, w0, H_q, r);
     to_operands();
     for (int cb = 0; cb < cnt; cb += kQC) {
       // Keep the LDS operand reads inside the chunk loop: hoisting them (they do
       // not change across chunks) would need 256 registers per lane.
       asm volatile("" ::: "memory");
-      // Prefetch the next chunk's pair and q rows while this chunk finishes.
-      // (After the item's last chunk this re-reads the item's first pair: a valid
-      // address, and it keeps the current q registers dead after the MFMAs.)
-
       const bool valid = cb + qs < cnt;
-      const int pr = item_pair_v(ia, ib, valid ? cb + qs : 0);  // the lane's own row
+      int pr;  // the pair of the lane's own row
+      if constexpr (G >= 4)
+        pr = __shfl(cur, (valid ? cb + qs : cnt - 1) & 63);
+      else
+        pr = item_pair_v(ip, valid ? cb + qs : cnt - 1);
       const int64_t i_local = pr >> 5;
       const int s = pr & 31;
       const int64_t i = w0 + i_local;
@@ -335,6 +364,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
       // S^T[row][qrow] with row -> key swap23(row): k-slot (h, e) of step t is dim
       // 64h + 8t + e in both operands.
       f32x16_t sacc[4];
+      // Matrix phases run at raised wave priority, so that the other wave on the
+      // SIMD fills the VALU slots with its softmax rather than competing for issue.
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         sacc[kt] = f32x16_t{};
@@ -359,7 +392,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
       // land while the softmax, PV and stores run.  (After the item's last chunk
       // this re-reads pair 0: valid addresses.)
       __builtin_amdgcn_sched_barrier(0);
-      gather_q<G>(qraw, q, ia, ib, cb + kQC, cnt, wave_u, lane, w0, H_q, r);
+      __builtin_amdgcn_s_setprio(0);
+      cur_n = chunk_reg(cb + kQC);
+      gather_q<G>(qraw, prs_n, q, ip, cur_n, cb + kQC, cnt, wave_u, lane, w0, H_q, r);
       __builtin_amdgcn_sched_barrier(0);
 
       // Causal mask, only where a lane's block reaches past its query: element v of
@@ -411,10 +446,14 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
       // The softmax is complete before PV starts (its fp32 scores are dead), which
       // leaves registers for V^T reads in flight.
       __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(1);
       // Unnormalised partial (bf16) plus its base-2 max and sum for the combine.
-      // Stores are unconditional: a row past the item's end computed pair 0's q
-      // against the same block, so it writes pair 0's partial again with the same
-      // bits (and both lane halves write their row's identical (m, l)).
+      // The partial rows are written once and read only by the combine, so they
+      // are stored non-temporally (kept from displacing the cached q and K/V).
+      // Stores are unconditional: a row past the item's end computed the item's
+      // last pair (same q head row, same block), so it writes that pair's partial
+      // row again with the same bits (and both lane halves write their row's
+      // identical (m, l)).
       const int64_t prow = ((i_local * H_kv + r) * kk + s) * G + g;
       Lpart[prow] = make_float2(empty ? -__builtin_inff() : m2, l);
 
@@ -442,6 +481,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);
+        if (hd == 1) {
+          __builtin_amdgcn_sched_barrier(0);
+          __builtin_amdgcn_s_setprio(0);
+        }
 
         // The half tile leaves the MFMA with lane (l32, h) holding dims 32j + 8c +
         // 4h .. +3 (c = 0..3) of row l32.  Through the wave's LDS buffer (half-row
@@ -462,23 +505,34 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
           const int rho = 8 * u + (lane >> 3), ch = lane & 7;
           const u32x4_t val = *reinterpret_cast<const u32x4_t*>(ost + rho * 128 + ((ch ^ (rho & 7)) << 4));
           if constexpr (G >= 8) {
-            // Half-rows 8u..8u+7 are heads g0..g0+7 of one pair: uniform base.
+            // Half-rows 8u..8u+7 are heads g0..g0+7 of the pair of gather load 2u:
+            // uniform base.
             const int row0 = wave_u * 32 + 8 * u;
-            const int qs0 = row0 / G, g0 = row0 % G;
-            const int pu = item_pair_u(ia, ib, cb + qs0 < cnt ? cb + qs0 : 0);
-            const int64_t prow0 = (((int64_t)(pu >> 5) * H_kv + r) * kk + (pu & 31)) * G + g0;
-            *reinterpret_cast<u32x4_t*>(Opart + prow0 * kDh + 64 * hd + (lane >> 3) * kDh + ch * 8) = val;
+            const int pu = prs[2 * u];
+            const int64_t prow0 = (((int64_t)(pu >> 5) * H_kv + r) * kk + (pu & 31)) * G + row0 % G;
+            __builtin_nontemporal_store(
+                val, reinterpret_cast<u32x4_t*>(Opart + prow0 * kDh + 64 * hd + (lane >> 3) * kDh + ch * 8));
+          } else if constexpr (G == 4) {
+            // Half-rows 8u..8u+3 and 8u+4..8u+7 belong to the pairs of gather loads
+            // 2u and 2u+1.
+            const int row = wave_u * 32 + rho;
+            const int pu = (lane >> 5) ? prs[2 * u + 1] : prs[2 * u];
+            const int64_t prow_s = (((int64_t)(pu >> 5) * H_kv + r) * kk + (pu & 31)) * G + row % G;
+            __builtin_nontemporal_store(val, reinterpret_cast<u32x4_t*>(Opart + prow_s * kDh + 64 * hd + ch * 8));
           } else {
             const int row = wave * 32 + rho;
-            const int pu = item_pair_v(ia, ib, cb + row / G < cnt ? cb + row / G : 0);
+            const int pu = item_pair_v(ip, cb + row / G < cnt ? cb + row / G : cnt - 1);
             const int64_t prow_s = (((int64_t)(pu >> 5) * H_kv + r) * kk + (pu & 31)) * G + row % G;
-            *reinterpret_cast<u32x4_t*>(Opart + prow_s * kDh + 64 * hd + ch * 8) = val;
+            __builtin_nontemporal_store(val, reinterpret_cast<u32x4_t*>(Opart + prow_s * kDh + 64 * hd + ch * 8));
           }
         }
       }
       // The next chunk's q rows to the operand layout here, after this chunk's
       // stores, so that the wait for them counts those stores as still in flight.
       to_operands();
+      cur = cur_n;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) prs[t] = prs_n[t];
 
     }
   }
@@ -609,9 +663,10 @@ AttnWorkspace attn_workspace_layout(int64_t W, int H_q, int H_kv, int kk, int64_
   const int64_t lists = (int64_t)H_kv * L.nW * B;
   const int64_t max_pairs = W * H_kv * kk;
   const int G = H_q / H_kv;
-  // At most 128 pairs per item: the attention kernel keeps an item's pairs in two
-  // registers per lane.
-  const int item_q = kItemChunks * (128 / G) < 128 ? kItemChunks * (128 / G) : 128;
+  // The attention kernel keeps an item's pairs in registers: at most 256 pairs
+  // for G >= 4 and 128 otherwise.
+  const int max_q = G >= 4 ? 256 : 128;
+  const int item_q = kItemChunks * (128 / G) < max_q ? kItemChunks * (128 / G) : max_q;
   const int64_t max_items = (max_pairs + item_q - 1) / item_q + lists;
   size_t off = 0;
   auto take = [&](size_t bytes) {
