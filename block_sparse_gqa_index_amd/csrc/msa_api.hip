@@ -149,6 +149,7 @@ static msa_status_t check_attn_shape(int64_t N, int H_q, int H_kv, int d_h, int 
     return fail(MSA_ERR_INVALID_ARG, "H_q must be a positive multiple of H_kv");
   const int G = H_q / H_kv;
   if (!is_pow2(G) || G > 128) return fail(MSA_ERR_UNSUPPORTED, "H_q / H_kv must be a power of two <= 128");
+  if (N * H_kv >= ((int64_t)1 << 31)) return fail(MSA_ERR_UNSUPPORTED, "N * H_kv too large");
   return MSA_OK;
 }
 

@@ -552,13 +552,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   constexpr int LPH = 64 / GW;               // lanes per head
   constexpr int DPL = kDh / LPH;             // dims per lane (2*GW)
   constexpr int HPW = G / GW;                // waves per (query, group)
+  // Consecutive waves take consecutive (query, group) rows, so the workgroups in
+  // flight stream one contiguous region of partials and of o.
   const int lane = threadIdx.x & 63;
   const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (gw >= W * H_kv * HPW) return;
   const int hw = (int)(gw % HPW);
-  const int64_t ir = gw / HPW;               // (i_local, r)
-  const int64_t i_local = ir / H_kv;
-  const int r = (int)(ir % H_kv);
+  const int64_t ir = gw / HPW;               // (i_local, r); ir < 2^32 (W <= 2^20, H_kv < 2^12)
+  const int64_t i_local = (uint32_t)ir / (uint32_t)H_kv;
+  const int r = (int)((uint32_t)ir - (uint32_t)i_local * (uint32_t)H_kv);
   const int64_t i = w0 + i_local;
   const int g = hw * GW + lane / LPH;
   const int d0 = (lane % LPH) * DPL;
