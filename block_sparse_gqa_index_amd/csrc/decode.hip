@@ -40,17 +40,25 @@ __global__ __launch_bounds__(256) void dec_score_kernel(const uint16_t* __restri
   for (int ks = 0; ks < 2; ++ks)
     qop[ks] = col < H_kv ? *reinterpret_cast<const uint4*>(q_idx + ((int64_t)s * H_kv + col) * kDidx + ks * 32 + 8 * grp)
                          : make_uint4(0, 0, 0, 0);
-  float runmax = -__builtin_inff();
-#pragma unroll 2
+  // The block's 128 index keys (16 KB, read once per step: non-temporal) are all
+  // requested before the first MFMA.  Keys past the sequence end re-read its last
+  // key (a valid address); their scores are masked below.
+  u32x4_t ka[8][2];
+#pragma unroll
   for (int kt = 0; kt < 8; ++kt) {
     const int64_t key = b * kBk + kt * 16 + col;  // this lane's A row
+    const int64_t kr = key < L ? key : L - 1;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      ka[kt][ks] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4_t*>(k_idx + (j0 + kr) * kDidx + ks * 32 + 8 * grp));
+  }
+  float runmax = -__builtin_inff();
+#pragma unroll
+  for (int kt = 0; kt < 8; ++kt) {
     f32x4_t acc = {};
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const uint4 a = key < L ? *reinterpret_cast<const uint4*>(k_idx + (j0 + key) * kDidx + ks * 32 + 8 * grp)
-                              : make_uint4(0, 0, 0, 0);
-      acc = mfma_16x16x32(as_bf16x8(a), as_bf16x8(qop[ks]), acc);
-    }
+    for (int ks = 0; ks < 2; ++ks) acc = mfma_16x16x32(as_bf16x8(ka[kt][ks]), as_bf16x8(qop[ks]), acc);
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int64_t pos = b * kBk + kt * 16 + 4 * grp + v;
@@ -114,20 +122,28 @@ __global__ __launch_bounds__(256) void dec_topk_kernel(const float* __restrict__
   }
 }
 
-// Split-K attention for one (sequence, group, slot): G heads x one block of 128 keys.
+// Split-K attention for one (sequence, group, slot): the G heads of the group
+// against one block of up to 128 keys, on 32x32x16 bf16 MFMAs.  Wave w takes keys
+// 32w .. 32w+31: it reads its K rows straight into MFMA operands (S^T = K Q^T,
+// heads as the 32 MFMA columns, G of them real), takes the softmax with its own
+// max, and computes O^T = V^T P^T from the block's V^T, which the workgroup stages
+// in LDS with coalesced 16-byte loads (non-temporal: V is read once per step).
+// The four waves' (max, sum, O) are merged in LDS (rescaled to
+// the common max) and the normalised partial plus its natural-log LSE is written.
+// 33 KB of LDS per workgroup: four workgroups per CU keep the loads in flight.
 template <int G>
-__global__ __launch_bounds__(256) void dec_attn_kernel(const uint16_t* __restrict__ q,
-                                                       const uint16_t* __restrict__ kc,
-                                                       const uint16_t* __restrict__ vc,
-                                                       const int64_t* __restrict__ cu,
-                                                       const int32_t* __restrict__ block_idx, int H_kv, int kk,
-                                                       float scale_log2, float* __restrict__ Opart,
-                                                       float* __restrict__ Lpart) {
-  __shared__ float qs[G][kDh];
-  __shared__ float S[G][kBk];
-  __shared__ float red[4][G][kDh];
-  __shared__ float inv_l[G];
+__global__ __launch_bounds__(256, 4) void dec_attn_kernel(const uint16_t* __restrict__ q,
+                                                          const uint16_t* __restrict__ kc,
+                                                          const uint16_t* __restrict__ vc,
+                                                          const int64_t* __restrict__ cu,
+                                                          const int32_t* __restrict__ block_idx, int H_kv,
+                                                          int kk, float scale_log2, float* __restrict__ Opart,
+                                                          float* __restrict__ Lpart) {
+  static_assert(G <= 16, "the merge reuses the 32 KB V^T buffer: 4 x G x 128 fp32");
+  __shared__ __attribute__((aligned(16))) uint8_t Vt[kDh * 256];  // reused for the merge
+  __shared__ float wm[4][32], wl[4][32];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
   const int64_t task = blockIdx.x;  // (s * H_kv + r) * kk + slot
   const int64_t sr = task / kk;
   const int s = (int)(sr / H_kv), r = (int)(sr % H_kv);
@@ -140,87 +156,123 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(const uint16_t* __restric
     if (tid < G) lp[tid] = -__builtin_inff();
     return;
   }
-  const int64_t kb = (int64_t)b * kBk;
-  const int nkeys = (L - kb < kBk) ? (int)(L - kb) : kBk;
-  for (int e = tid; e < G * kDh; e += 256) {
-    const int g = e / kDh, d = e % kDh;
-    qs[g][d] = bf16_to_f32(q[((int64_t)s * H_q + r * G + g) * kDh + d]);
-  }
-  __syncthreads();
-  // Scores: thread pair (2 keys' halves) -> key = tid/2, dims 64*(tid&1) .. +63.
+  const int64_t kb0 = (int64_t)b * kBk;
+  const int nvalid = (L - kb0 < kBk) ? (int)(L - kb0) : kBk;
+  const int row_stride = H_kv * kDh;
+  const uint16_t* kblk = kc + ((j0 + kb0) * H_kv + r) * kDh;
+  // K operand of this lane: row l32 of the wave's tile is key 32w + swap23(l32)
+  // (the prefill LDS order), chunk 8h + t at step t; keys past the end are clamped
+  // here and masked after the scores.
+  u32x4_t ka[8];
   {
-    const int key = tid >> 1, half = tid & 1;
-    float acc[G];
+    const int key = 32 * wave + swap23(l32);
+    const uint16_t* kr = kblk + (key < nvalid ? key : nvalid - 1) * row_stride + 64 * h;
 #pragma unroll
-    for (int g = 0; g < G; ++g) acc[g] = 0.f;
-    if (key < nkeys) {
-      const uint16_t* kr = kc + ((j0 + kb + key) * H_kv + r) * kDh + 64 * half;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const uint4 u = *reinterpret_cast<const uint4*>(kr + 8 * c);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const float k0 = __uint_as_float(w[m] << 16), k1 = __uint_as_float(w[m] & 0xffff0000u);
-          const int d = 64 * half + 8 * c + 2 * m;
-#pragma unroll
-          for (int g = 0; g < G; ++g) acc[g] += qs[g][d] * k0 + qs[g][d + 1] * k1;
-        }
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float tot = acc[g] + __shfl_xor(acc[g], 1);
-      if (half == 0) S[g][key] = key < nkeys ? tot * scale_log2 : -__builtin_inff();
-    }
+    for (int t = 0; t < 8; ++t) ka[t] = ld16<false>(kr + 8 * t);
   }
-  __syncthreads();
-  // Softmax per head: wave w handles heads w, w+4, ...
-  for (int g = wave; g < G; g += 4) {
-    const float x0 = S[g][lane], x1 = S[g][lane + 64];
-    const float mx = wave_max(fmaxf(x0, x1));
-    const float p0 = exp2f(x0 - mx), p1 = exp2f(x1 - mx);
-    const float l = wave_sum(p0 + p1);
-    S[g][lane] = p0;
-    S[g][lane + 64] = p1;
-    if (lane == 0) {
-      inv_l[g] = 1.f / l;
-      lp[g] = (mx + __log2f(l)) * kLn2;
-    }
-  }
-  __syncthreads();
-  // P V: thread -> dims 2*(tid%64) .. +1, keys 32*(tid/64) .. +31.
+  stage_v<true>(vc + ((j0 + kb0) * H_kv + r) * kDh, row_stride, nvalid, Vt, tid);
+  // q operand: k-slot (h, e) of step t is dim 64h + 8t + e of head l32 (zero for
+  // the padding columns l32 >= G).
+  u32x4_t qop[8];
   {
-    const int dp = tid & 63, kq = tid >> 6;
-    float a0[G], a1[G];
+    const uint16_t* qr = q + ((int64_t)s * H_q + r * G + (l32 < G ? l32 : 0)) * kDh + 64 * h;
 #pragma unroll
-    for (int g = 0; g < G; ++g) a0[g] = a1[g] = 0.f;
-    for (int kk2 = 0; kk2 < 32; ++kk2) {
-      const int key = kq * 32 + kk2;
-      if (key >= nkeys) break;
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(vc + ((j0 + kb + key) * H_kv + r) * kDh + 2 * dp);
-      const float v0 = __uint_as_float(w << 16), v1 = __uint_as_float(w & 0xffff0000u);
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float p = S[g][key];
-        a0[g] += p * v0;
-        a1[g] += p * v1;
-      }
+    for (int t = 0; t < 8; ++t) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(qr + 8 * t);
+      qop[t] = l32 < G ? v : u32x4_t{0u, 0u, 0u, 0u};
     }
+  }
+
+  // S^T tile of this wave: element v is key 32*wave + 16(v/8) + 4((v/4)%2) + v%4 + 8h.
+  f32x16_t sacc = f32x16_t{};
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      red[kq][g][2 * dp] = a0[g];
-      red[kq][g][2 * dp + 1] = a1[g];
+  for (int t = 0; t < 8; ++t) sacc = mfma_32x32x16(as_bf16x8(ka[t]), as_bf16x8(qop[t]), sacc);
+  if (nvalid < kBk) {
+    const int lim = nvalid - 1 - 32 * wave - 8 * h;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int off = 16 * (v >> 3) + 4 * ((v >> 2) & 1) + (v & 3);
+      sacc[v] = off <= lim ? sacc[v] : -__builtin_inff();
+    }
+  }
+  float mx = -__builtin_inff();
+#pragma unroll
+  for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[v]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const bool empty = mx == -__builtin_inff();  // every key of this wave's tile is past the end
+  const float m2 = empty ? 0.f : mx * scale_log2;
+  float l = 0.f;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const float p = __builtin_amdgcn_exp2f(fmaf(sacc[v], scale_log2, -m2));
+    sacc[v] = p;
+    l += p;
+  }
+  l += __shfl_xor(l, 32);
+  u32x4_t pb[2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    pb[hf].x = pack_bf16x2(sacc[8 * hf + 0], sacc[8 * hf + 1]);
+    pb[hf].y = pack_bf16x2(sacc[8 * hf + 2], sacc[8 * hf + 3]);
+    pb[hf].z = pack_bf16x2(sacc[8 * hf + 4], sacc[8 * hf + 5]);
+    pb[hf].w = pack_bf16x2(sacc[8 * hf + 6], sacc[8 * hf + 7]);
+  }
+  __syncthreads();  // V^T staged
+  // O^T[d][head] over this wave's keys: steps u = 2*wave + hf, V^T chunk 2u + h.
+  f32x16_t oacc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x16_t{};
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const int kc2 = 2 * (2 * wave + hf) + h;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const int d = dt * 32 + l32;
+      const u32x4_t va = *reinterpret_cast<const u32x4_t*>(Vt + d * 256 + ((kc2 ^ (d & 15)) << 4));
+      oacc[dt] = mfma_32x32x16(as_bf16x8(va), as_bf16x8(pb[hf]), oacc[dt]);
+    }
+  }
+  if (h == 0) {
+    wm[wave][l32] = empty ? -__builtin_inff() : m2;
+    wl[wave][l32] = l;
+  }
+  __syncthreads();  // every wave is done with V^T
+  // Merge: the four waves' O^T for the G real heads, rescaled to the common max.
+  float* red = reinterpret_cast<float*>(Vt);  // [4][G][128]
+  if (l32 < G) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int d = 32 * dt + 8 * c + 4 * h;
+        *reinterpret_cast<f32x4_t*>(red + ((wave * G + l32) * kDh + d)) =
+            f32x4_t{oacc[dt][4 * c], oacc[dt][4 * c + 1], oacc[dt][4 * c + 2], oacc[dt][4 * c + 3]};
+      }
     }
   }
   __syncthreads();
   float* op = Opart + task * G * kDh;
   for (int e = tid; e < G * kDh; e += 256) {
     const int g = e / kDh, d = e % kDh;
-    op[e] = (red[0][g][d] + red[1][g][d] + red[2][g][d] + red[3][g][d]) * inv_l[g];
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w][g]);
+    float acc = 0.f, ls = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float wt = wm[w][g] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(wm[w][g] - M);
+      acc += wt * red[(w * G + g) * kDh + d];
+      ls += wt * wl[w][g];
+    }
+    op[e] = acc / ls;
+    if (d == 0) lp[g] = (M + __log2f(ls)) * kLn2;
   }
 }
 
+// LSE merge of the k slot partials of one (sequence, head) per wave.  Lane t < k
+// reads slot t's block index and LSE (validity, the common max and each slot's
+// weight are then wave reductions and lane reads); lane j then accumulates dims
+// 2j, 2j+1 over the slots, with every slot's row load independent of the others.
 __global__ __launch_bounds__(256) void dec_combine_kernel(const float* __restrict__ Opart,
                                                           const float* __restrict__ Lpart,
                                                           const int32_t* __restrict__ block_idx,
@@ -236,30 +288,30 @@ __global__ __launch_bounds__(256) void dec_combine_kernel(const float* __restric
   const int64_t L = cu[s + 1] - cu[s];
   const int64_t bl = L > 0 ? (L - 1) / kBk : -1;
   const int64_t sr = (int64_t)s * H_kv + r;
-  const int32_t* sel = block_idx + sr * kk;
-  float mstar = -__builtin_inff();
-  for (int t = 0; t < kk; ++t) {
-    const int b = sel[t];
-    if (b >= 0 && b <= bl) mstar = fmaxf(mstar, Lpart[(sr * kk + t) * G + g]);
-  }
+  const int t = lane < kk ? lane : 0;
+  const int b = block_idx[sr * kk + t];
+  const float ls = Lpart[(sr * kk + t) * G + g];
+  const bool valid = lane < kk && b >= 0 && b <= bl && ls != -__builtin_inff();
+  const float mstar = wave_max(valid ? ls : -__builtin_inff());
   float* orow = o + gw * kDh;
   if (mstar == -__builtin_inff()) {
     *reinterpret_cast<float2*>(orow + 2 * lane) = make_float2(0.f, 0.f);
     if (lane == 0) lse[gw] = -__builtin_inff();
     return;
   }
-  float a0 = 0.f, a1 = 0.f, Ls = 0.f;
-  for (int t = 0; t < kk; ++t) {
-    const int b = sel[t];
-    if (!(b >= 0 && b <= bl)) continue;
-    const int64_t prow = (sr * kk + t) * G + g;
-    const float ls = Lpart[prow];
-    if (ls == -__builtin_inff()) continue;
-    const float wgt = __expf(ls - mstar);
-    const float2 pv = *reinterpret_cast<const float2*>(Opart + prow * kDh + 2 * lane);
-    a0 += wgt * pv.x;
-    a1 += wgt * pv.y;
-    Ls += wgt;
+  const float wgt = valid ? __expf(ls - mstar) : 0.f;
+  const float Ls = wave_sum(wgt);
+  const uint64_t vm = __ballot(valid);
+  const int first = (int)__builtin_ctzll(vm);  // vm != 0 here
+  float a0 = 0.f, a1 = 0.f;
+  for (int u = 0; u < kk; ++u) {
+    const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), u));
+    // Rows of invalid slots were never written: read the first valid slot's row
+    // instead (weight 0).
+    const int us = ((vm >> u) & 1) ? u : first;
+    const float2 pv = *reinterpret_cast<const float2*>(Opart + ((sr * kk + us) * G + g) * kDh + 2 * lane);
+    a0 += wu * pv.x;
+    a1 += wu * pv.y;
   }
   const float inv = 1.f / Ls;
   *reinterpret_cast<float2*>(orow + 2 * lane) = make_float2(a0 * inv, a1 * inv);

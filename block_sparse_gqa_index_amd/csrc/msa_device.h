@@ -174,4 +174,80 @@ __device__ __forceinline__ void write_selection(int (&cand)[N], int k, int b_loc
   }
 }
 
+// ---------------------------------------------------------------------------------
+// K / V block staging shared by the prefill and decode attention kernels (256
+// threads).
+// LDS row rho of the staged K tile holds key swap23(rho) (bits 2 and 3 of the row
+// index exchanged).  With that order the 32x32 MFMA leaves, in each lane half, the
+// probabilities of 8 consecutive keys per PV step, so V^T is read 16 B at a time.
+__device__ __forceinline__ int swap23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
+
+// 16-byte load, optionally non-temporal (data read once).
+template <bool NT>
+__device__ __forceinline__ u32x4_t ld16(const uint16_t* p) {
+  if constexpr (NT)
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  else
+    return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+// K block -> LDS: row rho (256 B = 16 chunks of 16 B) holds key swap23(rho), chunk c
+// at position c ^ (rho & 15).  kb points at (token b*128, group r); keys past
+// `nvalid` read as zero.
+template <bool NT = false>
+__device__ __forceinline__ void stage_k(const uint16_t* __restrict__ kb, int row_stride, int nvalid, uint8_t* Ks,
+                                        int tid) {
+  const int c = tid & 15;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const int rho = (tid >> 4) + 16 * m;
+    const int key = swap23(rho);
+    const int kr = key < nvalid ? key : nvalid - 1;  // branch-free: clamp, then zero
+    u32x4_t val = ld16<NT>(kb + kr * row_stride + c * 8);
+    if (key >= nvalid) val = u32x4_t{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4_t*>(Ks + rho * 256 + ((c ^ (rho & 15)) << 4)) = val;
+  }
+}
+
+// V block -> LDS transposed: Vt[d] (256 B) holds keys in natural order, 8-key chunk
+// kc at position kc ^ (d & 15).  vb points at (token b*128, group r); keys past
+// `nvalid` read as zero.
+template <bool NT = false>
+__device__ __forceinline__ void stage_v(const uint16_t* __restrict__ vb, int row_stride, int nvalid, uint8_t* Vt,
+                                        int tid) {
+  // Thread owns keys kg*8 .. +7 x dims dc*8 .. +7, transposed in registers.
+  const int kg = tid & 15;
+  const int dc = tid >> 4;
+  uint32_t w[8][4];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int key = kg * 8 + e;
+    const int kr = key < nvalid ? key : nvalid - 1;
+    u32x4_t val = ld16<NT>(vb + kr * row_stride + dc * 8);
+    if (key >= nvalid) val = u32x4_t{0u, 0u, 0u, 0u};
+    w[e][0] = val.x;
+    w[e][1] = val.y;
+    w[e][2] = val.z;
+    w[e][3] = val.w;
+  }
+#pragma unroll
+  for (int f = 0; f < 8; ++f) {
+    // dim d = dc*8+f for keys kg*8 .. +7: 4 dwords of (key 2m, key 2m+1)
+    u32x4_t o4;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t a = w[2 * m][f >> 1], cc = w[2 * m + 1][f >> 1];
+      o4[m] = (f & 1) ? ((a >> 16) | (cc & 0xffff0000u)) : ((a & 0xffffu) | (cc << 16));
+    }
+    const int d = dc * 8 + f;
+    *reinterpret_cast<u32x4_t*>(Vt + d * 256 + ((kg ^ (d & 15)) << 4)) = o4;
+  }
+}
+
+__device__ __forceinline__ void stage_kv(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ vb,
+                                         int row_stride, int nvalid, uint8_t* Ks, uint8_t* Vt, int tid) {
+  stage_k(kb, row_stride, nvalid, Ks, tid);
+  stage_v(vb, row_stride, nvalid, Vt, tid);
+}
+
 }  // namespace msa
