@@ -89,7 +89,21 @@ __global__ __launch_bounds__(256) void dec_topk_kernel(const float* __restrict__
   TopList<LIST> list;
   list.init();
   const float* mrow = M + row * Bmax;
-  for (int64_t b = lane; b < bl; b += 64) list.offer(mrow[b], (int)b);
+  // Batches of 16 scores per lane are loaded before any is offered (the loads
+  // would otherwise wait one at a time behind the list updates).
+  for (int64_t b0 = 0; b0 < bl; b0 += 16 * 64) {
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int64_t b = b0 + lane + 64 * j;
+      v[j] = mrow[b < bl ? b : 0];
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int64_t b = b0 + lane + 64 * j;
+      if (b < bl) list.offer(v[j], (int)b);
+    }
+  }
   // k-1 rounds of wave arg-max over the list heads (ties: lower block index).
   int cand[LIST + 1];
 #pragma unroll

@@ -16,7 +16,7 @@ constexpr int kBlockKeys = 128;
 constexpr int kItemChunks = 16;
 
 struct AttnWorkspace {
-  size_t counts, cursor, n_items, items, pairs, opart, lpart, total;
+  size_t counts, tsum, cursor, n_items, items, pairs, opart, lpart, total;
   int64_t max_items;
   int item_q;  // queries per work item
   int64_t WQ;  // queries per q-locality window

@@ -59,49 +59,84 @@ __global__ __launch_bounds__(256) void inv_count_kernel(const int32_t* __restric
   }
 }
 
-// One workgroup: exclusive scans of the per-list pair counts and item counts, the
-// list offsets, the scatter cursors and the explicit item table.
-__global__ __launch_bounds__(1024) void inv_scan_kernel(const int32_t* __restrict__ counts, int64_t L,
-                                                        int item_q, int32_t* __restrict__ cursor,
-                                                        int4* __restrict__ items, int32_t* __restrict__ n_items) {
-  __shared__ int64_t sp[1024], si[1024];
-  const int t = threadIdx.x;
-  const int64_t per = (L + 1023) / 1024;
-  const int64_t l0 = t * per, l1 = (l0 + per < L) ? l0 + per : L;
-  int64_t ps = 0, is = 0;
-  for (int64_t l = l0; l < l1; ++l) {
-    const int c = counts[l];
-    ps += c;
-    is += (c + item_q - 1) / item_q;
-  }
-  sp[t] = ps;
-  si[t] = is;
+// Exclusive scans of the per-list pair counts and item counts, in two passes over
+// tiles of 1024 lists: per-tile sums, then per tile the offsets of the preceding
+// tiles plus a tile-local scan, which gives the list offsets, the scatter cursors
+// and the explicit item table.
+constexpr int kScanTile = 1024;
+
+// Inclusive sum over the 1024 threads of a workgroup (lds: 16 slots).
+__device__ __forceinline__ int64_t block_sum_1024(int64_t x, int64_t* lds) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m);
   __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    int64_t a = 0, bb = 0;
-    if (t >= off) {
-      a = sp[t - off];
-      bb = si[t - off];
-    }
-    __syncthreads();
-    sp[t] += a;
-    si[t] += bb;
-    __syncthreads();
+  if (lane == 0) lds[wave] = x;
+  __syncthreads();
+  int64_t t = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) t += lds[w];
+  return t;
+}
+
+// Exclusive scan over the 1024 threads of a workgroup (lds: 16 slots).
+__device__ __forceinline__ int64_t block_excl_scan_1024(int64_t x, int64_t* lds) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int64_t inc = x;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const int64_t y = __shfl_up(inc, m);
+    if (lane >= m) inc += y;
   }
-  int64_t poff = sp[t] - ps, ioff = si[t] - is;
-  for (int64_t l = l0; l < l1; ++l) {
-    const int c = counts[l];
+  __syncthreads();
+  if (lane == 63) lds[wave] = inc;
+  __syncthreads();
+  int64_t before = 0;
+  for (int w = 0; w < wave; ++w) before += lds[w];
+  return before + inc - x;
+}
+
+__global__ __launch_bounds__(kScanTile) void inv_tile_sums_kernel(const int32_t* __restrict__ counts, int64_t L,
+                                                                int item_q, int64_t* __restrict__ tsum) {
+  __shared__ int64_t lds[16];
+  const int64_t l = (int64_t)blockIdx.x * kScanTile + threadIdx.x;
+  const int c = l < L ? counts[l] : 0;
+  const int64_t p = block_sum_1024(c, lds);
+  const int64_t it = block_sum_1024((c + item_q - 1) / item_q, lds);
+  if (threadIdx.x == 0) {
+    tsum[2 * blockIdx.x] = p;
+    tsum[2 * blockIdx.x + 1] = it;
+  }
+}
+
+__global__ __launch_bounds__(kScanTile) void inv_scan_write_kernel(const int32_t* __restrict__ counts, int64_t L,
+                                                                 int item_q, const int64_t* __restrict__ tsum,
+                                                                 int32_t* __restrict__ cursor,
+                                                                 int4* __restrict__ items,
+                                                                 int32_t* __restrict__ n_items) {
+  __shared__ int64_t lds[16];
+  const int tile = blockIdx.x;
+  int64_t pp = 0, ip = 0;
+  for (int j = threadIdx.x; j < tile; j += kScanTile) {
+    pp += tsum[2 * j];
+    ip += tsum[2 * j + 1];
+  }
+  pp = block_sum_1024(pp, lds);
+  ip = block_sum_1024(ip, lds);
+  const int64_t l = (int64_t)tile * kScanTile + threadIdx.x;
+  const int c = l < L ? counts[l] : 0;
+  const int nit = (c + item_q - 1) / item_q;
+  const int64_t poff = pp + block_excl_scan_1024(c, lds);
+  const int64_t ioff = ip + block_excl_scan_1024(nit, lds);
+  if (l < L) {
     cursor[l] = (int32_t)poff;
-    const int nit = (c + item_q - 1) / item_q;
     for (int it = 0; it < nit; ++it) {
       const int start = (int)poff + it * item_q;
       const int cnt = (c - it * item_q < item_q) ? c - it * item_q : item_q;
       items[ioff + it] = make_int4((int)l, start, cnt, 0);
     }
-    poff += c;
-    ioff += nit;
   }
-  if (t == 1023) *n_items = (int32_t)si[1023];
+  if (l == L - 1) *n_items = (int32_t)(ioff + nit);
 }
 
 template <int PPT>
@@ -627,6 +662,7 @@ AttnWorkspace attn_workspace_layout(int64_t W, int H_q, int H_kv, int kk, int64_
     return o;
   };
   L.counts = take(sizeof(int32_t) * lists);
+  L.tsum = take(sizeof(int64_t) * 2 * ((lists + kScanTile - 1) / kScanTile));
   L.cursor = take(sizeof(int32_t) * lists);
   L.n_items = take(sizeof(int32_t) * 4);
   L.items = take(sizeof(int4) * max_items);
@@ -668,7 +704,12 @@ hipError_t launch_sparse_attn_window(const uint16_t* q, const uint16_t* k, const
   inv_count_kernel<<<igrid, dim3(256), lds_count, stream>>>(block_idx, w0, W, H_kv, kk, B, TQ, L.WQ, L.nW,
                                                              counts);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  inv_scan_kernel<<<dim3(1), dim3(1024), 0, stream>>>(counts, lists, L.item_q, cursor, items, n_items);
+  const unsigned tiles = (unsigned)((lists + kScanTile - 1) / kScanTile);
+  int64_t* tsum = reinterpret_cast<int64_t*>(ws + L.tsum);
+  inv_tile_sums_kernel<<<dim3(tiles), dim3(kScanTile), 0, stream>>>(counts, lists, L.item_q, tsum);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  inv_scan_write_kernel<<<dim3(tiles), dim3(kScanTile), 0, stream>>>(counts, lists, L.item_q, tsum, cursor, items,
+                                                                    n_items);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   inv_scatter_kernel<16><<<igrid, dim3(256), 2 * lds_count, stream>>>(block_idx, w0, W, H_kv, kk, B, TQ, L.WQ,
                                                                       L.nW, cursor, pairs);
