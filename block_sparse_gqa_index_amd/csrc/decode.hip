@@ -11,9 +11,10 @@
 //      token); 16x16x32 MFMAs give all groups' scores, max-pooled per block.
 //   2. top-k: one wave per (sequence, group); per-lane register lists over a
 //      strided share of the blocks, merged by k-1 rounds of wave arg-max.
-//   3. split-K attention: one workgroup per (sequence, group, chosen block)
-//      streams that block's K/V (64 KB) once for the G heads of the group.
-//   4. combine: LSE merge of the k partials per (sequence, head).
+//   3. split-K attention: one workgroup per (sequence, group, part of up to 8
+//      chosen blocks) streams those blocks' K/V (64 KB each) once for the G heads
+//      of the group, with an online softmax across the part's blocks.
+//   4. combine: LSE merge of the parts per (sequence, head).
 #include "msa_device.h"
 #include "msa_kernels.h"
 
@@ -70,18 +71,22 @@ __global__ __launch_bounds__(256) void dec_score_kernel(const uint16_t* __restri
   if (lane < 16 && col < H_kv) M[((int64_t)s * H_kv + col) * Bmax + b] = runmax * 0.125f;
 }
 
+// Top-k of one (sequence, group) row per workgroup: wave w offers blocks
+// 64j + lane with (j % 4) == w to per-lane register lists, extracts its k-1 best
+// by k-1 rounds of wave arg-max, and the four waves' candidates are merged by
+// wave 0 the same way.  The local (last) block is then added.
 template <int LIST>
 __global__ __launch_bounds__(256) void dec_topk_kernel(const float* __restrict__ M, const int64_t* __restrict__ cu,
                                                        int batch, int H_kv, int64_t Bmax, int k,
                                                        int32_t* __restrict__ block_idx) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= (int64_t)batch * H_kv) return;
+  __shared__ uint64_t cand[4][LIST];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t row = blockIdx.x;
   const int s = (int)(row / H_kv);
   const int64_t L = cu[s + 1] - cu[s];
   int32_t* out = block_idx + row * k;
   if (L <= 0) {
-    for (int t = lane; t < k; t += 64) out[t] = -1;
+    for (int t = threadIdx.x; t < k; t += 256) out[t] = -1;
     return;
   }
   int64_t bl = (L - 1) / kBk;
@@ -89,168 +94,240 @@ __global__ __launch_bounds__(256) void dec_topk_kernel(const float* __restrict__
   TopList<LIST> list;
   list.init();
   const float* mrow = M + row * Bmax;
-  // Batches of 16 scores per lane are loaded before any is offered (the loads
-  // would otherwise wait one at a time behind the list updates).
-  for (int64_t b0 = 0; b0 < bl; b0 += 16 * 64) {
-    float v[16];
+  // Scores are loaded in batches of 8 per lane before any is offered.
+  for (int64_t b0 = 64 * wave; b0 < bl; b0 += 8 * 256) {
+    float v[8];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int64_t b = b0 + lane + 64 * j;
+    for (int j = 0; j < 8; ++j) {
+      const int64_t b = b0 + lane + 256 * j;
       v[j] = mrow[b < bl ? b : 0];
     }
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int64_t b = b0 + lane + 64 * j;
+    for (int j = 0; j < 8; ++j) {
+      const int64_t b = b0 + lane + 256 * j;
       if (b < bl) list.offer(v[j], (int)b);
     }
   }
-  // k-1 rounds of wave arg-max over the list heads (ties: lower block index).
-  int cand[LIST + 1];
+  // This wave's k-1 best, best first.
 #pragma unroll
-  for (int t = 0; t <= LIST; ++t) cand[t] = 0x7fffffff;
+  for (int t = 0; t < LIST; ++t) {
+    uint64_t best = 0;
+    if (t < k - 1) {
+      const uint64_t mine = rank_key(list.v[0], list.b[0]);
+      best = wave_max_u64(mine);
+      if (best != 0 && mine == best) list.pop();
+    }
+    if (lane == 0) cand[wave][t] = best;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  // Merge: candidate c = LIST*w + t (wave w's t-th) sits in lane c % 64, slot c / 64
+  // (at most 4*31 = 124 candidates); the waves' blocks are disjoint.
+  const uint64_t* flat = &cand[0][0];
+  const uint64_t c0 = lane < 4 * LIST ? flat[lane] : 0, c1 = lane + 64 < 4 * LIST ? flat[lane + 64] : 0;
+  uint64_t hi = c0 > c1 ? c0 : c1, lo = c0 > c1 ? c1 : c0;
+  int sel[LIST + 1];
+#pragma unroll
+  for (int t = 0; t <= LIST; ++t) sel[t] = 0x7fffffff;
 #pragma unroll
   for (int t = 0; t < LIST; ++t) {
     if (t < k - 1) {
-      float bv = list.v[0];
-      int bb = list.b[0];
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) {
-        const float ov = __shfl_xor(bv, m);
-        const int ob = __shfl_xor(bb, m);
-        const bool take = (ob >= 0) && (bb < 0 || ov > bv || (ov == bv && ob < bb));
-        bv = take ? ov : bv;
-        bb = take ? ob : bb;
-      }
-      if (bb >= 0) {
-        cand[t] = bb;
-        if (list.b[0] == bb) list.pop();
+      const uint64_t best = wave_max_u64(hi);
+      if (best != 0) {
+        sel[t] = rank_key_block(best);
+        if (hi == best) {
+          hi = lo;
+          lo = 0;
+        }
       }
     }
   }
   if (lane == 0) {
     int32_t o[LIST + 1];
-    write_selection<LIST + 1>(cand, k, (int)bl, o);
+    write_selection<LIST + 1>(sel, k, (int)bl, o);
 #pragma unroll
     for (int t = 0; t <= LIST; ++t)
       if (t < k) out[t] = o[t];
   }
 }
 
-// Split-K attention for one (sequence, group, slot): the G heads of the group
-// against one block of up to 128 keys, on 32x32x16 bf16 MFMAs.  Wave w takes keys
-// 32w .. 32w+31: it reads its K rows straight into MFMA operands (S^T = K Q^T,
-// heads as the 32 MFMA columns, G of them real), takes the softmax with its own
-// max, and computes O^T = V^T P^T from the block's V^T, which the workgroup stages
-// in LDS with coalesced 16-byte loads (non-temporal: V is read once per step).
-// The four waves' (max, sum, O) are merged in LDS (rescaled to
-// the common max) and the normalised partial plus its natural-log LSE is written.
-// 33 KB of LDS per workgroup: four workgroups per CU keep the loads in flight.
+// Split-K attention: one workgroup per (sequence, group, part), a part being up
+// to kDecSlotsPerPart of the row's selected blocks; parts are merged by the
+// combine kernel.  The G heads of the group are the (32, G real) MFMA columns of
+// 32x32x16 bf16 MFMAs.  Wave w takes keys 32w .. 32w+31 of every block: it reads
+// its K rows straight into MFMA operands (S^T = K Q^T), keeps a running max, sum
+// and output over the part's blocks (online softmax, base 2), and computes
+// O^T = V^T P^T from the block's V^T, which the workgroup stages in LDS.  While a
+// block is computed the next block's K and V are already being loaded into
+// registers.  At the end the four waves' (max, sum, O) are merged in LDS
+// (rescaled to the common max) and the normalised partial with its natural-log
+// LSE is written (LSE -inf: the part attended to nothing).
+constexpr int kDecSlotsPerPart = 8;
+
 template <int G>
-__global__ __launch_bounds__(256, 4) void dec_attn_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(256, 2) void dec_attn_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ kc,
                                                           const uint16_t* __restrict__ vc,
                                                           const int64_t* __restrict__ cu,
                                                           const int32_t* __restrict__ block_idx, int H_kv,
-                                                          int kk, float scale_log2, float* __restrict__ Opart,
-                                                          float* __restrict__ Lpart) {
+                                                          int kk, int nparts, float scale_log2,
+                                                          float* __restrict__ Opart, float* __restrict__ Lpart) {
   static_assert(G <= 16, "the merge reuses the 32 KB V^T buffer: 4 x G x 128 fp32");
   __shared__ __attribute__((aligned(16))) uint8_t Vt[kDh * 256];  // reused for the merge
   __shared__ float wm[4][32], wl[4][32];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
-  const int64_t task = blockIdx.x;  // (s * H_kv + r) * kk + slot
-  const int64_t sr = task / kk;
+  const int64_t task = blockIdx.x;  // (s * H_kv + r) * nparts + part
+  const int64_t sr = task / nparts;
+  const int part = (int)(task % nparts);
   const int s = (int)(sr / H_kv), r = (int)(sr % H_kv);
   const int64_t j0 = cu[s];
   const int64_t L = cu[s + 1] - j0;
-  const int b = block_idx[task];
   const int H_q = H_kv * G;
+  const int row_stride = H_kv * kDh;
+  const int32_t* sel = block_idx + sr * kk;
+  const int t0 = part * kDecSlotsPerPart;
+  const int t1 = (t0 + kDecSlotsPerPart < kk) ? t0 + kDecSlotsPerPart : kk;
+  const int64_t bl = L > 0 ? (L - 1) / kBk : -1;
+  // Next selected, valid slot at or after t (t1 if none); uniform.
+  auto next_valid = [&](int t) {
+    while (t < t1 && !(sel[t] >= 0 && sel[t] <= bl)) ++t;
+    return t;
+  };
+  int t = next_valid(t0);
   float* lp = Lpart + task * G;
-  if (L <= 0 || b < 0 || (int64_t)b > (L - 1) / kBk) {
+  if (t >= t1) {
     if (tid < G) lp[tid] = -__builtin_inff();
     return;
   }
-  const int64_t kb0 = (int64_t)b * kBk;
-  const int nvalid = (L - kb0 < kBk) ? (int)(L - kb0) : kBk;
-  const int row_stride = H_kv * kDh;
-  const uint16_t* kblk = kc + ((j0 + kb0) * H_kv + r) * kDh;
-  // K operand of this lane: row l32 of the wave's tile is key 32w + swap23(l32)
-  // (the prefill LDS order), chunk 8h + t at step t; keys past the end are clamped
-  // here and masked after the scores.
-  u32x4_t ka[8];
-  {
+  // Loads of one block into registers: this lane's K operand rows (row l32 of the
+  // wave's tile is key 32w + swap23(l32), chunk 8h + t at step t; keys past the end
+  // clamped, masked after the scores) and its share of V (8 keys x 8 dims).
+  u32x4_t ka[8], vr[8];
+  auto load_block = [&](int b) {
+    const int64_t kb0 = (int64_t)b * kBk;
+    const int nvalid = (L - kb0 < kBk) ? (int)(L - kb0) : kBk;
+    const int64_t base = ((j0 + kb0) * H_kv + r) * kDh;
     const int key = 32 * wave + swap23(l32);
-    const uint16_t* kr = kblk + (key < nvalid ? key : nvalid - 1) * row_stride + 64 * h;
+    const uint16_t* kr = kc + base + (int64_t)(key < nvalid ? key : nvalid - 1) * row_stride + 64 * h;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) ka[t] = ld16<false>(kr + 8 * t);
-  }
-  stage_v<true>(vc + ((j0 + kb0) * H_kv + r) * kDh, row_stride, nvalid, Vt, tid);
-  // q operand: k-slot (h, e) of step t is dim 64h + 8t + e of head l32 (zero for
+    for (int st = 0; st < 8; ++st) ka[st] = ld16<false>(kr + 8 * st);
+    const int kg = tid & 15, dc = tid >> 4;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int kv = kg * 8 + e;
+      vr[e] = ld16<true>(vc + base + (int64_t)(kv < nvalid ? kv : nvalid - 1) * row_stride + dc * 8);
+      if (kv >= nvalid) vr[e] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
+  // V^T to LDS from the registers: Vt[d] (256 B) holds keys in natural order,
+  // 8-key chunk kc at position kc ^ (d & 15).
+  auto store_vt = [&]() {
+    const int kg = tid & 15, dc = tid >> 4;
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+      u32x4_t o4;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t x = vr[2 * m][f >> 1], y = vr[2 * m + 1][f >> 1];
+        o4[m] = (f & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
+      }
+      const int d = dc * 8 + f;
+      *reinterpret_cast<u32x4_t*>(Vt + d * 256 + ((kg ^ (d & 15)) << 4)) = o4;
+    }
+  };
+  // q operand: k-slot (h, e) of step st is dim 64h + 8st + e of head l32 (zero for
   // the padding columns l32 >= G).
   u32x4_t qop[8];
   {
     const uint16_t* qr = q + ((int64_t)s * H_q + r * G + (l32 < G ? l32 : 0)) * kDh + 64 * h;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(qr + 8 * t);
-      qop[t] = l32 < G ? v : u32x4_t{0u, 0u, 0u, 0u};
+    for (int st = 0; st < 8; ++st) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(qr + 8 * st);
+      qop[st] = l32 < G ? v : u32x4_t{0u, 0u, 0u, 0u};
     }
   }
-
-  // S^T tile of this wave: element v is key 32*wave + 16(v/8) + 4((v/4)%2) + v%4 + 8h.
-  f32x16_t sacc = f32x16_t{};
-#pragma unroll
-  for (int t = 0; t < 8; ++t) sacc = mfma_32x32x16(as_bf16x8(ka[t]), as_bf16x8(qop[t]), sacc);
-  if (nvalid < kBk) {
-    const int lim = nvalid - 1 - 32 * wave - 8 * h;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int off = 16 * (v >> 3) + 4 * ((v >> 2) & 1) + (v & 3);
-      sacc[v] = off <= lim ? sacc[v] : -__builtin_inff();
-    }
-  }
-  float mx = -__builtin_inff();
-#pragma unroll
-  for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[v]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const bool empty = mx == -__builtin_inff();  // every key of this wave's tile is past the end
-  const float m2 = empty ? 0.f : mx * scale_log2;
-  float l = 0.f;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const float p = __builtin_amdgcn_exp2f(fmaf(sacc[v], scale_log2, -m2));
-    sacc[v] = p;
-    l += p;
-  }
-  l += __shfl_xor(l, 32);
-  u32x4_t pb[2];
-#pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
-    pb[hf].x = pack_bf16x2(sacc[8 * hf + 0], sacc[8 * hf + 1]);
-    pb[hf].y = pack_bf16x2(sacc[8 * hf + 2], sacc[8 * hf + 3]);
-    pb[hf].z = pack_bf16x2(sacc[8 * hf + 4], sacc[8 * hf + 5]);
-    pb[hf].w = pack_bf16x2(sacc[8 * hf + 6], sacc[8 * hf + 7]);
-  }
-  __syncthreads();  // V^T staged
-  // O^T[d][head] over this wave's keys: steps u = 2*wave + hf, V^T chunk 2u + h.
+  int b = sel[t];
+  load_block(b);
+  store_vt();
+  float m_run = -__builtin_inff(), l_run = 0.f;  // base-2 scaled max, sum (per column)
   f32x16_t oacc[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x16_t{};
+  while (true) {
+    const int64_t kb0 = (int64_t)b * kBk;
+    const int nvalid = (L - kb0 < kBk) ? (int)(L - kb0) : kBk;
+    const int tn = next_valid(t + 1);
+    const int bn = tn < t1 ? sel[tn] : b;
+    __syncthreads();  // V^T of this block staged
+
+    // S^T tile of this wave: element v is key 32w + 16(v/8) + 4((v/4)%2) + v%4 + 8h.
+    f32x16_t sacc = f32x16_t{};
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
-    const int kc2 = 2 * (2 * wave + hf) + h;
+    for (int st = 0; st < 8; ++st) sacc = mfma_32x32x16(as_bf16x8(ka[st]), as_bf16x8(qop[st]), sacc);
+    // The K registers are consumed and this block's V is in LDS: the next block's
+    // loads go in flight while the softmax and PV run.
+    if (tn < t1) load_block(bn);
+    if (nvalid < kBk) {
+      const int lim = nvalid - 1 - 32 * wave - 8 * h;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int off = 16 * (v >> 3) + 4 * ((v >> 2) & 1) + (v & 3);
+        sacc[v] = off <= lim ? sacc[v] : -__builtin_inff();
+      }
+    }
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[v]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx == -__builtin_inff() ? -__builtin_inff() : mx * scale_log2);
+    // Rescale what was accumulated so far (nothing to rescale while m_run = -inf).
+    const float alpha = m_run == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    const float msub = m_new == -__builtin_inff() ? 0.f : m_new;
+    float lt = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(sacc[v], scale_log2, -msub));
+      sacc[v] = p;
+      lt += p;
+    }
+    lt += __shfl_xor(lt, 32);
+    l_run = l_run * alpha + lt;
+    m_run = m_new;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-      const int d = dt * 32 + l32;
-      const u32x4_t va = *reinterpret_cast<const u32x4_t*>(Vt + d * 256 + ((kc2 ^ (d & 15)) << 4));
-      oacc[dt] = mfma_32x32x16(as_bf16x8(va), as_bf16x8(pb[hf]), oacc[dt]);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
     }
+    u32x4_t pb[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      pb[hf].x = pack_bf16x2(sacc[8 * hf + 0], sacc[8 * hf + 1]);
+      pb[hf].y = pack_bf16x2(sacc[8 * hf + 2], sacc[8 * hf + 3]);
+      pb[hf].z = pack_bf16x2(sacc[8 * hf + 4], sacc[8 * hf + 5]);
+      pb[hf].w = pack_bf16x2(sacc[8 * hf + 6], sacc[8 * hf + 7]);
+    }
+    // O^T[d][head] += V^T P^T over this wave's keys: steps u = 2w + hf, V^T chunk 2u + h.
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int kc2 = 2 * (2 * wave + hf) + h;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const int d = dt * 32 + l32;
+        const u32x4_t va = *reinterpret_cast<const u32x4_t*>(Vt + d * 256 + ((kc2 ^ (d & 15)) << 4));
+        oacc[dt] = mfma_32x32x16(as_bf16x8(va), as_bf16x8(pb[hf]), oacc[dt]);
+      }
+    }
+    __syncthreads();  // every wave is done with this block's V^T
+    if (tn >= t1) break;
+    store_vt();
+    t = tn;
+    b = bn;
   }
   if (h == 0) {
-    wm[wave][l32] = empty ? -__builtin_inff() : m2;
-    wl[wave][l32] = l;
+    wm[wave][l32] = m_run;
+    wl[wave][l32] = l_run;
   }
-  __syncthreads();  // every wave is done with V^T
   // Merge: the four waves' O^T for the G real heads, rescaled to the common max.
   float* red = reinterpret_cast<float*>(Vt);  // [4][G][128]
   if (l32 < G) {
@@ -283,15 +360,12 @@ __global__ __launch_bounds__(256, 4) void dec_attn_kernel(const uint16_t* __rest
   }
 }
 
-// LSE merge of the k slot partials of one (sequence, head) per wave.  Lane t < k
-// reads slot t's block index and LSE (validity, the common max and each slot's
-// weight are then wave reductions and lane reads); lane j then accumulates dims
-// 2j, 2j+1 over the slots, with every slot's row load independent of the others.
+// LSE merge of the parts of one (sequence, head) per wave: lane p < nparts reads
+// part p's LSE (-inf: the part attended to nothing); the common max and each part's
+// weight are wave reductions and lane reads; lane j then accumulates dims 2j, 2j+1.
 __global__ __launch_bounds__(256) void dec_combine_kernel(const float* __restrict__ Opart,
-                                                          const float* __restrict__ Lpart,
-                                                          const int32_t* __restrict__ block_idx,
-                                                          const int64_t* __restrict__ cu, int batch, int H_kv,
-                                                          int G, int kk, float* __restrict__ o,
+                                                          const float* __restrict__ Lpart, int batch, int H_kv,
+                                                          int G, int nparts, float* __restrict__ o,
                                                           float* __restrict__ lse) {
   const int lane = threadIdx.x & 63;
   const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -299,14 +373,10 @@ __global__ __launch_bounds__(256) void dec_combine_kernel(const float* __restric
   if (gw >= (int64_t)batch * H_q) return;
   const int s = (int)(gw / H_q), hh = (int)(gw % H_q);
   const int r = hh / G, g = hh % G;
-  const int64_t L = cu[s + 1] - cu[s];
-  const int64_t bl = L > 0 ? (L - 1) / kBk : -1;
   const int64_t sr = (int64_t)s * H_kv + r;
-  const int t = lane < kk ? lane : 0;
-  const int b = block_idx[sr * kk + t];
-  const float ls = Lpart[(sr * kk + t) * G + g];
-  const bool valid = lane < kk && b >= 0 && b <= bl && ls != -__builtin_inff();
-  const float mstar = wave_max(valid ? ls : -__builtin_inff());
+  const float ls = lane < nparts ? Lpart[(sr * nparts + lane) * G + g] : -__builtin_inff();
+  const bool valid = ls != -__builtin_inff();
+  const float mstar = wave_max(ls);
   float* orow = o + gw * kDh;
   if (mstar == -__builtin_inff()) {
     *reinterpret_cast<float2*>(orow + 2 * lane) = make_float2(0.f, 0.f);
@@ -318,12 +388,11 @@ __global__ __launch_bounds__(256) void dec_combine_kernel(const float* __restric
   const uint64_t vm = __ballot(valid);
   const int first = (int)__builtin_ctzll(vm);  // vm != 0 here
   float a0 = 0.f, a1 = 0.f;
-  for (int u = 0; u < kk; ++u) {
+  for (int u = 0; u < nparts; ++u) {
     const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), u));
-    // Rows of invalid slots were never written: read the first valid slot's row
-    // instead (weight 0).
+    // Empty parts wrote no row: read the first non-empty part's row (weight 0).
     const int us = ((vm >> u) & 1) ? u : first;
-    const float2 pv = *reinterpret_cast<const float2*>(Opart + ((sr * kk + us) * G + g) * kDh + 2 * lane);
+    const float2 pv = *reinterpret_cast<const float2*>(Opart + ((sr * nparts + us) * G + g) * kDh + 2 * lane);
     a0 += wu * pv.x;
     a1 += wu * pv.y;
   }
@@ -344,8 +413,9 @@ DecodeWorkspace decode_workspace_layout(int batch, int H_q, int H_kv, int kk, in
     return o;
   };
   L.M = take(sizeof(float) * (size_t)batch * H_kv * Bmax);
-  L.opart = take(sizeof(float) * (size_t)batch * H_kv * kk * G * kDh);
-  L.lpart = take(sizeof(float) * (size_t)batch * H_kv * kk * G);
+  const int nparts = (kk + kDecSlotsPerPart - 1) / kDecSlotsPerPart;
+  L.opart = take(sizeof(float) * (size_t)batch * H_kv * nparts * G * kDh);
+  L.lpart = take(sizeof(float) * (size_t)batch * H_kv * nparts * G);
   L.total = off;
   return L;
 }
@@ -362,7 +432,7 @@ hipError_t launch_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_
   dec_score_kernel<<<dim3((unsigned)batch, (unsigned)((Bmax + kScoreBlocksPerWG - 1) / kScoreBlocksPerWG)),
                      dim3(256), 0, stream>>>(q_idx, k_idx_cache, cu, H_kv, Bmax, M);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const unsigned rows_grid = (unsigned)(((int64_t)batch * H_kv + 3) / 4);
+  const unsigned rows_grid = (unsigned)((int64_t)batch * H_kv);
   if (kk <= 8)
     dec_topk_kernel<7><<<dim3(rows_grid), dim3(256), 0, stream>>>(M, cu, batch, H_kv, Bmax, kk, block_idx);
   else if (kk <= 16)
@@ -371,12 +441,13 @@ hipError_t launch_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_
     dec_topk_kernel<31><<<dim3(rows_grid), dim3(256), 0, stream>>>(M, cu, batch, H_kv, Bmax, kk, block_idx);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const float scale_log2 = scale * kLog2e;
-  const unsigned tasks = (unsigned)((int64_t)batch * H_kv * kk);
+  const int nparts = (kk + kDecSlotsPerPart - 1) / kDecSlotsPerPart;
+  const unsigned tasks = (unsigned)((int64_t)batch * H_kv * nparts);
   switch (G) {
 #define MSA_DEC_CASE(GG)                                                                              \
   case GG:                                                                                            \
     dec_attn_kernel<GG><<<dim3(tasks), dim3(256), 0, stream>>>(q, k_cache, v_cache, cu, block_idx, H_kv, \
-                                                               kk, scale_log2, opart, lpart);          \
+                                                               kk, nparts, scale_log2, opart, lpart);  \
     break;
     MSA_DEC_CASE(1)
     MSA_DEC_CASE(2)
@@ -389,8 +460,8 @@ hipError_t launch_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t waves = (int64_t)batch * H_q;
-  dec_combine_kernel<<<dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream>>>(opart, lpart, block_idx, cu,
-                                                                                  batch, H_kv, G, kk, o, lse);
+  dec_combine_kernel<<<dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream>>>(opart, lpart, batch, H_kv, G,
+                                                                                  nparts, o, lse);
   return hipGetLastError();
 }
 

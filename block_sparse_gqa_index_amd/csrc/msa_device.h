@@ -107,6 +107,29 @@ struct TopList {
   }
 };
 
+// Wave-wide maximum of a 64-bit key, returned to every lane, with DPP lane moves
+// (register-speed) instead of LDS shuffles: quad xor 1 and xor 2, half-row and row
+// mirrors, then the row broadcasts 15 and 31 leave the maximum in lane 63.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
+  const int lo = (int)(uint32_t)x, hi = (int)(uint32_t)(x >> 32);
+  const uint32_t nlo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROW_MASK, 0xf, false);
+  const uint32_t nhi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROW_MASK, 0xf, false);
+  return ((uint64_t)nhi << 32) | nlo;
+}
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
+  x = max_u64(x, dpp_u64<0xB1, 0xf>(x));   // quad_perm [1,0,3,2]
+  x = max_u64(x, dpp_u64<0x4E, 0xf>(x));   // quad_perm [2,3,0,1]
+  x = max_u64(x, dpp_u64<0x141, 0xf>(x));  // row_half_mirror
+  x = max_u64(x, dpp_u64<0x140, 0xf>(x));  // row_mirror
+  x = max_u64(x, dpp_u64<0x142, 0xa>(x));  // row_bcast:15 into rows 1 and 3
+  x = max_u64(x, dpp_u64<0x143, 0xc>(x));  // row_bcast:31 into rows 2 and 3
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 // (value, block) packed so that a larger key means a better entry: value
 // descending, then block ascending; empty entries (block < 0) get key 0.
 __device__ __forceinline__ uint64_t rank_key(float v, int blk) {
