@@ -641,9 +641,11 @@ static int inv_tile_queries(int kk) {
 
 AttnWorkspace attn_workspace_layout(int64_t W, int H_q, int H_kv, int kk, int64_t B) {
   AttnWorkspace L{};
-  // q-locality window: about 128 pairs per (group, window, block) list on average,
-  // a multiple of 4096 queries (so every inverse-index tile lies in one window).
-  int64_t WQ = ((8 * B + 4095) / 4096) * 4096;
+  // q-locality window of 64*B queries (a multiple of 4096, so every inverse-index
+  // tile lies in one window): each K/V block is staged once per (group, window)
+  // list, so fewer, longer lists cut the staging traffic; measured at 128K, 64*B
+  // (two windows) beat 8*B (16 windows) by 6% and equals a single window.
+  int64_t WQ = ((64 * B + 4095) / 4096) * 4096;
   if (WQ > W) WQ = ((W + 4095) / 4096) * 4096;
   L.WQ = WQ;
   L.nW = (int)((W + WQ - 1) / WQ);
