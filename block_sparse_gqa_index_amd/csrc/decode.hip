@@ -28,6 +28,7 @@ __global__ __launch_bounds__(256) void dec_score_kernel(const uint16_t* __restri
                                                         const uint16_t* __restrict__ k_idx,
                                                         const int64_t* __restrict__ cu, int H_kv, int64_t Bmax,
                                                         float* __restrict__ M) {
+  __shared__ __attribute__((aligned(16))) uint8_t kstage[kScoreBlocksPerWG][64 * 128];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int s = blockIdx.x;
   const int64_t j0 = cu[s];
@@ -42,28 +43,43 @@ __global__ __launch_bounds__(256) void dec_score_kernel(const uint16_t* __restri
     qop[ks] = col < H_kv ? *reinterpret_cast<const uint4*>(q_idx + ((int64_t)s * H_kv + col) * kDidx + ks * 32 + 8 * grp)
                          : make_uint4(0, 0, 0, 0);
   // The block's 128 index keys (16 KB, read once per step: non-temporal) are all
-  // requested before the first MFMA.  Keys past the sequence end re-read its last
+  // requested before the first MFMA, fully coalesced: load j of lane l reads
+  // 16-byte chunk l%8 of row 8j + l/8.  Keys past the sequence end re-read its last
   // key (a valid address); their scores are masked below.
-  u32x4_t ka[8][2];
+  u32x4_t raw[16];
 #pragma unroll
-  for (int kt = 0; kt < 8; ++kt) {
-    const int64_t key = b * kBk + kt * 16 + col;  // this lane's A row
+  for (int j = 0; j < 16; ++j) {
+    const int64_t key = b * kBk + 8 * j + (lane >> 3);
     const int64_t kr = key < L ? key : L - 1;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      ka[kt][ks] = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4_t*>(k_idx + (j0 + kr) * kDidx + ks * 32 + 8 * grp));
+    raw[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(k_idx + (j0 + kr) * kDidx + (lane & 7) * 8));
   }
+  // Half a block at a time through the wave's LDS buffer into the MFMA operand
+  // layout (lane (col, grp) holds row col of a 16-row tile, dims 32ks + 8grp ..
+  // +7): row rr of the half at rr*128, chunk c at position c ^ (rr & 7).
+  uint8_t* st = kstage[wave];
   float runmax = -__builtin_inff();
 #pragma unroll
-  for (int kt = 0; kt < 8; ++kt) {
-    f32x4_t acc = {};
+  for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) acc = mfma_16x16x32(as_bf16x8(ka[kt][ks]), as_bf16x8(qop[ks]), acc);
+    for (int jj = 0; jj < 8; ++jj) {
+      const int rr = 8 * jj + (lane >> 3);
+      *reinterpret_cast<u32x4_t*>(st + rr * 128 + (((lane & 7) ^ (rr & 7)) << 4)) = raw[8 * hf + jj];
+    }
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t pos = b * kBk + kt * 16 + 4 * grp + v;
-      runmax = fmaxf(runmax, pos < L ? acc[v] : -__builtin_inff());
+    for (int kt = 0; kt < 4; ++kt) {
+      const int rr = 16 * kt + col;
+      f32x4_t acc = {};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int c = 4 * ks + grp;
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(st + rr * 128 + ((c ^ (rr & 7)) << 4));
+        acc = mfma_16x16x32(as_bf16x8(a), as_bf16x8(qop[ks]), acc);
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t pos = b * kBk + 64 * hf + kt * 16 + 4 * grp + v;
+        runmax = fmaxf(runmax, pos < L ? acc[v] : -__builtin_inff());
+      }
     }
   }
   runmax = fmaxf(runmax, __shfl_xor(runmax, 16));
@@ -154,12 +170,11 @@ __global__ __launch_bounds__(256) void dec_topk_kernel(const float* __restrict__
 // Split-K attention: one workgroup per (sequence, group, part), a part being up
 // to kDecSlotsPerPart of the row's selected blocks; parts are merged by the
 // combine kernel.  The G heads of the group are the (32, G real) MFMA columns of
-// 32x32x16 bf16 MFMAs.  Wave w takes keys 32w .. 32w+31 of every block: it reads
-// its K rows straight into MFMA operands (S^T = K Q^T), keeps a running max, sum
-// and output over the part's blocks (online softmax, base 2), and computes
-// O^T = V^T P^T from the block's V^T, which the workgroup stages in LDS.  While a
-// block is computed the next block's K and V are already being loaded into
-// registers.  At the end the four waves' (max, sum, O) are merged in LDS
+// 32x32x16 bf16 MFMAs.  The workgroup stages each block's K and V^T in LDS from
+// coalesced loads (the prefill layouts); while a block is computed the next
+// block's K and V are already being loaded into registers.  Wave w takes keys
+// 32w .. 32w+31 of every block (S^T = K Q^T), keeps a running max, sum and output
+// over the part's blocks (online softmax, base 2) and computes O^T = V^T P^T.  At the end the four waves' (max, sum, O) are merged in LDS
 // (rescaled to the common max) and the normalised partial with its natural-log
 // LSE is written (LSE -inf: the part attended to nothing).
 constexpr int kDecSlotsPerPart = 8;
@@ -173,6 +188,7 @@ __global__ __launch_bounds__(256, 2) void dec_attn_kernel(const uint16_t* __rest
                                                           int kk, int nparts, float scale_log2,
                                                           float* __restrict__ Opart, float* __restrict__ Lpart) {
   static_assert(G <= 16, "the merge reuses the 32 KB V^T buffer: 4 x G x 128 fp32");
+  __shared__ __attribute__((aligned(16))) uint8_t Ks[kBk * 256];
   __shared__ __attribute__((aligned(16))) uint8_t Vt[kDh * 256];  // reused for the merge
   __shared__ float wm[4][32], wl[4][32];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -200,18 +216,21 @@ __global__ __launch_bounds__(256, 2) void dec_attn_kernel(const uint16_t* __rest
     if (tid < G) lp[tid] = -__builtin_inff();
     return;
   }
-  // Loads of one block into registers: this lane's K operand rows (row l32 of the
-  // wave's tile is key 32w + swap23(l32), chunk 8h + t at step t; keys past the end
-  // clamped, masked after the scores) and its share of V (8 keys x 8 dims).
-  u32x4_t ka[8], vr[8];
+  // Loads of one block into registers, coalesced: K as 8 rows x 16 B per thread
+  // (row (tid >> 4) + 16m holds key swap23 of it, chunk tid & 15), V as 8 keys x 8
+  // dims per thread; keys past the end are clamped, then zeroed.
+  u32x4_t kr[8], vr[8];
   auto load_block = [&](int b) {
     const int64_t kb0 = (int64_t)b * kBk;
     const int nvalid = (L - kb0 < kBk) ? (int)(L - kb0) : kBk;
     const int64_t base = ((j0 + kb0) * H_kv + r) * kDh;
-    const int key = 32 * wave + swap23(l32);
-    const uint16_t* kr = kc + base + (int64_t)(key < nvalid ? key : nvalid - 1) * row_stride + 64 * h;
+    const int c = tid & 15;
 #pragma unroll
-    for (int st = 0; st < 8; ++st) ka[st] = ld16<false>(kr + 8 * st);
+    for (int m = 0; m < 8; ++m) {
+      const int key = swap23((tid >> 4) + 16 * m);
+      kr[m] = ld16<false>(kc + base + (int64_t)(key < nvalid ? key : nvalid - 1) * row_stride + c * 8);
+      if (key >= nvalid) kr[m] = u32x4_t{0u, 0u, 0u, 0u};
+    }
     const int kg = tid & 15, dc = tid >> 4;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -220,9 +239,16 @@ __global__ __launch_bounds__(256, 2) void dec_attn_kernel(const uint16_t* __rest
       if (kv >= nvalid) vr[e] = u32x4_t{0u, 0u, 0u, 0u};
     }
   };
-  // V^T to LDS from the registers: Vt[d] (256 B) holds keys in natural order,
-  // 8-key chunk kc at position kc ^ (d & 15).
-  auto store_vt = [&]() {
+  // The block to LDS from the registers: K row rho (256 B) at rho*256, chunk c at
+  // position c ^ (rho & 15); V^T[d] (256 B) holds keys in natural order, 8-key
+  // chunk kc at position kc ^ (d & 15).
+  auto store_block = [&]() {
+    const int c = tid & 15;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int rho = (tid >> 4) + 16 * m;
+      *reinterpret_cast<u32x4_t*>(Ks + rho * 256 + ((c ^ (rho & 15)) << 4)) = kr[m];
+    }
     const int kg = tid & 15, dc = tid >> 4;
 #pragma unroll
     for (int f = 0; f < 8; ++f) {
@@ -249,7 +275,7 @@ __global__ __launch_bounds__(256, 2) void dec_attn_kernel(const uint16_t* __rest
   }
   int b = sel[t];
   load_block(b);
-  store_vt();
+  store_block();
   float m_run = -__builtin_inff(), l_run = 0.f;  // base-2 scaled max, sum (per column)
   f32x16_t oacc[4];
 #pragma unroll
@@ -259,15 +285,23 @@ __global__ __launch_bounds__(256, 2) void dec_attn_kernel(const uint16_t* __rest
     const int nvalid = (L - kb0 < kBk) ? (int)(L - kb0) : kBk;
     const int tn = next_valid(t + 1);
     const int bn = tn < t1 ? sel[tn] : b;
-    __syncthreads();  // V^T of this block staged
-
-    // S^T tile of this wave: element v is key 32w + 16(v/8) + 4((v/4)%2) + v%4 + 8h.
-    f32x16_t sacc = f32x16_t{};
-#pragma unroll
-    for (int st = 0; st < 8; ++st) sacc = mfma_32x32x16(as_bf16x8(ka[st]), as_bf16x8(qop[st]), sacc);
-    // The K registers are consumed and this block's V is in LDS: the next block's
-    // loads go in flight while the softmax and PV run.
+    __syncthreads();  // this block's K and V^T staged
+    // The staging registers are free: the next block's loads go in flight while
+    // this block is computed.
     if (tn < t1) load_block(bn);
+
+    // S^T tile of this wave (LDS row 32w + l32 holds key 32w + swap23(l32)):
+    // element v is key 32w + 16(v/8) + 4((v/4)%2) + v%4 + 8h.
+    f32x16_t sacc = f32x16_t{};
+    {
+      const int row = 32 * wave + l32;
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const int c = 8 * h + st;
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(Ks + row * 256 + ((c ^ (row & 15)) << 4));
+        sacc = mfma_32x32x16(as_bf16x8(a), as_bf16x8(qop[st]), sacc);
+      }
+    }
     if (nvalid < kBk) {
       const int lim = nvalid - 1 - 32 * wave - 8 * h;
 #pragma unroll
@@ -318,9 +352,9 @@ __global__ __launch_bounds__(256, 2) void dec_attn_kernel(const uint16_t* __rest
         oacc[dt] = mfma_32x32x16(as_bf16x8(va), as_bf16x8(pb[hf]), oacc[dt]);
       }
     }
-    __syncthreads();  // every wave is done with this block's V^T
+    __syncthreads();  // every wave is done with this block's K and V^T
     if (tn >= t1) break;
-    store_vt();
+    store_block();
     t = tn;
     b = bn;
   }
