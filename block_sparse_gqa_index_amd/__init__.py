@@ -5,7 +5,7 @@ provides device memory and the current stream.  The functions carry the C names
 (``msa_index_topk``, ``msa_sparse_attn_fwd``, ``msa_decode``, ...) and accept torch
 tensors; outputs and workspaces are allocated here when not given.
 
-If the library has not been built (``python -m block_sparse_gqa_index_amd.build``
+If the library has not been built (``python block_sparse_gqa_index_amd/build.py``
 or ``__graft_entry__.build()``) importing the binding fails loudly: there is no
 fallback implementation.
 """
@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmsa.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m block_sparse_gqa_index_amd.build`")
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python block_sparse_gqa_index_amd/build.py`")
 
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -42,6 +42,11 @@ _SIGS = {
     "msa_index_block_scores": ([_P, _P, _I64, _I32, _I32, _I32, _P, _P], _I32),
     "msa_topk_from_scores": ([_P, _I64, _I32, _I64, _I32, _I32, _P, _P], _I32),
     "msa_set_profile_events": ([ctypes.POINTER(_P), _I32], _I32),
+    "msa_index_topk_varlen": ([_P, _P, _P, _I32, _I64, _I64, _I32, _I32, _I32, _I32, _P, _P], _I32),
+    "msa_sparse_attn_fwd_varlen_workspace": ([_I64, _I32, _I32, _I32, _I32, _I32, _I32], _SZ),
+    "msa_sparse_attn_fwd_varlen_workspace_min": ([_I64, _I32, _I32, _I32, _I32, _I32, _I32], _SZ),
+    "msa_sparse_attn_fwd_varlen": ([_P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32, _I32, _I32, _F32, _P, _P, _P,
+                                    _SZ, _P], _I32),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -165,6 +170,59 @@ def msa_sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block
     _check(_lib.msa_sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), N, H_q, H_kv, d_h, B_k, kk,
                                     float(scale), _ptr(o), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
                                     _stream(stream)), "msa_sparse_attn_fwd")
+    return o, lse
+
+
+# ----------------------------------------------------------------- Packed sequences
+def msa_index_topk_varlen(q_idx: torch.Tensor, k_idx: torch.Tensor, cu_seqlens: torch.Tensor, max_len: int, k: int,
+                          B_k: int = 128, block_idx: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Eq. 6-7 per packed sequence: block_idx [T, H_kv, k] int32, block numbers within each row's sequence."""
+    T, H_kv, d_idx = q_idx.shape
+    batch = cu_seqlens.shape[0] - 1
+    _need(q_idx, "q_idx", torch.bfloat16, (T, H_kv, d_idx))
+    _need(k_idx, "k_idx", torch.bfloat16, (T, d_idx))
+    _need(cu_seqlens, "cu_seqlens", torch.int64, (batch + 1,))
+    if block_idx is None:
+        block_idx = torch.empty((T, H_kv, k), dtype=torch.int32, device=q_idx.device)
+    _need(block_idx, "block_idx", torch.int32, (T, H_kv, k))
+    _check(_lib.msa_index_topk_varlen(_ptr(q_idx), _ptr(k_idx), _ptr(cu_seqlens), batch, T, max_len, H_kv, d_idx,
+                                      B_k, k, _ptr(block_idx), _stream(stream)), "msa_index_topk_varlen")
+    return block_idx
+
+
+def msa_sparse_attn_fwd_varlen_workspace(T: int, batch: int, H_q: int, H_kv: int, k: int, d_h: int = 128,
+                                         B_k: int = 128, minimum: bool = False) -> int:
+    fn = _lib.msa_sparse_attn_fwd_varlen_workspace_min if minimum else _lib.msa_sparse_attn_fwd_varlen_workspace
+    return int(fn(T, batch, H_q, H_kv, d_h, B_k, k))
+
+
+def msa_sparse_attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_idx: torch.Tensor,
+                               cu_seqlens: torch.Tensor, B_k: int = 128, scale: float | None = None,
+                               o: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                               workspace: torch.Tensor | None = None, stream=None):
+    """Eq. 8 per packed sequence.  Returns (o [T,H_q,d_h] fp32, lse [T,H_q] fp32)."""
+    T, H_q, d_h = q.shape
+    H_kv = k.shape[1]
+    kk = block_idx.shape[2]
+    batch = cu_seqlens.shape[0] - 1
+    _need(q, "q", torch.bfloat16, (T, H_q, d_h))
+    _need(k, "k", torch.bfloat16, (T, H_kv, d_h))
+    _need(v, "v", torch.bfloat16, (T, H_kv, d_h))
+    _need(block_idx, "block_idx", torch.int32, (T, H_kv, kk))
+    _need(cu_seqlens, "cu_seqlens", torch.int64, (batch + 1,))
+    if scale is None:
+        scale = d_h ** -0.5
+    if o is None:
+        o = torch.empty((T, H_q, d_h), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((T, H_q), dtype=torch.float32, device=q.device)
+    _need(o, "o", torch.float32, (T, H_q, d_h))
+    _need(lse, "lse", torch.float32, (T, H_q))
+    ws = _ws(_lib.msa_sparse_attn_fwd_varlen_workspace(T, batch, H_q, H_kv, d_h, B_k, kk), q.device, workspace)
+    _check(_lib.msa_sparse_attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), _ptr(cu_seqlens), batch, T,
+                                           H_q, H_kv, d_h, B_k, kk, float(scale), _ptr(o), _ptr(lse), _ptr(ws),
+                                           ws.numel() * ws.element_size(), _stream(stream)),
+           "msa_sparse_attn_fwd_varlen")
     return o, lse
 
 

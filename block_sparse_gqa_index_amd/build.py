@@ -1,4 +1,8 @@
-"""Build libmsa.so (all HIP kernels + the C ABI) in-tree for gfx950 with hipcc."""
+"""Build libmsa.so (all HIP kernels + the C ABI) in-tree for gfx950 with hipcc.
+
+Self-contained on purpose: run it as a script, or load it by file path
+(``load_builder()`` in ``__graft_entry__``), since importing the package itself
+needs the library it builds."""
 from __future__ import annotations
 
 import os

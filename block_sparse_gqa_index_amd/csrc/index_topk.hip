@@ -111,10 +111,15 @@ __device__ __forceinline__ void idx_block_max(const uint8_t* buf, const uint4 (&
 // halves hold both block maxima of their column; the lower half offers block b to
 // its list and the upper half block b+1 to its own, so one insertion sequence
 // serves two blocks.  The two lists (even / odd blocks) are merged at the end.
+// Sequences: with cu == nullptr the call is one sequence of N tokens; otherwise
+// cu[0..batch] (device) are the packed sequence offsets, grid.y is the sequence and
+// grid.x the column tile within it (tiles past the sequence's end exit).  Every
+// position below (queries, blocks, keys) is relative to the sequence start j0;
+// columns and output rows are global.
 template <int LIST, int CT, bool WRITE_M>
 __global__ __launch_bounds__(kIdxThreads, 2) void index_topk_kernel(
-    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, int64_t N, int H_kv,
-    int k, int64_t B, int32_t* __restrict__ block_idx, float* __restrict__ M) {
+    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx_all, int64_t N_all, int H_kv,
+    int k, int64_t B, int32_t* __restrict__ block_idx, float* __restrict__ M, const int64_t* __restrict__ cu) {
   constexpr int kColsPerWave = 32 * CT;
   constexpr int kCols = kIdxWaves * kColsPerWave;
   constexpr int kBlkBytes = kBk * kDidx * 2;
@@ -123,22 +128,28 @@ __global__ __launch_bounds__(kIdxThreads, 2) void index_topk_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
-  const int64_t total = N * H_kv;
+  const int64_t j0 = cu ? cu[blockIdx.y] : 0;
+  const int64_t N = cu ? cu[blockIdx.y + 1] - j0 : N_all;  // tokens of this sequence
+  const uint16_t* __restrict__ k_idx = k_idx_all + j0 * kDidx;
+  const int64_t total = N * H_kv;                          // columns of this sequence
+  const int64_t ntiles = (total + kCols - 1) / kCols;
+  if ((int64_t)blockIdx.x >= ntiles) return;
   // Longest sweeps (largest query positions) are dispatched first.
-  const int64_t tile = (int64_t)gridDim.x - 1 - blockIdx.x;
+  const int64_t tile = ntiles - 1 - blockIdx.x;
   const int64_t c0 = tile * kCols;
   const int64_t c_end = (c0 + kCols < total ? c0 + kCols : total);
   const int64_t b_last = ((c_end - 1) / H_kv) / kBk;
   const int64_t wave_c0 = c0 + wave * kColsPerWave;
   const int64_t i_min_wave = wave_c0 / H_kv;
+  const int64_t gcol0 = j0 * H_kv;  // global column of the sequence's first column
 
   int64_t col[CT], qi[CT];
   uint4 qop[CT][4];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
-    col[ct] = wave_c0 + ct * 32 + l32;
-    const bool ok = col[ct] < total;
-    qi[ct] = ok ? col[ct] / H_kv : -1;
+    col[ct] = gcol0 + wave_c0 + ct * 32 + l32;
+    const bool ok = wave_c0 + ct * 32 + l32 < total;
+    qi[ct] = ok ? (wave_c0 + ct * 32 + l32) / H_kv : -1;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
       qop[ct][ks] = ok ? *reinterpret_cast<const uint4*>(q_idx + col[ct] * kDidx + ks * 16 + 8 * h)
@@ -258,24 +269,27 @@ __global__ void fill_f32_kernel(float* __restrict__ p, int64_t n, float val) {
 
 }  // namespace
 
+// cu == nullptr: one sequence of N tokens; otherwise `batch` packed sequences with
+// device offsets cu[0..batch] and N = the longest length (grid.x is sized by it).
 hipError_t launch_index_topk(const uint16_t* q_idx, const uint16_t* k_idx, int64_t N, int H_kv, int k,
-                             int32_t* block_idx, hipStream_t stream) {
+                             int32_t* block_idx, const int64_t* cu, int batch, hipStream_t stream) {
   const int64_t total = N * H_kv;
+  const unsigned gy = cu ? (unsigned)batch : 1u;
   if (k <= 8) {
     constexpr int CT = 2;
     const int64_t grid = (total + kIdxWaves * 32 * CT - 1) / (kIdxWaves * 32 * CT);
-    index_topk_kernel<7, CT, false><<<dim3((unsigned)grid), dim3(kIdxThreads), 0, stream>>>(
-        q_idx, k_idx, N, H_kv, k, 0, block_idx, nullptr);
+    index_topk_kernel<7, CT, false><<<dim3((unsigned)grid, gy), dim3(kIdxThreads), 0, stream>>>(
+        q_idx, k_idx, N, H_kv, k, 0, block_idx, nullptr, cu);
   } else if (k <= 16) {
     constexpr int CT = 2;
     const int64_t grid = (total + kIdxWaves * 32 * CT - 1) / (kIdxWaves * 32 * CT);
-    index_topk_kernel<15, CT, false><<<dim3((unsigned)grid), dim3(kIdxThreads), 0, stream>>>(
-        q_idx, k_idx, N, H_kv, k, 0, block_idx, nullptr);
+    index_topk_kernel<15, CT, false><<<dim3((unsigned)grid, gy), dim3(kIdxThreads), 0, stream>>>(
+        q_idx, k_idx, N, H_kv, k, 0, block_idx, nullptr, cu);
   } else {
     constexpr int CT = 1;
     const int64_t grid = (total + kIdxWaves * 32 * CT - 1) / (kIdxWaves * 32 * CT);
-    index_topk_kernel<31, CT, false><<<dim3((unsigned)grid), dim3(kIdxThreads), 0, stream>>>(
-        q_idx, k_idx, N, H_kv, k, 0, block_idx, nullptr);
+    index_topk_kernel<31, CT, false><<<dim3((unsigned)grid, gy), dim3(kIdxThreads), 0, stream>>>(
+        q_idx, k_idx, N, H_kv, k, 0, block_idx, nullptr, cu);
   }
   return hipGetLastError();
 }
@@ -291,7 +305,7 @@ hipError_t launch_index_block_scores(const uint16_t* q_idx, const uint16_t* k_id
   const int64_t total = N * H_kv;
   const int64_t grid = (total + kIdxWaves * 32 * CT - 1) / (kIdxWaves * 32 * CT);
   index_topk_kernel<1, CT, true><<<dim3((unsigned)grid), dim3(kIdxThreads), 0, stream>>>(
-      q_idx, k_idx, N, H_kv, 1, B, nullptr, M);
+      q_idx, k_idx, N, H_kv, 1, B, nullptr, M, nullptr);
   return hipGetLastError();
 }
 

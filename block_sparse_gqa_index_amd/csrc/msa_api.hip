@@ -62,10 +62,10 @@ int num_cus() {
   return cache[dev];
 }
 
-int64_t window_for_bytes(int64_t N, int H_q, int H_kv, int k, size_t ws_bytes) {
-  const int64_t B = (N + msa::kBlockKeys - 1) / msa::kBlockKeys;
-  // Windows are whole blocks of queries; the largest that fits wins.
-  int64_t lo = 0, hi = B;
+// Largest query window (whole blocks of queries, at least one block) whose
+// per-window workspace fits in ws_bytes; B is the list stride in blocks.
+int64_t window_for_bytes(int64_t N, int64_t B, int H_q, int H_kv, int k, size_t ws_bytes) {
+  int64_t lo = 0, hi = (N + msa::kBlockKeys - 1) / msa::kBlockKeys;
   while (lo < hi) {
     const int64_t mid = (lo + hi + 1) / 2;
     const int64_t W = mid * msa::kBlockKeys < N ? mid * msa::kBlockKeys : N;
@@ -74,7 +74,9 @@ int64_t window_for_bytes(int64_t N, int H_q, int H_kv, int k, size_t ws_bytes) {
     else
       hi = mid - 1;
   }
-  return lo * msa::kBlockKeys < N ? lo * msa::kBlockKeys : N;
+  const int64_t W = lo * msa::kBlockKeys < N ? lo * msa::kBlockKeys : N;
+  const int64_t Wmin = N < msa::kBlockKeys ? N : msa::kBlockKeys;
+  return W > Wmin ? W : Wmin;
 }
 
 }  // namespace
@@ -107,7 +109,7 @@ msa_status_t msa_index_topk(const void* q_idx, const void* k_idx, int64_t N, int
     return fail(MSA_ERR_INVALID_ARG, "misaligned pointer (q_idx/k_idx need 16 B, block_idx 4 B)");
   if (N * H_kv >= ((int64_t)1 << 31)) return fail(MSA_ERR_UNSUPPORTED, "N * H_kv too large");
   hipError_t e = msa::launch_index_topk(static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx),
-                                        N, H_kv, k, block_idx, static_cast<hipStream_t>(hip_stream));
+                                        N, H_kv, k, block_idx, nullptr, 0, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_fail(e, "index_topk launch");
   return ok();
 }
@@ -153,18 +155,52 @@ static msa_status_t check_attn_shape(int64_t N, int H_q, int H_kv, int d_h, int 
   return MSA_OK;
 }
 
+// Attention over N tokens with list stride B (blocks), given sequence tables si (si.cu
+// null: one sequence).  The workspace holds the sequence tables (S) and then the
+// per-window buffers.
+static msa_status_t attn_run(const void* q, const void* k, const void* v, const int32_t* block_idx, int64_t N,
+                             int64_t B, const msa::SeqInfo& si, const msa::SeqTables& S, int H_q, int H_kv, int k_sel,
+                             float scale, float* o, float* lse, uint8_t* ws, size_t ws_bytes, hipStream_t stream) {
+  const size_t avail = ws_bytes - S.total;
+  const int64_t W = window_for_bytes(N, B, H_q, H_kv, k_sel, avail);
+  const msa::AttnWorkspace L = msa::attn_workspace_layout(W, H_q, H_kv, k_sel, B);
+  const int cus = num_cus();
+  for (int64_t w0 = 0; w0 < N; w0 += W) {
+    const int64_t Wn = (N - w0 < W) ? N - w0 : W;
+    hipError_t e = msa::launch_sparse_attn_window(
+        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), block_idx,
+        N, B, si, H_q, H_kv, k_sel, scale, w0, Wn, cus, o, lse, ws + S.total, L, stream,
+        g_phase_events_on ? g_phase_events : nullptr);
+    if (e != hipSuccess) return hip_fail(e, "sparse_attn launch");
+  }
+  return ok();
+}
+
+static size_t attn_workspace_bytes(int64_t N, int64_t B, const msa::SeqTables& S, int H_q, int H_kv, int k,
+                                   bool minimum) {
+  const int64_t Wmin = N < msa::kBlockKeys ? N : msa::kBlockKeys;
+  const int64_t W = minimum ? Wmin : window_for_bytes(N, B, H_q, H_kv, k, kDefaultAttnWorkspace);
+  return S.total + msa::attn_workspace_layout(W, H_q, H_kv, k, B).total;
+}
+
+static msa_status_t check_attn_ptrs(const void* q, const void* k, const void* v, const int32_t* block_idx,
+                                    const float* o, const float* lse, float scale) {
+  if (!(scale > 0.f) || scale != scale) return fail(MSA_ERR_INVALID_ARG, "scale must be a positive number");
+  if (!q || !k || !v || !block_idx || !o || !lse) return fail(MSA_ERR_INVALID_ARG, "null pointer");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(block_idx, 4) || !aligned(o, 16) ||
+      !aligned(lse, 4))
+    return fail(MSA_ERR_INVALID_ARG, "misaligned pointer (q/k/v/o need 16 B)");
+  return MSA_OK;
+}
+
 size_t msa_sparse_attn_fwd_workspace(int64_t N, int H_q, int H_kv, int d_h, int B_k, int k) {
   if (check_attn_shape(N, H_q, H_kv, d_h, B_k, k) != MSA_OK || N == 0) return 0;
-  const int64_t W = window_for_bytes(N, H_q, H_kv, k, kDefaultAttnWorkspace);
-  const int64_t B = (N + B_k - 1) / B_k;
-  const int64_t Wmin = N < B_k ? N : B_k;
-  return msa::attn_workspace_layout(W > Wmin ? W : Wmin, H_q, H_kv, k, B).total;
+  return attn_workspace_bytes(N, (N + B_k - 1) / B_k, msa::SeqTables{}, H_q, H_kv, k, false);
 }
 
 size_t msa_sparse_attn_fwd_workspace_min(int64_t N, int H_q, int H_kv, int d_h, int B_k, int k) {
   if (check_attn_shape(N, H_q, H_kv, d_h, B_k, k) != MSA_OK || N == 0) return 0;
-  const int64_t B = (N + B_k - 1) / B_k;
-  return msa::attn_workspace_layout(N < B_k ? N : B_k, H_q, H_kv, k, B).total;
+  return attn_workspace_bytes(N, (N + B_k - 1) / B_k, msa::SeqTables{}, H_q, H_kv, k, true);
 }
 
 msa_status_t msa_sparse_attn_fwd(const void* q, const void* k, const void* v, const int32_t* block_idx, int64_t N,
@@ -174,29 +210,92 @@ msa_status_t msa_sparse_attn_fwd(const void* q, const void* k, const void* v, co
   if (st != MSA_OK) return st;
   if (!(scale > 0.f) || scale != scale) return fail(MSA_ERR_INVALID_ARG, "scale must be a positive number");
   if (N == 0) return ok();
-  if (!q || !k || !v || !block_idx || !o || !lse) return fail(MSA_ERR_INVALID_ARG, "null pointer");
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(block_idx, 4) || !aligned(o, 16) ||
-      !aligned(lse, 4))
-    return fail(MSA_ERR_INVALID_ARG, "misaligned pointer (q/k/v/o need 16 B)");
+  if ((st = check_attn_ptrs(q, k, v, block_idx, o, lse, scale)) != MSA_OK) return st;
   const size_t need = msa_sparse_attn_fwd_workspace_min(N, H_q, H_kv, d_h, B_k, k_sel);
   if (!ws || ws_bytes < need)
     return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes is below the minimum %zu", ws ? ws_bytes : 0, need);
   if (!aligned(ws, 256)) return fail(MSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  const int64_t B = (N + B_k - 1) / B_k;
-  int64_t W = window_for_bytes(N, H_q, H_kv, k_sel, ws_bytes);
-  const int64_t Wmin = N < B_k ? N : B_k;
-  if (W < Wmin) W = Wmin;
-  const msa::AttnWorkspace L = msa::attn_workspace_layout(W, H_q, H_kv, k_sel, B);
-  const int cus = num_cus();
-  for (int64_t w0 = 0; w0 < N; w0 += W) {
-    const int64_t Wn = (N - w0 < W) ? N - w0 : W;
-    hipError_t e = msa::launch_sparse_attn_window(
-        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), block_idx,
-        N, H_q, H_kv, k_sel, scale, w0, Wn, cus, o, lse, static_cast<uint8_t*>(ws), L,
-        static_cast<hipStream_t>(hip_stream), g_phase_events_on ? g_phase_events : nullptr);
-    if (e != hipSuccess) return hip_fail(e, "sparse_attn launch");
-  }
+  return attn_run(q, k, v, block_idx, N, (N + B_k - 1) / B_k, msa::SeqInfo{}, msa::SeqTables{}, H_q, H_kv, k_sel,
+                  scale, o, lse, static_cast<uint8_t*>(ws), ws_bytes, static_cast<hipStream_t>(hip_stream));
+}
+
+// ---------------------------------------------------------------- packed sequences
+static msa_status_t check_varlen(int batch, int64_t T, int64_t max_len) {
+  if (batch < 0) return fail(MSA_ERR_INVALID_ARG, "batch must be >= 0");
+  if (T < 0 || max_len < 0) return fail(MSA_ERR_INVALID_ARG, "T and max_len must be >= 0");
+  if (max_len > T) return fail(MSA_ERR_INVALID_ARG, "max_len must be <= T");
+  if ((T + msa::kBlockKeys - 1) / msa::kBlockKeys + batch > kMaxBlocks)
+    return fail(MSA_ERR_UNSUPPORTED, "ceil(T / B_k) + batch must be <= %lld", (long long)kMaxBlocks);
+  return MSA_OK;
+}
+
+static int64_t varlen_blocks(int64_t T, int batch) { return (T + msa::kBlockKeys - 1) / msa::kBlockKeys + batch; }
+
+msa_status_t msa_index_topk_varlen(const void* q_idx, const void* k_idx, const int64_t* cu_seqlens, int batch,
+                                   int64_t T, int64_t max_len, int H_kv, int d_idx, int B_k, int k,
+                                   int32_t* block_idx, void* hip_stream) {
+  msa_status_t st = check_common(T, d_idx, msa::kIndexDim, "d_idx", B_k, k);
+  if (st != MSA_OK) return st;
+  if ((st = check_varlen(batch, T, max_len)) != MSA_OK) return st;
+  if (batch > 0 && T > 0 && max_len == 0) return fail(MSA_ERR_INVALID_ARG, "max_len must be >= 1");
+  if (H_kv < 1) return fail(MSA_ERR_INVALID_ARG, "H_kv must be >= 1");
+  if (batch == 0 || T == 0) return ok();
+  if (!q_idx || !k_idx || !block_idx || !cu_seqlens) return fail(MSA_ERR_INVALID_ARG, "null pointer");
+  if (!aligned(q_idx, 16) || !aligned(k_idx, 16) || !aligned(block_idx, 4) || !aligned(cu_seqlens, 8))
+    return fail(MSA_ERR_INVALID_ARG, "misaligned pointer");
+  if (T * H_kv >= ((int64_t)1 << 31)) return fail(MSA_ERR_UNSUPPORTED, "T * H_kv too large");
+  if (batch > 65535) return fail(MSA_ERR_UNSUPPORTED, "batch must be <= 65535");
+  hipError_t e = msa::launch_index_topk(static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx),
+                                        max_len, H_kv, k, block_idx, cu_seqlens, batch,
+                                        static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "index_topk launch");
   return ok();
+}
+
+size_t msa_sparse_attn_fwd_varlen_workspace(int64_t T, int batch, int H_q, int H_kv, int d_h, int B_k, int k) {
+  if (check_attn_shape(T, H_q, H_kv, d_h, B_k, k) != MSA_OK || check_varlen(batch, T, 0) != MSA_OK || T == 0 ||
+      batch == 0)
+    return 0;
+  const int64_t Bt = varlen_blocks(T, batch);
+  return attn_workspace_bytes(T, Bt, msa::seq_tables_layout(T, batch, Bt), H_q, H_kv, k, false);
+}
+
+size_t msa_sparse_attn_fwd_varlen_workspace_min(int64_t T, int batch, int H_q, int H_kv, int d_h, int B_k, int k) {
+  if (check_attn_shape(T, H_q, H_kv, d_h, B_k, k) != MSA_OK || check_varlen(batch, T, 0) != MSA_OK || T == 0 ||
+      batch == 0)
+    return 0;
+  const int64_t Bt = varlen_blocks(T, batch);
+  return attn_workspace_bytes(T, Bt, msa::seq_tables_layout(T, batch, Bt), H_q, H_kv, k, true);
+}
+
+msa_status_t msa_sparse_attn_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* block_idx,
+                                        const int64_t* cu_seqlens, int batch, int64_t T, int H_q, int H_kv, int d_h,
+                                        int B_k, int k_sel, float scale, float* o, float* lse, void* ws,
+                                        size_t ws_bytes, void* hip_stream) {
+  msa_status_t st = check_attn_shape(T, H_q, H_kv, d_h, B_k, k_sel);
+  if (st != MSA_OK) return st;
+  if ((st = check_varlen(batch, T, 0)) != MSA_OK) return st;
+  if (!(scale > 0.f) || scale != scale) return fail(MSA_ERR_INVALID_ARG, "scale must be a positive number");
+  if (batch == 0 || T == 0) return ok();
+  if ((st = check_attn_ptrs(q, k, v, block_idx, o, lse, scale)) != MSA_OK) return st;
+  if (!cu_seqlens) return fail(MSA_ERR_INVALID_ARG, "null pointer");
+  if (!aligned(cu_seqlens, 8)) return fail(MSA_ERR_INVALID_ARG, "misaligned pointer");
+  const size_t need = msa_sparse_attn_fwd_varlen_workspace_min(T, batch, H_q, H_kv, d_h, B_k, k_sel);
+  if (!ws || ws_bytes < need)
+    return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes is below the minimum %zu", ws ? ws_bytes : 0, need);
+  if (!aligned(ws, 256)) return fail(MSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const int64_t Bt = varlen_blocks(T, batch);
+  const msa::SeqTables S = msa::seq_tables_layout(T, batch, Bt);
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  hipError_t e = msa::launch_seq_tables(cu_seqlens, batch, w, S, stream);
+  if (e != hipSuccess) return hip_fail(e, "sequence tables launch");
+  msa::SeqInfo si;
+  si.cu = cu_seqlens;
+  si.bstart = reinterpret_cast<const int32_t*>(w + S.bstart);
+  si.seq_tok = reinterpret_cast<const int32_t*>(w + S.seq_tok);
+  si.seq_blk = reinterpret_cast<const int32_t*>(w + S.seq_blk);
+  return attn_run(q, k, v, block_idx, T, Bt, si, S, H_q, H_kv, k_sel, scale, o, lse, w, ws_bytes, stream);
 }
 
 msa_status_t msa_set_profile_events(void* const* events, int n) {

@@ -28,17 +28,37 @@ struct DecodeWorkspace {
 };
 
 hipError_t launch_index_topk(const uint16_t* q_idx, const uint16_t* k_idx, int64_t N, int H_kv, int k,
-                             int32_t* block_idx, hipStream_t stream);
+                             int32_t* block_idx, const int64_t* cu, int batch, hipStream_t stream);
 hipError_t launch_index_block_scores(const uint16_t* q_idx, const uint16_t* k_idx, int64_t N, int H_kv,
                                      float* M, hipStream_t stream);
 hipError_t launch_topk_from_scores(const float* M, int64_t N, int H_kv, int64_t B, int k, int32_t* block_idx,
                                    hipStream_t stream);
 
+// Packed sequences of a varlen call: cu == nullptr means one sequence [0, N).
+// bstart[s] is the first global block of sequence s (blocks of all sequences are
+// numbered consecutively; bstart[batch] = their count), seq_tok[t] the sequence of
+// token t and seq_blk[gb] the sequence of global block gb.
+struct SeqInfo {
+  const int64_t* cu = nullptr;
+  const int32_t* bstart = nullptr;
+  const int32_t* seq_tok = nullptr;
+  const int32_t* seq_blk = nullptr;
+};
+struct SeqTables {
+  size_t bstart, seq_tok, seq_blk, total;
+};
+// Workspace bytes of the tables for T tokens in `batch` sequences with at most Bt
+// global blocks (0 for a single sequence).
+SeqTables seq_tables_layout(int64_t T, int batch, int64_t Bt);
+hipError_t launch_seq_tables(const int64_t* cu, int batch, uint8_t* ws, const SeqTables& S, hipStream_t stream);
+
+// B: the list stride in blocks (the block count, or for several sequences an upper
+// bound of the global block count).
 AttnWorkspace attn_workspace_layout(int64_t W, int H_q, int H_kv, int kk, int64_t B);
 hipError_t launch_sparse_attn_window(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                     const int32_t* block_idx, int64_t N, int H_q, int H_kv, int kk,
-                                     float scale, int64_t w0, int64_t W, int num_cus, float* o, float* lse,
-                                     uint8_t* ws, const AttnWorkspace& L, hipStream_t stream,
+                                     const int32_t* block_idx, int64_t N, int64_t B, const SeqInfo& si, int H_q,
+                                     int H_kv, int kk, float scale, int64_t w0, int64_t W, int num_cus, float* o,
+                                     float* lse, uint8_t* ws, const AttnWorkspace& L, hipStream_t stream,
                                      const hipEvent_t* events);  // 4 phase events or null
 
 DecodeWorkspace decode_workspace_layout(int batch, int H_q, int H_kv, int kk, int64_t Bmax);

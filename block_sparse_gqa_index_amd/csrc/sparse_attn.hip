@@ -25,37 +25,62 @@ namespace msa {
 namespace {
 
 // --------------------------------------------------------------------- inverse index
-// Pair validity: 0 <= b <= b_loc(i) and b < B.  Later blocks add no token.
-__device__ __forceinline__ bool pair_valid(int b, int64_t i, int64_t B) {
-  return b >= 0 && (int64_t)b < B && (int64_t)b <= i / kBk;
+// Pair validity for a query at position i_rel of its sequence: 0 <= b <= b_loc.
+// Later blocks add no token.
+__device__ __forceinline__ bool pair_valid(int b, int64_t i_rel) { return b >= 0 && (int64_t)b <= i_rel / kBk; }
+
+// Start of the sequence of global token i (and its index s).
+__device__ __forceinline__ int64_t seq_start(const SeqInfo& si, int64_t i, int& s) {
+  if (!si.cu) {
+    s = 0;
+    return 0;
+  }
+  s = si.seq_tok[i];
+  return si.cu[s];
 }
+__device__ __forceinline__ int64_t gblock(const SeqInfo& si, int s, int b) { return si.cu ? si.bstart[s] + b : b; }
 
 // Lists are keyed (group r, query window w, block b): list (r * nW + w) * B + b holds
 // the pairs of queries in window w (WQ queries) that chose block b for group r.
 // Processing lists in key order keeps the q rows being gathered (one window of one
 // group) and the K/V blocks being staged (one group) small enough to stay cached.
-__global__ __launch_bounds__(256) void inv_count_kernel(const int32_t* __restrict__ block_idx, int64_t w0,
-                                                        int64_t W, int H_kv, int kk, int64_t B, int TQ,
+// Blocks are numbered globally (sequence s's block b is gblock(s, b)); the blocks a
+// tile of queries can choose form one range [gb_lo, gb_hi] of global blocks, which
+// the LDS histogram covers.
+__device__ __forceinline__ void tile_block_range(const SeqInfo& si, int64_t q0, int64_t q1, int64_t& gb_lo,
+                                                 int64_t& nh) {
+  int sf, sl;
+  (void)seq_start(si, q0, sf);
+  const int64_t jl = seq_start(si, q1 - 1, sl);
+  gb_lo = si.cu ? si.bstart[sf] : 0;
+  nh = gblock(si, sl, (int)((q1 - 1 - jl) / kBk)) - gb_lo + 1;
+}
+
+__global__ __launch_bounds__(256) void inv_count_kernel(const int32_t* __restrict__ block_idx, SeqInfo si,
+                                                        int64_t w0, int64_t W, int H_kv, int kk, int64_t B, int TQ,
                                                         int64_t WQ, int nW, int32_t* __restrict__ counts) {
   extern __shared__ int32_t hist[];
   const int r = blockIdx.y;
   const int64_t q0 = w0 + (int64_t)blockIdx.x * TQ;
   const int64_t lbase = ((int64_t)r * nW + (q0 - w0) / WQ) * B;
   const int64_t q1 = (q0 + TQ < w0 + W) ? q0 + TQ : w0 + W;
-  const int64_t bmax = ((q1 - 1) / kBk < B - 1) ? (q1 - 1) / kBk : B - 1;
-  for (int64_t b = threadIdx.x; b <= bmax; b += 256) hist[b] = 0;
+  int64_t gb_lo, nh;
+  tile_block_range(si, q0, q1, gb_lo, nh);
+  for (int64_t b = threadIdx.x; b < nh; b += 256) hist[b] = 0;
   __syncthreads();
   const int64_t npairs = (q1 - q0) * kk;
   for (int64_t p = threadIdx.x; p < npairs; p += 256) {
     const int64_t i = q0 + p / kk;
     const int s = (int)(p % kk);
+    int sq;
+    const int64_t j0 = seq_start(si, i, sq);
     const int b = block_idx[(i * H_kv + r) * kk + s];
-    if (pair_valid(b, i, B)) atomicAdd(&hist[b], 1);
+    if (pair_valid(b, i - j0)) atomicAdd(&hist[gblock(si, sq, b) - gb_lo], 1);
   }
   __syncthreads();
-  for (int64_t b = threadIdx.x; b <= bmax; b += 256) {
+  for (int64_t b = threadIdx.x; b < nh; b += 256) {
     const int c = hist[b];
-    if (c) atomicAdd(&counts[lbase + b], c);
+    if (c) atomicAdd(&counts[lbase + gb_lo + b], c);
   }
 }
 
@@ -140,9 +165,9 @@ __global__ __launch_bounds__(kScanTile) void inv_scan_write_kernel(const int32_t
 }
 
 template <int PPT>
-__global__ __launch_bounds__(256) void inv_scatter_kernel(const int32_t* __restrict__ block_idx, int64_t w0,
-                                                          int64_t W, int H_kv, int kk, int64_t B, int TQ,
-                                                          int64_t WQ, int nW, int32_t* __restrict__ cursor,
+__global__ __launch_bounds__(256) void inv_scatter_kernel(const int32_t* __restrict__ block_idx, SeqInfo si,
+                                                          int64_t w0, int64_t W, int H_kv, int kk, int64_t B,
+                                                          int TQ, int64_t WQ, int nW, int32_t* __restrict__ cursor,
                                                           int32_t* __restrict__ pairs) {
   extern __shared__ int32_t sh[];
   int32_t* hist = sh;
@@ -151,26 +176,33 @@ __global__ __launch_bounds__(256) void inv_scatter_kernel(const int32_t* __restr
   const int64_t q0 = w0 + (int64_t)blockIdx.x * TQ;
   const int64_t lbase = ((int64_t)r * nW + (q0 - w0) / WQ) * B;
   const int64_t q1 = (q0 + TQ < w0 + W) ? q0 + TQ : w0 + W;
-  const int64_t bmax = ((q1 - 1) / kBk < B - 1) ? (q1 - 1) / kBk : B - 1;
-  for (int64_t b = threadIdx.x; b <= bmax; b += 256) hist[b] = 0;
+  int64_t gb_lo, nh;
+  tile_block_range(si, q0, q1, gb_lo, nh);
+  for (int64_t b = threadIdx.x; b < nh; b += 256) hist[b] = 0;
   __syncthreads();
   const int64_t npairs = (q1 - q0) * kk;
-  int rank[PPT];
+  int rank[PPT], slot[PPT];
 #pragma unroll
   for (int u = 0; u < PPT; ++u) {
     const int64_t p = threadIdx.x + 256 * u;
     rank[u] = -1;
+    slot[u] = 0;
     if (p < npairs) {
       const int64_t i = q0 + p / kk;
       const int s = (int)(p % kk);
+      int sq;
+      const int64_t j0 = seq_start(si, i, sq);
       const int b = block_idx[(i * H_kv + r) * kk + s];
-      if (pair_valid(b, i, B)) rank[u] = atomicAdd(&hist[b], 1);
+      if (pair_valid(b, i - j0)) {
+        slot[u] = (int)(gblock(si, sq, b) - gb_lo);
+        rank[u] = atomicAdd(&hist[slot[u]], 1);
+      }
     }
   }
   __syncthreads();
-  for (int64_t b = threadIdx.x; b <= bmax; b += 256) {
+  for (int64_t b = threadIdx.x; b < nh; b += 256) {
     const int c = hist[b];
-    if (c) base[b] = atomicAdd(&cursor[lbase + b], c);
+    if (c) base[b] = atomicAdd(&cursor[lbase + gb_lo + b], c);
   }
   __syncthreads();
 #pragma unroll
@@ -179,8 +211,7 @@ __global__ __launch_bounds__(256) void inv_scatter_kernel(const int32_t* __restr
     const int64_t p = threadIdx.x + 256 * u;
     const int64_t i = q0 + p / kk;
     const int s = (int)(p % kk);
-    const int b = block_idx[(i * H_kv + r) * kk + s];
-    pairs[base[b] + rank[u]] = (int32_t)(((i - w0) << 5) | s);
+    pairs[base[slot[u]] + rank[u]] = (int32_t)(((i - w0) << 5) | s);
   }
 }
 
@@ -259,8 +290,8 @@ template <int G>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
     const int4* __restrict__ items, const int32_t* __restrict__ n_items_ptr, const int32_t* __restrict__ pairs,
-    int64_t N, int H_kv, int64_t B, int nW, int kk, int64_t w0, float scale_log2, uint16_t* __restrict__ Opart,
-    float2* __restrict__ Lpart) {
+    int64_t N, SeqInfo si, int H_kv, int64_t B, int nW, int kk, int64_t w0, float scale_log2,
+    uint16_t* __restrict__ Opart, float2* __restrict__ Lpart) {
   constexpr int kQC = 128 / G;         // gathered queries per chunk
   __shared__ __attribute__((aligned(16))) uint8_t Ks[kBk * 256];
   __shared__ __attribute__((aligned(16))) uint8_t Vt[kDh * 256];
@@ -281,8 +312,13 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
     const int64_t item = round * grid + (int64_t)xcd * per_xcd + slot_in_xcd;
     if (item >= n_items) break;
     const int4 it = items[item];
-    const int64_t b = it.x % B, r = (it.x / B) / nW;
+    const int64_t gb = it.x % B, r = (it.x / B) / nW;
     const int start = it.y, cnt = it.z;
+    // The list's block: block b of sequence s_item, whose tokens are [j0, j0 + seqN).
+    const int s_item = si.cu ? si.seq_blk[gb] : 0;
+    const int64_t b = gb - (si.cu ? si.bstart[s_item] : 0);
+    const int64_t j0 = si.cu ? si.cu[s_item] : 0;
+    const int64_t seqN = si.cu ? si.cu[s_item + 1] - j0 : N;
 
     constexpr int NR = kPairRegs<G>;
     int ip[NR];
@@ -294,10 +330,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
       // invariant address registers live across the whole kernel.
       int stid = tid;
       asm volatile("" : "+v"(stid));
-      const int64_t tok0 = b * kBk;
+      const int64_t tok0 = b * kBk;  // within the sequence
       const int row_stride = H_kv * kDh;
-      const int nvalid = (N - tok0 < kBk) ? (int)(N - tok0) : kBk;
-      const int64_t base = tok0 * row_stride + r * kDh;
+      const int nvalid = (seqN - tok0 < kBk) ? (int)(seqN - tok0) : kBk;
+      const int64_t base = (j0 + tok0) * row_stride + r * kDh;
       stage_kv(kp + base, vp + base, row_stride, nvalid, Ks, Vt, stid);
     }
     __syncthreads();
@@ -344,7 +380,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
         pr = item_pair_v(ip, valid ? cb + qs : cnt - 1);
       const int64_t i_local = pr >> 5;
       const int s = pr & 31;
-      const int64_t i = w0 + i_local;
+      const int64_t i = w0 + i_local - j0;  // query position within its sequence
 
       // S^T[row][qrow] with row -> key swap23(row): k-slot (h, e) of step t is dim
       // 64h + 8t + e in both operands.
@@ -530,8 +566,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
 template <int G, int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ Opart,
                                                       const float2* __restrict__ Lpart,
-                                                      const int32_t* __restrict__ block_idx, int64_t w0,
-                                                      int64_t W, int H_kv, int kk, int64_t B,
+                                                      const int32_t* __restrict__ block_idx, SeqInfo si,
+                                                      int64_t w0, int64_t W, int H_kv, int kk,
                                                       float* __restrict__ o, float* __restrict__ lse) {
   constexpr int GW = G < 32 ? G : 32;       // heads per wave
   constexpr int LPH = 64 / GW;               // lanes per head
@@ -547,6 +583,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   const int64_t i_local = (uint32_t)ir / (uint32_t)H_kv;
   const int r = (int)((uint32_t)ir - (uint32_t)i_local * (uint32_t)H_kv);
   const int64_t i = w0 + i_local;
+  int sq;
+  const int64_t i_rel = i - seq_start(si, i, sq);
   const int g = hw * GW + lane / LPH;
   const int d0 = (lane % LPH) * DPL;
   const int H_q = H_kv * G;
@@ -561,7 +599,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   int first = -1;
 #pragma unroll
   for (int s = 0; s < KMAX; ++s) {
-    valid[s] = s < kk && pair_valid(sel[s < kk ? s : 0], i, B);
+    valid[s] = s < kk && pair_valid(sel[s < kk ? s : 0], i_rel);
     if (valid[s] && first < 0) first = s;
   }
   float* orow = o + (i * H_q + r * G + g) * kDh + d0;
@@ -625,6 +663,31 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   if (lane % LPH == 0) lse[i * H_q + r * G + g] = (mstar + __log2f(L)) * kLn2;
 }
 
+// Tables of a varlen call (one workgroup): bstart[s] = sum over earlier sequences
+// of their block counts ceil(len / B_k), bstart[batch] = the total.
+__global__ __launch_bounds__(kScanTile) void seq_block_starts_kernel(const int64_t* __restrict__ cu, int batch,
+                                                                   int32_t* __restrict__ bstart) {
+  __shared__ int64_t lds[16];
+  int64_t carry = 0;
+  for (int s0 = 0; s0 < batch; s0 += kScanTile) {
+    const int s = s0 + threadIdx.x;
+    const int64_t nb = s < batch ? (cu[s + 1] - cu[s] + kBk - 1) / kBk : 0;
+    const int64_t ex = block_excl_scan_1024(nb, lds);
+    if (s < batch) bstart[s] = (int32_t)(carry + ex);
+    carry += block_sum_1024(nb, lds);
+  }
+  if (threadIdx.x == 0) bstart[batch] = (int32_t)carry;
+}
+
+// One workgroup per sequence: the sequence of each of its tokens and blocks.
+__global__ __launch_bounds__(256) void seq_fill_kernel(const int64_t* __restrict__ cu,
+                                                       const int32_t* __restrict__ bstart,
+                                                       int32_t* __restrict__ seq_tok, int32_t* __restrict__ seq_blk) {
+  const int s = blockIdx.x;
+  for (int64_t t = cu[s] + threadIdx.x; t < cu[s + 1]; t += 256) seq_tok[t] = s;
+  for (int64_t gb = bstart[s] + threadIdx.x; gb < bstart[s + 1]; gb += 256) seq_blk[gb] = s;
+}
+
 __global__ void fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t val) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += stride) p[e] = val;
@@ -637,6 +700,32 @@ static int inv_tile_queries(int kk) {
   int tq = 1;
   while (tq * 2 * kk <= 4096) tq *= 2;
   return tq;
+}
+
+SeqTables seq_tables_layout(int64_t T, int batch, int64_t Bt) {
+  SeqTables S{};
+  if (batch <= 0) return S;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) & ~size_t(255);
+    return o;
+  };
+  S.bstart = take(sizeof(int32_t) * ((size_t)batch + 1));
+  S.seq_tok = take(sizeof(int32_t) * (size_t)T);
+  S.seq_blk = take(sizeof(int32_t) * (size_t)Bt);
+  S.total = off;
+  return S;
+}
+
+hipError_t launch_seq_tables(const int64_t* cu, int batch, uint8_t* ws, const SeqTables& S, hipStream_t stream) {
+  int32_t* bstart = reinterpret_cast<int32_t*>(ws + S.bstart);
+  seq_block_starts_kernel<<<dim3(1), dim3(kScanTile), 0, stream>>>(cu, batch, bstart);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  seq_fill_kernel<<<dim3((unsigned)batch), dim3(256), 0, stream>>>(cu, bstart, reinterpret_cast<int32_t*>(ws + S.seq_tok),
+                                                                   reinterpret_cast<int32_t*>(ws + S.seq_blk));
+  return hipGetLastError();
 }
 
 AttnWorkspace attn_workspace_layout(int64_t W, int H_q, int H_kv, int kk, int64_t B) {
@@ -678,11 +767,10 @@ AttnWorkspace attn_workspace_layout(int64_t W, int H_q, int H_kv, int kk, int64_
 }
 
 hipError_t launch_sparse_attn_window(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                     const int32_t* block_idx, int64_t N, int H_q, int H_kv, int kk,
-                                     float scale, int64_t w0, int64_t W, int num_cus, float* o, float* lse,
-                                     uint8_t* ws, const AttnWorkspace& L, hipStream_t stream,
+                                     const int32_t* block_idx, int64_t N, int64_t B, const SeqInfo& si, int H_q,
+                                     int H_kv, int kk, float scale, int64_t w0, int64_t W, int num_cus, float* o,
+                                     float* lse, uint8_t* ws, const AttnWorkspace& L, hipStream_t stream,
                                      const hipEvent_t* events) {
-  const int64_t B = (N + kBk - 1) / kBk;
   const int64_t lists = (int64_t)H_kv * L.nW * B;
   const int G = H_q / H_kv;
   int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
@@ -703,7 +791,7 @@ hipError_t launch_sparse_attn_window(const uint16_t* q, const uint16_t* k, const
   const int TQ = inv_tile_queries(kk);
   const dim3 igrid((unsigned)((W + TQ - 1) / TQ), (unsigned)H_kv);
   const size_t lds_count = sizeof(int32_t) * B;
-  inv_count_kernel<<<igrid, dim3(256), lds_count, stream>>>(block_idx, w0, W, H_kv, kk, B, TQ, L.WQ, L.nW,
+  inv_count_kernel<<<igrid, dim3(256), lds_count, stream>>>(block_idx, si, w0, W, H_kv, kk, B, TQ, L.WQ, L.nW,
                                                              counts);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const unsigned tiles = (unsigned)((lists + kScanTile - 1) / kScanTile);
@@ -713,8 +801,8 @@ hipError_t launch_sparse_attn_window(const uint16_t* q, const uint16_t* k, const
   inv_scan_write_kernel<<<dim3(tiles), dim3(kScanTile), 0, stream>>>(counts, lists, L.item_q, tsum, cursor, items,
                                                                     n_items);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  inv_scatter_kernel<16><<<igrid, dim3(256), 2 * lds_count, stream>>>(block_idx, w0, W, H_kv, kk, B, TQ, L.WQ,
-                                                                      L.nW, cursor, pairs);
+  inv_scatter_kernel<16><<<igrid, dim3(256), 2 * lds_count, stream>>>(block_idx, si, w0, W, H_kv, kk, B, TQ,
+                                                                      L.WQ, L.nW, cursor, pairs);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
   int64_t grid = (int64_t)num_cus * 2;
@@ -726,7 +814,7 @@ hipError_t launch_sparse_attn_window(const uint16_t* q, const uint16_t* k, const
 #define MSA_ATTN_CASE(GG)                                                                            \
   case GG:                                                                                           \
     attn_kvouter_kernel<GG><<<dim3((unsigned)grid), dim3(kAttnThreads), 0, stream>>>(                \
-        q, k, v, items, n_items, pairs, N, H_kv, B, L.nW, kk, w0, scale_log2, opart, lpart);         \
+        q, k, v, items, n_items, pairs, N, si, H_kv, B, L.nW, kk, w0, scale_log2, opart, lpart);     \
     break;
     MSA_ATTN_CASE(1)
     MSA_ATTN_CASE(2)
@@ -749,9 +837,9 @@ hipError_t launch_sparse_attn_window(const uint16_t* q, const uint16_t* k, const
 #define MSA_COMBINE_CASE(GG)                                                                          \
   case GG:                                                                                           \
     if (kk <= 16)                                                                                    \
-      combine_kernel<GG, 16><<<cgrid, dim3(256), 0, stream>>>(opart, lpart, block_idx, w0, W, H_kv, kk, B, o, lse); \
+      combine_kernel<GG, 16><<<cgrid, dim3(256), 0, stream>>>(opart, lpart, block_idx, si, w0, W, H_kv, kk, o, lse); \
     else                                                                                             \
-      combine_kernel<GG, 32><<<cgrid, dim3(256), 0, stream>>>(opart, lpart, block_idx, w0, W, H_kv, kk, B, o, lse); \
+      combine_kernel<GG, 32><<<cgrid, dim3(256), 0, stream>>>(opart, lpart, block_idx, si, w0, W, H_kv, kk, o, lse); \
     break;
     MSA_COMBINE_CASE(1)
     MSA_COMBINE_CASE(2)

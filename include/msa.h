@@ -94,6 +94,38 @@ msa_status_t msa_sparse_attn_fwd(const void* q, const void* k, const void* v,
                                  int B_k, int k_sel, float scale, float* o, float* lse, void* ws,
                                  size_t ws_bytes, void* hip_stream);
 
+/* ------------------------------------------------------------------ Packed sequences
+ * Variable-length prefill: `batch` independent sequences packed along the token
+ * axis, each with its own causal mask, block grid and local block (every position
+ * in Eq. 6 - Eq. 8 counts from the start of its own sequence).  The pages train
+ * on such packed documents; the arithmetic per sequence is that of the calls above.
+ *   cu_seqlens int64 [batch + 1], device memory: cu[0] = 0, non-decreasing,
+ *              cu[batch] = T; sequence s holds tokens cu[s] .. cu[s+1]-1 (length 0
+ *              is allowed).  Not checked on the device: other values read out of
+ *              bounds.
+ *   Tensors are those of the calls above with N replaced by T (rows stay global);
+ *   block_idx entries are block numbers within the row's own sequence.
+ *   Limits: ceil(T / B_k) + batch <= 8192, batch <= 65535.
+ *
+ * msa_index_topk_varlen — max_len (host) bounds every sequence length and sizes the
+ *   launch; for a sequence longer than max_len some of its rows are left unwritten.
+ * msa_sparse_attn_fwd_varlen — the workspace holds sequence tables built on the
+ *   device from cu_seqlens, then the KV-outer buffers; sizes as for
+ *   msa_sparse_attn_fwd.
+ */
+msa_status_t msa_index_topk_varlen(const void* q_idx, const void* k_idx, const int64_t* cu_seqlens,
+                                   int batch, int64_t T, int64_t max_len, int H_kv, int d_idx,
+                                   int B_k, int k, int32_t* block_idx, void* hip_stream);
+size_t msa_sparse_attn_fwd_varlen_workspace(int64_t T, int batch, int H_q, int H_kv, int d_h,
+                                            int B_k, int k);
+size_t msa_sparse_attn_fwd_varlen_workspace_min(int64_t T, int batch, int H_q, int H_kv, int d_h,
+                                                int B_k, int k);
+msa_status_t msa_sparse_attn_fwd_varlen(const void* q, const void* k, const void* v,
+                                        const int32_t* block_idx, const int64_t* cu_seqlens,
+                                        int batch, int64_t T, int H_q, int H_kv, int d_h, int B_k,
+                                        int k_sel, float scale, float* o, float* lse, void* ws,
+                                        size_t ws_bytes, void* hip_stream);
+
 /* ------------------------------------------------------------------ Decode
  * msa_decode — one new token per sequence against packed variable-length caches.
  * The new token's K/V and index key are already the last cache entry of its

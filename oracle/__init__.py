@@ -203,3 +203,50 @@ def decode_attn(q, k_cache, v_cache, cu_seqlens, block_idx, B_k: int, scale: flo
     _load().msa_oracle_decode_attn(_ptr(qq), _ptr(kc), _ptr(vc), _ptr(cu), batch, H_q, H_kv, d_h, B_k, kk,
                                    float(scale), _ptr(bi), _ptr(o), _ptr(lse))
     return o, lse
+
+
+def _cu(cu_seqlens) -> np.ndarray:
+    try:
+        import torch
+        if isinstance(cu_seqlens, torch.Tensor):
+            cu_seqlens = cu_seqlens.cpu().numpy()
+    except ImportError:
+        pass
+    return np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+
+
+def index_topk_varlen(q_idx, k_idx, cu_seqlens, k: int, B_k: int, want_scores: bool = False):
+    """Packed sequences, each its own instance of Eq. 6-7 (positions count from the
+    sequence start).  Returns block_idx [T, H_kv, k] with sequence-local block numbers
+    [, per-sequence score arrays M_s]."""
+    qi, ki = _u16(q_idx), _u16(k_idx)
+    cu = _cu(cu_seqlens)
+    T, H_kv, _ = qi.shape
+    out = np.full((T, H_kv, k), -1, dtype=np.int32)
+    Ms = []
+    for s in range(cu.size - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if b == a:
+            Ms.append(None)
+            continue
+        M = block_scores(qi[a:b], ki[a:b], B_k)
+        out[a:b] = topk(M, k, B_k)
+        Ms.append(M)
+    return (out, Ms) if want_scores else out
+
+
+def sparse_attn_varlen(q, k, v, block_idx, cu_seqlens, B_k: int, scale: float | None = None):
+    """Packed sequences, each its own instance of Eq. 8 over its rows of block_idx
+    (sequence-local block numbers).  Returns (o [T,H_q,d_h], lse [T,H_q]) float64."""
+    qq, kk_, vv = _u16(q), _u16(k), _u16(v)
+    cu = _cu(cu_seqlens)
+    bi = np.asarray(block_idx, dtype=np.int32)
+    T, H_q, d_h = qq.shape
+    o = np.zeros((T, H_q, d_h), dtype=np.float64)
+    lse = np.full((T, H_q), -np.inf, dtype=np.float64)
+    for s in range(cu.size - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if b == a:
+            continue
+        o[a:b], lse[a:b] = sparse_attn(qq[a:b], kk_[a:b], vv[a:b], bi[a:b], B_k, scale)
+    return o, lse

@@ -259,3 +259,37 @@ def small_prefill(N: int, H_q: int, H_kv: int, k: int, seed: int, mode: str = "l
     cfg = PrefillConfig(f"small_N{N}", N=N, H_q=H_q, H_kv=H_kv, k=k, d_h=d_h, d_idx=d_idx, B_k=B_k,
                         needles=needles, seed=seed)
     return make_prefill(cfg, mode, device)
+
+
+@dataclass
+class PackedPrefillInputs:
+    lengths: list
+    cu_seqlens: torch.Tensor  # [batch + 1] int64 (on ``device``)
+    q: torch.Tensor           # [T, H_q, d_h] bf16
+    k: torch.Tensor           # [T, H_kv, d_h] bf16
+    v: torch.Tensor           # [T, H_kv, d_h] bf16
+    q_idx: torch.Tensor       # [T, H_kv, d_idx] bf16
+    k_idx: torch.Tensor       # [T, d_idx] bf16
+
+
+def packed_prefill(lengths, H_q: int, H_kv: int, k: int, seed: int, mode: str = "literal", needles: int = 1,
+                   device="cpu") -> PackedPrefillInputs:
+    """Packed variable-length prefill: sequence s is ``small_prefill`` of its own length
+    with seed ``seed + s`` (its own sink block and needles), concatenated on the
+    token axis."""
+    parts = []
+    for s, L in enumerate(lengths):
+        if L == 0:
+            continue
+        fits = (int(L) + 127) // 128 - 1 >= needles * H_kv
+        parts.append(small_prefill(int(L), H_q, H_kv, k, seed + s, mode, needles=needles if fits else 0,
+                                   device=device))
+    cu = torch.zeros(len(lengths) + 1, dtype=torch.int64)
+    cu[1:] = torch.cumsum(torch.tensor(list(lengths), dtype=torch.int64), 0)
+
+    def cat(name, shape_tail):
+        ts = [getattr(p, name) for p in parts]
+        return torch.cat(ts) if ts else torch.empty((0, *shape_tail), dtype=torch.bfloat16, device=device)
+
+    return PackedPrefillInputs(list(lengths), cu.to(device), cat("q", (H_q, 128)), cat("k", (H_kv, 128)),
+                               cat("v", (H_kv, 128)), cat("q_idx", (H_kv, 64)), cat("k_idx", (64,)))

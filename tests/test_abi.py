@@ -20,8 +20,8 @@ def _declared():
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
-        from block_sparse_gqa_index_amd.build import build
-        build()
+        from __graft_entry__ import load_builder
+        load_builder().build()
     import block_sparse_gqa_index_amd as m
     return m
 
@@ -141,3 +141,35 @@ def test_binding_fails_loudly_without_library(tmp_path):
     r = subprocess.run([sys.executable, "-c", "import block_sparse_gqa_index_amd"], cwd=tmp_path,
                        capture_output=True, text=True)
     assert r.returncode != 0 and "libmsa.so is missing" in r.stderr
+
+
+def test_varlen_rejects_bad_arguments(lib):
+    raw = lib.raw()
+    f = 0x10000
+
+    def idx(batch=3, T=4096, max_len=2048, H_kv=2, d_idx=64, B_k=128, k=8, cu=f, q=f):
+        return raw.msa_index_topk_varlen(q, f, cu, batch, T, max_len, H_kv, d_idx, B_k, k, f, None)
+
+    assert idx(batch=-1) == lib.MSA_ERR_INVALID_ARG
+    assert idx(max_len=4097) == lib.MSA_ERR_INVALID_ARG  # longer than T
+    assert idx(max_len=0) == lib.MSA_ERR_INVALID_ARG
+    assert idx(cu=None) == lib.MSA_ERR_INVALID_ARG
+    assert idx(cu=f + 4) == lib.MSA_ERR_INVALID_ARG
+    assert idx(d_idx=128) == lib.MSA_ERR_UNSUPPORTED
+    assert idx(T=8192 * 128, max_len=128, batch=2) == lib.MSA_ERR_UNSUPPORTED  # blocks + batch > 8192
+    assert idx(batch=0, cu=None, q=None) == lib.MSA_OK
+
+    def attn(batch=3, T=4096, H_q=8, H_kv=2, d_h=128, k=8, ws=f, ws_bytes=1 << 40, cu=f, scale=0.088):
+        return raw.msa_sparse_attn_fwd_varlen(f, f, f, f, cu, batch, T, H_q, H_kv, d_h, 128, k, scale, f, f, ws,
+                                              ws_bytes, None)
+
+    assert attn(d_h=64) == lib.MSA_ERR_UNSUPPORTED
+    assert attn(cu=None) == lib.MSA_ERR_INVALID_ARG
+    assert attn(scale=-1.0) == lib.MSA_ERR_INVALID_ARG
+    assert attn(ws=None) == lib.MSA_ERR_WORKSPACE
+    need = raw.msa_sparse_attn_fwd_varlen_workspace_min(4096, 3, 8, 2, 128, 128, 8)
+    # the sequence tables sit in front of the per-window buffers
+    assert need > raw.msa_sparse_attn_fwd_workspace_min(4096, 8, 2, 128, 128, 8)
+    assert attn(ws_bytes=need - 1) == lib.MSA_ERR_WORKSPACE
+    assert attn(batch=0) == lib.MSA_OK
+    assert raw.msa_sparse_attn_fwd_varlen_workspace(4096, 0, 8, 2, 128, 128, 8) == 0

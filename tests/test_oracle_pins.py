@@ -294,3 +294,48 @@ def test_decode_attn_on_given_selection_equals_decode():
     o2, l2 = oracle.decode_attn(d.q, d.k_cache, d.v_cache, d.cu_seqlens, bi, 128)
     np.testing.assert_array_equal(o, o2)
     np.testing.assert_array_equal(lse, l2)
+
+
+# --- Packed sequences --------------------------------------------------------------------
+
+def test_varlen_first_sequence_equals_causal_prefix():
+    # Causality makes the rows of the first packed sequence a prefix problem: the
+    # unpacked oracle over the concatenation gives them the same selection and output
+    # when the first sequence ends on a block boundary.  Other sequences must differ
+    # from the concatenated run (they may not see earlier sequences).
+    lengths = [256, 300, 0, 77]
+    p = synth.packed_prefill(lengths, H_q=4, H_kv=2, k=3, seed=21)
+    bi = oracle.index_topk_varlen(p.q_idx, p.k_idx, p.cu_seqlens, 3, 128)
+    o, lse = oracle.sparse_attn_varlen(p.q, p.k, p.v, bi, p.cu_seqlens, 128)
+    T = sum(lengths)
+    M_all = oracle.block_scores(p.q_idx, p.k_idx, 128)
+    bi_all = oracle.topk(M_all, 3, 128)
+    np.testing.assert_array_equal(bi[:256], bi_all[:256])
+    o_all, l_all = oracle.sparse_attn(p.q, p.k, p.v, bi_all[:256], 128, rows=range(256))
+    np.testing.assert_array_equal(o[:256], o_all)
+    np.testing.assert_array_equal(lse[:256], l_all)
+    # Second sequence: its local block numbering restarts at 0.
+    pos = np.arange(300)
+    assert np.all((bi[256:556] == (pos // 128)[:, None, None]).any(axis=2))
+    # Sequence 3 (77 tokens, one block): everything selects block 0 and pads.
+    assert np.all(bi[556:, :, 0] == 0) and np.all(bi[556:, :, 1:] == -1)
+    assert bi.shape == (T, 2, 3)
+
+
+def test_varlen_sequence_is_independent_of_neighbours():
+    # Replacing every other sequence's tokens leaves a sequence's results unchanged.
+    lengths = [200, 333, 129]
+    a = synth.packed_prefill(lengths, H_q=4, H_kv=2, k=2, seed=5)
+    b = synth.packed_prefill(lengths, H_q=4, H_kv=2, k=2, seed=5)
+    for name in ("q", "k", "v", "q_idx", "k_idx"):
+        t = getattr(b, name)
+        t[:200] = -t[:200]
+        t[533:] = 0.5 * t[533:]
+    ra = oracle.index_topk_varlen(a.q_idx, a.k_idx, a.cu_seqlens, 2, 128)
+    rb = oracle.index_topk_varlen(b.q_idx, b.k_idx, b.cu_seqlens, 2, 128)
+    np.testing.assert_array_equal(ra[200:533], rb[200:533])
+    oa, la = oracle.sparse_attn_varlen(a.q, a.k, a.v, ra, a.cu_seqlens, 128)
+    ob, lb = oracle.sparse_attn_varlen(b.q, b.k, b.v, rb, b.cu_seqlens, 128)
+    np.testing.assert_array_equal(oa[200:533], ob[200:533])
+    np.testing.assert_array_equal(la[200:533], lb[200:533])
+    assert not np.array_equal(oa[:200], ob[:200])
