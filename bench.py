@@ -59,18 +59,30 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 ROOT = os.path.dirname(os.path.abspath(__file__))
 # Sources the KV-outer kernel is compiled from: a recorded traffic figure holds only
 # while their hash is unchanged.
-ATTN_SOURCES = ("block_sparse_gqa_index_amd/csrc/sparse_attn.hip", "block_sparse_gqa_index_amd/csrc/msa_device.h",
-                "block_sparse_gqa_index_amd/csrc/msa_kernels.h")
+# What decides the KV-outer kernel's memory traffic: its own code (the phase-1 part
+# of sparse_attn.hip), the workspace layout and the launches up to it, and the shared
+# device helpers.  The counter summary is reused only while these are unchanged.
+ATTN_FILE = "block_sparse_gqa_index_amd/csrc/sparse_attn.hip"
+ATTN_HELPERS = ("block_sparse_gqa_index_amd/csrc/msa_device.h",)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kvouter_kernel_128k_traffic.txt")
+
+
+def _attn_kernel_text() -> str:
+    src = open(os.path.join(ROOT, ATTN_FILE)).read()
+    p1 = src.index("// " + "-" * 69 + " phase 1")
+    p2 = src.index("// " + "-" * 69 + " phase 2")
+    lay = src.index("AttnWorkspace attn_workspace_layout(")
+    launch = src.index("hipError_t launch_sparse_attn_window(")
+    p1_end = src.index("hipEventRecord(events[2]", launch)  # the launcher up to phase 1's launch
+    parts = [src[p1:p2], src[lay:src.index("\n}\n", lay)], src[launch:p1_end]]
+    for f in ATTN_HELPERS:
+        parts.append(open(os.path.join(ROOT, f)).read())
+    return "\0".join(parts)
 
 
 def attn_source_hash() -> str:
     import hashlib
-    h = hashlib.sha256()
-    for f in ATTN_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()
+    return hashlib.sha256(_attn_kernel_text().encode()).hexdigest()
 
 
 def recorded_traffic(mode: str):
@@ -127,6 +139,50 @@ def write_traffic_summary(fetch_csv: str, write_csv: str, mode: str, command: st
     with open(TRAFFIC_FILE, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     return TRAFFIC_FILE
+
+
+STATS_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                          "prefill_128k_decode_128k_kernel_stats.txt")
+
+
+def write_stats_summary(stats_csv: str, log_path: str, command: str) -> str:
+    """Short text form of a rocprofv3 ``--kernel-trace --stats`` run of this script: the
+    library's kernels from ``*_kernel_stats.csv`` and the HIP-event phase times the same
+    run printed in its JSON line (``log_path``)."""
+    import csv
+    import re
+    rows = []
+    for r in csv.DictReader(open(stats_csv)):
+        m = re.search(r"msa::\(anonymous namespace\)::([A-Za-z0-9_]+(?:<[^()]*?>)?)\(", r["Name"])
+        if m:
+            rows.append((m.group(1), int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                         float(r["MaxNs"]) / 1e3, float(r["TotalDurationNs"])))
+    rows.sort(key=lambda x: -x[5])
+    res = None
+    for line in open(log_path):
+        if line.startswith("{") and '"metric"' in line:
+            res = json.loads(line)
+    if res is None:
+        raise SystemExit(f"{log_path}: no result line")
+    pre, dec = res["prefill"], res.get("decode")
+    lines = [
+        "# rocprofv3 kernel statistics: " + res["config"]["workload"] + f" ({res['config']['mode']} inputs)",
+        "# and " + (dec["workload"] if dec else "no decode") + "; MI355X, one GPU.",
+        f"# command: {command}",
+        f"# {res['warmup']} warmup + {res['steps']} timed prefill steps; rows of the stats CSV for the",
+        "# library's kernels (times in microseconds).  HIP events in the same run (timed steps):",
+        f"# index {pre['ms_index_topk'] * 1e3:.1f} us, inverse index {pre['ms_inverse_index'] * 1e3:.1f} us, "
+        f"phase 1 {pre['ms_kvouter_phase1'] * 1e3:.1f} us, combine {pre['ms_combine'] * 1e3:.1f} us"
+        + (f"; decode step {dec['ms_per_step'] * 1e3:.1f} us" if dec else "") + ".",
+        "",
+        f"{'kernel':<44} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10}",
+    ]
+    for name, calls, avg, mn, mx, _ in rows:
+        lines.append(f"{name:<44} {calls:>6} {avg:>10.1f} {mn:>10.1f} {mx:>10.1f}")
+    os.makedirs(os.path.dirname(STATS_FILE), exist_ok=True)
+    with open(STATS_FILE, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return STATS_FILE
 
 
 COPY_BYTES = 1 << 30
@@ -313,8 +369,13 @@ def main(argv=None) -> int:
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic summary from two rocprofv3 counter CSVs and exit")
     ap.add_argument("--traffic-command", default="", help="the command the counter CSVs came from")
+    ap.add_argument("--stats-from", nargs=2, metavar=("STATS_CSV", "RUN_LOG"),
+                    help="write the kernel statistics summary from a rocprofv3 --stats run and exit")
     args = ap.parse_args(argv)
 
+    if args.stats_from:
+        print(write_stats_summary(args.stats_from[0], args.stats_from[1], args.traffic_command))
+        return 0
     if args.traffic_from:
         print(write_traffic_summary(args.traffic_from[0], args.traffic_from[1], args.mode, args.traffic_command))
         return 0
