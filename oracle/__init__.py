@@ -61,6 +61,7 @@ def _load():
     lib.msa_oracle_decode.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, dbl,
                                       P, P, P, P, i64]
     lib.msa_oracle_decode_attn.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, dbl, P, P, P]
+    lib.msa_oracle_sparse_kl.argtypes = [P, P, P, P, P, i64, i32, i32, i32, i32, i32, i32, dbl, P, i64, P, P]
     _lib = lib
     return lib
 
@@ -150,6 +151,26 @@ def sparse_attn(q, k, v, block_idx, B_k: int, scale: float | None = None, rows=N
     _load().msa_oracle_sparse_attn(_ptr(qq), _ptr(kk_), _ptr(vv), _ptr(bi), N, H_q, H_kv, d_h, B_k, kk,
                                    float(scale), None if r is None else _ptr(r), nrows, _ptr(o), _ptr(lse))
     return o, lse
+
+
+def sparse_kl(q, k, q_idx, k_idx, block_idx, B_k: int, scale: float | None = None, rows=None):
+    """Eq. 9-10 per (query, group) on the selected token set: returns (kl [nrows, H_kv],
+    lse_idx [nrows, H_kv]) float64; the loss of Eq. 10 is kl.mean() over all rows."""
+    qq, kk_, qi, ki = _u16(q), _u16(k), _u16(q_idx), _u16(k_idx)
+    N, H_q, d_h = qq.shape
+    H_kv, d_idx = qi.shape[1], qi.shape[2]
+    assert kk_.shape == (N, H_kv, d_h) and ki.shape == (N, d_idx)
+    r, nrows = _rows(rows, N)
+    bi = np.ascontiguousarray(np.asarray(block_idx), dtype=np.int32)
+    assert bi.shape[0] == nrows and bi.shape[1] == H_kv
+    if scale is None:
+        scale = 1.0 / np.sqrt(d_h)
+    kl = np.empty((nrows, H_kv), dtype=np.float64)
+    lse_idx = np.empty((nrows, H_kv), dtype=np.float64)
+    _load().msa_oracle_sparse_kl(_ptr(qq), _ptr(kk_), _ptr(qi), _ptr(ki), _ptr(bi), N, H_q, H_kv, d_h, d_idx,
+                                 B_k, bi.shape[2], float(scale), None if r is None else _ptr(r), nrows,
+                                 _ptr(kl), _ptr(lse_idx))
+    return kl, lse_idx
 
 
 def decode(q, q_idx, k_cache, v_cache, k_idx_cache, cu_seqlens, k: int, B_k: int,

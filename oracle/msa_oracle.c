@@ -6,6 +6,7 @@
  *   Eq. 6  index scores + max-pool   -> score_row()
  *   Eq. 7  Top-k, local block forced -> topk_row()
  *   Eq. 8  softmax over the chosen   -> attn_row()
+ *   Eq. 9-10 KL alignment per row    -> kl_row()
  * (page "MiniMax Sparse Attention (MSA)" paper review, section 3; page
  * "papers.chlience.com" reading notes, section 5.1 and 5.1.1.)
  * No blocking, fusion or reordering beyond the definitions; OpenMP only
@@ -246,6 +247,95 @@ void msa_oracle_decode_attn(const uint16_t* q, const uint16_t* k_cache, const ui
       }
     }
     free(s_buf);
+    free(inset);
+  }
+}
+
+/*
+ * Eq. 9-10 for one (query, group) row.  T is the selected token set (tokens j <= i
+ * of the chosen blocks).  The index distribution is the softmax of the index
+ * scores over T; the teacher is the mean over the group's G heads of each head's
+ * Main Branch softmax over T.  Returns KL(teacher || index) and writes the log
+ * partition of the index scores over T.  An empty T gives 0 and -inf.
+ */
+static double kl_row(const uint16_t* qh0, const uint16_t* kbase, int64_t kstride, const uint16_t* qiv,
+                     const uint16_t* kidx, int64_t i, int64_t N, int G, int d_h, int d_idx, int B_k,
+                     const char* inset, double scale, double* lse_idx_out, int64_t* tok, double* sidx,
+                     double* s_buf, double* P) {
+  int64_t nt = 0;
+  int64_t jmax = i < N - 1 ? i : N - 1;
+  for (int64_t j = 0; j <= jmax; ++j)
+    if (inset[block_of(j, B_k)]) tok[nt++] = j;
+  if (nt == 0) {
+    *lse_idx_out = -INFINITY;
+    return 0.0;
+  }
+  /* index distribution (Eq. 9, left) through its log partition */
+  double mi = -INFINITY;
+  for (int64_t t = 0; t < nt; ++t) {
+    double sv = 0.0;
+    for (int d = 0; d < d_idx; ++d) sv += bf16(qiv[d]) * bf16(kidx[tok[t] * d_idx + d]);
+    sidx[t] = sv / sqrt((double)d_idx);
+    if (sidx[t] > mi) mi = sidx[t];
+  }
+  double li = 0.0;
+  for (int64_t t = 0; t < nt; ++t) li += exp(sidx[t] - mi);
+  double lse_idx = mi + log(li);
+  *lse_idx_out = lse_idx;
+  /* teacher (Eq. 9, right): mean over heads of each head's softmax over T */
+  for (int64_t t = 0; t < nt; ++t) P[t] = 0.0;
+  for (int g = 0; g < G; ++g) {
+    const uint16_t* qv = qh0 + (int64_t)g * d_h;
+    double m = -INFINITY;
+    for (int64_t t = 0; t < nt; ++t) {
+      double sv = 0.0;
+      for (int d = 0; d < d_h; ++d) sv += bf16(qv[d]) * bf16(kbase[tok[t] * kstride + d]);
+      s_buf[t] = sv * scale;
+      if (s_buf[t] > m) m = s_buf[t];
+    }
+    double l = 0.0;
+    for (int64_t t = 0; t < nt; ++t) l += exp(s_buf[t] - m);
+    for (int64_t t = 0; t < nt; ++t) P[t] += exp(s_buf[t] - m) / l / G;
+  }
+  /* Eq. 10 summand: KL(P || P_idx) = sum_j P_j (log P_j - log P_idx_j) */
+  double kl = 0.0;
+  for (int64_t t = 0; t < nt; ++t)
+    if (P[t] > 0.0) kl += P[t] * (log(P[t]) - (sidx[t] - lse_idx));
+  return kl;
+}
+
+void msa_oracle_sparse_kl(const uint16_t* q, const uint16_t* k, const uint16_t* q_idx,
+                          const uint16_t* k_idx, const int32_t* block_idx, int64_t N, int H_q,
+                          int H_kv, int d_h, int d_idx, int B_k, int kk, double scale,
+                          const int64_t* rows, int64_t nrows, double* kl, double* lse_idx) {
+  int64_t B = msa_oracle_num_blocks(N, B_k);
+  int G = H_q / H_kv;
+#pragma omp parallel
+  {
+    size_t cap = (size_t)(N > 0 ? N : 1);
+    char* inset = (char*)malloc((size_t)B + 1);
+    int64_t* tok = (int64_t*)malloc(sizeof(int64_t) * cap);
+    double* sidx = (double*)malloc(sizeof(double) * cap);
+    double* s_buf = (double*)malloc(sizeof(double) * cap);
+    double* P = (double*)malloc(sizeof(double) * cap);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t n = 0; n < nrows; ++n) {
+      int64_t i = rows ? rows[n] : n;
+      for (int r = 0; r < H_kv; ++r) {
+        memset(inset, 0, (size_t)B + 1);
+        const int32_t* sel = block_idx + (n * H_kv + r) * kk;
+        for (int s = 0; s < kk; ++s)
+          if (sel[s] >= 0 && sel[s] < B) inset[sel[s]] = 1;
+        kl[n * H_kv + r] = kl_row(q + (i * H_q + (int64_t)r * G) * d_h, k + (int64_t)r * d_h,
+                                  (int64_t)H_kv * d_h, q_idx + (i * H_kv + r) * d_idx, k_idx, i, N, G,
+                                  d_h, d_idx, B_k, inset, scale, lse_idx + n * H_kv + r, tok, sidx,
+                                  s_buf, P);
+      }
+    }
+    free(P);
+    free(s_buf);
+    free(sidx);
+    free(tok);
     free(inset);
   }
 }

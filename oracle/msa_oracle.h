@@ -7,7 +7,7 @@
  *
  * Plain loops in double precision over the same bf16 input bytes the GPU sees.
  * Each function follows one step of the pages (page "MiniMax Sparse Attention
- * (MSA)" paper review, section 3 "core formulas", Eq. 4, 6, 7, 8; page
+ * (MSA)" paper review, section 3 "core formulas", Eq. 4, 6, 7, 8, 9, 10; page
  * "papers.chlience.com" reading notes, section 5.1.1 "block Top-k procedure").
  *
  * Conventions shared by all functions:
@@ -86,6 +86,22 @@ void msa_oracle_decode_attn(const uint16_t* q, const uint16_t* k_cache, const ui
                             const int64_t* cu_seqlens, int batch, int H_q, int H_kv, int d_h,
                             int B_k, int kk, double scale, const int32_t* block_idx_in, double* o,
                             double* lse);
+
+/*
+ * Eq. 9-10 (KL alignment) for row n (position i) and group r, over the selected
+ * token set T = { j <= i : block_of(j) listed in block_idx[n][r][:] }:
+ *   P_idx(j) = softmax over T of S_idx(j) = <q_idx[i][r], k_idx[j]> / sqrt(d_idx),
+ *   P(j)     = (1/G) sum over the group's heads h of softmax over T of
+ *              scale * <q[i][h], k[j][r]>,
+ *   kl[n][r] = sum over j in T of P(j) log(P(j) / P_idx(j))  (0 log 0 = 0),
+ *   lse_idx[n][r] = log sum over j in T of exp(S_idx(j)).
+ * Empty T: kl = 0, lse_idx = -inf.  The loss of Eq. 10 is the mean of kl over all
+ * (i, r).  kl, lse_idx: [nrows][H_kv] (double).
+ */
+void msa_oracle_sparse_kl(const uint16_t* q, const uint16_t* k, const uint16_t* q_idx,
+                          const uint16_t* k_idx, const int32_t* block_idx, int64_t N, int H_q,
+                          int H_kv, int d_h, int d_idx, int B_k, int kk, double scale,
+                          const int64_t* rows, int64_t nrows, double* kl, double* lse_idx);
 
 #ifdef __cplusplus
 }

@@ -34,6 +34,14 @@ MUTANTS = [
     ("attn_value_from_key", "orow[d] += p * bf16(vbase[j * stride + d]);",
      "orow[d] += p * bf16(kbase[j * stride + d]);"),
     ("decode_query_position", "int64_t i = L - 1; /* the new token", "int64_t i = L - 2; /* the new token"),
+    ("kl_no_head_mean", "P[t] += exp(s_buf[t] - m) / l / G;", "P[t] += exp(s_buf[t] - m) / l;"),
+    ("kl_mean_of_log_probs", "P[t] += exp(s_buf[t] - m) / l / G;", "P[t] *= pow(exp(s_buf[t] - m) / l, 1.0 / G);"),
+    ("kl_reversed", "if (P[t] > 0.0) kl += P[t] * (log(P[t]) - (sidx[t] - lse_idx));",
+     "kl += exp(sidx[t] - lse_idx) * ((sidx[t] - lse_idx) - log(P[t]));"),
+    ("kl_index_scale_dropped", "sidx[t] = sv / sqrt((double)d_idx);", "sidx[t] = sv;"),
+    ("kl_not_causal", "for (int64_t j = 0; j <= jmax; ++j)\n    if (inset", "for (int64_t j = 0; j < N; ++j)\n    if (inset"),
+    ("kl_index_query_group", "q_idx + (i * H_kv + r) * d_idx", "q_idx + (i * H_kv) * d_idx"),
+    ("kl_lse_idx_missing_max", "double lse_idx = mi + log(li);", "double lse_idx = log(li);"),
 ]
 
 
@@ -54,6 +62,10 @@ def _all_pins():
     yield "lse_merge", pins.test_lse_merge_of_disjoint_partials
     yield "order", pins.test_block_order_and_empty_sets
     yield "decode", pins.test_decode_equals_last_prefill_row
+    yield "kl_zero", pins.test_kl_zero_when_index_scores_equal_main_scores
+    yield "kl_closed_form", pins.test_kl_closed_form_mean_of_two_heads
+    yield "kl_token_set", pins.test_kl_token_set_is_causal_and_selected
+    yield "kl_groups", pins.test_kl_is_nonnegative_and_groups_are_separate
 
 
 @pytest.mark.parametrize("mutant", MUTANTS, ids=lambda m: m[0])

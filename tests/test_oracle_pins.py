@@ -339,3 +339,83 @@ def test_varlen_sequence_is_independent_of_neighbours():
     np.testing.assert_array_equal(oa[200:533], ob[200:533])
     np.testing.assert_array_equal(la[200:533], lb[200:533])
     assert not np.array_equal(oa[:200], ob[:200])
+
+
+# --- Eq. 9-10: KL alignment ---------------------------------------------------------------
+
+def _bf(a):
+    return torch.tensor(np.asarray(a, dtype=np.float32)).to(torch.bfloat16)
+
+
+def test_kl_zero_when_index_scores_equal_main_scores():
+    # q and k live in the first 64 dims, the index inputs are those same 64 dims and
+    # the main scale is 1/sqrt(64): every index score equals every main score, and
+    # the two heads of the group are identical, so the teacher equals the index
+    # distribution and KL = 0; the index log partition is then the main lse.
+    N, d = 700, 64
+    g = torch.Generator().manual_seed(31)
+    q0 = torch.randn(N, 1, d, generator=g)
+    k0 = torch.randn(N, 1, d, generator=g)
+    q = torch.zeros(N, 2, 128)
+    q[:, 0, :d] = q0[:, 0]
+    q[:, 1, :d] = q0[:, 0]
+    k = torch.zeros(N, 1, 128)
+    k[:, 0, :d] = k0[:, 0]
+    q, k = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    q_idx, k_idx = q0.to(torch.bfloat16), k0[:, 0].to(torch.bfloat16)
+    bi = oracle.topk(oracle.block_scores(q_idx, k_idx, 128), 3, 128)
+    kl, lse_idx = oracle.sparse_kl(q, k, q_idx, k_idx, bi, 128, scale=0.125)
+    assert np.max(np.abs(kl)) < 1e-12
+    _, lse = oracle.sparse_attn(q, k, k, bi, 128, scale=0.125)
+    np.testing.assert_allclose(lse_idx[:, 0], lse[:, 0], rtol=0, atol=1e-12)
+
+
+def test_kl_closed_form_mean_of_two_heads():
+    # Uniform index scores (k_idx = 0): P_idx = 1/n.  Main scores take two levels:
+    # head h scores alpha_h on the first m tokens and 0 elsewhere (scale 1), so each
+    # head's softmax and their mean have closed forms, and so has the KL.
+    N, n, m = 256, 256, 32
+    alphas = (1.0, 2.0)
+    q = np.zeros((N, 2, 128), np.float32)
+    k = np.zeros((N, 1, 128), np.float32)
+    q[:, 0, 0], q[:, 1, 0] = alphas
+    k[:m, 0, 0] = 1.0
+    q_idx = np.ones((N, 1, 64), np.float32)
+    k_idx = np.zeros((N, 64), np.float32)
+    bi = np.array([[[0, 1]]], np.int32)
+    kl, lse_idx = oracle.sparse_kl(_bf(q), _bf(k), _bf(q_idx), _bf(k_idx), bi, 128, scale=1.0, rows=[N - 1])
+    pa = sum(math.exp(a) / (m * math.exp(a) + n - m) for a in alphas) / 2
+    pb = sum(1.0 / (m * math.exp(a) + n - m) for a in alphas) / 2
+    want = m * pa * math.log(n * pa) + (n - m) * pb * math.log(n * pb)
+    assert abs(kl[0, 0] - want) < 1e-12
+    assert abs(lse_idx[0, 0] - math.log(n)) < 1e-12
+
+
+def test_kl_token_set_is_causal_and_selected():
+    # With all scores zero both distributions are uniform over the selected causal
+    # tokens: KL = 0 and the index log partition is log |T|.
+    N = 300
+    z3 = _bf(np.zeros((N, 1, 128)))
+    q_idx, k_idx = _bf(np.zeros((N, 1, 64))), _bf(np.zeros((N, 64)))
+    rows = [200, 200, 200, 5, 299]
+    bi = np.array([[[0, 1, -1]], [[1, 7, -1]], [[2, 0, -1]], [[-1, -1, -1]], [[2, 1, 0]]], np.int32)
+    kl, lse_idx = oracle.sparse_kl(z3, z3, q_idx, k_idx, bi, 128, rows=rows)
+    sizes = [201, 73, 128, 0, 300]
+    for t, n in enumerate(sizes):
+        if n == 0:
+            assert kl[t, 0] == 0 and lse_idx[t, 0] == -np.inf
+        else:
+            assert abs(kl[t, 0]) < 1e-12
+            assert abs(lse_idx[t, 0] - math.log(n)) < 1e-12
+
+
+def test_kl_is_nonnegative_and_groups_are_separate():
+    inp = synth.small_prefill(N=900, H_q=8, H_kv=2, k=3, seed=17)
+    bi = oracle.topk(oracle.block_scores(inp.q_idx, inp.k_idx, 128), 3, 128)
+    kl, lse_idx = oracle.sparse_kl(inp.q, inp.k, inp.q_idx, inp.k_idx, bi, 128)
+    assert np.all(kl >= -1e-12) and np.all(np.isfinite(lse_idx))
+    assert kl[1:].mean() > 0.05  # unrelated distributions differ
+    # Group 1 alone (its heads, its KV head, its index query) gives the same numbers.
+    kl1, li1 = oracle.sparse_kl(inp.q[:, 4:], inp.k[:, 1:], inp.q_idx[:, 1:], inp.k_idx, bi[:, 1:], 128)
+    np.testing.assert_array_equal(kl1[:, 0], kl[:, 1])
+    np.testing.assert_array_equal(li1[:, 0], lse_idx[:, 1])
