@@ -42,6 +42,10 @@ _SIGS = {
     "msa_index_block_scores": ([_P, _P, _I64, _I32, _I32, _I32, _P, _P], _I32),
     "msa_topk_from_scores": ([_P, _I64, _I32, _I64, _I32, _I32, _P, _P], _I32),
     "msa_set_profile_events": ([ctypes.POINTER(_P), _I32], _I32),
+    "msa_sparse_kl_fwd_workspace": ([_I64, _I32, _I32, _I32, _I32, _I32, _I32], _SZ),
+    "msa_sparse_kl_fwd_workspace_min": ([_I64, _I32, _I32, _I32, _I32, _I32, _I32], _SZ),
+    "msa_sparse_kl_fwd": ([_P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _F32, _P, _P, _P, _P, _SZ,
+                           _P], _I32),
     "msa_index_topk_varlen": ([_P, _P, _P, _I32, _I64, _I64, _I32, _I32, _I32, _I32, _P, _P], _I32),
     "msa_sparse_attn_fwd_varlen_workspace": ([_I64, _I32, _I32, _I32, _I32, _I32, _I32], _SZ),
     "msa_sparse_attn_fwd_varlen_workspace_min": ([_I64, _I32, _I32, _I32, _I32, _I32, _I32], _SZ),
@@ -171,6 +175,46 @@ def msa_sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block
                                     float(scale), _ptr(o), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
                                     _stream(stream)), "msa_sparse_attn_fwd")
     return o, lse
+
+
+# ----------------------------------------------------------------- KL alignment
+def msa_sparse_kl_fwd_workspace(N: int, H_q: int, H_kv: int, k: int, d_h: int = 128, d_idx: int = 64,
+                                B_k: int = 128, minimum: bool = False) -> int:
+    fn = _lib.msa_sparse_kl_fwd_workspace_min if minimum else _lib.msa_sparse_kl_fwd_workspace
+    return int(fn(N, H_q, H_kv, d_h, d_idx, B_k, k))
+
+
+def msa_sparse_kl_fwd(q: torch.Tensor, k: torch.Tensor, q_idx: torch.Tensor, k_idx: torch.Tensor,
+                      block_idx: torch.Tensor, lse: torch.Tensor, B_k: int = 128, scale: float | None = None,
+                      kl: torch.Tensor | None = None, lse_idx: torch.Tensor | None = None,
+                      loss: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
+    """Eq. 9-10 on the selected tokens.  Returns (kl [N,H_kv], lse_idx [N,H_kv], loss [1]) fp32."""
+    N, H_q, d_h = q.shape
+    H_kv, d_idx = q_idx.shape[1], q_idx.shape[2]
+    kk = block_idx.shape[2]
+    _need(q, "q", torch.bfloat16, (N, H_q, d_h))
+    _need(k, "k", torch.bfloat16, (N, H_kv, d_h))
+    _need(q_idx, "q_idx", torch.bfloat16, (N, H_kv, d_idx))
+    _need(k_idx, "k_idx", torch.bfloat16, (N, d_idx))
+    _need(block_idx, "block_idx", torch.int32, (N, H_kv, kk))
+    _need(lse, "lse", torch.float32, (N, H_q))
+    if scale is None:
+        scale = d_h ** -0.5
+    dev = q.device
+    if kl is None:
+        kl = torch.empty((N, H_kv), dtype=torch.float32, device=dev)
+    if lse_idx is None:
+        lse_idx = torch.empty((N, H_kv), dtype=torch.float32, device=dev)
+    if loss is None:
+        loss = torch.empty((1,), dtype=torch.float32, device=dev)
+    _need(kl, "kl", torch.float32, (N, H_kv))
+    _need(lse_idx, "lse_idx", torch.float32, (N, H_kv))
+    _need(loss, "loss", torch.float32, (1,))
+    ws = _ws(_lib.msa_sparse_kl_fwd_workspace(N, H_q, H_kv, d_h, d_idx, B_k, kk), dev, workspace)
+    _check(_lib.msa_sparse_kl_fwd(_ptr(q), _ptr(k), _ptr(q_idx), _ptr(k_idx), _ptr(block_idx), _ptr(lse), N, H_q,
+                                  H_kv, d_h, d_idx, B_k, kk, float(scale), _ptr(kl), _ptr(lse_idx), _ptr(loss),
+                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "msa_sparse_kl_fwd")
+    return kl, lse_idx, loss
 
 
 # ----------------------------------------------------------------- Packed sequences

@@ -64,12 +64,12 @@ int num_cus() {
 
 // Largest query window (whole blocks of queries, at least one block) whose
 // per-window workspace fits in ws_bytes; B is the list stride in blocks.
-int64_t window_for_bytes(int64_t N, int64_t B, int H_q, int H_kv, int k, size_t ws_bytes) {
+int64_t window_for_bytes(int64_t N, int64_t B, int H_q, int H_kv, int k, size_t ws_bytes, bool kl_parts = false) {
   int64_t lo = 0, hi = (N + msa::kBlockKeys - 1) / msa::kBlockKeys;
   while (lo < hi) {
     const int64_t mid = (lo + hi + 1) / 2;
     const int64_t W = mid * msa::kBlockKeys < N ? mid * msa::kBlockKeys : N;
-    if (msa::attn_workspace_layout(W, H_q, H_kv, k, B).total <= ws_bytes)
+    if (msa::attn_workspace_layout(W, H_q, H_kv, k, B, kl_parts).total <= ws_bytes)
       lo = mid;
     else
       hi = mid - 1;
@@ -296,6 +296,70 @@ msa_status_t msa_sparse_attn_fwd_varlen(const void* q, const void* k, const void
   si.seq_tok = reinterpret_cast<const int32_t*>(w + S.seq_tok);
   si.seq_blk = reinterpret_cast<const int32_t*>(w + S.seq_blk);
   return attn_run(q, k, v, block_idx, T, Bt, si, S, H_q, H_kv, k_sel, scale, o, lse, w, ws_bytes, stream);
+}
+
+// ---------------------------------------------------------------- KL alignment
+static constexpr size_t kKlLossBytes = sizeof(double) * msa::kKlLossParts;
+
+static size_t kl_workspace_bytes(int64_t N, int H_q, int H_kv, int k, bool minimum) {
+  const int64_t B = (N + msa::kBlockKeys - 1) / msa::kBlockKeys;
+  const int64_t Wmin = N < msa::kBlockKeys ? N : msa::kBlockKeys;
+  const int64_t W = minimum ? Wmin : window_for_bytes(N, B, H_q, H_kv, k, kDefaultAttnWorkspace, true);
+  return kKlLossBytes + msa::attn_workspace_layout(W, H_q, H_kv, k, B, true).total;
+}
+
+static msa_status_t check_kl_shape(int64_t N, int H_q, int H_kv, int d_h, int d_idx, int B_k, int k) {
+  msa_status_t st = check_attn_shape(N, H_q, H_kv, d_h, B_k, k);
+  if (st != MSA_OK) return st;
+  if (d_idx != msa::kIndexDim) return fail(MSA_ERR_UNSUPPORTED, "d_idx must be %d (got %d)", msa::kIndexDim, d_idx);
+  if (H_q / H_kv > 32) return fail(MSA_ERR_UNSUPPORTED, "G = H_q / H_kv must be <= 32 for the KL pass");
+  return MSA_OK;
+}
+
+size_t msa_sparse_kl_fwd_workspace(int64_t N, int H_q, int H_kv, int d_h, int d_idx, int B_k, int k) {
+  if (check_kl_shape(N, H_q, H_kv, d_h, d_idx, B_k, k) != MSA_OK || N == 0) return 0;
+  return kl_workspace_bytes(N, H_q, H_kv, k, false);
+}
+
+size_t msa_sparse_kl_fwd_workspace_min(int64_t N, int H_q, int H_kv, int d_h, int d_idx, int B_k, int k) {
+  if (check_kl_shape(N, H_q, H_kv, d_h, d_idx, B_k, k) != MSA_OK || N == 0) return 0;
+  return kl_workspace_bytes(N, H_q, H_kv, k, true);
+}
+
+msa_status_t msa_sparse_kl_fwd(const void* q, const void* k, const void* q_idx, const void* k_idx,
+                               const int32_t* block_idx, const float* lse, int64_t N, int H_q, int H_kv, int d_h,
+                               int d_idx, int B_k, int k_sel, float scale, float* kl, float* lse_idx, float* loss,
+                               void* ws, size_t ws_bytes, void* hip_stream) {
+  msa_status_t st = check_kl_shape(N, H_q, H_kv, d_h, d_idx, B_k, k_sel);
+  if (st != MSA_OK) return st;
+  if (!(scale > 0.f) || scale != scale) return fail(MSA_ERR_INVALID_ARG, "scale must be a positive number");
+  if (N == 0) return ok();
+  if (!q || !k || !q_idx || !k_idx || !block_idx || !lse || !kl || !lse_idx || !loss)
+    return fail(MSA_ERR_INVALID_ARG, "null pointer");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(q_idx, 16) || !aligned(k_idx, 16) || !aligned(block_idx, 4) ||
+      !aligned(lse, 4) || !aligned(kl, 4) || !aligned(lse_idx, 4) || !aligned(loss, 4))
+    return fail(MSA_ERR_INVALID_ARG, "misaligned pointer (q/k/q_idx/k_idx need 16 B)");
+  const size_t need = msa_sparse_kl_fwd_workspace_min(N, H_q, H_kv, d_h, d_idx, B_k, k_sel);
+  if (!ws || ws_bytes < need)
+    return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes is below the minimum %zu", ws ? ws_bytes : 0, need);
+  if (!aligned(ws, 256)) return fail(MSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const int64_t B = (N + B_k - 1) / B_k;
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  const int64_t W = window_for_bytes(N, B, H_q, H_kv, k_sel, ws_bytes - kKlLossBytes, true);
+  const msa::AttnWorkspace L = msa::attn_workspace_layout(W, H_q, H_kv, k_sel, B, true);
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  const int cus = num_cus();
+  for (int64_t w0 = 0; w0 < N; w0 += W) {
+    const int64_t Wn = (N - w0 < W) ? N - w0 : W;
+    hipError_t e = msa::launch_sparse_kl_window(
+        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(q_idx),
+        static_cast<const uint16_t*>(k_idx), lse, block_idx, N, B, H_q, H_kv, k_sel, scale, w0, Wn, cus, kl, lse_idx,
+        w + kKlLossBytes, L, stream);
+    if (e != hipSuccess) return hip_fail(e, "sparse_kl launch");
+  }
+  hipError_t e = msa::launch_kl_loss(kl, N * H_kv, reinterpret_cast<double*>(w), loss, stream);
+  if (e != hipSuccess) return hip_fail(e, "kl loss launch");
+  return ok();
 }
 
 msa_status_t msa_set_profile_events(void* const* events, int n) {

@@ -15,6 +15,9 @@ constexpr int kBlockKeys = 128;
 // Chunks (of 128 MFMA rows) per work item of the KV-outer kernel.
 constexpr int kItemChunks = 16;
 
+// Floats per (query, group, slot) partial of the KL pass.
+constexpr int kKlPart = 8;
+
 struct AttnWorkspace {
   size_t counts, tsum, cursor, n_items, items, pairs, opart, lpart, total;
   int64_t max_items;
@@ -54,12 +57,25 @@ hipError_t launch_seq_tables(const int64_t* cu, int batch, uint8_t* ws, const Se
 
 // B: the list stride in blocks (the block count, or for several sequences an upper
 // bound of the global block count).
-AttnWorkspace attn_workspace_layout(int64_t W, int H_q, int H_kv, int kk, int64_t B);
+// kl_parts: partials of the KL pass (kKlPart floats per pair) instead of the
+// attention's partial rows.
+AttnWorkspace attn_workspace_layout(int64_t W, int H_q, int H_kv, int kk, int64_t B, bool kl_parts = false);
 hipError_t launch_sparse_attn_window(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                      const int32_t* block_idx, int64_t N, int64_t B, const SeqInfo& si, int H_q,
                                      int H_kv, int kk, float scale, int64_t w0, int64_t W, int num_cus, float* o,
                                      float* lse, uint8_t* ws, const AttnWorkspace& L, hipStream_t stream,
                                      const hipEvent_t* events);  // 4 phase events or null
+
+// KL alignment pass over one query window (single sequence of N tokens): per
+// (query, group) kl and lse_idx.  launch_kl_loss then reduces kl [n] to its mean in
+// a fixed order (partial: kKlLossParts doubles of workspace).
+constexpr int kKlLossParts = 256;
+hipError_t launch_sparse_kl_window(const uint16_t* q, const uint16_t* k, const uint16_t* q_idx,
+                                   const uint16_t* k_idx, const float* lse, const int32_t* block_idx, int64_t N,
+                                   int64_t B, int H_q, int H_kv, int kk, float scale, int64_t w0, int64_t W,
+                                   int num_cus, float* kl, float* lse_idx, uint8_t* ws, const AttnWorkspace& L,
+                                   hipStream_t stream);
+hipError_t launch_kl_loss(const float* kl, int64_t n, double* partial, float* loss, hipStream_t stream);
 
 DecodeWorkspace decode_workspace_layout(int batch, int H_q, int H_kv, int kk, int64_t Bmax);
 hipError_t launch_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_t* k_cache,

@@ -690,6 +690,302 @@ __global__ __launch_bounds__(256) void seq_fill_kernel(const int64_t* __restrict
   for (int64_t gb = bstart[s] + threadIdx.x; gb < bstart[s + 1]; gb += 256) seq_blk[gb] = s;
 }
 
+// --------------------------------------------------------------------- KL alignment
+// Eq. 9-10 on the selected token set, KV-outer like phase 1 (same lists, items,
+// gather and K staging).  Per pair (query i, group r, slot s, block b), over the
+// block's tokens j <= i:
+//   Z = sum_j P_j,  A = sum_j P_j ln P_j,  C = sum_j P_j S_j,
+//   m = max_j S_j,  l = sum_j exp(S_j - m),
+// with S_j = <q_idx[i][r], k_idx[j]> / sqrt(d_idx) the index score and
+// P_j = (1/G) sum_h exp(s_hj - lse_h) the teacher: the mean of the group's head
+// softmaxes, each normalised by its head's final log partition lse_h from the main
+// pass.  Summed over the slots, KL(P || P_idx) = A - C + Z * LSE_idx with
+// LSE_idx = ln sum_s l_s e^{m_s}.  Z is 1 up to rounding; it is kept exact.
+
+// K_idx block -> LDS in the staged K tile's key order: row rho (128 B = 8 chunks of
+// 16 B) holds key swap23(rho), chunk c at position c ^ ((rho >> 1) & 7).
+__device__ __forceinline__ void stage_kidx(const uint16_t* __restrict__ kib, int nvalid, uint8_t* KIs, int tid) {
+  const int c = tid & 7;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int rho = (tid >> 3) + 32 * m;
+    const int key = swap23(rho);
+    const int kr = key < nvalid ? key : nvalid - 1;
+    u32x4_t val = *reinterpret_cast<const u32x4_t*>(kib + kr * kDidx + c * 8);
+    if (key >= nvalid) val = u32x4_t{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4_t*>(KIs + rho * 128 + ((c ^ ((rho >> 1) & 7)) << 4)) = val;
+  }
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over the G adjacent lanes holding one query's heads (G <= 32).
+template <int G>
+__device__ __forceinline__ float head_sum(float x) {
+  if constexpr (G >= 2) x = dpp_add<0xB1>(x);    // quad_perm [1,0,3,2]
+  if constexpr (G >= 4) x = dpp_add<0x4E>(x);    // quad_perm [2,3,0,1]
+  if constexpr (G >= 8) x = dpp_add<0x141>(x);   // row_half_mirror
+  if constexpr (G >= 16) x = dpp_add<0x140>(x);  // row_mirror
+  if constexpr (G >= 32) x += __shfl_xor(x, 16);
+  return x;
+}
+
+template <int G>
+__global__ __launch_bounds__(kAttnThreads, 2) void kl_pair_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp, const uint16_t* __restrict__ q_idx,
+    const uint16_t* __restrict__ k_idx, const float* __restrict__ lse, const int4* __restrict__ items,
+    const int32_t* __restrict__ n_items_ptr, const int32_t* __restrict__ pairs, int64_t N, int H_kv, int64_t B,
+    int nW, int kk, int64_t w0, float scale_log2, float* __restrict__ part) {
+  constexpr int kQC = 128 / G;
+  static_assert(G <= 32, "a query's heads must lie in one 32-lane half");
+  __shared__ __attribute__((aligned(16))) uint8_t Ks[kBk * 256];
+  __shared__ __attribute__((aligned(16))) uint8_t KIs[kBk * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t Qs[4][32 * 256];  // per wave: its 32 q rows
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int H_q = H_kv * G;
+  const int n_items = *n_items_ptr;
+  const int grid = gridDim.x;
+  const int per_xcd = grid >> 3;
+  const int xcd = blockIdx.x & 7, slot_in_xcd = blockIdx.x >> 3;
+  for (int64_t round = 0;; ++round) {
+    const int64_t item = round * grid + (int64_t)xcd * per_xcd + slot_in_xcd;
+    if (item >= n_items) break;
+    const int4 it = items[item];
+    const int64_t b = it.x % B, r = (it.x / B) / nW;
+    const int start = it.y, cnt = it.z;
+
+    constexpr int NR = kPairRegs<G>;
+    int ip[NR];
+#pragma unroll
+    for (int k = 0; k < NR; ++k) ip[k] = pairs[start + (64 * k + lane < cnt ? 64 * k + lane : cnt - 1)];
+    __syncthreads();  // previous item's LDS reads are done
+    {
+      int stid = tid;
+      asm volatile("" : "+v"(stid));
+      const int64_t tok0 = b * kBk;
+      const int nvalid = (N - tok0 < kBk) ? (int)(N - tok0) : kBk;
+      stage_k(kp + tok0 * H_kv * kDh + r * kDh, H_kv * kDh, nvalid, Ks, stid);
+      stage_kidx(k_idx + tok0 * kDidx, nvalid, KIs, stid);
+    }
+    __syncthreads();
+
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int qrow = wave * 32 + l32;
+    const int qs = qrow / G, g = qrow % G;
+    // The chunk's gathered q rows wait in the wave's LDS rows (row rho, 16-byte chunk
+    // c at position c ^ (rho & 15)) and are read as MFMA operands tile by tile,
+    // which keeps them out of registers.
+    uint8_t* qs_w = Qs[wave];
+    u32x4_t qraw[8];
+    auto to_lds = [&]() {
+      int ln = lane;  // addresses formed per call, not held across the loop
+      asm volatile("" : "+v"(ln));
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int rho = 4 * t + (ln >> 4);
+        *reinterpret_cast<u32x4_t*>(qs_w + rho * 256 + (((ln & 15) ^ (rho & 15)) << 4)) = qraw[t];
+      }
+    };
+    auto chunk_reg = [&](int cbase) { return pick_reg(ip, (cbase < cnt ? cbase : cnt - 1) >> 6); };
+    // The lane's own pair in chunk cbase (rows past the item's end take its last pair).
+    auto lane_pair = [&](int cbase, int curv) {
+      const int idx = cbase + qs < cnt ? cbase + qs : cnt - 1;
+      if constexpr (G >= 4)
+        return __shfl(curv, idx & 63);
+      else
+        return item_pair_v(ip, idx);
+    };
+    // Per-lane operands of a pair: its index query (dims 32h + 8t .. +7 for step t)
+    // and its head's main log partition in base 2.
+    auto lane_operands = [&](int prv, u32x4_t (&qi)[4], float& l2) {
+      const int64_t iq = w0 + (prv >> 5);
+      const uint16_t* src = q_idx + (iq * H_kv + r) * kDidx + 32 * h;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) qi[t] = *reinterpret_cast<const u32x4_t*>(src + 8 * t);
+      l2 = lse[iq * H_q + r * G + g] * kLog2e;
+    };
+
+    int cur = chunk_reg(0), cur_n = cur;
+    int prs[8];
+    gather_q<G>(qraw, prs, q, ip, cur, 0, cnt, wave_u, lane, w0, H_q, r);
+    int pr = lane_pair(0, cur);
+    u32x4_t qi_op[4];
+    float l2h;
+    lane_operands(pr, qi_op, l2h);
+    to_lds();
+    for (int cb = 0; cb < cnt; cb += kQC) {
+      asm volatile("" ::: "memory");
+      const int64_t i_local = pr >> 5;
+      const int s = pr & 31;
+      const int64_t i = w0 + i_local;
+
+      // Next chunk's q rows and per-lane operands, in flight during this chunk.
+      cur_n = chunk_reg(cb + kQC);
+      gather_q<G>(qraw, prs, q, ip, cur_n, cb + kQC, cnt, wave_u, lane, w0, H_q, r);
+      const int pr_n = lane_pair(cb + kQC, cur_n);
+      u32x4_t qi_n[4];
+      float l2_n;
+      lane_operands(pr_n, qi_n, l2_n);
+
+      // One 32-key tile at a time: main scores S^T[key][qrow] (as in phase 1) and
+      // index scores in the same layout (the index query repeated over the group's
+      // G columns), then the tile's terms.  Element v of tile kt is key kt*32 +
+      // 16*(v/8) + 4*((v/4)%2) + v%4 + 8h of the block; keys past the query are
+      // outside the token set.  The index partition is accumulated against a
+      // running maximum.
+      const int lim = (int)(i - b * kBk) - 8 * h;
+      const bool part_blk = __any(b * kBk + (kBk - 1) > i);
+      // Operand addresses are formed here from a laundered lane id: hoisted out of
+      // the loops they would hold ~60 registers for the whole kernel.  Row kt*32 +
+      // l32 differs from row l32 by a constant offset in both tiles.
+      int ln = l32;
+      asm volatile("" : "+v"(ln));
+      const uint8_t* ks_row = Ks + ln * 256;
+      const uint8_t* q_row = qs_w + ln * 256;
+      const uint8_t* ki_row = KIs + ln * 128;
+      const int ks_sw = ln & 15, ki_sw = (ln >> 1) & 7;
+      float A = 0.f, C = 0.f, Z = 0.f, l = 0.f, mx = -__builtin_inff();
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        f32x16_t sacc = f32x16_t{}, iacc = f32x16_t{};
+        const uint8_t* qr = q_row;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int c = 8 * h + t;
+          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(ks_row + kt * 32 * 256 + ((c ^ ks_sw) << 4));
+          const u32x4_t bq = *reinterpret_cast<const u32x4_t*>(qr + ((c ^ ks_sw) << 4));
+          sacc = mfma_32x32x16(as_bf16x8(a), as_bf16x8(bq), sacc);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int c = 4 * h + t;
+          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(ki_row + kt * 32 * 128 + ((c ^ ki_sw) << 4));
+          iacc = mfma_32x32x16(as_bf16x8(a), as_bf16x8(qi_op[t]), iacc);
+        }
+        float tm = -__builtin_inff();
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int off = kt * 32 + 16 * (v >> 3) + 4 * ((v >> 2) & 1) + (v & 3);
+          const bool in = !part_blk || off <= lim;
+          const float p = in ? __builtin_amdgcn_exp2f(fmaf(sacc[v], scale_log2, -l2h)) : 0.f;
+          const float P = head_sum<G>(p) * (1.f / G);
+          const float sv = in ? iacc[v] * 0.125f : -__builtin_inff();  // 1 / sqrt(d_idx)
+          iacc[v] = sv;
+          tm = fmaxf(tm, sv);
+          const bool pos = P > 0.f;
+          Z += P;
+          C += pos ? P * sv : 0.f;
+          A += pos ? P * (__log2f(P) * kLn2) : 0.f;
+        }
+        const float nm = fmaxf(mx, tm);
+        if (nm != -__builtin_inff()) {
+          float lt = 0.f;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) lt += __builtin_amdgcn_exp2f((iacc[v] - nm) * kLog2e);
+          l = (mx == -__builtin_inff() ? 0.f : l * __builtin_amdgcn_exp2f((mx - nm) * kLog2e)) + lt;
+          mx = nm;
+        }
+        // One tile's accumulators live at a time.
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // Merge the two lane halves (the other 64 keys of the block).
+      const float mo = __shfl_xor(mx, 32), lo = __shfl_xor(l, 32);
+      const float mi = fmaxf(mx, mo);
+      if (mi != -__builtin_inff())
+        l = (mx == -__builtin_inff() ? 0.f : l * __builtin_amdgcn_exp2f((mx - mi) * kLog2e)) +
+            (mo == -__builtin_inff() ? 0.f : lo * __builtin_amdgcn_exp2f((mo - mi) * kLog2e));
+      A += __shfl_xor(A, 32);
+      C += __shfl_xor(C, 32);
+      Z += __shfl_xor(Z, 32);
+      if (g == 0 && h == 0) {
+        float* dst = part + (((int64_t)i_local * H_kv + r) * kk + s) * kKlPart;
+        *reinterpret_cast<float4*>(dst) = make_float4(A, C, Z, mi);
+        dst[4] = l;
+      }
+
+      to_lds();
+      cur = cur_n;
+      pr = pr_n;
+      l2h = l2_n;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) qi_op[t] = qi_n[t];
+    }
+  }
+}
+
+// Per (query, group): sum of the valid slots' partials, then KL and LSE_idx.
+__global__ __launch_bounds__(256) void kl_combine_kernel(const float* __restrict__ part,
+                                                         const int32_t* __restrict__ block_idx, int64_t w0,
+                                                         int64_t W, int H_kv, int kk, float* __restrict__ kl,
+                                                         float* __restrict__ lse_idx) {
+  const int64_t ir = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (ir >= W * H_kv) return;
+  const int64_t i = w0 + ir / H_kv;
+  const int32_t* sel = block_idx + (w0 * H_kv + ir) * kk;
+  float A = 0.f, C = 0.f, Z = 0.f, M = -__builtin_inff(), L = 0.f;
+  for (int s = 0; s < kk; ++s) {
+    if (!pair_valid(sel[s], i)) continue;
+    const float* src = part + (ir * kk + s) * kKlPart;
+    const float4 a = *reinterpret_cast<const float4*>(src);
+    const float l = src[4];
+    A += a.x;
+    C += a.y;
+    Z += a.z;
+    if (a.w == -__builtin_inff()) continue;
+    if (a.w > M) {
+      L = L * __expf(M - a.w) + l;
+      M = a.w;
+    } else {
+      L += l * __expf(a.w - M);
+    }
+  }
+  const int64_t o = w0 * H_kv + ir;
+  if (M == -__builtin_inff()) {
+    kl[o] = 0.f;
+    lse_idx[o] = -__builtin_inff();
+  } else {
+    const float lse_i = M + __logf(L);
+    kl[o] = A - C + lse_i * Z;
+    lse_idx[o] = lse_i;
+  }
+}
+
+// Fixed-order reduction of kl[0..n): workgroup w sums its contiguous share in fp64.
+__global__ __launch_bounds__(256) void kl_sum_kernel(const float* __restrict__ kl, int64_t n,
+                                                     double* __restrict__ partial) {
+  __shared__ double red[256];
+  const int64_t share = (n + gridDim.x - 1) / gridDim.x;
+  const int64_t e0 = (int64_t)blockIdx.x * share;
+  const int64_t e1 = e0 + share < n ? e0 + share : n;
+  double acc = 0.0;
+  for (int64_t e = e0 + threadIdx.x; e < e1; e += 256) acc += (double)kl[e];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) partial[blockIdx.x] = red[0];
+}
+
+__global__ __launch_bounds__(256) void kl_mean_kernel(const double* __restrict__ partial, int np, int64_t n,
+                                                      float* __restrict__ loss) {
+  __shared__ double red[256];
+  red[threadIdx.x] = (int)threadIdx.x < np ? partial[threadIdx.x] : 0.0;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) loss[0] = (float)(red[0] / (double)n);
+}
+
 __global__ void fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t val) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += stride) p[e] = val;
@@ -730,7 +1026,7 @@ hipError_t launch_seq_tables(const int64_t* cu, int batch, uint8_t* ws, const Se
   return hipGetLastError();
 }
 
-AttnWorkspace attn_workspace_layout(int64_t W, int H_q, int H_kv, int kk, int64_t B) {
+AttnWorkspace attn_workspace_layout(int64_t W, int H_q, int H_kv, int kk, int64_t B, bool kl_parts) {
   AttnWorkspace L{};
   // q-locality window of 64*B queries (a multiple of 4096, so every inverse-index
   // tile lies in one window): each K/V block is staged once per (group, window)
@@ -760,31 +1056,31 @@ AttnWorkspace attn_workspace_layout(int64_t W, int H_q, int H_kv, int kk, int64_
   L.n_items = take(sizeof(int32_t) * 4);
   L.items = take(sizeof(int4) * max_items);
   L.pairs = take(sizeof(int32_t) * max_pairs);
-  L.opart = take(sizeof(uint16_t) * max_pairs * G * kDh);
-  L.lpart = take(sizeof(float2) * max_pairs * G);
+  if (kl_parts) {
+    L.opart = take(sizeof(float) * kKlPart * max_pairs);
+    L.lpart = take(0);
+  } else {
+    L.opart = take(sizeof(uint16_t) * max_pairs * G * kDh);
+    L.lpart = take(sizeof(float2) * max_pairs * G);
+  }
   L.total = off;
   L.max_items = max_items;
   L.item_q = item_q;
   return L;
 }
 
-hipError_t launch_sparse_attn_window(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                     const int32_t* block_idx, int64_t N, int64_t B, const SeqInfo& si, int H_q,
-                                     int H_kv, int kk, float scale, int64_t w0, int64_t W, int num_cus, float* o,
-                                     float* lse, uint8_t* ws, const AttnWorkspace& L, hipStream_t stream,
-                                     const hipEvent_t* events) {
+// Inverse index of one query window: per-list pair counts, their scan into list
+// offsets and the item table, then the scatter of the (query, slot) pairs.
+static hipError_t launch_inverse_index(const int32_t* block_idx, int64_t B, const SeqInfo& si, int H_kv, int kk,
+                                       int64_t w0, int64_t W, uint8_t* ws, const AttnWorkspace& L,
+                                       hipStream_t stream) {
   const int64_t lists = (int64_t)H_kv * L.nW * B;
-  const int G = H_q / H_kv;
   int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
   int32_t* cursor = reinterpret_cast<int32_t*>(ws + L.cursor);
   int32_t* n_items = reinterpret_cast<int32_t*>(ws + L.n_items);
   int4* items = reinterpret_cast<int4*>(ws + L.items);
   int32_t* pairs = reinterpret_cast<int32_t*>(ws + L.pairs);
-  uint16_t* opart = reinterpret_cast<uint16_t*>(ws + L.opart);
-  float2* lpart = reinterpret_cast<float2*>(ws + L.lpart);
-
   hipError_t e;
-  if (events && (e = hipEventRecord(events[0], stream)) != hipSuccess) return e;
   fill_i32_kernel<<<dim3(256), dim3(256), 0, stream>>>(counts, lists, 0);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -805,7 +1101,24 @@ hipError_t launch_sparse_attn_window(const uint16_t* q, const uint16_t* k, const
   if ((e = hipGetLastError()) != hipSuccess) return e;
   inv_scatter_kernel<16><<<igrid, dim3(256), 2 * lds_count, stream>>>(block_idx, si, w0, W, H_kv, kk, B, TQ,
                                                                       L.WQ, L.nW, cursor, pairs);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_attn_window(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                     const int32_t* block_idx, int64_t N, int64_t B, const SeqInfo& si, int H_q,
+                                     int H_kv, int kk, float scale, int64_t w0, int64_t W, int num_cus, float* o,
+                                     float* lse, uint8_t* ws, const AttnWorkspace& L, hipStream_t stream,
+                                     const hipEvent_t* events) {
+  const int G = H_q / H_kv;
+  const int32_t* n_items = reinterpret_cast<const int32_t*>(ws + L.n_items);
+  const int4* items = reinterpret_cast<const int4*>(ws + L.items);
+  const int32_t* pairs = reinterpret_cast<const int32_t*>(ws + L.pairs);
+  uint16_t* opart = reinterpret_cast<uint16_t*>(ws + L.opart);
+  float2* lpart = reinterpret_cast<float2*>(ws + L.lpart);
+
+  hipError_t e;
+  if (events && (e = hipEventRecord(events[0], stream)) != hipSuccess) return e;
+  if ((e = launch_inverse_index(block_idx, B, si, H_kv, kk, w0, W, ws, L, stream)) != hipSuccess) return e;
 
   int64_t grid = (int64_t)num_cus * 2;
   if (grid > L.max_items) grid = L.max_items;
@@ -866,6 +1179,53 @@ hipError_t launch_sparse_attn_window(const uint16_t* q, const uint16_t* k, const
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (events && (e = hipEventRecord(events[3], stream)) != hipSuccess) return e;
   return hipSuccess;
+}
+
+hipError_t launch_sparse_kl_window(const uint16_t* q, const uint16_t* k, const uint16_t* q_idx,
+                                   const uint16_t* k_idx, const float* lse, const int32_t* block_idx, int64_t N,
+                                   int64_t B, int H_q, int H_kv, int kk, float scale, int64_t w0, int64_t W,
+                                   int num_cus, float* kl, float* lse_idx, uint8_t* ws, const AttnWorkspace& L,
+                                   hipStream_t stream) {
+  const int G = H_q / H_kv;
+  hipError_t e = launch_inverse_index(block_idx, B, SeqInfo{}, H_kv, kk, w0, W, ws, L, stream);
+  if (e != hipSuccess) return e;
+  const int32_t* n_items = reinterpret_cast<const int32_t*>(ws + L.n_items);
+  const int4* items = reinterpret_cast<const int4*>(ws + L.items);
+  const int32_t* pairs = reinterpret_cast<const int32_t*>(ws + L.pairs);
+  float* part = reinterpret_cast<float*>(ws + L.opart);
+  int64_t grid = (int64_t)num_cus * 2;
+  if (grid > L.max_items) grid = L.max_items;
+  grid = ((grid + 7) / 8) * 8;
+  const float scale_log2 = scale * kLog2e;
+  switch (G) {
+#define MSA_KL_CASE(GG)                                                                                    \
+  case GG:                                                                                                 \
+    kl_pair_kernel<GG><<<dim3((unsigned)grid), dim3(kAttnThreads), 0, stream>>>(                           \
+        q, k, q_idx, k_idx, lse, items, n_items, pairs, N, H_kv, B, L.nW, kk, w0, scale_log2, part);       \
+    break;
+    MSA_KL_CASE(1)
+    MSA_KL_CASE(2)
+    MSA_KL_CASE(4)
+    MSA_KL_CASE(8)
+    MSA_KL_CASE(16)
+    MSA_KL_CASE(32)
+#undef MSA_KL_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t rows = W * H_kv;
+  kl_combine_kernel<<<dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream>>>(part, block_idx, w0, W, H_kv,
+                                                                                     kk, kl, lse_idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_kl_loss(const float* kl, int64_t n, double* partial, float* loss, hipStream_t stream) {
+  kl_sum_kernel<<<dim3(kKlLossParts), dim3(256), 0, stream>>>(kl, n, partial);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  kl_mean_kernel<<<dim3(1), dim3(256), 0, stream>>>(partial, kKlLossParts, n, loss);
+  return hipGetLastError();
 }
 
 }  // namespace msa

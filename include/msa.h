@@ -94,6 +94,37 @@ msa_status_t msa_sparse_attn_fwd(const void* q, const void* k, const void* v,
                                  int B_k, int k_sel, float scale, float* o, float* lse, void* ws,
                                  size_t ws_bytes, void* hip_stream);
 
+/* ------------------------------------------------------------------ KL alignment
+ * msa_sparse_kl_fwd — Eq. 9-10 (the Index Branch's alignment loss, Algorithm 1
+ * step 7) on the selected token set T of each (query, group): the tokens j <= i
+ * of the blocks in block_idx (same rules as msa_sparse_attn_fwd).
+ *   P_idx(j) = softmax over T of the index scores <q_idx[i][r], k_idx[j]> / sqrt(d_idx)
+ *   P(j)     = mean over the group's G heads of each head's Main Branch softmax
+ *              over T, the teacher (scores scale * <q[i][h], k[j][r]>)
+ *   kl[i][r] = KL(P || P_idx);  loss = mean of kl over all (i, r)  (Eq. 10)
+ * Inputs as for msa_index_topk / msa_sparse_attn_fwd, plus
+ *   lse       fp32 [N, H_q]  the log partitions that msa_sparse_attn_fwd emitted
+ *             for the same q, k, block_idx and scale (the pages' kernel emits
+ *             these scalars in the main pass; the teacher is normalised by them).
+ * Outputs (device):
+ *   kl        fp32 [N, H_kv]
+ *   lse_idx   fp32 [N, H_kv]  log sum over T of exp(index score): the scalar a
+ *             backward pass would load; an empty T gives kl = 0, lse_idx = -inf.
+ *   loss      fp32 [1]        mean of kl (fixed-order fp64 sum; deterministic).
+ * Limits: G = H_q / H_kv <= 32, d_idx = 64, and the other limits of
+ * msa_sparse_attn_fwd.  Workspace sizes as for msa_sparse_attn_fwd (its own
+ * queries; smaller workspaces run in query windows).
+ */
+size_t msa_sparse_kl_fwd_workspace(int64_t N, int H_q, int H_kv, int d_h, int d_idx, int B_k,
+                                   int k);
+size_t msa_sparse_kl_fwd_workspace_min(int64_t N, int H_q, int H_kv, int d_h, int d_idx, int B_k,
+                                       int k);
+msa_status_t msa_sparse_kl_fwd(const void* q, const void* k, const void* q_idx, const void* k_idx,
+                               const int32_t* block_idx, const float* lse, int64_t N, int H_q,
+                               int H_kv, int d_h, int d_idx, int B_k, int k_sel, float scale,
+                               float* kl, float* lse_idx, float* loss, void* ws, size_t ws_bytes,
+                               void* hip_stream);
+
 /* ------------------------------------------------------------------ Packed sequences
  * Variable-length prefill: `batch` independent sequences packed along the token
  * axis, each with its own causal mask, block grid and local block (every position

@@ -173,3 +173,26 @@ def test_varlen_rejects_bad_arguments(lib):
     assert attn(ws_bytes=need - 1) == lib.MSA_ERR_WORKSPACE
     assert attn(batch=0) == lib.MSA_OK
     assert raw.msa_sparse_attn_fwd_varlen_workspace(4096, 0, 8, 2, 128, 128, 8) == 0
+
+
+def test_sparse_kl_rejects_bad_arguments(lib):
+    raw = lib.raw()
+    f = 0x10000
+
+    def call(N=4096, H_q=8, H_kv=2, d_h=128, d_idx=64, k=8, scale=0.088, ws=f, ws_bytes=1 << 40, lse=f, loss=f):
+        return raw.msa_sparse_kl_fwd(f, f, f, f, f, lse, N, H_q, H_kv, d_h, d_idx, 128, k, scale, f, f, loss, ws,
+                                     ws_bytes, None)
+
+    assert call(d_idx=32) == lib.MSA_ERR_UNSUPPORTED
+    assert call(H_q=128, H_kv=2) == lib.MSA_ERR_UNSUPPORTED  # G = 64 > 32
+    assert call(lse=None) == lib.MSA_ERR_INVALID_ARG
+    assert call(loss=None) == lib.MSA_ERR_INVALID_ARG
+    assert call(scale=0.0) == lib.MSA_ERR_INVALID_ARG
+    assert call(ws=None) == lib.MSA_ERR_WORKSPACE
+    need = raw.msa_sparse_kl_fwd_workspace_min(4096, 8, 2, 128, 64, 128, 8)
+    assert 0 < need < raw.msa_sparse_kl_fwd_workspace(4096, 8, 2, 128, 64, 128, 8)
+    assert call(ws_bytes=need - 1) == lib.MSA_ERR_WORKSPACE
+    assert call(N=0) == lib.MSA_OK
+    # partials are 32 bytes per (query, group, slot): far below the attention's rows
+    full_kl = raw.msa_sparse_kl_fwd_workspace(131072, 64, 8, 128, 64, 128, 16)
+    assert 0 < full_kl < raw.msa_sparse_attn_fwd_workspace(131072, 64, 8, 128, 128, 16) // 8

@@ -1,0 +1,128 @@
+"""GPU parity of the KL alignment pass (Eq. 9-10) against the oracle.
+
+The GPU pass takes the main branch's emitted lse (from msa_sparse_attn_fwd on the
+GPU); the oracle computes everything itself in fp64 from the same bf16 inputs.
+Tolerances (derived in the design notes): kl within 5e-4 + 2e-3 |kl|, lse_idx
+within 1e-3, loss within 5e-4 + 1e-3 |loss|.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def msa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_sparse_gqa_index_amd as m
+    return m
+
+
+def _check_kl(kl, lse_idx, loss, kl_ref, li_ref, what):
+    kl, lse_idx = kl.cpu().double().numpy(), lse_idx.cpu().double().numpy()
+    fin = np.isfinite(li_ref)
+    assert np.array_equal(np.isfinite(lse_idx), fin), what
+    assert np.all(lse_idx[~fin] == -np.inf) and np.all(kl[~fin] == 0), what
+    err = np.abs(kl - kl_ref)
+    assert np.all(err <= 5e-4 + 2e-3 * np.abs(kl_ref)), (what, err.max())
+    assert np.abs(lse_idx[fin] - li_ref[fin]).max(initial=0) <= 1e-3, what
+    ref_loss = kl_ref.mean()
+    assert abs(float(loss.item()) - ref_loss) <= 5e-4 + 1e-3 * abs(ref_loss), (what, float(loss.item()), ref_loss)
+    # the loss is the mean of the kl the pass returned (fixed-order fp64 sum)
+    assert abs(float(loss.item()) - kl.mean()) <= 1e-6 * max(1.0, abs(kl.mean())), what
+
+
+KL_SHAPES = [  # N, H_q, H_kv, k
+    (4096, 4, 1, 8),
+    (1000, 16, 2, 4),
+    (700, 8, 8, 3),
+    (300, 4, 2, 16),
+    (1, 8, 1, 4),
+    (129, 32, 1, 2),
+    (2600, 16, 1, 5),
+    (3000, 8, 1, 16),
+    (900, 2, 2, 6),
+    (1500, 4, 2, 7),
+    (512, 64, 2, 4),
+]
+
+
+@pytest.mark.parametrize("N,H_q,H_kv,k", KL_SHAPES)
+def test_sparse_kl_on_oracle_selection(msa, N, H_q, H_kv, k):
+    inp = synth.small_prefill(N=N, H_q=H_q, H_kv=H_kv, k=k, seed=1100 + N, needles=1 if N >= 2000 else 0,
+                              device=DEV)
+    bi = oracle.topk(oracle.block_scores(inp.q_idx, inp.k_idx, 128), k, 128)
+    bi_d = torch.from_numpy(bi).to(DEV)
+    _, lse = msa.msa_sparse_attn_fwd(inp.q, inp.k, inp.v, bi_d)
+    kl, lse_idx, loss = msa.msa_sparse_kl_fwd(inp.q, inp.k, inp.q_idx, inp.k_idx, bi_d, lse)
+    torch.cuda.synchronize()
+    kl_ref, li_ref = oracle.sparse_kl(inp.q, inp.k, inp.q_idx, inp.k_idx, bi, 128)
+    _check_kl(kl, lse_idx, loss, kl_ref, li_ref, f"N={N} H_q={H_q} H_kv={H_kv} k={k}")
+
+
+@pytest.mark.parametrize("mode", ["literal", "structured"])
+def test_sparse_kl_end_to_end(msa, mode):
+    """Selection, attention and KL all on the GPU (the oracle on the GPU's selection)."""
+    N, H_q, H_kv, k = 3000, 16, 2, 8
+    inp = synth.small_prefill(N=N, H_q=H_q, H_kv=H_kv, k=k, seed=1201, mode=mode, needles=2, device=DEV)
+    bi = msa.msa_index_topk(inp.q_idx, inp.k_idx, k)
+    _, lse = msa.msa_sparse_attn_fwd(inp.q, inp.k, inp.v, bi)
+    kl, lse_idx, loss = msa.msa_sparse_kl_fwd(inp.q, inp.k, inp.q_idx, inp.k_idx, bi, lse)
+    torch.cuda.synchronize()
+    kl_ref, li_ref = oracle.sparse_kl(inp.q, inp.k, inp.q_idx, inp.k_idx, bi.cpu().numpy(), 128)
+    _check_kl(kl, lse_idx, loss, kl_ref, li_ref, f"e2e {mode}")
+
+
+def test_sparse_kl_arbitrary_block_sets(msa):
+    """-1 entries, future blocks and empty rows (kl 0, lse_idx -inf)."""
+    N, H_q, H_kv, k = 1500, 8, 2, 5
+    inp = synth.small_prefill(N=N, H_q=H_q, H_kv=H_kv, k=k, seed=1202, device=DEV)
+    g = np.random.default_rng(5)
+    B = (N + 127) // 128
+    bi = np.full((N, H_kv, k), -1, dtype=np.int32)
+    for i in range(N):
+        for r in range(H_kv):
+            c = g.choice(B, size=g.integers(0, k + 1), replace=False)
+            bi[i, r, :len(c)] = c
+    bi[7] = -1
+    bi_d = torch.from_numpy(bi).to(DEV)
+    _, lse = msa.msa_sparse_attn_fwd(inp.q, inp.k, inp.v, bi_d)
+    kl, lse_idx, loss = msa.msa_sparse_kl_fwd(inp.q, inp.k, inp.q_idx, inp.k_idx, bi_d, lse)
+    torch.cuda.synchronize()
+    kl_ref, li_ref = oracle.sparse_kl(inp.q, inp.k, inp.q_idx, inp.k_idx, bi, 128)
+    assert np.all(np.isinf(li_ref[7]))
+    _check_kl(kl, lse_idx, loss, kl_ref, li_ref, "arbitrary sets")
+
+
+def test_sparse_kl_windows_and_reruns_are_bitwise_identical(msa):
+    N, H_q, H_kv, k = 2500, 8, 2, 6
+    inp = synth.small_prefill(N=N, H_q=H_q, H_kv=H_kv, k=k, seed=1203, needles=2, device=DEV)
+    bi = msa.msa_index_topk(inp.q_idx, inp.k_idx, k)
+    _, lse = msa.msa_sparse_attn_fwd(inp.q, inp.k, inp.v, bi)
+    r1 = msa.msa_sparse_kl_fwd(inp.q, inp.k, inp.q_idx, inp.k_idx, bi, lse)
+    wmin = msa.msa_sparse_kl_fwd_workspace(N, H_q, H_kv, k, minimum=True)
+    ws = torch.empty(wmin, dtype=torch.uint8, device=DEV)
+    r2 = msa.msa_sparse_kl_fwd(inp.q, inp.k, inp.q_idx, inp.k_idx, bi, lse, workspace=ws)
+    r3 = msa.msa_sparse_kl_fwd(inp.q, inp.k, inp.q_idx, inp.k_idx, bi, lse)
+    torch.cuda.synchronize()
+    for a, b in ((r1, r2), (r1, r3)):
+        for x, y in zip(a, b):
+            assert torch.equal(x, y)
+
+
+def test_sparse_kl_empty(msa):
+    q = torch.empty((0, 8, 128), dtype=torch.bfloat16, device=DEV)
+    kv = torch.empty((0, 2, 128), dtype=torch.bfloat16, device=DEV)
+    qi = torch.empty((0, 2, 64), dtype=torch.bfloat16, device=DEV)
+    ki = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    bi = torch.empty((0, 2, 4), dtype=torch.int32, device=DEV)
+    lse = torch.empty((0, 8), dtype=torch.float32, device=DEV)
+    kl, li, loss = msa.msa_sparse_kl_fwd(q, kv, qi, ki, bi, lse)
+    assert kl.shape == (0, 2) and li.shape == (0, 2)
