@@ -206,7 +206,7 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def run_prefill(msa, synth, cfg, mode, steps, warmup):
+def run_prefill(msa, synth, cfg, mode, steps, warmup, with_kl=False):
     import torch
     dev = "cuda"
     N, H_q, H_kv, k, B_k = cfg.N, cfg.H_q, cfg.H_kv, cfg.k, cfg.B_k
@@ -285,8 +285,48 @@ def run_prefill(msa, synth, cfg, mode, steps, warmup):
         "block0_fanin_per_group": int(fan[:, 0].float().mean().item()), "max_fanin": int(fan.max().item()),
         "median_fanin": float(fan.float().median().item()),
     }
-    del o, lse, ws, block_idx
+    del o, ws
+    if with_kl:
+        res["kl"] = run_kl(msa, inp, cfg, block_idx, lse, slot_pairs, lists, pairs, steps)
+    del lse, block_idx
     return res, inp
+
+
+def run_kl(msa, inp, cfg, block_idx, lse, slot_pairs, lists, pairs, steps):
+    """The KL alignment pass (Eq. 9-10) on the step's selection and lse, timed on its
+    own: it follows the forward in training and is not part of the timed step."""
+    import torch
+    N, H_q, H_kv, k, B_k = cfg.N, cfg.H_q, cfg.H_kv, cfg.k, cfg.B_k
+    G = H_q // H_kv
+    dev = "cuda"
+    kws = torch.empty(msa.msa_sparse_kl_fwd_workspace(N, H_q, H_kv, k), dtype=torch.uint8, device=dev)
+    kl = torch.empty((N, H_kv), dtype=torch.float32, device=dev)
+    lse_idx = torch.empty((N, H_kv), dtype=torch.float32, device=dev)
+    loss = torch.empty((1,), dtype=torch.float32, device=dev)
+
+    def kl_step():
+        msa.msa_sparse_kl_fwd(inp.q, inp.k, inp.q_idx, inp.k_idx, block_idx, lse, kl=kl, lse_idx=lse_idx, loss=loss,
+                              workspace=kws)
+
+    kl_step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        kl_step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    # Per (query, group, slot) pair: G q rows, the index query row, G lse values and
+    # the 32-byte partial; per (group, block) list: its K block and index-key block.
+    nbytes = slot_pairs * (G * cfg.d_h * 2 + cfg.d_idx * 2 + G * 4 + 32) + lists * B_k * (cfg.d_h + cfg.d_idx) * 2
+    # QK for every attended (query, head, key) and one index dot product per (query, group, key).
+    flops = 2 * cfg.d_h * pairs + 2 * cfg.d_idx * (pairs // G)
+    out = {"ms": round(ms, 4), "algorithmic_bytes": nbytes, "GB_s": round(nbytes / (ms / 1e3) / 1e9, 1),
+           "tflops": round(flops / (ms / 1e3) / 1e12, 2), "loss": round(float(loss.item()), 6), "steps": steps}
+    del kws, kl, lse_idx, loss
+    return out
 
 
 def run_decode(msa, synth, dcfg, mode, steps, warmup):
@@ -363,6 +403,7 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-rows", type=int, default=4096, help="query rows in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-kl", action="store_true", help="skip the separately timed KL alignment pass")
     ap.add_argument("--single-mode", action="store_true", help="skip the second input mode")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="start with plain copies of known size (for counter runs)")
@@ -396,7 +437,7 @@ def main(argv=None) -> int:
     N, H_q, H_kv, k, B_k = cfg.N, cfg.H_q, cfg.H_kv, cfg.k, cfg.B_k
     other = "structured" if args.mode == "literal" else "literal"
 
-    pre, inp = run_prefill(msa, synth, cfg, args.mode, args.steps, args.warmup)
+    pre, inp = run_prefill(msa, synth, cfg, args.mode, args.steps, args.warmup, with_kl=not args.no_kl)
     result = {
         "metric": "MSA prefill tokens/s + TFLOP/s at 128K; decode tokens/s at 128K KV (1 GPU)",
         "value": pre["tokens_per_s"],

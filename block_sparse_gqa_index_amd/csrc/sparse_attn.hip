@@ -718,20 +718,38 @@ __device__ __forceinline__ void stage_kidx(const uint16_t* __restrict__ kib, int
 }
 
 template <int CTRL>
-__device__ __forceinline__ float dpp_add(float x) {
-  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
 }
 
-// Sum over the G adjacent lanes holding one query's heads (G <= 32).
-template <int G>
-__device__ __forceinline__ float head_sum(float x) {
-  if constexpr (G >= 2) x = dpp_add<0xB1>(x);    // quad_perm [1,0,3,2]
-  if constexpr (G >= 4) x = dpp_add<0x4E>(x);    // quad_perm [2,3,0,1]
-  if constexpr (G >= 8) x = dpp_add<0x141>(x);   // row_half_mirror
-  if constexpr (G >= 16) x = dpp_add<0x140>(x);  // row_mirror
-  if constexpr (G >= 32) x += __shfl_xor(x, 16);
-  return x;
+// Sum / max over the 32 lanes of a wave half (every lane gets the result).
+__device__ __forceinline__ float half_sum(float x) {
+  x += dpp_f<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_f<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_f<0x141>(x);  // row_half_mirror
+  x += dpp_f<0x140>(x);  // row_mirror
+  return x + __shfl_xor(x, 16);
 }
+__device__ __forceinline__ float half_max(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));
+  x = fmaxf(x, dpp_f<0x4E>(x));
+  x = fmaxf(x, dpp_f<0x141>(x));
+  x = fmaxf(x, dpp_f<0x140>(x));
+  return fmaxf(x, __shfl_xor(x, 16));
+}
+
+// Score tiles here are Q K^T (q rows as MFMA rows): element v of lane (l32, h) is q
+// row 8*(v/4) + 4h + v%4 of the wave's 32 (query slot x head) and column l32, key
+// kt*32 + swap23(l32) of the block.  A query's heads then sit in GL consecutive
+// elements of one lane (and, for G >= 8, in both lane halves), so the teacher's
+// head mean is a few in-lane adds, and the per-query terms are computed NQ times
+// per lane instead of once per head.
+template <int G>
+struct KlRows {
+  static constexpr int GL = G <= 4 ? G : G / 2;  // heads of one query per lane
+  static constexpr int NQ = 16 / GL;             // queries per lane and tile
+  static constexpr bool kCross = G >= 8;         // the other heads are in lane ^ 32
+};
 
 template <int G>
 __global__ __launch_bounds__(kAttnThreads, 2) void kl_pair_kernel(
@@ -740,7 +758,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void kl_pair_kernel(
     const int32_t* __restrict__ n_items_ptr, const int32_t* __restrict__ pairs, int64_t N, int H_kv, int64_t B,
     int nW, int kk, int64_t w0, float scale_log2, float* __restrict__ part) {
   constexpr int kQC = 128 / G;
-  static_assert(G <= 32, "a query's heads must lie in one 32-lane half");
+  constexpr int GL = KlRows<G>::GL, NQ = KlRows<G>::NQ;
+  static_assert(G <= 32, "a query's heads must lie in one wave");
   __shared__ __attribute__((aligned(16))) uint8_t Ks[kBk * 256];
   __shared__ __attribute__((aligned(16))) uint8_t KIs[kBk * 128];
   __shared__ __attribute__((aligned(16))) uint8_t Qs[4][32 * 256];  // per wave: its 32 q rows
@@ -776,13 +795,14 @@ __global__ __launch_bounds__(kAttnThreads, 2) void kl_pair_kernel(
     __syncthreads();
 
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    const int qrow = wave * 32 + l32;
+    const int qrow = wave * 32 + l32;  // the lane's own row (operand side)
     const int qs = qrow / G, g = qrow % G;
-    // The chunk's gathered q rows wait in the wave's LDS rows (row rho, 16-byte chunk
-    // c at position c ^ (rho & 15)) and are read as MFMA operands tile by tile,
-    // which keeps them out of registers.
     uint8_t* qs_w = Qs[wave];
     u32x4_t qraw[8];
+    // The chunk's gathered q rows wait in the wave's LDS rows (row rho, 16-byte
+    // chunk c at position c ^ (rho & 15)) and are read as MFMA operands tile by
+    // tile (the block's K, K_idx and these rows fill the 80 KB that two
+    // workgroups per CU allow).
     auto to_lds = [&]() {
       int ln = lane;  // addresses formed per call, not held across the loop
       asm volatile("" : "+v"(ln));
@@ -793,7 +813,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void kl_pair_kernel(
       }
     };
     auto chunk_reg = [&](int cbase) { return pick_reg(ip, (cbase < cnt ? cbase : cnt - 1) >> 6); };
-    // The lane's own pair in chunk cbase (rows past the item's end take its last pair).
+    // The pair of the lane's own row in chunk cbase (rows past the item's end take
+    // its last pair).
     auto lane_pair = [&](int cbase, int curv) {
       const int idx = cbase + qs < cnt ? cbase + qs : cnt - 1;
       if constexpr (G >= 4)
@@ -801,8 +822,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void kl_pair_kernel(
       else
         return item_pair_v(ip, idx);
     };
-    // Per-lane operands of a pair: its index query (dims 32h + 8t .. +7 for step t)
-    // and its head's main log partition in base 2.
+    // Index query of the lane's own row (dims 32h + 8t .. +7 for step t) and its
+    // head's main log partition in base 2.
     auto lane_operands = [&](int prv, u32x4_t (&qi)[4], float& l2) {
       const int64_t iq = w0 + (prv >> 5);
       const uint16_t* src = q_idx + (iq * H_kv + r) * kDidx + 32 * h;
@@ -816,14 +837,22 @@ __global__ __launch_bounds__(kAttnThreads, 2) void kl_pair_kernel(
     gather_q<G>(qraw, prs, q, ip, cur, 0, cnt, wave_u, lane, w0, H_q, r);
     int pr = lane_pair(0, cur);
     u32x4_t qi_op[4];
-    float l2h;
-    lane_operands(pr, qi_op, l2h);
+    float l2own;
+    lane_operands(pr, qi_op, l2own);
     to_lds();
     for (int cb = 0; cb < cnt; cb += kQC) {
       asm volatile("" ::: "memory");
-      const int64_t i_local = pr >> 5;
-      const int s = pr & 31;
-      const int64_t i = w0 + i_local;
+      // Output rows of this lane (row 8*(v/4) + 4h + v%4 is the own row of lane
+      // with that l32): lse of all 16, pair of each query.
+      float l2v[16];
+      int prq[NQ];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) l2v[v] = __shfl(l2own, 8 * (v >> 2) + 4 * h + (v & 3));
+#pragma unroll
+      for (int qq = 0; qq < NQ; ++qq) {
+        const int v0 = qq * GL;
+        prq[qq] = __shfl(pr, 8 * (v0 >> 2) + 4 * h + (v0 & 3));
+      }
 
       // Next chunk's q rows and per-lane operands, in flight during this chunk.
       cur_n = chunk_reg(cb + kQC);
@@ -833,86 +862,89 @@ __global__ __launch_bounds__(kAttnThreads, 2) void kl_pair_kernel(
       float l2_n;
       lane_operands(pr_n, qi_n, l2_n);
 
-      // One 32-key tile at a time: main scores S^T[key][qrow] (as in phase 1) and
-      // index scores in the same layout (the index query repeated over the group's
-      // G columns), then the tile's terms.  Element v of tile kt is key kt*32 +
-      // 16*(v/8) + 4*((v/4)%2) + v%4 + 8h of the block; keys past the query are
-      // outside the token set.  The index partition is accumulated against a
-      // running maximum.
-      const int lim = (int)(i - b * kBk) - 8 * h;
-      const bool part_blk = __any(b * kBk + (kBk - 1) > i);
-      // Operand addresses are formed here from a laundered lane id: hoisted out of
-      // the loops they would hold ~60 registers for the whole kernel.  Row kt*32 +
-      // l32 differs from row l32 by a constant offset in both tiles.
       int ln = l32;
       asm volatile("" : "+v"(ln));
       const uint8_t* ks_row = Ks + ln * 256;
-      const uint8_t* q_row = qs_w + ln * 256;
       const uint8_t* ki_row = KIs + ln * 128;
+      const uint8_t* q_row = qs_w + ln * 256;
       const int ks_sw = ln & 15, ki_sw = (ln >> 1) & 7;
-      float A = 0.f, C = 0.f, Z = 0.f, l = 0.f, mx = -__builtin_inff();
+      const int koff0 = swap23(ln);  // key of column l32 in tile 0
+      int lim[NQ];
+      bool part_blk = false;
+#pragma unroll
+      for (int qq = 0; qq < NQ; ++qq) {
+        lim[qq] = (int)(w0 + (prq[qq] >> 5) - b * kBk);
+        part_blk |= lim[qq] < kBk - 1;
+      }
+      part_blk = __any(part_blk);
+      float A[NQ], C[NQ], Z[NQ], mx[NQ], l[NQ];
+#pragma unroll
+      for (int qq = 0; qq < NQ; ++qq) {
+        A[qq] = C[qq] = Z[qq] = l[qq] = 0.f;
+        mx[qq] = -__builtin_inff();
+      }
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         f32x16_t sacc = f32x16_t{}, iacc = f32x16_t{};
-        const uint8_t* qr = q_row;
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
           const int c = 8 * h + t;
-          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(ks_row + kt * 32 * 256 + ((c ^ ks_sw) << 4));
-          const u32x4_t bq = *reinterpret_cast<const u32x4_t*>(qr + ((c ^ ks_sw) << 4));
-          sacc = mfma_32x32x16(as_bf16x8(a), as_bf16x8(bq), sacc);
+          const u32x4_t aq = *reinterpret_cast<const u32x4_t*>(q_row + ((c ^ ks_sw) << 4));
+          const u32x4_t bk = *reinterpret_cast<const u32x4_t*>(ks_row + kt * 32 * 256 + ((c ^ ks_sw) << 4));
+          sacc = mfma_32x32x16(as_bf16x8(aq), as_bf16x8(bk), sacc);
         }
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int c = 4 * h + t;
-          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(ki_row + kt * 32 * 128 + ((c ^ ki_sw) << 4));
-          iacc = mfma_32x32x16(as_bf16x8(a), as_bf16x8(qi_op[t]), iacc);
+          const u32x4_t bk = *reinterpret_cast<const u32x4_t*>(ki_row + kt * 32 * 128 + ((c ^ ki_sw) << 4));
+          iacc = mfma_32x32x16(as_bf16x8(qi_op[t]), as_bf16x8(bk), iacc);
         }
-        float tm = -__builtin_inff();
+        const int koff = kt * 32 + koff0;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int off = kt * 32 + 16 * (v >> 3) + 4 * ((v >> 2) & 1) + (v & 3);
-          const bool in = !part_blk || off <= lim;
-          const float p = in ? __builtin_amdgcn_exp2f(fmaf(sacc[v], scale_log2, -l2h)) : 0.f;
-          const float P = head_sum<G>(p) * (1.f / G);
-          const float sv = in ? iacc[v] * 0.125f : -__builtin_inff();  // 1 / sqrt(d_idx)
-          iacc[v] = sv;
-          tm = fmaxf(tm, sv);
+        for (int qq = 0; qq < NQ; ++qq) {
+          const bool in = !part_blk || koff <= lim[qq];
+          float ps = 0.f;
+#pragma unroll
+          for (int e = 0; e < GL; ++e) {
+            const int v = qq * GL + e;
+            ps += __builtin_amdgcn_exp2f(fmaf(sacc[v], scale_log2, -l2v[v]));
+          }
+          if constexpr (KlRows<G>::kCross) ps += __shfl_xor(ps, 32);
+          const float P = in ? ps * (1.f / G) : 0.f;
+          const float S = iacc[qq * GL] * 0.125f;  // 1 / sqrt(d_idx)
           const bool pos = P > 0.f;
-          Z += P;
-          C += pos ? P * sv : 0.f;
-          A += pos ? P * (__log2f(P) * kLn2) : 0.f;
+          Z[qq] += P;
+          C[qq] += pos ? P * S : 0.f;
+          A[qq] += pos ? P * (__log2f(P) * kLn2) : 0.f;
+          // running log partition of the index scores
+          const float Sm = in ? S : -__builtin_inff();
+          const float nm = fmaxf(mx[qq], Sm);
+          const float ref = nm == -__builtin_inff() ? 0.f : nm;
+          l[qq] = l[qq] * __builtin_amdgcn_exp2f((mx[qq] - ref) * kLog2e) +
+                  __builtin_amdgcn_exp2f((Sm - ref) * kLog2e);
+          mx[qq] = nm;
         }
-        const float nm = fmaxf(mx, tm);
-        if (nm != -__builtin_inff()) {
-          float lt = 0.f;
-#pragma unroll
-          for (int v = 0; v < 16; ++v) lt += __builtin_amdgcn_exp2f((iacc[v] - nm) * kLog2e);
-          l = (mx == -__builtin_inff() ? 0.f : l * __builtin_amdgcn_exp2f((mx - nm) * kLog2e)) + lt;
-          mx = nm;
-        }
-        // One tile's accumulators live at a time.
-        __builtin_amdgcn_sched_barrier(0);
       }
-      // Merge the two lane halves (the other 64 keys of the block).
-      const float mo = __shfl_xor(mx, 32), lo = __shfl_xor(l, 32);
-      const float mi = fmaxf(mx, mo);
-      if (mi != -__builtin_inff())
-        l = (mx == -__builtin_inff() ? 0.f : l * __builtin_amdgcn_exp2f((mx - mi) * kLog2e)) +
-            (mo == -__builtin_inff() ? 0.f : lo * __builtin_amdgcn_exp2f((mo - mi) * kLog2e));
-      A += __shfl_xor(A, 32);
-      C += __shfl_xor(C, 32);
-      Z += __shfl_xor(Z, 32);
-      if (g == 0 && h == 0) {
-        float* dst = part + (((int64_t)i_local * H_kv + r) * kk + s) * kKlPart;
-        *reinterpret_cast<float4*>(dst) = make_float4(A, C, Z, mi);
-        dst[4] = l;
+      // Sum over the block's keys (the 32 columns of a lane half, 4 tiles each).
+#pragma unroll
+      for (int qq = 0; qq < NQ; ++qq) {
+        const float a = half_sum(A[qq]), c = half_sum(C[qq]), z = half_sum(Z[qq]);
+        const float M = half_max(mx[qq]);
+        const float ref = M == -__builtin_inff() ? 0.f : M;
+        const float ls = half_sum(l[qq] * __builtin_amdgcn_exp2f((mx[qq] - ref) * kLog2e));
+        const bool writer = l32 == 0 && (!KlRows<G>::kCross || h == 0);
+        if (writer) {
+          const int pq = prq[qq];
+          float* dst = part + (((int64_t)(pq >> 5) * H_kv + r) * kk + (pq & 31)) * kKlPart;
+          *reinterpret_cast<float4*>(dst) = make_float4(a, c, z, M);
+          dst[4] = ls;
+        }
       }
 
       to_lds();
       cur = cur_n;
       pr = pr_n;
-      l2h = l2_n;
+      l2own = l2_n;
 #pragma unroll
       for (int t = 0; t < 4; ++t) qi_op[t] = qi_n[t];
     }
