@@ -62,6 +62,10 @@ def _load():
                                       P, P, P, P, i64]
     lib.msa_oracle_decode_attn.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, dbl, P, P, P]
     lib.msa_oracle_sparse_kl.argtypes = [P, P, P, P, P, i64, i32, i32, i32, i32, i32, i32, dbl, P, i64, P, P]
+    lib.msa_oracle_fp8_e4m3.argtypes = [ctypes.c_uint8]
+    lib.msa_oracle_fp8_e4m3.restype = dbl
+    lib.msa_oracle_decode_paged.argtypes = [P, P, P, P, dbl, dbl, P, P, i64, P, i32, i32, i32, i32, i32, i32, i32,
+                                            dbl, P, P, P, P, i64]
     _lib = lib
     return lib
 
@@ -271,3 +275,48 @@ def sparse_attn_varlen(q, k, v, block_idx, cu_seqlens, B_k: int, scale: float | 
             continue
         o[a:b], lse[a:b] = sparse_attn(qq[a:b], kk_[a:b], vv[a:b], bi[a:b], B_k, scale)
     return o, lse
+
+
+def fp8_e4m3(code: int) -> float:
+    """OCP FP8 E4M3 code -> value."""
+    return float(_load().msa_oracle_fp8_e4m3(code))
+
+
+def _u8(x) -> np.ndarray:
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().cpu()
+            if x.dtype != torch.uint8:
+                x = x.view(torch.uint8)
+            return np.ascontiguousarray(x.numpy())
+    except ImportError:
+        pass
+    return np.ascontiguousarray(np.asarray(x, dtype=np.uint8))
+
+
+def decode_paged(q, q_idx, k_pages, v_pages, k_scale: float, v_scale: float, kidx_pages, block_table, seqlens,
+                 k: int, B_k: int, scale: float | None = None, want_scores: bool = False):
+    """Decode over paged caches (FP8 E4M3 K/V pages, bf16 index-key pages).  Returns
+    block_idx, o, lse[, M] as ``decode``."""
+    qq, qi, kip = _u16(q), _u16(q_idx), _u16(kidx_pages)
+    kp, vp = _u8(k_pages), _u8(v_pages)
+    bt = np.ascontiguousarray(np.asarray(block_table.cpu() if hasattr(block_table, "cpu") else block_table,
+                                         dtype=np.int32))
+    lens = np.ascontiguousarray(np.asarray(seqlens.cpu() if hasattr(seqlens, "cpu") else seqlens, dtype=np.int64))
+    batch, H_q, d_h = qq.shape
+    H_kv, d_idx = qi.shape[1], qi.shape[2]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d_h)
+    Bmax = int((lens.max() + B_k - 1) // B_k) if batch else 0
+    bi = np.empty((batch, H_kv, k), dtype=np.int32)
+    o = np.empty((batch, H_q, d_h), dtype=np.float64)
+    lse = np.empty((batch, H_q), dtype=np.float64)
+    M = np.empty((batch, H_kv, Bmax), dtype=np.float64) if want_scores else None
+    _load().msa_oracle_decode_paged(_ptr(qq), _ptr(qi), _ptr(kp), _ptr(vp), float(k_scale), float(v_scale),
+                                    _ptr(kip), _ptr(bt), bt.shape[1], _ptr(lens), batch, H_q, H_kv, d_h, d_idx, B_k,
+                                    k, float(scale), _ptr(bi), _ptr(o), _ptr(lse), None if M is None else _ptr(M),
+                                    Bmax)
+    if want_scores:
+        return bi, o, lse, M
+    return bi, o, lse

@@ -7,6 +7,8 @@
  *   Eq. 7  Top-k, local block forced -> topk_row()
  *   Eq. 8  softmax over the chosen   -> attn_row()
  *   Eq. 9-10 KL alignment per row    -> kl_row()
+ *   paged FP8 decode: OCP E4M3 codes -> msa_oracle_fp8_e4m3(), pages looked up
+ *   per token
  * (page "MiniMax Sparse Attention (MSA)" paper review, section 3; page
  * "papers.chlience.com" reading notes, section 5.1 and 5.1.1.)
  * No blocking, fusion or reordering beyond the definitions; OpenMP only
@@ -337,5 +339,88 @@ void msa_oracle_sparse_kl(const uint16_t* q, const uint16_t* k, const uint16_t* 
     free(sidx);
     free(tok);
     free(inset);
+  }
+}
+
+/*
+ * OCP FP8 E4M3 (the "fn" variant: no infinities, S.1111.111 is NaN): 1 sign bit,
+ * 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 holds the
+ * subnormals m/8 * 2^-6.
+ */
+double msa_oracle_fp8_e4m3(uint8_t x) {
+  int sgn = x >> 7, e = (x >> 3) & 15, m = x & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexp(m / 8.0, -6);
+  else
+    v = ldexp(1.0 + m / 8.0, e - 7);
+  return sgn ? -v : v;
+}
+
+void msa_oracle_decode_paged(const uint16_t* q, const uint16_t* q_idx, const uint8_t* k_pages,
+                             const uint8_t* v_pages, double k_scale, double v_scale,
+                             const uint16_t* kidx_pages, const int32_t* block_table,
+                             int64_t max_blocks, const int64_t* seqlens, int batch, int H_q,
+                             int H_kv, int d_h, int d_idx, int B_k, int kk, double scale,
+                             int32_t* block_idx, double* o, double* lse, double* M, int64_t Bmax) {
+  int G = H_q / H_kv;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int s = 0; s < batch; ++s) {
+    int64_t L = seqlens[s];
+    if (L <= 0) continue;
+    int64_t i = L - 1; /* the new token is the last cached token */
+    int64_t B = msa_oracle_num_blocks(L, B_k);
+    const int32_t* pages = block_table + (int64_t)s * max_blocks;
+    /* the sequence's index keys in token order, gathered from its pages */
+    uint16_t* kidx = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)L * d_idx);
+    for (int64_t j = 0; j < L; ++j)
+      memcpy(kidx + j * d_idx, kidx_pages + ((int64_t)pages[j / B_k] * B_k + j % B_k) * d_idx,
+             sizeof(uint16_t) * d_idx);
+    double* Mrow = (double*)malloc(sizeof(double) * (size_t)B);
+    char* chosen = (char*)malloc((size_t)B + 1);
+    double* s_buf = (double*)malloc(sizeof(double) * (size_t)L);
+    for (int r = 0; r < H_kv; ++r) {
+      score_row(q_idx + ((int64_t)s * H_kv + r) * d_idx, kidx, i, d_idx, B_k, B, Mrow);
+      if (M) {
+        double* Mo = M + ((int64_t)s * H_kv + r) * Bmax;
+        for (int64_t b = 0; b < Bmax; ++b) Mo[b] = b < B ? Mrow[b] : -INFINITY;
+      }
+      int32_t* sel = block_idx + ((int64_t)s * H_kv + r) * kk;
+      topk_row(Mrow, i, B_k, kk, sel, chosen);
+      memset(chosen, 0, (size_t)B);
+      for (int t = 0; t < kk; ++t)
+        if (sel[t] >= 0) chosen[sel[t]] = 1;
+      /* Eq. 8 with K = k_scale * code, V = v_scale * code, read through the pages */
+      for (int g = 0; g < G; ++g) {
+        int h = r * G + g;
+        const uint16_t* qv = q + ((int64_t)s * H_q + h) * d_h;
+        double m = -INFINITY;
+        for (int64_t j = 0; j <= i; ++j) {
+          if (!chosen[block_of(j, B_k)]) continue;
+          const uint8_t* kr = k_pages + (((int64_t)pages[j / B_k] * B_k + j % B_k) * H_kv + r) * d_h;
+          double sv = 0.0;
+          for (int d = 0; d < d_h; ++d) sv += bf16(qv[d]) * (k_scale * msa_oracle_fp8_e4m3(kr[d]));
+          s_buf[j] = sv * scale;
+          if (s_buf[j] > m) m = s_buf[j];
+        }
+        double* orow = o + ((int64_t)s * H_q + h) * d_h;
+        for (int d = 0; d < d_h; ++d) orow[d] = 0.0;
+        double l = 0.0;
+        for (int64_t j = 0; j <= i; ++j) {
+          if (!chosen[block_of(j, B_k)]) continue;
+          const uint8_t* vr = v_pages + (((int64_t)pages[j / B_k] * B_k + j % B_k) * H_kv + r) * d_h;
+          double p = exp(s_buf[j] - m);
+          l += p;
+          for (int d = 0; d < d_h; ++d) orow[d] += p * (v_scale * msa_oracle_fp8_e4m3(vr[d]));
+        }
+        for (int d = 0; d < d_h; ++d) orow[d] /= l;
+        lse[(int64_t)s * H_q + h] = m + log(l);
+      }
+    }
+    free(s_buf);
+    free(chosen);
+    free(Mrow);
+    free(kidx);
   }
 }

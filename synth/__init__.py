@@ -293,3 +293,63 @@ def packed_prefill(lengths, H_q: int, H_kv: int, k: int, seed: int, mode: str = 
 
     return PackedPrefillInputs(list(lengths), cu.to(device), cat("q", (H_q, 128)), cat("k", (H_kv, 128)),
                                cat("v", (H_kv, 128)), cat("q_idx", (H_kv, 64)), cat("k_idx", (64,)))
+
+
+T_PAGE = 10  # tensor id of the page permutation
+
+
+@dataclass
+class PagedDecodeInputs:
+    lengths: list
+    seqlens: torch.Tensor      # [batch] int64
+    block_table: torch.Tensor  # [batch, max_blocks] int32 (unused entries -1)
+    q: torch.Tensor            # [batch, H_q, d_h] bf16
+    q_idx: torch.Tensor        # [batch, H_kv, d_idx] bf16
+    k_pages: torch.Tensor      # [P, B_k, H_kv, d_h] uint8 (FP8 E4M3 codes)
+    v_pages: torch.Tensor      # [P, B_k, H_kv, d_h] uint8
+    kidx_pages: torch.Tensor   # [P, B_k, d_idx] bf16
+    k_scale: float
+    v_scale: float
+    contiguous: DecodeInputs   # the bf16 caches the pages were made from
+
+
+def quantize_fp8(x: torch.Tensor):
+    """Per-tensor scale amax / 448 and the OCP E4M3 codes (torch's round-to-nearest)."""
+    amax = float(x.float().abs().max()) if x.numel() else 1.0
+    scale = amax / 448.0 if amax > 0 else 1.0
+    codes = (x.float() / scale).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes, scale
+
+
+def make_decode_paged(cfg: DecodeConfig, mode: str = "literal", device="cpu", lengths=None,
+                      spare_pages: int = 3) -> PagedDecodeInputs:
+    """The decode inputs of ``make_decode`` moved into a paged cache: K/V quantised to
+    FP8 E4M3 with per-tensor scales, index keys kept bf16, pages of B_k tokens placed
+    in a seeded random order (plus a few unused pages)."""
+    d = make_decode(cfg, mode, device="cpu", lengths=lengths)
+    B_k = cfg.B_k
+    nblk = [(L + B_k - 1) // B_k for L in d.lengths]
+    P = sum(nblk) + spare_pages
+    perm = torch.randperm(P, generator=_gen(cfg.seed, T_PAGE, "cpu"))
+    max_blocks = max(nblk) if nblk else 1
+    table = torch.full((len(d.lengths), max_blocks), -1, dtype=torch.int32)
+    kq, k_scale = quantize_fp8(d.k_cache)
+    vq, v_scale = quantize_fp8(d.v_cache)
+    k_pages = torch.zeros((P, B_k, cfg.H_kv, cfg.d_h), dtype=torch.uint8)
+    v_pages = torch.zeros_like(k_pages)
+    kidx_pages = torch.zeros((P, B_k, cfg.d_idx), dtype=torch.bfloat16)
+    cu = d.cu_seqlens.tolist()
+    nxt = 0
+    for s, L in enumerate(d.lengths):
+        for b in range(nblk[s]):
+            p = int(perm[nxt])
+            nxt += 1
+            table[s, b] = p
+            t0, t1 = cu[s] + b * B_k, min(cu[s] + (b + 1) * B_k, cu[s + 1])
+            k_pages[p, :t1 - t0] = kq[t0:t1]
+            v_pages[p, :t1 - t0] = vq[t0:t1]
+            kidx_pages[p, :t1 - t0] = d.k_idx_cache[t0:t1]
+    seqlens = torch.tensor(d.lengths, dtype=torch.int64)
+    mv = lambda t: t.to(device)
+    return PagedDecodeInputs(list(d.lengths), mv(seqlens), mv(table), mv(d.q), mv(d.q_idx), mv(k_pages),
+                             mv(v_pages), mv(kidx_pages), k_scale, v_scale, d)

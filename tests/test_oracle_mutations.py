@@ -42,6 +42,14 @@ MUTANTS = [
     ("kl_not_causal", "for (int64_t j = 0; j <= jmax; ++j)\n    if (inset", "for (int64_t j = 0; j < N; ++j)\n    if (inset"),
     ("kl_index_query_group", "q_idx + (i * H_kv + r) * d_idx", "q_idx + (i * H_kv) * d_idx"),
     ("kl_lse_idx_missing_max", "double lse_idx = mi + log(li);", "double lse_idx = log(li);"),
+    ("fp8_exponent_bias", "v = ldexp(1.0 + m / 8.0, e - 7);", "v = ldexp(1.0 + m / 8.0, e - 8);"),
+    ("fp8_subnormal_scale", "v = ldexp(m / 8.0, -6);", "v = ldexp(m / 8.0, -7);"),
+    ("paged_wrong_row", "(((int64_t)pages[j / B_k] * B_k + j % B_k) * H_kv + r) * d_h;\n          double sv",
+     "(((int64_t)pages[j / B_k] * B_k + (j + 1) % B_k) * H_kv + r) * d_h;\n          double sv"),
+    ("paged_scales_swapped", "sv += bf16(qv[d]) * (k_scale * msa_oracle_fp8_e4m3(kr[d]));",
+     "sv += bf16(qv[d]) * (v_scale * msa_oracle_fp8_e4m3(kr[d]));"),
+    ("paged_index_page", "kidx_pages + ((int64_t)pages[j / B_k] * B_k + j % B_k) * d_idx",
+     "kidx_pages + ((int64_t)(j / B_k) * B_k + j % B_k) * d_idx"),
 ]
 
 
@@ -66,6 +74,9 @@ def _all_pins():
     yield "kl_closed_form", pins.test_kl_closed_form_mean_of_two_heads
     yield "kl_token_set", pins.test_kl_token_set_is_causal_and_selected
     yield "kl_groups", pins.test_kl_is_nonnegative_and_groups_are_separate
+    yield "fp8", pins.test_fp8_e4m3_decoding
+    yield "paged", pins.test_paged_fp8_decode_equals_contiguous_decode
+    yield "paged_scales", pins.test_paged_fp8_scales_multiply_keys_and_values
 
 
 @pytest.mark.parametrize("mutant", MUTANTS, ids=lambda m: m[0])

@@ -419,3 +419,75 @@ def test_kl_is_nonnegative_and_groups_are_separate():
     kl1, li1 = oracle.sparse_kl(inp.q[:, 4:], inp.k[:, 1:], inp.q_idx[:, 1:], inp.k_idx, bi[:, 1:], 128)
     np.testing.assert_array_equal(kl1[:, 0], kl[:, 1])
     np.testing.assert_array_equal(li1[:, 0], lse_idx[:, 1])
+
+
+# --- Paged FP8 decode ------------------------------------------------------------------------
+
+def test_fp8_e4m3_decoding():
+    codes = torch.arange(256, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).double().numpy()  # the library's own decoding
+    got = np.array([oracle.fp8_e4m3(c) for c in range(256)])
+    assert np.array_equal(np.isnan(got), np.isnan(ref)) and np.isnan(got).sum() == 2
+    np.testing.assert_array_equal(got[~np.isnan(got)], ref[~np.isnan(ref)])
+    # format definition: 1.0, the largest finite 448, the smallest subnormal 2^-9,
+    # the smallest normal 2^-6, and the sign bit
+    assert (got[0x38], got[0x7E], got[0x01], got[0x08], got[0xB8]) == (1.0, 448.0, 2.0 ** -9, 2.0 ** -6, -1.0)
+
+
+def _exact_fp8_decode_case(lengths, seed):
+    """A decode case whose bf16 K/V hold exactly FP8-representable values, with the
+    paged FP8 copy of it (scales 1)."""
+    cfg = synth.DecodeConfig("t", batch=len(lengths), H_q=4, H_kv=2, k=3, len_lo_blocks=1, len_hi_blocks=1,
+                             seed=seed)
+    d = synth.make_decode(cfg, lengths=lengths)
+    for t in (d.k_cache, d.v_cache):
+        t.copy_(t.float().to(torch.float8_e4m3fn).float().to(torch.bfloat16))
+    return cfg, d
+
+
+def _paged_copy(d, B_k, perm_seed, k_div=1.0, v_div=1.0):
+    nblk = [(L + B_k - 1) // B_k for L in d.lengths]
+    P = sum(nblk) + 2
+    perm = np.random.default_rng(perm_seed).permutation(P)
+    H_kv, d_h = d.k_cache.shape[1], d.k_cache.shape[2]
+    kp = torch.zeros((P, B_k, H_kv, d_h), dtype=torch.uint8)
+    vp = torch.zeros_like(kp)
+    kip = torch.zeros((P, B_k, d.k_idx_cache.shape[1]), dtype=torch.bfloat16)
+    table = np.full((len(d.lengths), max(nblk)), -1, np.int32)
+    cu = d.cu_seqlens.tolist()
+    kq = (d.k_cache.float() / k_div).to(torch.float8_e4m3fn).view(torch.uint8)
+    vq = (d.v_cache.float() / v_div).to(torch.float8_e4m3fn).view(torch.uint8)
+    n = 0
+    for s, L in enumerate(d.lengths):
+        for b in range(nblk[s]):
+            p = int(perm[n])
+            n += 1
+            table[s, b] = p
+            t0, t1 = cu[s] + b * B_k, min(cu[s] + (b + 1) * B_k, cu[s + 1])
+            kp[p, :t1 - t0], vp[p, :t1 - t0] = kq[t0:t1], vq[t0:t1]
+            kip[p, :t1 - t0] = d.k_idx_cache[t0:t1]
+    return kp, vp, kip, table
+
+
+def test_paged_fp8_decode_equals_contiguous_decode():
+    # Exactly representable K/V, scales 1, pages in a shuffled order: the paged FP8
+    # decode must reproduce the contiguous bf16 decode bit for bit.
+    lengths = [130, 64, 257, 1]
+    cfg, d = _exact_fp8_decode_case(lengths, 41)
+    kp, vp, kip, table = _paged_copy(d, 128, 5)
+    ref = oracle.decode(d.q, d.q_idx, d.k_cache, d.v_cache, d.k_idx_cache, d.cu_seqlens, 3, 128, want_scores=True)
+    got = oracle.decode_paged(d.q, d.q_idx, kp, vp, 1.0, 1.0, kip, table, lengths, 3, 128, want_scores=True)
+    for a, b in zip(got, ref):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_paged_fp8_scales_multiply_keys_and_values():
+    # Codes of 2K and 4V with k_scale 1/2 and v_scale 1/4 describe the same K and V
+    # (scaling up by powers of two keeps every value exact).
+    lengths = [300, 129]
+    cfg, d = _exact_fp8_decode_case(lengths, 43)
+    kp, vp, kip, table = _paged_copy(d, 128, 6, k_div=0.5, v_div=0.25)
+    ref = oracle.decode(d.q, d.q_idx, d.k_cache, d.v_cache, d.k_idx_cache, d.cu_seqlens, 3, 128)
+    got = oracle.decode_paged(d.q, d.q_idx, kp, vp, 0.5, 0.25, kip, table, lengths, 3, 128)
+    for a, b in zip(got, ref):
+        np.testing.assert_array_equal(a, b)
