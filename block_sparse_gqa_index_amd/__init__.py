@@ -46,6 +46,8 @@ _SIGS = {
     "msa_sparse_kl_fwd_workspace_min": ([_I64, _I32, _I32, _I32, _I32, _I32, _I32], _SZ),
     "msa_sparse_kl_fwd": ([_P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _F32, _P, _P, _P, _P, _SZ,
                            _P], _I32),
+    "msa_decode_paged": ([_P, _P, _P, _P, _F32, _F32, _P, _P, _I64, _P, _I32, _I64, _I32, _I32, _I32, _I32, _I32, _I32,
+                          _F32, _P, _P, _P, _P, _SZ, _P], _I32),
     "msa_index_topk_varlen": ([_P, _P, _P, _I32, _I64, _I64, _I32, _I32, _I32, _I32, _P, _P], _I32),
     "msa_sparse_attn_fwd_varlen_workspace": ([_I64, _I32, _I32, _I32, _I32, _I32, _I32], _SZ),
     "msa_sparse_attn_fwd_varlen_workspace_min": ([_I64, _I32, _I32, _I32, _I32, _I32, _I32], _SZ),
@@ -305,6 +307,43 @@ def msa_decode(q: torch.Tensor, q_idx: torch.Tensor, k_cache: torch.Tensor, v_ca
     _check(_lib.msa_decode(_ptr(q), _ptr(q_idx), _ptr(k_cache), _ptr(v_cache), _ptr(k_idx_cache), _ptr(cu_seqlens),
                            batch, max_len, H_q, H_kv, d_h, d_idx, B_k, k, float(scale), _ptr(block_idx), _ptr(o),
                            _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "msa_decode")
+    return block_idx, o, lse
+
+
+def msa_decode_paged(q: torch.Tensor, q_idx: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
+                     k_scale: float, v_scale: float, k_idx_pages: torch.Tensor, block_table: torch.Tensor,
+                     seqlens: torch.Tensor, max_len: int, k: int, B_k: int = 128, scale: float | None = None,
+                     block_idx=None, o=None, lse=None, workspace=None, stream=None):
+    """Decode over paged FP8 E4M3 K/V pages (uint8 codes) and bf16 index-key pages.
+    Returns (block_idx, o, lse)."""
+    batch, H_q, d_h = q.shape
+    H_kv, d_idx = q_idx.shape[1], q_idx.shape[2]
+    P = k_pages.shape[0]
+    _need(q, "q", torch.bfloat16, (batch, H_q, d_h))
+    _need(q_idx, "q_idx", torch.bfloat16, (batch, H_kv, d_idx))
+    _need(k_pages, "k_pages", torch.uint8, (P, B_k, H_kv, d_h))
+    _need(v_pages, "v_pages", torch.uint8, (P, B_k, H_kv, d_h))
+    _need(k_idx_pages, "k_idx_pages", torch.bfloat16, (P, B_k, d_idx))
+    _need(block_table, "block_table", torch.int32, (batch, block_table.shape[1]))
+    _need(seqlens, "seqlens", torch.int64, (batch,))
+    if scale is None:
+        scale = d_h ** -0.5
+    dev = q.device
+    if block_idx is None:
+        block_idx = torch.empty((batch, H_kv, k), dtype=torch.int32, device=dev)
+    if o is None:
+        o = torch.empty((batch, H_q, d_h), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((batch, H_q), dtype=torch.float32, device=dev)
+    _need(block_idx, "block_idx", torch.int32, (batch, H_kv, k))
+    _need(o, "o", torch.float32, (batch, H_q, d_h))
+    _need(lse, "lse", torch.float32, (batch, H_q))
+    ws = _ws(_lib.msa_decode_workspace(batch, H_q, H_kv, d_h, d_idx, B_k, k, max_len), dev, workspace)
+    _check(_lib.msa_decode_paged(_ptr(q), _ptr(q_idx), _ptr(k_pages), _ptr(v_pages), float(k_scale), float(v_scale),
+                                 _ptr(k_idx_pages), _ptr(block_table), block_table.shape[1], _ptr(seqlens), batch,
+                                 max_len, H_q, H_kv, d_h, d_idx, B_k, k, float(scale), _ptr(block_idx), _ptr(o),
+                                 _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "msa_decode_paged")
     return block_idx, o, lse
 
 

@@ -15,6 +15,8 @@
 //      chosen blocks) streams those blocks' K/V (64 KB each) once for the G heads
 //      of the group, with an online softmax across the part's blocks.
 //   4. combine: LSE merge of the parts per (sequence, head).
+#include <type_traits>
+
 #include "msa_device.h"
 #include "msa_kernels.h"
 
@@ -24,18 +26,61 @@ namespace {
 
 constexpr int kScoreBlocksPerWG = 4;  // one block (128 keys) per wave
 
-__global__ __launch_bounds__(256) void dec_score_kernel(const uint16_t* __restrict__ q_idx,
-                                                        const uint16_t* __restrict__ k_idx,
-                                                        const int64_t* __restrict__ cu, int H_kv, int64_t Bmax,
-                                                        float* __restrict__ M) {
+// Where a sequence's cached tokens live.
+// Packed: sequences back to back (offsets cu), bf16 K/V rows [T][H_kv][d_h].
+struct PackedCache {
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* kidx;
+  const int64_t* cu;
+  __device__ int64_t len(int s) const { return cu[s + 1] - cu[s]; }
+  // First index key of block b of sequence s (keys of a block are consecutive rows).
+  __device__ const uint16_t* kidx_block(int s, int64_t b) const { return kidx + (cu[s] + b * kBk) * kDidx; }
+  // Element offset of (block b, key 0, group r) in the K/V rows; rows are H_kv * d_h apart.
+  __device__ int64_t kv_block(int s, int64_t b, int r, int H_kv) const { return ((cu[s] + b * kBk) * H_kv + r) * kDh; }
+};
+
+// Paged: pages of kBk tokens, token j of sequence s in row j % kBk of page
+// table[s][j / kBk]; K/V pages hold FP8 E4M3 codes (K = k_scale * value, V = v_scale *
+// value, the scales applied by the caller's arithmetic), index-key pages bf16.
+struct PagedFp8Cache {
+  const uint8_t* k;
+  const uint8_t* v;
+  const uint16_t* kidx;
+  const int32_t* table;
+  int64_t max_blocks;
+  const int64_t* lens;
+  __device__ int64_t len(int s) const { return lens[s]; }
+  __device__ int64_t page(int s, int64_t b) const { return table[(int64_t)s * max_blocks + b]; }
+  __device__ const uint16_t* kidx_block(int s, int64_t b) const { return kidx + page(s, b) * kBk * kDidx; }
+  __device__ int64_t kv_block(int s, int64_t b, int r, int H_kv) const {
+    return (page(s, b) * kBk * H_kv + r) * kDh;
+  }
+};
+
+// Eight FP8 E4M3 codes -> eight bf16 (exact: an E4M3 value has at most 4
+// significant bits, so its f32 form has zero low halves).
+__device__ __forceinline__ u32x4_t fp8x8_to_bf16x8(u32x2_t w) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const f2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false);
+  const f2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
+  const f2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false);
+  const f2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
+  auto pk = [](float lo, float hi) { return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u); };
+  return u32x4_t{pk(a.x, a.y), pk(b.x, b.y), pk(c.x, c.y), pk(d.x, d.y)};
+}
+
+template <class Cache>
+__global__ __launch_bounds__(256) void dec_score_kernel(const uint16_t* __restrict__ q_idx, Cache cache, int H_kv,
+                                                        int64_t Bmax, float* __restrict__ M) {
   __shared__ __attribute__((aligned(16))) uint8_t kstage[kScoreBlocksPerWG][64 * 128];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int s = blockIdx.x;
-  const int64_t j0 = cu[s];
-  const int64_t L = cu[s + 1] - j0;
+  const int64_t L = cache.len(s);
   const int64_t nb = (L + kBk - 1) / kBk;
   const int64_t b = (int64_t)blockIdx.y * kScoreBlocksPerWG + wave;
   if (b >= nb || b >= Bmax) return;
+  const uint16_t* __restrict__ kb = cache.kidx_block(s, b);
   const int col = lane & 15, grp = lane >> 4;
   uint4 qop[2];
 #pragma unroll
@@ -50,8 +95,8 @@ __global__ __launch_bounds__(256) void dec_score_kernel(const uint16_t* __restri
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int64_t key = b * kBk + 8 * j + (lane >> 3);
-    const int64_t kr = key < L ? key : L - 1;
-    raw[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(k_idx + (j0 + kr) * kDidx + (lane & 7) * 8));
+    const int kr = (int)((key < L ? key : L - 1) - b * kBk);
+    raw[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kb + kr * kDidx + (lane & 7) * 8));
   }
   // Half a block at a time through the wave's LDS buffer into the MFMA operand
   // layout (lane (col, grp) holds row col of a 16-row tile, dims 32ks + 8grp ..
@@ -91,15 +136,14 @@ __global__ __launch_bounds__(256) void dec_score_kernel(const uint16_t* __restri
 // 64j + lane with (j % 4) == w to per-lane register lists, extracts its k-1 best
 // by k-1 rounds of wave arg-max, and the four waves' candidates are merged by
 // wave 0 the same way.  The local (last) block is then added.
-template <int LIST>
-__global__ __launch_bounds__(256) void dec_topk_kernel(const float* __restrict__ M, const int64_t* __restrict__ cu,
-                                                       int batch, int H_kv, int64_t Bmax, int k,
-                                                       int32_t* __restrict__ block_idx) {
+template <int LIST, class Cache>
+__global__ __launch_bounds__(256) void dec_topk_kernel(const float* __restrict__ M, Cache cache, int batch, int H_kv,
+                                                       int64_t Bmax, int k, int32_t* __restrict__ block_idx) {
   __shared__ uint64_t cand[4][LIST];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t row = blockIdx.x;
   const int s = (int)(row / H_kv);
-  const int64_t L = cu[s + 1] - cu[s];
+  const int64_t L = cache.len(s);
   int32_t* out = block_idx + row * k;
   if (L <= 0) {
     for (int t = threadIdx.x; t < k; t += 256) out[t] = -1;
@@ -179,14 +223,14 @@ __global__ __launch_bounds__(256) void dec_topk_kernel(const float* __restrict__
 // LSE is written (LSE -inf: the part attended to nothing).
 constexpr int kDecSlotsPerPart = 8;
 
-template <int G>
-__global__ __launch_bounds__(256, 2) void dec_attn_kernel(const uint16_t* __restrict__ q,
-                                                          const uint16_t* __restrict__ kc,
-                                                          const uint16_t* __restrict__ vc,
-                                                          const int64_t* __restrict__ cu,
+// FP8 caches: the codes are widened to bf16 (exactly) on their way to LDS; the K
+// scale is folded into scale_log2 and the V scale (v_mul) into the partial output.
+template <int G, class Cache>
+__global__ __launch_bounds__(256, 2) void dec_attn_kernel(const uint16_t* __restrict__ q, Cache cache,
                                                           const int32_t* __restrict__ block_idx, int H_kv,
-                                                          int kk, int nparts, float scale_log2,
+                                                          int kk, int nparts, float scale_log2, float v_mul,
                                                           float* __restrict__ Opart, float* __restrict__ Lpart) {
+  constexpr bool kFp8 = sizeof(*cache.k) == 1;
   static_assert(G <= 16, "the merge reuses the 32 KB V^T buffer: 4 x G x 128 fp32");
   __shared__ __attribute__((aligned(16))) uint8_t Ks[kBk * 256];
   __shared__ __attribute__((aligned(16))) uint8_t Vt[kDh * 256];  // reused for the merge
@@ -197,10 +241,9 @@ __global__ __launch_bounds__(256, 2) void dec_attn_kernel(const uint16_t* __rest
   const int64_t sr = task / nparts;
   const int part = (int)(task % nparts);
   const int s = (int)(sr / H_kv), r = (int)(sr % H_kv);
-  const int64_t j0 = cu[s];
-  const int64_t L = cu[s + 1] - j0;
+  const int64_t L = cache.len(s);
   const int H_q = H_kv * G;
-  const int row_stride = H_kv * kDh;
+  const int row_stride = H_kv * kDh;  // elements between a group's consecutive key rows
   const int32_t* sel = block_idx + sr * kk;
   const int t0 = part * kDecSlotsPerPart;
   const int t1 = (t0 + kDecSlotsPerPart < kk) ? t0 + kDecSlotsPerPart : kk;
@@ -216,28 +259,43 @@ __global__ __launch_bounds__(256, 2) void dec_attn_kernel(const uint16_t* __rest
     if (tid < G) lp[tid] = -__builtin_inff();
     return;
   }
-  // Loads of one block into registers, coalesced: K as 8 rows x 16 B per thread
-  // (row (tid >> 4) + 16m holds key swap23 of it, chunk tid & 15), V as 8 keys x 8
-  // dims per thread; keys past the end are clamped, then zeroed.
-  u32x4_t kr[8], vr[8];
+  // Loads of one block into registers, coalesced: K as 8 rows x 8 dims per thread
+  // (row (tid >> 4) + 16m holds key swap23 of it, dims 8 * (tid & 15) ..), V as 8
+  // keys x 8 dims per thread; keys past the end are clamped, then zeroed.  FP8 rows
+  // arrive as 8-byte pieces and are widened in store_block.
+  using Raw = typename std::conditional<kFp8, u32x2_t, u32x4_t>::type;
+  Raw kr[8], vr[8];
+  auto load8 = [&](const auto* p, bool nt) -> Raw {
+    if constexpr (kFp8)
+      return nt ? __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p))
+                : *reinterpret_cast<const u32x2_t*>(p);
+    else
+      return nt ? ld16<true>(p) : ld16<false>(p);
+  };
   auto load_block = [&](int b) {
     const int64_t kb0 = (int64_t)b * kBk;
     const int nvalid = (L - kb0 < kBk) ? (int)(L - kb0) : kBk;
-    const int64_t base = ((j0 + kb0) * H_kv + r) * kDh;
+    const int64_t base = cache.kv_block(s, b, r, H_kv);
     const int c = tid & 15;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       const int key = swap23((tid >> 4) + 16 * m);
-      kr[m] = ld16<false>(kc + base + (int64_t)(key < nvalid ? key : nvalid - 1) * row_stride + c * 8);
-      if (key >= nvalid) kr[m] = u32x4_t{0u, 0u, 0u, 0u};
+      kr[m] = load8(cache.k + base + (int64_t)(key < nvalid ? key : nvalid - 1) * row_stride + c * 8, false);
+      if (key >= nvalid) kr[m] = Raw{};
     }
     const int kg = tid & 15, dc = tid >> 4;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int kv = kg * 8 + e;
-      vr[e] = ld16<true>(vc + base + (int64_t)(kv < nvalid ? kv : nvalid - 1) * row_stride + dc * 8);
-      if (kv >= nvalid) vr[e] = u32x4_t{0u, 0u, 0u, 0u};
+      vr[e] = load8(cache.v + base + (int64_t)(kv < nvalid ? kv : nvalid - 1) * row_stride + dc * 8, true);
+      if (kv >= nvalid) vr[e] = Raw{};
     }
+  };
+  auto widen = [&](const Raw& x) -> u32x4_t {
+    if constexpr (kFp8)
+      return fp8x8_to_bf16x8(x);
+    else
+      return x;
   };
   // The block to LDS from the registers: K row rho (256 B) at rho*256, chunk c at
   // position c ^ (rho & 15); V^T[d] (256 B) holds keys in natural order, 8-key
@@ -247,15 +305,18 @@ __global__ __launch_bounds__(256, 2) void dec_attn_kernel(const uint16_t* __rest
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       const int rho = (tid >> 4) + 16 * m;
-      *reinterpret_cast<u32x4_t*>(Ks + rho * 256 + ((c ^ (rho & 15)) << 4)) = kr[m];
+      *reinterpret_cast<u32x4_t*>(Ks + rho * 256 + ((c ^ (rho & 15)) << 4)) = widen(kr[m]);
     }
     const int kg = tid & 15, dc = tid >> 4;
+    u32x4_t vw[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vw[e] = widen(vr[e]);
 #pragma unroll
     for (int f = 0; f < 8; ++f) {
       u32x4_t o4;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const uint32_t x = vr[2 * m][f >> 1], y = vr[2 * m + 1][f >> 1];
+        const uint32_t x = vw[2 * m][f >> 1], y = vw[2 * m + 1][f >> 1];
         o4[m] = (f & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
       }
       const int d = dc * 8 + f;
@@ -389,7 +450,7 @@ __global__ __launch_bounds__(256, 2) void dec_attn_kernel(const uint16_t* __rest
       acc += wt * red[(w * G + g) * kDh + d];
       ls += wt * wl[w][g];
     }
-    op[e] = acc / ls;
+    op[e] = acc / ls * v_mul;
     if (d == 0) lp[g] = (M + __log2f(ls)) * kLn2;
   }
 }
@@ -454,34 +515,34 @@ DecodeWorkspace decode_workspace_layout(int batch, int H_q, int H_kv, int kk, in
   return L;
 }
 
-hipError_t launch_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_t* k_cache,
-                         const uint16_t* v_cache, const uint16_t* k_idx_cache, const int64_t* cu, int batch,
-                         int64_t Bmax, int H_q, int H_kv, int kk, float scale, int32_t* block_idx, float* o,
-                         float* lse, uint8_t* ws, const DecodeWorkspace& L, hipStream_t stream) {
+template <class Cache>
+static hipError_t launch_decode_impl(const uint16_t* q, const uint16_t* q_idx, const Cache& cache, int batch,
+                                     int64_t Bmax, int H_q, int H_kv, int kk, float scale_log2, float v_mul,
+                                     int32_t* block_idx, float* o, float* lse, uint8_t* ws,
+                                     const DecodeWorkspace& L, hipStream_t stream) {
   const int G = H_q / H_kv;
   float* M = reinterpret_cast<float*>(ws + L.M);
   float* opart = reinterpret_cast<float*>(ws + L.opart);
   float* lpart = reinterpret_cast<float*>(ws + L.lpart);
   hipError_t e;
-  dec_score_kernel<<<dim3((unsigned)batch, (unsigned)((Bmax + kScoreBlocksPerWG - 1) / kScoreBlocksPerWG)),
-                     dim3(256), 0, stream>>>(q_idx, k_idx_cache, cu, H_kv, Bmax, M);
+  dec_score_kernel<Cache><<<dim3((unsigned)batch, (unsigned)((Bmax + kScoreBlocksPerWG - 1) / kScoreBlocksPerWG)),
+                            dim3(256), 0, stream>>>(q_idx, cache, H_kv, Bmax, M);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const unsigned rows_grid = (unsigned)((int64_t)batch * H_kv);
   if (kk <= 8)
-    dec_topk_kernel<7><<<dim3(rows_grid), dim3(256), 0, stream>>>(M, cu, batch, H_kv, Bmax, kk, block_idx);
+    dec_topk_kernel<7, Cache><<<dim3(rows_grid), dim3(256), 0, stream>>>(M, cache, batch, H_kv, Bmax, kk, block_idx);
   else if (kk <= 16)
-    dec_topk_kernel<15><<<dim3(rows_grid), dim3(256), 0, stream>>>(M, cu, batch, H_kv, Bmax, kk, block_idx);
+    dec_topk_kernel<15, Cache><<<dim3(rows_grid), dim3(256), 0, stream>>>(M, cache, batch, H_kv, Bmax, kk, block_idx);
   else
-    dec_topk_kernel<31><<<dim3(rows_grid), dim3(256), 0, stream>>>(M, cu, batch, H_kv, Bmax, kk, block_idx);
+    dec_topk_kernel<31, Cache><<<dim3(rows_grid), dim3(256), 0, stream>>>(M, cache, batch, H_kv, Bmax, kk, block_idx);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const float scale_log2 = scale * kLog2e;
   const int nparts = (kk + kDecSlotsPerPart - 1) / kDecSlotsPerPart;
   const unsigned tasks = (unsigned)((int64_t)batch * H_kv * nparts);
   switch (G) {
-#define MSA_DEC_CASE(GG)                                                                              \
-  case GG:                                                                                            \
-    dec_attn_kernel<GG><<<dim3(tasks), dim3(256), 0, stream>>>(q, k_cache, v_cache, cu, block_idx, H_kv, \
-                                                               kk, nparts, scale_log2, opart, lpart);  \
+#define MSA_DEC_CASE(GG)                                                                                   \
+  case GG:                                                                                                 \
+    dec_attn_kernel<GG, Cache><<<dim3(tasks), dim3(256), 0, stream>>>(q, cache, block_idx, H_kv, kk, nparts, \
+                                                                      scale_log2, v_mul, opart, lpart);    \
     break;
     MSA_DEC_CASE(1)
     MSA_DEC_CASE(2)
@@ -497,6 +558,25 @@ hipError_t launch_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_
   dec_combine_kernel<<<dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream>>>(opart, lpart, batch, H_kv, G,
                                                                                   nparts, o, lse);
   return hipGetLastError();
+}
+
+hipError_t launch_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_t* k_cache,
+                         const uint16_t* v_cache, const uint16_t* k_idx_cache, const int64_t* cu, int batch,
+                         int64_t Bmax, int H_q, int H_kv, int kk, float scale, int32_t* block_idx, float* o,
+                         float* lse, uint8_t* ws, const DecodeWorkspace& L, hipStream_t stream) {
+  const PackedCache cache{k_cache, v_cache, k_idx_cache, cu};
+  return launch_decode_impl(q, q_idx, cache, batch, Bmax, H_q, H_kv, kk, scale * kLog2e, 1.f, block_idx, o, lse, ws,
+                            L, stream);
+}
+
+hipError_t launch_decode_paged(const uint16_t* q, const uint16_t* q_idx, const uint8_t* k_pages,
+                               const uint8_t* v_pages, float k_scale, float v_scale, const uint16_t* kidx_pages,
+                               const int32_t* block_table, int64_t max_blocks, const int64_t* seqlens, int batch,
+                               int64_t Bmax, int H_q, int H_kv, int kk, float scale, int32_t* block_idx, float* o,
+                               float* lse, uint8_t* ws, const DecodeWorkspace& L, hipStream_t stream) {
+  const PagedFp8Cache cache{k_pages, v_pages, kidx_pages, block_table, max_blocks, seqlens};
+  return launch_decode_impl(q, q_idx, cache, batch, Bmax, H_q, H_kv, kk, scale * k_scale * kLog2e, v_scale,
+                            block_idx, o, lse, ws, L, stream);
 }
 
 }  // namespace msa

@@ -425,4 +425,41 @@ msa_status_t msa_decode(const void* q, const void* q_idx, const void* k_cache, c
   return ok();
 }
 
+msa_status_t msa_decode_paged(const void* q, const void* q_idx, const void* k_pages, const void* v_pages,
+                              float k_scale, float v_scale, const void* k_idx_pages, const int32_t* block_table,
+                              int64_t max_blocks, const int64_t* seqlens, int batch, int64_t max_len, int H_q,
+                              int H_kv, int d_h, int d_idx, int B_k, int k, float scale, int32_t* block_idx,
+                              float* o, float* lse, void* ws, size_t ws_bytes, void* hip_stream) {
+  msa_status_t st = check_decode_shape(batch, max_len, H_q, H_kv, d_h, d_idx, B_k, k);
+  if (st != MSA_OK) return st;
+  if (!(scale > 0.f) || scale != scale) return fail(MSA_ERR_INVALID_ARG, "scale must be a positive number");
+  if (!(k_scale > 0.f) || !(v_scale > 0.f) || k_scale != k_scale || v_scale != v_scale ||
+      k_scale == __builtin_inff() || v_scale == __builtin_inff())
+    return fail(MSA_ERR_INVALID_ARG, "k_scale and v_scale must be positive finite numbers");
+  if (batch == 0) return ok();
+  if (max_len == 0) return fail(MSA_ERR_INVALID_ARG, "max_len must be >= 1 when batch > 0");
+  const int64_t Bmax = (max_len + B_k - 1) / B_k;
+  if (max_blocks < Bmax)
+    return fail(MSA_ERR_INVALID_ARG, "max_blocks (%lld) must cover ceil(max_len / B_k) = %lld",
+                (long long)max_blocks, (long long)Bmax);
+  if (!q || !q_idx || !k_pages || !v_pages || !k_idx_pages || !block_table || !seqlens || !block_idx || !o || !lse)
+    return fail(MSA_ERR_INVALID_ARG, "null pointer");
+  if (!aligned(q, 16) || !aligned(q_idx, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) ||
+      !aligned(k_idx_pages, 16) || !aligned(block_table, 4) || !aligned(seqlens, 8) || !aligned(block_idx, 4) ||
+      !aligned(o, 16) || !aligned(lse, 4))
+    return fail(MSA_ERR_INVALID_ARG, "misaligned pointer");
+  const size_t need = msa_decode_workspace(batch, H_q, H_kv, d_h, d_idx, B_k, k, max_len);
+  if (!ws || ws_bytes < need)
+    return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes is below the required %zu", ws ? ws_bytes : 0, need);
+  if (!aligned(ws, 256)) return fail(MSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const msa::DecodeWorkspace L = msa::decode_workspace_layout(batch, H_q, H_kv, k, Bmax);
+  hipError_t e = msa::launch_decode_paged(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(q_idx), static_cast<const uint8_t*>(k_pages),
+      static_cast<const uint8_t*>(v_pages), k_scale, v_scale, static_cast<const uint16_t*>(k_idx_pages), block_table,
+      max_blocks, seqlens, batch, Bmax, H_q, H_kv, k, scale, block_idx, o, lse, static_cast<uint8_t*>(ws), L,
+      static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "paged decode launch");
+  return ok();
+}
+
 }  // extern "C"

@@ -177,6 +177,31 @@ msa_status_t msa_decode(const void* q, const void* q_idx, const void* k_cache, c
                         float scale, int32_t* block_idx, float* o, float* lse, void* ws,
                         size_t ws_bytes, void* hip_stream);
 
+/* ------------------------------------------------------------------ Paged FP8 decode
+ * msa_decode_paged — msa_decode over a paged cache whose K/V are FP8 (the open
+ * interface's paged FP8 decode path, reading notes, section 5.4).  Pages hold B_k
+ * tokens; token j of sequence s is row j % B_k of page block_table[s][j / B_k].
+ *   k_pages, v_pages  uint8 [P, B_k, H_kv, d_h]  OCP FP8 E4M3 codes; the cached
+ *                     K = k_scale * value, V = v_scale * value (per-tensor scales)
+ *   k_idx_pages       bf16 [P, B_k, d_idx]       index keys (kept at bf16: they
+ *                     decide the selection)
+ *   block_table       int32 [batch, max_blocks], device; entries for blocks
+ *                     0 .. ceil(L_s / B_k) - 1 must be valid page numbers (not
+ *                     checked on the device), the rest are never read
+ *   seqlens           int64 [batch], device: L_s (the new token is position L_s - 1)
+ *   max_len           host-side bound on every L_s, as for msa_decode
+ * Other arguments and outputs as msa_decode; the workspace size is
+ * msa_decode_workspace() of the same shapes.  FP8 values are widened to bf16
+ * exactly; the K scale multiplies the scores and the V scale the output.
+ */
+msa_status_t msa_decode_paged(const void* q, const void* q_idx, const void* k_pages,
+                              const void* v_pages, float k_scale, float v_scale,
+                              const void* k_idx_pages, const int32_t* block_table,
+                              int64_t max_blocks, const int64_t* seqlens, int batch,
+                              int64_t max_len, int H_q, int H_kv, int d_h, int d_idx, int B_k,
+                              int k, float scale, int32_t* block_idx, float* o, float* lse,
+                              void* ws, size_t ws_bytes, void* hip_stream);
+
 /* ------------------------------------------------------------------ Split entry points
  * The pages' open interface separates a pass that emits per-block max scores from
  * the Top-k select (reading notes page, section 5.4).  These two calls expose the

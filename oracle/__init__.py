@@ -65,7 +65,7 @@ def _load():
     lib.msa_oracle_fp8_e4m3.argtypes = [ctypes.c_uint8]
     lib.msa_oracle_fp8_e4m3.restype = dbl
     lib.msa_oracle_decode_paged.argtypes = [P, P, P, P, dbl, dbl, P, P, i64, P, i32, i32, i32, i32, i32, i32, i32,
-                                            dbl, P, P, P, P, i64]
+                                            dbl, P, P, P, P, P, i64]
     _lib = lib
     return lib
 
@@ -296,9 +296,10 @@ def _u8(x) -> np.ndarray:
 
 
 def decode_paged(q, q_idx, k_pages, v_pages, k_scale: float, v_scale: float, kidx_pages, block_table, seqlens,
-                 k: int, B_k: int, scale: float | None = None, want_scores: bool = False):
+                 k: int, B_k: int, scale: float | None = None, want_scores: bool = False, block_idx=None):
     """Decode over paged caches (FP8 E4M3 K/V pages, bf16 index-key pages).  Returns
-    block_idx, o, lse[, M] as ``decode``."""
+    block_idx, o, lse[, M] as ``decode``; a given ``block_idx`` [batch, H_kv, k] is
+    used instead of the Top-k."""
     qq, qi, kip = _u16(q), _u16(q_idx), _u16(kidx_pages)
     kp, vp = _u8(k_pages), _u8(v_pages)
     bt = np.ascontiguousarray(np.asarray(block_table.cpu() if hasattr(block_table, "cpu") else block_table,
@@ -313,10 +314,15 @@ def decode_paged(q, q_idx, k_pages, v_pages, k_scale: float, v_scale: float, kid
     o = np.empty((batch, H_q, d_h), dtype=np.float64)
     lse = np.empty((batch, H_q), dtype=np.float64)
     M = np.empty((batch, H_kv, Bmax), dtype=np.float64) if want_scores else None
+    given = None
+    if block_idx is not None:
+        given = np.ascontiguousarray(np.asarray(block_idx.cpu() if hasattr(block_idx, "cpu") else block_idx,
+                                                dtype=np.int32))
+        assert given.shape == (batch, H_kv, k)
     _load().msa_oracle_decode_paged(_ptr(qq), _ptr(qi), _ptr(kp), _ptr(vp), float(k_scale), float(v_scale),
                                     _ptr(kip), _ptr(bt), bt.shape[1], _ptr(lens), batch, H_q, H_kv, d_h, d_idx, B_k,
-                                    k, float(scale), _ptr(bi), _ptr(o), _ptr(lse), None if M is None else _ptr(M),
-                                    Bmax)
+                                    k, float(scale), None if given is None else _ptr(given), _ptr(bi), _ptr(o),
+                                    _ptr(lse), None if M is None else _ptr(M), Bmax)
     if want_scores:
         return bi, o, lse, M
     return bi, o, lse

@@ -363,7 +363,8 @@ void msa_oracle_decode_paged(const uint16_t* q, const uint16_t* q_idx, const uin
                              const uint16_t* kidx_pages, const int32_t* block_table,
                              int64_t max_blocks, const int64_t* seqlens, int batch, int H_q,
                              int H_kv, int d_h, int d_idx, int B_k, int kk, double scale,
-                             int32_t* block_idx, double* o, double* lse, double* M, int64_t Bmax) {
+                             const int32_t* block_idx_in, int32_t* block_idx, double* o, double* lse,
+                             double* M, int64_t Bmax) {
   int G = H_q / H_kv;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int s = 0; s < batch; ++s) {
@@ -387,10 +388,13 @@ void msa_oracle_decode_paged(const uint16_t* q, const uint16_t* q_idx, const uin
         for (int64_t b = 0; b < Bmax; ++b) Mo[b] = b < B ? Mrow[b] : -INFINITY;
       }
       int32_t* sel = block_idx + ((int64_t)s * H_kv + r) * kk;
-      topk_row(Mrow, i, B_k, kk, sel, chosen);
+      if (block_idx_in) /* attention on a given selection */
+        memcpy(sel, block_idx_in + ((int64_t)s * H_kv + r) * kk, sizeof(int32_t) * kk);
+      else
+        topk_row(Mrow, i, B_k, kk, sel, chosen);
       memset(chosen, 0, (size_t)B);
       for (int t = 0; t < kk; ++t)
-        if (sel[t] >= 0) chosen[sel[t]] = 1;
+        if (sel[t] >= 0 && sel[t] < B) chosen[sel[t]] = 1;
       /* Eq. 8 with K = k_scale * code, V = v_scale * code, read through the pages */
       for (int g = 0; g < G; ++g) {
         int h = r * G + g;

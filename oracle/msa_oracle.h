@@ -111,14 +111,17 @@ double msa_oracle_fp8_e4m3(uint8_t x);
  * j % B_k of page block_table[s][j / B_k] (block_table: [batch][max_blocks]).
  * k_pages, v_pages: [P][B_k][H_kv][d_h] FP8 E4M3 codes with K = k_scale * value,
  * V = v_scale * value; kidx_pages: [P][B_k][d_idx] bf16; seqlens: [batch].  The new
- * token is the last cached one (position L_s - 1).  Outputs as msa_oracle_decode.
+ * token is the last cached one (position L_s - 1).  Outputs as msa_oracle_decode;
+ * with block_idx_in (not NULL) that selection is used (and copied to block_idx)
+ * instead of the Top-k.
  */
 void msa_oracle_decode_paged(const uint16_t* q, const uint16_t* q_idx, const uint8_t* k_pages,
                              const uint8_t* v_pages, double k_scale, double v_scale,
                              const uint16_t* kidx_pages, const int32_t* block_table,
                              int64_t max_blocks, const int64_t* seqlens, int batch, int H_q,
                              int H_kv, int d_h, int d_idx, int B_k, int kk, double scale,
-                             int32_t* block_idx, double* o, double* lse, double* M, int64_t Bmax);
+                             const int32_t* block_idx_in, int32_t* block_idx, double* o, double* lse,
+                             double* M, int64_t Bmax);
 
 #ifdef __cplusplus
 }

@@ -322,19 +322,28 @@ def quantize_fp8(x: torch.Tensor):
 
 
 def make_decode_paged(cfg: DecodeConfig, mode: str = "literal", device="cpu", lengths=None,
-                      spare_pages: int = 3) -> PagedDecodeInputs:
+                      spare_pages: int = 3, unit_scale: bool = False) -> PagedDecodeInputs:
     """The decode inputs of ``make_decode`` moved into a paged cache: K/V quantised to
     FP8 E4M3 with per-tensor scales, index keys kept bf16, pages of B_k tokens placed
-    in a seeded random order (plus a few unused pages)."""
+    in a seeded random order (plus a few unused pages).  ``unit_scale``: the
+    contiguous K/V are first rounded to FP8 values themselves and the scales are 1,
+    so that both caches hold the same numbers."""
     d = make_decode(cfg, mode, device="cpu", lengths=lengths)
+    if unit_scale:
+        for t in (d.k_cache, d.v_cache):
+            t.copy_(t.float().to(torch.float8_e4m3fn).float().to(torch.bfloat16))
     B_k = cfg.B_k
     nblk = [(L + B_k - 1) // B_k for L in d.lengths]
     P = sum(nblk) + spare_pages
     perm = torch.randperm(P, generator=_gen(cfg.seed, T_PAGE, "cpu"))
     max_blocks = max(nblk) if nblk else 1
     table = torch.full((len(d.lengths), max_blocks), -1, dtype=torch.int32)
-    kq, k_scale = quantize_fp8(d.k_cache)
-    vq, v_scale = quantize_fp8(d.v_cache)
+    if unit_scale:
+        kq, k_scale = d.k_cache.float().to(torch.float8_e4m3fn).view(torch.uint8), 1.0
+        vq, v_scale = d.v_cache.float().to(torch.float8_e4m3fn).view(torch.uint8), 1.0
+    else:
+        kq, k_scale = quantize_fp8(d.k_cache)
+        vq, v_scale = quantize_fp8(d.v_cache)
     k_pages = torch.zeros((P, B_k, cfg.H_kv, cfg.d_h), dtype=torch.uint8)
     v_pages = torch.zeros_like(k_pages)
     kidx_pages = torch.zeros((P, B_k, cfg.d_idx), dtype=torch.bfloat16)

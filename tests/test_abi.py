@@ -196,3 +196,22 @@ def test_sparse_kl_rejects_bad_arguments(lib):
     # partials are 32 bytes per (query, group, slot): far below the attention's rows
     full_kl = raw.msa_sparse_kl_fwd_workspace(131072, 64, 8, 128, 64, 128, 16)
     assert 0 < full_kl < raw.msa_sparse_attn_fwd_workspace(131072, 64, 8, 128, 128, 16) // 8
+
+
+def test_decode_paged_rejects_bad_arguments(lib):
+    raw = lib.raw()
+    f = 0x10000
+
+    def call(batch=4, max_len=1024, H_q=16, H_kv=2, k=4, ks=0.01, vs=0.01, max_blocks=8, bt=f, lens=f,
+             ws=f, ws_bytes=1 << 40):
+        return raw.msa_decode_paged(f, f, f, f, ks, vs, f, bt, max_blocks, lens, batch, max_len, H_q, H_kv, 128, 64,
+                                    128, k, 0.088, f, f, f, ws, ws_bytes, None)
+
+    assert call(ks=0.0) == lib.MSA_ERR_INVALID_ARG
+    assert call(vs=float("inf")) == lib.MSA_ERR_INVALID_ARG
+    assert call(max_blocks=7) == lib.MSA_ERR_INVALID_ARG  # ceil(1024 / 128) = 8 blocks per row needed
+    assert call(bt=None) == lib.MSA_ERR_INVALID_ARG
+    assert call(lens=f + 4) == lib.MSA_ERR_INVALID_ARG
+    assert call(H_q=64, H_kv=2) == lib.MSA_ERR_UNSUPPORTED
+    assert call(ws_bytes=16) == lib.MSA_ERR_WORKSPACE
+    assert call(batch=0) == lib.MSA_OK
