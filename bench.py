@@ -329,7 +329,7 @@ def run_kl(msa, inp, cfg, block_idx, lse, slot_pairs, lists, pairs, steps):
     return out
 
 
-def run_decode(msa, synth, dcfg, mode, steps, warmup):
+def run_decode(msa, synth, dcfg, mode, steps, warmup, paged=False):
     import torch
     dev = "cuda"
     B_k = dcfg.B_k
@@ -362,13 +362,58 @@ def run_decode(msa, synth, dcfg, mode, steps, warmup):
     chosen = int((dbi >= 0).sum().item())
     dbytes = T * dcfg.d_idx * 2 + chosen * B_k * dcfg.d_h * 2 * 2
     del d
-    return {
+    out = {
         "workload": f"decode batch={dcfg.batch} L={min(synth.decode_lengths(dcfg))}..{max_len} H_q={dcfg.H_q} "
                     f"H_kv={dcfg.H_kv} k={dcfg.k}",
         "ms_per_step": round(dms, 4), "tokens_per_s": round(dcfg.batch / (dms / 1e3), 1),
         "algorithmic_bytes": dbytes, "GB_s": round(dbytes / (dms / 1e3) / 1e9, 1),
         "hbm_peak_frac": round(dbytes / (dms / 1e3) / 1e9 / PEAK_HBM_GBS, 4), "steps": steps,
     }
+    if paged:
+        torch.cuda.empty_cache()
+        out["paged_fp8"] = run_decode_paged(msa, synth, dcfg, mode, steps, warmup)
+    return out
+
+
+def run_decode_paged(msa, synth, dcfg, mode, steps, warmup):
+    """The same decode over a paged cache with FP8 E4M3 K/V (bf16 index keys)."""
+    import torch
+    dev = "cuda"
+    B_k = dcfg.B_k
+    log(f"generating {dcfg.name} ({mode}) paged FP8 decode inputs")
+    p = synth.make_decode_paged(dcfg, mode, device=dev)
+    del p.contiguous.k_cache, p.contiguous.v_cache
+    torch.cuda.empty_cache()
+    max_len = max(p.lengths)
+    dbi = torch.empty((dcfg.batch, dcfg.H_kv, dcfg.k), dtype=torch.int32, device=dev)
+    do = torch.empty((dcfg.batch, dcfg.H_q, dcfg.d_h), dtype=torch.float32, device=dev)
+    dl = torch.empty((dcfg.batch, dcfg.H_q), dtype=torch.float32, device=dev)
+    dws = torch.empty(msa.msa_decode_workspace(dcfg.batch, dcfg.H_q, dcfg.H_kv, dcfg.k, max_len),
+                      dtype=torch.uint8, device=dev)
+
+    def step():
+        msa.msa_decode_paged(p.q, p.q_idx, p.k_pages, p.v_pages, p.k_scale, p.v_scale, p.kidx_pages, p.block_table,
+                             p.seqlens, max_len, dcfg.k, block_idx=dbi, o=do, lse=dl, workspace=dws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dms = e0.elapsed_time(e1) / steps
+    T = sum(p.lengths)
+    chosen = int((dbi >= 0).sum().item())
+    # every cached index key (bf16) + the FP8 K and V rows of the chosen blocks
+    dbytes = T * dcfg.d_idx * 2 + chosen * B_k * dcfg.d_h * 1 * 2
+    del p
+    return {"ms_per_step": round(dms, 4), "tokens_per_s": round(dcfg.batch / (dms / 1e3), 1),
+            "algorithmic_bytes": dbytes, "GB_s": round(dbytes / (dms / 1e3) / 1e9, 1),
+            "hbm_peak_frac": round(dbytes / (dms / 1e3) / 1e9 / PEAK_HBM_GBS, 4), "steps": steps}
 
 
 def cpu_baseline(inp, cfg, n_rows):
@@ -404,6 +449,7 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-kl", action="store_true", help="skip the separately timed KL alignment pass")
+    ap.add_argument("--no-paged", action="store_true", help="skip the paged FP8 decode measurement")
     ap.add_argument("--single-mode", action="store_true", help="skip the second input mode")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="start with plain copies of known size (for counter runs)")
@@ -472,7 +518,8 @@ def main(argv=None) -> int:
 
     if not args.no_decode:
         dcfg = synth.CONFIGS[args.decode_workload]
-        result["decode"] = run_decode(msa, synth, dcfg, args.mode, max(args.steps, 50), args.warmup)
+        result["decode"] = run_decode(msa, synth, dcfg, args.mode, max(args.steps, 50), args.warmup,
+                                      paged=not args.no_paged)
         torch.cuda.empty_cache()
     if not args.single_mode:
         pre2, inp2 = run_prefill(msa, synth, cfg, other, args.steps, args.warmup)

@@ -328,7 +328,7 @@ def make_decode_paged(cfg: DecodeConfig, mode: str = "literal", device="cpu", le
     in a seeded random order (plus a few unused pages).  ``unit_scale``: the
     contiguous K/V are first rounded to FP8 values themselves and the scales are 1,
     so that both caches hold the same numbers."""
-    d = make_decode(cfg, mode, device="cpu", lengths=lengths)
+    d = make_decode(cfg, mode, device=device, lengths=lengths)
     if unit_scale:
         for t in (d.k_cache, d.v_cache):
             t.copy_(t.float().to(torch.float8_e4m3fn).float().to(torch.bfloat16))
@@ -344,21 +344,28 @@ def make_decode_paged(cfg: DecodeConfig, mode: str = "literal", device="cpu", le
     else:
         kq, k_scale = quantize_fp8(d.k_cache)
         vq, v_scale = quantize_fp8(d.v_cache)
-    k_pages = torch.zeros((P, B_k, cfg.H_kv, cfg.d_h), dtype=torch.uint8)
+    k_pages = torch.zeros((P, B_k, cfg.H_kv, cfg.d_h), dtype=torch.uint8, device=device)
     v_pages = torch.zeros_like(k_pages)
-    kidx_pages = torch.zeros((P, B_k, cfg.d_idx), dtype=torch.bfloat16)
+    kidx_pages = torch.zeros((P, B_k, cfg.d_idx), dtype=torch.bfloat16, device=device)
     cu = d.cu_seqlens.tolist()
     nxt = 0
     for s, L in enumerate(d.lengths):
-        for b in range(nblk[s]):
-            p = int(perm[nxt])
-            nxt += 1
-            table[s, b] = p
-            t0, t1 = cu[s] + b * B_k, min(cu[s] + (b + 1) * B_k, cu[s + 1])
+        ids = perm[nxt:nxt + nblk[s]]
+        nxt += nblk[s]
+        table[s, :nblk[s]] = ids.to(torch.int32)
+        full = L // B_k  # whole pages in one indexed copy, then the partial last page
+        if full:
+            idx = ids[:full].to(device)
+            t0 = cu[s]
+            k_pages[idx] = kq[t0:t0 + full * B_k].view(full, B_k, cfg.H_kv, cfg.d_h)
+            v_pages[idx] = vq[t0:t0 + full * B_k].view(full, B_k, cfg.H_kv, cfg.d_h)
+            kidx_pages[idx] = d.k_idx_cache[t0:t0 + full * B_k].view(full, B_k, cfg.d_idx)
+        if L % B_k:
+            p = int(ids[full])
+            t0, t1 = cu[s] + full * B_k, cu[s + 1]
             k_pages[p, :t1 - t0] = kq[t0:t1]
             v_pages[p, :t1 - t0] = vq[t0:t1]
             kidx_pages[p, :t1 - t0] = d.k_idx_cache[t0:t1]
-    seqlens = torch.tensor(d.lengths, dtype=torch.int64)
-    mv = lambda t: t.to(device)
-    return PagedDecodeInputs(list(d.lengths), mv(seqlens), mv(table), mv(d.q), mv(d.q_idx), mv(k_pages),
-                             mv(v_pages), mv(kidx_pages), k_scale, v_scale, d)
+    seqlens = torch.tensor(d.lengths, dtype=torch.int64, device=device)
+    return PagedDecodeInputs(list(d.lengths), seqlens, table.to(device), d.q, d.q_idx, k_pages, v_pages,
+                             kidx_pages, k_scale, v_scale, d)
