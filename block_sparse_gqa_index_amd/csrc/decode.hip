@@ -28,16 +28,18 @@ constexpr int kScoreBlocksPerWG = 4;  // one block (128 keys) per wave
 
 // Where a sequence's cached tokens live.
 // Packed: sequences back to back (offsets cu), bf16 K/V rows [T][H_kv][d_h].
+// bk: keys per block (64 or 128).
 struct PackedCache {
   const uint16_t* k;
   const uint16_t* v;
   const uint16_t* kidx;
   const int64_t* cu;
+  int bk;
   __device__ int64_t len(int s) const { return cu[s + 1] - cu[s]; }
-  // First index key of block b of sequence s (keys of a block are consecutive rows).
-  __device__ const uint16_t* kidx_block(int s, int64_t b) const { return kidx + (cu[s] + b * kBk) * kDidx; }
+  // First index key of 128-key tile t of sequence s (keys are consecutive rows).
+  __device__ const uint16_t* kidx_tile(int s, int64_t t) const { return kidx + (cu[s] + t * kBk) * kDidx; }
   // Element offset of (block b, key 0, group r) in the K/V rows; rows are H_kv * d_h apart.
-  __device__ int64_t kv_block(int s, int64_t b, int r, int H_kv) const { return ((cu[s] + b * kBk) * H_kv + r) * kDh; }
+  __device__ int64_t kv_block(int s, int64_t b, int r, int H_kv) const { return ((cu[s] + b * bk) * H_kv + r) * kDh; }
 };
 
 // Paged: pages of kBk tokens, token j of sequence s in row j % kBk of page
@@ -50,9 +52,10 @@ struct PagedFp8Cache {
   const int32_t* table;
   int64_t max_blocks;
   const int64_t* lens;
+  static constexpr int bk = kBk;  // a page is one block
   __device__ int64_t len(int s) const { return lens[s]; }
   __device__ int64_t page(int s, int64_t b) const { return table[(int64_t)s * max_blocks + b]; }
-  __device__ const uint16_t* kidx_block(int s, int64_t b) const { return kidx + page(s, b) * kBk * kDidx; }
+  __device__ const uint16_t* kidx_tile(int s, int64_t t) const { return kidx + page(s, t) * kBk * kDidx; }
   __device__ int64_t kv_block(int s, int64_t b, int r, int H_kv) const {
     return (page(s, b) * kBk * H_kv + r) * kDh;
   }
@@ -77,10 +80,11 @@ __global__ __launch_bounds__(256) void dec_score_kernel(const uint16_t* __restri
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int s = blockIdx.x;
   const int64_t L = cache.len(s);
-  const int64_t nb = (L + kBk - 1) / kBk;
+  const int bk = cache.bk;
+  const int64_t nb = (L + kBk - 1) / kBk;  // 128-key tiles of this sequence
   const int64_t b = (int64_t)blockIdx.y * kScoreBlocksPerWG + wave;
-  if (b >= nb || b >= Bmax) return;
-  const uint16_t* __restrict__ kb = cache.kidx_block(s, b);
+  if (b >= nb || b * (kBk / bk) >= Bmax) return;
+  const uint16_t* __restrict__ kb = cache.kidx_tile(s, b);
   const int col = lane & 15, grp = lane >> 4;
   uint4 qop[2];
 #pragma unroll
@@ -102,9 +106,10 @@ __global__ __launch_bounds__(256) void dec_score_kernel(const uint16_t* __restri
   // layout (lane (col, grp) holds row col of a 16-row tile, dims 32ks + 8grp ..
   // +7): row rr of the half at rr*128, chunk c at position c ^ (rr & 7).
   uint8_t* st = kstage[wave];
-  float runmax = -__builtin_inff();
+  float hmax[2];
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
+    float runmax = -__builtin_inff();
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
       const int rr = 8 * jj + (lane >> 3);
@@ -126,10 +131,20 @@ __global__ __launch_bounds__(256) void dec_score_kernel(const uint16_t* __restri
         runmax = fmaxf(runmax, pos < L ? acc[v] : -__builtin_inff());
       }
     }
+    runmax = fmaxf(runmax, __shfl_xor(runmax, 16));
+    hmax[hf] = fmaxf(runmax, __shfl_xor(runmax, 32));
   }
-  runmax = fmaxf(runmax, __shfl_xor(runmax, 16));
-  runmax = fmaxf(runmax, __shfl_xor(runmax, 32));
-  if (lane < 16 && col < H_kv) M[((int64_t)s * H_kv + col) * Bmax + b] = runmax * 0.125f;
+  // A 128-key tile is one block (B_k = 128) or blocks 2b and 2b+1 (B_k = 64).
+  if (lane < 16 && col < H_kv) {
+    float* mrow = M + ((int64_t)s * H_kv + col) * Bmax;
+    if (bk == kBk) {
+      mrow[b] = fmaxf(hmax[0], hmax[1]) * 0.125f;
+    } else {
+      const int64_t nblk = (L + bk - 1) / bk;
+      mrow[2 * b] = hmax[0] * 0.125f;
+      if (2 * b + 1 < nblk && 2 * b + 1 < Bmax) mrow[2 * b + 1] = hmax[1] * 0.125f;
+    }
+  }
 }
 
 // Top-k of one (sequence, group) row per workgroup: wave w offers blocks
@@ -149,7 +164,7 @@ __global__ __launch_bounds__(256) void dec_topk_kernel(const float* __restrict__
     for (int t = threadIdx.x; t < k; t += 256) out[t] = -1;
     return;
   }
-  int64_t bl = (L - 1) / kBk;
+  int64_t bl = (L - 1) / cache.bk;
   if (bl > Bmax - 1) bl = Bmax - 1;
   TopList<LIST> list;
   list.init();
@@ -247,7 +262,8 @@ __global__ __launch_bounds__(256, 2) void dec_attn_kernel(const uint16_t* __rest
   const int32_t* sel = block_idx + sr * kk;
   const int t0 = part * kDecSlotsPerPart;
   const int t1 = (t0 + kDecSlotsPerPart < kk) ? t0 + kDecSlotsPerPart : kk;
-  const int64_t bl = L > 0 ? (L - 1) / kBk : -1;
+  const int bk = cache.bk;
+  const int64_t bl = L > 0 ? (L - 1) / bk : -1;
   // Next selected, valid slot at or after t (t1 if none); uniform.
   auto next_valid = [&](int t) {
     while (t < t1 && !(sel[t] >= 0 && sel[t] <= bl)) ++t;
@@ -273,8 +289,8 @@ __global__ __launch_bounds__(256, 2) void dec_attn_kernel(const uint16_t* __rest
       return nt ? ld16<true>(p) : ld16<false>(p);
   };
   auto load_block = [&](int b) {
-    const int64_t kb0 = (int64_t)b * kBk;
-    const int nvalid = (L - kb0 < kBk) ? (int)(L - kb0) : kBk;
+    const int64_t kb0 = (int64_t)b * bk;
+    const int nvalid = (L - kb0 < bk) ? (int)(L - kb0) : bk;
     const int64_t base = cache.kv_block(s, b, r, H_kv);
     const int c = tid & 15;
 #pragma unroll
@@ -342,8 +358,8 @@ __global__ __launch_bounds__(256, 2) void dec_attn_kernel(const uint16_t* __rest
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x16_t{};
   while (true) {
-    const int64_t kb0 = (int64_t)b * kBk;
-    const int nvalid = (L - kb0 < kBk) ? (int)(L - kb0) : kBk;
+    const int64_t kb0 = (int64_t)b * bk;
+    const int nvalid = (L - kb0 < bk) ? (int)(L - kb0) : bk;
     const int tn = next_valid(t + 1);
     const int bn = tn < t1 ? sel[tn] : b;
     __syncthreads();  // this block's K and V^T staged
@@ -525,7 +541,8 @@ static hipError_t launch_decode_impl(const uint16_t* q, const uint16_t* q_idx, c
   float* opart = reinterpret_cast<float*>(ws + L.opart);
   float* lpart = reinterpret_cast<float*>(ws + L.lpart);
   hipError_t e;
-  dec_score_kernel<Cache><<<dim3((unsigned)batch, (unsigned)((Bmax + kScoreBlocksPerWG - 1) / kScoreBlocksPerWG)),
+  const int64_t tiles = (Bmax * cache.bk + kBk - 1) / kBk;  // 128-key tiles of the longest sequence
+  dec_score_kernel<Cache><<<dim3((unsigned)batch, (unsigned)((tiles + kScoreBlocksPerWG - 1) / kScoreBlocksPerWG)),
                             dim3(256), 0, stream>>>(q_idx, cache, H_kv, Bmax, M);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const unsigned rows_grid = (unsigned)((int64_t)batch * H_kv);
@@ -562,9 +579,9 @@ static hipError_t launch_decode_impl(const uint16_t* q, const uint16_t* q_idx, c
 
 hipError_t launch_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_t* k_cache,
                          const uint16_t* v_cache, const uint16_t* k_idx_cache, const int64_t* cu, int batch,
-                         int64_t Bmax, int H_q, int H_kv, int kk, float scale, int32_t* block_idx, float* o,
+                         int64_t Bmax, int bk, int H_q, int H_kv, int kk, float scale, int32_t* block_idx, float* o,
                          float* lse, uint8_t* ws, const DecodeWorkspace& L, hipStream_t stream) {
-  const PackedCache cache{k_cache, v_cache, k_idx_cache, cu};
+  const PackedCache cache{k_cache, v_cache, k_idx_cache, cu, bk};
   return launch_decode_impl(q, q_idx, cache, batch, Bmax, H_q, H_kv, kk, scale * kLog2e, 1.f, block_idx, o, lse, ws,
                             L, stream);
 }

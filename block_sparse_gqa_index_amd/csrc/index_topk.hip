@@ -8,9 +8,9 @@
 //
 // Layout of the work: the (query, group) pairs are flattened into "columns"
 // c = i * H_kv + r (the natural row order of q_idx and block_idx).  A workgroup
-// owns a run of consecutive columns and sweeps the key blocks 0..b_last in order.
-// Each key block (128 keys x 64 dims, 16 KB) is staged once in LDS and shared by
-// every wave.  A wave computes S^T = K_block * Q^T with 32x32x16 bf16 MFMAs, so
+// owns a run of consecutive columns and sweeps the 128-key tiles 0..b_last in
+// order; a tile is one block (B_k = 128) or two (B_k = 64).  Each tile (128 keys x
+// 64 dims, 16 KB) is staged once in LDS and shared by every wave.  A wave computes S^T = K_block * Q^T with 32x32x16 bf16 MFMAs, so
 // each lane owns one column and holds 16 of the 32 keys of a tile: the max-pool is
 // a per-lane running max plus one swap between the two lane halves.  The block
 // score then goes straight into a per-lane Top-L register list (Top-k fused) or,
@@ -69,12 +69,18 @@ __device__ __forceinline__ void idx_tile_reduce(const f32x16_t& acc, int64_t qi,
   }
 }
 
-template <int CT>
+// NS blocks per staged tile (1 for B_k = 128, 2 for B_k = 64): 32-key MFMA tile kt
+// belongs to block kt / (4 / NS) of the staged tile.
+template <int CT, int NS>
 __device__ __forceinline__ void idx_block_max(const uint8_t* buf, const uint4 (&qop)[CT][4], const int64_t (&qi)[CT],
-                                              int64_t b, bool need_mask, int h, int l32, float (&bmax)[CT]) {
+                                              int64_t b, bool need_mask, int h, int l32, float (&bmax)[CT][NS]) {
   constexpr int kTiles = 4 * CT;
+  constexpr int kPerBlock = 4 / NS;
 #pragma unroll
-  for (int ct = 0; ct < CT; ++ct) bmax[ct] = -__builtin_inff();
+  for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) bmax[ct][u] = -__builtin_inff();
+  }
   u32x4_t a[4];
   f32x16_t acc[2];
 #pragma unroll
@@ -93,33 +99,38 @@ __device__ __forceinline__ void idx_block_max(const uint8_t* buf, const uint4 (&
     for (int ks = 0; ks < 4; ++ks) acc[j & 1] = mfma_32x32x16(as_bf16x8(a[ks]), as_bf16x8(qop[ct][ks]), acc[j & 1]);
     if (j > 0) {
       const int pj = j - 1, pkt = pj / CT, pct = pj % CT;
-      idx_tile_reduce<CT>(acc[pj & 1], qi[pct], b, pkt, need_mask, h, bmax[pct]);
+      idx_tile_reduce<CT>(acc[pj & 1], qi[pct], b, pkt, need_mask, h, bmax[pct][pkt / kPerBlock]);
     }
   }
   {
     constexpr int pj = kTiles - 1, pkt = pj / CT, pct = pj % CT;
-    idx_tile_reduce<CT>(acc[pj & 1], qi[pct], b, pkt, need_mask, h, bmax[pct]);
+    idx_tile_reduce<CT>(acc[pj & 1], qi[pct], b, pkt, need_mask, h, bmax[pct][pkt / kPerBlock]);
   }
 #pragma unroll
-  for (int ct = 0; ct < CT; ++ct) bmax[ct] = fmaxf(bmax[ct], __shfl_xor(bmax[ct], 32));
+  for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) bmax[ct][u] = fmaxf(bmax[ct][u], __shfl_xor(bmax[ct][u], 32));
+  }
 }
 
 // LIST: register list length (>= k-1); CT: 32-column tiles per wave.
 // WRITE_M: emit block scores M[c][b] (scaled) instead of selecting.
 //
-// Selection: key blocks are swept in pairs (b, b+1).  After the pair, both lane
-// halves hold both block maxima of their column; the lower half offers block b to
-// its list and the upper half block b+1 to its own, so one insertion sequence
-// serves two blocks.  The two lists (even / odd blocks) are merged at the end.
+// Selection: staged tiles are swept in pairs (b, b+1).  After the pair, both lane
+// halves hold every block maximum of their column; the lower half offers tile b's
+// blocks to its list and the upper half tile b+1's to its own, so one insertion
+// sequence serves two tiles.  The two lists (blocks of even / odd tiles) are
+// merged at the end.
 // Sequences: with cu == nullptr the call is one sequence of N tokens; otherwise
 // cu[0..batch] (device) are the packed sequence offsets, grid.y is the sequence and
 // grid.x the column tile within it (tiles past the sequence's end exit).  Every
 // position below (queries, blocks, keys) is relative to the sequence start j0;
 // columns and output rows are global.
-template <int LIST, int CT, bool WRITE_M>
+template <int LIST, int CT, bool WRITE_M, int BK>
 __global__ __launch_bounds__(kIdxThreads, 2) void index_topk_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx_all, int64_t N_all, int H_kv,
     int k, int64_t B, int32_t* __restrict__ block_idx, float* __restrict__ M, const int64_t* __restrict__ cu) {
+  constexpr int NS = kBk / BK;  // blocks per staged 128-key tile
   constexpr int kColsPerWave = 32 * CT;
   constexpr int kCols = kIdxWaves * kColsPerWave;
   constexpr int kBlkBytes = kBk * kDidx * 2;
@@ -176,26 +187,30 @@ __global__ __launch_bounds__(kIdxThreads, 2) void index_topk_kernel(
     if (b + 2 <= b_last) idx_load_block(k_idx, N, b + 2, tid, pre[0]);
     if (b + 3 <= b_last) idx_load_block(k_idx, N, b + 3, tid, pre[1]);
 
-    float m0[CT], m1[CT];
-    idx_block_max<CT>(buf0, qop, qi, b, b * kBk + (kBk - 1) > i_min_wave, h, l32, m0);
+    float m0[CT][NS], m1[CT][NS];
+    idx_block_max<CT, NS>(buf0, qop, qi, b, b * kBk + (kBk - 1) > i_min_wave, h, l32, m0);
     if (two) {
-      idx_block_max<CT>(buf1, qop, qi, b + 1, (b + 1) * kBk + (kBk - 1) > i_min_wave, h, l32, m1);
+      idx_block_max<CT, NS>(buf1, qop, qi, b + 1, (b + 1) * kBk + (kBk - 1) > i_min_wave, h, l32, m1);
     } else {
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) m1[ct] = -__builtin_inff();
+      for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+        for (int u = 0; u < NS; ++u) m1[ct][u] = -__builtin_inff();
+      }
     }
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
-      if constexpr (WRITE_M) {
-        if (qi[ct] >= 0) {
-          if (h == 0) M[col[ct] * B + b] = m0[ct] * 0.125f;  // 1/sqrt(64), exact
-          if (h == 1 && two) M[col[ct] * B + b + 1] = m1[ct] * 0.125f;
+#pragma unroll
+      for (int u = 0; u < NS; ++u) {
+        // block (b + h) * NS + u: this lane half's tile
+        const int64_t blk = (b + h) * NS + u;
+        const float x = h ? m1[ct][u] : m0[ct][u];
+        if constexpr (WRITE_M) {
+          if (qi[ct] >= 0 && (h == 0 || two) && blk < B) M[col[ct] * B + blk] = x * 0.125f;  // 1/sqrt(64), exact
+        } else {
+          // Blocks before the local one compete; the local block is forced later.
+          if (blk < qi[ct] / BK) list[ct].offer(x, (int)blk);
         }
-      } else {
-        // Blocks before the local one compete; the local block is forced later.
-        const int64_t blk = b + h;
-        const float x = h ? m1[ct] : m0[ct];
-        if (blk < qi[ct] / kBk) list[ct].offer(x, (int)blk);
       }
     }
   }
@@ -227,7 +242,7 @@ __global__ __launch_bounds__(kIdxThreads, 2) void index_topk_kernel(
       }
       cand[LIST] = 0x7fffffff;
       int32_t out[LIST + 1];
-      write_selection<LIST + 1>(cand, k, (int)(qi[ct] / kBk), out);
+      write_selection<LIST + 1>(cand, k, (int)(qi[ct] / BK), out);
       int32_t* row = block_idx + col[ct] * k;
       const int half = (k + 1) >> 1;
 #pragma unroll
@@ -240,12 +255,12 @@ __global__ __launch_bounds__(kIdxThreads, 2) void index_topk_kernel(
 
 template <int LIST>
 __global__ __launch_bounds__(256) void topk_from_scores_kernel(const float* __restrict__ M, int64_t N,
-                                                                int H_kv, int64_t B, int k,
+                                                                int H_kv, int64_t B, int k, int bk,
                                                                 int32_t* __restrict__ block_idx) {
   const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (c >= N * H_kv) return;
   const int64_t i = c / H_kv;
-  const int64_t bl = i / kBk;
+  const int64_t bl = i / bk;
   TopList<LIST> list;
   list.init();
   const float* row = M + c * B;
@@ -271,32 +286,39 @@ __global__ void fill_f32_kernel(float* __restrict__ p, int64_t n, float val) {
 
 // cu == nullptr: one sequence of N tokens; otherwise `batch` packed sequences with
 // device offsets cu[0..batch] and N = the longest length (grid.x is sized by it).
-hipError_t launch_index_topk(const uint16_t* q_idx, const uint16_t* k_idx, int64_t N, int H_kv, int k,
-                             int32_t* block_idx, const int64_t* cu, int batch, hipStream_t stream) {
+template <int BK>
+static hipError_t launch_index_topk_bk(const uint16_t* q_idx, const uint16_t* k_idx, int64_t N, int H_kv, int k,
+                                       int32_t* block_idx, const int64_t* cu, int batch, hipStream_t stream) {
   const int64_t total = N * H_kv;
   const unsigned gy = cu ? (unsigned)batch : 1u;
   if (k <= 8) {
     constexpr int CT = 2;
     const int64_t grid = (total + kIdxWaves * 32 * CT - 1) / (kIdxWaves * 32 * CT);
-    index_topk_kernel<7, CT, false><<<dim3((unsigned)grid, gy), dim3(kIdxThreads), 0, stream>>>(
+    index_topk_kernel<7, CT, false, BK><<<dim3((unsigned)grid, gy), dim3(kIdxThreads), 0, stream>>>(
         q_idx, k_idx, N, H_kv, k, 0, block_idx, nullptr, cu);
   } else if (k <= 16) {
     constexpr int CT = 2;
     const int64_t grid = (total + kIdxWaves * 32 * CT - 1) / (kIdxWaves * 32 * CT);
-    index_topk_kernel<15, CT, false><<<dim3((unsigned)grid, gy), dim3(kIdxThreads), 0, stream>>>(
+    index_topk_kernel<15, CT, false, BK><<<dim3((unsigned)grid, gy), dim3(kIdxThreads), 0, stream>>>(
         q_idx, k_idx, N, H_kv, k, 0, block_idx, nullptr, cu);
   } else {
     constexpr int CT = 1;
     const int64_t grid = (total + kIdxWaves * 32 * CT - 1) / (kIdxWaves * 32 * CT);
-    index_topk_kernel<31, CT, false><<<dim3((unsigned)grid, gy), dim3(kIdxThreads), 0, stream>>>(
+    index_topk_kernel<31, CT, false, BK><<<dim3((unsigned)grid, gy), dim3(kIdxThreads), 0, stream>>>(
         q_idx, k_idx, N, H_kv, k, 0, block_idx, nullptr, cu);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_index_block_scores(const uint16_t* q_idx, const uint16_t* k_idx, int64_t N, int H_kv,
+hipError_t launch_index_topk(const uint16_t* q_idx, const uint16_t* k_idx, int64_t N, int H_kv, int k,
+                             int32_t* block_idx, const int64_t* cu, int batch, int bk, hipStream_t stream) {
+  if (bk == 64) return launch_index_topk_bk<64>(q_idx, k_idx, N, H_kv, k, block_idx, cu, batch, stream);
+  return launch_index_topk_bk<128>(q_idx, k_idx, N, H_kv, k, block_idx, cu, batch, stream);
+}
+
+hipError_t launch_index_block_scores(const uint16_t* q_idx, const uint16_t* k_idx, int64_t N, int H_kv, int bk,
                                      float* M, hipStream_t stream) {
-  const int64_t B = (N + kBk - 1) / kBk;
+  const int64_t B = (N + bk - 1) / bk;
   const int64_t nM = N * H_kv * B;
   fill_f32_kernel<<<dim3(1024), dim3(256), 0, stream>>>(M, nM, -__builtin_inff());
   hipError_t e = hipGetLastError();
@@ -304,20 +326,24 @@ hipError_t launch_index_block_scores(const uint16_t* q_idx, const uint16_t* k_id
   constexpr int CT = 2;
   const int64_t total = N * H_kv;
   const int64_t grid = (total + kIdxWaves * 32 * CT - 1) / (kIdxWaves * 32 * CT);
-  index_topk_kernel<1, CT, true><<<dim3((unsigned)grid), dim3(kIdxThreads), 0, stream>>>(
-      q_idx, k_idx, N, H_kv, 1, B, nullptr, M, nullptr);
+  if (bk == 64)
+    index_topk_kernel<1, CT, true, 64><<<dim3((unsigned)grid), dim3(kIdxThreads), 0, stream>>>(
+        q_idx, k_idx, N, H_kv, 1, B, nullptr, M, nullptr);
+  else
+    index_topk_kernel<1, CT, true, 128><<<dim3((unsigned)grid), dim3(kIdxThreads), 0, stream>>>(
+        q_idx, k_idx, N, H_kv, 1, B, nullptr, M, nullptr);
   return hipGetLastError();
 }
 
-hipError_t launch_topk_from_scores(const float* M, int64_t N, int H_kv, int64_t B, int k, int32_t* block_idx,
-                                   hipStream_t stream) {
+hipError_t launch_topk_from_scores(const float* M, int64_t N, int H_kv, int64_t B, int k, int bk,
+                                   int32_t* block_idx, hipStream_t stream) {
   const int64_t grid = (N * H_kv + 255) / 256;
   if (k <= 8)
-    topk_from_scores_kernel<7><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(M, N, H_kv, B, k, block_idx);
+    topk_from_scores_kernel<7><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(M, N, H_kv, B, k, bk, block_idx);
   else if (k <= 16)
-    topk_from_scores_kernel<15><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(M, N, H_kv, B, k, block_idx);
+    topk_from_scores_kernel<15><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(M, N, H_kv, B, k, bk, block_idx);
   else
-    topk_from_scores_kernel<31><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(M, N, H_kv, B, k, block_idx);
+    topk_from_scores_kernel<31><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(M, N, H_kv, B, k, bk, block_idx);
   return hipGetLastError();
 }
 

@@ -43,7 +43,7 @@ constexpr size_t kDefaultAttnWorkspace = (size_t)40 << 30;
 msa_status_t check_common(int64_t N, int d, int expect_d, const char* dname, int B_k, int k) {
   if (N < 0) return fail(MSA_ERR_INVALID_ARG, "N must be >= 0 (got %lld)", (long long)N);
   if (d != expect_d) return fail(MSA_ERR_UNSUPPORTED, "%s must be %d (got %d)", dname, expect_d, d);
-  if (B_k != msa::kBlockKeys) return fail(MSA_ERR_UNSUPPORTED, "B_k must be 128 (got %d)", B_k);
+  if (B_k != 64 && B_k != 128) return fail(MSA_ERR_UNSUPPORTED, "B_k must be 64 or 128 (got %d)", B_k);
   if (k < 1 || k > 32) return fail(MSA_ERR_UNSUPPORTED, "k must be in [1, 32] (got %d)", k);
   if (N >= kMaxN) return fail(MSA_ERR_UNSUPPORTED, "N must be < 2^24 (got %lld)", (long long)N);
   if ((N + B_k - 1) / B_k > kMaxBlocks) return fail(MSA_ERR_UNSUPPORTED, "too many blocks");
@@ -109,7 +109,7 @@ msa_status_t msa_index_topk(const void* q_idx, const void* k_idx, int64_t N, int
     return fail(MSA_ERR_INVALID_ARG, "misaligned pointer (q_idx/k_idx need 16 B, block_idx 4 B)");
   if (N * H_kv >= ((int64_t)1 << 31)) return fail(MSA_ERR_UNSUPPORTED, "N * H_kv too large");
   hipError_t e = msa::launch_index_topk(static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx),
-                                        N, H_kv, k, block_idx, nullptr, 0, static_cast<hipStream_t>(hip_stream));
+                                        N, H_kv, k, block_idx, nullptr, 0, B_k, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_fail(e, "index_topk launch");
   return ok();
 }
@@ -124,7 +124,7 @@ msa_status_t msa_index_block_scores(const void* q_idx, const void* k_idx, int64_
   if (!aligned(q_idx, 16) || !aligned(k_idx, 16) || !aligned(M, 4))
     return fail(MSA_ERR_INVALID_ARG, "misaligned pointer");
   hipError_t e = msa::launch_index_block_scores(static_cast<const uint16_t*>(q_idx),
-                                                static_cast<const uint16_t*>(k_idx), N, H_kv, M,
+                                                static_cast<const uint16_t*>(k_idx), N, H_kv, B_k, M,
                                                 static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_fail(e, "index_block_scores launch");
   return ok();
@@ -139,7 +139,8 @@ msa_status_t msa_topk_from_scores(const float* M, int64_t N, int H_kv, int64_t B
   if (N == 0) return ok();
   if (!M || !block_idx) return fail(MSA_ERR_INVALID_ARG, "null pointer");
   if (!aligned(M, 4) || !aligned(block_idx, 4)) return fail(MSA_ERR_INVALID_ARG, "misaligned pointer");
-  hipError_t e = msa::launch_topk_from_scores(M, N, H_kv, B, k, block_idx, static_cast<hipStream_t>(hip_stream));
+  hipError_t e =
+      msa::launch_topk_from_scores(M, N, H_kv, B, k, B_k, block_idx, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_fail(e, "topk_from_scores launch");
   return ok();
 }
@@ -159,8 +160,9 @@ static msa_status_t check_attn_shape(int64_t N, int H_q, int H_kv, int d_h, int 
 // null: one sequence).  The workspace holds the sequence tables (S) and then the
 // per-window buffers.
 static msa_status_t attn_run(const void* q, const void* k, const void* v, const int32_t* block_idx, int64_t N,
-                             int64_t B, const msa::SeqInfo& si, const msa::SeqTables& S, int H_q, int H_kv, int k_sel,
-                             float scale, float* o, float* lse, uint8_t* ws, size_t ws_bytes, hipStream_t stream) {
+                             int64_t B, const msa::SeqInfo& si, const msa::SeqTables& S, int B_k, int H_q, int H_kv,
+                             int k_sel, float scale, float* o, float* lse, uint8_t* ws, size_t ws_bytes,
+                             hipStream_t stream) {
   const size_t avail = ws_bytes - S.total;
   const int64_t W = window_for_bytes(N, B, H_q, H_kv, k_sel, avail);
   const msa::AttnWorkspace L = msa::attn_workspace_layout(W, H_q, H_kv, k_sel, B);
@@ -169,7 +171,7 @@ static msa_status_t attn_run(const void* q, const void* k, const void* v, const 
     const int64_t Wn = (N - w0 < W) ? N - w0 : W;
     hipError_t e = msa::launch_sparse_attn_window(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), block_idx,
-        N, B, si, H_q, H_kv, k_sel, scale, w0, Wn, cus, o, lse, ws + S.total, L, stream,
+        N, B, si, B_k, H_q, H_kv, k_sel, scale, w0, Wn, cus, o, lse, ws + S.total, L, stream,
         g_phase_events_on ? g_phase_events : nullptr);
     if (e != hipSuccess) return hip_fail(e, "sparse_attn launch");
   }
@@ -215,28 +217,28 @@ msa_status_t msa_sparse_attn_fwd(const void* q, const void* k, const void* v, co
   if (!ws || ws_bytes < need)
     return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes is below the minimum %zu", ws ? ws_bytes : 0, need);
   if (!aligned(ws, 256)) return fail(MSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  return attn_run(q, k, v, block_idx, N, (N + B_k - 1) / B_k, msa::SeqInfo{}, msa::SeqTables{}, H_q, H_kv, k_sel,
+  return attn_run(q, k, v, block_idx, N, (N + B_k - 1) / B_k, msa::SeqInfo{}, msa::SeqTables{}, B_k, H_q, H_kv, k_sel,
                   scale, o, lse, static_cast<uint8_t*>(ws), ws_bytes, static_cast<hipStream_t>(hip_stream));
 }
 
 // ---------------------------------------------------------------- packed sequences
-static msa_status_t check_varlen(int batch, int64_t T, int64_t max_len) {
+static msa_status_t check_varlen(int batch, int64_t T, int64_t max_len, int B_k) {
   if (batch < 0) return fail(MSA_ERR_INVALID_ARG, "batch must be >= 0");
   if (T < 0 || max_len < 0) return fail(MSA_ERR_INVALID_ARG, "T and max_len must be >= 0");
   if (max_len > T) return fail(MSA_ERR_INVALID_ARG, "max_len must be <= T");
-  if ((T + msa::kBlockKeys - 1) / msa::kBlockKeys + batch > kMaxBlocks)
+  if ((T + B_k - 1) / B_k + batch > kMaxBlocks)
     return fail(MSA_ERR_UNSUPPORTED, "ceil(T / B_k) + batch must be <= %lld", (long long)kMaxBlocks);
   return MSA_OK;
 }
 
-static int64_t varlen_blocks(int64_t T, int batch) { return (T + msa::kBlockKeys - 1) / msa::kBlockKeys + batch; }
+static int64_t varlen_blocks(int64_t T, int batch, int B_k) { return (T + B_k - 1) / B_k + batch; }
 
 msa_status_t msa_index_topk_varlen(const void* q_idx, const void* k_idx, const int64_t* cu_seqlens, int batch,
                                    int64_t T, int64_t max_len, int H_kv, int d_idx, int B_k, int k,
                                    int32_t* block_idx, void* hip_stream) {
   msa_status_t st = check_common(T, d_idx, msa::kIndexDim, "d_idx", B_k, k);
   if (st != MSA_OK) return st;
-  if ((st = check_varlen(batch, T, max_len)) != MSA_OK) return st;
+  if ((st = check_varlen(batch, T, max_len, B_k)) != MSA_OK) return st;
   if (batch > 0 && T > 0 && max_len == 0) return fail(MSA_ERR_INVALID_ARG, "max_len must be >= 1");
   if (H_kv < 1) return fail(MSA_ERR_INVALID_ARG, "H_kv must be >= 1");
   if (batch == 0 || T == 0) return ok();
@@ -246,25 +248,25 @@ msa_status_t msa_index_topk_varlen(const void* q_idx, const void* k_idx, const i
   if (T * H_kv >= ((int64_t)1 << 31)) return fail(MSA_ERR_UNSUPPORTED, "T * H_kv too large");
   if (batch > 65535) return fail(MSA_ERR_UNSUPPORTED, "batch must be <= 65535");
   hipError_t e = msa::launch_index_topk(static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx),
-                                        max_len, H_kv, k, block_idx, cu_seqlens, batch,
+                                        max_len, H_kv, k, block_idx, cu_seqlens, batch, B_k,
                                         static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_fail(e, "index_topk launch");
   return ok();
 }
 
 size_t msa_sparse_attn_fwd_varlen_workspace(int64_t T, int batch, int H_q, int H_kv, int d_h, int B_k, int k) {
-  if (check_attn_shape(T, H_q, H_kv, d_h, B_k, k) != MSA_OK || check_varlen(batch, T, 0) != MSA_OK || T == 0 ||
+  if (check_attn_shape(T, H_q, H_kv, d_h, B_k, k) != MSA_OK || check_varlen(batch, T, 0, B_k) != MSA_OK || T == 0 ||
       batch == 0)
     return 0;
-  const int64_t Bt = varlen_blocks(T, batch);
+  const int64_t Bt = varlen_blocks(T, batch, B_k);
   return attn_workspace_bytes(T, Bt, msa::seq_tables_layout(T, batch, Bt), H_q, H_kv, k, false);
 }
 
 size_t msa_sparse_attn_fwd_varlen_workspace_min(int64_t T, int batch, int H_q, int H_kv, int d_h, int B_k, int k) {
-  if (check_attn_shape(T, H_q, H_kv, d_h, B_k, k) != MSA_OK || check_varlen(batch, T, 0) != MSA_OK || T == 0 ||
+  if (check_attn_shape(T, H_q, H_kv, d_h, B_k, k) != MSA_OK || check_varlen(batch, T, 0, B_k) != MSA_OK || T == 0 ||
       batch == 0)
     return 0;
-  const int64_t Bt = varlen_blocks(T, batch);
+  const int64_t Bt = varlen_blocks(T, batch, B_k);
   return attn_workspace_bytes(T, Bt, msa::seq_tables_layout(T, batch, Bt), H_q, H_kv, k, true);
 }
 
@@ -274,7 +276,7 @@ msa_status_t msa_sparse_attn_fwd_varlen(const void* q, const void* k, const void
                                         size_t ws_bytes, void* hip_stream) {
   msa_status_t st = check_attn_shape(T, H_q, H_kv, d_h, B_k, k_sel);
   if (st != MSA_OK) return st;
-  if ((st = check_varlen(batch, T, 0)) != MSA_OK) return st;
+  if ((st = check_varlen(batch, T, 0, B_k)) != MSA_OK) return st;
   if (!(scale > 0.f) || scale != scale) return fail(MSA_ERR_INVALID_ARG, "scale must be a positive number");
   if (batch == 0 || T == 0) return ok();
   if ((st = check_attn_ptrs(q, k, v, block_idx, o, lse, scale)) != MSA_OK) return st;
@@ -284,18 +286,18 @@ msa_status_t msa_sparse_attn_fwd_varlen(const void* q, const void* k, const void
   if (!ws || ws_bytes < need)
     return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes is below the minimum %zu", ws ? ws_bytes : 0, need);
   if (!aligned(ws, 256)) return fail(MSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  const int64_t Bt = varlen_blocks(T, batch);
+  const int64_t Bt = varlen_blocks(T, batch, B_k);
   const msa::SeqTables S = msa::seq_tables_layout(T, batch, Bt);
   uint8_t* w = static_cast<uint8_t*>(ws);
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  hipError_t e = msa::launch_seq_tables(cu_seqlens, batch, w, S, stream);
+  hipError_t e = msa::launch_seq_tables(cu_seqlens, batch, B_k, w, S, stream);
   if (e != hipSuccess) return hip_fail(e, "sequence tables launch");
   msa::SeqInfo si;
   si.cu = cu_seqlens;
   si.bstart = reinterpret_cast<const int32_t*>(w + S.bstart);
   si.seq_tok = reinterpret_cast<const int32_t*>(w + S.seq_tok);
   si.seq_blk = reinterpret_cast<const int32_t*>(w + S.seq_blk);
-  return attn_run(q, k, v, block_idx, T, Bt, si, S, H_q, H_kv, k_sel, scale, o, lse, w, ws_bytes, stream);
+  return attn_run(q, k, v, block_idx, T, Bt, si, S, B_k, H_q, H_kv, k_sel, scale, o, lse, w, ws_bytes, stream);
 }
 
 // ---------------------------------------------------------------- KL alignment
@@ -313,6 +315,7 @@ static msa_status_t check_kl_shape(int64_t N, int H_q, int H_kv, int d_h, int d_
   if (st != MSA_OK) return st;
   if (d_idx != msa::kIndexDim) return fail(MSA_ERR_UNSUPPORTED, "d_idx must be %d (got %d)", msa::kIndexDim, d_idx);
   if (H_q / H_kv > 32) return fail(MSA_ERR_UNSUPPORTED, "G = H_q / H_kv must be <= 32 for the KL pass");
+  if (B_k != msa::kBlockKeys) return fail(MSA_ERR_UNSUPPORTED, "the KL pass supports B_k = 128");
   return MSA_OK;
 }
 
@@ -419,8 +422,8 @@ msa_status_t msa_decode(const void* q, const void* q_idx, const void* k_cache, c
   const msa::DecodeWorkspace L = msa::decode_workspace_layout(batch, H_q, H_kv, k, Bmax);
   hipError_t e = msa::launch_decode(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_cache),
-      static_cast<const uint16_t*>(v_cache), static_cast<const uint16_t*>(k_idx_cache), cu_seqlens, batch, Bmax, H_q,
-      H_kv, k, scale, block_idx, o, lse, static_cast<uint8_t*>(ws), L, static_cast<hipStream_t>(hip_stream));
+      static_cast<const uint16_t*>(v_cache), static_cast<const uint16_t*>(k_idx_cache), cu_seqlens, batch, Bmax, B_k,
+      H_q, H_kv, k, scale, block_idx, o, lse, static_cast<uint8_t*>(ws), L, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return ok();
 }
@@ -432,6 +435,7 @@ msa_status_t msa_decode_paged(const void* q, const void* q_idx, const void* k_pa
                               float* o, float* lse, void* ws, size_t ws_bytes, void* hip_stream) {
   msa_status_t st = check_decode_shape(batch, max_len, H_q, H_kv, d_h, d_idx, B_k, k);
   if (st != MSA_OK) return st;
+  if (B_k != msa::kBlockKeys) return fail(MSA_ERR_UNSUPPORTED, "paged decode uses pages of B_k = 128 tokens");
   if (!(scale > 0.f) || scale != scale) return fail(MSA_ERR_INVALID_ARG, "scale must be a positive number");
   if (!(k_scale > 0.f) || !(v_scale > 0.f) || k_scale != k_scale || v_scale != v_scale ||
       k_scale == __builtin_inff() || v_scale == __builtin_inff())

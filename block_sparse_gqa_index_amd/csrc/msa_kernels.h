@@ -30,12 +30,13 @@ struct DecodeWorkspace {
   size_t M, opart, lpart, total;
 };
 
+// bk: keys per block, 64 or 128.
 hipError_t launch_index_topk(const uint16_t* q_idx, const uint16_t* k_idx, int64_t N, int H_kv, int k,
-                             int32_t* block_idx, const int64_t* cu, int batch, hipStream_t stream);
-hipError_t launch_index_block_scores(const uint16_t* q_idx, const uint16_t* k_idx, int64_t N, int H_kv,
+                             int32_t* block_idx, const int64_t* cu, int batch, int bk, hipStream_t stream);
+hipError_t launch_index_block_scores(const uint16_t* q_idx, const uint16_t* k_idx, int64_t N, int H_kv, int bk,
                                      float* M, hipStream_t stream);
-hipError_t launch_topk_from_scores(const float* M, int64_t N, int H_kv, int64_t B, int k, int32_t* block_idx,
-                                   hipStream_t stream);
+hipError_t launch_topk_from_scores(const float* M, int64_t N, int H_kv, int64_t B, int k, int bk,
+                                   int32_t* block_idx, hipStream_t stream);
 
 // Packed sequences of a varlen call: cu == nullptr means one sequence [0, N).
 // bstart[s] is the first global block of sequence s (blocks of all sequences are
@@ -53,17 +54,19 @@ struct SeqTables {
 // Workspace bytes of the tables for T tokens in `batch` sequences with at most Bt
 // global blocks (0 for a single sequence).
 SeqTables seq_tables_layout(int64_t T, int batch, int64_t Bt);
-hipError_t launch_seq_tables(const int64_t* cu, int batch, uint8_t* ws, const SeqTables& S, hipStream_t stream);
+hipError_t launch_seq_tables(const int64_t* cu, int batch, int bk, uint8_t* ws, const SeqTables& S,
+                             hipStream_t stream);
 
 // B: the list stride in blocks (the block count, or for several sequences an upper
 // bound of the global block count).
 // kl_parts: partials of the KL pass (kKlPart floats per pair) instead of the
 // attention's partial rows.
 AttnWorkspace attn_workspace_layout(int64_t W, int H_q, int H_kv, int kk, int64_t B, bool kl_parts = false);
+// bk: keys per block, 64 or 128.
 hipError_t launch_sparse_attn_window(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                     const int32_t* block_idx, int64_t N, int64_t B, const SeqInfo& si, int H_q,
-                                     int H_kv, int kk, float scale, int64_t w0, int64_t W, int num_cus, float* o,
-                                     float* lse, uint8_t* ws, const AttnWorkspace& L, hipStream_t stream,
+                                     const int32_t* block_idx, int64_t N, int64_t B, const SeqInfo& si, int bk,
+                                     int H_q, int H_kv, int kk, float scale, int64_t w0, int64_t W, int num_cus,
+                                     float* o, float* lse, uint8_t* ws, const AttnWorkspace& L, hipStream_t stream,
                                      const hipEvent_t* events);  // 4 phase events or null
 
 // KL alignment pass over one query window (single sequence of N tokens): per
@@ -80,7 +83,7 @@ hipError_t launch_kl_loss(const float* kl, int64_t n, double* partial, float* lo
 DecodeWorkspace decode_workspace_layout(int batch, int H_q, int H_kv, int kk, int64_t Bmax);
 hipError_t launch_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_t* k_cache,
                          const uint16_t* v_cache, const uint16_t* k_idx_cache, const int64_t* cu, int batch,
-                         int64_t Bmax, int H_q, int H_kv, int kk, float scale, int32_t* block_idx, float* o,
+                         int64_t Bmax, int bk, int H_q, int H_kv, int kk, float scale, int32_t* block_idx, float* o,
                          float* lse, uint8_t* ws, const DecodeWorkspace& L, hipStream_t stream);
 // Paged caches: FP8 E4M3 K/V pages and bf16 index-key pages of kBlockKeys tokens.
 hipError_t launch_decode_paged(const uint16_t* q, const uint16_t* q_idx, const uint8_t* k_pages,

@@ -25,9 +25,11 @@ namespace msa {
 namespace {
 
 // --------------------------------------------------------------------- inverse index
-// Pair validity for a query at position i_rel of its sequence: 0 <= b <= b_loc.
-// Later blocks add no token.
-__device__ __forceinline__ bool pair_valid(int b, int64_t i_rel) { return b >= 0 && (int64_t)b <= i_rel / kBk; }
+// Pair validity for a query at position i_rel of its sequence: 0 <= b <= b_loc =
+// i_rel >> bsh (bsh = log2 B_k).  Later blocks add no token.
+__device__ __forceinline__ bool pair_valid(int b, int64_t i_rel, int bsh) {
+  return b >= 0 && (int64_t)b <= (i_rel >> bsh);
+}
 
 // Start of the sequence of global token i (and its index s).
 __device__ __forceinline__ int64_t seq_start(const SeqInfo& si, int64_t i, int& s) {
@@ -47,25 +49,25 @@ __device__ __forceinline__ int64_t gblock(const SeqInfo& si, int s, int b) { ret
 // Blocks are numbered globally (sequence s's block b is gblock(s, b)); the blocks a
 // tile of queries can choose form one range [gb_lo, gb_hi] of global blocks, which
 // the LDS histogram covers.
-__device__ __forceinline__ void tile_block_range(const SeqInfo& si, int64_t q0, int64_t q1, int64_t& gb_lo,
-                                                 int64_t& nh) {
+__device__ __forceinline__ void tile_block_range(const SeqInfo& si, int64_t q0, int64_t q1, int bsh,
+                                                 int64_t& gb_lo, int64_t& nh) {
   int sf, sl;
   (void)seq_start(si, q0, sf);
   const int64_t jl = seq_start(si, q1 - 1, sl);
   gb_lo = si.cu ? si.bstart[sf] : 0;
-  nh = gblock(si, sl, (int)((q1 - 1 - jl) / kBk)) - gb_lo + 1;
+  nh = gblock(si, sl, (int)((q1 - 1 - jl) >> bsh)) - gb_lo + 1;
 }
 
 __global__ __launch_bounds__(256) void inv_count_kernel(const int32_t* __restrict__ block_idx, SeqInfo si,
-                                                        int64_t w0, int64_t W, int H_kv, int kk, int64_t B, int TQ,
-                                                        int64_t WQ, int nW, int32_t* __restrict__ counts) {
+                                                        int bsh, int64_t w0, int64_t W, int H_kv, int kk, int64_t B,
+                                                        int TQ, int64_t WQ, int nW, int32_t* __restrict__ counts) {
   extern __shared__ int32_t hist[];
   const int r = blockIdx.y;
   const int64_t q0 = w0 + (int64_t)blockIdx.x * TQ;
   const int64_t lbase = ((int64_t)r * nW + (q0 - w0) / WQ) * B;
   const int64_t q1 = (q0 + TQ < w0 + W) ? q0 + TQ : w0 + W;
   int64_t gb_lo, nh;
-  tile_block_range(si, q0, q1, gb_lo, nh);
+  tile_block_range(si, q0, q1, bsh, gb_lo, nh);
   for (int64_t b = threadIdx.x; b < nh; b += 256) hist[b] = 0;
   __syncthreads();
   const int64_t npairs = (q1 - q0) * kk;
@@ -75,7 +77,7 @@ __global__ __launch_bounds__(256) void inv_count_kernel(const int32_t* __restric
     int sq;
     const int64_t j0 = seq_start(si, i, sq);
     const int b = block_idx[(i * H_kv + r) * kk + s];
-    if (pair_valid(b, i - j0)) atomicAdd(&hist[gblock(si, sq, b) - gb_lo], 1);
+    if (pair_valid(b, i - j0, bsh)) atomicAdd(&hist[gblock(si, sq, b) - gb_lo], 1);
   }
   __syncthreads();
   for (int64_t b = threadIdx.x; b < nh; b += 256) {
@@ -166,9 +168,9 @@ __global__ __launch_bounds__(kScanTile) void inv_scan_write_kernel(const int32_t
 
 template <int PPT>
 __global__ __launch_bounds__(256) void inv_scatter_kernel(const int32_t* __restrict__ block_idx, SeqInfo si,
-                                                          int64_t w0, int64_t W, int H_kv, int kk, int64_t B,
-                                                          int TQ, int64_t WQ, int nW, int32_t* __restrict__ cursor,
-                                                          int32_t* __restrict__ pairs) {
+                                                          int bsh, int64_t w0, int64_t W, int H_kv, int kk,
+                                                          int64_t B, int TQ, int64_t WQ, int nW,
+                                                          int32_t* __restrict__ cursor, int32_t* __restrict__ pairs) {
   extern __shared__ int32_t sh[];
   int32_t* hist = sh;
   int32_t* base = sh + B;
@@ -177,7 +179,7 @@ __global__ __launch_bounds__(256) void inv_scatter_kernel(const int32_t* __restr
   const int64_t lbase = ((int64_t)r * nW + (q0 - w0) / WQ) * B;
   const int64_t q1 = (q0 + TQ < w0 + W) ? q0 + TQ : w0 + W;
   int64_t gb_lo, nh;
-  tile_block_range(si, q0, q1, gb_lo, nh);
+  tile_block_range(si, q0, q1, bsh, gb_lo, nh);
   for (int64_t b = threadIdx.x; b < nh; b += 256) hist[b] = 0;
   __syncthreads();
   const int64_t npairs = (q1 - q0) * kk;
@@ -193,7 +195,7 @@ __global__ __launch_bounds__(256) void inv_scatter_kernel(const int32_t* __restr
       int sq;
       const int64_t j0 = seq_start(si, i, sq);
       const int b = block_idx[(i * H_kv + r) * kk + s];
-      if (pair_valid(b, i - j0)) {
+      if (pair_valid(b, i - j0, bsh)) {
         slot[u] = (int)(gblock(si, sq, b) - gb_lo);
         rank[u] = atomicAdd(&hist[slot[u]], 1);
       }
@@ -286,13 +288,16 @@ __device__ __forceinline__ void gather_q(u32x4_t (&qraw)[8], int (&prs)[8], cons
   }
 }
 
-template <int G>
+// BK: keys per block.  The staged tiles hold 128 keys; a 64-key block fills the
+// first half, and only its two 32-key MFMA tiles (and PV steps) are computed.
+template <int G, int BK>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
     const int4* __restrict__ items, const int32_t* __restrict__ n_items_ptr, const int32_t* __restrict__ pairs,
     int64_t N, SeqInfo si, int H_kv, int64_t B, int nW, int kk, int64_t w0, float scale_log2,
     uint16_t* __restrict__ Opart, float2* __restrict__ Lpart) {
   constexpr int kQC = 128 / G;         // gathered queries per chunk
+  constexpr int NKT = BK / 32;         // 32-key MFMA tiles per block
   __shared__ __attribute__((aligned(16))) uint8_t Ks[kBk * 256];
   __shared__ __attribute__((aligned(16))) uint8_t Vt[kDh * 256];
   __shared__ __attribute__((aligned(16))) uint8_t Ostage[4][16 * 256];  // per wave: 16 rows
@@ -330,9 +335,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
       // invariant address registers live across the whole kernel.
       int stid = tid;
       asm volatile("" : "+v"(stid));
-      const int64_t tok0 = b * kBk;  // within the sequence
+      const int64_t tok0 = b * BK;  // within the sequence
       const int row_stride = H_kv * kDh;
-      const int nvalid = (seqN - tok0 < kBk) ? (int)(seqN - tok0) : kBk;
+      const int nvalid = (seqN - tok0 < BK) ? (int)(seqN - tok0) : BK;
       const int64_t base = (j0 + tok0) * row_stride + r * kDh;
       stage_kv(kp + base, vp + base, row_stride, nvalid, Ks, Vt, stid);
     }
@@ -384,13 +389,13 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
 
       // S^T[row][qrow] with row -> key swap23(row): k-slot (h, e) of step t is dim
       // 64h + 8t + e in both operands.
-      f32x16_t sacc[4];
+      f32x16_t sacc[NKT];
       // Matrix phases run at raised wave priority, so that the other wave on the
       // SIMD fills the VALU slots with its softmax rather than competing for issue.
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
+      for (int kt = 0; kt < NKT; ++kt) {
         sacc[kt] = f32x16_t{};
         const int row = kt * 32 + l32;
 #pragma unroll
@@ -403,7 +408,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
       // Keep 8 K-operand reads in flight ahead of the MFMAs that consume them.
       __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-      for (int j = 0; j < 24; ++j) {
+      for (int j = 0; j < 8 * NKT - 8; ++j) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
@@ -420,10 +425,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
 
       // Causal mask, only where a lane's block reaches past its query: element v of
       // tile kt is key kt*32 + 16*(v/8) + 4*((v/4)%2) + v%4 + 8h of the block.
-      const int lim = (int)(i - b * kBk) - 8 * h;
-      if (__any(b * kBk + (kBk - 1) > i)) {
+      const int lim = (int)(i - b * BK) - 8 * h;
+      if (__any(b * BK + (BK - 1) > i)) {
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
+        for (int kt = 0; kt < NKT; ++kt) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int off = kt * 32 + 16 * (v >> 3) + 4 * ((v >> 2) & 1) + (v & 3);
@@ -434,7 +439,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
       // Softmax over this block's keys in base 2 with the scale folded into one FMA.
       float mx = -__builtin_inff();
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
+      for (int kt = 0; kt < NKT; ++kt) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kt][v]);
       }
@@ -443,7 +448,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
       const float m2 = empty ? 0.f : mx * scale_log2;
       float l = 0.f;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
+      for (int kt = 0; kt < NKT; ++kt) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kt][v], scale_log2, -m2));
@@ -454,9 +459,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
       l += __shfl_xor(l, 32);
 
       // P in bf16 as the B operand of step u: keys 32*(u/2) + 16*(u%2) + 8h + e.
-      u32x4_t pb[8];
+      u32x4_t pb[2 * NKT];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < 2 * NKT; ++u) {
         const int kt = u >> 1, hf = u & 1;
         pb[u].x = pack_bf16x2(sacc[kt][8 * hf + 0], sacc[kt][8 * hf + 1]);
         pb[u].y = pack_bf16x2(sacc[kt][8 * hf + 2], sacc[kt][8 * hf + 3]);
@@ -485,7 +490,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
       for (int hd = 0; hd < 2; ++hd) {
         f32x16_t oacc[2] = {f32x16_t{}, f32x16_t{}};
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 2 * NKT; ++u) {
           const int kc = 2 * u + h;
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
@@ -497,7 +502,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
         // V^T-operand reads run 8 ahead of their MFMAs.
         __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < 4 * NKT - 8; ++j) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
         }
@@ -570,7 +575,7 @@ template <int G, int KMAX, bool SEQ>
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ Opart,
                                                       const float2* __restrict__ Lpart,
                                                       const int32_t* __restrict__ block_idx, SeqInfo si,
-                                                      int64_t w0, int64_t W, int H_kv, int kk,
+                                                      int bsh, int64_t w0, int64_t W, int H_kv, int kk,
                                                       float* __restrict__ o, float* __restrict__ lse) {
   constexpr int GW = G < 32 ? G : 32;       // heads per wave
   constexpr int LPH = 64 / GW;               // lanes per head
@@ -601,7 +606,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   int first = -1;
 #pragma unroll
   for (int s = 0; s < KMAX; ++s) {
-    valid[s] = s < kk && pair_valid(sel[s < kk ? s : 0], i_rel);
+    valid[s] = s < kk && pair_valid(sel[s < kk ? s : 0], i_rel, bsh);
     if (valid[s] && first < 0) first = s;
   }
   float* orow = o + (i * H_q + r * G + g) * kDh + d0;
@@ -668,12 +673,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 // Tables of a varlen call (one workgroup): bstart[s] = sum over earlier sequences
 // of their block counts ceil(len / B_k), bstart[batch] = the total.
 __global__ __launch_bounds__(kScanTile) void seq_block_starts_kernel(const int64_t* __restrict__ cu, int batch,
-                                                                   int32_t* __restrict__ bstart) {
+                                                                   int bk, int32_t* __restrict__ bstart) {
   __shared__ int64_t lds[16];
   int64_t carry = 0;
   for (int s0 = 0; s0 < batch; s0 += kScanTile) {
     const int s = s0 + threadIdx.x;
-    const int64_t nb = s < batch ? (cu[s + 1] - cu[s] + kBk - 1) / kBk : 0;
+    const int64_t nb = s < batch ? (cu[s + 1] - cu[s] + bk - 1) / bk : 0;
     const int64_t ex = block_excl_scan_1024(nb, lds);
     if (s < batch) bstart[s] = (int32_t)(carry + ex);
     carry += block_sum_1024(nb, lds);
@@ -962,7 +967,7 @@ __global__ __launch_bounds__(256) void kl_combine_kernel(const float* __restrict
   const int32_t* sel = block_idx + (w0 * H_kv + ir) * kk;
   float A = 0.f, C = 0.f, Z = 0.f, M = -__builtin_inff(), L = 0.f;
   for (int s = 0; s < kk; ++s) {
-    if (!pair_valid(sel[s], i)) continue;
+    if (!pair_valid(sel[s], i, 7)) continue;  // B_k = 128
     const float* src = part + (ir * kk + s) * kKlPart;
     const float4 a = *reinterpret_cast<const float4*>(src);
     const float l = src[4];
@@ -1048,9 +1053,10 @@ SeqTables seq_tables_layout(int64_t T, int batch, int64_t Bt) {
   return S;
 }
 
-hipError_t launch_seq_tables(const int64_t* cu, int batch, uint8_t* ws, const SeqTables& S, hipStream_t stream) {
+hipError_t launch_seq_tables(const int64_t* cu, int batch, int bk, uint8_t* ws, const SeqTables& S,
+                             hipStream_t stream) {
   int32_t* bstart = reinterpret_cast<int32_t*>(ws + S.bstart);
-  seq_block_starts_kernel<<<dim3(1), dim3(kScanTile), 0, stream>>>(cu, batch, bstart);
+  seq_block_starts_kernel<<<dim3(1), dim3(kScanTile), 0, stream>>>(cu, batch, bk, bstart);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   seq_fill_kernel<<<dim3((unsigned)batch), dim3(256), 0, stream>>>(cu, bstart, reinterpret_cast<int32_t*>(ws + S.seq_tok),
@@ -1103,8 +1109,8 @@ AttnWorkspace attn_workspace_layout(int64_t W, int H_q, int H_kv, int kk, int64_
 
 // Inverse index of one query window: per-list pair counts, their scan into list
 // offsets and the item table, then the scatter of the (query, slot) pairs.
-static hipError_t launch_inverse_index(const int32_t* block_idx, int64_t B, const SeqInfo& si, int H_kv, int kk,
-                                       int64_t w0, int64_t W, uint8_t* ws, const AttnWorkspace& L,
+static hipError_t launch_inverse_index(const int32_t* block_idx, int64_t B, const SeqInfo& si, int bsh, int H_kv,
+                                       int kk, int64_t w0, int64_t W, uint8_t* ws, const AttnWorkspace& L,
                                        hipStream_t stream) {
   const int64_t lists = (int64_t)H_kv * L.nW * B;
   int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
@@ -1121,8 +1127,8 @@ static hipError_t launch_inverse_index(const int32_t* block_idx, int64_t B, cons
   const int TQ = inv_tile_queries(kk);
   const dim3 igrid((unsigned)((W + TQ - 1) / TQ), (unsigned)H_kv);
   const size_t lds_count = sizeof(int32_t) * B;
-  inv_count_kernel<<<igrid, dim3(256), lds_count, stream>>>(block_idx, si, w0, W, H_kv, kk, B, TQ, L.WQ, L.nW,
-                                                             counts);
+  inv_count_kernel<<<igrid, dim3(256), lds_count, stream>>>(block_idx, si, bsh, w0, W, H_kv, kk, B, TQ, L.WQ,
+                                                             L.nW, counts);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const unsigned tiles = (unsigned)((lists + kScanTile - 1) / kScanTile);
   int64_t* tsum = reinterpret_cast<int64_t*>(ws + L.tsum);
@@ -1131,16 +1137,17 @@ static hipError_t launch_inverse_index(const int32_t* block_idx, int64_t B, cons
   inv_scan_write_kernel<<<dim3(tiles), dim3(kScanTile), 0, stream>>>(counts, lists, L.item_q, tsum, cursor, items,
                                                                     n_items);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  inv_scatter_kernel<16><<<igrid, dim3(256), 2 * lds_count, stream>>>(block_idx, si, w0, W, H_kv, kk, B, TQ,
-                                                                      L.WQ, L.nW, cursor, pairs);
+  inv_scatter_kernel<16><<<igrid, dim3(256), 2 * lds_count, stream>>>(block_idx, si, bsh, w0, W, H_kv, kk, B,
+                                                                      TQ, L.WQ, L.nW, cursor, pairs);
   return hipGetLastError();
 }
 
 hipError_t launch_sparse_attn_window(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                     const int32_t* block_idx, int64_t N, int64_t B, const SeqInfo& si, int H_q,
-                                     int H_kv, int kk, float scale, int64_t w0, int64_t W, int num_cus, float* o,
-                                     float* lse, uint8_t* ws, const AttnWorkspace& L, hipStream_t stream,
+                                     const int32_t* block_idx, int64_t N, int64_t B, const SeqInfo& si, int bk,
+                                     int H_q, int H_kv, int kk, float scale, int64_t w0, int64_t W, int num_cus,
+                                     float* o, float* lse, uint8_t* ws, const AttnWorkspace& L, hipStream_t stream,
                                      const hipEvent_t* events) {
+  const int bsh = bk == 64 ? 6 : 7;
   const int G = H_q / H_kv;
   const int32_t* n_items = reinterpret_cast<const int32_t*>(ws + L.n_items);
   const int4* items = reinterpret_cast<const int4*>(ws + L.items);
@@ -1150,7 +1157,7 @@ hipError_t launch_sparse_attn_window(const uint16_t* q, const uint16_t* k, const
 
   hipError_t e;
   if (events && (e = hipEventRecord(events[0], stream)) != hipSuccess) return e;
-  if ((e = launch_inverse_index(block_idx, B, si, H_kv, kk, w0, W, ws, L, stream)) != hipSuccess) return e;
+  if ((e = launch_inverse_index(block_idx, B, si, bsh, H_kv, kk, w0, W, ws, L, stream)) != hipSuccess) return e;
 
   int64_t grid = (int64_t)num_cus * 2;
   if (grid > L.max_items) grid = L.max_items;
@@ -1160,8 +1167,12 @@ hipError_t launch_sparse_attn_window(const uint16_t* q, const uint16_t* k, const
   switch (G) {
 #define MSA_ATTN_CASE(GG)                                                                            \
   case GG:                                                                                           \
-    attn_kvouter_kernel<GG><<<dim3((unsigned)grid), dim3(kAttnThreads), 0, stream>>>(                \
-        q, k, v, items, n_items, pairs, N, si, H_kv, B, L.nW, kk, w0, scale_log2, opart, lpart);     \
+    if (bk == 64)                                                                                    \
+      attn_kvouter_kernel<GG, 64><<<dim3((unsigned)grid), dim3(kAttnThreads), 0, stream>>>(          \
+          q, k, v, items, n_items, pairs, N, si, H_kv, B, L.nW, kk, w0, scale_log2, opart, lpart);   \
+    else                                                                                             \
+      attn_kvouter_kernel<GG, 128><<<dim3((unsigned)grid), dim3(kAttnThreads), 0, stream>>>(         \
+          q, k, v, items, n_items, pairs, N, si, H_kv, B, L.nW, kk, w0, scale_log2, opart, lpart);   \
     break;
     MSA_ATTN_CASE(1)
     MSA_ATTN_CASE(2)
@@ -1184,16 +1195,16 @@ hipError_t launch_sparse_attn_window(const uint16_t* q, const uint16_t* k, const
 #define MSA_COMBINE_CASE(GG)                                                                          \
   case GG:                                                                                           \
     if (kk <= 16 && !si.cu)                                                                          \
-      combine_kernel<GG, 16, false><<<cgrid, dim3(256), 0, stream>>>(opart, lpart, block_idx, si, w0, W, H_kv, kk, o, \
+      combine_kernel<GG, 16, false><<<cgrid, dim3(256), 0, stream>>>(opart, lpart, block_idx, si, bsh, w0, W, H_kv, kk, o, \
                                                                      lse);                           \
     else if (kk <= 16)                                                                               \
-      combine_kernel<GG, 16, true><<<cgrid, dim3(256), 0, stream>>>(opart, lpart, block_idx, si, w0, W, H_kv, kk, o, \
+      combine_kernel<GG, 16, true><<<cgrid, dim3(256), 0, stream>>>(opart, lpart, block_idx, si, bsh, w0, W, H_kv, kk, o, \
                                                                     lse);                            \
     else if (!si.cu)                                                                                 \
-      combine_kernel<GG, 32, false><<<cgrid, dim3(256), 0, stream>>>(opart, lpart, block_idx, si, w0, W, H_kv, kk, o, \
+      combine_kernel<GG, 32, false><<<cgrid, dim3(256), 0, stream>>>(opart, lpart, block_idx, si, bsh, w0, W, H_kv, kk, o, \
                                                                      lse);                           \
     else                                                                                             \
-      combine_kernel<GG, 32, true><<<cgrid, dim3(256), 0, stream>>>(opart, lpart, block_idx, si, w0, W, H_kv, kk, o, \
+      combine_kernel<GG, 32, true><<<cgrid, dim3(256), 0, stream>>>(opart, lpart, block_idx, si, bsh, w0, W, H_kv, kk, o, \
                                                                     lse);                            \
     break;
     MSA_COMBINE_CASE(1)
@@ -1219,7 +1230,7 @@ hipError_t launch_sparse_kl_window(const uint16_t* q, const uint16_t* k, const u
                                    int num_cus, float* kl, float* lse_idx, uint8_t* ws, const AttnWorkspace& L,
                                    hipStream_t stream) {
   const int G = H_q / H_kv;
-  hipError_t e = launch_inverse_index(block_idx, B, SeqInfo{}, H_kv, kk, w0, W, ws, L, stream);
+  hipError_t e = launch_inverse_index(block_idx, B, SeqInfo{}, 7, H_kv, kk, w0, W, ws, L, stream);
   if (e != hipSuccess) return e;
   const int32_t* n_items = reinterpret_cast<const int32_t*>(ws + L.n_items);
   const int4* items = reinterpret_cast<const int4*>(ws + L.items);

@@ -54,7 +54,9 @@ def test_index_topk_rejects_bad_arguments(lib):
     call = lambda N=4096, H_kv=1, d_idx=64, B_k=128, k=8, q=fake, kk=fake, out=fake: raw.msa_index_topk(
         q, kk, N, H_kv, d_idx, B_k, k, out, None, 0, None)
     assert call(d_idx=32) == lib.MSA_ERR_UNSUPPORTED
-    assert call(B_k=64) == lib.MSA_ERR_UNSUPPORTED
+    assert call(B_k=32) == lib.MSA_ERR_UNSUPPORTED
+    assert call(B_k=256) == lib.MSA_ERR_UNSUPPORTED
+    assert call(N=8192 * 64 + 1, B_k=64) == lib.MSA_ERR_UNSUPPORTED  # more than 8192 blocks
     assert call(k=0) == lib.MSA_ERR_UNSUPPORTED
     assert call(k=33) == lib.MSA_ERR_UNSUPPORTED
     assert call(N=-1) == lib.MSA_ERR_INVALID_ARG
@@ -179,9 +181,12 @@ def test_sparse_kl_rejects_bad_arguments(lib):
     raw = lib.raw()
     f = 0x10000
 
-    def call(N=4096, H_q=8, H_kv=2, d_h=128, d_idx=64, k=8, scale=0.088, ws=f, ws_bytes=1 << 40, lse=f, loss=f):
-        return raw.msa_sparse_kl_fwd(f, f, f, f, f, lse, N, H_q, H_kv, d_h, d_idx, 128, k, scale, f, f, loss, ws,
+    def call(N=4096, H_q=8, H_kv=2, d_h=128, d_idx=64, k=8, scale=0.088, ws=f, ws_bytes=1 << 40, lse=f, loss=f,
+             B_k=128):
+        return raw.msa_sparse_kl_fwd(f, f, f, f, f, lse, N, H_q, H_kv, d_h, d_idx, B_k, k, scale, f, f, loss, ws,
                                      ws_bytes, None)
+
+    assert call(B_k=64) == lib.MSA_ERR_UNSUPPORTED
 
     assert call(d_idx=32) == lib.MSA_ERR_UNSUPPORTED
     assert call(H_q=128, H_kv=2) == lib.MSA_ERR_UNSUPPORTED  # G = 64 > 32
@@ -203,9 +208,11 @@ def test_decode_paged_rejects_bad_arguments(lib):
     f = 0x10000
 
     def call(batch=4, max_len=1024, H_q=16, H_kv=2, k=4, ks=0.01, vs=0.01, max_blocks=8, bt=f, lens=f,
-             ws=f, ws_bytes=1 << 40):
+             ws=f, ws_bytes=1 << 40, B_k=128):
         return raw.msa_decode_paged(f, f, f, f, ks, vs, f, bt, max_blocks, lens, batch, max_len, H_q, H_kv, 128, 64,
-                                    128, k, 0.088, f, f, f, ws, ws_bytes, None)
+                                    B_k, k, 0.088, f, f, f, ws, ws_bytes, None)
+
+    assert call(B_k=64, max_blocks=16) == lib.MSA_ERR_UNSUPPORTED
 
     assert call(ks=0.0) == lib.MSA_ERR_INVALID_ARG
     assert call(vs=float("inf")) == lib.MSA_ERR_INVALID_ARG
