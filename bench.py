@@ -153,7 +153,8 @@ def write_stats_summary(stats_csv: str, log_path: str, command: str) -> str:
     import re
     rows = []
     for r in csv.DictReader(open(stats_csv)):
-        m = re.search(r"msa::\(anonymous namespace\)::([A-Za-z0-9_]+(?:<[^()]*?>)?)\(", r["Name"])
+        name = r["Name"].replace("(anonymous namespace)::", "")
+        m = re.search(r"msa::([A-Za-z0-9_]+(?:<[^()]*?>)?)\(", name)
         if m:
             rows.append((m.group(1), int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
                          float(r["MaxNs"]) / 1e3, float(r["TotalDurationNs"])))

@@ -28,13 +28,15 @@ constexpr int kScoreBlocksPerWG = 4;  // one block (128 keys) per wave
 
 // Where a sequence's cached tokens live.
 // Packed: sequences back to back (offsets cu), bf16 K/V rows [T][H_kv][d_h].
-// bk: keys per block (64 or 128).
+// BK: keys per block (64 or 128), a compile-time constant so that the block
+// arithmetic stays shifts.
+template <int BK>
 struct PackedCache {
   const uint16_t* k;
   const uint16_t* v;
   const uint16_t* kidx;
   const int64_t* cu;
-  int bk;
+  static constexpr int bk = BK;
   __device__ int64_t len(int s) const { return cu[s + 1] - cu[s]; }
   // First index key of 128-key tile t of sequence s (keys are consecutive rows).
   __device__ const uint16_t* kidx_tile(int s, int64_t t) const { return kidx + (cu[s] + t * kBk) * kDidx; }
@@ -581,7 +583,12 @@ hipError_t launch_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_
                          const uint16_t* v_cache, const uint16_t* k_idx_cache, const int64_t* cu, int batch,
                          int64_t Bmax, int bk, int H_q, int H_kv, int kk, float scale, int32_t* block_idx, float* o,
                          float* lse, uint8_t* ws, const DecodeWorkspace& L, hipStream_t stream) {
-  const PackedCache cache{k_cache, v_cache, k_idx_cache, cu, bk};
+  if (bk == 64) {
+    const PackedCache<64> cache{k_cache, v_cache, k_idx_cache, cu};
+    return launch_decode_impl(q, q_idx, cache, batch, Bmax, H_q, H_kv, kk, scale * kLog2e, 1.f, block_idx, o, lse,
+                              ws, L, stream);
+  }
+  const PackedCache<128> cache{k_cache, v_cache, k_idx_cache, cu};
   return launch_decode_impl(q, q_idx, cache, batch, Bmax, H_q, H_kv, kk, scale * kLog2e, 1.f, block_idx, o, lse, ws,
                             L, stream);
 }
