@@ -62,6 +62,7 @@ def _load():
                                       P, P, P, P, i64]
     lib.msa_oracle_decode_attn.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, dbl, P, P, P]
     lib.msa_oracle_sparse_kl.argtypes = [P, P, P, P, P, i64, i32, i32, i32, i32, i32, i32, dbl, P, i64, P, P]
+    lib.msa_oracle_sparse_attn_bwd.argtypes = [P, P, P, P, P, i64, i32, i32, i32, i32, i32, dbl, P, P, P]
     lib.msa_oracle_fp8_e4m3.argtypes = [ctypes.c_uint8]
     lib.msa_oracle_fp8_e4m3.restype = dbl
     lib.msa_oracle_decode_paged.argtypes = [P, P, P, P, dbl, dbl, P, P, i64, P, i32, i32, i32, i32, i32, i32, i32,
@@ -175,6 +176,24 @@ def sparse_kl(q, k, q_idx, k_idx, block_idx, B_k: int, scale: float | None = Non
                                  B_k, bi.shape[2], float(scale), None if r is None else _ptr(r), nrows,
                                  _ptr(kl), _ptr(lse_idx))
     return kl, lse_idx
+
+
+def sparse_attn_bwd(q, k, v, dO, block_idx, B_k: int, scale: float | None = None):
+    """Gradients of Eq. 8 for upstream dO (selection fixed): returns (dq, dk, dv) float64."""
+    qq, kk_, vv, gg = _u16(q), _u16(k), _u16(v), _u16(dO)
+    N, H_q, d_h = qq.shape
+    H_kv = kk_.shape[1]
+    assert gg.shape == qq.shape and vv.shape == kk_.shape
+    bi = np.ascontiguousarray(np.asarray(block_idx), dtype=np.int32)
+    assert bi.shape[:2] == (N, H_kv)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d_h)
+    dq = np.empty((N, H_q, d_h), dtype=np.float64)
+    dk = np.empty((N, H_kv, d_h), dtype=np.float64)
+    dv = np.empty((N, H_kv, d_h), dtype=np.float64)
+    _load().msa_oracle_sparse_attn_bwd(_ptr(qq), _ptr(kk_), _ptr(vv), _ptr(gg), _ptr(bi), N, H_q, H_kv, d_h, B_k,
+                                       bi.shape[2], float(scale), _ptr(dq), _ptr(dk), _ptr(dv))
+    return dq, dk, dv
 
 
 def decode(q, q_idx, k_cache, v_cache, k_idx_cache, cu_seqlens, k: int, B_k: int,

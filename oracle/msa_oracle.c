@@ -9,6 +9,7 @@
  *   Eq. 9-10 KL alignment per row    -> kl_row()
  *   paged FP8 decode: OCP E4M3 codes -> msa_oracle_fp8_e4m3(), pages looked up
  *   per token
+ *   gradients of Eq. 8 (backward)    -> msa_oracle_sparse_attn_bwd()
  * (page "MiniMax Sparse Attention (MSA)" paper review, section 3; page
  * "papers.chlience.com" reading notes, section 5.1 and 5.1.1.)
  * No blocking, fusion or reordering beyond the definitions; OpenMP only
@@ -426,5 +427,88 @@ void msa_oracle_decode_paged(const uint16_t* q, const uint16_t* q_idx, const uin
     free(chosen);
     free(Mrow);
     free(kidx);
+  }
+}
+
+/*
+ * Gradients of Eq. 8 with respect to q, k and v for the upstream gradient dO of o
+ * (the selection is held fixed).  Per query i and head h of group r, over the token
+ * set T of reading 6: P_j = softmax_j(scale <q, k_j>), o = sum_j P_j v_j, and with
+ * D = <dO, o>:  dv_j += P_j dO,  dS_j = P_j (<dO, v_j> - D),
+ * dq += scale sum_j dS_j k_j,  dk_j += scale dS_j q.
+ * Threads split the KV groups, so the key/value gradients of a group have one writer.
+ */
+void msa_oracle_sparse_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                const uint16_t* dO, const int32_t* block_idx, int64_t N, int H_q,
+                                int H_kv, int d_h, int B_k, int kk, double scale, double* dq,
+                                double* dk, double* dv) {
+  int64_t B = msa_oracle_num_blocks(N, B_k);
+  int G = H_q / H_kv;
+  for (int64_t e = 0; e < N * H_q * d_h; ++e) dq[e] = 0.0;
+  for (int64_t e = 0; e < N * H_kv * d_h; ++e) dk[e] = dv[e] = 0.0;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int r = 0; r < H_kv; ++r) {
+    char* inset = (char*)malloc((size_t)B + 1);
+    double* P = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+    double* o = (double*)malloc(sizeof(double) * (size_t)d_h);
+    for (int64_t i = 0; i < N; ++i) {
+      memset(inset, 0, (size_t)B + 1);
+      const int32_t* sel = block_idx + (i * H_kv + r) * kk;
+      for (int t = 0; t < kk; ++t)
+        if (sel[t] >= 0 && sel[t] < B) inset[sel[t]] = 1;
+      for (int g = 0; g < G; ++g) {
+        int h = r * G + g;
+        const uint16_t* qv = q + (i * H_q + h) * d_h;
+        const uint16_t* dov = dO + (i * H_q + h) * d_h;
+        /* forward: softmax over T and o */
+        double m = -INFINITY;
+        int64_t nt = 0;
+        for (int64_t j = 0; j <= i; ++j) {
+          if (!inset[block_of(j, B_k)]) continue;
+          const uint16_t* kr = k + (j * H_kv + r) * d_h;
+          double sv = 0.0;
+          for (int d = 0; d < d_h; ++d) sv += bf16(qv[d]) * bf16(kr[d]);
+          P[j] = sv * scale;
+          if (P[j] > m) m = P[j];
+          ++nt;
+        }
+        if (nt == 0) continue; /* no token: o = 0, no gradient */
+        double l = 0.0;
+        for (int64_t j = 0; j <= i; ++j)
+          if (inset[block_of(j, B_k)]) {
+            P[j] = exp(P[j] - m);
+            l += P[j];
+          }
+        for (int d = 0; d < d_h; ++d) o[d] = 0.0;
+        for (int64_t j = 0; j <= i; ++j) {
+          if (!inset[block_of(j, B_k)]) continue;
+          P[j] /= l;
+          const uint16_t* vr = v + (j * H_kv + r) * d_h;
+          for (int d = 0; d < d_h; ++d) o[d] += P[j] * bf16(vr[d]);
+        }
+        double D = 0.0;
+        for (int d = 0; d < d_h; ++d) D += bf16(dov[d]) * o[d];
+        /* backward */
+        double* dqr = dq + (i * H_q + h) * d_h;
+        for (int64_t j = 0; j <= i; ++j) {
+          if (!inset[block_of(j, B_k)]) continue;
+          const uint16_t* kr = k + (j * H_kv + r) * d_h;
+          const uint16_t* vr = v + (j * H_kv + r) * d_h;
+          double dp = 0.0;
+          for (int d = 0; d < d_h; ++d) dp += bf16(dov[d]) * bf16(vr[d]);
+          double ds = P[j] * (dp - D);
+          double* dkr = dk + (j * H_kv + r) * d_h;
+          double* dvr = dv + (j * H_kv + r) * d_h;
+          for (int d = 0; d < d_h; ++d) {
+            dqr[d] += scale * ds * bf16(kr[d]);
+            dkr[d] += scale * ds * bf16(qv[d]);
+            dvr[d] += P[j] * bf16(dov[d]);
+          }
+        }
+      }
+    }
+    free(o);
+    free(P);
+    free(inset);
   }
 }

@@ -123,6 +123,16 @@ void msa_oracle_decode_paged(const uint16_t* q, const uint16_t* q_idx, const uin
                              const int32_t* block_idx_in, int32_t* block_idx, double* o, double* lse,
                              double* M, int64_t Bmax);
 
+/*
+ * Gradients of Eq. 8 (selection fixed) for the upstream gradient dO [N][H_q][d_h]
+ * (bf16): dq [N][H_q][d_h], dk, dv [N][H_kv][d_h] (double), all rows of the
+ * block_idx [N][H_kv][kk] given.  Rows with no attended token get no gradient.
+ */
+void msa_oracle_sparse_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                const uint16_t* dO, const int32_t* block_idx, int64_t N, int H_q,
+                                int H_kv, int d_h, int B_k, int kk, double scale, double* dq,
+                                double* dk, double* dv);
+
 #ifdef __cplusplus
 }
 #endif

@@ -48,6 +48,10 @@ MUTANTS = [
      "(((int64_t)pages[j / B_k] * B_k + (j + 1) % B_k) * H_kv + r) * d_h;\n          double sv"),
     ("paged_scales_swapped", "sv += bf16(qv[d]) * (k_scale * msa_oracle_fp8_e4m3(kr[d]));",
      "sv += bf16(qv[d]) * (v_scale * msa_oracle_fp8_e4m3(kr[d]));"),
+    ("bwd_no_scale_dq", "dqr[d] += scale * ds * bf16(kr[d]);", "dqr[d] += ds * bf16(kr[d]);"),
+    ("bwd_no_D", "double ds = P[j] * (dp - D);", "double ds = P[j] * dp;"),
+    ("bwd_dv_from_ds", "dvr[d] += P[j] * bf16(dov[d]);", "dvr[d] += ds * bf16(dov[d]);"),
+    ("bwd_dk_wrong_operand", "dkr[d] += scale * ds * bf16(qv[d]);", "dkr[d] += scale * ds * bf16(dov[d]);"),
     ("paged_index_page", "kidx_pages + ((int64_t)pages[j / B_k] * B_k + j % B_k) * d_idx",
      "kidx_pages + ((int64_t)(j / B_k) * B_k + j % B_k) * d_idx"),
 ]
@@ -74,6 +78,8 @@ def _all_pins():
     yield "kl_closed_form", pins.test_kl_closed_form_mean_of_two_heads
     yield "kl_token_set", pins.test_kl_token_set_is_causal_and_selected
     yield "kl_groups", pins.test_kl_is_nonnegative_and_groups_are_separate
+    yield "bwd_autograd", lambda: pins.test_attention_backward_matches_autograd(300, 4, 2, 2, 64)
+    yield "bwd_fd", pins.test_attention_backward_finite_differences
     yield "fp8", pins.test_fp8_e4m3_decoding
     yield "paged", pins.test_paged_fp8_decode_equals_contiguous_decode
     yield "paged_scales", pins.test_paged_fp8_scales_multiply_keys_and_values

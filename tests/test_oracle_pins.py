@@ -491,3 +491,80 @@ def test_paged_fp8_scales_multiply_keys_and_values():
     got = oracle.decode_paged(d.q, d.q_idx, kp, vp, 0.5, 0.25, kip, table, lengths, 3, 128)
     for a, b in zip(got, ref):
         np.testing.assert_array_equal(a, b)
+
+
+# --- Backward of Eq. 8 -----------------------------------------------------------------------
+
+def _masked_attention_autograd(q, k, v, dO, bi, B_k, scale):
+    """Eq. 8 as dense attention with the selection as a mask, differentiated by torch's
+    autograd in fp64 (an independent implementation of the same gradients)."""
+    N, H_q, d_h = q.shape
+    H_kv = k.shape[1]
+    G = H_q // H_kv
+    qd = q.double().clone().requires_grad_(True)
+    kd = k.double().clone().requires_grad_(True)
+    vd = v.double().clone().requires_grad_(True)
+    i = torch.arange(N).view(N, 1)
+    j = torch.arange(N).view(1, N)
+    outs = []
+    for h in range(H_q):
+        r = h // G
+        sel = torch.from_numpy(bi[:, r, :].astype(np.int64))  # [N, kk]
+        chosen = torch.zeros(N, (N + B_k - 1) // B_k + 1, dtype=torch.bool)
+        chosen.scatter_(1, torch.where(sel >= 0, sel, chosen.shape[1] - 1), True)
+        chosen[:, -1] = False
+        mask = chosen[:, (j // B_k).view(-1)].view(N, N) & (j <= i)
+        s = (qd[:, h] @ kd[:, r].T) * scale
+        s = s.masked_fill(~mask, float("-inf"))
+        p = torch.softmax(s, dim=1)
+        p = torch.nan_to_num(p, nan=0.0)
+        outs.append(p @ vd[:, r])
+    o = torch.stack(outs, dim=1)
+    (o * dO.double()).sum().backward()
+    return qd.grad.numpy(), kd.grad.numpy(), vd.grad.numpy()
+
+
+@pytest.mark.parametrize("N,H_q,H_kv,k,B_k", [(300, 4, 2, 2, 64), (260, 2, 1, 3, 128), (129, 4, 4, 1, 32)])
+def test_attention_backward_matches_autograd(N, H_q, H_kv, k, B_k):
+    inp = synth.small_prefill(N=N, H_q=H_q, H_kv=H_kv, k=k, seed=60 + N, B_k=B_k)
+    bi = oracle.topk(oracle.block_scores(inp.q_idx, inp.k_idx, B_k), k, B_k)
+    bi[7] = -1  # a row with no token: no gradient
+    g = torch.Generator().manual_seed(N)
+    dO = torch.randn(N, H_q, 128, generator=g).to(torch.bfloat16)
+    scale = 1.0 / math.sqrt(128)
+    got = oracle.sparse_attn_bwd(inp.q, inp.k, inp.v, dO, bi, B_k)
+    ref = _masked_attention_autograd(inp.q, inp.k, inp.v, dO, bi, B_k, scale)
+    for a, b, name in zip(got, ref, ("dq", "dk", "dv")):
+        np.testing.assert_allclose(a, b, rtol=1e-9, atol=1e-11, err_msg=name)
+
+
+def test_attention_backward_finite_differences():
+    # Directional derivatives of L = <dO, o> (the forward oracle) against the gradients.
+    N, H_q, H_kv, k, B_k = 40, 2, 1, 2, 16
+    inp = synth.small_prefill(N=N, H_q=H_q, H_kv=H_kv, k=k, seed=71, B_k=B_k, d_h=128)
+    bi = oracle.topk(oracle.block_scores(inp.q_idx, inp.k_idx, B_k), k, B_k)
+    g = torch.Generator().manual_seed(5)
+    dO = torch.randn(N, H_q, 128, generator=g).to(torch.bfloat16)
+    dq, dk, dv = oracle.sparse_attn_bwd(inp.q, inp.k, inp.v, dO, bi, B_k)
+    dOd = dO.double().numpy()
+
+    def loss(q, kk, v):
+        o, _ = oracle.sparse_attn(q, kk, v, bi, B_k)
+        return float((o * dOd).sum())
+
+    # Inputs are bf16: perturb along directions of exactly representable steps and
+    # compare with the exact central difference of a quadratic fit (eps small).
+    rng = np.random.default_rng(1)
+    for name, grad in (("q", dq), ("k", dk), ("v", dv)):
+        base = getattr(inp, name).float()
+        direction = torch.from_numpy(rng.choice([-1.0, 1.0], size=tuple(base.shape)).astype(np.float32))
+        eps = 2.0 ** -6
+        args_p = {n: getattr(inp, n) for n in ("q", "k", "v")}
+        args_m = dict(args_p)
+        args_p[name] = (base + eps * direction).to(torch.bfloat16)
+        args_m[name] = (base - eps * direction).to(torch.bfloat16)
+        # the perturbation must be exact in bf16 for the difference to mean anything
+        step = (args_p[name].double() - args_m[name].double()) / 2
+        fd = (loss(args_p["q"], args_p["k"], args_p["v"]) - loss(args_m["q"], args_m["k"], args_m["v"])) / 2
+        lin = float((grad * step.numpy()).sum())
+        assert abs(fd - lin) <= 2e-3 * max(1.0, abs(lin)), (name, fd, lin)
