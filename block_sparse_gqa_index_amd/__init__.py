@@ -46,6 +46,10 @@ _SIGS = {
     "msa_sparse_kl_fwd_workspace_min": ([_I64, _I32, _I32, _I32, _I32, _I32, _I32], _SZ),
     "msa_sparse_kl_fwd": ([_P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _F32, _P, _P, _P, _P, _SZ,
                            _P], _I32),
+    "msa_sparse_attn_bwd_workspace": ([_I64, _I32, _I32, _I32, _I32, _I32], _SZ),
+    "msa_sparse_attn_bwd_workspace_min": ([_I64, _I32, _I32, _I32, _I32, _I32], _SZ),
+    "msa_sparse_attn_bwd": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _F32, _P, _P, _P, _P, _SZ,
+                             _P], _I32),
     "msa_decode_paged": ([_P, _P, _P, _P, _F32, _F32, _P, _P, _I64, _P, _I32, _I64, _I32, _I32, _I32, _I32, _I32, _I32,
                           _F32, _P, _P, _P, _P, _SZ, _P], _I32),
     "msa_index_topk_varlen": ([_P, _P, _P, _I32, _I64, _I64, _I32, _I32, _I32, _I32, _P, _P], _I32),
@@ -177,6 +181,46 @@ def msa_sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block
                                     float(scale), _ptr(o), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
                                     _stream(stream)), "msa_sparse_attn_fwd")
     return o, lse
+
+
+# ----------------------------------------------------------------- Backward
+def msa_sparse_attn_bwd_workspace(N: int, H_q: int, H_kv: int, k: int, d_h: int = 128, B_k: int = 128,
+                                  minimum: bool = False) -> int:
+    fn = _lib.msa_sparse_attn_bwd_workspace_min if minimum else _lib.msa_sparse_attn_bwd_workspace
+    return int(fn(N, H_q, H_kv, d_h, B_k, k))
+
+
+def msa_sparse_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+                        dO: torch.Tensor, block_idx: torch.Tensor, B_k: int = 128, scale: float | None = None,
+                        dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Gradients of Eq. 8 (selection fixed).  Returns (dq [N,H_q,d_h], dk, dv [N,H_kv,d_h]) fp32."""
+    N, H_q, d_h = q.shape
+    H_kv = k.shape[1]
+    kk = block_idx.shape[2]
+    _need(q, "q", torch.bfloat16, (N, H_q, d_h))
+    _need(k, "k", torch.bfloat16, (N, H_kv, d_h))
+    _need(v, "v", torch.bfloat16, (N, H_kv, d_h))
+    _need(o, "o", torch.float32, (N, H_q, d_h))
+    _need(lse, "lse", torch.float32, (N, H_q))
+    _need(dO, "dO", torch.bfloat16, (N, H_q, d_h))
+    _need(block_idx, "block_idx", torch.int32, (N, H_kv, kk))
+    if scale is None:
+        scale = d_h ** -0.5
+    dev = q.device
+    if dq is None:
+        dq = torch.empty((N, H_q, d_h), dtype=torch.float32, device=dev)
+    if dk is None:
+        dk = torch.empty((N, H_kv, d_h), dtype=torch.float32, device=dev)
+    if dv is None:
+        dv = torch.empty((N, H_kv, d_h), dtype=torch.float32, device=dev)
+    _need(dq, "dq", torch.float32, (N, H_q, d_h))
+    _need(dk, "dk", torch.float32, (N, H_kv, d_h))
+    _need(dv, "dv", torch.float32, (N, H_kv, d_h))
+    ws = _ws(_lib.msa_sparse_attn_bwd_workspace(N, H_q, H_kv, d_h, B_k, kk), dev, workspace)
+    _check(_lib.msa_sparse_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), _ptr(block_idx), N, H_q,
+                                    H_kv, d_h, B_k, kk, float(scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream(stream)), "msa_sparse_attn_bwd")
+    return dq, dk, dv
 
 
 # ----------------------------------------------------------------- KL alignment

@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmsa.so")
-SOURCES = ["msa_api.hip", "index_topk.hip", "sparse_attn.hip", "decode.hip"]
+SOURCES = ["msa_api.hip", "index_topk.hip", "sparse_attn.hip", "decode.hip", "backward.hip"]
 
 
 def hipcc_command(out: str = LIB, extra=()) -> list[str]:

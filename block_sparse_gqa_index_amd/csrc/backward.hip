@@ -1,0 +1,422 @@
+// Main Branch backward: the gradients of Eq. 8 with respect to q, k and v for a
+// fixed selection (the selection itself has no gradient).
+//
+// Method: page "MiniMax Sparse Attention (MSA)" paper review, section 3, Eq. 8
+// (softmax attention over the chosen blocks) differentiated; reading notes page,
+// section 5.4 (the backward walks the same KV-outer work and needs load balancing
+// for data-dependent sparsity).  With P = softmax(scale q K^T) over the selected
+// tokens, o = P V and D = <dO, o> per (query, head):
+//   dV = P^T dO,  dS = P * (dO V^T - D),  dQ = scale dS K,  dK = scale dS^T Q.
+//
+// Work decomposition on gfx950.  The forward's inverse index is rebuilt: for every
+// (group, block) list, items of at most 256 (query, slot) pairs.  A workgroup
+// stages the block's K, V (rows) and K^T in LDS once per item and walks the item
+// in sub-chunks of 64 MFMA rows ((64 / G) queries x G heads), with the q and dO rows
+// of the sub-chunk in LDS both row-major and transposed.  Wave w owns keys
+// 32w .. 32w+31 of the block:
+//   S = Q K^T and dP = dO V^T on 32x32x16 MFMAs give, per lane, one key (the lane)
+//   and 32 rows (registers), so P and dS are formed in registers;
+//   dV += P^T dO and dK += dS^T Q use P and dS directly as MFMA operands, and
+//   accumulate in registers over the whole item;
+//   dS goes to LDS, and each wave then computes dQ for 32 rows x 64 dims over all
+//   128 keys (dS K, with K^T as the operand).
+// dQ leaves as one fp32 partial row per (query, slot, head), summed over the slots
+// by a second kernel; dK and dV leave as one fp32 partial block per item, summed in
+// item order per (group, block) by a third.  No atomics touch a gradient.  dq is
+// bitwise reproducible; dK and dV sum a list's rows in the order the inverse index
+// placed its pairs (decided by its atomic counters), so they can differ between runs
+// by fp32 rounding.
+#include "msa_device.h"
+#include "msa_kernels.h"
+
+namespace msa {
+
+namespace {
+
+constexpr int kBwdThreads = 256;
+constexpr int kBwdRows = 64;  // MFMA rows per sub-chunk
+constexpr int kBwdPairRegs = 4;  // an item holds at most 256 pairs: 4 registers of 64 lanes
+
+// Pair idx of the item (any lane): register idx / 64 of lane idx % 64.
+__device__ __forceinline__ int bwd_pair_at(const int (&ip)[kBwdPairRegs], int idx) {
+  int v = 0;
+#pragma unroll
+  for (int k = 0; k < kBwdPairRegs; ++k) {
+    const int x = __shfl(ip[k], idx & 63);
+    v = (idx >> 6) == k ? x : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint16_t to_bf16(float x) { return (uint16_t)(pack_bf16x2(x, 0.f) & 0xffffu); }
+
+__device__ __forceinline__ u32x4_t pack8(const float* x) {
+  return u32x4_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                 pack_bf16x2(x[6], x[7])};
+}
+
+// D[row] = <dO[row], o[row]> over the 128 dims, 16 lanes per row.
+__global__ __launch_bounds__(256) void bwd_rowdot_kernel(const uint16_t* __restrict__ dO, const float* __restrict__ o,
+                                                         int64_t rows, float* __restrict__ D) {
+  const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
+  const int l = threadIdx.x & 15;
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4_t g = *reinterpret_cast<const u32x4_t*>(dO + row * kDh + l * 8);
+    const float4 a = *reinterpret_cast<const float4*>(o + row * kDh + l * 8);
+    const float4 c = *reinterpret_cast<const float4*>(o + row * kDh + l * 8 + 4);
+    auto lo = [](uint32_t w) { return __uint_as_float(w << 16); };
+    auto hi = [](uint32_t w) { return __uint_as_float(w & 0xffff0000u); };
+    acc = lo(g.x) * a.x + hi(g.x) * a.y + lo(g.y) * a.z + hi(g.y) * a.w + lo(g.z) * c.x + hi(g.z) * c.y +
+          lo(g.w) * c.z + hi(g.w) * c.w;
+  }
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) acc += __shfl_xor(acc, m);
+  if (row < rows && l == 0) D[row] = acc;
+}
+
+template <int G>
+__global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
+    const uint16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Drow,
+    const int4* __restrict__ items, const int32_t* __restrict__ n_items_ptr, const int32_t* __restrict__ pairs,
+    int64_t N, int H_kv, int64_t B, int nW, int kk, int64_t w0, float scale, float scale_log2,
+    float* __restrict__ dq_part, float* __restrict__ dkv_part) {
+  static_assert(G <= 32, "a sub-chunk holds at least two queries");
+  constexpr int kQS = kBwdRows / G;  // queries per sub-chunk
+  // 3 x 32 KB block tiles + 4 x 16 KB sub-chunk tiles = 160 KB (one workgroup per CU).
+  __shared__ __attribute__((aligned(16))) uint8_t Ks[kBk * 256];   // K rows (key swap23(rho) at row rho)
+  __shared__ __attribute__((aligned(16))) uint8_t Vs[kBk * 256];   // V rows, same order
+  __shared__ __attribute__((aligned(16))) uint8_t Kt[kDh * 256];   // K^T, keys in natural order
+  __shared__ __attribute__((aligned(16))) uint8_t Qs[kBwdRows * 256];   // q rows; later dS rows
+  __shared__ __attribute__((aligned(16))) uint8_t dOs[kBwdRows * 256];  // dO rows
+  __shared__ __attribute__((aligned(16))) uint8_t Qt[kDh * 128];   // q^T, rows at position swap23 within 32
+  __shared__ __attribute__((aligned(16))) uint8_t dOt[kDh * 128];  // dO^T, same
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int H_q = H_kv * G;
+  const int n_items = *n_items_ptr;
+  const int grid = gridDim.x;
+  const int per_xcd = grid >> 3;
+  const int xcd = blockIdx.x & 7, slot_in_xcd = blockIdx.x >> 3;
+  for (int64_t round = 0;; ++round) {
+    const int64_t item = round * grid + (int64_t)xcd * per_xcd + slot_in_xcd;
+    if (item >= n_items) break;
+    const int4 it = items[item];
+    const int64_t b = it.x % B, r = (it.x / B) / nW;
+    const int start = it.y, cnt = it.z;
+    int ip[kBwdPairRegs];
+#pragma unroll
+    for (int k = 0; k < kBwdPairRegs; ++k) ip[k] = pairs[start + (64 * k + lane < cnt ? 64 * k + lane : cnt - 1)];
+    __syncthreads();  // the previous item's LDS reads are done
+    {
+      int stid = tid;
+      asm volatile("" : "+v"(stid));
+      const int64_t tok0 = b * kBk;
+      const int nvalid = (N - tok0 < kBk) ? (int)(N - tok0) : kBk;
+      const int64_t base = tok0 * H_kv * kDh + r * kDh;
+      stage_k(kp + base, H_kv * kDh, nvalid, Ks, stid);
+      stage_k(vp + base, H_kv * kDh, nvalid, Vs, stid);
+      stage_v(kp + base, H_kv * kDh, nvalid, Kt, stid);
+    }
+
+    f32x16_t dv_acc[4], dk_acc[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) dv_acc[dt] = dk_acc[dt] = f32x16_t{};
+    const int koff = 32 * wave + swap23(l32);  // this lane's key (as S/dP column)
+
+    for (int cb = 0; cb < cnt; cb += kQS) {
+      asm volatile("" ::: "memory");
+      // Row l of the sub-chunk (l = 0..63) is (pair cb + l / G, head l % G); lane l
+      // keeps that row's pair, lse and D for the others to read by shuffles.
+      const int my_idx = cb + lane / G;
+      const bool my_valid = my_idx < cnt;
+      const int my_pr = bwd_pair_at(ip, my_valid ? my_idx : cnt - 1);
+      const int64_t my_i = w0 + (my_pr >> 5);
+      const int64_t my_row = my_i * H_q + r * G + lane % G;
+      const float my_l2 = lse[my_row] * kLog2e;
+      const float my_D = Drow[my_row];
+      {
+        // Gather: thread t loads 16-byte chunk t & 15 of rows (t >> 4) + 16j.
+        const int c = tid & 15;
+        u32x4_t qv[4], gv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int rho = (tid >> 4) + 16 * j;
+          const int idx = cb + rho / G;
+          const int pr = bwd_pair_at(ip, idx < cnt ? idx : cnt - 1);
+          const int64_t src = ((w0 + (pr >> 5)) * H_q + r * G + rho % G) * kDh + c * 8;
+          qv[j] = *reinterpret_cast<const u32x4_t*>(q + src);
+          gv[j] = *reinterpret_cast<const u32x4_t*>(dO + src);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int rho = (tid >> 4) + 16 * j;
+          *reinterpret_cast<u32x4_t*>(Qs + rho * 256 + ((c ^ (rho & 15)) << 4)) = qv[j];
+          *reinterpret_cast<u32x4_t*>(dOs + rho * 256 + ((c ^ (rho & 15)) << 4)) = gv[j];
+        }
+      }
+      __syncthreads();  // rows staged (and, on the first sub-chunk, the block)
+      {
+        // Transposes: threads 0..127 build Qt, 128..255 dOt.  Thread (pg, dc) moves
+        // positions 8pg .. 8pg+7 (row (pos & ~31) | swap23(pos & 31)) x dims 8dc .. +7.
+        const int tt = tid & 127;
+        const uint8_t* src = tid < 128 ? Qs : dOs;
+        uint8_t* dst = tid < 128 ? Qt : dOt;
+        const int pg = tt & 7, dc = tt >> 3;
+        u32x4_t w[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int pos = 8 * pg + j;
+          const int rho = (pos & ~31) | swap23(pos & 31);
+          w[j] = *reinterpret_cast<const u32x4_t*>(src + rho * 256 + ((dc ^ (rho & 15)) << 4));
+        }
+#pragma unroll
+        for (int f = 0; f < 8; ++f) {
+          u32x4_t o4;
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const uint32_t x = w[2 * m][f >> 1], y = w[2 * m + 1][f >> 1];
+            o4[m] = (f & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
+          }
+          const int d = dc * 8 + f;
+          *reinterpret_cast<u32x4_t*>(dst + d * 128 + ((pg ^ (d & 7)) << 4)) = o4;
+        }
+      }
+      __syncthreads();  // transposes done
+
+      // S and dP: element v of row tile rt is row rt*32 + 8(v/4) + 4h + v%4, key koff.
+      float P[2][16], dS[2][16];
+      {
+        const int krow = 32 * wave + l32;
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          f32x16_t sacc = f32x16_t{}, pacc = f32x16_t{};
+          const int row = rt * 32 + l32;
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const int c = 8 * h + t;
+            const u32x4_t aq = *reinterpret_cast<const u32x4_t*>(Qs + row * 256 + ((c ^ (row & 15)) << 4));
+            const u32x4_t bk = *reinterpret_cast<const u32x4_t*>(Ks + krow * 256 + ((c ^ (krow & 15)) << 4));
+            sacc = mfma_32x32x16(as_bf16x8(aq), as_bf16x8(bk), sacc);
+            const u32x4_t ag = *reinterpret_cast<const u32x4_t*>(dOs + row * 256 + ((c ^ (row & 15)) << 4));
+            const u32x4_t bv = *reinterpret_cast<const u32x4_t*>(Vs + krow * 256 + ((c ^ (krow & 15)) << 4));
+            pacc = mfma_32x32x16(as_bf16x8(ag), as_bf16x8(bv), pacc);
+          }
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int rv = rt * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+            const float l2 = __shfl(my_l2, rv), Dv = __shfl(my_D, rv);
+            const int il = __shfl(my_pr, rv) >> 5;
+            const bool vv = __shfl((int)my_valid, rv) != 0;
+            const bool in = vv && b * kBk + koff <= w0 + il;  // causal, and a real row
+            const float p = in ? __builtin_amdgcn_exp2f(fmaf(sacc[v], scale_log2, -l2)) : 0.f;
+            P[rt][v] = p;
+            dS[rt][v] = p * (pacc[v] - Dv);
+          }
+          __builtin_amdgcn_sched_barrier(0);  // one row tile's accumulators at a time
+        }
+      }
+      // dV += P^T dO and dK += dS^T Q: MFMA rows are this wave's keys (row i holds
+      // key 32w + swap23(i)); k-slot (h, j) of step (rt, s2) is row
+      // rt*32 + 8(2 s2 + j/4) + 4h + j%4, the transposed tiles' position
+      // rt*32 + 16 s2 + 8h + j.
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const u32x4_t ap = pack8(&P[rt][8 * s2]);
+          const u32x4_t ad = pack8(&dS[rt][8 * s2]);
+          const int ch = 4 * rt + 2 * s2 + h;
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            const int d = dt * 32 + l32;
+            const u32x4_t bo = *reinterpret_cast<const u32x4_t*>(dOt + d * 128 + ((ch ^ (d & 7)) << 4));
+            dv_acc[dt] = mfma_32x32x16(as_bf16x8(ap), as_bf16x8(bo), dv_acc[dt]);
+            const u32x4_t bq = *reinterpret_cast<const u32x4_t*>(Qt + d * 128 + ((ch ^ (d & 7)) << 4));
+            dk_acc[dt] = mfma_32x32x16(as_bf16x8(ad), as_bf16x8(bq), dk_acc[dt]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      __syncthreads();  // every wave is done with Qs: dS replaces it
+      // dS rows in Qs: row-major, keys in natural order, chunk kc at kc ^ (row & 15).
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int rv = rt * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+          *reinterpret_cast<uint16_t*>(Qs + rv * 256 + ((((koff >> 3) ^ (rv & 15))) << 4) + (koff & 7) * 2) =
+              to_bf16(dS[rt][v]);
+        }
+      }
+      __syncthreads();  // dS complete
+      {
+        // dQ rows 32(w & 1) + 0..31, dims 64(w >> 1) + 0..63, over all 128 keys.
+        const int row = 32 * (wave & 1) + l32;
+        f32x16_t qacc[2] = {f32x16_t{}, f32x16_t{}};
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int kc = 2 * t + h;
+          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(Qs + row * 256 + ((kc ^ (row & 15)) << 4));
+#pragma unroll
+          for (int dt = 0; dt < 2; ++dt) {
+            const int d = 64 * (wave >> 1) + 32 * dt + l32;
+            const u32x4_t bk = *reinterpret_cast<const u32x4_t*>(Kt + d * 256 + ((kc ^ (d & 15)) << 4));
+            qacc[dt] = mfma_32x32x16(as_bf16x8(a), as_bf16x8(bk), qacc[dt]);
+          }
+        }
+        // element v: row 32(w & 1) + 8(v/4) + 4h + v%4, dim 64(w >> 1) + 32dt + l32
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int rv = 32 * (wave & 1) + 8 * (v >> 2) + 4 * h + (v & 3);
+          const int pr = __shfl(my_pr, rv);
+          const bool vv = __shfl((int)my_valid, rv) != 0;
+          if (vv) {
+            const int64_t prow = (((int64_t)(pr >> 5) * H_kv + r) * kk + (pr & 31)) * G + rv % G;
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt)
+              dq_part[prow * kDh + 64 * (wave >> 1) + 32 * dt + l32] = qacc[dt][v] * scale;
+          }
+        }
+      }
+      __syncthreads();  // the sub-chunk's LDS tiles may be replaced
+    }
+    // The item's dK (scaled) and dV: element v of lane (l32, h) is key
+    // 32w + swap23(8(v/4) + 4h + v%4), dim 32dt + l32.
+    float* kpart = dkv_part + item * 2 * (kBk * kDh);
+    float* vpart = kpart + kBk * kDh;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = 32 * wave + swap23(8 * (v >> 2) + 4 * h + (v & 3));
+        kpart[key * kDh + 32 * dt + l32] = dk_acc[dt][v] * scale;
+        vpart[key * kDh + 32 * dt + l32] = dv_acc[dt][v];
+      }
+    }
+  }
+}
+
+// dQ: per (query, head) the sum of its valid slots' partial rows; 32 lanes per row.
+__global__ __launch_bounds__(256) void bwd_dq_combine_kernel(const float* __restrict__ dq_part,
+                                                             const int32_t* __restrict__ block_idx, int64_t w0,
+                                                             int64_t W, int H_kv, int G, int kk,
+                                                             float* __restrict__ dq) {
+  const int64_t gr = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 5;  // (query in window, head)
+  const int l = threadIdx.x & 31;
+  const int H_q = H_kv * G;
+  if (gr >= W * H_q) return;
+  const int64_t il = gr / H_q;
+  const int hh = (int)(gr % H_q);
+  const int r = hh / G, g = hh % G;
+  const int64_t i = w0 + il;
+  const int32_t* sel = block_idx + (i * H_kv + r) * kk;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < kk; ++s) {
+    const int bb = sel[s];
+    if (bb < 0 || (int64_t)bb > (i >> 7)) continue;
+    const float4 x =
+        *reinterpret_cast<const float4*>(dq_part + ((((il * H_kv + r) * kk + s) * G + g) * kDh) + 4 * l);
+    acc.x += x.x;
+    acc.y += x.y;
+    acc.z += x.z;
+    acc.w += x.w;
+  }
+  *reinterpret_cast<float4*>(dq + (i * H_q + hh) * kDh + 4 * l) = acc;
+}
+
+// dK, dV of block b, group r: the partial blocks of the items of its lists (one per
+// query window), summed in item order and added to dk / dv.
+__global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(const float* __restrict__ dkv_part,
+                                                            const int32_t* __restrict__ counts,
+                                                            const int32_t* __restrict__ lfirst, int item_q,
+                                                            int64_t B, int nW, int H_kv, int64_t N,
+                                                            float* __restrict__ dk, float* __restrict__ dv) {
+  const int64_t rb = blockIdx.x;
+  const int r = (int)(rb / B);
+  const int64_t b = rb % B;
+  for (int e = threadIdx.x; e < 2 * kBk * kDh; e += 256) {
+    const int which = e / (kBk * kDh), kd = e % (kBk * kDh);
+    const int key = kd / kDh, d = kd % kDh;
+    const int64_t tok = b * kBk + key;
+    if (tok >= N) continue;
+    float acc = 0.f;
+    for (int w = 0; w < nW; ++w) {
+      const int64_t l = ((int64_t)r * nW + w) * B + b;
+      const int n = counts[l];
+      const int nit = (n + item_q - 1) / item_q;
+      const int64_t f = lfirst[l];
+      for (int t = 0; t < nit; ++t) acc += dkv_part[((f + t) * 2 + which) * (kBk * kDh) + kd];
+    }
+    float* out = which ? dv : dk;
+    out[(tok * H_kv + r) * kDh + d] += acc;
+  }
+}
+
+__global__ void bwd_zero_kernel(float* __restrict__ p, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += stride) p[e] = 0.f;
+}
+
+}  // namespace
+
+hipError_t launch_bwd_prepare(const uint16_t* dO, const float* o, int64_t rows, float* D, float* dk, float* dv,
+                              int64_t kv_elems, hipStream_t stream) {
+  bwd_rowdot_kernel<<<dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, stream>>>(dO, o, rows, D);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  bwd_zero_kernel<<<dim3(1024), dim3(256), 0, stream>>>(dk, kv_elems);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  bwd_zero_kernel<<<dim3(1024), dim3(256), 0, stream>>>(dv, kv_elems);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_window(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dO,
+                             const float* lse, const float* D, const int32_t* block_idx, int64_t N, int64_t B,
+                             int H_q, int H_kv, int kk, float scale, int64_t w0, int64_t W, int num_cus, float* dq,
+                             float* dk, float* dv, uint8_t* ws, const AttnWorkspace& L, hipStream_t stream) {
+  const int G = H_q / H_kv;
+  int32_t* lfirst = reinterpret_cast<int32_t*>(ws + L.lfirst);
+  hipError_t e = launch_inverse_index(block_idx, B, SeqInfo{}, 7, H_kv, kk, w0, W, ws, L, stream, lfirst);
+  if (e != hipSuccess) return e;
+  const int32_t* n_items = reinterpret_cast<const int32_t*>(ws + L.n_items);
+  const int4* items = reinterpret_cast<const int4*>(ws + L.items);
+  const int32_t* pairs = reinterpret_cast<const int32_t*>(ws + L.pairs);
+  const int32_t* counts = reinterpret_cast<const int32_t*>(ws + L.counts);
+  float* dq_part = reinterpret_cast<float*>(ws + L.opart);
+  float* dkv_part = reinterpret_cast<float*>(ws + L.lpart);
+  int64_t grid = num_cus;
+  if (grid > L.max_items) grid = L.max_items;
+  grid = ((grid + 7) / 8) * 8;
+  const float scale_log2 = scale * kLog2e;
+  switch (G) {
+#define MSA_BWD_CASE(GG)                                                                                  \
+  case GG:                                                                                                \
+    bwd_kernel<GG><<<dim3((unsigned)grid), dim3(kBwdThreads), 0, stream>>>(                                \
+        q, k, v, dO, lse, D, items, n_items, pairs, N, H_kv, B, L.nW, kk, w0, scale, scale_log2, dq_part,   \
+        dkv_part);                                                                                        \
+    break;
+    MSA_BWD_CASE(1)
+    MSA_BWD_CASE(2)
+    MSA_BWD_CASE(4)
+    MSA_BWD_CASE(8)
+    MSA_BWD_CASE(16)
+    MSA_BWD_CASE(32)
+#undef MSA_BWD_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t rows = W * H_q;
+  bwd_dq_combine_kernel<<<dim3((unsigned)((rows * 32 + 255) / 256)), dim3(256), 0, stream>>>(
+      dq_part, block_idx, w0, W, H_kv, G, kk, dq);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  bwd_kv_reduce_kernel<<<dim3((unsigned)(H_kv * B)), dim3(256), 0, stream>>>(dkv_part, counts, lfirst, L.item_q, B,
+                                                                             L.nW, H_kv, N, dk, dv);
+  return hipGetLastError();
+}
+
+}  // namespace msa

@@ -64,12 +64,12 @@ int num_cus() {
 
 // Largest query window (whole blocks of queries, at least one block) whose
 // per-window workspace fits in ws_bytes; B is the list stride in blocks.
-int64_t window_for_bytes(int64_t N, int64_t B, int H_q, int H_kv, int k, size_t ws_bytes, bool kl_parts = false) {
+int64_t window_for_bytes(int64_t N, int64_t B, int H_q, int H_kv, int k, size_t ws_bytes, int parts = msa::kPartsAttn) {
   int64_t lo = 0, hi = (N + msa::kBlockKeys - 1) / msa::kBlockKeys;
   while (lo < hi) {
     const int64_t mid = (lo + hi + 1) / 2;
     const int64_t W = mid * msa::kBlockKeys < N ? mid * msa::kBlockKeys : N;
-    if (msa::attn_workspace_layout(W, H_q, H_kv, k, B, kl_parts).total <= ws_bytes)
+    if (msa::attn_workspace_layout(W, H_q, H_kv, k, B, parts).total <= ws_bytes)
       lo = mid;
     else
       hi = mid - 1;
@@ -306,8 +306,8 @@ static constexpr size_t kKlLossBytes = sizeof(double) * msa::kKlLossParts;
 static size_t kl_workspace_bytes(int64_t N, int H_q, int H_kv, int k, bool minimum) {
   const int64_t B = (N + msa::kBlockKeys - 1) / msa::kBlockKeys;
   const int64_t Wmin = N < msa::kBlockKeys ? N : msa::kBlockKeys;
-  const int64_t W = minimum ? Wmin : window_for_bytes(N, B, H_q, H_kv, k, kDefaultAttnWorkspace, true);
-  return kKlLossBytes + msa::attn_workspace_layout(W, H_q, H_kv, k, B, true).total;
+  const int64_t W = minimum ? Wmin : window_for_bytes(N, B, H_q, H_kv, k, kDefaultAttnWorkspace, msa::kPartsKl);
+  return kKlLossBytes + msa::attn_workspace_layout(W, H_q, H_kv, k, B, msa::kPartsKl).total;
 }
 
 static msa_status_t check_kl_shape(int64_t N, int H_q, int H_kv, int d_h, int d_idx, int B_k, int k) {
@@ -348,8 +348,8 @@ msa_status_t msa_sparse_kl_fwd(const void* q, const void* k, const void* q_idx, 
   if (!aligned(ws, 256)) return fail(MSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   const int64_t B = (N + B_k - 1) / B_k;
   uint8_t* w = static_cast<uint8_t*>(ws);
-  const int64_t W = window_for_bytes(N, B, H_q, H_kv, k_sel, ws_bytes - kKlLossBytes, true);
-  const msa::AttnWorkspace L = msa::attn_workspace_layout(W, H_q, H_kv, k_sel, B, true);
+  const int64_t W = window_for_bytes(N, B, H_q, H_kv, k_sel, ws_bytes - kKlLossBytes, msa::kPartsKl);
+  const msa::AttnWorkspace L = msa::attn_workspace_layout(W, H_q, H_kv, k_sel, B, msa::kPartsKl);
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   const int cus = num_cus();
   for (int64_t w0 = 0; w0 < N; w0 += W) {
@@ -362,6 +362,72 @@ msa_status_t msa_sparse_kl_fwd(const void* q, const void* k, const void* q_idx, 
   }
   hipError_t e = msa::launch_kl_loss(kl, N * H_kv, reinterpret_cast<double*>(w), loss, stream);
   if (e != hipSuccess) return hip_fail(e, "kl loss launch");
+  return ok();
+}
+
+// ---------------------------------------------------------------- backward
+static size_t bwd_d_bytes(int64_t N, int H_q) { return ((sizeof(float) * (size_t)N * H_q) + 255) & ~size_t(255); }
+
+static msa_status_t check_bwd_shape(int64_t N, int H_q, int H_kv, int d_h, int B_k, int k) {
+  msa_status_t st = check_attn_shape(N, H_q, H_kv, d_h, B_k, k);
+  if (st != MSA_OK) return st;
+  if (B_k != msa::kBlockKeys) return fail(MSA_ERR_UNSUPPORTED, "the backward supports B_k = 128");
+  if (H_q / H_kv > 32) return fail(MSA_ERR_UNSUPPORTED, "the backward supports G = H_q / H_kv <= 32");
+  return MSA_OK;
+}
+
+static size_t bwd_workspace_bytes(int64_t N, int H_q, int H_kv, int k, bool minimum) {
+  const int64_t B = (N + msa::kBlockKeys - 1) / msa::kBlockKeys;
+  const int64_t Wmin = N < msa::kBlockKeys ? N : msa::kBlockKeys;
+  const int64_t W = minimum ? Wmin : window_for_bytes(N, B, H_q, H_kv, k, kDefaultAttnWorkspace, msa::kPartsBwd);
+  return bwd_d_bytes(N, H_q) + msa::attn_workspace_layout(W, H_q, H_kv, k, B, msa::kPartsBwd).total;
+}
+
+size_t msa_sparse_attn_bwd_workspace(int64_t N, int H_q, int H_kv, int d_h, int B_k, int k) {
+  if (check_bwd_shape(N, H_q, H_kv, d_h, B_k, k) != MSA_OK || N == 0) return 0;
+  return bwd_workspace_bytes(N, H_q, H_kv, k, false);
+}
+
+size_t msa_sparse_attn_bwd_workspace_min(int64_t N, int H_q, int H_kv, int d_h, int B_k, int k) {
+  if (check_bwd_shape(N, H_q, H_kv, d_h, B_k, k) != MSA_OK || N == 0) return 0;
+  return bwd_workspace_bytes(N, H_q, H_kv, k, true);
+}
+
+msa_status_t msa_sparse_attn_bwd(const void* q, const void* k, const void* v, const float* o, const float* lse,
+                                 const void* dO, const int32_t* block_idx, int64_t N, int H_q, int H_kv, int d_h,
+                                 int B_k, int k_sel, float scale, float* dq, float* dk, float* dv, void* ws,
+                                 size_t ws_bytes, void* hip_stream) {
+  msa_status_t st = check_bwd_shape(N, H_q, H_kv, d_h, B_k, k_sel);
+  if (st != MSA_OK) return st;
+  if (!(scale > 0.f) || scale != scale) return fail(MSA_ERR_INVALID_ARG, "scale must be a positive number");
+  if (N == 0) return ok();
+  if (!q || !k || !v || !o || !lse || !dO || !block_idx || !dq || !dk || !dv)
+    return fail(MSA_ERR_INVALID_ARG, "null pointer");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
+      !aligned(dO, 16) || !aligned(block_idx, 4) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+    return fail(MSA_ERR_INVALID_ARG, "misaligned pointer (q/k/v/o/dO/dq/dk/dv need 16 B)");
+  const size_t need = msa_sparse_attn_bwd_workspace_min(N, H_q, H_kv, d_h, B_k, k_sel);
+  if (!ws || ws_bytes < need)
+    return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes is below the minimum %zu", ws ? ws_bytes : 0, need);
+  if (!aligned(ws, 256)) return fail(MSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const int64_t B = (N + B_k - 1) / B_k;
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  float* D = reinterpret_cast<float*>(w);
+  const size_t dbytes = bwd_d_bytes(N, H_q);
+  const int64_t W = window_for_bytes(N, B, H_q, H_kv, k_sel, ws_bytes - dbytes, msa::kPartsBwd);
+  const msa::AttnWorkspace L = msa::attn_workspace_layout(W, H_q, H_kv, k_sel, B, msa::kPartsBwd);
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  hipError_t e = msa::launch_bwd_prepare(static_cast<const uint16_t*>(dO), o, N * H_q, D, dk, dv,
+                                         N * H_kv * msa::kHeadDim, stream);
+  if (e != hipSuccess) return hip_fail(e, "backward prepare launch");
+  const int cus = num_cus();
+  for (int64_t w0 = 0; w0 < N; w0 += W) {
+    const int64_t Wn = (N - w0 < W) ? N - w0 : W;
+    e = msa::launch_bwd_window(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                               static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dO), lse, D, block_idx,
+                               N, B, H_q, H_kv, k_sel, scale, w0, Wn, cus, dq, dk, dv, w + dbytes, L, stream);
+    if (e != hipSuccess) return hip_fail(e, "backward launch");
+  }
   return ok();
 }
 

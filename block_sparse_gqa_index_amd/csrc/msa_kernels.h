@@ -19,7 +19,7 @@ constexpr int kItemChunks = 16;
 constexpr int kKlPart = 8;
 
 struct AttnWorkspace {
-  size_t counts, tsum, cursor, n_items, items, pairs, opart, lpart, total;
+  size_t counts, tsum, cursor, n_items, items, pairs, opart, lpart, lfirst, total;
   int64_t max_items;
   int item_q;  // queries per work item
   int64_t WQ;  // queries per q-locality window
@@ -59,9 +59,17 @@ hipError_t launch_seq_tables(const int64_t* cu, int batch, int bk, uint8_t* ws, 
 
 // B: the list stride in blocks (the block count, or for several sequences an upper
 // bound of the global block count).
-// kl_parts: partials of the KL pass (kKlPart floats per pair) instead of the
-// attention's partial rows.
-AttnWorkspace attn_workspace_layout(int64_t W, int H_q, int H_kv, int kk, int64_t B, bool kl_parts = false);
+// Inverse index of one query window (lists, item table, pairs) in the workspace
+// regions of L; lfirst (lists entries, may be null) receives each list's first item.
+hipError_t launch_inverse_index(const int32_t* block_idx, int64_t B, const SeqInfo& si, int bsh, int H_kv, int kk,
+                                int64_t w0, int64_t W, uint8_t* ws, const AttnWorkspace& L, hipStream_t stream,
+                                int32_t* lfirst = nullptr);
+
+// What the per-pair and per-item buffers hold: the attention's partial rows, the KL
+// pass's kKlPart floats per pair, or the backward's fp32 dQ rows per pair plus a
+// dK/dV block per item (and each list's first item).
+enum PartKind { kPartsAttn = 0, kPartsKl = 1, kPartsBwd = 2 };
+AttnWorkspace attn_workspace_layout(int64_t W, int H_q, int H_kv, int kk, int64_t B, int parts = kPartsAttn);
 // bk: keys per block, 64 or 128.
 hipError_t launch_sparse_attn_window(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                      const int32_t* block_idx, int64_t N, int64_t B, const SeqInfo& si, int bk,
@@ -79,6 +87,16 @@ hipError_t launch_sparse_kl_window(const uint16_t* q, const uint16_t* k, const u
                                    int num_cus, float* kl, float* lse_idx, uint8_t* ws, const AttnWorkspace& L,
                                    hipStream_t stream);
 hipError_t launch_kl_loss(const float* kl, int64_t n, double* partial, float* loss, hipStream_t stream);
+
+// Backward of the Main Branch (single sequence, B_k = 128, G <= 32): D = <dO, o> per
+// (query, head) and zeroed dk / dv, then per query window the KV-outer pass and the
+// reductions of its dQ rows and dK/dV blocks.
+hipError_t launch_bwd_prepare(const uint16_t* dO, const float* o, int64_t rows, float* D, float* dk, float* dv,
+                              int64_t kv_elems, hipStream_t stream);
+hipError_t launch_bwd_window(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dO,
+                             const float* lse, const float* D, const int32_t* block_idx, int64_t N, int64_t B,
+                             int H_q, int H_kv, int kk, float scale, int64_t w0, int64_t W, int num_cus, float* dq,
+                             float* dk, float* dv, uint8_t* ws, const AttnWorkspace& L, hipStream_t stream);
 
 DecodeWorkspace decode_workspace_layout(int batch, int H_q, int H_kv, int kk, int64_t Bmax);
 hipError_t launch_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_t* k_cache,

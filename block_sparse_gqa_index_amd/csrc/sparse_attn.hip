@@ -140,7 +140,8 @@ __global__ __launch_bounds__(kScanTile) void inv_scan_write_kernel(const int32_t
                                                                  int item_q, const int64_t* __restrict__ tsum,
                                                                  int32_t* __restrict__ cursor,
                                                                  int4* __restrict__ items,
-                                                                 int32_t* __restrict__ n_items) {
+                                                                 int32_t* __restrict__ n_items,
+                                                                 int32_t* __restrict__ lfirst) {
   __shared__ int64_t lds[16];
   const int tile = blockIdx.x;
   int64_t pp = 0, ip = 0;
@@ -157,6 +158,7 @@ __global__ __launch_bounds__(kScanTile) void inv_scan_write_kernel(const int32_t
   const int64_t ioff = ip + block_excl_scan_1024(nit, lds);
   if (l < L) {
     cursor[l] = (int32_t)poff;
+    if (lfirst) lfirst[l] = (int32_t)ioff;  // first item of list l
     for (int it = 0; it < nit; ++it) {
       const int start = (int)poff + it * item_q;
       const int cnt = (c - it * item_q < item_q) ? c - it * item_q : item_q;
@@ -1064,7 +1066,7 @@ hipError_t launch_seq_tables(const int64_t* cu, int batch, int bk, uint8_t* ws, 
   return hipGetLastError();
 }
 
-AttnWorkspace attn_workspace_layout(int64_t W, int H_q, int H_kv, int kk, int64_t B, bool kl_parts) {
+AttnWorkspace attn_workspace_layout(int64_t W, int H_q, int H_kv, int kk, int64_t B, int parts) {
   AttnWorkspace L{};
   // q-locality window of 64*B queries (a multiple of 4096, so every inverse-index
   // tile lies in one window): each K/V block is staged once per (group, window)
@@ -1094,13 +1096,17 @@ AttnWorkspace attn_workspace_layout(int64_t W, int H_q, int H_kv, int kk, int64_
   L.n_items = take(sizeof(int32_t) * 4);
   L.items = take(sizeof(int4) * max_items);
   L.pairs = take(sizeof(int32_t) * max_pairs);
-  if (kl_parts) {
+  if (parts == kPartsKl) {
     L.opart = take(sizeof(float) * kKlPart * max_pairs);
     L.lpart = take(0);
+  } else if (parts == kPartsBwd) {
+    L.opart = take(sizeof(float) * max_pairs * G * kDh);         // dQ row per (pair, head)
+    L.lpart = take(sizeof(float) * max_items * 2 * kBk * kDh);   // dK and dV block per item
   } else {
     L.opart = take(sizeof(uint16_t) * max_pairs * G * kDh);
     L.lpart = take(sizeof(float2) * max_pairs * G);
   }
+  L.lfirst = take(parts == kPartsBwd ? sizeof(int32_t) * lists : 0);
   L.total = off;
   L.max_items = max_items;
   L.item_q = item_q;
@@ -1109,9 +1115,9 @@ AttnWorkspace attn_workspace_layout(int64_t W, int H_q, int H_kv, int kk, int64_
 
 // Inverse index of one query window: per-list pair counts, their scan into list
 // offsets and the item table, then the scatter of the (query, slot) pairs.
-static hipError_t launch_inverse_index(const int32_t* block_idx, int64_t B, const SeqInfo& si, int bsh, int H_kv,
-                                       int kk, int64_t w0, int64_t W, uint8_t* ws, const AttnWorkspace& L,
-                                       hipStream_t stream) {
+hipError_t launch_inverse_index(const int32_t* block_idx, int64_t B, const SeqInfo& si, int bsh, int H_kv, int kk,
+                                int64_t w0, int64_t W, uint8_t* ws, const AttnWorkspace& L, hipStream_t stream,
+                                int32_t* lfirst) {
   const int64_t lists = (int64_t)H_kv * L.nW * B;
   int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
   int32_t* cursor = reinterpret_cast<int32_t*>(ws + L.cursor);
@@ -1135,7 +1141,7 @@ static hipError_t launch_inverse_index(const int32_t* block_idx, int64_t B, cons
   inv_tile_sums_kernel<<<dim3(tiles), dim3(kScanTile), 0, stream>>>(counts, lists, L.item_q, tsum);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   inv_scan_write_kernel<<<dim3(tiles), dim3(kScanTile), 0, stream>>>(counts, lists, L.item_q, tsum, cursor, items,
-                                                                    n_items);
+                                                                    n_items, lfirst);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   inv_scatter_kernel<16><<<igrid, dim3(256), 2 * lds_count, stream>>>(block_idx, si, bsh, w0, W, H_kv, kk, B,
                                                                       TQ, L.WQ, L.nW, cursor, pairs);

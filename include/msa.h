@@ -125,6 +125,31 @@ msa_status_t msa_sparse_kl_fwd(const void* q, const void* k, const void* q_idx, 
                                float* kl, float* lse_idx, float* loss, void* ws, size_t ws_bytes,
                                void* hip_stream);
 
+/* ------------------------------------------------------------------ Backward
+ * msa_sparse_attn_bwd — gradients of Eq. 8 with respect to q, k and v for the
+ * upstream gradient dO of o, the selection block_idx held fixed (reading notes,
+ * section 5.4: the backward over data-dependent sparsity).  With P the softmax
+ * over each row's selected tokens and D = <dO, o> per (query, head):
+ *   dV = P^T dO,  dS = P (dO V^T - D),  dQ = scale dS K,  dK = scale dS^T Q.
+ *   q, k, v, block_idx, scale  as given to msa_sparse_attn_fwd
+ *   o, lse     fp32 [N, H_q, d_h], [N, H_q]  that call's outputs
+ *   dO         bf16 [N, H_q, d_h]
+ *   dq         fp32 [N, H_q, d_h]   out
+ *   dk, dv     fp32 [N, H_kv, d_h]  out (overwritten, not accumulated into)
+ * Limits: B_k = 128, G = H_q / H_kv <= 32, and those of msa_sparse_attn_fwd.
+ * Workspace as for the forward (smaller workspaces run in query windows).  No
+ * atomics touch a gradient: dq is bitwise reproducible across reruns and window
+ * sizes; dk and dv sum each block's rows in the order the inverse index lists its
+ * pairs (set by atomic counters there), so they vary at fp32 rounding level only.
+ */
+size_t msa_sparse_attn_bwd_workspace(int64_t N, int H_q, int H_kv, int d_h, int B_k, int k);
+size_t msa_sparse_attn_bwd_workspace_min(int64_t N, int H_q, int H_kv, int d_h, int B_k, int k);
+msa_status_t msa_sparse_attn_bwd(const void* q, const void* k, const void* v, const float* o,
+                                 const float* lse, const void* dO, const int32_t* block_idx,
+                                 int64_t N, int H_q, int H_kv, int d_h, int B_k, int k_sel,
+                                 float scale, float* dq, float* dk, float* dv, void* ws,
+                                 size_t ws_bytes, void* hip_stream);
+
 /* ------------------------------------------------------------------ Packed sequences
  * Variable-length prefill: `batch` independent sequences packed along the token
  * axis, each with its own causal mask, block grid and local block (every position

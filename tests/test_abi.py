@@ -222,3 +222,22 @@ def test_decode_paged_rejects_bad_arguments(lib):
     assert call(H_q=64, H_kv=2) == lib.MSA_ERR_UNSUPPORTED
     assert call(ws_bytes=16) == lib.MSA_ERR_WORKSPACE
     assert call(batch=0) == lib.MSA_OK
+
+
+def test_backward_rejects_bad_arguments(lib):
+    raw = lib.raw()
+    f = 0x10000
+
+    def call(N=4096, H_q=8, H_kv=2, d_h=128, B_k=128, k=8, ws=f, ws_bytes=1 << 40, o=f, dq=f):
+        return raw.msa_sparse_attn_bwd(f, f, f, o, f, f, f, N, H_q, H_kv, d_h, B_k, k, 0.088, dq, f, f, ws,
+                                       ws_bytes, None)
+
+    assert call(B_k=64) == lib.MSA_ERR_UNSUPPORTED
+    assert call(H_q=128, H_kv=2) == lib.MSA_ERR_UNSUPPORTED
+    assert call(o=None) == lib.MSA_ERR_INVALID_ARG
+    assert call(dq=f + 4) == lib.MSA_ERR_INVALID_ARG
+    assert call(ws=None) == lib.MSA_ERR_WORKSPACE
+    need = raw.msa_sparse_attn_bwd_workspace_min(4096, 8, 2, 128, 128, 8)
+    assert 0 < need < raw.msa_sparse_attn_bwd_workspace(4096, 8, 2, 128, 128, 8)
+    assert call(ws_bytes=need - 1) == lib.MSA_ERR_WORKSPACE
+    assert call(N=0) == lib.MSA_OK
