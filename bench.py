@@ -207,7 +207,7 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def run_prefill(msa, synth, cfg, mode, steps, warmup, with_kl=False):
+def run_prefill(msa, synth, cfg, mode, steps, warmup, with_kl=False, with_bwd=False):
     import torch
     dev = "cuda"
     N, H_q, H_kv, k, B_k = cfg.N, cfg.H_q, cfg.H_kv, cfg.k, cfg.B_k
@@ -286,11 +286,51 @@ def run_prefill(msa, synth, cfg, mode, steps, warmup, with_kl=False):
         "block0_fanin_per_group": int(fan[:, 0].float().mean().item()), "max_fanin": int(fan.max().item()),
         "median_fanin": float(fan.float().median().item()),
     }
-    del o, ws
+    del ws
     if with_kl:
         res["kl"] = run_kl(msa, inp, cfg, block_idx, lse, slot_pairs, lists, pairs, steps)
-    del lse, block_idx
+    if with_bwd:
+        res["backward"] = run_bwd(msa, inp, cfg, block_idx, o, lse, slot_pairs, pairs, max(2, steps // 4))
+    del o, lse, block_idx
     return res, inp
+
+
+def run_bwd(msa, inp, cfg, block_idx, o, lse, slot_pairs, pairs, steps):
+    """The Main Branch backward on the step's selection and outputs, for a seeded
+    upstream gradient, timed on its own (a training step's second half)."""
+    import torch
+    N, H_q, H_kv, k = cfg.N, cfg.H_q, cfg.H_kv, cfg.k
+    G = H_q // H_kv
+    dev = "cuda"
+    torch.cuda.empty_cache()
+    g = torch.Generator(device=dev).manual_seed(cfg.seed)
+    dO = torch.randn((N, H_q, cfg.d_h), generator=g, device=dev).to(torch.bfloat16)
+    dq = torch.empty((N, H_q, cfg.d_h), dtype=torch.float32, device=dev)
+    dk = torch.empty((N, H_kv, cfg.d_h), dtype=torch.float32, device=dev)
+    dv = torch.empty_like(dk)
+    ws = torch.empty(msa.msa_sparse_attn_bwd_workspace(N, H_q, H_kv, k), dtype=torch.uint8, device=dev)
+
+    def step():
+        msa.msa_sparse_attn_bwd(inp.q, inp.k, inp.v, o, lse, dO, block_idx, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    # S, dP, dV, dK and dQ: five products of 2 d_h FLOP per attended (query, head, key).
+    flops = 10 * cfg.d_h * pairs
+    out = {"ms": round(ms, 4), "tflops": round(flops / (ms / 1e3) / 1e12, 2),
+           "mfma_peak_frac": round(flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4), "steps": steps,
+           "workspace_bytes": int(ws.numel())}
+    del ws, dO, dq, dk, dv
+    torch.cuda.empty_cache()
+    return out
 
 
 def run_kl(msa, inp, cfg, block_idx, lse, slot_pairs, lists, pairs, steps):
@@ -451,6 +491,7 @@ def main(argv=None) -> int:
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-kl", action="store_true", help="skip the separately timed KL alignment pass")
     ap.add_argument("--no-paged", action="store_true", help="skip the paged FP8 decode measurement")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the separately timed backward")
     ap.add_argument("--single-mode", action="store_true", help="skip the second input mode")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="start with plain copies of known size (for counter runs)")
@@ -484,7 +525,8 @@ def main(argv=None) -> int:
     N, H_q, H_kv, k, B_k = cfg.N, cfg.H_q, cfg.H_kv, cfg.k, cfg.B_k
     other = "structured" if args.mode == "literal" else "literal"
 
-    pre, inp = run_prefill(msa, synth, cfg, args.mode, args.steps, args.warmup, with_kl=not args.no_kl)
+    pre, inp = run_prefill(msa, synth, cfg, args.mode, args.steps, args.warmup, with_kl=not args.no_kl,
+                           with_bwd=not args.no_bwd)
     result = {
         "metric": "MSA prefill tokens/s + TFLOP/s at 128K; decode tokens/s at 128K KV (1 GPU)",
         "value": pre["tokens_per_s"],
