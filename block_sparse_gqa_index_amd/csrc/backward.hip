@@ -127,30 +127,38 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
     for (int dt = 0; dt < 4; ++dt) dv_acc[dt] = dk_acc[dt] = f32x16_t{};
     const int koff = 32 * wave + swap23(l32);  // this lane's key (as S/dP column)
 
+    // Row l of a sub-chunk (l = 0..63) is (pair cb + l / G, head l % G); lane l keeps
+    // that row's pair, lse and D for the others to read by shuffles.  Thread t loads
+    // 16-byte chunk t & 15 of rows (t >> 4) + 16j of q and dO.  Both are fetched one
+    // sub-chunk ahead, so their latency hides under the previous sub-chunk's work.
+    u32x4_t qv[4], gv[4];
+    int my_pr;
+    bool my_valid;
+    float my_l2, my_D;
+    auto fetch = [&](int cbase) {
+      const int my_idx = cbase + lane / G;
+      my_valid = my_idx < cnt;
+      my_pr = bwd_pair_at(ip, my_valid ? my_idx : cnt - 1);
+      const int64_t my_row = (w0 + (my_pr >> 5)) * H_q + r * G + lane % G;
+      my_l2 = lse[my_row] * kLog2e;
+      my_D = Drow[my_row];
+      const int c = tid & 15;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rho = (tid >> 4) + 16 * j;
+        const int idx = cbase + rho / G;
+        const int pr = bwd_pair_at(ip, idx < cnt ? idx : cnt - 1);
+        const int64_t src = ((w0 + (pr >> 5)) * H_q + r * G + rho % G) * kDh + c * 8;
+        qv[j] = *reinterpret_cast<const u32x4_t*>(q + src);
+        gv[j] = *reinterpret_cast<const u32x4_t*>(dO + src);
+      }
+    };
+    fetch(0);
+
     for (int cb = 0; cb < cnt; cb += kQS) {
       asm volatile("" ::: "memory");
-      // Row l of the sub-chunk (l = 0..63) is (pair cb + l / G, head l % G); lane l
-      // keeps that row's pair, lse and D for the others to read by shuffles.
-      const int my_idx = cb + lane / G;
-      const bool my_valid = my_idx < cnt;
-      const int my_pr = bwd_pair_at(ip, my_valid ? my_idx : cnt - 1);
-      const int64_t my_i = w0 + (my_pr >> 5);
-      const int64_t my_row = my_i * H_q + r * G + lane % G;
-      const float my_l2 = lse[my_row] * kLog2e;
-      const float my_D = Drow[my_row];
       {
-        // Gather: thread t loads 16-byte chunk t & 15 of rows (t >> 4) + 16j.
         const int c = tid & 15;
-        u32x4_t qv[4], gv[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int rho = (tid >> 4) + 16 * j;
-          const int idx = cb + rho / G;
-          const int pr = bwd_pair_at(ip, idx < cnt ? idx : cnt - 1);
-          const int64_t src = ((w0 + (pr >> 5)) * H_q + r * G + rho % G) * kDh + c * 8;
-          qv[j] = *reinterpret_cast<const u32x4_t*>(q + src);
-          gv[j] = *reinterpret_cast<const u32x4_t*>(dO + src);
-        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int rho = (tid >> 4) + 16 * j;
@@ -158,6 +166,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
           *reinterpret_cast<u32x4_t*>(dOs + rho * 256 + ((c ^ (rho & 15)) << 4)) = gv[j];
         }
       }
+      const int cur_pr = my_pr;
+      const bool cur_valid = my_valid;
+      const float cur_l2 = my_l2, cur_D = my_D;
       __syncthreads();  // rows staged (and, on the first sub-chunk, the block)
       {
         // Transposes: threads 0..127 build Qt, 128..255 dOt.  Thread (pg, dc) moves
@@ -186,6 +197,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
         }
       }
       __syncthreads();  // transposes done
+      fetch(cb + kQS < cnt ? cb + kQS : cb);  // the next sub-chunk (past the end: reread, unused)
 
       // S and dP: element v of row tile rt is row rt*32 + 8(v/4) + 4h + v%4, key koff.
       float P[2][16], dS[2][16];
@@ -208,9 +220,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int rv = rt * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-            const float l2 = __shfl(my_l2, rv), Dv = __shfl(my_D, rv);
-            const int il = __shfl(my_pr, rv) >> 5;
-            const bool vv = __shfl((int)my_valid, rv) != 0;
+            const float l2 = __shfl(cur_l2, rv), Dv = __shfl(cur_D, rv);
+            const int il = __shfl(cur_pr, rv) >> 5;
+            const bool vv = __shfl((int)cur_valid, rv) != 0;
             const bool in = vv && b * kBk + koff <= w0 + il;  // causal, and a real row
             const float p = in ? __builtin_amdgcn_exp2f(fmaf(sacc[v], scale_log2, -l2)) : 0.f;
             P[rt][v] = p;
@@ -272,8 +284,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int rv = 32 * (wave & 1) + 8 * (v >> 2) + 4 * h + (v & 3);
-          const int pr = __shfl(my_pr, rv);
-          const bool vv = __shfl((int)my_valid, rv) != 0;
+          const int pr = __shfl(cur_pr, rv);
+          const bool vv = __shfl((int)cur_valid, rv) != 0;
           if (vv) {
             const int64_t prow = (((int64_t)(pr >> 5) * H_kv + r) * kk + (pr & 31)) * G + rv % G;
 #pragma unroll
