@@ -20,8 +20,8 @@
 //   accumulate in registers over the whole item;
 //   dS goes to LDS, and each wave then computes dQ for 32 rows x 64 dims over all
 //   128 keys (dS K, with K^T as the operand).
-// dQ leaves as one fp32 partial row per (query, slot, head), summed over the slots
-// by a second kernel; dK and dV leave as one fp32 partial block per item, summed in
+// dQ leaves as one bf16 partial row per (query, slot, head), summed over the slots
+// in fp32 by a second kernel; dK and dV leave as one fp32 partial block per item, summed in
 // item order per (group, block) by a third.  No atomics touch a gradient.  dq is
 // bitwise reproducible; dK and dV sum a list's rows in the order the inverse index
 // placed its pairs (decided by its atomic counters), so they can differ between runs
@@ -81,7 +81,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
     const uint16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Drow,
     const int4* __restrict__ items, const int32_t* __restrict__ n_items_ptr, const int32_t* __restrict__ pairs,
     int64_t N, int H_kv, int64_t B, int nW, int kk, int64_t w0, float scale, float scale_log2,
-    float* __restrict__ dq_part, float* __restrict__ dkv_part) {
+    uint16_t* __restrict__ dq_part, float* __restrict__ dkv_part) {
   static_assert(G <= 32, "a sub-chunk holds at least two queries");
   constexpr int kQS = kBwdRows / G;  // queries per sub-chunk
   // 3 x 32 KB block tiles + 4 x 16 KB sub-chunk tiles = 160 KB (one workgroup per CU).
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
             const int64_t prow = (((int64_t)(pr >> 5) * H_kv + r) * kk + (pr & 31)) * G + rv % G;
 #pragma unroll
             for (int dt = 0; dt < 2; ++dt)
-              dq_part[prow * kDh + 64 * (wave >> 1) + 32 * dt + l32] = qacc[dt][v] * scale;
+              dq_part[prow * kDh + 64 * (wave >> 1) + 32 * dt + l32] = to_bf16(qacc[dt][v] * scale);
           }
         }
       }
@@ -313,7 +313,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
 }
 
 // dQ: per (query, head) the sum of its valid slots' partial rows; 32 lanes per row.
-__global__ __launch_bounds__(256) void bwd_dq_combine_kernel(const float* __restrict__ dq_part,
+__global__ __launch_bounds__(256) void bwd_dq_combine_kernel(const uint16_t* __restrict__ dq_part,
                                                              const int32_t* __restrict__ block_idx, int64_t w0,
                                                              int64_t W, int H_kv, int G, int kk,
                                                              float* __restrict__ dq) {
@@ -330,12 +330,11 @@ __global__ __launch_bounds__(256) void bwd_dq_combine_kernel(const float* __rest
   for (int s = 0; s < kk; ++s) {
     const int bb = sel[s];
     if (bb < 0 || (int64_t)bb > (i >> 7)) continue;
-    const float4 x =
-        *reinterpret_cast<const float4*>(dq_part + ((((il * H_kv + r) * kk + s) * G + g) * kDh) + 4 * l);
-    acc.x += x.x;
-    acc.y += x.y;
-    acc.z += x.z;
-    acc.w += x.w;
+    const uint2 x = *reinterpret_cast<const uint2*>(dq_part + ((((il * H_kv + r) * kk + s) * G + g) * kDh) + 4 * l);
+    acc.x += __uint_as_float(x.x << 16);
+    acc.y += __uint_as_float(x.x & 0xffff0000u);
+    acc.z += __uint_as_float(x.y << 16);
+    acc.w += __uint_as_float(x.y & 0xffff0000u);
   }
   *reinterpret_cast<float4*>(dq + (i * H_q + hh) * kDh + 4 * l) = acc;
 }
@@ -398,7 +397,7 @@ hipError_t launch_bwd_window(const uint16_t* q, const uint16_t* k, const uint16_
   const int4* items = reinterpret_cast<const int4*>(ws + L.items);
   const int32_t* pairs = reinterpret_cast<const int32_t*>(ws + L.pairs);
   const int32_t* counts = reinterpret_cast<const int32_t*>(ws + L.counts);
-  float* dq_part = reinterpret_cast<float*>(ws + L.opart);
+  uint16_t* dq_part = reinterpret_cast<uint16_t*>(ws + L.opart);
   float* dkv_part = reinterpret_cast<float*>(ws + L.lpart);
   int64_t grid = num_cus;
   if (grid > L.max_items) grid = L.max_items;

@@ -1100,7 +1100,7 @@ AttnWorkspace attn_workspace_layout(int64_t W, int H_q, int H_kv, int kk, int64_
     L.opart = take(sizeof(float) * kKlPart * max_pairs);
     L.lpart = take(0);
   } else if (parts == kPartsBwd) {
-    L.opart = take(sizeof(float) * max_pairs * G * kDh);         // dQ row per (pair, head)
+    L.opart = take(sizeof(uint16_t) * max_pairs * G * kDh);      // bf16 dQ row per (pair, head)
     L.lpart = take(sizeof(float) * max_items * 2 * kBk * kDh);   // dK and dV block per item
   } else {
     L.opart = take(sizeof(uint16_t) * max_pairs * G * kDh);
