@@ -22,16 +22,18 @@ namespace msa {
 
 namespace {
 
-constexpr int kIdxWaves = 4;
+constexpr int kIdxWaves = 8;
 constexpr int kIdxThreads = kIdxWaves * kWave;
+constexpr int kIdxLoads = kBk * 8 / kIdxThreads;  // 16-byte chunks of a staged block per thread
+constexpr int kIdxBlocksPerCU = 8 / kIdxWaves;     // two waves per SIMD
 
 // Stage key block b of k_idx into LDS: 128 rows x 8 chunks of 16 B, chunk c of row
 // j stored at chunk position c ^ ((j >> 1) & 7): the 16 rows a 16-lane LDS pass
 // reads then fall on 16 different 16-byte bank groups.
 __device__ __forceinline__ void idx_load_block(const uint16_t* __restrict__ k_idx, int64_t N,
-                                               int64_t b, int tid, uint4 (&r)[4]) {
+                                               int64_t b, int tid, uint4 (&r)[kIdxLoads]) {
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
+  for (int m = 0; m < kIdxLoads; ++m) {
     const int cidx = tid + kIdxThreads * m;
     const int key = cidx >> 3, c = cidx & 7;
     const int64_t j = b * kBk + key;
@@ -39,9 +41,9 @@ __device__ __forceinline__ void idx_load_block(const uint16_t* __restrict__ k_id
   }
 }
 
-__device__ __forceinline__ void idx_store_block(uint8_t* buf, int tid, const uint4 (&r)[4]) {
+__device__ __forceinline__ void idx_store_block(uint8_t* buf, int tid, const uint4 (&r)[kIdxLoads]) {
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
+  for (int m = 0; m < kIdxLoads; ++m) {
     const int cidx = tid + kIdxThreads * m;
     const int key = cidx >> 3, c = cidx & 7;
     *reinterpret_cast<uint4*>(buf + key * 128 + ((c ^ ((key >> 1) & 7)) << 4)) = r[m];
@@ -127,7 +129,7 @@ __device__ __forceinline__ void idx_block_max(const uint8_t* buf, const uint4 (&
 // position below (queries, blocks, keys) is relative to the sequence start j0;
 // columns and output rows are global.
 template <int LIST, int CT, bool WRITE_M, int BK>
-__global__ __launch_bounds__(kIdxThreads, 2) void index_topk_kernel(
+__global__ __launch_bounds__(kIdxThreads, kIdxBlocksPerCU) void index_topk_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx_all, int64_t N_all, int H_kv,
     int k, int64_t B, int32_t* __restrict__ block_idx, float* __restrict__ M, const int64_t* __restrict__ cu) {
   constexpr int NS = kBk / BK;  // blocks per staged 128-key tile
@@ -173,7 +175,7 @@ __global__ __launch_bounds__(kIdxThreads, 2) void index_topk_kernel(
     for (int ct = 0; ct < CT; ++ct) list[ct].init();
   }
 
-  uint4 pre[2][4];
+  uint4 pre[2][kIdxLoads];
   idx_load_block(k_idx, N, 0, tid, pre[0]);
   if (b_last >= 1) idx_load_block(k_idx, N, 1, tid, pre[1]);
   int step = 0;
