@@ -457,6 +457,34 @@ def run_decode_paged(msa, synth, dcfg, mode, steps, warmup):
             "hbm_peak_frac": round(dbytes / (dms / 1e3) / 1e9 / PEAK_HBM_GBS, 4), "steps": steps}
 
 
+def run_table1(msa, steps=5):
+    """Top-k alone from given block scores at the shapes of the pages' Top-k table
+    ([N, B, k] rows; one score row per query, causal prefix b <= i / B_k), timed with
+    events.  The table's own row count and dtype are not stated: context only."""
+    import torch
+    out = []
+    for N, B, k in ((131072, 1024, 16), (131072, 1024, 32), (524288, 4096, 16), (524288, 8192, 32)):
+        B_k = N // B
+        g = torch.Generator(device="cuda").manual_seed(N + B + k)
+        M = torch.randn((N, 1, B), generator=g, device="cuda")
+        bi = torch.empty((N, 1, k), dtype=torch.int32, device="cuda")
+        msa.msa_topk_from_scores(M, k, B_k=B_k, block_idx=bi)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            msa.msa_topk_from_scores(M, k, B_k=B_k, block_idx=bi)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / steps * 1e3
+        causal_bytes = 4 * (B * (B + 1) // 2) * B_k  # the scores each row reads
+        out.append({"N": N, "blocks": B, "k": k, "B_k": B_k, "us": round(us, 1),
+                    "GB_s": round(causal_bytes / (us / 1e6) / 1e9, 1)})
+        del M, bi
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(inp, cfg, n_rows):
     """The oracle on a uniform sample of query rows of the same prefill (all groups and heads)."""
     import numpy as np
@@ -492,6 +520,7 @@ def main(argv=None) -> int:
     ap.add_argument("--no-kl", action="store_true", help="skip the separately timed KL alignment pass")
     ap.add_argument("--no-paged", action="store_true", help="skip the paged FP8 decode measurement")
     ap.add_argument("--no-bwd", action="store_true", help="skip the separately timed backward")
+    ap.add_argument("--table1", action="store_true", help="also time Top-k alone at the pages' Top-k table shapes")
     ap.add_argument("--single-mode", action="store_true", help="skip the second input mode")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="start with plain copies of known size (for counter runs)")
@@ -556,6 +585,8 @@ def main(argv=None) -> int:
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_rows)
+    if args.table1:
+        result["topk_table1"] = run_table1(msa)
     del inp
     torch.cuda.empty_cache()
 

@@ -255,28 +255,147 @@ __global__ __launch_bounds__(kIdxThreads, kIdxBlocksPerCU) void index_topk_kerne
   }
 }
 
-template <int LIST>
+// Top-k of given block scores (the split form of the selection), one wave per
+// (query, group) row, four rows per workgroup.  Block b < b_loc of the row has the
+// 64-bit key rank_key(score, b): score first, then the lower block.  The k-1 best
+// keys are found without sorting the row:
+//  1. lane l takes blocks l, l + 64, ... (coalesced across the wave; all of the
+//     row's R chunks of 64 stay in registers) and keeps its best key.  The (k-1)-th best of
+//     the 64 lane bests, t0, is reached by k-1 distinct blocks, so every one of the
+//     row's k-1 best keys is >= t0;
+//  2. the blocks with key >= t0 are compacted into LDS in block order (ballot and
+//     lane-prefix counts); only the k-1 lanes whose best reaches t0 contribute;
+//  3. a candidate is kept iff fewer than k-1 candidates beat it; the kept ones are
+//     written in candidate order, which is ascending block order, and the local
+//     block b_loc (larger than all) follows.
+// A row with more than kTfsCap candidates (a few lanes owning most of the best
+// blocks; impossible below 17 chunks) takes k-1 rounds of wave arg-max instead.
+constexpr int kTfsCap = 512;
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ int lane_prefix(uint64_t bal) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+}
+
+template <int R>
 __global__ __launch_bounds__(256) void topk_from_scores_kernel(const float* __restrict__ M, int64_t N,
                                                                 int H_kv, int64_t B, int k, int bk,
                                                                 int32_t* __restrict__ block_idx) {
-  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (c >= N * H_kv) return;
-  const int64_t i = c / H_kv;
-  const int64_t bl = i / bk;
-  TopList<LIST> list;
-  list.init();
+  __shared__ uint64_t s_cand[4][kTfsCap];
+  __shared__ uint64_t s_lbest[4][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t c = (int64_t)blockIdx.x * 4 + w;
+  if (c >= N * H_kv) return;  // whole waves
+  const int bl = (int)((c / H_kv) / bk);
+  const int kk = k - 1;  // blocks chosen besides the local one
   const float* row = M + c * B;
-  for (int64_t b = 0; b < bl; ++b) list.offer(row[b], (int)b);
-  int cand[LIST + 1];
-#pragma unroll
-  for (int j = 0; j < LIST; ++j) cand[j] = (j < k - 1 && list.b[j] >= 0) ? list.b[j] : 0x7fffffff;
-  cand[LIST] = 0x7fffffff;
-  int32_t out[LIST + 1];
-  write_selection<LIST + 1>(cand, k, (int)bl, out);
   int32_t* orow = block_idx + c * k;
+  if (kk == 0) {
+    if (lane == 0) orow[0] = bl;
+    return;
+  }
+  if (bl <= kk) {  // every causal block is chosen
+    for (int t = lane; t < k; t += 64) orow[t] = t <= bl ? t : -1;
+    return;
+  }
+  const int nch = (bl + 63) >> 6;  // >= 1; kk < bl blocks and kk < 64 lanes hold one
+
+  // 1. The row's scores, chunk j in x[j] (nch <= R); each lane's best key.
+  float x[R];
+  uint64_t lbest = 0;
 #pragma unroll
-  for (int t = 0; t <= LIST; ++t)
-    if (t < k) orow[t] = out[t];
+  for (int g = 0; g < R; g += 16) {
+    if (g < nch) {
+#pragma unroll
+      for (int j = g; j < g + 16; ++j) {
+        const int b = j * 64 + lane;
+        x[j] = row[b < bl ? b : 0];
+      }
+#pragma unroll
+      for (int j = g; j < g + 16; ++j) {
+        const int b = j * 64 + lane;
+        const uint64_t key = b < bl ? rank_key(x[j], b) : 0ull;
+        lbest = key > lbest ? key : lbest;
+      }
+    }
+  }
+  // t0: the lane best that exactly kk-1 lane bests exceed (nonzero keys are distinct
+  // and at least kk+1 lanes hold one).
+  s_lbest[w][lane] = lbest;
+  wave_lds_sync();
+  int above = 0;
+#pragma unroll 8
+  for (int l = 0; l < 64; ++l) above += s_lbest[w][l] > lbest;
+  const uint64_t who = __ballot(above == kk - 1);
+  const int wl = __builtin_ctzll(who);
+  const uint64_t t0 = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(lbest >> 32), wl) << 32) |
+                      (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)lbest, wl);
+
+  // 2. Candidates (key >= t0) in block order.
+  int C = 0;
+  auto offer = [&](uint64_t key) {
+    const bool p = key >= t0;
+    const uint64_t bal = __ballot(p);
+    const int pos = C + lane_prefix(bal);
+    if (p && pos < kTfsCap) s_cand[w][pos] = key;
+    C += __popcll(bal);
+  };
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    if (j < nch) {
+      const int b = j * 64 + lane;
+      offer(b < bl ? rank_key(x[j], b) : 0ull);
+    }
+  }
+  wave_lds_sync();
+
+  if (C <= kTfsCap) {
+    // 3. Keep the candidates that fewer than kk others beat, in block order.
+    int S = 0;
+    for (int m0 = 0; m0 < C; m0 += 64) {
+      const int ci = m0 + lane;
+      const uint64_t key = ci < C ? s_cand[w][ci] : ~0ull;
+      int beat = 0;
+      for (int cj = 0; cj < C; ++cj) beat += s_cand[w][cj] > key;
+      const bool keep = ci < C && beat < kk;
+      const uint64_t bal = __ballot(keep);
+      if (keep) orow[S + lane_prefix(bal)] = rank_key_block(key);
+      S += __popcll(bal);
+    }
+    if (lane == 0) orow[S] = bl;  // S == kk
+  } else {
+    // kk rounds of wave arg-max, each below the previous round's key; lane t keeps
+    // round t's block, then the kk blocks are placed by their rank.
+    uint64_t prev = ~0ull;
+    int mine = 0x7fffffff;
+    for (int t = 0; t < kk; ++t) {
+      uint64_t best = 0;
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        if (j < nch) {
+          const int b = j * 64 + lane;
+          const uint64_t key = b < bl ? rank_key(x[j], b) : 0ull;
+          best = (key < prev && key > best) ? key : best;
+        }
+      }
+      prev = wave_max_u64(best);
+      if (lane == t) mine = rank_key_block(prev);
+    }
+    wave_lds_sync();
+    s_cand[w][lane] = (uint64_t)(uint32_t)mine;
+    wave_lds_sync();
+    if (lane < kk) {
+      int pos = 0;
+      for (int t = 0; t < kk; ++t) pos += (int)s_cand[w][t] < mine;
+      orow[pos] = mine;
+    }
+    if (lane == 0) orow[kk] = bl;
+  }
 }
 
 __global__ void fill_f32_kernel(float* __restrict__ p, int64_t n, float val) {
@@ -339,13 +458,18 @@ hipError_t launch_index_block_scores(const uint16_t* q_idx, const uint16_t* k_id
 
 hipError_t launch_topk_from_scores(const float* M, int64_t N, int H_kv, int64_t B, int k, int bk,
                                    int32_t* block_idx, hipStream_t stream) {
-  const int64_t grid = (N * H_kv + 255) / 256;
-  if (k <= 8)
-    topk_from_scores_kernel<7><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(M, N, H_kv, B, k, bk, block_idx);
-  else if (k <= 16)
-    topk_from_scores_kernel<15><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(M, N, H_kv, B, k, bk, block_idx);
+  const int64_t grid = (N * H_kv + 3) / 4;
+  const int64_t chunks = (N - 1) / bk / 64 + 1;  // 64-block chunks of the longest prefix
+  if (chunks > 128) return hipErrorInvalidValue;  // above the 8,192-block limit
+  const dim3 g((unsigned)grid), t(256);
+  if (chunks <= 16)
+    topk_from_scores_kernel<16><<<g, t, 0, stream>>>(M, N, H_kv, B, k, bk, block_idx);
+  else if (chunks <= 32)
+    topk_from_scores_kernel<32><<<g, t, 0, stream>>>(M, N, H_kv, B, k, bk, block_idx);
+  else if (chunks <= 64)
+    topk_from_scores_kernel<64><<<g, t, 0, stream>>>(M, N, H_kv, B, k, bk, block_idx);
   else
-    topk_from_scores_kernel<31><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(M, N, H_kv, B, k, bk, block_idx);
+    topk_from_scores_kernel<128><<<g, t, 0, stream>>>(M, N, H_kv, B, k, bk, block_idx);
   return hipGetLastError();
 }
 

@@ -237,7 +237,8 @@ msa_status_t msa_decode_paged(const void* q, const void* q_idx, const void* k_pa
  *   -inf where block b has no visible token.
  * msa_topk_from_scores — Eq. 7 on given scores: M fp32 [N, H_kv, B] (row stride B,
  *   B >= ceil(N / B_k)); only M[i][r][b] for b < i / B_k is read.  Output as for
- *   msa_index_topk.
+ *   msa_index_topk.  -inf scores rank below every finite one (ties to the lower
+ *   block as usual); with NaN scores the selection is unspecified.
  */
 msa_status_t msa_index_block_scores(const void* q_idx, const void* k_idx, int64_t N, int H_kv,
                                     int d_idx, int B_k, float* M, void* hip_stream);
