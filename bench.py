@@ -221,35 +221,42 @@ def run_prefill(msa, synth, cfg, mode, steps, warmup, with_kl=False, with_bwd=Fa
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
+    n_win = msa.msa_sparse_attn_fwd_windows(N, H_q, H_kv, k, ws.numel())
+    # Per step: index start, attention start, attention end, then 4 per query window.
+    n_ev = 3 + 4 * n_win
+
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-            msa.msa_set_profile_events(ev[2:6])
+            msa.msa_set_profile_events(ev[3:])
         msa.msa_index_topk(inp.q_idx, inp.k_idx, k, block_idx=block_idx)
         if ev is not None:
             ev[1].record(stream)
         msa.msa_sparse_attn_fwd(inp.q, inp.k, inp.v, block_idx, o=o, lse=lse, workspace=ws)
         if ev is not None:
+            ev[2].record(stream)
             msa.msa_set_profile_events(None)
 
     log(f"prefill {mode}: warmup {warmup}")
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(steps)]
     for e in evs:  # create the event handles before the timed region
         for x in e:
             x.record(stream)
     torch.cuda.synchronize()
-    log(f"prefill {mode}: timed {steps} steps")
+    log(f"prefill {mode}: timed {steps} steps ({n_win} query window(s) per attention call)")
     t0 = time.perf_counter()
     for s in range(steps):
         step(evs[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     avg = lambda a, b: sum(e[a].elapsed_time(e[b]) for e in evs) / steps
-    t_index, t_attn = avg(0, 1), avg(2, 5)
-    t_inv, t_phase1, t_combine = avg(2, 3), avg(3, 4), avg(4, 5)
+    # Phase times summed over the query windows of a call.
+    wsum = lambda p: sum(avg(3 + 4 * w + p, 4 + 4 * w + p) for w in range(n_win))
+    t_index, t_attn = avg(0, 1), avg(1, 2)
+    t_inv, t_phase1, t_combine = wsum(0), wsum(1), wsum(2)
     ms_step = wall * 1e3 / steps
 
     pairs = attended_pairs(block_idx, B_k, G)
@@ -277,7 +284,7 @@ def run_prefill(msa, synth, cfg, mode, steps, warmup, with_kl=False, with_bwd=Fa
         "flop_index": f_index, "flop_main": f_main, "flop_eq12": f_eq12,
         "ms_index_topk": round(t_index, 4), "ms_sparse_attn_fwd": round(t_attn, 4),
         "ms_inverse_index": round(t_inv, 4), "ms_kvouter_phase1": round(t_phase1, 4),
-        "ms_combine": round(t_combine, 4),
+        "ms_combine": round(t_combine, 4), "query_windows": n_win,
         "index_tflops": round(f_index / (t_index / 1e3) / 1e12, 2),
         "phase1_tflops": round(f_main / (t_phase1 / 1e3) / 1e12, 2),
         "phase1_algorithmic_bytes": p1_bytes,
@@ -574,13 +581,15 @@ def main(argv=None) -> int:
         "prefill": pre,
     }
     # The dominant kernel is the KV-outer phase 1; it is bound by its HBM bytes
-    # (about 126 FLOP per byte, below the bf16 ridge of about 312).
+    # (about 126 FLOP per byte, below the bf16 ridge of about 312).  It runs once per
+    # query window: bytes per launch / average launch time = total bytes / total time.
     gbs = pre["phase1_algorithmic_bytes"] / (pre["ms_kvouter_phase1"] / 1e3) / 1e9
     traffic = recorded_traffic(args.mode)
     result["roofline"] = {"kernel": "attn_kvouter_kernel", "bound": "hbm", "achieved": round(gbs, 1),
                           "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                           "traffic": traffic,
                           "algorithmic_bytes": pre["phase1_algorithmic_bytes"],
+                          "launches_per_step": pre["query_windows"],
                           "mfma_frac": round(pre["phase1_tflops"] / PEAK_BF16_TFLOPS, 4)}
 
     if not args.no_cpu_baseline:

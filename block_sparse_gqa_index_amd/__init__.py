@@ -35,6 +35,7 @@ _SIGS = {
     "msa_index_topk": ([_P, _P, _I64, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P], _I32),
     "msa_sparse_attn_fwd_workspace": ([_I64, _I32, _I32, _I32, _I32, _I32], _SZ),
     "msa_sparse_attn_fwd_workspace_min": ([_I64, _I32, _I32, _I32, _I32, _I32], _SZ),
+    "msa_sparse_attn_fwd_windows": ([_I64, _I32, _I32, _I32, _I32, _I32, _SZ], _I64),
     "msa_sparse_attn_fwd": ([_P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _F32, _P, _P, _P, _SZ, _P], _I32),
     "msa_decode_workspace": ([_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I64], _SZ),
     "msa_decode": ([_P, _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _F32, _P, _P, _P, _P,
@@ -155,6 +156,15 @@ def msa_sparse_attn_fwd_workspace(N: int, H_q: int, H_kv: int, k: int, d_h: int 
                                   minimum: bool = False) -> int:
     fn = _lib.msa_sparse_attn_fwd_workspace_min if minimum else _lib.msa_sparse_attn_fwd_workspace
     return int(fn(N, H_q, H_kv, d_h, B_k, k))
+
+
+def msa_sparse_attn_fwd_windows(N: int, H_q: int, H_kv: int, k: int, ws_bytes: int, d_h: int = 128,
+                                B_k: int = 128) -> int:
+    """Query windows a msa_sparse_attn_fwd call runs with a workspace of ws_bytes."""
+    n = int(_lib.msa_sparse_attn_fwd_windows(N, H_q, H_kv, d_h, B_k, k, ws_bytes))
+    if n < 0:
+        raise ValueError("unsupported shape or workspace below the minimum")
+    return n
 
 
 def msa_sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_idx: torch.Tensor,
@@ -392,21 +402,22 @@ def msa_decode_paged(q: torch.Tensor, q_idx: torch.Tensor, k_pages: torch.Tensor
 
 
 def msa_set_profile_events(events=None) -> None:
-    """Record 4 caller-owned events at the phase boundaries of later msa_sparse_attn_fwd
-    calls on this thread (inverse index, KV-outer phase 1, combine, end); None clears.
+    """Record caller-owned events at the phase boundaries of later msa_sparse_attn_fwd
+    calls on this thread: 4 per query window (inverse index, KV-outer phase 1,
+    combine, end), for the first len(events) // 4 windows; None clears.
 
-    Takes torch.cuda.Event objects created with enable_timing=True.  Each event is
-    recorded once here on the current stream so that its handle exists."""
+    Takes torch.cuda.Event objects created with enable_timing=True.  An event whose
+    handle does not exist yet is recorded once here on the current stream."""
     if events is None:
         _check(_lib.msa_set_profile_events(None, 0), "msa_set_profile_events")
         return
-    if len(events) != 4:
-        raise ValueError("msa_set_profile_events takes 4 events")
+    if len(events) == 0 or len(events) % 4 != 0:
+        raise ValueError("msa_set_profile_events takes 4 events per query window")
     for e in events:
         if not e.cuda_event:
             e.record()
-    arr = (_P * 4)(*[e.cuda_event for e in events])
-    _check(_lib.msa_set_profile_events(arr, 4), "msa_set_profile_events")
+    arr = (_P * len(events))(*[e.cuda_event for e in events])
+    _check(_lib.msa_set_profile_events(arr, len(events)), "msa_set_profile_events")
 
 
 def raw():

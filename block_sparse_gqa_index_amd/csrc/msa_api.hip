@@ -11,8 +11,9 @@ namespace {
 
 thread_local char g_last_error[512] = "";
 // Caller-owned events recorded at the phase boundaries of msa_sparse_attn_fwd.
-thread_local hipEvent_t g_phase_events[4] = {nullptr, nullptr, nullptr, nullptr};
-thread_local bool g_phase_events_on = false;
+constexpr int kMaxProfileWindows = 1024;
+thread_local hipEvent_t g_phase_events[4 * kMaxProfileWindows] = {};
+thread_local int g_phase_windows = 0;  // windows with events; 0 = hook off
 
 msa_status_t fail(msa_status_t st, const char* fmt, ...) {
   va_list ap;
@@ -167,12 +168,13 @@ static msa_status_t attn_run(const void* q, const void* k, const void* v, const 
   const int64_t W = window_for_bytes(N, B, H_q, H_kv, k_sel, avail);
   const msa::AttnWorkspace L = msa::attn_workspace_layout(W, H_q, H_kv, k_sel, B);
   const int cus = num_cus();
-  for (int64_t w0 = 0; w0 < N; w0 += W) {
+  int64_t wi = 0;
+  for (int64_t w0 = 0; w0 < N; w0 += W, ++wi) {
     const int64_t Wn = (N - w0 < W) ? N - w0 : W;
     hipError_t e = msa::launch_sparse_attn_window(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), block_idx,
         N, B, si, B_k, H_q, H_kv, k_sel, scale, w0, Wn, cus, o, lse, ws + S.total, L, stream,
-        g_phase_events_on ? g_phase_events : nullptr);
+        wi < g_phase_windows ? g_phase_events + 4 * wi : nullptr);
     if (e != hipSuccess) return hip_fail(e, "sparse_attn launch");
   }
   return ok();
@@ -203,6 +205,14 @@ size_t msa_sparse_attn_fwd_workspace(int64_t N, int H_q, int H_kv, int d_h, int 
 size_t msa_sparse_attn_fwd_workspace_min(int64_t N, int H_q, int H_kv, int d_h, int B_k, int k) {
   if (check_attn_shape(N, H_q, H_kv, d_h, B_k, k) != MSA_OK || N == 0) return 0;
   return attn_workspace_bytes(N, (N + B_k - 1) / B_k, msa::SeqTables{}, H_q, H_kv, k, true);
+}
+
+int64_t msa_sparse_attn_fwd_windows(int64_t N, int H_q, int H_kv, int d_h, int B_k, int k, size_t ws_bytes) {
+  if (check_attn_shape(N, H_q, H_kv, d_h, B_k, k) != MSA_OK) return -1;
+  if (N == 0) return 0;
+  if (ws_bytes < msa_sparse_attn_fwd_workspace_min(N, H_q, H_kv, d_h, B_k, k)) return -1;
+  const int64_t W = window_for_bytes(N, (N + B_k - 1) / B_k, H_q, H_kv, k, ws_bytes);
+  return (N + W - 1) / W;
 }
 
 msa_status_t msa_sparse_attn_fwd(const void* q, const void* k, const void* v, const int32_t* block_idx, int64_t N,
@@ -433,14 +443,16 @@ msa_status_t msa_sparse_attn_bwd(const void* q, const void* k, const void* v, co
 
 msa_status_t msa_set_profile_events(void* const* events, int n) {
   if (n == 0) {
-    g_phase_events_on = false;
+    g_phase_windows = 0;
     return ok();
   }
-  if (n != 4 || !events) return fail(MSA_ERR_INVALID_ARG, "msa_set_profile_events takes 0 or 4 events");
-  for (int i = 0; i < 4; ++i)
+  if (n < 0 || n % 4 != 0 || n > 4 * kMaxProfileWindows || !events)
+    return fail(MSA_ERR_INVALID_ARG, "msa_set_profile_events takes 0 or 4 * m events, 1 <= m <= %d",
+                kMaxProfileWindows);
+  for (int i = 0; i < n; ++i)
     if (!events[i]) return fail(MSA_ERR_INVALID_ARG, "null event handle");
-  for (int i = 0; i < 4; ++i) g_phase_events[i] = static_cast<hipEvent_t>(events[i]);
-  g_phase_events_on = true;
+  for (int i = 0; i < n; ++i) g_phase_events[i] = static_cast<hipEvent_t>(events[i]);
+  g_phase_windows = n / 4;
   return ok();
 }
 

@@ -89,6 +89,10 @@ msa_status_t msa_index_topk(const void* q_idx, const void* k_idx, int64_t N, int
  */
 size_t msa_sparse_attn_fwd_workspace(int64_t N, int H_q, int H_kv, int d_h, int B_k, int k);
 size_t msa_sparse_attn_fwd_workspace_min(int64_t N, int H_q, int H_kv, int d_h, int B_k, int k);
+/* The number of query windows msa_sparse_attn_fwd runs for this shape with a
+ * workspace of ws_bytes (1 when the workspace covers all N queries at once); 0 for
+ * N == 0; -1 for an unsupported shape or ws_bytes below the minimum.  Host-only. */
+int64_t msa_sparse_attn_fwd_windows(int64_t N, int H_q, int H_kv, int d_h, int B_k, int k, size_t ws_bytes);
 msa_status_t msa_sparse_attn_fwd(const void* q, const void* k, const void* v,
                                  const int32_t* block_idx, int64_t N, int H_q, int H_kv, int d_h,
                                  int B_k, int k_sel, float scale, float* o, float* lse, void* ws,
@@ -245,13 +249,14 @@ msa_status_t msa_index_block_scores(const void* q_idx, const void* k_idx, int64_
 msa_status_t msa_topk_from_scores(const float* M, int64_t N, int H_kv, int64_t B, int B_k, int k,
                                   int32_t* block_idx, void* hip_stream);
 
-/* Measurement hook, not part of the method: while set, each msa_sparse_attn_fwd call
- * made on this host thread records, on its stream and for every query window,
- * events[0] before the inverse index (counts, scan, scatter), events[1] before the
- * KV-outer phase-1 kernel, events[2] before the combine and events[3] after it.
- * After a call the events therefore bracket the phases of its last window.
+/* Measurement hook, not part of the method: while set, each msa_sparse_attn_fwd or
+ * msa_sparse_attn_fwd_varlen call made on this host thread records, on its stream,
+ * for its query window w < n / 4: events[4w] before the inverse index (counts,
+ * scan, scatter), events[4w+1] before the KV-outer phase-1 kernel, events[4w+2]
+ * before the combine and events[4w+3] after it.  Later windows record nothing
+ * (msa_sparse_attn_fwd_windows gives a call's window count).
  *   events  n hipEvent_t handles owned by the caller; they must stay valid while set.
- *   n       4 to set, 0 to clear (events is then ignored).
+ *   n       4 * m with 1 <= m <= 1024 to set, 0 to clear (events is then ignored).
  * Returns MSA_ERR_INVALID_ARG for any other n or a null handle (the previous setting
  * is kept).  Host-only; no device work. */
 msa_status_t msa_set_profile_events(void* const* events, int n);

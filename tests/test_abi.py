@@ -129,7 +129,27 @@ def test_profile_events_hook_validates(lib):
     import ctypes as C
     arr = (C.c_void_p * 4)(0x10, 0x20, None, 0x40)
     assert raw.msa_set_profile_events(arr, 4) == lib.MSA_ERR_INVALID_ARG  # null handle
+    arr8 = (C.c_void_p * 8)(*range(0x10, 0x90, 0x10))
+    assert raw.msa_set_profile_events(arr8, 6) == lib.MSA_ERR_INVALID_ARG  # not 4 per window
+    assert raw.msa_set_profile_events(arr8, 4 * 1025) == lib.MSA_ERR_INVALID_ARG
     assert raw.msa_set_profile_events(None, 0) == lib.MSA_OK
+
+
+def test_window_count_query(lib):
+    raw = lib.raw()
+    N, H_q, H_kv, k = 131072, 64, 8, 16
+    full = raw.msa_sparse_attn_fwd_workspace(N, H_q, H_kv, 128, 128, k)
+    small = raw.msa_sparse_attn_fwd_workspace_min(N, H_q, H_kv, 128, 128, k)
+    assert raw.msa_sparse_attn_fwd_windows(N, H_q, H_kv, 128, 128, k, full) == 1
+    assert raw.msa_sparse_attn_fwd_windows(N, H_q, H_kv, 128, 128, k, small) == N // 128
+    assert raw.msa_sparse_attn_fwd_windows(N, H_q, H_kv, 128, 128, k, small - 1) == -1
+    half = raw.msa_sparse_attn_fwd_windows(N, H_q, H_kv, 128, 128, k, full // 2 + small)
+    assert 2 <= half <= 3
+    assert raw.msa_sparse_attn_fwd_windows(0, H_q, H_kv, 128, 128, k, 0) == 0
+    assert raw.msa_sparse_attn_fwd_windows(N, H_q, H_kv, 64, 128, k, full) == -1  # unsupported d_h
+    # 1M tokens under the default workspace run in several windows.
+    big = raw.msa_sparse_attn_fwd_workspace(1 << 20, H_q, H_kv, 128, 128, k)
+    assert raw.msa_sparse_attn_fwd_windows(1 << 20, H_q, H_kv, 128, 128, k, big) > 1
 
 
 def test_binding_fails_loudly_without_library(tmp_path):
