@@ -186,6 +186,40 @@ def test_query_windows_and_reruns_are_bitwise_identical(msa):
     assert torch.equal(o1, o3) and torch.equal(l1, l3)
 
 
+def test_profile_events_per_query_window(msa):
+    """The measurement hook records 4 events per query window for as many windows as
+    it was given; a windowed call's phases then add up to its whole duration."""
+    N, H_q, H_kv, k = 3000, 16, 2, 6
+    inp = _inputs(N, H_q, H_kv, k, seed=14, needles=2)
+    bi = msa.msa_index_topk(inp.q_idx, inp.k_idx, k)
+    wmin = msa.msa_sparse_attn_fwd_workspace(N, H_q, H_kv, k, minimum=True)
+    ws = torch.empty(wmin, dtype=torch.uint8, device=DEV)
+    n_win = msa.msa_sparse_attn_fwd_windows(N, H_q, H_kv, k, wmin)
+    assert n_win == (N + 127) // 128
+    assert msa.msa_sparse_attn_fwd_windows(N, H_q, H_kv, k,
+                                           msa.msa_sparse_attn_fwd_workspace(N, H_q, H_kv, k)) == 1
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4 * n_win)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    msa.msa_set_profile_events(ev)
+    try:
+        start.record(stream)
+        o, lse = msa.msa_sparse_attn_fwd(inp.q, inp.k, inp.v, bi, workspace=ws)
+        end.record(stream)
+    finally:
+        msa.msa_set_profile_events(None)
+    torch.cuda.synchronize()
+    phases = [ev[4 * w + p].elapsed_time(ev[4 * w + p + 1]) for w in range(n_win) for p in range(3)]
+    assert all(t >= 0 for t in phases)
+    gaps = [ev[4 * w + 3].elapsed_time(ev[4 * w + 4]) for w in range(n_win - 1)]
+    assert all(t >= 0 for t in gaps)  # windows run in order on the stream
+    total = start.elapsed_time(end)
+    assert sum(phases) <= total * 1.05 + 0.01
+    o_ref, l_ref = msa.msa_sparse_attn_fwd(inp.q, inp.k, inp.v, bi)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(lse, l_ref)
+
+
 def test_empty_inputs(msa):
     z = torch.empty((0, 2, 64), dtype=torch.bfloat16, device=DEV)
     bi = msa.msa_index_topk(z, torch.empty((0, 64), dtype=torch.bfloat16, device=DEV), 4)
