@@ -9,16 +9,19 @@
 //   dV = P^T dO,  dS = P * (dO V^T - D),  dQ = scale dS K,  dK = scale dS^T Q.
 //
 // Work decomposition on gfx950.  The forward's inverse index is rebuilt: for every
-// (group, block) list, items of at most 256 (query, slot) pairs.  A workgroup
-// stages the block's K, V (rows) and K^T in LDS once per item and walks the item
-// in sub-chunks of 64 MFMA rows ((64 / G) queries x G heads), with the q and dO rows
-// of the sub-chunk in LDS both row-major and transposed.  Wave w owns keys
-// 32w .. 32w+31 of the block:
+// (group, block) list, items of at most 256 (query, slot) pairs.  A workgroup of
+// eight waves (two per SIMD, so one wave's LDS and memory waits overlap the other's
+// work) stages the block's K, V (rows) and K^T in LDS once per item and walks the
+// item in sub-chunks of 64 MFMA rows ((64 / G) queries x G heads), with the q and dO
+// rows of the sub-chunk in LDS both row-major and transposed.  Wave w owns keys
+// 32(w % 4) .. +31 of the block and dims 64(w / 4) .. +63 of its dK and dV:
 //   S = Q K^T and dP = dO V^T on 32x32x16 MFMAs give, per lane, one key (the lane)
-//   and 32 rows (registers), so P and dS are formed in registers;
+//   and 32 rows (registers), so P and dS are formed in registers (both waves of a
+//   key slice compute them, identically: the matrix cores have room for it, and it
+//   halves the dK/dV accumulators a wave holds);
 //   dV += P^T dO and dK += dS^T Q use P and dS directly as MFMA operands, and
 //   accumulate in registers over the whole item;
-//   dS goes to LDS, and each wave then computes dQ for 32 rows x 64 dims over all
+//   dS goes to LDS, and each wave then computes dQ for 32 rows x 32 dims over all
 //   128 keys (dS K, with K^T as the operand).
 // dQ leaves as one bf16 partial row per (query, slot, head), summed over the slots
 // in fp32 by a second kernel; dK and dV leave as one fp32 partial block per item, summed in
@@ -33,7 +36,7 @@ namespace msa {
 
 namespace {
 
-constexpr int kBwdThreads = 256;
+constexpr int kBwdThreads = 512;
 constexpr int kBwdRows = 64;  // MFMA rows per sub-chunk
 constexpr int kBwdPairRegs = 4;  // an item holds at most 256 pairs: 4 registers of 64 lanes
 
@@ -47,8 +50,6 @@ __device__ __forceinline__ int bwd_pair_at(const int (&ip)[kBwdPairRegs], int id
   }
   return v;
 }
-
-__device__ __forceinline__ uint16_t to_bf16(float x) { return (uint16_t)(pack_bf16x2(x, 0.f) & 0xffffu); }
 
 __device__ __forceinline__ u32x4_t pack8(const float* x) {
   return u32x4_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
@@ -95,6 +96,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
+  const int ks = wave & 3, dh = wave >> 2;  // key slice, dK/dV dim half
   const int h = lane >> 5, l32 = lane & 31;
   const int H_q = H_kv * G;
   const int n_items = *n_items_ptr;
@@ -112,40 +114,46 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
     for (int k = 0; k < kBwdPairRegs; ++k) ip[k] = pairs[start + (64 * k + lane < cnt ? 64 * k + lane : cnt - 1)];
     __syncthreads();  // the previous item's LDS reads are done
     {
-      int stid = tid;
+      // Threads 0..255 stage K and V rows, threads 256..511 K^T.
+      int stid = tid & 255;
       asm volatile("" : "+v"(stid));
       const int64_t tok0 = b * kBk;
       const int nvalid = (N - tok0 < kBk) ? (int)(N - tok0) : kBk;
       const int64_t base = tok0 * H_kv * kDh + r * kDh;
-      stage_k(kp + base, H_kv * kDh, nvalid, Ks, stid);
-      stage_k(vp + base, H_kv * kDh, nvalid, Vs, stid);
-      stage_v(kp + base, H_kv * kDh, nvalid, Kt, stid);
+      if (tid < 256) {
+        stage_k(kp + base, H_kv * kDh, nvalid, Ks, stid);
+        stage_k(vp + base, H_kv * kDh, nvalid, Vs, stid);
+      } else {
+        stage_v(kp + base, H_kv * kDh, nvalid, Kt, stid);
+      }
     }
 
-    f32x16_t dv_acc[4], dk_acc[4];
+    f32x16_t dv_acc[2], dk_acc[2];
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) dv_acc[dt] = dk_acc[dt] = f32x16_t{};
-    const int koff = 32 * wave + swap23(l32);  // this lane's key (as S/dP column)
+    for (int dt = 0; dt < 2; ++dt) dv_acc[dt] = dk_acc[dt] = f32x16_t{};
 
     // Row l of a sub-chunk (l = 0..63) is (pair cb + l / G, head l % G); lane l keeps
-    // that row's pair, lse and D for the others to read by shuffles.  Thread t loads
-    // 16-byte chunk t & 15 of rows (t >> 4) + 16j of q and dO.  Both are fetched one
+    // that row's pair (-1: past the item's end), lse, D and last visible key offset
+    // within the block (-1: none) for the others to read by shuffles.  Thread t loads
+    // 16-byte chunk t & 15 of rows (t >> 4) + 32j of q and dO.  Both are fetched one
     // sub-chunk ahead, so their latency hides under the previous sub-chunk's work.
-    u32x4_t qv[4], gv[4];
-    int my_pr;
-    bool my_valid;
+    u32x4_t qv[2], gv[2];
+    int my_prv, my_lim;
     float my_l2, my_D;
     auto fetch = [&](int cbase) {
       const int my_idx = cbase + lane / G;
-      my_valid = my_idx < cnt;
-      my_pr = bwd_pair_at(ip, my_valid ? my_idx : cnt - 1);
+      const bool my_valid = my_idx < cnt;
+      const int my_pr = bwd_pair_at(ip, my_valid ? my_idx : cnt - 1);
       const int64_t my_row = (w0 + (my_pr >> 5)) * H_q + r * G + lane % G;
       my_l2 = lse[my_row] * kLog2e;
       my_D = Drow[my_row];
+      my_prv = my_valid ? my_pr : -1;
+      // A listed pair's query sees at least key 0 of the block: 0 <= lim.
+      my_lim = my_valid ? (int)(w0 + (my_pr >> 5) - b * kBk) : -1;
       const int c = tid & 15;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int rho = (tid >> 4) + 16 * j;
+      for (int j = 0; j < 2; ++j) {
+        const int rho = (tid >> 4) + 32 * j;
         const int idx = cbase + rho / G;
         const int pr = bwd_pair_at(ip, idx < cnt ? idx : cnt - 1);
         const int64_t src = ((w0 + (pr >> 5)) * H_q + r * G + rho % G) * kDh + c * 8;
@@ -160,17 +168,16 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
       {
         const int c = tid & 15;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int rho = (tid >> 4) + 16 * j;
+        for (int j = 0; j < 2; ++j) {
+          const int rho = (tid >> 4) + 32 * j;
           *reinterpret_cast<u32x4_t*>(Qs + rho * 256 + ((c ^ (rho & 15)) << 4)) = qv[j];
           *reinterpret_cast<u32x4_t*>(dOs + rho * 256 + ((c ^ (rho & 15)) << 4)) = gv[j];
         }
       }
-      const int cur_pr = my_pr;
-      const bool cur_valid = my_valid;
+      const int cur_prv = my_prv, cur_lim = my_lim;
       const float cur_l2 = my_l2, cur_D = my_D;
       __syncthreads();  // rows staged (and, on the first sub-chunk, the block)
-      {
+      if (tid < 256) {
         // Transposes: threads 0..127 build Qt, 128..255 dOt.  Thread (pg, dc) moves
         // positions 8pg .. 8pg+7 (row (pos & ~31) | swap23(pos & 31)) x dims 8dc .. +7.
         const int tt = tid & 127;
@@ -199,10 +206,22 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
       __syncthreads();  // transposes done
       fetch(cb + kQS < cnt ? cb + kQS : cb);  // the next sub-chunk (past the end: reread, unused)
 
+      // Lane-derived LDS addresses are recomputed in each phase from a copy of the
+      // lane id the compiler cannot see through, rather than held across the loop.
+      auto lane_v = [&]() {
+        int x = lane;
+        asm volatile("" : "+v"(x));
+        return x;
+      };
       // S and dP: element v of row tile rt is row rt*32 + 8(v/4) + 4h + v%4, key koff.
-      float P[2][16], dS[2][16];
+      // P and dS leave this phase as bf16 MFMA operands: Pp[rt][s2] holds elements
+      // 8 s2 .. 8 s2 + 7.
+      u32x4_t Pp[2][2], dSp[2][2];
       {
-        const int krow = 32 * wave + l32;
+        const int lv = lane_v();
+        const int h = lv >> 5, l32 = lv & 31;
+        const int krow = 32 * ks + l32;
+        const int koff = 32 * ks + swap23(l32);
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
           f32x16_t sacc = f32x16_t{}, pacc = f32x16_t{};
@@ -217,16 +236,20 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
             const u32x4_t bv = *reinterpret_cast<const u32x4_t*>(Vs + krow * 256 + ((c ^ (krow & 15)) << 4));
             pacc = mfma_32x32x16(as_bf16x8(ag), as_bf16x8(bv), pacc);
           }
+          float P[16], dS[16];
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int rv = rt * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
             const float l2 = __shfl(cur_l2, rv), Dv = __shfl(cur_D, rv);
-            const int il = __shfl(cur_pr, rv) >> 5;
-            const bool vv = __shfl((int)cur_valid, rv) != 0;
-            const bool in = vv && b * kBk + koff <= w0 + il;  // causal, and a real row
+            const bool in = koff <= __shfl(cur_lim, rv);  // a real row, and causal
             const float p = in ? __builtin_amdgcn_exp2f(fmaf(sacc[v], scale_log2, -l2)) : 0.f;
-            P[rt][v] = p;
-            dS[rt][v] = p * (pacc[v] - Dv);
+            P[v] = p;
+            dS[v] = p * (pacc[v] - Dv);
+          }
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            Pp[rt][s2] = pack8(&P[8 * s2]);
+            dSp[rt][s2] = pack8(&dS[8 * s2]);
           }
           __builtin_amdgcn_sched_barrier(0);  // one row tile's accumulators at a time
         }
@@ -235,16 +258,19 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
       // key 32w + swap23(i)); k-slot (h, j) of step (rt, s2) is row
       // rt*32 + 8(2 s2 + j/4) + 4h + j%4, the transposed tiles' position
       // rt*32 + 16 s2 + 8h + j.
+      {
+      const int lv = lane_v();
+      const int h = lv >> 5, l32 = lv & 31;
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-          const u32x4_t ap = pack8(&P[rt][8 * s2]);
-          const u32x4_t ad = pack8(&dS[rt][8 * s2]);
+          const u32x4_t ap = Pp[rt][s2];
+          const u32x4_t ad = dSp[rt][s2];
           const int ch = 4 * rt + 2 * s2 + h;
 #pragma unroll
-          for (int dt = 0; dt < 4; ++dt) {
-            const int d = dt * 32 + l32;
+          for (int dt = 0; dt < 2; ++dt) {
+            const int d = 64 * dh + dt * 32 + l32;
             const u32x4_t bo = *reinterpret_cast<const u32x4_t*>(dOt + d * 128 + ((ch ^ (d & 7)) << 4));
             dv_acc[dt] = mfma_32x32x16(as_bf16x8(ap), as_bf16x8(bo), dv_acc[dt]);
             const u32x4_t bq = *reinterpret_cast<const u32x4_t*>(Qt + d * 128 + ((ch ^ (d & 7)) << 4));
@@ -253,60 +279,70 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      }
       __syncthreads();  // every wave is done with Qs: dS replaces it
       // dS rows in Qs: row-major, keys in natural order, chunk kc at kc ^ (row & 15).
+      // The two waves of a key slice hold the same dS; each stores one row tile.
+      {
+        const int lv = lane_v();
+        const int h = lv >> 5;
+        const int koff = 32 * ks + swap23(lv & 31);
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
+        for (int rt = 0; rt < 2; ++rt) {
+          if (rt != dh) continue;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int rv = rt * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-          *reinterpret_cast<uint16_t*>(Qs + rv * 256 + ((((koff >> 3) ^ (rv & 15))) << 4) + (koff & 7) * 2) =
-              to_bf16(dS[rt][v]);
+          for (int v = 0; v < 16; ++v) {
+            const int rv = rt * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+            const uint32_t w2 = dSp[rt][v >> 3][(v & 7) >> 1];
+            *reinterpret_cast<uint16_t*>(Qs + rv * 256 + ((((koff >> 3) ^ (rv & 15))) << 4) + (koff & 7) * 2) =
+                (uint16_t)((v & 1) ? (w2 >> 16) : (w2 & 0xffffu));
+          }
         }
       }
       __syncthreads();  // dS complete
       {
-        // dQ rows 32(w & 1) + 0..31, dims 64(w >> 1) + 0..63, over all 128 keys.
+        // dQ^T = K^T dS^T over all 128 keys: wave w takes dQ rows 32(w & 1) + 0..31
+        // (MFMA columns, one per lane) and dims 32(w >> 1) + 0..31 (MFMA rows; lane l
+        // reads K^T row swap23(l), so a lane's 16 values are the two runs of 8
+        // consecutive dims 8h .. 8h+7 and 16+8h .. 16+8h+7 of its dQ row).
+        const int lv = lane_v();
+        const int h = lv >> 5, l32 = lv & 31;
         const int row = 32 * (wave & 1) + l32;
-        f32x16_t qacc[2] = {f32x16_t{}, f32x16_t{}};
+        const int d = 32 * (wave >> 1) + swap23(l32);
+        f32x16_t qacc = f32x16_t{};
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
           const int kc = 2 * t + h;
-          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(Qs + row * 256 + ((kc ^ (row & 15)) << 4));
-#pragma unroll
-          for (int dt = 0; dt < 2; ++dt) {
-            const int d = 64 * (wave >> 1) + 32 * dt + l32;
-            const u32x4_t bk = *reinterpret_cast<const u32x4_t*>(Kt + d * 256 + ((kc ^ (d & 15)) << 4));
-            qacc[dt] = mfma_32x32x16(as_bf16x8(a), as_bf16x8(bk), qacc[dt]);
-          }
+          const u32x4_t ak = *reinterpret_cast<const u32x4_t*>(Kt + d * 256 + ((kc ^ (d & 15)) << 4));
+          const u32x4_t bs = *reinterpret_cast<const u32x4_t*>(Qs + row * 256 + ((kc ^ (row & 15)) << 4));
+          qacc = mfma_32x32x16(as_bf16x8(ak), as_bf16x8(bs), qacc);
         }
-        // element v: row 32(w & 1) + 8(v/4) + 4h + v%4, dim 64(w >> 1) + 32dt + l32
+        const int pr = __shfl(cur_prv, row);
+        if (pr >= 0) {
+          const int64_t prow = (((int64_t)(pr >> 5) * H_kv + r) * kk + (pr & 31)) * G + row % G;
+          uint16_t* dst = dq_part + prow * kDh + 32 * (wave >> 1) + 8 * h;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int rv = 32 * (wave & 1) + 8 * (v >> 2) + 4 * h + (v & 3);
-          const int pr = __shfl(cur_pr, rv);
-          const bool vv = __shfl((int)cur_valid, rv) != 0;
-          if (vv) {
-            const int64_t prow = (((int64_t)(pr >> 5) * H_kv + r) * kk + (pr & 31)) * G + rv % G;
+          for (int run = 0; run < 2; ++run) {
+            float x[8];
 #pragma unroll
-            for (int dt = 0; dt < 2; ++dt)
-              dq_part[prow * kDh + 64 * (wave >> 1) + 32 * dt + l32] = to_bf16(qacc[dt][v] * scale);
+            for (int e = 0; e < 8; ++e) x[e] = qacc[8 * run + e] * scale;
+            *reinterpret_cast<u32x4_t*>(dst + 16 * run) = pack8(x);
           }
         }
       }
       __syncthreads();  // the sub-chunk's LDS tiles may be replaced
     }
     // The item's dK (scaled) and dV: element v of lane (l32, h) is key
-    // 32w + swap23(8(v/4) + 4h + v%4), dim 32dt + l32.
+    // 32(w % 4) + swap23(8(v/4) + 4h + v%4), dim 64(w / 4) + 32dt + l32.
     float* kpart = dkv_part + item * 2 * (kBk * kDh);
     float* vpart = kpart + kBk * kDh;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
+    for (int dt = 0; dt < 2; ++dt) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int key = 32 * wave + swap23(8 * (v >> 2) + 4 * h + (v & 3));
-        kpart[key * kDh + 32 * dt + l32] = dk_acc[dt][v] * scale;
-        vpart[key * kDh + 32 * dt + l32] = dv_acc[dt][v];
+        const int key = 32 * ks + swap23(8 * (v >> 2) + 4 * h + (v & 3));
+        kpart[key * kDh + 64 * dh + 32 * dt + l32] = dk_acc[dt][v] * scale;
+        vpart[key * kDh + 64 * dh + 32 * dt + l32] = dv_acc[dt][v];
       }
     }
   }
