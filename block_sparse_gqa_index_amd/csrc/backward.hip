@@ -29,6 +29,8 @@
 // bitwise reproducible; dK and dV sum a list's rows in the order the inverse index
 // placed its pairs (decided by its atomic counters), so they can differ between runs
 // by fp32 rounding.
+#include <utility>
+
 #include "msa_device.h"
 #include "msa_kernels.h"
 
@@ -54,6 +56,34 @@ __device__ __forceinline__ int bwd_pair_at(const int (&ip)[kBwdPairRegs], int id
 __device__ __forceinline__ u32x4_t pack8(const float* x) {
   return u32x4_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
                  pack_bf16x2(x[6], x[7])};
+}
+
+// Per-row values of a 64-row sub-chunk are kept one row per lane, row R on lane
+// bwd_row_lane(R): bit 2 of R picks the lane half and the other five bits the lane
+// within it.  The S/dP layout needs, in lane half h, rows whose bit 2 is h, so each
+// such read is a broadcast of one lane within the reader's own half.
+__device__ __forceinline__ int bwd_row_lane(int R) { return (((R >> 2) & 1) << 5) | (R & 3) | ((R >> 3) << 2); }
+__device__ __forceinline__ int bwd_lane_row(int L) { return (L & 3) | (((L >> 5) & 1) << 2) | (((L >> 2) & 7) << 3); }
+
+// Broadcast lane M of each 32-lane half (ds_swizzle, bit-mask mode: and 0, or M).
+template <int M>
+__device__ __forceinline__ int half_bcast(int x) {
+  static_assert(M >= 0 && M < 32, "lane within a half");
+  return __builtin_amdgcn_ds_swizzle(x, M << 5);
+}
+template <int M>
+__device__ __forceinline__ float half_bcast(float x) {
+  return __int_as_float(half_bcast<M>(__float_as_int(x)));
+}
+
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>), in order.
+template <class F, int... V>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, V...>) {
+  (f(std::integral_constant<int, V>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // D[row] = <dO[row], o[row]> over the 128 dims, 16 lanes per row.
@@ -141,10 +171,11 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
     int my_prv, my_lim;
     float my_l2, my_D;
     auto fetch = [&](int cbase) {
-      const int my_idx = cbase + lane / G;
+      const int my_r = bwd_lane_row(lane);  // the row this lane describes
+      const int my_idx = cbase + my_r / G;
       const bool my_valid = my_idx < cnt;
       const int my_pr = bwd_pair_at(ip, my_valid ? my_idx : cnt - 1);
-      const int64_t my_row = (w0 + (my_pr >> 5)) * H_q + r * G + lane % G;
+      const int64_t my_row = (w0 + (my_pr >> 5)) * H_q + r * G + my_r % G;
       my_l2 = lse[my_row] * kLog2e;
       my_D = Drow[my_row];
       my_prv = my_valid ? my_pr : -1;
@@ -237,15 +268,18 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
             pacc = mfma_32x32x16(as_bf16x8(ag), as_bf16x8(bv), pacc);
           }
           float P[16], dS[16];
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int rv = rt * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-            const float l2 = __shfl(cur_l2, rv), Dv = __shfl(cur_D, rv);
-            const bool in = koff <= __shfl(cur_lim, rv);  // a real row, and causal
+          // Element v: row rt*32 + 8(v/4) + 4h + v%4, held by lane v + 16 rt of this
+          // lane's half.
+          static_for<16>([&](auto VC) {
+            constexpr int v = decltype(VC)::value;
+            const float l2 = rt ? half_bcast<v + 16>(cur_l2) : half_bcast<v>(cur_l2);
+            const float Dv = rt ? half_bcast<v + 16>(cur_D) : half_bcast<v>(cur_D);
+            const int lim = rt ? half_bcast<v + 16>(cur_lim) : half_bcast<v>(cur_lim);
+            const bool in = koff <= lim;  // a real row, and causal
             const float p = in ? __builtin_amdgcn_exp2f(fmaf(sacc[v], scale_log2, -l2)) : 0.f;
             P[v] = p;
             dS[v] = p * (pacc[v] - Dv);
-          }
+          });
 #pragma unroll
           for (int s2 = 0; s2 < 2; ++s2) {
             Pp[rt][s2] = pack8(&P[8 * s2]);
@@ -317,7 +351,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
           const u32x4_t bs = *reinterpret_cast<const u32x4_t*>(Qs + row * 256 + ((kc ^ (row & 15)) << 4));
           qacc = mfma_32x32x16(as_bf16x8(ak), as_bf16x8(bs), qacc);
         }
-        const int pr = __shfl(cur_prv, row);
+        const int pr = __shfl(cur_prv, bwd_row_lane(row));
         if (pr >= 0) {
           const int64_t prow = (((int64_t)(pr >> 5) * H_kv + r) * kk + (pr & 31)) * G + row % G;
           uint16_t* dst = dq_part + prow * kDh + 32 * (wave >> 1) + 8 * h;
