@@ -208,30 +208,31 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
       const int cur_prv = my_prv, cur_lim = my_lim;
       const float cur_l2 = my_l2, cur_D = my_D;
       __syncthreads();  // rows staged (and, on the first sub-chunk, the block)
-      if (tid < 256) {
-        // Transposes: threads 0..127 build Qt, 128..255 dOt.  Thread (pg, dc) moves
-        // positions 8pg .. 8pg+7 (row (pos & ~31) | swap23(pos & 31)) x dims 8dc .. +7.
-        const int tt = tid & 127;
-        const uint8_t* src = tid < 128 ? Qs : dOs;
-        uint8_t* dst = tid < 128 ? Qt : dOt;
-        const int pg = tt & 7, dc = tt >> 3;
-        u32x4_t w[8];
+      {
+        // Transposes: threads 0..255 build Qt, 256..511 dOt.  Thread (pg, dc) moves
+        // positions 4pg .. 4pg+3 (row (pos & ~31) | swap23(pos & 31)) x dims 8dc .. +7;
+        // positions 8c .. 8c+7 of dim d form 16-byte chunk c ^ (d & 7) of its row.
+        const int tt = tid & 255;
+        const uint8_t* src = tid < 256 ? Qs : dOs;
+        uint8_t* dst = tid < 256 ? Qt : dOt;
+        const int pg = tt & 15, dc = tt >> 4;
+        u32x4_t w[4];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int pos = 8 * pg + j;
+        for (int j = 0; j < 4; ++j) {
+          const int pos = 4 * pg + j;
           const int rho = (pos & ~31) | swap23(pos & 31);
           w[j] = *reinterpret_cast<const u32x4_t*>(src + rho * 256 + ((dc ^ (rho & 15)) << 4));
         }
 #pragma unroll
         for (int f = 0; f < 8; ++f) {
-          u32x4_t o4;
+          u32x2_t o2;
 #pragma unroll
-          for (int m = 0; m < 4; ++m) {
+          for (int m = 0; m < 2; ++m) {
             const uint32_t x = w[2 * m][f >> 1], y = w[2 * m + 1][f >> 1];
-            o4[m] = (f & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
+            o2[m] = (f & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
           }
           const int d = dc * 8 + f;
-          *reinterpret_cast<u32x4_t*>(dst + d * 128 + ((pg ^ (d & 7)) << 4)) = o4;
+          *reinterpret_cast<u32x2_t*>(dst + d * 128 + (((pg >> 1) ^ (d & 7)) << 4) + (pg & 1) * 8) = o2;
         }
       }
       __syncthreads();  // transposes done
