@@ -383,7 +383,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
   }
 }
 
-// dQ: per (query, head) the sum of its valid slots' partial rows; 32 lanes per row.
+// dQ: per (query, head) the sum of its valid slots' partial rows in slot order; 32
+// lanes per row, 4 dims each.  The valid slots are listed first so that the row
+// loads can be issued four at a time.
 __global__ __launch_bounds__(256) void bwd_dq_combine_kernel(const uint16_t* __restrict__ dq_part,
                                                              const int32_t* __restrict__ block_idx, int64_t w0,
                                                              int64_t W, int H_kv, int G, int kk,
@@ -397,21 +399,44 @@ __global__ __launch_bounds__(256) void bwd_dq_combine_kernel(const uint16_t* __r
   const int r = hh / G, g = hh % G;
   const int64_t i = w0 + il;
   const int32_t* sel = block_idx + (i * H_kv + r) * kk;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  uint32_t vmask = 0;  // kk <= 32
   for (int s = 0; s < kk; ++s) {
     const int bb = sel[s];
-    if (bb < 0 || (int64_t)bb > (i >> 7)) continue;
-    const uint2 x = *reinterpret_cast<const uint2*>(dq_part + ((((il * H_kv + r) * kk + s) * G + g) * kDh) + 4 * l);
+    if (bb >= 0 && (int64_t)bb <= (i >> 7)) vmask |= 1u << s;
+  }
+  const uint16_t* base = dq_part + ((il * H_kv + r) * kk * G + g) * kDh + 4 * l;
+  const int64_t sstride = (int64_t)G * kDh;  // elements between consecutive slots' rows
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto add = [&](uint2 x) {
     acc.x += __uint_as_float(x.x << 16);
     acc.y += __uint_as_float(x.x & 0xffff0000u);
     acc.z += __uint_as_float(x.y << 16);
     acc.w += __uint_as_float(x.y & 0xffff0000u);
+  };
+  while (vmask) {
+    int sl[4];
+    int n = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sl[j] = vmask ? __builtin_ctz(vmask) : -1;
+      if (vmask) {
+        vmask &= vmask - 1;
+        ++n;
+      }
+    }
+    uint2 x[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = *reinterpret_cast<const uint2*>(base + (sl[j] < 0 ? sl[0] : sl[j]) * sstride);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (j < n) add(x[j]);
   }
   *reinterpret_cast<float4*>(dq + (i * H_q + hh) * kDh + 4 * l) = acc;
 }
 
 // dK, dV of block b, group r: the partial blocks of the items of its lists (one per
-// query window), summed in item order and added to dk / dv.
+// query window), summed in item order and added to dk / dv; a thread sums 4
+// consecutive elements, with four items' loads in flight.
 __global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(const float* __restrict__ dkv_part,
                                                             const int32_t* __restrict__ counts,
                                                             const int32_t* __restrict__ lfirst, int item_q,
@@ -420,21 +445,43 @@ __global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(const float* __restr
   const int64_t rb = blockIdx.x;
   const int r = (int)(rb / B);
   const int64_t b = rb % B;
-  for (int e = threadIdx.x; e < 2 * kBk * kDh; e += 256) {
-    const int which = e / (kBk * kDh), kd = e % (kBk * kDh);
+  constexpr int kBlockElems = kBk * kDh;
+  for (int e4 = threadIdx.x; e4 < 2 * kBlockElems / 4; e4 += 256) {
+    const int e = 4 * e4;
+    const int which = e / kBlockElems, kd = e % kBlockElems;
     const int key = kd / kDh, d = kd % kDh;
     const int64_t tok = b * kBk + key;
     if (tok >= N) continue;
-    float acc = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    auto add = [&](const float4& x) {
+      acc.x += x.x;
+      acc.y += x.y;
+      acc.z += x.z;
+      acc.w += x.w;
+    };
     for (int w = 0; w < nW; ++w) {
       const int64_t l = ((int64_t)r * nW + w) * B + b;
       const int n = counts[l];
       const int nit = (n + item_q - 1) / item_q;
-      const int64_t f = lfirst[l];
-      for (int t = 0; t < nit; ++t) acc += dkv_part[((f + t) * 2 + which) * (kBk * kDh) + kd];
+      const float* src = dkv_part + ((int64_t)lfirst[l] * 2 + which) * kBlockElems + kd;
+      constexpr int64_t kItemStride = 2 * kBlockElems;
+      int t = 0;
+      for (; t + 4 <= nit; t += 4) {
+        float4 x[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = *reinterpret_cast<const float4*>(src + (t + j) * kItemStride);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) add(x[j]);
+      }
+      for (; t < nit; ++t) add(*reinterpret_cast<const float4*>(src + t * kItemStride));
     }
-    float* out = which ? dv : dk;
-    out[(tok * H_kv + r) * kDh + d] += acc;
+    float* out = (which ? dv : dk) + (tok * H_kv + r) * kDh + d;
+    float4 o4 = *reinterpret_cast<float4*>(out);
+    o4.x += acc.x;
+    o4.y += acc.y;
+    o4.z += acc.z;
+    o4.w += acc.w;
+    *reinterpret_cast<float4*>(out) = o4;
   }
 }
 
