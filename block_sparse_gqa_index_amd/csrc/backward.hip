@@ -383,15 +383,15 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
   }
 }
 
-// dQ: per (query, head) the sum of its valid slots' partial rows in slot order; 32
-// lanes per row, 4 dims each.  The valid slots are listed first so that the row
+// dQ: per (query, head) the sum of its valid slots' partial rows in slot order; 16
+// lanes per row, 8 dims (16 bytes of each partial row) each.  The valid slots are listed first so that the row
 // loads can be issued four at a time.
 __global__ __launch_bounds__(256) void bwd_dq_combine_kernel(const uint16_t* __restrict__ dq_part,
                                                              const int32_t* __restrict__ block_idx, int64_t w0,
                                                              int64_t W, int H_kv, int G, int kk,
                                                              float* __restrict__ dq) {
-  const int64_t gr = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 5;  // (query in window, head)
-  const int l = threadIdx.x & 31;
+  const int64_t gr = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;  // (query in window, head)
+  const int l = threadIdx.x & 15;
   const int H_q = H_kv * G;
   if (gr >= W * H_q) return;
   const int64_t il = gr / H_q;
@@ -404,14 +404,15 @@ __global__ __launch_bounds__(256) void bwd_dq_combine_kernel(const uint16_t* __r
     const int bb = sel[s];
     if (bb >= 0 && (int64_t)bb <= (i >> 7)) vmask |= 1u << s;
   }
-  const uint16_t* base = dq_part + ((il * H_kv + r) * kk * G + g) * kDh + 4 * l;
+  const uint16_t* base = dq_part + ((il * H_kv + r) * kk * G + g) * kDh + 8 * l;
   const int64_t sstride = (int64_t)G * kDh;  // elements between consecutive slots' rows
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  auto add = [&](uint2 x) {
-    acc.x += __uint_as_float(x.x << 16);
-    acc.y += __uint_as_float(x.x & 0xffff0000u);
-    acc.z += __uint_as_float(x.y << 16);
-    acc.w += __uint_as_float(x.y & 0xffff0000u);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  auto add = [&](const u32x4_t& x) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      acc[2 * m] += __uint_as_float(x[m] << 16);
+      acc[2 * m + 1] += __uint_as_float(x[m] & 0xffff0000u);
+    }
   };
   while (vmask) {
     int sl[4];
@@ -424,14 +425,17 @@ __global__ __launch_bounds__(256) void bwd_dq_combine_kernel(const uint16_t* __r
         ++n;
       }
     }
-    uint2 x[4];
+    u32x4_t x[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) x[j] = *reinterpret_cast<const uint2*>(base + (sl[j] < 0 ? sl[0] : sl[j]) * sstride);
+    for (int j = 0; j < 4; ++j)
+      x[j] = *reinterpret_cast<const u32x4_t*>(base + (sl[j] < 0 ? sl[0] : sl[j]) * sstride);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       if (j < n) add(x[j]);
   }
-  *reinterpret_cast<float4*>(dq + (i * H_q + hh) * kDh + 4 * l) = acc;
+  float* out = dq + (i * H_q + hh) * kDh + 8 * l;
+  *reinterpret_cast<float4*>(out) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  *reinterpret_cast<float4*>(out + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
 }
 
 // dK, dV of block b, group r: the partial blocks of the items of its lists (one per
@@ -540,7 +544,7 @@ hipError_t launch_bwd_window(const uint16_t* q, const uint16_t* k, const uint16_
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t rows = W * H_q;
-  bwd_dq_combine_kernel<<<dim3((unsigned)((rows * 32 + 255) / 256)), dim3(256), 0, stream>>>(
+  bwd_dq_combine_kernel<<<dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, stream>>>(
       dq_part, block_idx, w0, W, H_kv, G, kk, dq);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   bwd_kv_reduce_kernel<<<dim3((unsigned)(H_kv * B)), dim3(256), 0, stream>>>(dkv_part, counts, lfirst, L.item_q, B,
