@@ -217,11 +217,11 @@ def run_prefill(msa, synth, cfg, mode, steps, warmup, with_kl=False, with_bwd=Fa
     block_idx = torch.empty((N, H_kv, k), dtype=torch.int32, device=dev)
     o = torch.empty((N, H_q, cfg.d_h), dtype=torch.float32, device=dev)
     lse = torch.empty((N, H_q), dtype=torch.float32, device=dev)
-    ws = torch.empty(msa.msa_sparse_attn_fwd_workspace(N, H_q, H_kv, k), dtype=torch.uint8, device=dev)
+    ws = torch.empty(msa.msa_sparse_attn_fwd_workspace(N, H_q, H_kv, k, B_k=B_k), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
-    n_win = msa.msa_sparse_attn_fwd_windows(N, H_q, H_kv, k, ws.numel())
+    n_win = msa.msa_sparse_attn_fwd_windows(N, H_q, H_kv, k, ws.numel(), B_k=B_k)
     # Per step: index start, attention start, attention end, then 4 per query window.
     n_ev = 3 + 4 * n_win
 
@@ -229,10 +229,10 @@ def run_prefill(msa, synth, cfg, mode, steps, warmup, with_kl=False, with_bwd=Fa
         if ev is not None:
             ev[0].record(stream)
             msa.msa_set_profile_events(ev[3:])
-        msa.msa_index_topk(inp.q_idx, inp.k_idx, k, block_idx=block_idx)
+        msa.msa_index_topk(inp.q_idx, inp.k_idx, k, B_k=B_k, block_idx=block_idx)
         if ev is not None:
             ev[1].record(stream)
-        msa.msa_sparse_attn_fwd(inp.q, inp.k, inp.v, block_idx, o=o, lse=lse, workspace=ws)
+        msa.msa_sparse_attn_fwd(inp.q, inp.k, inp.v, block_idx, B_k=B_k, o=o, lse=lse, workspace=ws)
         if ev is not None:
             ev[2].record(stream)
             msa.msa_set_profile_events(None)
@@ -300,6 +300,60 @@ def run_prefill(msa, synth, cfg, mode, steps, warmup, with_kl=False, with_bwd=Fa
         res["backward"] = run_bwd(msa, inp, cfg, block_idx, o, lse, slot_pairs, pairs, max(2, steps // 4))
     del o, lse, block_idx
     return res, inp
+
+
+def run_varlen(msa, synth, vcfg, mode, steps, warmup):
+    """Packed variable-length prefill: index Top-k and attention over a batch of
+    sequences of different lengths packed on the token axis (cu_seqlens)."""
+    import torch
+    dev = "cuda"
+    B_k, H_q, H_kv, k = vcfg.B_k, vcfg.H_q, vcfg.H_kv, vcfg.k
+    G = H_q // H_kv
+    lengths = synth.varlen_lengths(vcfg)
+    log(f"generating {vcfg.name} ({mode}) packed inputs: {len(lengths)} sequences")
+    p = synth.packed_prefill(lengths, H_q, H_kv, k, vcfg.seed, mode, device=dev)
+    T, batch, max_len = sum(lengths), len(lengths), max(lengths)
+    bi = torch.empty((T, H_kv, k), dtype=torch.int32, device=dev)
+    o = torch.empty((T, H_q, 128), dtype=torch.float32, device=dev)
+    lse = torch.empty((T, H_q), dtype=torch.float32, device=dev)
+    ws = torch.empty(msa.msa_sparse_attn_fwd_varlen_workspace(T, batch, H_q, H_kv, k, B_k=B_k), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        msa.msa_index_topk_varlen(p.q_idx, p.k_idx, p.cu_seqlens, max_len, k, B_k=B_k, block_idx=bi)
+        if ev is not None:
+            ev[1].record(stream)
+        msa.msa_sparse_attn_fwd_varlen(p.q, p.k, p.v, bi, p.cu_seqlens, B_k=B_k, o=o, lse=lse, workspace=ws)
+        if ev is not None:
+            ev[2].record(stream)
+
+    log(f"varlen {mode}: warmup {warmup}, timed {steps} steps")
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s in range(steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    avg = lambda a, b: sum(e[a].elapsed_time(e[b]) for e in evs) / steps
+    cu = p.cu_seqlens.cpu().tolist()
+    # Exact work per sequence: its own causal index scores and attended tokens.
+    f_index = sum(flops_index_exact(L, H_kv, 64) for L in lengths)
+    f_main = 4 * 128 * sum(attended_pairs(bi[cu[s]:cu[s + 1]], B_k, G) for s in range(batch) if lengths[s] > 0)
+    f = f_index + f_main
+    del p, bi, o, lse, ws
+    torch.cuda.empty_cache()
+    return {"workload": f"packed prefill T={T} batch={batch} lengths {min(lengths)}..{max_len} H_q={H_q} "
+                        f"H_kv={H_kv} B_k={B_k} k={k}",
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(T / (ms / 1e3), 1),
+            "ms_index_topk": round(avg(0, 1), 4), "ms_sparse_attn_fwd": round(avg(1, 2), 4),
+            "tflops": round(f / (ms / 1e3) / 1e12, 2),
+            "mfma_peak_frac": round(f / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4), "steps": steps}
 
 
 def run_bwd(msa, inp, cfg, block_idx, o, lse, slot_pairs, pairs, steps):
@@ -528,6 +582,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-paged", action="store_true", help="skip the paged FP8 decode measurement")
     ap.add_argument("--no-bwd", action="store_true", help="skip the separately timed backward")
     ap.add_argument("--table1", action="store_true", help="also time Top-k alone at the pages' Top-k table shapes")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the 128K prefill with B_k = 64 and the packed variable-length batch")
     ap.add_argument("--single-mode", action="store_true", help="skip the second input mode")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="start with plain copies of known size (for counter runs)")
@@ -604,6 +660,16 @@ def main(argv=None) -> int:
         result["decode"] = run_decode(msa, synth, dcfg, args.mode, max(args.steps, 50), args.warmup,
                                       paged=not args.no_paged)
         torch.cuda.empty_cache()
+    if not args.no_extra:
+        c64 = synth.CONFIGS["c2_bk64"]
+        pre64, inp64 = run_prefill(msa, synth, c64, args.mode, args.steps, args.warmup)
+        del inp64
+        torch.cuda.empty_cache()
+        pre64["workload"] = (f"prefill N={c64.N} H_q={c64.H_q} H_kv={c64.H_kv} d_h={c64.d_h} d_idx={c64.d_idx} "
+                             f"B_k={c64.B_k} k={c64.k}")
+        result["prefill_bk64"] = pre64
+        result["varlen"] = run_varlen(msa, synth, synth.VARLEN_CONFIGS["c2_varlen"], args.mode, args.steps,
+                                      args.warmup)
     if not args.single_mode:
         pre2, inp2 = run_prefill(msa, synth, cfg, other, args.steps, args.warmup)
         del inp2

@@ -85,7 +85,41 @@ CONFIGS = {
     "c3": DecodeConfig("c3", batch=64, H_q=64, H_kv=8, k=16, len_lo_blocks=256, len_hi_blocks=1024, seed=1003),
     "c3_128k": DecodeConfig("c3_128k", batch=64, H_q=64, H_kv=8, k=16, len_lo_blocks=1024, len_hi_blocks=1024, seed=1003),
     "c4": PrefillConfig("c4", N=1048576, H_q=64, H_kv=8, k=16, needles=32, needle_dist="loguniform", seed=1004),
+    # 128K with blocks of 64 keys and k = 32: the same 2048 attended keys per query.
+    "c2_bk64": PrefillConfig("c2_bk64", N=131072, H_q=64, H_kv=8, k=32, B_k=64, needles=8, seed=1005),
 }
+
+
+@dataclass(frozen=True)
+class VarlenConfig:
+    """A packed batch of about ``total`` tokens: lengths B_k * U{lo..hi} drawn from the
+    lengths stream until the total is reached (the last one cut to fit)."""
+    name: str
+    total: int
+    H_q: int
+    H_kv: int
+    k: int
+    len_lo_blocks: int
+    len_hi_blocks: int
+    B_k: int = 128
+    seed: int = 1006
+
+
+VARLEN_CONFIGS = {
+    "c2_varlen": VarlenConfig("c2_varlen", total=131072, H_q=64, H_kv=8, k=16, len_lo_blocks=8,
+                              len_hi_blocks=256),
+}
+
+
+def varlen_lengths(cfg: VarlenConfig):
+    g = _gen(cfg.seed, T_LEN, "cpu")
+    out, t = [], 0
+    while t < cfg.total:
+        L = int(torch.randint(cfg.len_lo_blocks, cfg.len_hi_blocks + 1, (1,), generator=g)) * cfg.B_k
+        L = min(L, cfg.total - t)
+        out.append(L)
+        t += L
+    return out
 
 
 def _gen(seed: int, tensor_id: int, device) -> torch.Generator:
