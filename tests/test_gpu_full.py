@@ -1,4 +1,5 @@
-"""GPU parity at the full workload sizes (32K, 128K and 1M prefill; 64-sequence decode),
+"""GPU parity at the full workload sizes (32K, 128K and 1M prefill, 128K with B_k = 64,
+a packed batch of 128K tokens; 64-sequence decode),
 in the launch configuration the benchmark times, on sampled rows the oracle computes
 one by one.  The sample holds rows with fewer than k causal blocks, uniform rows, the
 last rows of the sequence and rows right after needle blocks."""
@@ -39,8 +40,8 @@ def _run_prefill(msa, name, mode, n_uniform):
     print(f"[full] {name} {mode}: generating inputs", flush=True)
     inp = synth.make_prefill(cfg, mode, device=DEV)
     k = cfg.k
-    bi = msa.msa_index_topk(inp.q_idx, inp.k_idx, k)
-    o, lse = msa.msa_sparse_attn_fwd(inp.q, inp.k, inp.v, bi)
+    bi = msa.msa_index_topk(inp.q_idx, inp.k_idx, k, B_k=cfg.B_k)
+    o, lse = msa.msa_sparse_attn_fwd(inp.q, inp.k, inp.v, bi, B_k=cfg.B_k)
     torch.cuda.synchronize()
     rows = sample_rows(cfg, inp.needles, n_uniform, cfg.seed)
     print(f"[full] {name} {mode}: oracle on {len(rows)} rows", flush=True)
@@ -71,6 +72,41 @@ def test_prefill_128k(msa, mode):
 @pytest.mark.parametrize("mode", ["literal", "structured"])
 def test_prefill_1m(msa, mode):
     _run_prefill(msa, "c4", mode, n_uniform=48)
+
+
+@pytest.mark.parametrize("mode", ["literal", "structured"])
+def test_prefill_128k_bk64(msa, mode):
+    _run_prefill(msa, "c2_bk64", mode, n_uniform=128)
+
+
+@pytest.mark.parametrize("mode", ["literal", "structured"])
+def test_packed_batch_128k(msa, mode):
+    """The packed variable-length batch the benchmark times (9 sequences, 131072
+    tokens), checked per sequence on sampled rows."""
+    vcfg = synth.VARLEN_CONFIGS["c2_varlen"]
+    lengths = synth.varlen_lengths(vcfg)
+    print(f"[full] {vcfg.name} {mode}: generating {len(lengths)} sequences", flush=True)
+    p = synth.packed_prefill(lengths, vcfg.H_q, vcfg.H_kv, vcfg.k, vcfg.seed, mode, device=DEV)
+    k, B_k = vcfg.k, vcfg.B_k
+    bi = msa.msa_index_topk_varlen(p.q_idx, p.k_idx, p.cu_seqlens, max(lengths), k, B_k=B_k)
+    o, lse = msa.msa_sparse_attn_fwd_varlen(p.q, p.k, p.v, bi, p.cu_seqlens, B_k=B_k)
+    torch.cuda.synchronize()
+    cu = p.cu_seqlens.cpu().tolist()
+    for s, L in enumerate(lengths):
+        a = cu[s]
+        scfg = synth.PrefillConfig(f"seq{s}", N=L, H_q=vcfg.H_q, H_kv=vcfg.H_kv, k=k, B_k=B_k)
+        rows = sample_rows(scfg, None, min(24, L), vcfg.seed + s)
+        ridx = torch.from_numpy(rows + a).to(DEV)
+        bi_s = bi[ridx].cpu().numpy()
+        sl = slice(a, a + L)
+        M = oracle.block_scores(p.q_idx[sl].cpu(), p.k_idx[sl].cpu(), B_k, rows=rows)
+        tie = check_block_idx(bi_s, M, rows, k, B_k)
+        o_ref, lse_ref = oracle.sparse_attn(p.q[sl].cpu(), p.k[sl].cpu(), p.v[sl].cpu(), bi_s, B_k, rows=rows)
+        stats = check_attn(o[ridx].cpu().numpy(), lse[ridx].cpu().numpy(), o_ref, lse_ref,
+                           f"{vcfg.name} {mode} sequence {s}")
+        exact = oracle.topk(M, k, B_k, rows=rows)
+        np.testing.assert_array_equal(bi_s[~tie], exact[~tie])
+        print(f"[full] {vcfg.name} {mode} sequence {s} (L={L}): {len(rows)} rows, {stats}", flush=True)
 
 
 @pytest.mark.parametrize("name", ["c3", "c3_128k"])
