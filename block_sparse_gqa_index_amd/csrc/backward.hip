@@ -16,11 +16,12 @@
 // rows of the sub-chunk in LDS both row-major and transposed.  Wave w owns keys
 // 32(w % 4) .. +31 of the block and dims 64(w / 4) .. +63 of its dK and dV:
 //   S = Q K^T and dP = dO V^T on 32x32x16 MFMAs give, per lane, one key (the lane)
-//   and 32 rows (registers), so P and dS are formed in registers (both waves of a
-//   key slice compute them, identically: the matrix cores have room for it, and it
-//   halves the dK/dV accumulators a wave holds);
+//   and 32 rows (registers), so P and dS are formed in registers; the two waves of
+//   a key slice take one 32-row tile each and hand the other their P through LDS
+//   (their dS through the dS rows written for dQ);
 //   dV += P^T dO and dK += dS^T Q use P and dS directly as MFMA operands, and
-//   accumulate in registers over the whole item;
+//   accumulate in registers over the whole item (each wave holding half the dims,
+//   which is what lets two waves share a SIMD);
 //   dS goes to LDS, and each wave then computes dQ for 32 rows x 32 dims over all
 //   128 keys (dS K, with K^T as the operand).
 // dQ leaves as one bf16 partial row per (query, slot, head), summed over the slots
@@ -245,96 +246,122 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
         asm volatile("" : "+v"(x));
         return x;
       };
-      // S and dP: element v of row tile rt is row rt*32 + 8(v/4) + 4h + v%4, key koff.
-      // P and dS leave this phase as bf16 MFMA operands: Pp[rt][s2] holds elements
-      // 8 s2 .. 8 s2 + 7.
-      u32x4_t Pp[2][2], dSp[2][2];
-      {
+      // S and dP of this wave's row tile rt = dh (the other tile is its partner's,
+      // wave ^ 4, which owns the same keys): element v is row rt*32 + 8(v/4) + 4h + v%4,
+      // key koff.  P and dS leave this phase as bf16 MFMA operands: Pp[s2] holds
+      // elements 8 s2 .. 8 s2 + 7.
+      u32x4_t Pp[2], dSp[2];
+      auto s_dp = [&](auto RTC) {
+        constexpr int rt = decltype(RTC)::value;
         const int lv = lane_v();
         const int h = lv >> 5, l32 = lv & 31;
         const int krow = 32 * ks + l32;
         const int koff = 32 * ks + swap23(l32);
+        f32x16_t sacc = f32x16_t{}, pacc = f32x16_t{};
+        const int row = rt * 32 + l32;
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-          f32x16_t sacc = f32x16_t{}, pacc = f32x16_t{};
-          const int row = rt * 32 + l32;
-#pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const int c = 8 * h + t;
-            const u32x4_t aq = *reinterpret_cast<const u32x4_t*>(Qs + row * 256 + ((c ^ (row & 15)) << 4));
-            const u32x4_t bk = *reinterpret_cast<const u32x4_t*>(Ks + krow * 256 + ((c ^ (krow & 15)) << 4));
-            sacc = mfma_32x32x16(as_bf16x8(aq), as_bf16x8(bk), sacc);
-            const u32x4_t ag = *reinterpret_cast<const u32x4_t*>(dOs + row * 256 + ((c ^ (row & 15)) << 4));
-            const u32x4_t bv = *reinterpret_cast<const u32x4_t*>(Vs + krow * 256 + ((c ^ (krow & 15)) << 4));
-            pacc = mfma_32x32x16(as_bf16x8(ag), as_bf16x8(bv), pacc);
-          }
-          float P[16], dS[16];
-          // Element v: row rt*32 + 8(v/4) + 4h + v%4, held by lane v + 16 rt of this
-          // lane's half.
-          static_for<16>([&](auto VC) {
-            constexpr int v = decltype(VC)::value;
-            const float l2 = rt ? half_bcast<v + 16>(cur_l2) : half_bcast<v>(cur_l2);
-            const float Dv = rt ? half_bcast<v + 16>(cur_D) : half_bcast<v>(cur_D);
-            const int lim = rt ? half_bcast<v + 16>(cur_lim) : half_bcast<v>(cur_lim);
-            const bool in = koff <= lim;  // a real row, and causal
-            const float p = in ? __builtin_amdgcn_exp2f(fmaf(sacc[v], scale_log2, -l2)) : 0.f;
-            P[v] = p;
-            dS[v] = p * (pacc[v] - Dv);
-          });
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            Pp[rt][s2] = pack8(&P[8 * s2]);
-            dSp[rt][s2] = pack8(&dS[8 * s2]);
-          }
-          __builtin_amdgcn_sched_barrier(0);  // one row tile's accumulators at a time
+        for (int t = 0; t < 8; ++t) {
+          const int c = 8 * h + t;
+          const u32x4_t aq = *reinterpret_cast<const u32x4_t*>(Qs + row * 256 + ((c ^ (row & 15)) << 4));
+          const u32x4_t bk = *reinterpret_cast<const u32x4_t*>(Ks + krow * 256 + ((c ^ (krow & 15)) << 4));
+          sacc = mfma_32x32x16(as_bf16x8(aq), as_bf16x8(bk), sacc);
+          const u32x4_t ag = *reinterpret_cast<const u32x4_t*>(dOs + row * 256 + ((c ^ (row & 15)) << 4));
+          const u32x4_t bv = *reinterpret_cast<const u32x4_t*>(Vs + krow * 256 + ((c ^ (krow & 15)) << 4));
+          pacc = mfma_32x32x16(as_bf16x8(ag), as_bf16x8(bv), pacc);
         }
-      }
-      // dV += P^T dO and dK += dS^T Q: MFMA rows are this wave's keys (row i holds
-      // key 32w + swap23(i)); k-slot (h, j) of step (rt, s2) is row
-      // rt*32 + 8(2 s2 + j/4) + 4h + j%4, the transposed tiles' position
-      // rt*32 + 16 s2 + 8h + j.
-      {
-      const int lv = lane_v();
-      const int h = lv >> 5, l32 = lv & 31;
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
+        float P[16], dS[16];
+        // Element v: row rt*32 + 8(v/4) + 4h + v%4, held by lane v + 16 rt of this
+        // lane's half.
+        static_for<16>([&](auto VC) {
+          constexpr int v = decltype(VC)::value;
+          const float l2 = half_bcast<v + 16 * rt>(cur_l2);
+          const float Dv = half_bcast<v + 16 * rt>(cur_D);
+          const int lim = half_bcast<v + 16 * rt>(cur_lim);
+          const bool in = koff <= lim;  // a real row, and causal
+          const float p = in ? __builtin_amdgcn_exp2f(fmaf(sacc[v], scale_log2, -l2)) : 0.f;
+          P[v] = p;
+          dS[v] = p * (pacc[v] - Dv);
+        });
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-          const u32x4_t ap = Pp[rt][s2];
-          const u32x4_t ad = dSp[rt][s2];
-          const int ch = 4 * rt + 2 * s2 + h;
-#pragma unroll
-          for (int dt = 0; dt < 2; ++dt) {
-            const int d = 64 * dh + dt * 32 + l32;
-            const u32x4_t bo = *reinterpret_cast<const u32x4_t*>(dOt + d * 128 + ((ch ^ (d & 7)) << 4));
-            dv_acc[dt] = mfma_32x32x16(as_bf16x8(ap), as_bf16x8(bo), dv_acc[dt]);
-            const u32x4_t bq = *reinterpret_cast<const u32x4_t*>(Qt + d * 128 + ((ch ^ (d & 7)) << 4));
-            dk_acc[dt] = mfma_32x32x16(as_bf16x8(ad), as_bf16x8(bq), dk_acc[dt]);
-          }
-          __builtin_amdgcn_sched_barrier(0);
+          Pp[s2] = pack8(&P[8 * s2]);
+          dSp[s2] = pack8(&dS[8 * s2]);
         }
-      }
-      }
-      __syncthreads();  // every wave is done with Qs: dS replaces it
-      // dS rows in Qs: row-major, keys in natural order, chunk kc at kc ^ (row & 15).
-      // The two waves of a key slice hold the same dS; each stores one row tile.
+      };
+      if (dh == 0)
+        s_dp(std::integral_constant<int, 0>{});
+      else
+        s_dp(std::integral_constant<int, 1>{});
+      __syncthreads();  // every wave is done with Qs and dOs
+      // The wave's P goes to the dO-row area for its partner (wave w's 2 KB at w * 2 KB,
+      // operand s2 of lane l at (64 s2 + l) * 16 B); its dS rows go into Qs, row-major
+      // with keys in natural order and chunk kc at kc ^ (row & 15), for dQ and for the
+      // partner.
       {
         const int lv = lane_v();
         const int h = lv >> 5;
         const int koff = 32 * ks + swap23(lv & 31);
+        u32x4_t* xp = reinterpret_cast<u32x4_t*>(dOs + wave * 2048) + lv;
+        xp[0] = Pp[0];
+        xp[64] = Pp[1];
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-          if (rt != dh) continue;
+        for (int v = 0; v < 16; ++v) {
+          const int rv = dh * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+          const uint32_t w2 = dSp[v >> 3][(v & 7) >> 1];
+          *reinterpret_cast<uint16_t*>(Qs + rv * 256 + ((((koff >> 3) ^ (rv & 15))) << 4) + (koff & 7) * 2) =
+              (uint16_t)((v & 1) ? (w2 >> 16) : (w2 & 0xffffu));
+        }
+      }
+      __syncthreads();  // P exchanged, dS complete
+      // dV += P^T dO and dK += dS^T Q over both row tiles, this wave's first: MFMA rows
+      // are the wave's keys (row i holds key 32(w % 4) + swap23(i)); k-slot (h, j) of
+      // step (rt, s2) is row rt*32 + 8(2 s2 + j/4) + 4h + j%4, the transposed tiles'
+      // position rt*32 + 16 s2 + 8h + j.  The partner's P comes from the exchange area,
+      // its dS from the rows in Qs.
+      {
+        const int lv = lane_v();
+        const int h = lv >> 5, l32 = lv & 31;
+        const int koff = 32 * ks + swap23(l32);
+        const int rto = dh ^ 1;
+        u32x4_t Po[2], dSo[2];
+        const u32x4_t* xo = reinterpret_cast<const u32x4_t*>(dOs + (wave ^ 4) * 2048) + lv;
+        Po[0] = xo[0];
+        Po[1] = xo[64];
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int rv = rt * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-            const uint32_t w2 = dSp[rt][v >> 3][(v & 7) >> 1];
-            *reinterpret_cast<uint16_t*>(Qs + rv * 256 + ((((koff >> 3) ^ (rv & 15))) << 4) + (koff & 7) * 2) =
-                (uint16_t)((v & 1) ? (w2 >> 16) : (w2 & 0xffffu));
+        for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            uint32_t hw[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const int j = 2 * m + e;
+              const int row = rto * 32 + 8 * (2 * s2 + (j >> 2)) + 4 * h + (j & 3);
+              hw[e] = *reinterpret_cast<const uint16_t*>(Qs + row * 256 + ((((koff >> 3) ^ (row & 15))) << 4) +
+                                                         (koff & 7) * 2);
+            }
+            dSo[s2][m] = hw[0] | (hw[1] << 16);
+          }
+        }
+#pragma unroll
+        for (int tile = 0; tile < 2; ++tile) {
+          const int rt = tile ? rto : dh;
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const u32x4_t ap = tile ? Po[s2] : Pp[s2];
+            const u32x4_t ad = tile ? dSo[s2] : dSp[s2];
+            const int ch = 4 * rt + 2 * s2 + h;
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt) {
+              const int d = 64 * dh + dt * 32 + l32;
+              const u32x4_t bo = *reinterpret_cast<const u32x4_t*>(dOt + d * 128 + ((ch ^ (d & 7)) << 4));
+              dv_acc[dt] = mfma_32x32x16(as_bf16x8(ap), as_bf16x8(bo), dv_acc[dt]);
+              const u32x4_t bq = *reinterpret_cast<const u32x4_t*>(Qt + d * 128 + ((ch ^ (d & 7)) << 4));
+              dk_acc[dt] = mfma_32x32x16(as_bf16x8(ad), as_bf16x8(bq), dk_acc[dt]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
       }
-      __syncthreads();  // dS complete
       {
         // dQ^T = K^T dS^T over all 128 keys: wave w takes dQ rows 32(w & 1) + 0..31
         // (MFMA columns, one per lane) and dims 32(w >> 1) + 0..31 (MFMA rows; lane l
