@@ -120,10 +120,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t Ks[kBk * 256];   // K rows (key swap23(rho) at row rho)
   __shared__ __attribute__((aligned(16))) uint8_t Vs[kBk * 256];   // V rows, same order
   __shared__ __attribute__((aligned(16))) uint8_t Kt[kDh * 256];   // K^T, keys in natural order
-  __shared__ __attribute__((aligned(16))) uint8_t Qs[kBwdRows * 256];   // q rows; later dS rows
+  __shared__ __attribute__((aligned(16))) uint8_t Qs[kBwdRows * 256];   // q rows
   __shared__ __attribute__((aligned(16))) uint8_t dOs[kBwdRows * 256];  // dO rows
-  __shared__ __attribute__((aligned(16))) uint8_t Qt[kDh * 128];   // q^T, rows at position swap23 within 32
-  __shared__ __attribute__((aligned(16))) uint8_t dOt[kDh * 128];  // dO^T, same
+  __shared__ __attribute__((aligned(16))) uint8_t dSs[kBwdRows * 256];  // dS rows (keys in natural order)
+  __shared__ __attribute__((aligned(16))) uint8_t Px[8 * 2048];         // each wave's P for its partner
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -209,34 +209,6 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
       const int cur_prv = my_prv, cur_lim = my_lim;
       const float cur_l2 = my_l2, cur_D = my_D;
       __syncthreads();  // rows staged (and, on the first sub-chunk, the block)
-      {
-        // Transposes: threads 0..255 build Qt, 256..511 dOt.  Thread (pg, dc) moves
-        // positions 4pg .. 4pg+3 (row (pos & ~31) | swap23(pos & 31)) x dims 8dc .. +7;
-        // positions 8c .. 8c+7 of dim d form 16-byte chunk c ^ (d & 7) of its row.
-        const int tt = tid & 255;
-        const uint8_t* src = tid < 256 ? Qs : dOs;
-        uint8_t* dst = tid < 256 ? Qt : dOt;
-        const int pg = tt & 15, dc = tt >> 4;
-        u32x4_t w[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int pos = 4 * pg + j;
-          const int rho = (pos & ~31) | swap23(pos & 31);
-          w[j] = *reinterpret_cast<const u32x4_t*>(src + rho * 256 + ((dc ^ (rho & 15)) << 4));
-        }
-#pragma unroll
-        for (int f = 0; f < 8; ++f) {
-          u32x2_t o2;
-#pragma unroll
-          for (int m = 0; m < 2; ++m) {
-            const uint32_t x = w[2 * m][f >> 1], y = w[2 * m + 1][f >> 1];
-            o2[m] = (f & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
-          }
-          const int d = dc * 8 + f;
-          *reinterpret_cast<u32x2_t*>(dst + d * 128 + (((pg >> 1) ^ (d & 7)) << 4) + (pg & 1) * 8) = o2;
-        }
-      }
-      __syncthreads();  // transposes done
       fetch(cb + kQS < cnt ? cb + kQS : cb);  // the next sub-chunk (past the end: reread, unused)
 
       // Lane-derived LDS addresses are recomputed in each phase from a copy of the
@@ -292,39 +264,52 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
         s_dp(std::integral_constant<int, 0>{});
       else
         s_dp(std::integral_constant<int, 1>{});
-      __syncthreads();  // every wave is done with Qs and dOs
-      // The wave's P goes to the dO-row area for its partner (wave w's 2 KB at w * 2 KB,
-      // operand s2 of lane l at (64 s2 + l) * 16 B); its dS rows go into Qs, row-major
-      // with keys in natural order and chunk kc at kc ^ (row & 15), for dQ and for the
-      // partner.
+      // The wave's P goes to Px for its partner (wave w's 2 KB at w * 2 KB, operand s2
+      // of lane l at (64 s2 + l) * 16 B); its dS rows go into dSs, row-major with keys
+      // in natural order and chunk kc at kc ^ (row & 15), for dQ and for the partner.
+      // Both areas were last read before the previous sub-chunk's final barrier.
       {
         const int lv = lane_v();
         const int h = lv >> 5;
         const int koff = 32 * ks + swap23(lv & 31);
-        u32x4_t* xp = reinterpret_cast<u32x4_t*>(dOs + wave * 2048) + lv;
+        u32x4_t* xp = reinterpret_cast<u32x4_t*>(Px + wave * 2048) + lv;
         xp[0] = Pp[0];
         xp[64] = Pp[1];
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int rv = dh * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
           const uint32_t w2 = dSp[v >> 3][(v & 7) >> 1];
-          *reinterpret_cast<uint16_t*>(Qs + rv * 256 + ((((koff >> 3) ^ (rv & 15))) << 4) + (koff & 7) * 2) =
+          *reinterpret_cast<uint16_t*>(dSs + rv * 256 + ((((koff >> 3) ^ (rv & 15))) << 4) + (koff & 7) * 2) =
               (uint16_t)((v & 1) ? (w2 >> 16) : (w2 & 0xffffu));
         }
       }
       __syncthreads();  // P exchanged, dS complete
       // dV += P^T dO and dK += dS^T Q over both row tiles, this wave's first: MFMA rows
       // are the wave's keys (row i holds key 32(w % 4) + swap23(i)); k-slot (h, j) of
-      // step (rt, s2) is row rt*32 + 8(2 s2 + j/4) + 4h + j%4, the transposed tiles'
-      // position rt*32 + 16 s2 + 8h + j.  The partner's P comes from the exchange area,
-      // its dS from the rows in Qs.
+      // step (rt, s2) is row rt*32 + 16 s2 + 8(j/4) + 4h + j%4.  The partner's P comes
+      // from Px, its dS from the rows in dSs.  The dO and q operands (8 rows of one dim
+      // per lane) are read from the row-major tiles with transposing LDS reads: within
+      // each group of 16 lanes, lane i receives element i % 4 of the 8 bytes read by
+      // lane 4k + i / 4, for k = 0..3; so lane j of a group reads 4 dims 4(j % 4) ..
+      // of row R0 + j / 4, and lane i gets rows R0 .. R0+3 of dim i.
       {
         const int lv = lane_v();
         const int h = lv >> 5, l32 = lv & 31;
         const int koff = 32 * ks + swap23(l32);
         const int rto = dh ^ 1;
+        const int gi = lv & 15;  // index within the 16-lane group
+        // Transposing read of 4 rows R0 .. R0+3 of tile T for dims d0 .. d0+15.
+        auto tr4 = [&](const uint8_t* T, int R0, int d0) -> u32x2_t {
+          const int R = R0 + (gi >> 2);
+          const int col = d0 + 4 * (gi & 3);
+          const uint8_t* p = T + R * 256 + ((((col >> 3) ^ (R & 15))) << 4) + (col & 7) * 2;
+          typedef short v4i16 __attribute__((ext_vector_type(4)));
+          const v4i16 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (v4i16 __attribute__((address_space(3)))*)(const_cast<uint8_t*>(p)));
+          return __builtin_bit_cast(u32x2_t, x);
+        };
         u32x4_t Po[2], dSo[2];
-        const u32x4_t* xo = reinterpret_cast<const u32x4_t*>(dOs + (wave ^ 4) * 2048) + lv;
+        const u32x4_t* xo = reinterpret_cast<const u32x4_t*>(Px + (wave ^ 4) * 2048) + lv;
         Po[0] = xo[0];
         Po[1] = xo[64];
 #pragma unroll
@@ -336,7 +321,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
             for (int e = 0; e < 2; ++e) {
               const int j = 2 * m + e;
               const int row = rto * 32 + 8 * (2 * s2 + (j >> 2)) + 4 * h + (j & 3);
-              hw[e] = *reinterpret_cast<const uint16_t*>(Qs + row * 256 + ((((koff >> 3) ^ (row & 15))) << 4) +
+              hw[e] = *reinterpret_cast<const uint16_t*>(dSs + row * 256 + ((((koff >> 3) ^ (row & 15))) << 4) +
                                                          (koff & 7) * 2);
             }
             dSo[s2][m] = hw[0] | (hw[1] << 16);
@@ -349,13 +334,15 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
           for (int s2 = 0; s2 < 2; ++s2) {
             const u32x4_t ap = tile ? Po[s2] : Pp[s2];
             const u32x4_t ad = tile ? dSo[s2] : dSp[s2];
-            const int ch = 4 * rt + 2 * s2 + h;
+            const int R0 = rt * 32 + 16 * s2 + 4 * h;
 #pragma unroll
             for (int dt = 0; dt < 2; ++dt) {
-              const int d = 64 * dh + dt * 32 + l32;
-              const u32x4_t bo = *reinterpret_cast<const u32x4_t*>(dOt + d * 128 + ((ch ^ (d & 7)) << 4));
+              const int d0 = 64 * dh + dt * 32 + (l32 & 16);  // this lane group's 16 dims
+              const u32x2_t o0 = tr4(dOs, R0, d0), o1 = tr4(dOs, R0 + 8, d0);
+              const u32x4_t bo = u32x4_t{o0[0], o0[1], o1[0], o1[1]};
               dv_acc[dt] = mfma_32x32x16(as_bf16x8(ap), as_bf16x8(bo), dv_acc[dt]);
-              const u32x4_t bq = *reinterpret_cast<const u32x4_t*>(Qt + d * 128 + ((ch ^ (d & 7)) << 4));
+              const u32x2_t q0 = tr4(Qs, R0, d0), q1 = tr4(Qs, R0 + 8, d0);
+              const u32x4_t bq = u32x4_t{q0[0], q0[1], q1[0], q1[1]};
               dk_acc[dt] = mfma_32x32x16(as_bf16x8(ad), as_bf16x8(bq), dk_acc[dt]);
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -376,7 +363,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
         for (int t = 0; t < 8; ++t) {
           const int kc = 2 * t + h;
           const u32x4_t ak = *reinterpret_cast<const u32x4_t*>(Kt + d * 256 + ((kc ^ (d & 15)) << 4));
-          const u32x4_t bs = *reinterpret_cast<const u32x4_t*>(Qs + row * 256 + ((kc ^ (row & 15)) << 4));
+          const u32x4_t bs = *reinterpret_cast<const u32x4_t*>(dSs + row * 256 + ((kc ^ (row & 15)) << 4));
           qacc = mfma_32x32x16(as_bf16x8(ak), as_bf16x8(bs), qacc);
         }
         const int pr = __shfl(cur_prv, bwd_row_lane(row));
