@@ -231,9 +231,10 @@ __global__ __launch_bounds__(256) void dec_topk_kernel(const float* __restrict__
 // Split-K attention: one workgroup per (sequence, group, part), a part being up
 // to kDecSlotsPerPart of the row's selected blocks; parts are merged by the
 // combine kernel.  The G heads of the group are the (32, G real) MFMA columns of
-// 32x32x16 bf16 MFMAs.  The workgroup stages each block's K and V^T in LDS from
-// coalesced loads (the prefill layouts); while a block is computed the next
-// block's K and V are already being loaded into registers.  Wave w takes keys
+// 32x32x16 bf16 MFMAs.  The workgroup stages each block's K and V rows in LDS from
+// coalesced loads (V^T operands are then read with transposing LDS reads); while a
+// block is computed the next block's K and V are already being loaded into
+// registers.  Wave w takes keys
 // 32w .. 32w+31 of every block (S^T = K Q^T), keeps a running max, sum and output
 // over the part's blocks (online softmax, base 2) and computes O^T = V^T P^T.  At the end the four waves' (max, sum, O) are merged in LDS
 // (rescaled to the common max) and the normalised partial with its natural-log
@@ -248,9 +249,9 @@ __global__ __launch_bounds__(256, 2) void dec_attn_kernel(const uint16_t* __rest
                                                           int kk, int nparts, float scale_log2, float v_mul,
                                                           float* __restrict__ Opart, float* __restrict__ Lpart) {
   constexpr bool kFp8 = sizeof(*cache.k) == 1;
-  static_assert(G <= 16, "the merge reuses the 32 KB V^T buffer: 4 x G x 128 fp32");
+  static_assert(G <= 16, "the merge reuses the 32 KB V buffer: 4 x G x 128 fp32");
   __shared__ __attribute__((aligned(16))) uint8_t Ks[kBk * 256];
-  __shared__ __attribute__((aligned(16))) uint8_t Vt[kDh * 256];  // reused for the merge
+  __shared__ __attribute__((aligned(16))) uint8_t Vs[kBk * 256];  // V rows; reused for the merge
   __shared__ float wm[4][32], wl[4][32];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
@@ -301,12 +302,11 @@ __global__ __launch_bounds__(256, 2) void dec_attn_kernel(const uint16_t* __rest
       kr[m] = load8(cache.k + base + (int64_t)(key < nvalid ? key : nvalid - 1) * row_stride + c * 8, false);
       if (key >= nvalid) kr[m] = Raw{};
     }
-    const int kg = tid & 15, dc = tid >> 4;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int kv = kg * 8 + e;
-      vr[e] = load8(cache.v + base + (int64_t)(kv < nvalid ? kv : nvalid - 1) * row_stride + dc * 8, true);
-      if (kv >= nvalid) vr[e] = Raw{};
+    for (int m = 0; m < 8; ++m) {
+      const int key = (tid >> 4) + 16 * m;
+      vr[m] = load8(cache.v + base + (int64_t)(key < nvalid ? key : nvalid - 1) * row_stride + c * 8, true);
+      if (key >= nvalid) vr[m] = Raw{};
     }
   };
   auto widen = [&](const Raw& x) -> u32x4_t {
@@ -315,30 +315,15 @@ __global__ __launch_bounds__(256, 2) void dec_attn_kernel(const uint16_t* __rest
     else
       return x;
   };
-  // The block to LDS from the registers: K row rho (256 B) at rho*256, chunk c at
-  // position c ^ (rho & 15); V^T[d] (256 B) holds keys in natural order, 8-key
-  // chunk kc at position kc ^ (d & 15).
+  // The block to LDS from the registers: K row rho (256 B) at rho*256 and V row key
+  // at key*256, chunk c at position c ^ (row & 15).
   auto store_block = [&]() {
     const int c = tid & 15;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       const int rho = (tid >> 4) + 16 * m;
       *reinterpret_cast<u32x4_t*>(Ks + rho * 256 + ((c ^ (rho & 15)) << 4)) = widen(kr[m]);
-    }
-    const int kg = tid & 15, dc = tid >> 4;
-    u32x4_t vw[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) vw[e] = widen(vr[e]);
-#pragma unroll
-    for (int f = 0; f < 8; ++f) {
-      u32x4_t o4;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const uint32_t x = vw[2 * m][f >> 1], y = vw[2 * m + 1][f >> 1];
-        o4[m] = (f & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
-      }
-      const int d = dc * 8 + f;
-      *reinterpret_cast<u32x4_t*>(Vt + d * 256 + ((kg ^ (d & 15)) << 4)) = o4;
+      *reinterpret_cast<u32x4_t*>(Vs + rho * 256 + ((c ^ (rho & 15)) << 4)) = widen(vr[m]);
     }
   };
   // q operand: k-slot (h, e) of step st is dim 64h + 8st + e of head l32 (zero for
@@ -420,14 +405,29 @@ __global__ __launch_bounds__(256, 2) void dec_attn_kernel(const uint16_t* __rest
       pb[hf].z = pack_bf16x2(sacc[8 * hf + 4], sacc[8 * hf + 5]);
       pb[hf].w = pack_bf16x2(sacc[8 * hf + 6], sacc[8 * hf + 7]);
     }
-    // O^T[d][head] += V^T P^T over this wave's keys: steps u = 2w + hf, V^T chunk 2u + h.
+    // O^T[d][head] += V^T P^T over this wave's keys: step u = 2w + hf takes keys
+    // 8(2u + h) .. +7 for lane half h.  The V^T operand (8 keys of one dim per lane)
+    // comes from the V rows by transposing LDS reads: within each group of 16 lanes,
+    // lane i receives element i % 4 of the 8 bytes read by lane 4k + i / 4 (k = 0..3),
+    // so lane j reads dims 4(j % 4) .. +3 of key K0 + j / 4 and lane i gets keys
+    // K0 .. K0+3 of dim i.
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      const int kc2 = 2 * (2 * wave + hf) + h;
+      const int K0 = 8 * (2 * (2 * wave + hf) + h);
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const int d = dt * 32 + l32;
-        const u32x4_t va = *reinterpret_cast<const u32x4_t*>(Vt + d * 256 + ((kc2 ^ (d & 15)) << 4));
+        const int d0 = dt * 32 + (l32 & 16);  // this lane group's 16 dims
+        u32x2_t half[2];
+#pragma unroll
+        for (int part = 0; part < 2; ++part) {
+          const int key = K0 + 4 * part + ((lane & 15) >> 2);
+          const int col = d0 + 4 * (lane & 3);
+          const uint8_t* p = Vs + key * 256 + ((((col >> 3) ^ (key & 15))) << 4) + (col & 7) * 2;
+          typedef short v4i16 __attribute__((ext_vector_type(4)));
+          half[part] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                       (v4i16 __attribute__((address_space(3)))*)(const_cast<uint8_t*>(p))));
+        }
+        const u32x4_t va = u32x4_t{half[0][0], half[0][1], half[1][0], half[1][1]};
         oacc[dt] = mfma_32x32x16(as_bf16x8(va), as_bf16x8(pb[hf]), oacc[dt]);
       }
     }
@@ -442,7 +442,7 @@ __global__ __launch_bounds__(256, 2) void dec_attn_kernel(const uint16_t* __rest
     wl[wave][l32] = l_run;
   }
   // Merge: the four waves' O^T for the G real heads, rescaled to the common max.
-  float* red = reinterpret_cast<float*>(Vt);  // [4][G][128]
+  float* red = reinterpret_cast<float*>(Vs);  // [4][G][128]
   if (l32 < G) {
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
