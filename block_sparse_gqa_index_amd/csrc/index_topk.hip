@@ -85,6 +85,9 @@ __device__ __forceinline__ void idx_block_max(const uint8_t* buf, const uint4 (&
   }
   u32x4_t a[4];
   f32x16_t acc[2];
+  // Raised wave priority over the matrix section: of the two waves of a SIMD, the
+  // one issuing MFMAs keeps the issue slot (measured: 2% less time).
+  __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int j = 0; j < kTiles; ++j) {
     const int kt = j / CT, ct = j % CT;
@@ -108,6 +111,7 @@ __device__ __forceinline__ void idx_block_max(const uint8_t* buf, const uint4 (&
     constexpr int pj = kTiles - 1, pkt = pj / CT, pct = pj % CT;
     idx_tile_reduce<CT>(acc[pj & 1], qi[pct], b, pkt, need_mask, h, bmax[pct][pkt / kPerBlock]);
   }
+  __builtin_amdgcn_s_setprio(0);
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
 #pragma unroll
