@@ -26,10 +26,9 @@
 //   128 keys (dS K, with K^T as the operand).
 // dQ leaves as one bf16 partial row per (query, slot, head), summed over the slots
 // in fp32 by a second kernel; dK and dV leave as one fp32 partial block per item, summed in
-// item order per (group, block) by a third.  No atomics touch a gradient.  dq is
-// bitwise reproducible; dK and dV sum a list's rows in the order the inverse index
-// placed its pairs (decided by its atomic counters), so they can differ between runs
-// by fp32 rounding.
+// item order per (group, block) by a third.  No atomics touch a gradient, and the
+// inverse index is built in its ordered form (each list's pairs in (query, slot)
+// order), so dq, dK and dV are bitwise reproducible for a given workspace size.
 #include <utility>
 
 #include "msa_device.h"
@@ -527,7 +526,8 @@ hipError_t launch_bwd_window(const uint16_t* q, const uint16_t* k, const uint16_
                              float* dk, float* dv, uint8_t* ws, const AttnWorkspace& L, hipStream_t stream) {
   const int G = H_q / H_kv;
   int32_t* lfirst = reinterpret_cast<int32_t*>(ws + L.lfirst);
-  hipError_t e = launch_inverse_index(block_idx, B, SeqInfo{}, 7, H_kv, kk, w0, W, ws, L, stream, lfirst);
+  hipError_t e = launch_inverse_index(block_idx, B, SeqInfo{}, 7, H_kv, kk, w0, W, ws, L, stream, lfirst,
+                                      /*ordered=*/true);
   if (e != hipSuccess) return e;
   const int32_t* n_items = reinterpret_cast<const int32_t*>(ws + L.n_items);
   const int4* items = reinterpret_cast<const int4*>(ws + L.items);

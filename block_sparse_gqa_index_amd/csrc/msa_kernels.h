@@ -19,7 +19,7 @@ constexpr int kItemChunks = 16;
 constexpr int kKlPart = 8;
 
 struct AttnWorkspace {
-  size_t counts, tsum, cursor, n_items, items, pairs, opart, lpart, lfirst, total;
+  size_t counts, tsum, cursor, n_items, items, pairs, opart, lpart, lfirst, tcount, total;
   int64_t max_items;
   int item_q;  // queries per work item
   int64_t WQ;  // queries per q-locality window
@@ -61,9 +61,12 @@ hipError_t launch_seq_tables(const int64_t* cu, int batch, int bk, uint8_t* ws, 
 // bound of the global block count).
 // Inverse index of one query window (lists, item table, pairs) in the workspace
 // regions of L; lfirst (lists entries, may be null) receives each list's first item.
+// ordered: each list's pairs in (query, slot) order, decided by no atomic (needs the
+// workspace's per-tile counts, laid out for kPartsBwd); otherwise the order within a
+// list follows the scatter's atomic counters.
 hipError_t launch_inverse_index(const int32_t* block_idx, int64_t B, const SeqInfo& si, int bsh, int H_kv, int kk,
                                 int64_t w0, int64_t W, uint8_t* ws, const AttnWorkspace& L, hipStream_t stream,
-                                int32_t* lfirst = nullptr);
+                                int32_t* lfirst = nullptr, bool ordered = false);
 
 // What the per-pair and per-item buffers hold: the attention's partial rows, the KL
 // pass's kKlPart floats per pair, or the backward's fp32 dQ rows per pair plus a

@@ -60,7 +60,8 @@ __device__ __forceinline__ void tile_block_range(const SeqInfo& si, int64_t q0, 
 
 __global__ __launch_bounds__(256) void inv_count_kernel(const int32_t* __restrict__ block_idx, SeqInfo si,
                                                         int bsh, int64_t w0, int64_t W, int H_kv, int kk, int64_t B,
-                                                        int TQ, int64_t WQ, int nW, int32_t* __restrict__ counts) {
+                                                        int TQ, int64_t WQ, int nW, int32_t* __restrict__ counts,
+                                                        int32_t* __restrict__ tcount) {
   extern __shared__ int32_t hist[];
   const int r = blockIdx.y;
   const int64_t q0 = w0 + (int64_t)blockIdx.x * TQ;
@@ -83,6 +84,8 @@ __global__ __launch_bounds__(256) void inv_count_kernel(const int32_t* __restric
   for (int64_t b = threadIdx.x; b < nh; b += 256) {
     const int c = hist[b];
     if (c) atomicAdd(&counts[lbase + gb_lo + b], c);
+    // tcount[tile][r][block]: this tile's pairs of each list (zero elsewhere).
+    if (tcount) tcount[((int64_t)blockIdx.x * H_kv + r) * B + gb_lo + b] = c;
   }
 }
 
@@ -216,6 +219,122 @@ __global__ __launch_bounds__(256) void inv_scatter_kernel(const int32_t* __restr
     const int64_t i = q0 + p / kk;
     const int s = (int)(p % kk);
     pairs[base[slot[u]] + rank[u]] = (int32_t)(((i - w0) << 5) | s);
+  }
+}
+
+// Ordered placement (used by the backward, whose dK/dV sums follow the pair order).
+// The per-tile counts become absolute bases, tile by tile in query order: list l
+// of q-window wq (first tile t0) takes tiles t0 .. t1-1 in turn from its start.
+__global__ __launch_bounds__(256) void inv_tile_base_kernel(int32_t* __restrict__ tcount,
+                                                            const int32_t* __restrict__ cursor, int64_t B, int H_kv,
+                                                            int nW, int64_t tiles, int64_t tiles_per_window) {
+  const int64_t l = (int64_t)blockIdx.x * 256 + threadIdx.x;  // list (r, wq, b)
+  if (l >= (int64_t)H_kv * nW * B) return;
+  const int64_t b = l % B, rw = l / B;
+  const int r = (int)(rw / nW), wq = (int)(rw % nW);
+  const int64_t t0 = wq * tiles_per_window;
+  const int64_t t1 = (t0 + tiles_per_window < tiles) ? t0 + tiles_per_window : tiles;
+  int32_t run = cursor[l];  // the list's start
+  for (int64_t t = t0; t < t1; ++t) {
+    int32_t* c = tcount + (t * H_kv + r) * B + b;
+    const int32_t n = *c;
+    *c = run;
+    run += n;
+  }
+}
+
+// One workgroup per (query tile, group): the tile's valid pairs are sorted in LDS
+// by (list, pair index) with a bitonic network, so that within each list they come
+// in (query, slot) order, and written at the tile's base of each list.  A tile holds
+// at most 4096 pairs (keys: list << 12 | pair index).
+__global__ __launch_bounds__(256) void inv_scatter_ordered_kernel(const int32_t* __restrict__ block_idx, SeqInfo si,
+                                                                  int bsh, int64_t w0, int64_t W, int H_kv, int kk,
+                                                                  int64_t B, int TQ,
+                                                                  const int32_t* __restrict__ tbase,
+                                                                  int32_t* __restrict__ pairs) {
+  constexpr int kN = 4096;
+  extern __shared__ int32_t sh[];
+  int32_t* keys = sh;         // kN
+  int32_t* start = sh + kN;   // nh: first sorted position of each list
+  __shared__ int32_t wsum[4];
+  const int r = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int64_t q0 = w0 + (int64_t)blockIdx.x * TQ;
+  const int64_t q1 = (q0 + TQ < w0 + W) ? q0 + TQ : w0 + W;
+  int64_t gb_lo, nh;
+  tile_block_range(si, q0, q1, bsh, gb_lo, nh);
+  for (int64_t b = tid; b < nh; b += 256) start[b] = 0;
+  __syncthreads();
+  const int npairs = (int)((q1 - q0) * kk);
+  for (int p = tid; p < kN; p += 256) {
+    int key = 0x7fffffff;
+    if (p < npairs) {
+      const int64_t i = q0 + p / kk;
+      const int sl = p % kk;
+      int sq;
+      const int64_t j0 = seq_start(si, i, sq);
+      const int b = block_idx[(i * H_kv + r) * kk + sl];
+      if (pair_valid(b, i - j0, bsh)) {
+        const int ls = (int)(gblock(si, sq, b) - gb_lo);
+        key = (ls << 12) | p;
+        atomicAdd(&start[ls], 1);  // counts only: the order of these adds is irrelevant
+      }
+    }
+    keys[p] = key;
+  }
+  __syncthreads();
+  // Exclusive scan of the per-list counts: thread t scans entries [t*per, (t+1)*per).
+  const int per = (int)((nh + 255) / 256);
+  int local = 0;
+  for (int e = 0; e < per; ++e) {
+    const int64_t b = (int64_t)tid * per + e;
+    if (b < nh) local += start[b];
+  }
+  int inc = local;
+  const int lane = tid & 63, wv = tid >> 6;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const int y = __shfl_up(inc, m);
+    if (lane >= m) inc += y;
+  }
+  if (lane == 63) wsum[wv] = inc;
+  __syncthreads();
+  int before = inc - local;
+  for (int w = 0; w < wv; ++w) before += wsum[w];
+  for (int e = 0; e < per; ++e) {
+    const int64_t b = (int64_t)tid * per + e;
+    if (b < nh) {
+      const int c = start[b];
+      start[b] = before;
+      before += c;
+    }
+  }
+  // Bitonic sort of the kN keys, ascending.
+  for (int k2 = 2; k2 <= kN; k2 <<= 1) {
+    for (int j = k2 >> 1; j > 0; j >>= 1) {
+      __syncthreads();
+      for (int idx = tid; idx < kN; idx += 256) {
+        const int partner = idx ^ j;
+        if (partner > idx) {
+          const int a = keys[idx], c = keys[partner];
+          const bool up = (idx & k2) == 0;
+          if (up ? a > c : a < c) {
+            keys[idx] = c;
+            keys[partner] = a;
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int jpos = tid; jpos < kN; jpos += 256) {
+    const int key = keys[jpos];
+    if (key == 0x7fffffff) continue;
+    const int ls = key >> 12, p = key & 4095;
+    const int64_t i = q0 + p / kk;
+    const int sl = p % kk;
+    const int32_t base = tbase[((int64_t)blockIdx.x * H_kv + r) * B + gb_lo + ls];
+    pairs[base + (jpos - start[ls])] = (int32_t)(((i - w0) << 5) | sl);
   }
 }
 
@@ -1123,6 +1242,9 @@ AttnWorkspace attn_workspace_layout(int64_t W, int H_q, int H_kv, int kk, int64_
     L.lpart = take(sizeof(float2) * max_pairs * G);
   }
   L.lfirst = take(parts == kPartsBwd ? sizeof(int32_t) * lists : 0);
+  // Per-tile list counts (then bases) of the ordered placement: tiles x H_kv x B.
+  const int64_t tq = inv_tile_queries(kk);
+  L.tcount = take(parts == kPartsBwd ? sizeof(int32_t) * ((W + tq - 1) / tq) * H_kv * B : 0);
   L.total = off;
   L.max_items = max_items;
   L.item_q = item_q;
@@ -1133,7 +1255,7 @@ AttnWorkspace attn_workspace_layout(int64_t W, int H_q, int H_kv, int kk, int64_
 // offsets and the item table, then the scatter of the (query, slot) pairs.
 hipError_t launch_inverse_index(const int32_t* block_idx, int64_t B, const SeqInfo& si, int bsh, int H_kv, int kk,
                                 int64_t w0, int64_t W, uint8_t* ws, const AttnWorkspace& L, hipStream_t stream,
-                                int32_t* lfirst) {
+                                int32_t* lfirst, bool ordered) {
   const int64_t lists = (int64_t)H_kv * L.nW * B;
   int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
   int32_t* cursor = reinterpret_cast<int32_t*>(ws + L.cursor);
@@ -1147,10 +1269,16 @@ hipError_t launch_inverse_index(const int32_t* block_idx, int64_t B, const SeqIn
 
   // Query tiles of the inverse-index passes hold at most 4096 pairs (16 per thread).
   const int TQ = inv_tile_queries(kk);
-  const dim3 igrid((unsigned)((W + TQ - 1) / TQ), (unsigned)H_kv);
+  const int64_t qtiles = (W + TQ - 1) / TQ;
+  const dim3 igrid((unsigned)qtiles, (unsigned)H_kv);
   const size_t lds_count = sizeof(int32_t) * B;
+  int32_t* tcount = ordered ? reinterpret_cast<int32_t*>(ws + L.tcount) : nullptr;
+  if (ordered) {
+    fill_i32_kernel<<<dim3(256), dim3(256), 0, stream>>>(tcount, qtiles * H_kv * B, 0);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   inv_count_kernel<<<igrid, dim3(256), lds_count, stream>>>(block_idx, si, bsh, w0, W, H_kv, kk, B, TQ, L.WQ,
-                                                             L.nW, counts);
+                                                             L.nW, counts, tcount);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const unsigned tiles = (unsigned)((lists + kScanTile - 1) / kScanTile);
   int64_t* tsum = reinterpret_cast<int64_t*>(ws + L.tsum);
@@ -1159,6 +1287,14 @@ hipError_t launch_inverse_index(const int32_t* block_idx, int64_t B, const SeqIn
   inv_scan_write_kernel<<<dim3(tiles), dim3(kScanTile), 0, stream>>>(counts, lists, L.item_q, tsum, cursor, items,
                                                                     n_items, lfirst);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ordered) {
+    inv_tile_base_kernel<<<dim3((unsigned)((lists + 255) / 256)), dim3(256), 0, stream>>>(
+        tcount, cursor, B, H_kv, L.nW, qtiles, L.WQ / TQ);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    inv_scatter_ordered_kernel<<<igrid, dim3(256), sizeof(int32_t) * 4096 + lds_count, stream>>>(
+        block_idx, si, bsh, w0, W, H_kv, kk, B, TQ, tcount, pairs);
+    return hipGetLastError();
+  }
   inv_scatter_kernel<16><<<igrid, dim3(256), 2 * lds_count, stream>>>(block_idx, si, bsh, w0, W, H_kv, kk, B,
                                                                       TQ, L.WQ, L.nW, cursor, pairs);
   return hipGetLastError();

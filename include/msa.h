@@ -142,9 +142,10 @@ msa_status_t msa_sparse_kl_fwd(const void* q, const void* k, const void* q_idx, 
  *   dk, dv     fp32 [N, H_kv, d_h]  out (overwritten, not accumulated into)
  * Limits: B_k = 128, G = H_q / H_kv <= 32, and those of msa_sparse_attn_fwd.
  * Workspace as for the forward (smaller workspaces run in query windows).  No
- * atomics touch a gradient: dq is bitwise reproducible across reruns and window
- * sizes; dk and dv sum each block's rows in the order the inverse index lists its
- * pairs (set by atomic counters there), so they vary at fp32 rounding level only.
+ * atomics touch a gradient and each block's rows are listed in (query, slot) order,
+ * so all three gradients are bitwise reproducible across reruns with the same
+ * workspace size; dq also across workspace sizes, while dk and dv then group their
+ * per-window sums differently (fp32 rounding level).
  */
 size_t msa_sparse_attn_bwd_workspace(int64_t N, int H_q, int H_kv, int d_h, int B_k, int k);
 size_t msa_sparse_attn_bwd_workspace_min(int64_t N, int H_q, int H_kv, int d_h, int B_k, int k);
