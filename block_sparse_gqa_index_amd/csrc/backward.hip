@@ -8,12 +8,13 @@
 // tokens, o = P V and D = <dO, o> per (query, head):
 //   dV = P^T dO,  dS = P * (dO V^T - D),  dQ = scale dS K,  dK = scale dS^T Q.
 //
-// Work decomposition on gfx950.  The forward's inverse index is rebuilt: for every
-// (group, block) list, items of at most 256 (query, slot) pairs.  A workgroup of
-// eight waves (two per SIMD, so one wave's LDS and memory waits overlap the other's
-// work) stages the block's K, V (rows) and K^T in LDS once per item and walks the
-// item in sub-chunks of 64 MFMA rows ((64 / G) queries x G heads), with the q and dO
-// rows of the sub-chunk in LDS both row-major and transposed.  Wave w owns keys
+// Work decomposition on gfx950.  The forward's inverse index is rebuilt (in its
+// ordered form): for every (group, block) list, items of at most 256 (query, slot)
+// pairs.  A workgroup of eight waves (two per SIMD, so one wave's LDS and memory
+// waits overlap the other's work) stages the block's K, V (rows) and K^T in LDS
+// once per item and walks the item in sub-chunks of 64 MFMA rows ((64 / G) queries
+// x G heads), with the q and dO rows of the sub-chunk in LDS row-major (operands
+// that need them transposed use transposing LDS reads).  Wave w owns keys
 // 32(w % 4) .. +31 of the block and dims 64(w / 4) .. +63 of its dK and dV:
 //   S = Q K^T and dP = dO V^T on 32x32x16 MFMAs give, per lane, one key (the lane)
 //   and 32 rows (registers), so P and dS are formed in registers; the two waves of
