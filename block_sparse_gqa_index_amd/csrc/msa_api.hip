@@ -313,8 +313,8 @@ msa_status_t msa_sparse_attn_fwd_varlen(const void* q, const void* k, const void
 // ---------------------------------------------------------------- KL alignment
 static constexpr size_t kKlLossBytes = sizeof(double) * msa::kKlLossParts;
 
-static size_t kl_workspace_bytes(int64_t N, int H_q, int H_kv, int k, bool minimum) {
-  const int64_t B = (N + msa::kBlockKeys - 1) / msa::kBlockKeys;
+static size_t kl_workspace_bytes(int64_t N, int H_q, int H_kv, int k, int B_k, bool minimum) {
+  const int64_t B = (N + B_k - 1) / B_k;
   const int64_t Wmin = N < msa::kBlockKeys ? N : msa::kBlockKeys;
   const int64_t W = minimum ? Wmin : window_for_bytes(N, B, H_q, H_kv, k, kDefaultAttnWorkspace, msa::kPartsKl);
   return kKlLossBytes + msa::attn_workspace_layout(W, H_q, H_kv, k, B, msa::kPartsKl).total;
@@ -325,18 +325,17 @@ static msa_status_t check_kl_shape(int64_t N, int H_q, int H_kv, int d_h, int d_
   if (st != MSA_OK) return st;
   if (d_idx != msa::kIndexDim) return fail(MSA_ERR_UNSUPPORTED, "d_idx must be %d (got %d)", msa::kIndexDim, d_idx);
   if (H_q / H_kv > 32) return fail(MSA_ERR_UNSUPPORTED, "G = H_q / H_kv must be <= 32 for the KL pass");
-  if (B_k != msa::kBlockKeys) return fail(MSA_ERR_UNSUPPORTED, "the KL pass supports B_k = 128");
   return MSA_OK;
 }
 
 size_t msa_sparse_kl_fwd_workspace(int64_t N, int H_q, int H_kv, int d_h, int d_idx, int B_k, int k) {
   if (check_kl_shape(N, H_q, H_kv, d_h, d_idx, B_k, k) != MSA_OK || N == 0) return 0;
-  return kl_workspace_bytes(N, H_q, H_kv, k, false);
+  return kl_workspace_bytes(N, H_q, H_kv, k, B_k, false);
 }
 
 size_t msa_sparse_kl_fwd_workspace_min(int64_t N, int H_q, int H_kv, int d_h, int d_idx, int B_k, int k) {
   if (check_kl_shape(N, H_q, H_kv, d_h, d_idx, B_k, k) != MSA_OK || N == 0) return 0;
-  return kl_workspace_bytes(N, H_q, H_kv, k, true);
+  return kl_workspace_bytes(N, H_q, H_kv, k, B_k, true);
 }
 
 msa_status_t msa_sparse_kl_fwd(const void* q, const void* k, const void* q_idx, const void* k_idx,
@@ -366,7 +365,7 @@ msa_status_t msa_sparse_kl_fwd(const void* q, const void* k, const void* q_idx, 
     const int64_t Wn = (N - w0 < W) ? N - w0 : W;
     hipError_t e = msa::launch_sparse_kl_window(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(q_idx),
-        static_cast<const uint16_t*>(k_idx), lse, block_idx, N, B, H_q, H_kv, k_sel, scale, w0, Wn, cus, kl, lse_idx,
+        static_cast<const uint16_t*>(k_idx), lse, block_idx, N, B, B_k, H_q, H_kv, k_sel, scale, w0, Wn, cus, kl, lse_idx,
         w + kKlLossBytes, L, stream);
     if (e != hipSuccess) return hip_fail(e, "sparse_kl launch");
   }

@@ -893,7 +893,9 @@ struct KlRows {
   static constexpr bool kCross = G >= 8;         // the other heads are in lane ^ 32
 };
 
-template <int G>
+// BK: keys per block (64 or 128); a 64-key block fills the first half of the
+// staged tiles, and only its two 32-key tiles are computed.
+template <int G, int BK>
 __global__ __launch_bounds__(kAttnThreads, 2) void kl_pair_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp, const uint16_t* __restrict__ q_idx,
     const uint16_t* __restrict__ k_idx, const float* __restrict__ lse, const int4* __restrict__ items,
@@ -929,8 +931,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void kl_pair_kernel(
     {
       int stid = tid;
       asm volatile("" : "+v"(stid));
-      const int64_t tok0 = b * kBk;
-      const int nvalid = (N - tok0 < kBk) ? (int)(N - tok0) : kBk;
+      const int64_t tok0 = b * BK;
+      const int nvalid = (N - tok0 < BK) ? (int)(N - tok0) : BK;
       stage_k(kp + tok0 * H_kv * kDh + r * kDh, H_kv * kDh, nvalid, Ks, stid);
       stage_kidx(k_idx + tok0 * kDidx, nvalid, KIs, stid);
     }
@@ -1015,8 +1017,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void kl_pair_kernel(
       bool part_blk = false;
 #pragma unroll
       for (int qq = 0; qq < NQ; ++qq) {
-        lim[qq] = (int)(w0 + (prq[qq] >> 5) - b * kBk);
-        part_blk |= lim[qq] < kBk - 1;
+        lim[qq] = (int)(w0 + (prq[qq] >> 5) - b * BK);
+        part_blk |= lim[qq] < BK - 1;
       }
       part_blk = __any(part_blk);
       float A[NQ], C[NQ], Z[NQ], mx[NQ], l[NQ];
@@ -1026,7 +1028,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void kl_pair_kernel(
         mx[qq] = -__builtin_inff();
       }
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
+      for (int kt = 0; kt < BK / 32; ++kt) {
         f32x16_t sacc = f32x16_t{}, iacc = f32x16_t{};
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
@@ -1096,15 +1098,15 @@ __global__ __launch_bounds__(kAttnThreads, 2) void kl_pair_kernel(
 // Per (query, group): sum of the valid slots' partials, then KL and LSE_idx.
 __global__ __launch_bounds__(256) void kl_combine_kernel(const float* __restrict__ part,
                                                          const int32_t* __restrict__ block_idx, int64_t w0,
-                                                         int64_t W, int H_kv, int kk, float* __restrict__ kl,
-                                                         float* __restrict__ lse_idx) {
+                                                         int64_t W, int H_kv, int kk, int bsh,
+                                                         float* __restrict__ kl, float* __restrict__ lse_idx) {
   const int64_t ir = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (ir >= W * H_kv) return;
   const int64_t i = w0 + ir / H_kv;
   const int32_t* sel = block_idx + (w0 * H_kv + ir) * kk;
   float A = 0.f, C = 0.f, Z = 0.f, M = -__builtin_inff(), L = 0.f;
   for (int s = 0; s < kk; ++s) {
-    if (!pair_valid(sel[s], i, 7)) continue;  // B_k = 128
+    if (!pair_valid(sel[s], i, bsh)) continue;
     const float* src = part + (ir * kk + s) * kKlPart;
     const float4 a = *reinterpret_cast<const float4*>(src);
     const float l = src[4];
@@ -1384,11 +1386,12 @@ hipError_t launch_sparse_attn_window(const uint16_t* q, const uint16_t* k, const
 
 hipError_t launch_sparse_kl_window(const uint16_t* q, const uint16_t* k, const uint16_t* q_idx,
                                    const uint16_t* k_idx, const float* lse, const int32_t* block_idx, int64_t N,
-                                   int64_t B, int H_q, int H_kv, int kk, float scale, int64_t w0, int64_t W,
+                                   int64_t B, int bk, int H_q, int H_kv, int kk, float scale, int64_t w0, int64_t W,
                                    int num_cus, float* kl, float* lse_idx, uint8_t* ws, const AttnWorkspace& L,
                                    hipStream_t stream) {
   const int G = H_q / H_kv;
-  hipError_t e = launch_inverse_index(block_idx, B, SeqInfo{}, 7, H_kv, kk, w0, W, ws, L, stream);
+  const int bsh = bk == 64 ? 6 : 7;
+  hipError_t e = launch_inverse_index(block_idx, B, SeqInfo{}, bsh, H_kv, kk, w0, W, ws, L, stream);
   if (e != hipSuccess) return e;
   const int32_t* n_items = reinterpret_cast<const int32_t*>(ws + L.n_items);
   const int4* items = reinterpret_cast<const int4*>(ws + L.items);
@@ -1401,8 +1404,12 @@ hipError_t launch_sparse_kl_window(const uint16_t* q, const uint16_t* k, const u
   switch (G) {
 #define MSA_KL_CASE(GG)                                                                                    \
   case GG:                                                                                                 \
-    kl_pair_kernel<GG><<<dim3((unsigned)grid), dim3(kAttnThreads), 0, stream>>>(                           \
-        q, k, q_idx, k_idx, lse, items, n_items, pairs, N, H_kv, B, L.nW, kk, w0, scale_log2, part);       \
+    if (bk == 64)                                                                                          \
+      kl_pair_kernel<GG, 64><<<dim3((unsigned)grid), dim3(kAttnThreads), 0, stream>>>(                     \
+          q, k, q_idx, k_idx, lse, items, n_items, pairs, N, H_kv, B, L.nW, kk, w0, scale_log2, part);     \
+    else                                                                                                   \
+      kl_pair_kernel<GG, 128><<<dim3((unsigned)grid), dim3(kAttnThreads), 0, stream>>>(                    \
+          q, k, q_idx, k_idx, lse, items, n_items, pairs, N, H_kv, B, L.nW, kk, w0, scale_log2, part);     \
     break;
     MSA_KL_CASE(1)
     MSA_KL_CASE(2)
@@ -1417,7 +1424,7 @@ hipError_t launch_sparse_kl_window(const uint16_t* q, const uint16_t* k, const u
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t rows = W * H_kv;
   kl_combine_kernel<<<dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream>>>(part, block_idx, w0, W, H_kv,
-                                                                                     kk, kl, lse_idx);
+                                                                                     kk, bsh, kl, lse_idx);
   return hipGetLastError();
 }
 

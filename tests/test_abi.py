@@ -206,7 +206,7 @@ def test_sparse_kl_rejects_bad_arguments(lib):
         return raw.msa_sparse_kl_fwd(f, f, f, f, f, lse, N, H_q, H_kv, d_h, d_idx, B_k, k, scale, f, f, loss, ws,
                                      ws_bytes, None)
 
-    assert call(B_k=64) == lib.MSA_ERR_UNSUPPORTED
+    assert call(B_k=32) == lib.MSA_ERR_UNSUPPORTED
 
     assert call(d_idx=32) == lib.MSA_ERR_UNSUPPORTED
     assert call(H_q=128, H_kv=2) == lib.MSA_ERR_UNSUPPORTED  # G = 64 > 32

@@ -107,3 +107,21 @@ def test_decode_bk64(msa, case):
     if tie.any():
         o_ref, lse_ref = oracle.decode_attn(d.q, d.k_cache, d.v_cache, d.cu_seqlens, bi_gpu, BK)
     check_attn(o.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, f"decode B_k=64 case {case}")
+
+
+@pytest.mark.parametrize("N,H_q,H_kv,k", [(3000, 8, 2, 12), (700, 16, 1, 5), (129, 4, 4, 2), (2100, 32, 1, 32)])
+def test_sparse_kl_bk64(msa, N, H_q, H_kv, k):
+    """The KL alignment pass over 64-key blocks (Eq. 9-10), on the GPU's own selection."""
+    from tests.test_gpu_kl import _check_kl
+    inp = synth.small_prefill(N=N, H_q=H_q, H_kv=H_kv, k=k, seed=1900 + N, B_k=BK, needles=1 if N >= 2000 else 0,
+                              device=DEV)
+    bi = msa.msa_index_topk(inp.q_idx, inp.k_idx, k, B_k=BK)
+    _, lse = msa.msa_sparse_attn_fwd(inp.q, inp.k, inp.v, bi, B_k=BK)
+    kl, lse_idx, loss = msa.msa_sparse_kl_fwd(inp.q, inp.k, inp.q_idx, inp.k_idx, bi, lse, B_k=BK)
+    wmin = msa.msa_sparse_kl_fwd_workspace(N, H_q, H_kv, k, B_k=BK, minimum=True)
+    ws = torch.empty(wmin, dtype=torch.uint8, device=DEV)
+    kl2, li2, loss2 = msa.msa_sparse_kl_fwd(inp.q, inp.k, inp.q_idx, inp.k_idx, bi, lse, B_k=BK, workspace=ws)
+    torch.cuda.synchronize()
+    kl_ref, li_ref = oracle.sparse_kl(inp.q, inp.k, inp.q_idx, inp.k_idx, bi.cpu().numpy(), BK)
+    _check_kl(kl, lse_idx, loss, kl_ref, li_ref, f"B_k=64 N={N} H_q={H_q} H_kv={H_kv} k={k}")
+    assert torch.equal(kl, kl2) and torch.equal(lse_idx, li2)
