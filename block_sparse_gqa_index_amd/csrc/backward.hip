@@ -112,7 +112,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
     const uint16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Drow,
     const int4* __restrict__ items, const int32_t* __restrict__ n_items_ptr, const int32_t* __restrict__ pairs,
-    int64_t N, int H_kv, int64_t B, int nW, int kk, int64_t w0, float scale, float scale_log2,
+    int64_t N, int H_kv, int64_t B, int bk, int nW, int kk, int64_t w0, float scale, float scale_log2,
     uint16_t* __restrict__ dq_part, float* __restrict__ dkv_part) {
   static_assert(G <= 32, "a sub-chunk holds at least two queries");
   constexpr int kQS = kBwdRows / G;  // queries per sub-chunk
@@ -148,8 +148,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
       // Threads 0..255 stage K and V rows, threads 256..511 K^T.
       int stid = tid & 255;
       asm volatile("" : "+v"(stid));
-      const int64_t tok0 = b * kBk;
-      const int nvalid = (N - tok0 < kBk) ? (int)(N - tok0) : kBk;
+      // A block of bk (64 or 128) keys fills the first bk rows of the staged tiles.
+      const int64_t tok0 = b * bk;
+      const int nvalid = (N - tok0 < bk) ? (int)(N - tok0) : bk;
       const int64_t base = tok0 * H_kv * kDh + r * kDh;
       if (tid < 256) {
         stage_k(kp + base, H_kv * kDh, nvalid, Ks, stid);
@@ -180,8 +181,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
       my_l2 = lse[my_row] * kLog2e;
       my_D = Drow[my_row];
       my_prv = my_valid ? my_pr : -1;
-      // A listed pair's query sees at least key 0 of the block: 0 <= lim.
-      my_lim = my_valid ? (int)(w0 + (my_pr >> 5) - b * kBk) : -1;
+      // A listed pair's query sees at least key 0 of the block: 0 <= lim; keys past
+      // the block (bk = 64) are excluded with it.
+      const int64_t lim = w0 + (my_pr >> 5) - b * bk;
+      my_lim = my_valid ? (int)(lim < bk - 1 ? lim : bk - 1) : -1;
       const int c = tid & 15;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -402,7 +405,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
 // loads can be issued four at a time.
 __global__ __launch_bounds__(256) void bwd_dq_combine_kernel(const uint16_t* __restrict__ dq_part,
                                                              const int32_t* __restrict__ block_idx, int64_t w0,
-                                                             int64_t W, int H_kv, int G, int kk,
+                                                             int64_t W, int H_kv, int G, int kk, int bsh,
                                                              float* __restrict__ dq) {
   const int64_t gr = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;  // (query in window, head)
   const int l = threadIdx.x & 15;
@@ -416,7 +419,7 @@ __global__ __launch_bounds__(256) void bwd_dq_combine_kernel(const uint16_t* __r
   uint32_t vmask = 0;  // kk <= 32
   for (int s = 0; s < kk; ++s) {
     const int bb = sel[s];
-    if (bb >= 0 && (int64_t)bb <= (i >> 7)) vmask |= 1u << s;
+    if (bb >= 0 && (int64_t)bb <= (i >> bsh)) vmask |= 1u << s;
   }
   const uint16_t* base = dq_part + ((il * H_kv + r) * kk * G + g) * kDh + 8 * l;
   const int64_t sstride = (int64_t)G * kDh;  // elements between consecutive slots' rows
@@ -458,7 +461,7 @@ __global__ __launch_bounds__(256) void bwd_dq_combine_kernel(const uint16_t* __r
 __global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(const float* __restrict__ dkv_part,
                                                             const int32_t* __restrict__ counts,
                                                             const int32_t* __restrict__ lfirst, int item_q,
-                                                            int64_t B, int nW, int H_kv, int64_t N,
+                                                            int64_t B, int bk, int nW, int H_kv, int64_t N,
                                                             float* __restrict__ dk, float* __restrict__ dv) {
   const int64_t rb = blockIdx.x;
   const int r = (int)(rb / B);
@@ -468,8 +471,8 @@ __global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(const float* __restr
     const int e = 4 * e4;
     const int which = e / kBlockElems, kd = e % kBlockElems;
     const int key = kd / kDh, d = kd % kDh;
-    const int64_t tok = b * kBk + key;
-    if (tok >= N) continue;
+    const int64_t tok = b * bk + key;
+    if (key >= bk || tok >= N) continue;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     auto add = [&](const float4& x) {
       acc.x += x.x;
@@ -523,11 +526,13 @@ hipError_t launch_bwd_prepare(const uint16_t* dO, const float* o, int64_t rows, 
 
 hipError_t launch_bwd_window(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dO,
                              const float* lse, const float* D, const int32_t* block_idx, int64_t N, int64_t B,
-                             int H_q, int H_kv, int kk, float scale, int64_t w0, int64_t W, int num_cus, float* dq,
-                             float* dk, float* dv, uint8_t* ws, const AttnWorkspace& L, hipStream_t stream) {
+                             int bk, int H_q, int H_kv, int kk, float scale, int64_t w0, int64_t W, int num_cus,
+                             float* dq, float* dk, float* dv, uint8_t* ws, const AttnWorkspace& L,
+                             hipStream_t stream) {
   const int G = H_q / H_kv;
+  const int bsh = bk == 64 ? 6 : 7;
   int32_t* lfirst = reinterpret_cast<int32_t*>(ws + L.lfirst);
-  hipError_t e = launch_inverse_index(block_idx, B, SeqInfo{}, 7, H_kv, kk, w0, W, ws, L, stream, lfirst,
+  hipError_t e = launch_inverse_index(block_idx, B, SeqInfo{}, bsh, H_kv, kk, w0, W, ws, L, stream, lfirst,
                                       /*ordered=*/true);
   if (e != hipSuccess) return e;
   const int32_t* n_items = reinterpret_cast<const int32_t*>(ws + L.n_items);
@@ -544,7 +549,7 @@ hipError_t launch_bwd_window(const uint16_t* q, const uint16_t* k, const uint16_
 #define MSA_BWD_CASE(GG)                                                                                  \
   case GG:                                                                                                \
     bwd_kernel<GG><<<dim3((unsigned)grid), dim3(kBwdThreads), 0, stream>>>(                                \
-        q, k, v, dO, lse, D, items, n_items, pairs, N, H_kv, B, L.nW, kk, w0, scale, scale_log2, dq_part,   \
+        q, k, v, dO, lse, D, items, n_items, pairs, N, H_kv, B, bk, L.nW, kk, w0, scale, scale_log2, dq_part, \
         dkv_part);                                                                                        \
     break;
     MSA_BWD_CASE(1)
@@ -560,10 +565,10 @@ hipError_t launch_bwd_window(const uint16_t* q, const uint16_t* k, const uint16_
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t rows = W * H_q;
   bwd_dq_combine_kernel<<<dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, stream>>>(
-      dq_part, block_idx, w0, W, H_kv, G, kk, dq);
+      dq_part, block_idx, w0, W, H_kv, G, kk, bsh, dq);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   bwd_kv_reduce_kernel<<<dim3((unsigned)(H_kv * B)), dim3(256), 0, stream>>>(dkv_part, counts, lfirst, L.item_q, B,
-                                                                             L.nW, H_kv, N, dk, dv);
+                                                                             bk, L.nW, H_kv, N, dk, dv);
   return hipGetLastError();
 }
 

@@ -380,13 +380,12 @@ static size_t bwd_d_bytes(int64_t N, int H_q) { return ((sizeof(float) * (size_t
 static msa_status_t check_bwd_shape(int64_t N, int H_q, int H_kv, int d_h, int B_k, int k) {
   msa_status_t st = check_attn_shape(N, H_q, H_kv, d_h, B_k, k);
   if (st != MSA_OK) return st;
-  if (B_k != msa::kBlockKeys) return fail(MSA_ERR_UNSUPPORTED, "the backward supports B_k = 128");
   if (H_q / H_kv > 32) return fail(MSA_ERR_UNSUPPORTED, "the backward supports G = H_q / H_kv <= 32");
   return MSA_OK;
 }
 
-static size_t bwd_workspace_bytes(int64_t N, int H_q, int H_kv, int k, bool minimum) {
-  const int64_t B = (N + msa::kBlockKeys - 1) / msa::kBlockKeys;
+static size_t bwd_workspace_bytes(int64_t N, int H_q, int H_kv, int k, int B_k, bool minimum) {
+  const int64_t B = (N + B_k - 1) / B_k;
   const int64_t Wmin = N < msa::kBlockKeys ? N : msa::kBlockKeys;
   const int64_t W = minimum ? Wmin : window_for_bytes(N, B, H_q, H_kv, k, kDefaultAttnWorkspace, msa::kPartsBwd);
   return bwd_d_bytes(N, H_q) + msa::attn_workspace_layout(W, H_q, H_kv, k, B, msa::kPartsBwd).total;
@@ -394,12 +393,12 @@ static size_t bwd_workspace_bytes(int64_t N, int H_q, int H_kv, int k, bool mini
 
 size_t msa_sparse_attn_bwd_workspace(int64_t N, int H_q, int H_kv, int d_h, int B_k, int k) {
   if (check_bwd_shape(N, H_q, H_kv, d_h, B_k, k) != MSA_OK || N == 0) return 0;
-  return bwd_workspace_bytes(N, H_q, H_kv, k, false);
+  return bwd_workspace_bytes(N, H_q, H_kv, k, B_k, false);
 }
 
 size_t msa_sparse_attn_bwd_workspace_min(int64_t N, int H_q, int H_kv, int d_h, int B_k, int k) {
   if (check_bwd_shape(N, H_q, H_kv, d_h, B_k, k) != MSA_OK || N == 0) return 0;
-  return bwd_workspace_bytes(N, H_q, H_kv, k, true);
+  return bwd_workspace_bytes(N, H_q, H_kv, k, B_k, true);
 }
 
 msa_status_t msa_sparse_attn_bwd(const void* q, const void* k, const void* v, const float* o, const float* lse,
@@ -434,7 +433,7 @@ msa_status_t msa_sparse_attn_bwd(const void* q, const void* k, const void* v, co
     const int64_t Wn = (N - w0 < W) ? N - w0 : W;
     e = msa::launch_bwd_window(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dO), lse, D, block_idx,
-                               N, B, H_q, H_kv, k_sel, scale, w0, Wn, cus, dq, dk, dv, w + dbytes, L, stream);
+                               N, B, B_k, H_q, H_kv, k_sel, scale, w0, Wn, cus, dq, dk, dv, w + dbytes, L, stream);
     if (e != hipSuccess) return hip_fail(e, "backward launch");
   }
   return ok();

@@ -98,8 +98,9 @@ hipError_t launch_bwd_prepare(const uint16_t* dO, const float* o, int64_t rows, 
                               int64_t kv_elems, hipStream_t stream);
 hipError_t launch_bwd_window(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dO,
                              const float* lse, const float* D, const int32_t* block_idx, int64_t N, int64_t B,
-                             int H_q, int H_kv, int kk, float scale, int64_t w0, int64_t W, int num_cus, float* dq,
-                             float* dk, float* dv, uint8_t* ws, const AttnWorkspace& L, hipStream_t stream);
+                             int bk, int H_q, int H_kv, int kk, float scale, int64_t w0, int64_t W, int num_cus,
+                             float* dq, float* dk, float* dv, uint8_t* ws, const AttnWorkspace& L,
+                             hipStream_t stream);
 
 DecodeWorkspace decode_workspace_layout(int batch, int H_q, int H_kv, int kk, int64_t Bmax);
 hipError_t launch_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_t* k_cache,

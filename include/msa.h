@@ -28,8 +28,8 @@
  *     on the calling thread.
  *   - Blocks are numbered from 0: block b holds tokens [b*B_k, min((b+1)*B_k, N)).
  *     Head h belongs to group h / (H_q / H_kv) (adjacent heads share a KV head).
- *   - Supported shapes: d_h = 128, d_idx = 64, B_k = 64 or 128 (the paged decode
- *     and the backward: 128), 1 <= k <= 32,
+ *   - Supported shapes: d_h = 128, d_idx = 64, B_k = 64 or 128 (the paged decode:
+ *     128), 1 <= k <= 32,
  *     H_q / H_kv a power of two <= 128 and ceil(N / B_k) <= 8192 (N <= 2^20 at
  *     B_k = 128, 2^19 at 64).
  *     Other shapes return MSA_ERR_UNSUPPORTED.  N = 0 (or batch = 0) is a valid
@@ -142,7 +142,7 @@ msa_status_t msa_sparse_kl_fwd(const void* q, const void* k, const void* q_idx, 
  *   dO         bf16 [N, H_q, d_h]
  *   dq         fp32 [N, H_q, d_h]   out
  *   dk, dv     fp32 [N, H_kv, d_h]  out (overwritten, not accumulated into)
- * Limits: B_k = 128, G = H_q / H_kv <= 32, and those of msa_sparse_attn_fwd.
+ * Limits: G = H_q / H_kv <= 32, and those of msa_sparse_attn_fwd (B_k = 64 or 128).
  * Workspace as for the forward (smaller workspaces run in query windows).  No
  * atomics touch a gradient and each block's rows are listed in (query, slot) order,
  * so all three gradients are bitwise reproducible across reruns with the same

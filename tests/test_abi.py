@@ -252,7 +252,7 @@ def test_backward_rejects_bad_arguments(lib):
         return raw.msa_sparse_attn_bwd(f, f, f, o, f, f, f, N, H_q, H_kv, d_h, B_k, k, 0.088, dq, f, f, ws,
                                        ws_bytes, None)
 
-    assert call(B_k=64) == lib.MSA_ERR_UNSUPPORTED
+    assert call(B_k=32) == lib.MSA_ERR_UNSUPPORTED
     assert call(H_q=128, H_kv=2) == lib.MSA_ERR_UNSUPPORTED
     assert call(o=None) == lib.MSA_ERR_INVALID_ARG
     assert call(dq=f + 4) == lib.MSA_ERR_INVALID_ARG

@@ -125,3 +125,26 @@ def test_sparse_kl_bk64(msa, N, H_q, H_kv, k):
     kl_ref, li_ref = oracle.sparse_kl(inp.q, inp.k, inp.q_idx, inp.k_idx, bi.cpu().numpy(), BK)
     _check_kl(kl, lse_idx, loss, kl_ref, li_ref, f"B_k=64 N={N} H_q={H_q} H_kv={H_kv} k={k}")
     assert torch.equal(kl, kl2) and torch.equal(lse_idx, li2)
+
+
+@pytest.mark.parametrize("N,H_q,H_kv,k", [(1000, 16, 2, 4), (129, 8, 1, 2), (65, 4, 4, 3), (2600, 32, 1, 9),
+                                         (3000, 4, 2, 32)])
+def test_backward_bk64(msa, N, H_q, H_kv, k):
+    """Gradients of Eq. 8 over 64-key blocks (selection fixed, taken from the oracle), and
+    the same dK, dV bit for bit from a rerun with the minimum workspace."""
+    from tests.test_gpu_backward import check_grads
+    inp = synth.small_prefill(N=N, H_q=H_q, H_kv=H_kv, k=k, seed=2000 + N, B_k=BK, needles=1 if N >= 2000 else 0,
+                              device=DEV)
+    bi = oracle.topk(oracle.block_scores(inp.q_idx, inp.k_idx, BK), k, BK)
+    bi_d = torch.from_numpy(bi).to(DEV)
+    o, lse = msa.msa_sparse_attn_fwd(inp.q, inp.k, inp.v, bi_d, B_k=BK)
+    g = torch.Generator(device=DEV).manual_seed(N)
+    dO = torch.randn(inp.q.shape, generator=g, device=DEV).to(torch.bfloat16)
+    grads = msa.msa_sparse_attn_bwd(inp.q, inp.k, inp.v, o, lse, dO, bi_d, B_k=BK)
+    wmin = msa.msa_sparse_attn_bwd_workspace(N, H_q, H_kv, k, B_k=BK, minimum=True)
+    ws = torch.empty(wmin, dtype=torch.uint8, device=DEV)
+    g2 = msa.msa_sparse_attn_bwd(inp.q, inp.k, inp.v, o, lse, dO, bi_d, B_k=BK, workspace=ws)
+    torch.cuda.synchronize()
+    ref = oracle.sparse_attn_bwd(inp.q, inp.k, inp.v, dO, bi, BK)
+    check_grads(grads, ref, f"B_k=64 N={N} H_q={H_q} H_kv={H_kv} k={k}")
+    check_grads(g2, ref, f"B_k=64 min workspace N={N}")
