@@ -38,15 +38,18 @@ struct PackedCache {
   const int64_t* cu;
   static constexpr int bk = BK;
   __device__ int64_t len(int s) const { return cu[s + 1] - cu[s]; }
-  // First index key of 128-key tile t of sequence s (keys are consecutive rows).
-  __device__ const uint16_t* kidx_tile(int s, int64_t t) const { return kidx + (cu[s] + t * kBk) * kDidx; }
+  // Index key 64h of 128-key tile t of sequence s (keys are consecutive rows).
+  __device__ const uint16_t* kidx_half(int s, int64_t t, int h, int64_t) const {
+    return kidx + (cu[s] + t * kBk + 64 * h) * kDidx;
+  }
   // Element offset of (block b, key 0, group r) in the K/V rows; rows are H_kv * d_h apart.
   __device__ int64_t kv_block(int s, int64_t b, int r, int H_kv) const { return ((cu[s] + b * bk) * H_kv + r) * kDh; }
 };
 
-// Paged: pages of kBk tokens, token j of sequence s in row j % kBk of page
-// table[s][j / kBk]; K/V pages hold FP8 E4M3 codes (K = k_scale * value, V = v_scale *
-// value, the scales applied by the caller's arithmetic), index-key pages bf16.
+// Paged: pages of BK tokens (one block), token j of sequence s in row j % BK of
+// page table[s][j / BK]; K/V pages hold FP8 E4M3 codes (K = k_scale * value, V =
+// v_scale * value, the scales applied by the caller's arithmetic), index-key pages bf16.
+template <int BK>
 struct PagedFp8Cache {
   const uint8_t* k;
   const uint8_t* v;
@@ -54,12 +57,22 @@ struct PagedFp8Cache {
   const int32_t* table;
   int64_t max_blocks;
   const int64_t* lens;
-  static constexpr int bk = kBk;  // a page is one block
+  static constexpr int bk = BK;
   __device__ int64_t len(int s) const { return lens[s]; }
   __device__ int64_t page(int s, int64_t b) const { return table[(int64_t)s * max_blocks + b]; }
-  __device__ const uint16_t* kidx_tile(int s, int64_t t) const { return kidx + page(s, t) * kBk * kDidx; }
+  // Index key 64h of 128-key tile t.  With 64-token pages the half is a page of its
+  // own; a half past the sequence end (L tokens) reads no table entry of it.
+  __device__ const uint16_t* kidx_half(int s, int64_t t, int h, int64_t L) const {
+    if constexpr (BK == 64) {
+      const int64_t last = (L - 1) / BK;
+      const int64_t pb = (2 * t + h < last) ? 2 * t + h : last;
+      return kidx + page(s, pb) * BK * kDidx;
+    } else {
+      return kidx + (page(s, t) * BK + 64 * h) * kDidx;
+    }
+  }
   __device__ int64_t kv_block(int s, int64_t b, int r, int H_kv) const {
-    return (page(s, b) * kBk * H_kv + r) * kDh;
+    return (page(s, b) * BK * H_kv + r) * kDh;
   }
 };
 
@@ -86,7 +99,8 @@ __global__ __launch_bounds__(256) void dec_score_kernel(const uint16_t* __restri
   const int64_t nb = (L + kBk - 1) / kBk;  // 128-key tiles of this sequence
   const int64_t b = (int64_t)blockIdx.y * kScoreBlocksPerWG + wave;
   if (b >= nb || b * (kBk / bk) >= Bmax) return;
-  const uint16_t* __restrict__ kb = cache.kidx_tile(s, b);
+  const uint16_t* __restrict__ kb0 = cache.kidx_half(s, b, 0, L);
+  const uint16_t* __restrict__ kb1 = cache.kidx_half(s, b, 1, L);
   const int col = lane & 15, grp = lane >> 4;
   uint4 qop[2];
 #pragma unroll
@@ -96,13 +110,15 @@ __global__ __launch_bounds__(256) void dec_score_kernel(const uint16_t* __restri
   // The block's 128 index keys (16 KB, read once per step: non-temporal) are all
   // requested before the first MFMA, fully coalesced: load j of lane l reads
   // 16-byte chunk l%8 of row 8j + l/8.  Keys past the sequence end re-read its last
-  // key (a valid address); their scores are masked below.
+  // key (a valid address); their scores are masked below.  Rows 64 and up of the tile
+  // come from its second half (for j < 8 the row is below 64 by construction).
   u32x4_t raw[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int64_t key = b * kBk + 8 * j + (lane >> 3);
     const int kr = (int)((key < L ? key : L - 1) - b * kBk);
-    raw[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kb + kr * kDidx + (lane & 7) * 8));
+    const uint16_t* row = (j < 8 || kr < 64) ? kb0 + kr * kDidx : kb1 + (kr - 64) * kDidx;
+    raw[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row + (lane & 7) * 8));
   }
   // Half a block at a time through the wave's LDS buffer into the MFMA operand
   // layout (lane (col, grp) holds row col of a 16-row tile, dims 32ks + 8grp ..
@@ -596,9 +612,14 @@ hipError_t launch_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_
 hipError_t launch_decode_paged(const uint16_t* q, const uint16_t* q_idx, const uint8_t* k_pages,
                                const uint8_t* v_pages, float k_scale, float v_scale, const uint16_t* kidx_pages,
                                const int32_t* block_table, int64_t max_blocks, const int64_t* seqlens, int batch,
-                               int64_t Bmax, int H_q, int H_kv, int kk, float scale, int32_t* block_idx, float* o,
-                               float* lse, uint8_t* ws, const DecodeWorkspace& L, hipStream_t stream) {
-  const PagedFp8Cache cache{k_pages, v_pages, kidx_pages, block_table, max_blocks, seqlens};
+                               int64_t Bmax, int bk, int H_q, int H_kv, int kk, float scale, int32_t* block_idx,
+                               float* o, float* lse, uint8_t* ws, const DecodeWorkspace& L, hipStream_t stream) {
+  if (bk == 64) {
+    const PagedFp8Cache<64> cache{k_pages, v_pages, kidx_pages, block_table, max_blocks, seqlens};
+    return launch_decode_impl(q, q_idx, cache, batch, Bmax, H_q, H_kv, kk, scale * k_scale * kLog2e, v_scale,
+                              block_idx, o, lse, ws, L, stream);
+  }
+  const PagedFp8Cache<128> cache{k_pages, v_pages, kidx_pages, block_table, max_blocks, seqlens};
   return launch_decode_impl(q, q_idx, cache, batch, Bmax, H_q, H_kv, kk, scale * k_scale * kLog2e, v_scale,
                             block_idx, o, lse, ws, L, stream);
 }

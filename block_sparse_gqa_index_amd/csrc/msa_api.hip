@@ -511,7 +511,6 @@ msa_status_t msa_decode_paged(const void* q, const void* q_idx, const void* k_pa
                               float* o, float* lse, void* ws, size_t ws_bytes, void* hip_stream) {
   msa_status_t st = check_decode_shape(batch, max_len, H_q, H_kv, d_h, d_idx, B_k, k);
   if (st != MSA_OK) return st;
-  if (B_k != msa::kBlockKeys) return fail(MSA_ERR_UNSUPPORTED, "paged decode uses pages of B_k = 128 tokens");
   if (!(scale > 0.f) || scale != scale) return fail(MSA_ERR_INVALID_ARG, "scale must be a positive number");
   if (!(k_scale > 0.f) || !(v_scale > 0.f) || k_scale != k_scale || v_scale != v_scale ||
       k_scale == __builtin_inff() || v_scale == __builtin_inff())
@@ -536,7 +535,7 @@ msa_status_t msa_decode_paged(const void* q, const void* q_idx, const void* k_pa
   hipError_t e = msa::launch_decode_paged(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(q_idx), static_cast<const uint8_t*>(k_pages),
       static_cast<const uint8_t*>(v_pages), k_scale, v_scale, static_cast<const uint16_t*>(k_idx_pages), block_table,
-      max_blocks, seqlens, batch, Bmax, H_q, H_kv, k, scale, block_idx, o, lse, static_cast<uint8_t*>(ws), L,
+      max_blocks, seqlens, batch, Bmax, B_k, H_q, H_kv, k, scale, block_idx, o, lse, static_cast<uint8_t*>(ws), L,
       static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_fail(e, "paged decode launch");
   return ok();

@@ -111,7 +111,7 @@ hipError_t launch_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_
 hipError_t launch_decode_paged(const uint16_t* q, const uint16_t* q_idx, const uint8_t* k_pages,
                                const uint8_t* v_pages, float k_scale, float v_scale, const uint16_t* kidx_pages,
                                const int32_t* block_table, int64_t max_blocks, const int64_t* seqlens, int batch,
-                               int64_t Bmax, int H_q, int H_kv, int kk, float scale, int32_t* block_idx, float* o,
-                               float* lse, uint8_t* ws, const DecodeWorkspace& L, hipStream_t stream);
+                               int64_t Bmax, int bk, int H_q, int H_kv, int kk, float scale, int32_t* block_idx,
+                               float* o, float* lse, uint8_t* ws, const DecodeWorkspace& L, hipStream_t stream);
 
 }  // namespace msa

@@ -28,8 +28,7 @@
  *     on the calling thread.
  *   - Blocks are numbered from 0: block b holds tokens [b*B_k, min((b+1)*B_k, N)).
  *     Head h belongs to group h / (H_q / H_kv) (adjacent heads share a KV head).
- *   - Supported shapes: d_h = 128, d_idx = 64, B_k = 64 or 128 (the paged decode:
- *     128), 1 <= k <= 32,
+ *   - Supported shapes: d_h = 128, d_idx = 64, B_k = 64 or 128, 1 <= k <= 32,
  *     H_q / H_kv a power of two <= 128 and ceil(N / B_k) <= 8192 (N <= 2^20 at
  *     B_k = 128, 2^19 at 64).
  *     Other shapes return MSA_ERR_UNSUPPORTED.  N = 0 (or batch = 0) is a valid

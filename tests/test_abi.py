@@ -232,7 +232,7 @@ def test_decode_paged_rejects_bad_arguments(lib):
         return raw.msa_decode_paged(f, f, f, f, ks, vs, f, bt, max_blocks, lens, batch, max_len, H_q, H_kv, 128, 64,
                                     B_k, k, 0.088, f, f, f, ws, ws_bytes, None)
 
-    assert call(B_k=64, max_blocks=16) == lib.MSA_ERR_UNSUPPORTED
+    assert call(B_k=32, max_blocks=32) == lib.MSA_ERR_UNSUPPORTED
 
     assert call(ks=0.0) == lib.MSA_ERR_INVALID_ARG
     assert call(vs=float("inf")) == lib.MSA_ERR_INVALID_ARG

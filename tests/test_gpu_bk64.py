@@ -148,3 +148,25 @@ def test_backward_bk64(msa, N, H_q, H_kv, k):
     ref = oracle.sparse_attn_bwd(inp.q, inp.k, inp.v, dO, bi, BK)
     check_grads(grads, ref, f"B_k=64 N={N} H_q={H_q} H_kv={H_kv} k={k}")
     check_grads(g2, ref, f"B_k=64 min workspace N={N}")
+
+
+@pytest.mark.parametrize("case", range(3))
+def test_decode_paged_bk64(msa, case):
+    """Paged FP8 decode over 64-token pages (one page per block, in random order): a
+    128-key scoring tile spans two pages."""
+    lengths, H_q, H_kv, k = [([1, 64, 65, 129, 1000, 5000], 16, 2, 4), ([4096, 3000, 256, 640], 64, 8, 32),
+                             ([777, 130, 191], 8, 8, 16)][case]
+    cfg = synth.DecodeConfig("t", batch=len(lengths), H_q=H_q, H_kv=H_kv, k=k, len_lo_blocks=1, len_hi_blocks=1,
+                             B_k=BK, seed=2100 + case)
+    p = synth.make_decode_paged(cfg, "structured" if case == 1 else "literal", device=DEV, lengths=lengths)
+    bi, o, lse = msa.msa_decode_paged(p.q, p.q_idx, p.k_pages, p.v_pages, p.k_scale, p.v_scale, p.kidx_pages,
+                                      p.block_table, p.seqlens, max(lengths), k, B_k=BK)
+    torch.cuda.synchronize()
+    bi_ref, o_ref, lse_ref, M = oracle.decode_paged(p.q, p.q_idx, p.k_pages, p.v_pages, p.k_scale, p.v_scale,
+                                                    p.kidx_pages, p.block_table, p.seqlens, k, BK, want_scores=True)
+    bi_gpu = bi.cpu().numpy()
+    tie = check_block_idx(bi_gpu, M, np.array(lengths) - 1, k, BK)
+    if tie.any():
+        _, o_ref, lse_ref = oracle.decode_paged(p.q, p.q_idx, p.k_pages, p.v_pages, p.k_scale, p.v_scale,
+                                                p.kidx_pages, p.block_table, p.seqlens, k, BK, block_idx=bi_gpu)
+    check_attn(o.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, f"paged B_k=64 case {case}")
