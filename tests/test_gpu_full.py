@@ -1,5 +1,6 @@
 """GPU parity at the full workload sizes (32K, 128K and 1M prefill, 128K with B_k = 64,
-a packed batch of 128K tokens; 64-sequence decode),
+a packed batch of 128K tokens; 64-sequence decode, contiguous and paged FP8; the KL
+pass and the backward at 128K),
 in the launch configuration the benchmark times, on sampled rows the oracle computes
 one by one.  The sample holds rows with fewer than k causal blocks, uniform rows, the
 last rows of the sequence and rows right after needle blocks."""
@@ -129,3 +130,93 @@ def test_decode_64_sequences(msa, name, mode):
         o_ref, lse_ref = oracle.decode_attn(h(d.q), h(d.k_cache), h(d.v_cache), d.cu_seqlens, bi_g, cfg.B_k)
     stats = check_attn(o.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, f"{name} {mode}")
     print(f"[full] {name} {mode}: {int(tie.sum())} near-tie rows, {stats}", flush=True)
+
+
+def _prefill_128k(msa, mode="literal"):
+    cfg = synth.CONFIGS["c2"]
+    print(f"[full] c2 {mode}: generating inputs", flush=True)
+    inp = synth.make_prefill(cfg, mode, device=DEV)
+    bi = msa.msa_index_topk(inp.q_idx, inp.k_idx, cfg.k, B_k=cfg.B_k)
+    o, lse = msa.msa_sparse_attn_fwd(inp.q, inp.k, inp.v, bi, B_k=cfg.B_k)
+    return cfg, inp, bi, o, lse
+
+
+def test_sparse_kl_128k(msa):
+    """Eq. 9-10 at 128K with the default workspace, on sampled rows of the GPU's own
+    selection; the loss is the mean of the returned per-row KL over all rows."""
+    cfg, inp, bi, _, lse = _prefill_128k(msa)
+    kl, lse_idx, loss = msa.msa_sparse_kl_fwd(inp.q, inp.k, inp.q_idx, inp.k_idx, bi, lse, B_k=cfg.B_k)
+    torch.cuda.synchronize()
+    rows = sample_rows(cfg, inp.needles, 64, cfg.seed + 7)
+    ridx = torch.from_numpy(rows).to(DEV)
+    print(f"[full] c2 KL: oracle on {len(rows)} rows", flush=True)
+    kl_ref, li_ref = oracle.sparse_kl(inp.q.cpu(), inp.k.cpu(), inp.q_idx.cpu(), inp.k_idx.cpu(),
+                                      bi[ridx].cpu().numpy(), cfg.B_k, rows=rows)
+    kl_s, li_s = kl[ridx].cpu().double().numpy(), lse_idx[ridx].cpu().double().numpy()
+    assert np.all(np.isfinite(li_ref)) and np.all(np.isfinite(li_s))
+    err = np.abs(kl_s - kl_ref)
+    assert np.all(err <= 5e-4 + 2e-3 * np.abs(kl_ref)), err.max()
+    assert np.abs(li_s - li_ref).max() <= 1e-3
+    kl_all = kl.double()
+    assert bool(torch.isfinite(kl_all).all()) and float(kl_all.min()) >= -1e-4
+    assert abs(float(loss.item()) - float(kl_all.mean())) <= 1e-6 * max(1.0, abs(float(kl_all.mean())))
+    print(f"[full] c2 KL: max err {err.max():.2e}, loss {float(loss.item()):.6f}", flush=True)
+
+
+def test_backward_128k(msa):
+    """Gradients of Eq. 8 at 128K with the default workspace (query windows).
+    dQ of the first 1024 rows: those rows see only keys < 1024, so the oracle on that
+    prefix gives their exact gradient.  dK, dV over all tokens: for each KV head r,
+    sum_t dK[t, r] = 0 (every row of dS sums to 0) and sum_t dV[t, r] = the sum of dO
+    over the rows of r's heads (every row of P sums to 1).  The GPU rounds P and dS to
+    bf16 (relative 2^-9) before its matrix products; those errors change sign from
+    row to row, so each identity is asserted to 2^-9 of the sum of the magnitudes it
+    adds up."""
+    from tests.test_gpu_backward import check_grads
+    cfg, inp, bi, o, lse = _prefill_128k(msa)
+    g = torch.Generator(device=DEV).manual_seed(cfg.seed + 11)
+    dO = torch.randn(inp.q.shape, generator=g, device=DEV).to(torch.bfloat16)
+    dq, dk, dv = msa.msa_sparse_attn_bwd(inp.q, inp.k, inp.v, o, lse, dO, bi, B_k=cfg.B_k)
+    torch.cuda.synchronize()
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert bool(torch.isfinite(t).all()), name
+    P0 = 1024
+    print(f"[full] c2 backward: oracle on the first {P0} rows", flush=True)
+    ref = oracle.sparse_attn_bwd(inp.q[:P0].cpu(), inp.k[:P0].cpu(), inp.v[:P0].cpu(), dO[:P0].cpu(),
+                                 bi[:P0].cpu().numpy(), cfg.B_k)
+    check_grads((dq[:P0],), (ref[0],), "c2 backward dq, first rows")
+    G = cfg.H_q // cfg.H_kv
+    dk_sum, dk_mag = dk.double().sum(0), dk.double().abs().sum(0)
+    dv_sum = dv.double().sum(0)
+    do_sum = dO.double().view(cfg.N, cfg.H_kv, G, -1).sum((0, 2))
+    do_mag = dO.double().abs().view(cfg.N, cfg.H_kv, G, -1).sum((0, 2))
+    rk = float((dk_sum.abs() / dk_mag).max())
+    rv = float(((dv_sum - do_sum).abs() / do_mag).max())
+    print(f"[full] c2 backward: |sum dK| / sum |dK| <= {rk:.2e}, |sum dV - sum dO| / sum |dO| <= {rv:.2e}",
+          flush=True)
+    assert rk <= 2.0 ** -9 and rv <= 2.0 ** -9
+
+
+def test_decode_paged_64_sequences(msa):
+    """The paged FP8 decode at the benchmark's size (64 sequences of 128K tokens, pages
+    in random order), every sequence against the oracle on the same FP8 codes."""
+    cfg = synth.CONFIGS["c3_128k"]
+    print("[full] c3_128k paged: generating caches", flush=True)
+    p = synth.make_decode_paged(cfg, "literal", device=DEV)
+    bi, o, lse = msa.msa_decode_paged(p.q, p.q_idx, p.k_pages, p.v_pages, p.k_scale, p.v_scale, p.kidx_pages,
+                                      p.block_table, p.seqlens, max(p.lengths), cfg.k, B_k=cfg.B_k)
+    torch.cuda.synchronize()
+    print("[full] c3_128k paged: oracle on all sequences", flush=True)
+    h = lambda t: t.cpu()
+    bi_ref, o_ref, lse_ref, M = oracle.decode_paged(h(p.q), h(p.q_idx), h(p.k_pages), h(p.v_pages), p.k_scale,
+                                                    p.v_scale, h(p.kidx_pages), p.block_table, p.seqlens, cfg.k,
+                                                    cfg.B_k, want_scores=True)
+    bi_g = bi.cpu().numpy()
+    tie = check_block_idx(bi_g, M, np.array(p.lengths) - 1, cfg.k, cfg.B_k)
+    np.testing.assert_array_equal(bi_g[~tie], bi_ref[~tie])
+    if tie.any():
+        _, o_ref, lse_ref = oracle.decode_paged(h(p.q), h(p.q_idx), h(p.k_pages), h(p.v_pages), p.k_scale,
+                                                p.v_scale, h(p.kidx_pages), p.block_table, p.seqlens, cfg.k,
+                                                cfg.B_k, block_idx=bi_g)
+    stats = check_attn(o.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, "c3_128k paged")
+    print(f"[full] c3_128k paged: {int(tie.sum())} near-tie rows, {stats}", flush=True)
