@@ -215,8 +215,8 @@ __device__ __forceinline__ u32x4_t ld16(const uint16_t* p) {
 }
 
 // K block -> LDS: row rho (256 B = 16 chunks of 16 B) holds key swap23(rho), chunk c
-// at position c ^ (rho & 15).  kb points at (token b*128, group r); keys past
-// `nvalid` read as zero.
+// at position c ^ (rho & 15).  kb points at (the block's first token, group r); all
+// 128 rows past `nvalid` read as zero (a 64-key block fills half the tile).
 template <bool NT = false>
 __device__ __forceinline__ void stage_k(const uint16_t* __restrict__ kb, int row_stride, int nvalid, uint8_t* Ks,
                                         int tid) {
@@ -233,8 +233,8 @@ __device__ __forceinline__ void stage_k(const uint16_t* __restrict__ kb, int row
 }
 
 // V block -> LDS transposed: Vt[d] (256 B) holds keys in natural order, 8-key chunk
-// kc at position kc ^ (d & 15).  vb points at (token b*128, group r); keys past
-// `nvalid` read as zero.
+// kc at position kc ^ (d & 15).  vb points at (the block's first token, group r);
+// keys past `nvalid` read as zero.
 template <bool NT = false>
 __device__ __forceinline__ void stage_v(const uint16_t* __restrict__ vb, int row_stride, int nvalid, uint8_t* Vt,
                                         int tid) {
