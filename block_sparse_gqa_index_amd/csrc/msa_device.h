@@ -131,9 +131,12 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
 }
 
 // (value, block) packed so that a larger key means a better entry: value
-// descending, then block ascending; empty entries (block < 0) get key 0.
+// descending, then block ascending; empty entries (block < 0) get key 0.  -0.0 is
+// taken as +0.0 first, so the two zeros tie (lower block first) as they compare
+// equal in the float comparisons of TopList.
 __device__ __forceinline__ uint64_t rank_key(float v, int blk) {
-  const uint32_t u = __float_as_uint(v);
+  uint32_t u = __float_as_uint(v);
+  u = u == 0x80000000u ? 0u : u;
   const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   return blk < 0 ? 0ull : ((uint64_t)ord << 32) | (uint32_t)(0x7fffffff - blk);
 }

@@ -91,7 +91,7 @@ hipError_t launch_sparse_kl_window(const uint16_t* q, const uint16_t* k, const u
                                    hipStream_t stream);
 hipError_t launch_kl_loss(const float* kl, int64_t n, double* partial, float* loss, hipStream_t stream);
 
-// Backward of the Main Branch (single sequence, B_k = 128, G <= 32): D = <dO, o> per
+// Backward of the Main Branch (single sequence, B_k = 64 or 128, G <= 32): D = <dO, o> per
 // (query, head) and zeroed dk / dv, then per query window the KV-outer pass and the
 // reductions of its dQ rows and dK/dV blocks.
 hipError_t launch_bwd_prepare(const uint16_t* dO, const float* o, int64_t rows, float* D, float* dk, float* dv,
@@ -107,7 +107,7 @@ hipError_t launch_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_
                          const uint16_t* v_cache, const uint16_t* k_idx_cache, const int64_t* cu, int batch,
                          int64_t Bmax, int bk, int H_q, int H_kv, int kk, float scale, int32_t* block_idx, float* o,
                          float* lse, uint8_t* ws, const DecodeWorkspace& L, hipStream_t stream);
-// Paged caches: FP8 E4M3 K/V pages and bf16 index-key pages of kBlockKeys tokens.
+// Paged caches: FP8 E4M3 K/V pages and bf16 index-key pages of bk tokens (64 or 128).
 hipError_t launch_decode_paged(const uint16_t* q, const uint16_t* q_idx, const uint8_t* k_pages,
                                const uint8_t* v_pages, float k_scale, float v_scale, const uint16_t* kidx_pages,
                                const int32_t* block_table, int64_t max_blocks, const int64_t* seqlens, int batch,

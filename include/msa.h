@@ -189,9 +189,17 @@ msa_status_t msa_sparse_attn_fwd_varlen(const void* q, const void* k, const void
                                         size_t ws_bytes, void* hip_stream);
 
 /* ------------------------------------------------------------------ Decode
- * msa_decode — one new token per sequence against packed variable-length caches.
- * The new token's K/V and index key are already the last cache entry of its
- * sequence (position L_s - 1), so its local block is block (L_s - 1) / B_k.
+ * msa_decode — one new token per sequence against packed variable-length caches:
+ * the decoding step whose wall-clock speedup the paper review page reports (section
+ * 6, efficiency comparison, Figure 4; the reading notes page, result 3).  The
+ * arithmetic is that of a single query row of the two-branch structure (reading
+ * notes page, section 5.1: block scores, Top-k with the forced local block, then
+ * softmax attention over the chosen blocks; paper review page, section 3, Eq. 6-8),
+ * taken for the newest token only.  The new token's K/V and index key are already
+ * the last cache entry of its sequence (position L_s - 1), so its local block is
+ * block (L_s - 1) / B_k.  Every cached index key is scored once (an HBM-bound scan),
+ * the best k blocks of each (sequence, group) are chosen, and the attention over
+ * them is split across workgroups and merged by log-sum-exp.
  *   q            bf16 [batch, H_q, d_h];  q_idx  bf16 [batch, H_kv, d_idx]
  *   k_cache, v_cache bf16 [T, H_kv, d_h]; k_idx_cache bf16 [T, d_idx]
  *   cu_seqlens   int64 [batch + 1], device memory, cu[0] = 0, cu[s+1] - cu[s] = L_s
@@ -200,6 +208,10 @@ msa_status_t msa_sparse_attn_fwd_varlen(const void* q, const void* k, const void
  *   block_idx    int32 [batch, H_kv, k]  out (as for msa_index_topk)
  *   o            fp32 [batch, H_q, d_h]; lse fp32 [batch, H_q]  out
  */
+/* msa_decode_workspace — bytes of device workspace msa_decode needs for these shapes
+ * (block scores of every cached block of every (sequence, group), then the partial
+ * (m, l, o) of each split of the attention); it also sizes msa_decode_paged.  Returns
+ * 0 for an unsupported shape.  Host-only. */
 size_t msa_decode_workspace(int batch, int H_q, int H_kv, int d_h, int d_idx, int B_k, int k,
                             int64_t max_len);
 msa_status_t msa_decode(const void* q, const void* q_idx, const void* k_cache, const void* v_cache,

@@ -60,6 +60,45 @@ def check_block_idx(gpu_bi: np.ndarray, M: np.ndarray, rows, k: int, B_k: int):
     return tie
 
 
+def check_exact_twin_ties(gpu_bi: np.ndarray, M: np.ndarray, rows, k: int, B_k: int) -> int:
+    """Rows whose selection boundary is an exact tie between two blocks with equal
+    scores (duplicated index keys), with every other block clearly (> 1e-3 relative)
+    above or below the tied value: the only freedom left is which of the two tied
+    blocks takes the last slot, and the lower block index must win.  On such rows the
+    GPU set must equal the oracle's bit for bit.  Returns the number of rows checked.
+
+    The caller makes the tied blocks exact copies, so the GPU's fp32 scores of the
+    two are equal too (same bf16 products in the same order); it checks that on the
+    GPU's own block scores where an entry point exposes them."""
+    gpu_bi = np.asarray(gpu_bi)
+    n, H_kv, _ = gpu_bi.shape
+    rows = np.asarray(rows)
+    checked = 0
+    for a in range(n):
+        bl = int(rows[a]) // B_k
+        if bl + 1 <= k:
+            continue
+        for r in range(H_kv):
+            m = M[a, r, :bl]
+            order = np.lexsort((np.arange(bl), -m))
+            t, t2 = m[order[k - 2]], m[order[k - 1]]
+            if t != t2:
+                continue
+            tol = REL_GAP * max(abs(t), 1e-30)
+            above_ok = k < 3 or m[order[k - 3]] - t > tol
+            below_ok = bl <= k or t - m[order[k]] > tol
+            if not (above_ok and below_ok):
+                continue
+            expect = np.sort(np.append(order[:k - 1], bl))
+            assert order[k - 2] < order[k - 1]
+            g = gpu_bi[a, r]
+            assert g.tolist() == expect.tolist(), \
+                f"row {int(rows[a])} group {r}: exact tie between blocks {order[k - 2]} and {order[k - 1]} " \
+                f"must go to the lower one; gpu {g.tolist()}, oracle {expect.tolist()}"
+            checked += 1
+    return checked
+
+
 def check_attn(o, lse, o_ref, lse_ref, what: str = ""):
     o = np.asarray(o, dtype=np.float64)
     lse = np.asarray(lse, dtype=np.float64)

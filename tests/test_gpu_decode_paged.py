@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import synth
-from tests.parity import check_attn, check_block_idx
+from tests.parity import check_attn, check_block_idx, check_exact_twin_ties
 
 pytestmark = pytest.mark.gpu
 
@@ -71,3 +71,28 @@ def test_decode_paged_equals_contiguous_when_exact(msa):
     torch.cuda.synchronize()
     assert torch.equal(bi_p, bi_c)
     assert torch.equal(o_p, o_c) and torch.equal(l_p, l_c)
+
+
+@pytest.mark.parametrize("B_k", [128, 64])
+@pytest.mark.parametrize("k", [4, 16, 32])
+def test_decode_paged_exact_ties_go_to_lower_block(msa, k, B_k):
+    """Index-key pages duplicated pairwise (the page of odd block b holds the keys of
+    block b - 1): exact boundary ties must go to the lower block, bit-exactly."""
+    batch, H_q, H_kv = 48, 16, 8
+    cfg = synth.DecodeConfig("t", batch=batch, H_q=H_q, H_kv=H_kv, k=k, len_lo_blocks=24, len_hi_blocks=48,
+                             B_k=B_k, seed=960 + k + B_k)
+    p = synth.make_decode_paged(cfg, device=DEV)
+    table = p.block_table.cpu()
+    for s, L in enumerate(p.lengths):
+        for b in range(1, L // B_k, 2):
+            p.kidx_pages[int(table[s, b])] = p.kidx_pages[int(table[s, b - 1])]
+    bi, o, lse = msa.msa_decode_paged(p.q, p.q_idx, p.k_pages, p.v_pages, p.k_scale, p.v_scale, p.kidx_pages,
+                                      p.block_table, p.seqlens, max(p.lengths), k, B_k=B_k)
+    torch.cuda.synchronize()
+    _, _, _, M = oracle.decode_paged(p.q, p.q_idx, p.k_pages, p.v_pages, p.k_scale, p.v_scale, p.kidx_pages,
+                                     p.block_table, p.seqlens, k, B_k, want_scores=True)
+    pos = np.array(p.lengths) - 1
+    bi = bi.cpu().numpy()
+    check_block_idx(bi, M, pos, k, B_k)
+    n_tied = check_exact_twin_ties(bi, M, pos, k, B_k)
+    assert n_tied >= batch * H_kv // 4, f"only {n_tied} rows had an isolated exact tie"

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import synth
-from tests.parity import check_attn, check_block_idx
+from tests.parity import check_attn, check_block_idx, check_exact_twin_ties
 
 pytestmark = pytest.mark.gpu
 
@@ -86,20 +86,37 @@ def test_index_topk_matches_oracle(msa, N, H_kv, k, mode):
     _check_index(msa, inp, k)
 
 
-def test_index_topk_exact_ties_go_to_lower_block(msa):
-    """Duplicated index keys make exact ties; the lower block index must win."""
-    N, H_kv, k = 2048, 2, 4
-    inp = _inputs(N, H_kv, H_kv, k, seed=7)
-    kidx = inp.k_idx.clone()
-    for b in range(1, 16, 2):  # block b is an exact copy of block b-1
-        kidx[b * 128:(b + 1) * 128] = kidx[(b - 1) * 128:b * 128]
-    bi = msa.msa_index_topk(inp.q_idx, kidx, k)
+def _twin_blocks(k_idx, B_k, n_blocks):
+    """Make block b an exact copy of block b - 1 for every odd b < n_blocks (full blocks only)."""
+    k_idx = k_idx.clone()
+    for b in range(1, n_blocks, 2):
+        k_idx[b * B_k:(b + 1) * B_k] = k_idx[(b - 1) * B_k:b * B_k]
+    return k_idx
+
+
+@pytest.mark.parametrize("B_k", [128, 64])
+@pytest.mark.parametrize("N,H_kv,k", [(2048, 2, 4), (4096, 3, 8), (5000, 2, 16), (3000, 1, 2), (6000, 2, 32)])
+def test_index_topk_exact_ties_go_to_lower_block(msa, N, H_kv, k, B_k):
+    """Duplicated index-key blocks make exact ties in block score, so the k-th slot
+    falls between two equal blocks on most rows.  Where the tie is the only freedom
+    (every other block clearly above or below it), the fused kernel must pick the
+    lower block, bit-exactly as the oracle does; all other rows follow the usual rule."""
+    inp = _inputs(N, H_kv, H_kv, k, seed=7 + N + k + B_k)
+    nb = N // B_k
+    kidx = _twin_blocks(inp.k_idx, B_k, nb)
+    bi = msa.msa_index_topk(inp.q_idx, kidx, k, B_k=B_k)
+    Mg = msa.msa_index_block_scores(inp.q_idx, kidx, B_k=B_k)
     torch.cuda.synchronize()
-    M = oracle.block_scores(inp.q_idx, kidx, 128)
-    assert np.any(M[:, :, 0:16:2] == M[:, :, 1:16:2])  # ties exist
-    tie = check_block_idx(bi.cpu().numpy(), M, np.arange(N), k, 128)
-    exact = oracle.topk(M, k, 128)
-    np.testing.assert_array_equal(bi.cpu().numpy()[~tie], exact[~tie])
+    M = oracle.block_scores(inp.q_idx, kidx, B_k)
+    # The GPU's own fp32 scores of twin blocks are equal wherever both are fully visible.
+    Mg = Mg.cpu().numpy()
+    for b in range(1, nb, 2):
+        past = np.arange(N) >= (b + 1) * B_k
+        assert np.array_equal(Mg[past, :, b - 1], Mg[past, :, b]), f"GPU scores of twin blocks {b - 1}, {b} differ"
+    bi = bi.cpu().numpy()
+    check_block_idx(bi, M, np.arange(N), k, B_k)
+    n_tied = check_exact_twin_ties(bi, M, np.arange(N), k, B_k)
+    assert n_tied >= N * H_kv // 8, f"only {n_tied} rows had an isolated exact tie"
 
 
 ATTN_SHAPES = [  # N, H_q, H_kv, k
@@ -255,3 +272,36 @@ def test_decode_matches_oracle(msa, case, mode):
     if tie.any():  # attention compared on the GPU's own selection
         o_ref, lse_ref = oracle.decode_attn(d.q, d.k_cache, d.v_cache, d.cu_seqlens, bi_gpu, 128)
     check_attn(o.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, f"decode case {case}")
+
+
+def _twin_cache_blocks(k_idx_cache, lengths, B_k):
+    """In every sequence of a packed cache, make full block b an exact copy of block
+    b - 1 for odd b."""
+    out = k_idx_cache.clone()
+    t0 = 0
+    for L in lengths:
+        for b in range(1, L // B_k, 2):
+            out[t0 + b * B_k:t0 + (b + 1) * B_k] = out[t0 + (b - 1) * B_k:t0 + b * B_k]
+        t0 += L
+    return out
+
+
+@pytest.mark.parametrize("B_k", [128, 64])
+@pytest.mark.parametrize("k", [2, 4, 16, 32])
+def test_decode_exact_ties_go_to_lower_block(msa, k, B_k):
+    """Duplicated cached index-key blocks: the decode Top-k must give an exact boundary
+    tie to the lower block, bit-exactly as the oracle does."""
+    batch, H_q, H_kv = 48, 16, 8
+    cfg = synth.DecodeConfig("t", batch=batch, H_q=H_q, H_kv=H_kv, k=k, len_lo_blocks=24, len_hi_blocks=48,
+                             B_k=B_k, seed=560 + k + B_k)
+    d = synth.make_decode(cfg, device=DEV)
+    kidx = _twin_cache_blocks(d.k_idx_cache, d.lengths, B_k)
+    bi, o, lse = msa.msa_decode(d.q, d.q_idx, d.k_cache, d.v_cache, kidx, d.cu_seqlens, max(d.lengths), k,
+                                B_k=B_k)
+    torch.cuda.synchronize()
+    _, _, _, M = oracle.decode(d.q, d.q_idx, d.k_cache, d.v_cache, kidx, d.cu_seqlens, k, B_k, want_scores=True)
+    pos = np.array(d.lengths) - 1
+    bi = bi.cpu().numpy()
+    check_block_idx(bi, M, pos, k, B_k)
+    n_tied = check_exact_twin_ties(bi, M, pos, k, B_k)
+    assert n_tied >= batch * H_kv // 4, f"only {n_tied} rows had an isolated exact tie"

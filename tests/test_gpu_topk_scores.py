@@ -97,3 +97,16 @@ def test_rows_at_block_limit(msa):
     _check_rows(bi, M, _sample_rows(N, 100, 63), k, BK)
     del M
     torch.cuda.empty_cache()
+
+
+def test_signed_zeros_tie(msa):
+    """-0.0 and +0.0 compare equal, so a tie between them goes to the lower block like
+    any other tie (scores drawn from {-1, -0, +0, 1})."""
+    N, H_kv, k = 5000, 2, 8
+    B = (N + 127) // 128
+    g = torch.Generator().manual_seed(6400)
+    M = torch.tensor([-1.0, -0.0, 0.0, 1.0])[torch.randint(0, 4, (N, H_kv, B), generator=g)]
+    assert (torch.signbit(M) & (M == 0)).any() and (~torch.signbit(M) & (M == 0)).any()
+    bi = msa.msa_topk_from_scores(M.to(DEV), k)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bi.cpu().numpy(), oracle.topk(M.double().numpy(), k, 128))
