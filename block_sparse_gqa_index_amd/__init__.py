@@ -40,6 +40,8 @@ _SIGS = {
     "msa_decode_workspace": ([_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I64], _SZ),
     "msa_decode": ([_P, _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _F32, _P, _P, _P, _P,
                     _SZ, _P], _I32),
+    "msa_decode_noalloc": ([_P, _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _F32, _P, _P,
+                            _P, _P], _I32),
     "msa_index_block_scores": ([_P, _P, _I64, _I32, _I32, _I32, _P, _P], _I32),
     "msa_topk_from_scores": ([_P, _I64, _I32, _I64, _I32, _I32, _P, _P], _I32),
     "msa_set_profile_events": ([ctypes.POINTER(_P), _I32], _I32),
@@ -361,6 +363,38 @@ def msa_decode(q: torch.Tensor, q_idx: torch.Tensor, k_cache: torch.Tensor, v_ca
     _check(_lib.msa_decode(_ptr(q), _ptr(q_idx), _ptr(k_cache), _ptr(v_cache), _ptr(k_idx_cache), _ptr(cu_seqlens),
                            batch, max_len, H_q, H_kv, d_h, d_idx, B_k, k, float(scale), _ptr(block_idx), _ptr(o),
                            _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "msa_decode")
+    return block_idx, o, lse
+
+
+def msa_decode_noalloc(q: torch.Tensor, q_idx: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                       k_idx_cache: torch.Tensor, cu_seqlens: torch.Tensor, max_len: int, k: int, B_k: int = 128,
+                       scale: float | None = None, block_idx=None, o=None, lse=None, stream=None):
+    """msa_decode with the library's static scratch as its workspace (the C call
+    allocates nothing; pass block_idx, o and lse to allocate nothing here either)."""
+    batch, H_q, d_h = q.shape
+    H_kv, d_idx = q_idx.shape[1], q_idx.shape[2]
+    T = k_cache.shape[0]
+    _need(q, "q", torch.bfloat16, (batch, H_q, d_h))
+    _need(q_idx, "q_idx", torch.bfloat16, (batch, H_kv, d_idx))
+    _need(k_cache, "k_cache", torch.bfloat16, (T, H_kv, d_h))
+    _need(v_cache, "v_cache", torch.bfloat16, (T, H_kv, d_h))
+    _need(k_idx_cache, "k_idx_cache", torch.bfloat16, (T, d_idx))
+    _need(cu_seqlens, "cu_seqlens", torch.int64, (batch + 1,))
+    if scale is None:
+        scale = d_h ** -0.5
+    dev = q.device
+    if block_idx is None:
+        block_idx = torch.empty((batch, H_kv, k), dtype=torch.int32, device=dev)
+    if o is None:
+        o = torch.empty((batch, H_q, d_h), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((batch, H_q), dtype=torch.float32, device=dev)
+    _need(block_idx, "block_idx", torch.int32, (batch, H_kv, k))
+    _need(o, "o", torch.float32, (batch, H_q, d_h))
+    _need(lse, "lse", torch.float32, (batch, H_q))
+    _check(_lib.msa_decode_noalloc(_ptr(q), _ptr(q_idx), _ptr(k_cache), _ptr(v_cache), _ptr(k_idx_cache),
+                                   _ptr(cu_seqlens), batch, max_len, H_q, H_kv, d_h, d_idx, B_k, k, float(scale),
+                                   _ptr(block_idx), _ptr(o), _ptr(lse), _stream(stream)), "msa_decode_noalloc")
     return block_idx, o, lse
 
 

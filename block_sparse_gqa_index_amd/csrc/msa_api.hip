@@ -4,8 +4,16 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "msa.h"
 #include "msa_kernels.h"
+
+// Device memory of msa_decode_noalloc: one copy per GPU, created when the library's
+// code object is loaded on that GPU and held until the process ends.  In host code
+// `scratch` only names the symbol; its device address on the current GPU comes from
+// hipGetSymbolAddress (scratch_on_current_device below).
+static __device__ __align__(256) uint8_t scratch[MSA_DECODE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -48,6 +56,30 @@ msa_status_t check_common(int64_t N, int d, int expect_d, const char* dname, int
   if (k < 1 || k > 32) return fail(MSA_ERR_UNSUPPORTED, "k must be in [1, 32] (got %d)", k);
   if (N >= kMaxN) return fail(MSA_ERR_UNSUPPORTED, "N must be < 2^24 (got %lld)", (long long)N);
   if ((N + B_k - 1) / B_k > kMaxBlocks) return fail(MSA_ERR_UNSUPPORTED, "too many blocks");
+  return MSA_OK;
+}
+
+// Device address of `scratch` per device ordinal, looked up on the first
+// msa_decode_noalloc call made with that device current.
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_ptr[kMaxScratchDevices] = {};
+
+msa_status_t scratch_on_current_device(uint8_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MSA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(MSA_ERR_UNSUPPORTED, "device ordinal %d is above %d", dev, kMaxScratchDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MSA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = static_cast<uint8_t*>(p);
+  }
+  *out = g_scratch_ptr[dev];
   return MSA_OK;
 }
 
@@ -475,22 +507,18 @@ size_t msa_decode_workspace(int batch, int H_q, int H_kv, int d_h, int d_idx, in
   return msa::decode_workspace_layout(batch, H_q, H_kv, k, Bmax > 0 ? Bmax : 1).total;
 }
 
-msa_status_t msa_decode(const void* q, const void* q_idx, const void* k_cache, const void* v_cache,
-                        const void* k_idx_cache, const int64_t* cu_seqlens, int batch, int64_t max_len, int H_q,
-                        int H_kv, int d_h, int d_idx, int B_k, int k, float scale, int32_t* block_idx, float* o,
-                        float* lse, void* ws, size_t ws_bytes, void* hip_stream) {
-  msa_status_t st = check_decode_shape(batch, max_len, H_q, H_kv, d_h, d_idx, B_k, k);
-  if (st != MSA_OK) return st;
-  if (!(scale > 0.f) || scale != scale) return fail(MSA_ERR_INVALID_ARG, "scale must be a positive number");
-  if (batch == 0) return ok();
-  if (max_len == 0) return fail(MSA_ERR_INVALID_ARG, "max_len must be >= 1 when batch > 0");
+// msa_decode after its shape checks: pointers, workspace, launch.
+static msa_status_t decode_run(const void* q, const void* q_idx, const void* k_cache, const void* v_cache,
+                               const void* k_idx_cache, const int64_t* cu_seqlens, int batch, int64_t max_len,
+                               int H_q, int H_kv, int B_k, int k, float scale, int32_t* block_idx, float* o,
+                               float* lse, void* ws, size_t ws_bytes, void* hip_stream) {
   if (!q || !q_idx || !k_cache || !v_cache || !k_idx_cache || !cu_seqlens || !block_idx || !o || !lse)
     return fail(MSA_ERR_INVALID_ARG, "null pointer");
   if (!aligned(q, 16) || !aligned(q_idx, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
       !aligned(k_idx_cache, 16) || !aligned(cu_seqlens, 8) || !aligned(block_idx, 4) || !aligned(o, 16) ||
       !aligned(lse, 4))
     return fail(MSA_ERR_INVALID_ARG, "misaligned pointer");
-  const size_t need = msa_decode_workspace(batch, H_q, H_kv, d_h, d_idx, B_k, k, max_len);
+  const size_t need = msa_decode_workspace(batch, H_q, H_kv, msa::kHeadDim, msa::kIndexDim, B_k, k, max_len);
   if (!ws || ws_bytes < need)
     return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes is below the required %zu", ws ? ws_bytes : 0, need);
   if (!aligned(ws, 256)) return fail(MSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
@@ -502,6 +530,39 @@ msa_status_t msa_decode(const void* q, const void* q_idx, const void* k_cache, c
       H_q, H_kv, k, scale, block_idx, o, lse, static_cast<uint8_t*>(ws), L, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return ok();
+}
+
+msa_status_t msa_decode(const void* q, const void* q_idx, const void* k_cache, const void* v_cache,
+                        const void* k_idx_cache, const int64_t* cu_seqlens, int batch, int64_t max_len, int H_q,
+                        int H_kv, int d_h, int d_idx, int B_k, int k, float scale, int32_t* block_idx, float* o,
+                        float* lse, void* ws, size_t ws_bytes, void* hip_stream) {
+  msa_status_t st = check_decode_shape(batch, max_len, H_q, H_kv, d_h, d_idx, B_k, k);
+  if (st != MSA_OK) return st;
+  if (!(scale > 0.f) || scale != scale) return fail(MSA_ERR_INVALID_ARG, "scale must be a positive number");
+  if (batch == 0) return ok();
+  if (max_len == 0) return fail(MSA_ERR_INVALID_ARG, "max_len must be >= 1 when batch > 0");
+  return decode_run(q, q_idx, k_cache, v_cache, k_idx_cache, cu_seqlens, batch, max_len, H_q, H_kv, B_k, k, scale,
+                    block_idx, o, lse, ws, ws_bytes, hip_stream);
+}
+
+msa_status_t msa_decode_noalloc(const void* q, const void* q_idx, const void* k_cache, const void* v_cache,
+                                const void* k_idx_cache, const int64_t* cu_seqlens, int batch, int64_t max_len,
+                                int H_q, int H_kv, int d_h, int d_idx, int B_k, int k, float scale,
+                                int32_t* block_idx, float* o, float* lse, void* hip_stream) {
+  msa_status_t st = check_decode_shape(batch, max_len, H_q, H_kv, d_h, d_idx, B_k, k);
+  if (st != MSA_OK) return st;
+  if (!(scale > 0.f) || scale != scale) return fail(MSA_ERR_INVALID_ARG, "scale must be a positive number");
+  if (batch == 0) return ok();
+  if (max_len == 0) return fail(MSA_ERR_INVALID_ARG, "max_len must be >= 1 when batch > 0");
+  const size_t need = msa_decode_workspace(batch, H_q, H_kv, d_h, d_idx, B_k, k, max_len);
+  if (need > (size_t)MSA_DECODE_NOALLOC_SCRATCH_BYTES)
+    return fail(MSA_ERR_WORKSPACE,
+                "these shapes need %zu bytes of scratch, above the library's static %zu bytes; "
+                "call msa_decode with a workspace instead", need, (size_t)MSA_DECODE_NOALLOC_SCRATCH_BYTES);
+  uint8_t* ws = nullptr;
+  if ((st = scratch_on_current_device(&ws)) != MSA_OK) return st;
+  return decode_run(q, q_idx, k_cache, v_cache, k_idx_cache, cu_seqlens, batch, max_len, H_q, H_kv, B_k, k, scale,
+                    block_idx, o, lse, ws, (size_t)MSA_DECODE_NOALLOC_SCRATCH_BYTES, hip_stream);
 }
 
 msa_status_t msa_decode_paged(const void* q, const void* q_idx, const void* k_pages, const void* v_pages,

@@ -220,6 +220,30 @@ msa_status_t msa_decode(const void* q, const void* q_idx, const void* k_cache, c
                         float scale, int32_t* block_idx, float* o, float* lse, void* ws,
                         size_t ws_bytes, void* hip_stream);
 
+/* ------------------------------------------------------------------ Decode without allocation
+ * msa_decode_noalloc — msa_decode for callers that cannot allocate device memory or
+ * pass a workspace: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Arguments, outputs, results and errors are those of msa_decode
+ * (bit-identical outputs for the same inputs); the workspace is the library's own
+ * static device array of MSA_DECODE_NOALLOC_SCRATCH_BYTES (32 MiB), one per GPU,
+ * which each GPU the library runs on holds until the process ends.  The call makes
+ * no allocation of any kind.
+ *   Limit: msa_decode_workspace() of the same shapes must be at most
+ *   MSA_DECODE_NOALLOC_SCRATCH_BYTES (for example 64 sequences of up to 1M tokens with
+ *   H_q = 64, H_kv = 8, k = 16 need 20 MiB; at 128K tokens, 6 MiB); larger shapes
+ *   return MSA_ERR_WORKSPACE and launch nothing.
+ *   Every call on a GPU uses that GPU's one array: calls that overlap in time on one
+ *   GPU (different streams or host threads) race and give undefined results; calls
+ *   ordered on one stream are safe.  Nothing in the array needs clearing between
+ *   calls: each call writes every scratch value it reads.
+ */
+#define MSA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+msa_status_t msa_decode_noalloc(const void* q, const void* q_idx, const void* k_cache,
+                                const void* v_cache, const void* k_idx_cache,
+                                const int64_t* cu_seqlens, int batch, int64_t max_len, int H_q,
+                                int H_kv, int d_h, int d_idx, int B_k, int k, float scale,
+                                int32_t* block_idx, float* o, float* lse, void* hip_stream);
+
 /* ------------------------------------------------------------------ Paged FP8 decode
  * msa_decode_paged — msa_decode over a paged cache whose K/V are FP8 (the open
  * interface's paged FP8 decode path, reading notes, section 5.4).  Pages hold B_k

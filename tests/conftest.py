@@ -14,8 +14,14 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # Full-size workloads run last so that a failure there hides nothing else.
-    items.sort(key=lambda it: 1 if it.get_closest_marker("slow") else 0)
+    # Full-size workloads run late so that a failure there hides nothing else; the
+    # allocation-free entry point's file runs after everything.
+    def order(it):
+        if os.path.basename(str(it.fspath)).startswith("test_zz_"):
+            return 2
+        return 1 if it.get_closest_marker("slow") else 0
+
+    items.sort(key=order)
 
 
 def pytest_runtest_logstart(nodeid, location):

@@ -261,3 +261,15 @@ def test_backward_rejects_bad_arguments(lib):
     assert 0 < need < raw.msa_sparse_attn_bwd_workspace(4096, 8, 2, 128, 128, 8)
     assert call(ws_bytes=need - 1) == lib.MSA_ERR_WORKSPACE
     assert call(N=0) == lib.MSA_OK
+
+
+def test_noalloc_decode_rejects_shapes_beyond_its_static_scratch(lib):
+    raw = lib.raw()
+    f = 0x10000  # never dereferenced: the size check comes before any pointer or device use
+    # 512 sequences of 1M tokens need 128 MiB of block scores: above the 32 MiB scratch.
+    st = raw.msa_decode_noalloc(f, f, f, f, f, f, 512, 1 << 20, 64, 8, 128, 64, 128, 16, 0.088, f, f, f, None)
+    assert st == lib.MSA_ERR_WORKSPACE
+    assert "static" in raw.msa_last_error().decode()
+    assert raw.msa_decode_noalloc(f, f, f, f, f, f, 0, 0, 64, 8, 128, 64, 128, 16, 0.088, f, f, f, None) == lib.MSA_OK
+    assert raw.msa_decode_noalloc(f, f, f, f, f, f, 4, 4096, 64, 8, 64, 64, 128, 16, 0.088, f, f, f,
+                                  None) == lib.MSA_ERR_UNSUPPORTED  # d_h = 64
