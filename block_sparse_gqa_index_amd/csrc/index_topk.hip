@@ -55,12 +55,11 @@ __device__ __forceinline__ void idx_store_block(uint8_t* buf, int tid, const uin
 // The 4 x CT output tiles are software-pipelined over two accumulators: the four
 // MFMAs of tile j+1 are issued before tile j is max-reduced, so the VALU reduction
 // of one tile runs under the matrix work of the next.
-template <int CT>
-__device__ __forceinline__ void idx_tile_reduce(const f32x16_t& acc, int64_t qi, int64_t b, int kt, bool need_mask,
-                                                int h, float& bmax) {
-  if (need_mask) {
+template <bool MASK>
+__device__ __forceinline__ void idx_tile_reduce(const f32x16_t& acc, int qi, int64_t b, int kt, int h, float& bmax) {
+  if constexpr (MASK) {
     // key b*128 + kt*32 + 8*(v/4) + 4h + v%4 is visible iff its offset <= lim
-    int64_t lim64 = qi - (b * kBk + kt * 32 + 4 * h);
+    int64_t lim64 = (int64_t)qi - (b * kBk + kt * 32 + 4 * h);
     lim64 = lim64 < -1 ? -1 : (lim64 > 64 ? 64 : lim64);
     const int lim = (int)lim64;
 #pragma unroll
@@ -72,10 +71,12 @@ __device__ __forceinline__ void idx_tile_reduce(const f32x16_t& acc, int64_t qi,
 }
 
 // NS blocks per staged tile (1 for B_k = 128, 2 for B_k = 64): 32-key MFMA tile kt
-// belongs to block kt / (4 / NS) of the staged tile.
-template <int CT, int NS>
-__device__ __forceinline__ void idx_block_max(const uint8_t* buf, const uint4 (&qop)[CT][4], const int64_t (&qi)[CT],
-                                              int64_t b, bool need_mask, int h, int l32, float (&bmax)[CT][NS]) {
+// belongs to block kt / (4 / NS) of the staged tile.  MASK: some key of the tile
+// lies past some column's query (the causal mask is applied per key); decided once
+// per staged tile, so the unmasked sweep carries no per-tile branch.
+template <int CT, int NS, bool MASK>
+__device__ __forceinline__ void idx_block_max(const uint8_t* buf, const uint4 (&qop)[CT][4], const int (&qi)[CT],
+                                              int64_t b, int h, int l32, float (&bmax)[CT][NS]) {
   constexpr int kTiles = 4 * CT;
   constexpr int kPerBlock = 4 / NS;
 #pragma unroll
@@ -104,12 +105,12 @@ __device__ __forceinline__ void idx_block_max(const uint8_t* buf, const uint4 (&
     for (int ks = 0; ks < 4; ++ks) acc[j & 1] = mfma_32x32x16(as_bf16x8(a[ks]), as_bf16x8(qop[ct][ks]), acc[j & 1]);
     if (j > 0) {
       const int pj = j - 1, pkt = pj / CT, pct = pj % CT;
-      idx_tile_reduce<CT>(acc[pj & 1], qi[pct], b, pkt, need_mask, h, bmax[pct][pkt / kPerBlock]);
+      idx_tile_reduce<MASK>(acc[pj & 1], qi[pct], b, pkt, h, bmax[pct][pkt / kPerBlock]);
     }
   }
   {
     constexpr int pj = kTiles - 1, pkt = pj / CT, pct = pj % CT;
-    idx_tile_reduce<CT>(acc[pj & 1], qi[pct], b, pkt, need_mask, h, bmax[pct][pkt / kPerBlock]);
+    idx_tile_reduce<MASK>(acc[pj & 1], qi[pct], b, pkt, h, bmax[pct][pkt / kPerBlock]);
   }
   __builtin_amdgcn_s_setprio(0);
 #pragma unroll
@@ -119,14 +120,23 @@ __device__ __forceinline__ void idx_block_max(const uint8_t* buf, const uint4 (&
   }
 }
 
-// LIST: register list length (>= k-1); CT: 32-column tiles per wave.
+template <int CT, int NS>
+__device__ __forceinline__ void idx_block_max(const uint8_t* buf, const uint4 (&qop)[CT][4], const int (&qi)[CT],
+                                              int64_t b, bool need_mask, int h, int l32, float (&bmax)[CT][NS]) {
+  if (need_mask)
+    idx_block_max<CT, NS, true>(buf, qop, qi, b, h, l32, bmax);
+  else
+    idx_block_max<CT, NS, false>(buf, qop, qi, b, h, l32, bmax);
+}
+
+// LIST: register list length (>= k-1); CT: 32-column tiles per wave (even).
 // WRITE_M: emit block scores M[c][b] (scaled) instead of selecting.
 //
-// Selection: staged tiles are swept in pairs (b, b+1).  After the pair, both lane
-// halves hold every block maximum of their column; the lower half offers tile b's
-// blocks to its list and the upper half tile b+1's to its own, so one insertion
-// sequence serves two tiles.  The two lists (blocks of even / odd tiles) are
-// merged at the end.
+// Selection: staged tiles are swept in pairs (b, b+1).  After a pair both lane halves
+// hold every block maximum of all CT columns of the lane; the lower half keeps the
+// Top-k lists of the first CT/2 columns and offers them both tiles' blocks, the upper
+// half those of the other CT/2 columns, so each column has one list and needs no
+// merge at the end.
 // Sequences: with cu == nullptr the call is one sequence of N tokens; otherwise
 // cu[0..batch] (device) are the packed sequence offsets, grid.y is the sequence and
 // grid.x the column tile within it (tiles past the sequence's end exit).  Every
@@ -135,7 +145,8 @@ __device__ __forceinline__ void idx_block_max(const uint8_t* buf, const uint4 (&
 template <int LIST, int CT, bool WRITE_M, int BK>
 __global__ __launch_bounds__(kIdxThreads, kIdxBlocksPerCU) void index_topk_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx_all, int64_t N_all, int H_kv,
-    int k, int64_t B, int32_t* __restrict__ block_idx, float* __restrict__ M, const int64_t* __restrict__ cu) {
+    int k, int64_t B, int32_t* __restrict__ block_idx, float* __restrict__ M, const int64_t* __restrict__ cu,
+    uint32_t imask) {
   constexpr int NS = kBk / BK;  // blocks per staged 128-key tile
   constexpr int kColsPerWave = 32 * CT;
   constexpr int kCols = kIdxWaves * kColsPerWave;
@@ -160,23 +171,31 @@ __global__ __launch_bounds__(kIdxThreads, kIdxBlocksPerCU) void index_topk_kerne
   const int64_t i_min_wave = wave_c0 / H_kv;
   const int64_t gcol0 = j0 * H_kv;  // global column of the sequence's first column
 
-  int64_t col[CT], qi[CT];
+  static_assert(CT % 2 == 0, "the lane halves keep the lists of CT / 2 columns each");
+  constexpr int CH = CT / 2;
+  int qi[CT];  // query position of the lane's column in tile ct (-1 past the end)
   uint4 qop[CT][4];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
-    col[ct] = gcol0 + wave_c0 + ct * 32 + l32;
-    const bool ok = wave_c0 + ct * 32 + l32 < total;
-    qi[ct] = ok ? (wave_c0 + ct * 32 + l32) / H_kv : -1;
+    const int64_t c = wave_c0 + ct * 32 + l32;
+    const bool ok = c < total;
+    qi[ct] = ok ? (int)(c / H_kv) : -1;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      qop[ct][ks] = ok ? *reinterpret_cast<const uint4*>(q_idx + col[ct] * kDidx + ks * 16 + 8 * h)
+      qop[ct][ks] = ok ? *reinterpret_cast<const uint4*>(q_idx + (gcol0 + c) * kDidx + ks * 16 + 8 * h)
                        : make_uint4(0, 0, 0, 0);
   }
 
-  TopList<LIST> list[CT];
+  // This lane half's columns: tiles h * CH .. h * CH + CH - 1; their local blocks.
+  KeyList<LIST> list[CH];
+  int bloc[CH];
   if constexpr (!WRITE_M) {
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) list[ct].init();
+    for (int c = 0; c < CH; ++c) {
+      list[c].init();
+      const int q = h ? qi[CH + c] : qi[c];
+      bloc[c] = q >= 0 ? q / BK : -1;
+    }
   }
 
   uint4 pre[2][kIdxLoads];
@@ -204,18 +223,31 @@ __global__ __launch_bounds__(kIdxThreads, kIdxBlocksPerCU) void index_topk_kerne
         for (int u = 0; u < NS; ++u) m1[ct][u] = -__builtin_inff();
       }
     }
+    if constexpr (WRITE_M) {
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
+      for (int ct = 0; ct < CT; ++ct) {
 #pragma unroll
-      for (int u = 0; u < NS; ++u) {
-        // block (b + h) * NS + u: this lane half's tile
-        const int64_t blk = (b + h) * NS + u;
-        const float x = h ? m1[ct][u] : m0[ct][u];
-        if constexpr (WRITE_M) {
-          if (qi[ct] >= 0 && (h == 0 || two) && blk < B) M[col[ct] * B + blk] = x * 0.125f;  // 1/sqrt(64), exact
-        } else {
-          // Blocks before the local one compete; the local block is forced later.
-          if (blk < qi[ct] / BK) list[ct].offer(x, (int)blk);
+        for (int u = 0; u < NS; ++u) {
+          // block (b + h) * NS + u: this lane half's tile
+          const int64_t blk = (b + h) * NS + u;
+          const float x = h ? m1[ct][u] : m0[ct][u];
+          if (qi[ct] >= 0 && (h == 0 || two) && blk < B)
+            M[(gcol0 + wave_c0 + ct * 32 + l32) * B + blk] = x * 0.125f;  // 1/sqrt(64), exact
+        }
+      }
+    } else {
+      // Blocks before the local one compete (key 0 offers nothing); the local block
+      // is forced when the row is written.  A block past b_last has no visible key
+      // for any column, so its -inf maximum is never offered.
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+          const int blk0 = (int)b * NS + u, blk1 = (int)(b + 1) * NS + u;
+          const float x0 = h ? m0[CH + c][u] : m0[c][u];
+          const float x1 = h ? m1[CH + c][u] : m1[c][u];
+          list[c].offer(blk0 < bloc[c] ? block_key(x0, blk0, imask) : 0u);
+          list[c].offer(blk1 < bloc[c] ? block_key(x1, blk1, imask) : 0u);
         }
       }
     }
@@ -223,37 +255,21 @@ __global__ __launch_bounds__(kIdxThreads, kIdxBlocksPerCU) void index_topk_kerne
 
   if constexpr (!WRITE_M) {
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      // Merge the even-block list (lower half) with the odd-block list (upper half):
-      // own run descending, partner's run reversed, one bitonic merge.
-      uint64_t key[2 * (LIST + 1)];
-#pragma unroll
-      for (int j = 0; j < LIST; ++j) {
-        const uint64_t mine = rank_key(list[ct].v[j], list[ct].b[j]);
-        const float ov = __shfl_xor(list[ct].v[j], 32);
-        const int ob = __shfl_xor(list[ct].b[j], 32);
-        key[j] = mine;
-        key[2 * (LIST + 1) - 1 - j] = rank_key(ov, ob);
-      }
-      key[LIST] = 0ull;
-      key[LIST + 1] = 0ull;
-      bitonic_merge_desc<2 * (LIST + 1)>(key);
-      if (qi[ct] < 0) continue;
-      // Lanes l and l+32 now hold identical merged runs; each writes half of the row.
+    for (int c = 0; c < CH; ++c) {
+      if (bloc[c] < 0) continue;
       int cand[LIST + 1];
 #pragma unroll
       for (int j = 0; j < LIST; ++j) {
-        const int blk = rank_key_block(key[j]);
+        const int blk = block_key_block(list[c].k[j], imask);
         cand[j] = (j < k - 1 && blk >= 0) ? blk : 0x7fffffff;
       }
       cand[LIST] = 0x7fffffff;
       int32_t out[LIST + 1];
-      write_selection<LIST + 1>(cand, k, (int)(qi[ct] / BK), out);
-      int32_t* row = block_idx + col[ct] * k;
-      const int half = (k + 1) >> 1;
+      write_selection<LIST + 1>(cand, k, bloc[c], out);
+      int32_t* row = block_idx + (gcol0 + wave_c0 + (h * CH + c) * 32 + l32) * k;
 #pragma unroll
       for (int t = 0; t <= LIST; ++t) {
-        if (t < k && ((t < half) == (h == 0))) row[t] = out[t];
+        if (t < k) row[t] = out[t];
       }
     }
   }
@@ -411,26 +427,36 @@ __global__ void fill_f32_kernel(float* __restrict__ p, int64_t n, float val) {
 
 // cu == nullptr: one sequence of N tokens; otherwise `batch` packed sequences with
 // device offsets cu[0..batch] and N = the longest length (grid.x is sized by it).
+// Low bits of the selection key that number the blocks: enough for every block
+// index of a sequence of up to N tokens.
+static uint32_t block_key_mask(int64_t N, int bk) {
+  const int64_t nb = (N + bk - 1) / bk;
+  uint32_t m = 1;
+  while ((int64_t)m < nb - 1) m = m * 2 + 1;
+  return m;
+}
+
 template <int BK>
 static hipError_t launch_index_topk_bk(const uint16_t* q_idx, const uint16_t* k_idx, int64_t N, int H_kv, int k,
                                        int32_t* block_idx, const int64_t* cu, int batch, hipStream_t stream) {
   const int64_t total = N * H_kv;
+  const uint32_t imask = block_key_mask(N, BK);
   const unsigned gy = cu ? (unsigned)batch : 1u;
   if (k <= 8) {
-    constexpr int CT = 2;
+    constexpr int CT = 4;
     const int64_t grid = (total + kIdxWaves * 32 * CT - 1) / (kIdxWaves * 32 * CT);
     index_topk_kernel<7, CT, false, BK><<<dim3((unsigned)grid, gy), dim3(kIdxThreads), 0, stream>>>(
-        q_idx, k_idx, N, H_kv, k, 0, block_idx, nullptr, cu);
+        q_idx, k_idx, N, H_kv, k, 0, block_idx, nullptr, cu, imask);
   } else if (k <= 16) {
-    constexpr int CT = 2;
+    constexpr int CT = BK == 128 ? 4 : 2;  // at B_k = 64 four tiles would spill registers
     const int64_t grid = (total + kIdxWaves * 32 * CT - 1) / (kIdxWaves * 32 * CT);
     index_topk_kernel<15, CT, false, BK><<<dim3((unsigned)grid, gy), dim3(kIdxThreads), 0, stream>>>(
-        q_idx, k_idx, N, H_kv, k, 0, block_idx, nullptr, cu);
+        q_idx, k_idx, N, H_kv, k, 0, block_idx, nullptr, cu, imask);
   } else {
-    constexpr int CT = 1;
+    constexpr int CT = 2;
     const int64_t grid = (total + kIdxWaves * 32 * CT - 1) / (kIdxWaves * 32 * CT);
     index_topk_kernel<31, CT, false, BK><<<dim3((unsigned)grid, gy), dim3(kIdxThreads), 0, stream>>>(
-        q_idx, k_idx, N, H_kv, k, 0, block_idx, nullptr, cu);
+        q_idx, k_idx, N, H_kv, k, 0, block_idx, nullptr, cu, imask);
   }
   return hipGetLastError();
 }
@@ -453,10 +479,10 @@ hipError_t launch_index_block_scores(const uint16_t* q_idx, const uint16_t* k_id
   const int64_t grid = (total + kIdxWaves * 32 * CT - 1) / (kIdxWaves * 32 * CT);
   if (bk == 64)
     index_topk_kernel<1, CT, true, 64><<<dim3((unsigned)grid), dim3(kIdxThreads), 0, stream>>>(
-        q_idx, k_idx, N, H_kv, 1, B, nullptr, M, nullptr);
+        q_idx, k_idx, N, H_kv, 1, B, nullptr, M, nullptr, 0u);
   else
     index_topk_kernel<1, CT, true, 128><<<dim3((unsigned)grid), dim3(kIdxThreads), 0, stream>>>(
-        q_idx, k_idx, N, H_kv, 1, B, nullptr, M, nullptr);
+        q_idx, k_idx, N, H_kv, 1, B, nullptr, M, nullptr, 0u);
   return hipGetLastError();
 }
 

@@ -107,6 +107,50 @@ struct TopList {
   }
 };
 
+// 32-bit selection key of a finite block score: the score's order-preserving
+// unsigned image with its low bits (imask = 2^ib - 1, ib bits to number the blocks)
+// replaced by imask - block.  A larger key is a better block: a higher score first,
+// and among scores whose images agree above the low ib bits, the lower block.  The
+// rounding keeps 23 - ib mantissa bits (relative resolution 2^-(23-ib)); -0.0 is
+// taken as +0.0.  Key 0 is below every real key and means "no block".
+__device__ __forceinline__ uint32_t block_key(float v, int blk, uint32_t imask) {
+  uint32_t u = __float_as_uint(v);
+  u = u == 0x80000000u ? 0u : u;
+  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (ord & ~imask) | (imask - (uint32_t)blk);
+}
+
+__device__ __forceinline__ int block_key_block(uint32_t key, uint32_t imask) {
+  return key == 0u ? -1 : (int)(imask - (key & imask));
+}
+
+__device__ __forceinline__ uint32_t med3_u32(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t r;
+  asm("v_med3_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// Top-L list of distinct 32-bit keys kept in registers by one lane, descending.
+// Inserting x: position j takes the median of (old k[j-1], x, old k[j]), which is
+// k[j-1] when x lies above it, x when x falls between, k[j] otherwise; so one
+// branchless instruction per position, and offering 0 (or anything below k[L-1])
+// changes nothing.
+template <int L>
+struct KeyList {
+  uint32_t k[L];
+
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int j = 0; j < L; ++j) k[j] = 0u;
+  }
+
+  __device__ __forceinline__ void offer(uint32_t x) {
+#pragma unroll
+    for (int j = L - 1; j >= 1; --j) k[j] = med3_u32(k[j - 1], x, k[j]);
+    k[0] = k[0] > x ? k[0] : x;
+  }
+};
+
 // Wave-wide maximum of a 64-bit key, returned to every lane, with DPP lane moves
 // (register-speed) instead of LDS shuffles: quad xor 1 and xor 2, half-row and row
 // mirrors, then the row broadcasts 15 and 31 leave the maximum in lane 63.
@@ -159,6 +203,22 @@ __device__ __forceinline__ void bitonic_merge_desc(uint64_t (&a)[N]) {
         const bool sw = y > x;
         a[i] = sw ? y : x;
         a[j] = sw ? x : y;
+      }
+    }
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void bitonic_merge_desc(uint32_t (&a)[N]) {
+#pragma unroll
+  for (int stride = N >> 1; stride > 0; stride >>= 1) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int j = i ^ stride;
+      if (j > i) {
+        const uint32_t x = a[i], y = a[j];
+        a[i] = x > y ? x : y;
+        a[j] = x > y ? y : x;
       }
     }
   }
