@@ -57,6 +57,28 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
+def kernel_rooflines(pre, peaks):
+    """Roofline of each timed kernel of the prefill step against the vendor peak and,
+    when measured, against this GPU's own ceiling: the index kernel on MFMA (its exact
+    FLOP count), KV-outer phase 1 and the combine on HBM (their algorithmic bytes)."""
+    out = {}
+    ms_idx = pre["ms_index_topk"]
+    tf = pre["flop_index"] / (ms_idx / 1e3) / 1e12
+    out["index_topk_kernel"] = {"bound": "mfma", "achieved": round(tf, 1), "unit": "TFLOP/s",
+                                "peak": PEAK_BF16_TFLOPS, "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+    gb1 = pre["phase1_algorithmic_bytes"] / (pre["ms_kvouter_phase1"] / 1e3) / 1e9
+    out["attn_kvouter_kernel"] = {"bound": "hbm", "achieved": round(gb1, 1), "unit": "GB/s", "peak": PEAK_HBM_GBS,
+                                  "frac": round(gb1 / PEAK_HBM_GBS, 4)}
+    gbc = pre["combine_GB_s"]
+    out["combine_kernel"] = {"bound": "hbm", "achieved": gbc, "unit": "GB/s", "peak": PEAK_HBM_GBS,
+                             "frac": round(gbc / PEAK_HBM_GBS, 4)}
+    if peaks:
+        out["index_topk_kernel"]["frac_of_measured"] = round(tf / peaks["mfma_bf16_tflops"], 4)
+        out["attn_kvouter_kernel"]["frac_of_measured_copy"] = round(gb1 / peaks["hbm_copy_GB_s"], 4)
+        out["combine_kernel"]["frac_of_measured_read"] = round(gbc / peaks["hbm_read_GB_s"], 4)
+    return out
 # Sources the KV-outer kernel is compiled from: a recorded traffic figure holds only
 # while their hash is unchanged.
 # What decides the KV-outer kernel's memory traffic: its own code (the phase-1 part
@@ -546,24 +568,106 @@ def run_table1(msa, steps=5):
     return out
 
 
+def measured_peaks():
+    """Measured ceilings of this GPU, beside the vendor figures: a register-only bf16
+    MFMA loop (32x32x16, four independent chains per wave, two waves per SIMD), a
+    streaming read of 4 GiB and a 2 GiB device copy, each timed with HIP events."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "block_sparse_gqa_index_amd", "libmsa_peaks.so"))
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    lib.msa_peak_mfma.argtypes = [I32, I32, I32, P, P]
+    lib.msa_peak_read.argtypes = [P, I64, I32, P, P]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps / 1e3
+
+    waves, iters = 8, 20000
+    sink = torch.empty(cus * waves * 64, dtype=torch.float32, device="cuda")
+    t = timed(lambda: lib.msa_peak_mfma(cus, waves, iters, sink.data_ptr(), stream.cuda_stream), 3)
+    mfma = cus * waves * iters * 4 * 32768 / t / 1e12
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    out = torch.empty(1, dtype=torch.int32, device="cuda")
+    t = timed(lambda: lib.msa_peak_read(buf.data_ptr(), buf.numel(), cus, out.data_ptr(), stream.cuda_stream), 5)
+    read = buf.numel() / t / 1e9
+    src, dst = buf[: 2 << 30], buf[2 << 30:]
+    t = timed(lambda: dst.copy_(src), 5)
+    copy = 2 * src.numel() / t / 1e9
+    del buf, sink
+    torch.cuda.empty_cache()
+    return {"mfma_bf16_tflops": round(mfma, 1), "hbm_read_GB_s": round(read, 1), "hbm_copy_GB_s": round(copy, 1),
+            "vendor_mfma_bf16_tflops": PEAK_BF16_TFLOPS, "vendor_hbm_GB_s": PEAK_HBM_GBS}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inp, cfg, n_rows):
-    """The oracle on a uniform sample of query rows of the same prefill (all groups and heads)."""
+    """The oracle on a uniform sample of query rows of the same prefill (all groups and
+    heads), timed in two halves by query position, which fit a per-row cost
+    t(i) = a + b i (index scoring grows with i; the attention budget is fixed): the
+    full 128K and 1M runs are extrapolated from it, and the 4K workload is run whole."""
     import numpy as np
     import oracle
+    import synth
     N, k, B_k = cfg.N, cfg.k, cfg.B_k
     log(f"cpu baseline: oracle on {n_rows} sampled query rows")
     g = np.random.default_rng(cfg.seed)
     rows = np.sort(g.choice(N, size=min(n_rows, N), replace=False))
     qi_h, ki_h = inp.q_idx.cpu(), inp.k_idx.cpu()
     q_h, k_h, v_h = inp.q.cpu(), inp.k.cpu(), inp.v.cpu()
+
+    def run(rs):
+        t0 = time.perf_counter()
+        M = oracle.block_scores(qi_h, ki_h, B_k, rows=rs)
+        bi = oracle.topk(M, k, B_k, rows=rs)
+        oracle.sparse_attn(q_h, k_h, v_h, bi, B_k, rows=rs)
+        return time.perf_counter() - t0
+
+    lo, hi = rows[: len(rows) // 2], rows[len(rows) // 2:]
+    t_lo, t_hi = run(lo), run(hi)
+    tc = t_lo + t_hi
+    # Mean row cost of each half is a + b * (its mean position).
+    c_lo, c_hi = t_lo / len(lo), t_hi / len(hi)
+    b = (c_hi - c_lo) / (hi.mean() - lo.mean())
+    a = c_lo - b * lo.mean()
+    full = lambda n: n * a + b * n * (n - 1) / 2
+    del qi_h, ki_h, q_h, k_h, v_h
+    # The 4K workload (H_q = 4, H_kv = 1, k = 8) whole.
+    c0 = synth.CONFIGS["c0"]
+    i0 = synth.make_prefill(c0, "literal", device="cpu")
     t0 = time.perf_counter()
-    M = oracle.block_scores(qi_h, ki_h, B_k, rows=rows)
-    bi = oracle.topk(M, k, B_k, rows=rows)
-    oracle.sparse_attn(q_h, k_h, v_h, bi, B_k, rows=rows)
-    tc = time.perf_counter() - t0
+    M0 = oracle.block_scores(i0.q_idx, i0.k_idx, c0.B_k)
+    oracle.sparse_attn(i0.q, i0.k, i0.v, oracle.topk(M0, c0.k, c0.B_k), c0.B_k)
+    t_c0 = time.perf_counter() - t0
     return {"value": round(len(rows) / tc, 3), "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(),
             "sample": f"{len(rows)} uniformly drawn query rows of the same {N}-token prefill (all groups and "
-                      f"heads; index scoring, Top-k and attention), {tc:.1f} s"}
+                      f"heads; index scoring, Top-k and attention), {tc:.1f} s",
+            "full_4k_prefill_s": round(t_c0, 2),
+            "extrapolated": {"model": "per-row cost t(i) = a + b i fitted on the two halves of the sample",
+                             "a_s": a, "b_s": b,
+                             "prefill_128k_s": round(full(N), 1),
+                             "prefill_1m_s": round(full(1 << 20), 1),
+                             "prefill_1m_tokens_per_s": round((1 << 20) / full(1 << 20), 3)}}
 
 
 def main(argv=None) -> int:
@@ -585,6 +689,9 @@ def main(argv=None) -> int:
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the 128K prefill with B_k = 64 and the packed variable-length batch")
     ap.add_argument("--single-mode", action="store_true", help="skip the second input mode")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured MFMA / HBM peak kernels")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the 32K and 1M prefill and the mixed-length decode lines")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="start with plain copies of known size (for counter runs)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -654,11 +761,22 @@ def main(argv=None) -> int:
         result["topk_table1"] = run_table1(msa)
     del inp
     torch.cuda.empty_cache()
+    peaks = None
+    if not args.no_peaks:
+        log("measured peaks: MFMA loop, streaming read, device copy")
+        peaks = measured_peaks()
+        result["measured_peaks"] = peaks
+    result["rooflines"] = kernel_rooflines(pre, peaks)
 
     if not args.no_decode:
         dcfg = synth.CONFIGS[args.decode_workload]
         result["decode"] = run_decode(msa, synth, dcfg, args.mode, max(args.steps, 50), args.warmup,
                                       paged=not args.no_paged)
+        if peaks:
+            dec = result["decode"]
+            dec["frac_of_measured_read"] = round(dec["GB_s"] / peaks["hbm_read_GB_s"], 4)
+            if "paged_fp8" in dec:
+                dec["paged_fp8"]["frac_of_measured_read"] = round(dec["paged_fp8"]["GB_s"] / peaks["hbm_read_GB_s"], 4)
         torch.cuda.empty_cache()
     if not args.no_extra:
         c64 = synth.CONFIGS["c2_bk64"]
@@ -670,6 +788,26 @@ def main(argv=None) -> int:
         result["prefill_bk64"] = pre64
         result["varlen"] = run_varlen(msa, synth, synth.VARLEN_CONFIGS["c2_varlen"], args.mode, args.steps,
                                       args.warmup)
+    if not args.no_configs:
+        # The pages' other contexts (32K and 1M prefill) and the decode batch with its
+        # specified mixed lengths, in the headline input mode.
+        other_cfgs = {}
+        pre1, inp1 = run_prefill(msa, synth, synth.CONFIGS["c1"], args.mode, args.steps, args.warmup)
+        del inp1
+        torch.cuda.empty_cache()
+        pre1["workload"] = "prefill N=32768 H_q=32 H_kv=4 d_h=128 d_idx=64 B_k=128 k=16"
+        other_cfgs["prefill_32k"] = pre1
+        if not args.no_decode:
+            other_cfgs["decode_mixed"] = run_decode(msa, synth, synth.CONFIGS["c3"], args.mode, max(args.steps, 50),
+                                                    args.warmup)
+            torch.cuda.empty_cache()
+        c4 = synth.CONFIGS["c4"]
+        pre4, inp4 = run_prefill(msa, synth, c4, args.mode, max(1, min(args.steps, 3)), 1)
+        del inp4
+        torch.cuda.empty_cache()
+        pre4["workload"] = "prefill N=1048576 H_q=64 H_kv=8 d_h=128 d_idx=64 B_k=128 k=16"
+        other_cfgs["prefill_1m"] = pre4
+        result["configs"] = other_cfgs
     if not args.single_mode:
         pre2, inp2 = run_prefill(msa, synth, cfg, other, args.steps, args.warmup)
         del inp2

@@ -16,22 +16,28 @@ LIB = os.path.join(PKG, "libmsa.so")
 SOURCES = ["msa_api.hip", "index_topk.hip", "sparse_attn.hip", "decode.hip", "backward.hip"]
 
 
-def hipcc_command(out: str = LIB, extra=()) -> list[str]:
+def hipcc_command(out: str = LIB, extra=(), sources=SOURCES) -> list[str]:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     return [hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-Wall", "-Wno-unused-result",
             "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-            *extra, "-o", out, *[os.path.join(CSRC, s) for s in SOURCES]]
+            *extra, "-o", out, *[os.path.join(CSRC, s) for s in sources]]
+
+
+# The benchmark's measured-peak kernels: a library of their own, not part of libmsa.
+PEAKS_LIB = os.path.join(PKG, "libmsa_peaks.so")
+PEAKS_SOURCES = ["peak_probe.hip"]
 
 
 def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = hipcc_command(tmp)
-    if verbose:
-        print(" ".join(cmd), file=sys.stderr)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    for out, srcs in ((LIB, SOURCES), (PEAKS_LIB, PEAKS_SOURCES)):
+        tmp = out + ".tmp"
+        cmd = hipcc_command(tmp, sources=srcs)
+        if verbose:
+            print(" ".join(cmd), file=sys.stderr)
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, out)
     return LIB
 
 
