@@ -208,6 +208,85 @@ def write_stats_summary(stats_csv: str, log_path: str, command: str) -> str:
     return STATS_FILE
 
 
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "kernel_counters_128k.txt")
+UTIL_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT",
+                 "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_BUSY_CU_CYCLES", "SQ_ACTIVE_INST_LDS", "GRBM_GUI_ACTIVE")
+
+
+def write_counter_summary(util_csv: str, fetch_csv: str, write_csv: str, command: str) -> str:
+    """Per-kernel counter summary of the library's kernels from three rocprofv3 --pmc
+    passes over the same short run (utilisation counters; FETCH_SIZE; WRITE_SIZE), each
+    value averaged over the kernel's dispatches.  Utilisation is per cycle of the
+    kernel: GRBM_GUI_ACTIVE is summed over the 8 XCDs, so a dispatch lasts GUI / 8
+    shader cycles; MFMA busy is per SIMD (1024 of them), VALU / LDS activity per CU
+    (256).  HBM bytes are scaled by what each counter reads for the 1 GiB calibration
+    copies at the start of the run (FETCH_SIZE and WRITE_SIZE are in KiB)."""
+    import csv
+    import re
+
+    def short(name):
+        name = name.replace("(anonymous namespace)::", "")
+        m = re.search(r"msa::([A-Za-z0-9_]+(?:<[^()]*?>)?)\(", name)
+        return m.group(1) if m else None
+
+    def load(path):
+        per = {}
+        for r in csv.DictReader(open(path)):
+            n = short(r["Kernel_Name"]) if "msa::" in r["Kernel_Name"] else (
+                "copy" if "copyBuffer" in r["Kernel_Name"] else None)
+            if n is None:
+                continue
+            d = per.setdefault(n, {}).setdefault(int(r["Dispatch_Id"]), {})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            d["_ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        return per
+
+    util, fetch, write = load(util_csv), load(fetch_csv), load(write_csv)
+
+    def avg(per, n, c):
+        v = [d[c] for d in per.get(n, {}).values() if c in d]
+        return sum(v) / len(v) if v else float("nan")
+
+    def copy_factor(per, c):
+        v = sorted(per.get("copy", {}).items())[:COPY_REPS]
+        kib = sum(d[c] for _, d in v) / max(1, len(v))
+        return COPY_BYTES / (kib * 1024.0)
+
+    ff, fw = copy_factor(fetch, "FETCH_SIZE"), copy_factor(write, "WRITE_SIZE")
+    lines = [
+        "# rocprofv3 counters of the library's kernels: 128K prefill (N=131072 H_q=64 H_kv=8 d_h=128",
+        "# B_k=128 k=16, literal inputs), the paged and packed 128K decode (64 sequences) and the",
+        "# split-form Top-k at the pages' table shapes; MI355X, one GPU.  Per kernel: dispatches,",
+        "# mean duration, shader clock (GUI cycles / duration), MFMA busy per SIMD, VALU busy,",
+        "# LDS-indexed activity and LDS bank-conflict cycles per CU (fractions of the kernel's",
+        "# cycles), and HBM bytes fetched / written per dispatch (calibrated by 1 GiB copies:",
+        f"# FETCH x {ff:.4f}, WRITE x {fw:.4f}).",
+        f"# command: {command}",
+        "",
+        f"{'kernel':<46} {'n':>3} {'ms':>8} {'MHz':>6} {'mfma':>6} {'valu':>6} {'lds':>6} {'ldsbc':>6} "
+        f"{'fetch_GB':>9} {'write_GB':>9} {'GB/s':>7}",
+    ]
+    names = sorted((n for n in util if n != "copy"), key=lambda n: -avg(util, n, "_ns"))
+    for n in names:
+        ns = avg(util, n, "_ns")
+        gui = avg(util, n, "GRBM_GUI_ACTIVE") / 8
+        if not (ns > 20000):  # below 20 us the counter windows are not meaningful
+            continue
+        mfma = avg(util, n, "SQ_VALU_MFMA_BUSY_CYCLES") / (gui * 1024)
+        valu = avg(util, n, "SQ_ACTIVE_INST_VALU") / (gui * 256)
+        lds = avg(util, n, "SQ_LDS_IDX_ACTIVE") / (gui * 256)
+        bc = avg(util, n, "SQ_LDS_BANK_CONFLICT") / (gui * 256)
+        fb = avg(fetch, n, "FETCH_SIZE") * 1024 * ff / 1e9
+        wb = avg(write, n, "WRITE_SIZE") * 1024 * fw / 1e9
+        fns = avg(fetch, n, "_ns")
+        lines.append(f"{n:<46} {len(util[n]):>3} {ns / 1e6:>8.3f} {gui / (ns / 1e3):>6.0f} {mfma:>6.3f} {valu:>6.3f} "
+                     f"{lds:>6.3f} {bc:>6.3f} {fb:>9.3f} {wb:>9.3f} {(fb + wb) / (fns / 1e9):>7.0f}")
+    os.makedirs(os.path.dirname(COUNTERS_FILE), exist_ok=True)
+    with open(COUNTERS_FILE, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return COUNTERS_FILE
+
+
 COPY_BYTES = 1 << 30
 COPY_REPS = 3
 
@@ -697,12 +776,17 @@ def main(argv=None) -> int:
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic summary from two rocprofv3 counter CSVs and exit")
     ap.add_argument("--traffic-command", default="", help="the command the counter CSVs came from")
+    ap.add_argument("--counters-from", nargs=3, metavar=("UTIL_CSV", "FETCH_CSV", "WRITE_CSV"),
+                    help="write the per-kernel counter summary from three rocprofv3 --pmc runs and exit")
     ap.add_argument("--stats-from", nargs=2, metavar=("STATS_CSV", "RUN_LOG"),
                     help="write the kernel statistics summary from a rocprofv3 --stats run and exit")
     args = ap.parse_args(argv)
 
     if args.stats_from:
         print(write_stats_summary(args.stats_from[0], args.stats_from[1], args.traffic_command))
+        return 0
+    if args.counters_from:
+        print(write_counter_summary(*args.counters_from, args.traffic_command))
         return 0
     if args.traffic_from:
         print(write_traffic_summary(args.traffic_from[0], args.traffic_from[1], args.mode, args.traffic_command))
