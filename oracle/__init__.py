@@ -63,6 +63,8 @@ def _load():
     lib.msa_oracle_decode_attn.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, dbl, P, P, P]
     lib.msa_oracle_sparse_kl.argtypes = [P, P, P, P, P, i64, i32, i32, i32, i32, i32, i32, dbl, P, i64, P, P]
     lib.msa_oracle_sparse_attn_bwd.argtypes = [P, P, P, P, P, i64, i32, i32, i32, i32, i32, dbl, P, P, P]
+    lib.msa_oracle_sparse_attn_bwd_part.argtypes = [P, P, P, P, P, i64, i32, i32, i32, i32, i32, dbl, P, i64, P,
+                                                    i64, i32, P, P]
     lib.msa_oracle_fp8_e4m3.argtypes = [ctypes.c_uint8]
     lib.msa_oracle_fp8_e4m3.restype = dbl
     lib.msa_oracle_decode_paged.argtypes = [P, P, P, P, dbl, dbl, P, P, i64, P, i32, i32, i32, i32, i32, i32, i32,
@@ -194,6 +196,30 @@ def sparse_attn_bwd(q, k, v, dO, block_idx, B_k: int, scale: float | None = None
     _load().msa_oracle_sparse_attn_bwd(_ptr(qq), _ptr(kk_), _ptr(vv), _ptr(gg), _ptr(bi), N, H_q, H_kv, d_h, B_k,
                                        bi.shape[2], float(scale), _ptr(dq), _ptr(dk), _ptr(dv))
     return dq, dk, dv
+
+
+def sparse_attn_bwd_part(q, k, v, dO, block_idx, B_k: int, rows=(), key_block: int = -1, group: int = 0,
+                         scale: float | None = None):
+    """The gradients of Eq. 8 restricted: dq [len(rows), H_q, d_h] of the listed query
+    rows, and dk, dv [B_k, d_h] of key block `key_block` of KV head `group` (None when
+    key_block < 0).  float64."""
+    qq, kk_, vv, gg = _u16(q), _u16(k), _u16(v), _u16(dO)
+    N, H_q, d_h = qq.shape
+    H_kv = kk_.shape[1]
+    assert gg.shape == qq.shape and vv.shape == kk_.shape
+    bi = np.ascontiguousarray(np.asarray(block_idx), dtype=np.int32)
+    assert bi.shape[:2] == (N, H_kv)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d_h)
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    assert r.size == 0 or (r.min() >= 0 and r.max() < N)
+    dq = np.empty((max(1, r.size), H_q, d_h), dtype=np.float64)
+    dk = np.empty((B_k, d_h), dtype=np.float64)
+    dv = np.empty((B_k, d_h), dtype=np.float64)
+    _load().msa_oracle_sparse_attn_bwd_part(_ptr(qq), _ptr(kk_), _ptr(vv), _ptr(gg), _ptr(bi), N, H_q, H_kv, d_h,
+                                            B_k, bi.shape[2], float(scale), _ptr(r), r.size, _ptr(dq),
+                                            int(key_block), int(group), _ptr(dk), _ptr(dv))
+    return dq[:r.size], (dk, dv) if key_block >= 0 else None
 
 
 def decode(q, q_idx, k_cache, v_cache, k_idx_cache, cu_seqlens, k: int, B_k: int,

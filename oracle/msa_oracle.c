@@ -9,7 +9,8 @@
  *   Eq. 9-10 KL alignment per row    -> kl_row()
  *   paged FP8 decode: OCP E4M3 codes -> msa_oracle_fp8_e4m3(), pages looked up
  *   per token
- *   gradients of Eq. 8 (backward)    -> msa_oracle_sparse_attn_bwd()
+ *   gradients of Eq. 8 (backward)    -> msa_oracle_sparse_attn_bwd(), and the
+ *   same gradients on given query rows / one key block -> msa_oracle_sparse_attn_bwd_part()
  * (page "MiniMax Sparse Attention (MSA)" paper review, section 3; page
  * "papers.chlience.com" reading notes, section 5.1 and 5.1.1.)
  * No blocking, fusion or reordering beyond the definitions; OpenMP only
@@ -511,4 +512,141 @@ void msa_oracle_sparse_attn_bwd(const uint16_t* q, const uint16_t* k, const uint
     free(P);
     free(inset);
   }
+}
+
+/*
+ * One (query i, head h of group r) row of the backward of Eq. 8: the softmax P over
+ * the row's token set T (tokens j <= i of the blocks marked in inset), o and
+ * D = <dO, o>, then dS_j = P_j (<dO, V_j> - D).  When dqr is given it receives
+ * scale * sum_j dS_j K_j; tokens j in [jlo, jhi) add scale * dS_j * q to dk and
+ * P_j * dO to dv (rows j - jlo).  P is scratch of at least i + 1 doubles.
+ * Returns 0 when T is empty (no gradient).
+ */
+static int bwd_row(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dO,
+                   const char* inset, int64_t i, int r, int h, int H_q, int H_kv, int d_h, int B_k,
+                   double scale, double* P, double* o, double* dqr, int64_t jlo, int64_t jhi,
+                   double* dk, double* dv) {
+  const uint16_t* qv = q + (i * H_q + h) * d_h;
+  const uint16_t* dov = dO + (i * H_q + h) * d_h;
+  double m = -INFINITY;
+  int64_t nt = 0;
+  for (int64_t j = 0; j <= i; ++j) {
+    if (!inset[block_of(j, B_k)]) continue;
+    const uint16_t* kr = k + (j * H_kv + r) * d_h;
+    double sv = 0.0;
+    for (int d = 0; d < d_h; ++d) sv += bf16(qv[d]) * bf16(kr[d]);
+    P[j] = sv * scale;
+    if (P[j] > m) m = P[j];
+    ++nt;
+  }
+  if (nt == 0) return 0;
+  double l = 0.0;
+  for (int64_t j = 0; j <= i; ++j)
+    if (inset[block_of(j, B_k)]) {
+      P[j] = exp(P[j] - m);
+      l += P[j];
+    }
+  for (int d = 0; d < d_h; ++d) o[d] = 0.0;
+  for (int64_t j = 0; j <= i; ++j) {
+    if (!inset[block_of(j, B_k)]) continue;
+    P[j] /= l;
+    const uint16_t* vr = v + (j * H_kv + r) * d_h;
+    for (int d = 0; d < d_h; ++d) o[d] += P[j] * bf16(vr[d]);
+  }
+  double D = 0.0;
+  for (int d = 0; d < d_h; ++d) D += bf16(dov[d]) * o[d];
+  for (int64_t j = 0; j <= i; ++j) {
+    if (!inset[block_of(j, B_k)]) continue;
+    const int in_blk = j >= jlo && j < jhi;
+    if (!dqr && !in_blk) continue;
+    const uint16_t* kr = k + (j * H_kv + r) * d_h;
+    const uint16_t* vr = v + (j * H_kv + r) * d_h;
+    double dp = 0.0;
+    for (int d = 0; d < d_h; ++d) dp += bf16(dov[d]) * bf16(vr[d]);
+    double ds = P[j] * (dp - D);
+    if (dqr)
+      for (int d = 0; d < d_h; ++d) dqr[d] += scale * ds * bf16(kr[d]);
+    if (in_blk) {
+      double* dkr = dk + (j - jlo) * d_h;
+      double* dvr = dv + (j - jlo) * d_h;
+      for (int d = 0; d < d_h; ++d) {
+        dkr[d] += scale * ds * bf16(qv[d]);
+        dvr[d] += P[j] * bf16(dov[d]);
+      }
+    }
+  }
+  return 1;
+}
+
+/* Marks the blocks of one (query, group) selection row in inset (B + 1 entries). */
+static void mark_row(const int32_t* sel, int kk, int64_t B, char* inset) {
+  memset(inset, 0, (size_t)B + 1);
+  for (int t = 0; t < kk; ++t)
+    if (sel[t] >= 0 && sel[t] < B) inset[sel[t]] = 1;
+}
+
+void msa_oracle_sparse_attn_bwd_part(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                     const uint16_t* dO, const int32_t* block_idx, int64_t N, int H_q,
+                                     int H_kv, int d_h, int B_k, int kk, double scale, const int64_t* rows,
+                                     int64_t nrows, double* dq_rows, int64_t kb, int kr, double* dk_blk,
+                                     double* dv_blk) {
+  int64_t B = msa_oracle_num_blocks(N, B_k);
+  int G = H_q / H_kv;
+  for (int64_t e = 0; e < nrows * H_q * d_h; ++e) dq_rows[e] = 0.0;
+  /* dq of the listed rows: each row's own softmax and its selected tokens. */
+#pragma omp parallel
+  {
+    char* inset = (char*)malloc((size_t)B + 1);
+    double* P = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+    double* o = (double*)malloc(sizeof(double) * (size_t)d_h);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t a = 0; a < nrows; ++a) {
+      int64_t i = rows[a];
+      for (int r = 0; r < H_kv; ++r) {
+        mark_row(block_idx + (i * H_kv + r) * kk, kk, B, inset);
+        for (int g = 0; g < G; ++g)
+          bwd_row(q, k, v, dO, inset, i, r, r * G + g, H_q, H_kv, d_h, B_k, scale, P, o,
+                  dq_rows + (a * H_q + r * G + g) * d_h, 0, 0, NULL, NULL);
+      }
+    }
+    free(o);
+    free(P);
+    free(inset);
+  }
+  if (kb < 0 || kb >= B || kr < 0 || kr >= H_kv) return;
+  /* dk, dv of key block kb of group kr: every query row whose selection holds kb. */
+  int64_t jlo = kb * B_k, jhi = (kb + 1) * B_k < N ? (kb + 1) * B_k : N;
+  int64_t nb = (int64_t)B_k * d_h;
+  for (int64_t e = 0; e < nb; ++e) dk_blk[e] = dv_blk[e] = 0.0;
+  int nth = msa_oracle_threads();
+  double* acc = (double*)calloc((size_t)nth * 2 * (size_t)nb, sizeof(double));
+#pragma omp parallel num_threads(nth)
+  {
+    int t = 0;
+#ifdef _OPENMP
+    t = omp_get_thread_num();
+#endif
+    double* dk_t = acc + (size_t)t * 2 * nb;
+    double* dv_t = dk_t + nb;
+    char* inset = (char*)malloc((size_t)B + 1);
+    double* P = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+    double* o = (double*)malloc(sizeof(double) * (size_t)d_h);
+#pragma omp for schedule(static)
+    for (int64_t i = jlo; i < N; ++i) {
+      mark_row(block_idx + (i * H_kv + kr) * kk, kk, B, inset);
+      if (!inset[kb]) continue;
+      for (int g = 0; g < G; ++g)
+        bwd_row(q, k, v, dO, inset, i, kr, kr * G + g, H_q, H_kv, d_h, B_k, scale, P, o, NULL, jlo, jhi,
+                dk_t, dv_t);
+    }
+    free(o);
+    free(P);
+    free(inset);
+  }
+  for (int t = 0; t < nth; ++t)
+    for (int64_t e = 0; e < nb; ++e) {
+      dk_blk[e] += acc[(size_t)t * 2 * nb + e];
+      dv_blk[e] += acc[(size_t)t * 2 * nb + nb + e];
+    }
+  free(acc);
 }

@@ -133,6 +133,19 @@ void msa_oracle_sparse_attn_bwd(const uint16_t* q, const uint16_t* k, const uint
                                 int H_kv, int d_h, int B_k, int kk, double scale, double* dq,
                                 double* dk, double* dv);
 
+/*
+ * The same gradients restricted, for checks at sizes where the full backward is too
+ * slow: dq_rows [nrows][H_q][d_h] for the listed query rows, and dk_blk, dv_blk
+ * [B_k][d_h] for the tokens of key block kb of group kr (every query row whose
+ * selection holds kb contributes; rows of the block past N stay 0).  kb < 0 skips
+ * the block part.
+ */
+void msa_oracle_sparse_attn_bwd_part(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                     const uint16_t* dO, const int32_t* block_idx, int64_t N, int H_q,
+                                     int H_kv, int d_h, int B_k, int kk, double scale, const int64_t* rows,
+                                     int64_t nrows, double* dq_rows, int64_t kb, int kr, double* dk_blk,
+                                     double* dv_blk);
+
 #ifdef __cplusplus
 }
 #endif

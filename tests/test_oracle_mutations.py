@@ -52,6 +52,10 @@ MUTANTS = [
     ("bwd_no_D", "double ds = P[j] * (dp - D);", "double ds = P[j] * dp;"),
     ("bwd_dv_from_ds", "dvr[d] += P[j] * bf16(dov[d]);", "dvr[d] += ds * bf16(dov[d]);"),
     ("bwd_dk_wrong_operand", "dkr[d] += scale * ds * bf16(qv[d]);", "dkr[d] += scale * ds * bf16(dov[d]);"),
+    ("bwdpart_diagonal_block", "for (int64_t i = jlo; i < N; ++i)", "for (int64_t i = jhi; i < N; ++i)"),
+    ("bwdpart_block_range", "const int in_blk = j >= jlo && j < jhi;", "const int in_blk = j > jlo && j < jhi;"),
+    ("bwdpart_dq_row_head", "dq_rows + (a * H_q + r * G + g) * d_h", "dq_rows + (a * H_q + g * H_kv + r) * d_h"),
+    ("bwdpart_dv_operand", "bf16(qv[d]);\n        dvr[d] += P[j] * bf16(dov[d]);", "bf16(qv[d]);\n        dvr[d] += P[j] * bf16(qv[d]);"),
     ("paged_index_page", "kidx_pages + ((int64_t)pages[j / B_k] * B_k + j % B_k) * d_idx",
      "kidx_pages + ((int64_t)(j / B_k) * B_k + j % B_k) * d_idx"),
 ]
@@ -80,6 +84,8 @@ def _all_pins():
     yield "kl_groups", pins.test_kl_is_nonnegative_and_groups_are_separate
     yield "bwd_autograd", lambda: pins.test_attention_backward_matches_autograd(300, 4, 2, 2, 64)
     yield "bwd_fd", pins.test_attention_backward_finite_differences
+    yield "bwd_part", lambda: pins.test_restricted_backward_matches_autograd(300, 4, 2, 2, 64)
+    yield "bwd_part_full", pins.test_restricted_backward_equals_full_oracle
     yield "fp8", pins.test_fp8_e4m3_decoding
     yield "paged", pins.test_paged_fp8_decode_equals_contiguous_decode
     yield "paged_scales", pins.test_paged_fp8_scales_multiply_keys_and_values

@@ -568,3 +568,41 @@ def test_attention_backward_finite_differences():
         fd = (loss(args_p["q"], args_p["k"], args_p["v"]) - loss(args_m["q"], args_m["k"], args_m["v"])) / 2
         lin = float((grad * step.numpy()).sum())
         assert abs(fd - lin) <= 2e-3 * max(1.0, abs(lin)), (name, fd, lin)
+
+
+@pytest.mark.parametrize("N,H_q,H_kv,k,B_k", [(300, 4, 2, 2, 64), (700, 8, 2, 3, 128)])
+def test_restricted_backward_matches_autograd(N, H_q, H_kv, k, B_k):
+    """dq on chosen rows and dk, dv of one key block (the checks used at full size)
+    against torch fp64 autograd of the dense masked attention, with arbitrary
+    selections (-1, repeats of nothing, future blocks) on some rows."""
+    inp = synth.small_prefill(N=N, H_q=H_q, H_kv=H_kv, k=k, seed=80 + N, B_k=B_k)
+    bi = oracle.topk(oracle.block_scores(inp.q_idx, inp.k_idx, B_k), k, B_k)
+    bi[5] = -1
+    bi[N - 3, 0, 0] = (N - 1) // B_k  # a block reaching past the row (causal: no tokens)
+    g = torch.Generator().manual_seed(N + 1)
+    dO = torch.randn(N, H_q, 128, generator=g).to(torch.bfloat16)
+    scale = 1.0 / math.sqrt(128)
+    ref_dq, ref_dk, ref_dv = _masked_attention_autograd(inp.q, inp.k, inp.v, dO, bi, B_k, scale)
+    rows = np.array([0, 5, 7, B_k - 1, B_k, N // 2, N - 3, N - 1])
+    nb = (N + B_k - 1) // B_k
+    for kb, r in ((0, 0), (nb // 2, H_kv - 1), (nb - 1, 0)):
+        dq, (dk, dv) = oracle.sparse_attn_bwd_part(inp.q, inp.k, inp.v, dO, bi, B_k, rows=rows, key_block=kb, group=r)
+        np.testing.assert_allclose(dq, ref_dq[rows], rtol=1e-9, atol=1e-11, err_msg="dq rows")
+        j0, j1 = kb * B_k, min(N, (kb + 1) * B_k)
+        np.testing.assert_allclose(dk[:j1 - j0], ref_dk[j0:j1, r], rtol=1e-9, atol=1e-11, err_msg=f"dk block {kb}")
+        np.testing.assert_allclose(dv[:j1 - j0], ref_dv[j0:j1, r], rtol=1e-9, atol=1e-11, err_msg=f"dv block {kb}")
+        assert np.all(dk[j1 - j0:] == 0) and np.all(dv[j1 - j0:] == 0)
+
+
+def test_restricted_backward_equals_full_oracle():
+    N, H_q, H_kv, k, B_k = 1000, 4, 2, 4, 128
+    inp = synth.small_prefill(N=N, H_q=H_q, H_kv=H_kv, k=k, seed=91, B_k=B_k, needles=1)
+    bi = oracle.topk(oracle.block_scores(inp.q_idx, inp.k_idx, B_k), k, B_k)
+    g = torch.Generator().manual_seed(92)
+    dO = torch.randn(N, H_q, 128, generator=g).to(torch.bfloat16)
+    dq_f, dk_f, dv_f = oracle.sparse_attn_bwd(inp.q, inp.k, inp.v, dO, bi, B_k)
+    rows = np.arange(0, N, 37)
+    dq, (dk, dv) = oracle.sparse_attn_bwd_part(inp.q, inp.k, inp.v, dO, bi, B_k, rows=rows, key_block=3, group=1)
+    np.testing.assert_allclose(dq, dq_f[rows], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(dk, dk_f[384:512, 1], rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(dv, dv_f[384:512, 1], rtol=1e-9, atol=1e-12)
