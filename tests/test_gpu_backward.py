@@ -28,11 +28,14 @@ def msa():
     return m
 
 
-def check_grads(got, ref, what):
+def check_grads(got, ref, what, floor=1.0):
+    """Max error <= 1e-2 and mean error <= 1e-3 of max(max |ref|, floor); None skips."""
     stats = {}
     for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+        if a is None:
+            continue
         a = a.cpu().double().numpy()
-        scale = max(np.abs(b).max(), 1.0)
+        scale = max(np.abs(b).max(), floor)
         err = np.abs(a - b)
         stats[name] = (float(err.max() / scale), float(err.mean() / scale))
         assert err.max() <= 1e-2 * scale, (what, name, stats[name])

@@ -195,6 +195,45 @@ def test_backward_128k(msa):
     print(f"[full] c2 backward: |sum dK| / sum |dK| <= {rk:.2e}, |sum dV - sum dO| / sum |dO| <= {rv:.2e}",
           flush=True)
     assert rk <= 2.0 ** -9 and rv <= 2.0 ** -9
+    # Element-wise at full size: dQ on sampled rows past the first window (rows right
+    # after needle blocks, uniform rows, the last rows), and dK, dV of whole key blocks
+    # of one KV head, each the sum over every row that selected the block: the last
+    # block, a block of median fan-in and a needle block (the sink block, selected by
+    # almost every row, costs the oracle too much and is left to the identities above).
+    rows = sample_rows(cfg, inp.needles, 24, cfg.seed + 13)
+    rows = rows[rows >= P0]
+    nb = (cfg.N + cfg.B_k - 1) // cfg.B_k
+    picks = []
+    for r in (0, cfg.H_kv - 1):
+        sel = bi[:, r, :]
+        fan = torch.bincount(sel[sel >= 0].long(), minlength=nb).cpu().numpy()
+        if r == 0:
+            picks.append((nb - 1, r, int(fan[nb - 1])))
+            nd = [b for b in (inp.needles[r] if inp.needles else []) if fan[b] <= 32768]
+            if nd:
+                b = max(nd, key=lambda b: fan[b])
+                picks.append((b, r, int(fan[b])))
+        else:
+            inner = np.arange(1, nb - 1)
+            b = int(inner[np.argsort(fan[inner], kind="stable")[len(inner) // 2]])
+            picks.append((b, r, int(fan[b])))
+    q_h, k_h, v_h, g_h, bi_h = inp.q.cpu(), inp.k.cpu(), inp.v.cpu(), dO.cpu(), bi.cpu().numpy()
+    ridx = torch.from_numpy(rows).to(DEV)
+    for n, (kb, r, f) in enumerate(picks):
+        print(f"[full] c2 backward: oracle on {len(rows) if n == 0 else 0} rows and key block {kb} of "
+              f"KV head {r} (fan-in {f} rows)", flush=True)
+        dq_ref, (dk_ref, dv_ref) = oracle.sparse_attn_bwd_part(q_h, k_h, v_h, g_h, bi_h, cfg.B_k,
+                                                               rows=rows if n == 0 else (), key_block=kb, group=r)
+        j0, j1 = kb * cfg.B_k, min(cfg.N, (kb + 1) * cfg.B_k)
+        got_kv = (dk[j0:j1, r], dv[j0:j1, r])
+        ref_kv = (dk_ref[:j1 - j0], dv_ref[:j1 - j0])
+        if n == 0:
+            st = check_grads((dq[ridx],) + got_kv, (dq_ref,) + ref_kv, f"c2 backward, block {kb}",
+                             floor=1e-6)
+        else:
+            st = check_grads((None,) + got_kv, (None,) + ref_kv, f"c2 backward, block {kb}",
+                             floor=1e-6)
+        print(f"[full] c2 backward: block {kb}: {st}", flush=True)
 
 
 def test_decode_paged_64_sequences(msa):
