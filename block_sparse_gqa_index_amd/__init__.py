@@ -38,9 +38,9 @@ _SIGS = {
     "msa_sparse_attn_fwd_windows": ([_I64, _I32, _I32, _I32, _I32, _I32, _SZ], _I64),
     "msa_sparse_attn_fwd": ([_P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _F32, _P, _P, _P, _SZ, _P], _I32),
     "msa_decode_workspace": ([_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I64], _SZ),
-    "msa_decode": ([_P, _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _F32, _P, _P, _P, _P,
+    "msa_decode": ([_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _F32, _P, _P, _P, _P,
                     _SZ, _P], _I32),
-    "msa_decode_noalloc": ([_P, _P, _P, _P, _P, _P, _I32, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _F32, _P, _P,
+    "msa_decode_noalloc": ([_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _F32, _P, _P,
                             _P, _P], _I32),
     "msa_index_block_scores": ([_P, _P, _I64, _I32, _I32, _I32, _P, _P], _I32),
     "msa_topk_from_scores": ([_P, _I64, _I32, _I64, _I32, _I32, _P, _P], _I32),
@@ -53,7 +53,7 @@ _SIGS = {
     "msa_sparse_attn_bwd_workspace_min": ([_I64, _I32, _I32, _I32, _I32, _I32], _SZ),
     "msa_sparse_attn_bwd": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _F32, _P, _P, _P, _P, _SZ,
                              _P], _I32),
-    "msa_decode_paged": ([_P, _P, _P, _P, _F32, _F32, _P, _P, _I64, _P, _I32, _I64, _I32, _I32, _I32, _I32, _I32, _I32,
+    "msa_decode_paged": ([_P, _P, _P, _P, _F32, _F32, _P, _P, _I64, _I64, _P, _I32, _I64, _I32, _I32, _I32, _I32, _I32, _I32,
                           _F32, _P, _P, _P, _P, _SZ, _P], _I32),
     "msa_index_topk_varlen": ([_P, _P, _P, _I32, _I64, _I64, _I32, _I32, _I32, _I32, _P, _P], _I32),
     "msa_sparse_attn_fwd_varlen_workspace": ([_I64, _I32, _I32, _I32, _I32, _I32, _I32], _SZ),
@@ -361,7 +361,7 @@ def msa_decode(q: torch.Tensor, q_idx: torch.Tensor, k_cache: torch.Tensor, v_ca
     _need(lse, "lse", torch.float32, (batch, H_q))
     ws = _ws(_lib.msa_decode_workspace(batch, H_q, H_kv, d_h, d_idx, B_k, k, max_len), dev, workspace)
     _check(_lib.msa_decode(_ptr(q), _ptr(q_idx), _ptr(k_cache), _ptr(v_cache), _ptr(k_idx_cache), _ptr(cu_seqlens),
-                           batch, max_len, H_q, H_kv, d_h, d_idx, B_k, k, float(scale), _ptr(block_idx), _ptr(o),
+                           batch, T, max_len, H_q, H_kv, d_h, d_idx, B_k, k, float(scale), _ptr(block_idx), _ptr(o),
                            _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "msa_decode")
     return block_idx, o, lse
 
@@ -393,7 +393,7 @@ def msa_decode_noalloc(q: torch.Tensor, q_idx: torch.Tensor, k_cache: torch.Tens
     _need(o, "o", torch.float32, (batch, H_q, d_h))
     _need(lse, "lse", torch.float32, (batch, H_q))
     _check(_lib.msa_decode_noalloc(_ptr(q), _ptr(q_idx), _ptr(k_cache), _ptr(v_cache), _ptr(k_idx_cache),
-                                   _ptr(cu_seqlens), batch, max_len, H_q, H_kv, d_h, d_idx, B_k, k, float(scale),
+                                   _ptr(cu_seqlens), batch, T, max_len, H_q, H_kv, d_h, d_idx, B_k, k, float(scale),
                                    _ptr(block_idx), _ptr(o), _ptr(lse), _stream(stream)), "msa_decode_noalloc")
     return block_idx, o, lse
 
@@ -428,7 +428,7 @@ def msa_decode_paged(q: torch.Tensor, q_idx: torch.Tensor, k_pages: torch.Tensor
     _need(lse, "lse", torch.float32, (batch, H_q))
     ws = _ws(_lib.msa_decode_workspace(batch, H_q, H_kv, d_h, d_idx, B_k, k, max_len), dev, workspace)
     _check(_lib.msa_decode_paged(_ptr(q), _ptr(q_idx), _ptr(k_pages), _ptr(v_pages), float(k_scale), float(v_scale),
-                                 _ptr(k_idx_pages), _ptr(block_table), block_table.shape[1], _ptr(seqlens), batch,
+                                 _ptr(k_idx_pages), _ptr(block_table), block_table.shape[1], P, _ptr(seqlens), batch,
                                  max_len, H_q, H_kv, d_h, d_idx, B_k, k, float(scale), _ptr(block_idx), _ptr(o),
                                  _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "msa_decode_paged")

@@ -138,7 +138,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
     const int64_t item = round * grid + (int64_t)xcd * per_xcd + slot_in_xcd;
     if (item >= n_items) break;
     const int4 it = items[item];
-    const int64_t b = it.x % B, r = (it.x / B) / nW;
+    const int64_t b = it.x, r = it.w;
     const int start = it.y, cnt = it.z;
     int ip[kBwdPairRegs];
 #pragma unroll

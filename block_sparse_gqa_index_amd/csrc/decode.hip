@@ -19,6 +19,7 @@
 
 #include "msa_device.h"
 #include "msa_kernels.h"
+#include "table_clamp.h"
 
 namespace msa {
 
@@ -26,7 +27,10 @@ namespace {
 
 constexpr int kScoreBlocksPerWG = 4;  // one block (128 keys) per wave
 
-// Where a sequence's cached tokens live.
+// Where a sequence's cached tokens live.  The caller's tables (offsets, lengths, page
+// numbers) are read through the clamps of table_clamp.h, so that a malformed table
+// cannot move an access outside the cache buffers; every kernel reads a sequence's
+// tokens 0 .. len(s) - 1 only.
 // Packed: sequences back to back (offsets cu), bf16 K/V rows [T][H_kv][d_h].
 // BK: keys per block (64 or 128), a compile-time constant so that the block
 // arithmetic stays shifts.
@@ -36,14 +40,18 @@ struct PackedCache {
   const uint16_t* v;
   const uint16_t* kidx;
   const int64_t* cu;
+  int64_t T;  // cached tokens (rows of k, v and kidx)
   static constexpr int bk = BK;
-  __device__ int64_t len(int s) const { return cu[s + 1] - cu[s]; }
+  __device__ int64_t start(int s) const { return clamp_i64(cu[s], 0, T); }
+  __device__ int64_t len(int s) const { return packed_span(cu[s], cu[s + 1], T).len; }
   // Index key 64h of 128-key tile t of sequence s (keys are consecutive rows).
   __device__ const uint16_t* kidx_half(int s, int64_t t, int h, int64_t) const {
-    return kidx + (cu[s] + t * kBk + 64 * h) * kDidx;
+    return kidx + (start(s) + t * kBk + 64 * h) * kDidx;
   }
   // Element offset of (block b, key 0, group r) in the K/V rows; rows are H_kv * d_h apart.
-  __device__ int64_t kv_block(int s, int64_t b, int r, int H_kv) const { return ((cu[s] + b * bk) * H_kv + r) * kDh; }
+  __device__ int64_t kv_block(int s, int64_t b, int r, int H_kv) const {
+    return ((start(s) + b * bk) * H_kv + r) * kDh;
+  }
 };
 
 // Paged: pages of BK tokens (one block), token j of sequence s in row j % BK of
@@ -57,9 +65,13 @@ struct PagedFp8Cache {
   const int32_t* table;
   int64_t max_blocks;
   const int64_t* lens;
+  int64_t num_pages;  // pages in k, v and kidx
   static constexpr int bk = BK;
-  __device__ int64_t len(int s) const { return lens[s]; }
-  __device__ int64_t page(int s, int64_t b) const { return table[(int64_t)s * max_blocks + b]; }
+  // At most max_blocks pages, so every table entry read is in its row.
+  __device__ int64_t len(int s) const { return paged_len(lens[s], max_blocks, BK); }
+  __device__ int64_t page(int s, int64_t b) const {
+    return page_number(table[(int64_t)s * max_blocks + b], num_pages);
+  }
   // Index key 64h of 128-key tile t.  With 64-token pages the half is a page of its
   // own; a half past the sequence end (L tokens) reads no table entry of it.
   __device__ const uint16_t* kidx_half(int s, int64_t t, int h, int64_t L) const {
@@ -597,29 +609,31 @@ static hipError_t launch_decode_impl(const uint16_t* q, const uint16_t* q_idx, c
 
 hipError_t launch_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_t* k_cache,
                          const uint16_t* v_cache, const uint16_t* k_idx_cache, const int64_t* cu, int batch,
-                         int64_t Bmax, int bk, int H_q, int H_kv, int kk, float scale, int32_t* block_idx, float* o,
+                         int64_t T, int64_t Bmax, int bk, int H_q, int H_kv, int kk, float scale, int32_t* block_idx, float* o,
                          float* lse, uint8_t* ws, const DecodeWorkspace& L, hipStream_t stream) {
   if (bk == 64) {
-    const PackedCache<64> cache{k_cache, v_cache, k_idx_cache, cu};
+    const PackedCache<64> cache{k_cache, v_cache, k_idx_cache, cu, T};
     return launch_decode_impl(q, q_idx, cache, batch, Bmax, H_q, H_kv, kk, scale * kLog2e, 1.f, block_idx, o, lse,
                               ws, L, stream);
   }
-  const PackedCache<128> cache{k_cache, v_cache, k_idx_cache, cu};
+  const PackedCache<128> cache{k_cache, v_cache, k_idx_cache, cu, T};
   return launch_decode_impl(q, q_idx, cache, batch, Bmax, H_q, H_kv, kk, scale * kLog2e, 1.f, block_idx, o, lse, ws,
                             L, stream);
 }
 
 hipError_t launch_decode_paged(const uint16_t* q, const uint16_t* q_idx, const uint8_t* k_pages,
                                const uint8_t* v_pages, float k_scale, float v_scale, const uint16_t* kidx_pages,
-                               const int32_t* block_table, int64_t max_blocks, const int64_t* seqlens, int batch,
-                               int64_t Bmax, int bk, int H_q, int H_kv, int kk, float scale, int32_t* block_idx,
+                               const int32_t* block_table, int64_t max_blocks, int64_t num_pages,
+                               const int64_t* seqlens, int batch, int64_t Bmax, int bk, int H_q, int H_kv, int kk, float scale, int32_t* block_idx,
                                float* o, float* lse, uint8_t* ws, const DecodeWorkspace& L, hipStream_t stream) {
   if (bk == 64) {
-    const PagedFp8Cache<64> cache{k_pages, v_pages, kidx_pages, block_table, max_blocks, seqlens};
+    const PagedFp8Cache<64> cache{k_pages, v_pages, kidx_pages, block_table, max_blocks, seqlens,
+                                          num_pages};
     return launch_decode_impl(q, q_idx, cache, batch, Bmax, H_q, H_kv, kk, scale * k_scale * kLog2e, v_scale,
                               block_idx, o, lse, ws, L, stream);
   }
-  const PagedFp8Cache<128> cache{k_pages, v_pages, kidx_pages, block_table, max_blocks, seqlens};
+  const PagedFp8Cache<128> cache{k_pages, v_pages, kidx_pages, block_table, max_blocks, seqlens,
+                                          num_pages};
   return launch_decode_impl(q, q_idx, cache, batch, Bmax, H_q, H_kv, kk, scale * k_scale * kLog2e, v_scale,
                             block_idx, o, lse, ws, L, stream);
 }

@@ -17,6 +17,7 @@
 // for the split entry point, to memory.  The token scores never leave registers.
 #include "msa_device.h"
 #include "msa_kernels.h"
+#include "table_clamp.h"
 
 namespace msa {
 
@@ -138,15 +139,17 @@ __device__ __forceinline__ void idx_block_max(const uint8_t* buf, const uint4 (&
 // half those of the other CT/2 columns, so each column has one list and needs no
 // merge at the end.
 // Sequences: with cu == nullptr the call is one sequence of N tokens; otherwise
-// cu[0..batch] (device) are the packed sequence offsets, grid.y is the sequence and
-// grid.x the column tile within it (tiles past the sequence's end exit).  Every
+// cu[0..batch] (device) are the packed sequence offsets of T tokens, grid.y is the
+// sequence and grid.x the column tile within it (tiles past the sequence's end exit).
+// The span read from cu is clamped into [0, T) and its length to N_all (the host's
+// bound on every length), so a malformed table stays inside the buffers.  Every
 // position below (queries, blocks, keys) is relative to the sequence start j0;
 // columns and output rows are global.
 template <int LIST, int CT, bool WRITE_M, int BK>
 __global__ __launch_bounds__(kIdxThreads, kIdxBlocksPerCU) void index_topk_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx_all, int64_t N_all, int H_kv,
     int k, int64_t B, int32_t* __restrict__ block_idx, float* __restrict__ M, const int64_t* __restrict__ cu,
-    uint32_t imask) {
+    int64_t T, uint32_t imask) {
   constexpr int NS = kBk / BK;  // blocks per staged 128-key tile
   constexpr int kColsPerWave = 32 * CT;
   constexpr int kCols = kIdxWaves * kColsPerWave;
@@ -154,10 +157,12 @@ __global__ __launch_bounds__(kIdxThreads, kIdxBlocksPerCU) void index_topk_kerne
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][2][kBlkBytes];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: kept in scalar registers
   const int h = lane >> 5, l32 = lane & 31;
-  const int64_t j0 = cu ? cu[blockIdx.y] : 0;
-  const int64_t N = cu ? cu[blockIdx.y + 1] - j0 : N_all;  // tokens of this sequence
+  const PackedSpan span = cu ? packed_span(cu[blockIdx.y], cu[blockIdx.y + 1], T) : PackedSpan{0, N_all};
+  const int64_t j0 = span.start;
+  const int64_t N = span.len < N_all ? span.len : N_all;  // tokens of this sequence
   const uint16_t* __restrict__ k_idx = k_idx_all + j0 * kDidx;
   const int64_t total = N * H_kv;                          // columns of this sequence
   const int64_t ntiles = (total + kCols - 1) / kCols;
@@ -193,8 +198,10 @@ __global__ __launch_bounds__(kIdxThreads, kIdxBlocksPerCU) void index_topk_kerne
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       list[c].init();
-      const int q = h ? qi[CH + c] : qi[c];
-      bloc[c] = q >= 0 ? q / BK : -1;
+      // The column's query, recomputed rather than taken from qi[] by the lane's half
+      // (an index the compiler would lower to a private-memory array).
+      const int64_t col = wave_c0 + (h * CH + c) * 32 + l32;
+      bloc[c] = col < total ? (int)(col / H_kv) / BK : -1;
     }
   }
 
@@ -254,6 +261,9 @@ __global__ __launch_bounds__(kIdxThreads, kIdxBlocksPerCU) void index_topk_kerne
   }
 
   if constexpr (!WRITE_M) {
+    // The lane's number, taken afresh (not kept live across the sweep, where every
+    // register is in use).
+    const int lid = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       if (bloc[c] < 0) continue;
@@ -266,7 +276,7 @@ __global__ __launch_bounds__(kIdxThreads, kIdxBlocksPerCU) void index_topk_kerne
       cand[LIST] = 0x7fffffff;
       int32_t out[LIST + 1];
       write_selection<LIST + 1>(cand, k, bloc[c], out);
-      int32_t* row = block_idx + (gcol0 + wave_c0 + (h * CH + c) * 32 + l32) * k;
+      int32_t* row = block_idx + (gcol0 + wave_c0 + ((lid >> 5) * CH + c) * 32 + (lid & 31)) * k;
 #pragma unroll
       for (int t = 0; t <= LIST; ++t) {
         if (t < k) row[t] = out[t];
@@ -425,8 +435,9 @@ __global__ void fill_f32_kernel(float* __restrict__ p, int64_t n, float val) {
 
 }  // namespace
 
-// cu == nullptr: one sequence of N tokens; otherwise `batch` packed sequences with
-// device offsets cu[0..batch] and N = the longest length (grid.x is sized by it).
+// cu == nullptr: one sequence of N tokens; otherwise `batch` packed sequences of T
+// tokens with device offsets cu[0..batch] and N = the longest length (grid.x is
+// sized by it).
 // Low bits of the selection key that number the blocks: enough for every block
 // index of a sequence of up to N tokens.
 static uint32_t block_key_mask(int64_t N, int bk) {
@@ -438,33 +449,35 @@ static uint32_t block_key_mask(int64_t N, int bk) {
 
 template <int BK>
 static hipError_t launch_index_topk_bk(const uint16_t* q_idx, const uint16_t* k_idx, int64_t N, int H_kv, int k,
-                                       int32_t* block_idx, const int64_t* cu, int batch, hipStream_t stream) {
+                                       int32_t* block_idx, const int64_t* cu, int batch, int64_t T,
+                                       hipStream_t stream) {
   const int64_t total = N * H_kv;
   const uint32_t imask = block_key_mask(N, BK);
   const unsigned gy = cu ? (unsigned)batch : 1u;
   if (k <= 8) {
-    constexpr int CT = 4;
+    constexpr int CT = BK == 128 ? 4 : 2;  // at B_k = 64 four tiles would spill registers
     const int64_t grid = (total + kIdxWaves * 32 * CT - 1) / (kIdxWaves * 32 * CT);
     index_topk_kernel<7, CT, false, BK><<<dim3((unsigned)grid, gy), dim3(kIdxThreads), 0, stream>>>(
-        q_idx, k_idx, N, H_kv, k, 0, block_idx, nullptr, cu, imask);
+        q_idx, k_idx, N, H_kv, k, 0, block_idx, nullptr, cu, T, imask);
   } else if (k <= 16) {
     constexpr int CT = BK == 128 ? 4 : 2;  // at B_k = 64 four tiles would spill registers
     const int64_t grid = (total + kIdxWaves * 32 * CT - 1) / (kIdxWaves * 32 * CT);
     index_topk_kernel<15, CT, false, BK><<<dim3((unsigned)grid, gy), dim3(kIdxThreads), 0, stream>>>(
-        q_idx, k_idx, N, H_kv, k, 0, block_idx, nullptr, cu, imask);
+        q_idx, k_idx, N, H_kv, k, 0, block_idx, nullptr, cu, T, imask);
   } else {
     constexpr int CT = 2;
     const int64_t grid = (total + kIdxWaves * 32 * CT - 1) / (kIdxWaves * 32 * CT);
     index_topk_kernel<31, CT, false, BK><<<dim3((unsigned)grid, gy), dim3(kIdxThreads), 0, stream>>>(
-        q_idx, k_idx, N, H_kv, k, 0, block_idx, nullptr, cu, imask);
+        q_idx, k_idx, N, H_kv, k, 0, block_idx, nullptr, cu, T, imask);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_index_topk(const uint16_t* q_idx, const uint16_t* k_idx, int64_t N, int H_kv, int k,
-                             int32_t* block_idx, const int64_t* cu, int batch, int bk, hipStream_t stream) {
-  if (bk == 64) return launch_index_topk_bk<64>(q_idx, k_idx, N, H_kv, k, block_idx, cu, batch, stream);
-  return launch_index_topk_bk<128>(q_idx, k_idx, N, H_kv, k, block_idx, cu, batch, stream);
+                             int32_t* block_idx, const int64_t* cu, int batch, int64_t T, int bk,
+                             hipStream_t stream) {
+  if (bk == 64) return launch_index_topk_bk<64>(q_idx, k_idx, N, H_kv, k, block_idx, cu, batch, T, stream);
+  return launch_index_topk_bk<128>(q_idx, k_idx, N, H_kv, k, block_idx, cu, batch, T, stream);
 }
 
 hipError_t launch_index_block_scores(const uint16_t* q_idx, const uint16_t* k_idx, int64_t N, int H_kv, int bk,
@@ -479,10 +492,10 @@ hipError_t launch_index_block_scores(const uint16_t* q_idx, const uint16_t* k_id
   const int64_t grid = (total + kIdxWaves * 32 * CT - 1) / (kIdxWaves * 32 * CT);
   if (bk == 64)
     index_topk_kernel<1, CT, true, 64><<<dim3((unsigned)grid), dim3(kIdxThreads), 0, stream>>>(
-        q_idx, k_idx, N, H_kv, 1, B, nullptr, M, nullptr, 0u);
+        q_idx, k_idx, N, H_kv, 1, B, nullptr, M, nullptr, N, 0u);
   else
     index_topk_kernel<1, CT, true, 128><<<dim3((unsigned)grid), dim3(kIdxThreads), 0, stream>>>(
-        q_idx, k_idx, N, H_kv, 1, B, nullptr, M, nullptr, 0u);
+        q_idx, k_idx, N, H_kv, 1, B, nullptr, M, nullptr, N, 0u);
   return hipGetLastError();
 }
 

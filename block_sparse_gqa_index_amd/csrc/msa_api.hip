@@ -142,7 +142,7 @@ msa_status_t msa_index_topk(const void* q_idx, const void* k_idx, int64_t N, int
     return fail(MSA_ERR_INVALID_ARG, "misaligned pointer (q_idx/k_idx need 16 B, block_idx 4 B)");
   if (N * H_kv >= ((int64_t)1 << 31)) return fail(MSA_ERR_UNSUPPORTED, "N * H_kv too large");
   hipError_t e = msa::launch_index_topk(static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx),
-                                        N, H_kv, k, block_idx, nullptr, 0, B_k, static_cast<hipStream_t>(hip_stream));
+                                        N, H_kv, k, block_idx, nullptr, 0, N, B_k, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_fail(e, "index_topk launch");
   return ok();
 }
@@ -290,7 +290,7 @@ msa_status_t msa_index_topk_varlen(const void* q_idx, const void* k_idx, const i
   if (T * H_kv >= ((int64_t)1 << 31)) return fail(MSA_ERR_UNSUPPORTED, "T * H_kv too large");
   if (batch > 65535) return fail(MSA_ERR_UNSUPPORTED, "batch must be <= 65535");
   hipError_t e = msa::launch_index_topk(static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx),
-                                        max_len, H_kv, k, block_idx, cu_seqlens, batch, B_k,
+                                        max_len, H_kv, k, block_idx, cu_seqlens, batch, T, B_k,
                                         static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_fail(e, "index_topk launch");
   return ok();
@@ -332,10 +332,10 @@ msa_status_t msa_sparse_attn_fwd_varlen(const void* q, const void* k, const void
   const msa::SeqTables S = msa::seq_tables_layout(T, batch, Bt);
   uint8_t* w = static_cast<uint8_t*>(ws);
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  hipError_t e = msa::launch_seq_tables(cu_seqlens, batch, B_k, w, S, stream);
+  hipError_t e = msa::launch_seq_tables(cu_seqlens, batch, T, B_k, w, S, stream);
   if (e != hipSuccess) return hip_fail(e, "sequence tables launch");
   msa::SeqInfo si;
-  si.cu = cu_seqlens;
+  si.cu = reinterpret_cast<const int64_t*>(w + S.cu);  // the sanitised copy
   si.bstart = reinterpret_cast<const int32_t*>(w + S.bstart);
   si.seq_tok = reinterpret_cast<const int32_t*>(w + S.seq_tok);
   si.seq_blk = reinterpret_cast<const int32_t*>(w + S.seq_blk);
@@ -509,7 +509,8 @@ size_t msa_decode_workspace(int batch, int H_q, int H_kv, int d_h, int d_idx, in
 
 // msa_decode after its shape checks: pointers, workspace, launch.
 static msa_status_t decode_run(const void* q, const void* q_idx, const void* k_cache, const void* v_cache,
-                               const void* k_idx_cache, const int64_t* cu_seqlens, int batch, int64_t max_len,
+                               const void* k_idx_cache, const int64_t* cu_seqlens, int batch, int64_t T,
+                               int64_t max_len,
                                int H_q, int H_kv, int B_k, int k, float scale, int32_t* block_idx, float* o,
                                float* lse, void* ws, size_t ws_bytes, void* hip_stream) {
   if (!q || !q_idx || !k_cache || !v_cache || !k_idx_cache || !cu_seqlens || !block_idx || !o || !lse)
@@ -526,31 +527,33 @@ static msa_status_t decode_run(const void* q, const void* q_idx, const void* k_c
   const msa::DecodeWorkspace L = msa::decode_workspace_layout(batch, H_q, H_kv, k, Bmax);
   hipError_t e = msa::launch_decode(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_cache),
-      static_cast<const uint16_t*>(v_cache), static_cast<const uint16_t*>(k_idx_cache), cu_seqlens, batch, Bmax, B_k,
+      static_cast<const uint16_t*>(v_cache), static_cast<const uint16_t*>(k_idx_cache), cu_seqlens, batch, T, Bmax, B_k,
       H_q, H_kv, k, scale, block_idx, o, lse, static_cast<uint8_t*>(ws), L, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return ok();
 }
 
 msa_status_t msa_decode(const void* q, const void* q_idx, const void* k_cache, const void* v_cache,
-                        const void* k_idx_cache, const int64_t* cu_seqlens, int batch, int64_t max_len, int H_q,
-                        int H_kv, int d_h, int d_idx, int B_k, int k, float scale, int32_t* block_idx, float* o,
-                        float* lse, void* ws, size_t ws_bytes, void* hip_stream) {
+                        const void* k_idx_cache, const int64_t* cu_seqlens, int batch, int64_t T, int64_t max_len,
+                        int H_q, int H_kv, int d_h, int d_idx, int B_k, int k, float scale, int32_t* block_idx,
+                        float* o, float* lse, void* ws, size_t ws_bytes, void* hip_stream) {
   msa_status_t st = check_decode_shape(batch, max_len, H_q, H_kv, d_h, d_idx, B_k, k);
   if (st != MSA_OK) return st;
+  if (T < 0) return fail(MSA_ERR_INVALID_ARG, "T must be >= 0");
   if (!(scale > 0.f) || scale != scale) return fail(MSA_ERR_INVALID_ARG, "scale must be a positive number");
   if (batch == 0) return ok();
   if (max_len == 0) return fail(MSA_ERR_INVALID_ARG, "max_len must be >= 1 when batch > 0");
-  return decode_run(q, q_idx, k_cache, v_cache, k_idx_cache, cu_seqlens, batch, max_len, H_q, H_kv, B_k, k, scale,
-                    block_idx, o, lse, ws, ws_bytes, hip_stream);
+  return decode_run(q, q_idx, k_cache, v_cache, k_idx_cache, cu_seqlens, batch, T, max_len, H_q, H_kv, B_k, k,
+                    scale, block_idx, o, lse, ws, ws_bytes, hip_stream);
 }
 
 msa_status_t msa_decode_noalloc(const void* q, const void* q_idx, const void* k_cache, const void* v_cache,
-                                const void* k_idx_cache, const int64_t* cu_seqlens, int batch, int64_t max_len,
-                                int H_q, int H_kv, int d_h, int d_idx, int B_k, int k, float scale,
+                                const void* k_idx_cache, const int64_t* cu_seqlens, int batch, int64_t T,
+                                int64_t max_len, int H_q, int H_kv, int d_h, int d_idx, int B_k, int k, float scale,
                                 int32_t* block_idx, float* o, float* lse, void* hip_stream) {
   msa_status_t st = check_decode_shape(batch, max_len, H_q, H_kv, d_h, d_idx, B_k, k);
   if (st != MSA_OK) return st;
+  if (T < 0) return fail(MSA_ERR_INVALID_ARG, "T must be >= 0");
   if (!(scale > 0.f) || scale != scale) return fail(MSA_ERR_INVALID_ARG, "scale must be a positive number");
   if (batch == 0) return ok();
   if (max_len == 0) return fail(MSA_ERR_INVALID_ARG, "max_len must be >= 1 when batch > 0");
@@ -561,13 +564,14 @@ msa_status_t msa_decode_noalloc(const void* q, const void* q_idx, const void* k_
                 "call msa_decode with a workspace instead", need, (size_t)MSA_DECODE_NOALLOC_SCRATCH_BYTES);
   uint8_t* ws = nullptr;
   if ((st = scratch_on_current_device(&ws)) != MSA_OK) return st;
-  return decode_run(q, q_idx, k_cache, v_cache, k_idx_cache, cu_seqlens, batch, max_len, H_q, H_kv, B_k, k, scale,
-                    block_idx, o, lse, ws, (size_t)MSA_DECODE_NOALLOC_SCRATCH_BYTES, hip_stream);
+  return decode_run(q, q_idx, k_cache, v_cache, k_idx_cache, cu_seqlens, batch, T, max_len, H_q, H_kv, B_k, k,
+                    scale, block_idx, o, lse, ws, (size_t)MSA_DECODE_NOALLOC_SCRATCH_BYTES, hip_stream);
 }
 
 msa_status_t msa_decode_paged(const void* q, const void* q_idx, const void* k_pages, const void* v_pages,
                               float k_scale, float v_scale, const void* k_idx_pages, const int32_t* block_table,
-                              int64_t max_blocks, const int64_t* seqlens, int batch, int64_t max_len, int H_q,
+                              int64_t max_blocks, int64_t num_pages, const int64_t* seqlens, int batch,
+                              int64_t max_len, int H_q,
                               int H_kv, int d_h, int d_idx, int B_k, int k, float scale, int32_t* block_idx,
                               float* o, float* lse, void* ws, size_t ws_bytes, void* hip_stream) {
   msa_status_t st = check_decode_shape(batch, max_len, H_q, H_kv, d_h, d_idx, B_k, k);
@@ -582,6 +586,7 @@ msa_status_t msa_decode_paged(const void* q, const void* q_idx, const void* k_pa
   if (max_blocks < Bmax)
     return fail(MSA_ERR_INVALID_ARG, "max_blocks (%lld) must cover ceil(max_len / B_k) = %lld",
                 (long long)max_blocks, (long long)Bmax);
+  if (num_pages < 1) return fail(MSA_ERR_INVALID_ARG, "num_pages must be >= 1 when batch > 0");
   if (!q || !q_idx || !k_pages || !v_pages || !k_idx_pages || !block_table || !seqlens || !block_idx || !o || !lse)
     return fail(MSA_ERR_INVALID_ARG, "null pointer");
   if (!aligned(q, 16) || !aligned(q_idx, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) ||
@@ -596,8 +601,8 @@ msa_status_t msa_decode_paged(const void* q, const void* q_idx, const void* k_pa
   hipError_t e = msa::launch_decode_paged(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(q_idx), static_cast<const uint8_t*>(k_pages),
       static_cast<const uint8_t*>(v_pages), k_scale, v_scale, static_cast<const uint16_t*>(k_idx_pages), block_table,
-      max_blocks, seqlens, batch, Bmax, B_k, H_q, H_kv, k, scale, block_idx, o, lse, static_cast<uint8_t*>(ws), L,
-      static_cast<hipStream_t>(hip_stream));
+      max_blocks, num_pages, seqlens, batch, Bmax, B_k, H_q, H_kv, k, scale, block_idx, o, lse,
+      static_cast<uint8_t*>(ws), L, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_fail(e, "paged decode launch");
   return ok();
 }

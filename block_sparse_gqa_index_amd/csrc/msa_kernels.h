@@ -32,7 +32,8 @@ struct DecodeWorkspace {
 
 // bk: keys per block, 64 or 128.
 hipError_t launch_index_topk(const uint16_t* q_idx, const uint16_t* k_idx, int64_t N, int H_kv, int k,
-                             int32_t* block_idx, const int64_t* cu, int batch, int bk, hipStream_t stream);
+                             int32_t* block_idx, const int64_t* cu, int batch, int64_t T, int bk,
+                             hipStream_t stream);
 hipError_t launch_index_block_scores(const uint16_t* q_idx, const uint16_t* k_idx, int64_t N, int H_kv, int bk,
                                      float* M, hipStream_t stream);
 hipError_t launch_topk_from_scores(const float* M, int64_t N, int H_kv, int64_t B, int k, int bk,
@@ -49,12 +50,15 @@ struct SeqInfo {
   const int32_t* seq_blk = nullptr;
 };
 struct SeqTables {
-  size_t bstart, seq_tok, seq_blk, total;
+  size_t cu, bstart, seq_tok, seq_blk, total;
 };
 // Workspace bytes of the tables for T tokens in `batch` sequences with at most Bt
 // global blocks (0 for a single sequence).
 SeqTables seq_tables_layout(int64_t T, int batch, int64_t Bt);
-hipError_t launch_seq_tables(const int64_t* cu, int batch, int bk, uint8_t* ws, const SeqTables& S,
+// Builds the tables from the caller's offsets cu[0..batch]: first a sanitised copy of
+// the offsets (region S.cu; every later kernel reads that copy), then the block starts
+// and the per-token and per-block sequence numbers.
+hipError_t launch_seq_tables(const int64_t* cu, int batch, int64_t T, int bk, uint8_t* ws, const SeqTables& S,
                              hipStream_t stream);
 
 // B: the list stride in blocks (the block count, or for several sequences an upper
@@ -105,13 +109,13 @@ hipError_t launch_bwd_window(const uint16_t* q, const uint16_t* k, const uint16_
 DecodeWorkspace decode_workspace_layout(int batch, int H_q, int H_kv, int kk, int64_t Bmax);
 hipError_t launch_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_t* k_cache,
                          const uint16_t* v_cache, const uint16_t* k_idx_cache, const int64_t* cu, int batch,
-                         int64_t Bmax, int bk, int H_q, int H_kv, int kk, float scale, int32_t* block_idx, float* o,
+                         int64_t T, int64_t Bmax, int bk, int H_q, int H_kv, int kk, float scale, int32_t* block_idx, float* o,
                          float* lse, uint8_t* ws, const DecodeWorkspace& L, hipStream_t stream);
 // Paged caches: FP8 E4M3 K/V pages and bf16 index-key pages of bk tokens (64 or 128).
 hipError_t launch_decode_paged(const uint16_t* q, const uint16_t* q_idx, const uint8_t* k_pages,
                                const uint8_t* v_pages, float k_scale, float v_scale, const uint16_t* kidx_pages,
-                               const int32_t* block_table, int64_t max_blocks, const int64_t* seqlens, int batch,
-                               int64_t Bmax, int bk, int H_q, int H_kv, int kk, float scale, int32_t* block_idx,
+                               const int32_t* block_table, int64_t max_blocks, int64_t num_pages,
+                               const int64_t* seqlens, int batch, int64_t Bmax, int bk, int H_q, int H_kv, int kk, float scale, int32_t* block_idx,
                                float* o, float* lse, uint8_t* ws, const DecodeWorkspace& L, hipStream_t stream);
 
 }  // namespace msa

@@ -19,6 +19,7 @@
 // partials of hot (sink) blocks spread over many workgroups without atomics.
 #include "msa_device.h"
 #include "msa_kernels.h"
+#include "table_clamp.h"
 
 namespace msa {
 
@@ -109,6 +110,29 @@ __device__ __forceinline__ int64_t block_sum_1024(int64_t x, int64_t* lds) {
   return t;
 }
 
+// Inclusive running maximum over the 1024 threads of a workgroup (lds: 16 slots);
+// *all receives the maximum over every thread.
+__device__ __forceinline__ int64_t block_incl_max_1024(int64_t x, int64_t* lds, int64_t* all) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int64_t inc = x;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const int64_t y = __shfl_up(inc, m);
+    if (lane >= m && y > inc) inc = y;
+  }
+  __syncthreads();
+  if (lane == 63) lds[wave] = inc;
+  __syncthreads();
+  int64_t before = inc, tot = lds[0];
+  for (int w = 0; w < 16; ++w) {
+    const int64_t t = lds[w];
+    if (w < wave && t > before) before = t;
+    if (t > tot) tot = t;
+  }
+  *all = tot;
+  return before;
+}
+
 // Exclusive scan over the 1024 threads of a workgroup (lds: 16 slots).
 __device__ __forceinline__ int64_t block_excl_scan_1024(int64_t x, int64_t* lds) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -140,7 +164,8 @@ __global__ __launch_bounds__(kScanTile) void inv_tile_sums_kernel(const int32_t*
 }
 
 __global__ __launch_bounds__(kScanTile) void inv_scan_write_kernel(const int32_t* __restrict__ counts, int64_t L,
-                                                                 int item_q, const int64_t* __restrict__ tsum,
+                                                                 int64_t B, int nW, int item_q,
+                                                                 const int64_t* __restrict__ tsum,
                                                                  int32_t* __restrict__ cursor,
                                                                  int4* __restrict__ items,
                                                                  int32_t* __restrict__ n_items,
@@ -165,7 +190,7 @@ __global__ __launch_bounds__(kScanTile) void inv_scan_write_kernel(const int32_t
     for (int it = 0; it < nit; ++it) {
       const int start = (int)poff + it * item_q;
       const int cnt = (c - it * item_q < item_q) ? c - it * item_q : item_q;
-      items[ioff + it] = make_int4((int)l, start, cnt, 0);
+      items[ioff + it] = make_int4((int)(l % B), start, cnt, (int)((l / B) / nW));
     }
   }
   if (l == L - 1) *n_items = (int32_t)(ioff + nit);
@@ -438,7 +463,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
     const int64_t item = round * grid + (int64_t)xcd * per_xcd + slot_in_xcd;
     if (item >= n_items) break;
     const int4 it = items[item];
-    const int64_t gb = it.x % B, r = (it.x / B) / nW;
+    const int64_t gb = it.x, r = it.w;
     const int start = it.y, cnt = it.z;
     // The list's block: block b of sequence s_item, whose tokens are [j0, j0 + seqN).
     const int s_item = si.cu ? si.seq_blk[gb] : 0;
@@ -663,7 +688,11 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
             // Half-rows 8u..8u+3 and 8u+4..8u+7 belong to the pairs of gather loads
             // 2u and 2u+1.
             const int row = wave_u * 32 + rho;
-            const int pu = (lane >> 5) ? prs[2 * u + 1] : prs[2 * u];
+            // A blend with an opaque mask: a plain select by lane half becomes an
+            // indexed load from a stack copy of prs.
+            int hm = -(lane >> 5);
+            asm volatile("" : "+v"(hm));
+            const int pu = (prs[2 * u + 1] & hm) | (prs[2 * u] & ~hm);
             const int64_t prow_s = (((int64_t)(pu >> 5) * H_kv + r) * kk + (pu & 31)) * G + row % G;
             __builtin_nontemporal_store(val, reinterpret_cast<u32x4_t*>(Opart + prow_s * kDh + 64 * hd + ch * 8));
           } else {
@@ -807,11 +836,25 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   if (lane % LPH == 0) lse[i * H_q + r * G + g] = (mstar + __log2f(L)) * kLn2;
 }
 
-// Tables of a varlen call (one workgroup): bstart[s] = sum over earlier sequences
-// of their block counts ceil(len / B_k), bstart[batch] = the total.
-__global__ __launch_bounds__(kScanTile) void seq_block_starts_kernel(const int64_t* __restrict__ cu, int batch,
-                                                                   int bk, int32_t* __restrict__ bstart) {
+// Tables of a varlen call (one workgroup).  First the caller's offsets cu_in[0..batch]
+// are copied to cu as sanitized_offset() of their running maximum: 0, non-decreasing,
+// T at the end, so the sequences partition [0, T) even if the table is malformed (a
+// well-formed table is copied unchanged).  Then, from that copy, bstart[s] = the sum
+// over earlier sequences of their block counts ceil(len / B_k), bstart[batch] = the
+// total.
+__global__ __launch_bounds__(kScanTile) void seq_block_starts_kernel(const int64_t* __restrict__ cu_in, int batch,
+                                                                   int64_t T, int bk, int64_t* __restrict__ cu,
+                                                                   int32_t* __restrict__ bstart) {
   __shared__ int64_t lds[16];
+  int64_t pmax = INT64_MIN;
+  for (int s0 = 0; s0 <= batch; s0 += kScanTile) {
+    const int s = s0 + threadIdx.x;
+    int64_t tile_max;
+    const int64_t run = block_incl_max_1024(s <= batch ? cu_in[s] : INT64_MIN, lds, &tile_max);
+    if (s <= batch) cu[s] = sanitized_offset(run > pmax ? run : pmax, s, batch, T);
+    if (tile_max > pmax) pmax = tile_max;
+  }
+  __syncthreads();  // the copy is read back below by other threads of the workgroup
   int64_t carry = 0;
   for (int s0 = 0; s0 < batch; s0 += kScanTile) {
     const int s = s0 + threadIdx.x;
@@ -893,10 +936,24 @@ struct KlRows {
   static constexpr bool kCross = G >= 8;         // the other heads are in lane ^ 32
 };
 
+// Register budget of kl_pair_kernel<G, BK>.  A lane keeps the running sums of its
+// KlRows<G>::NQ queries (16 at G = 1) and the next chunk's operands in flight, which
+// leaves the compiler little slack at two workgroups per CU.  Per variant, chosen
+// from the compiler's resource-usage report so that none spills registers:
+//  - G = 1, and G = 2 with 64-key blocks, run one workgroup per CU (their running
+//    sums do not fit the 256 registers of two);
+//  - G = 4 with 128-key blocks walks its four key tiles in a loop rather than
+//    unrolled (the unrolled form spills at two workgroups per CU).
+template <int G, int BK>
+struct KlRegs {
+  static constexpr int kBlocksPerCU = (G == 1 || (G == 2 && BK == 64)) ? 1 : 2;
+  static constexpr int kTileUnroll = (G == 4 && BK == 128) ? 1 : BK / 32;
+};
+
 // BK: keys per block (64 or 128); a 64-key block fills the first half of the
 // staged tiles, and only its two 32-key tiles are computed.
 template <int G, int BK>
-__global__ __launch_bounds__(kAttnThreads, 2) void kl_pair_kernel(
+__global__ __launch_bounds__(kAttnThreads, (KlRegs<G, BK>::kBlocksPerCU)) void kl_pair_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp, const uint16_t* __restrict__ q_idx,
     const uint16_t* __restrict__ k_idx, const float* __restrict__ lse, const int4* __restrict__ items,
     const int32_t* __restrict__ n_items_ptr, const int32_t* __restrict__ pairs, int64_t N, int H_kv, int64_t B,
@@ -920,7 +977,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void kl_pair_kernel(
     const int64_t item = round * grid + (int64_t)xcd * per_xcd + slot_in_xcd;
     if (item >= n_items) break;
     const int4 it = items[item];
-    const int64_t b = it.x % B, r = (it.x / B) / nW;
+    const int64_t b = it.x, r = it.w;
     const int start = it.y, cnt = it.z;
 
     constexpr int NR = kPairRegs<G>;
@@ -969,8 +1026,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void kl_pair_kernel(
     // Index query of the lane's own row (dims 32h + 8t .. +7 for step t) and its
     // head's main log partition in base 2.
     auto lane_operands = [&](int prv, u32x4_t (&qi)[4], float& l2) {
+      int hh = h;  // opaque: the lane's base address is formed per call, not held
+      asm volatile("" : "+v"(hh));
       const int64_t iq = w0 + (prv >> 5);
-      const uint16_t* src = q_idx + (iq * H_kv + r) * kDidx + 32 * h;
+      const uint16_t* src = q_idx + (iq * H_kv + r) * kDidx + 32 * hh;
 #pragma unroll
       for (int t = 0; t < 4; ++t) qi[t] = *reinterpret_cast<const u32x4_t*>(src + 8 * t);
       l2 = lse[iq * H_q + r * G + g] * kLog2e;
@@ -988,14 +1047,18 @@ __global__ __launch_bounds__(kAttnThreads, 2) void kl_pair_kernel(
       asm volatile("" ::: "memory");
       // Output rows of this lane (row 8*(v/4) + 4h + v%4 is the own row of lane
       // with that l32): lse of all 16, pair of each query.
+      // (The source lanes are formed from an opaque base each chunk: as constants
+      // they would be hoisted and hold 16 + NQ registers across the loop.)
       float l2v[16];
       int prq[NQ];
+      int hb = 4 * h;
+      asm volatile("" : "+v"(hb));
 #pragma unroll
-      for (int v = 0; v < 16; ++v) l2v[v] = __shfl(l2own, 8 * (v >> 2) + 4 * h + (v & 3));
+      for (int v = 0; v < 16; ++v) l2v[v] = __shfl(l2own, 8 * (v >> 2) + hb + (v & 3));
 #pragma unroll
       for (int qq = 0; qq < NQ; ++qq) {
         const int v0 = qq * GL;
-        prq[qq] = __shfl(pr, 8 * (v0 >> 2) + 4 * h + (v0 & 3));
+        prq[qq] = __shfl(pr, 8 * (v0 >> 2) + hb + (v0 & 3));
       }
 
       // Next chunk's q rows and per-lane operands, in flight during this chunk.
@@ -1027,7 +1090,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void kl_pair_kernel(
         A[qq] = C[qq] = Z[qq] = l[qq] = 0.f;
         mx[qq] = -__builtin_inff();
       }
-#pragma unroll
+#pragma unroll KlRegs<G, BK>::kTileUnroll
       for (int kt = 0; kt < BK / 32; ++kt) {
         f32x16_t sacc = f32x16_t{}, iacc = f32x16_t{};
 #pragma unroll
@@ -1185,6 +1248,7 @@ SeqTables seq_tables_layout(int64_t T, int batch, int64_t Bt) {
     off += (bytes + 255) & ~size_t(255);
     return o;
   };
+  S.cu = take(sizeof(int64_t) * ((size_t)batch + 1));
   S.bstart = take(sizeof(int32_t) * ((size_t)batch + 1));
   S.seq_tok = take(sizeof(int32_t) * (size_t)T);
   S.seq_blk = take(sizeof(int32_t) * (size_t)Bt);
@@ -1192,10 +1256,11 @@ SeqTables seq_tables_layout(int64_t T, int batch, int64_t Bt) {
   return S;
 }
 
-hipError_t launch_seq_tables(const int64_t* cu, int batch, int bk, uint8_t* ws, const SeqTables& S,
+hipError_t launch_seq_tables(const int64_t* cu_in, int batch, int64_t T, int bk, uint8_t* ws, const SeqTables& S,
                              hipStream_t stream) {
   int32_t* bstart = reinterpret_cast<int32_t*>(ws + S.bstart);
-  seq_block_starts_kernel<<<dim3(1), dim3(kScanTile), 0, stream>>>(cu, batch, bk, bstart);
+  int64_t* cu = reinterpret_cast<int64_t*>(ws + S.cu);
+  seq_block_starts_kernel<<<dim3(1), dim3(kScanTile), 0, stream>>>(cu_in, batch, T, bk, cu, bstart);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   seq_fill_kernel<<<dim3((unsigned)batch), dim3(256), 0, stream>>>(cu, bstart, reinterpret_cast<int32_t*>(ws + S.seq_tok),
@@ -1286,8 +1351,8 @@ hipError_t launch_inverse_index(const int32_t* block_idx, int64_t B, const SeqIn
   int64_t* tsum = reinterpret_cast<int64_t*>(ws + L.tsum);
   inv_tile_sums_kernel<<<dim3(tiles), dim3(kScanTile), 0, stream>>>(counts, lists, L.item_q, tsum);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  inv_scan_write_kernel<<<dim3(tiles), dim3(kScanTile), 0, stream>>>(counts, lists, L.item_q, tsum, cursor, items,
-                                                                    n_items, lfirst);
+  inv_scan_write_kernel<<<dim3(tiles), dim3(kScanTile), 0, stream>>>(counts, lists, B, L.nW, L.item_q, tsum, cursor,
+                                                                    items, n_items, lfirst);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ordered) {
     inv_tile_base_kernel<<<dim3((unsigned)((lists + 255) / 256)), dim3(256), 0, stream>>>(

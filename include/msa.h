@@ -163,8 +163,14 @@ msa_status_t msa_sparse_attn_bwd(const void* q, const void* k, const void* v, co
  * on such packed documents; the arithmetic per sequence is that of the calls above.
  *   cu_seqlens int64 [batch + 1], device memory: cu[0] = 0, non-decreasing,
  *              cu[batch] = T; sequence s holds tokens cu[s] .. cu[s+1]-1 (length 0
- *              is allowed).  Not checked on the device: other values read out of
- *              bounds.
+ *              is allowed).  The host cannot check it; the kernels clamp what they
+ *              read so that no access leaves the buffers: the index call reads
+ *              sequence s as [clamp(cu[s], 0, T), clamp(cu[s+1], that, T)), the
+ *              attention call first copies the table into its workspace with entry s
+ *              replaced by the running maximum of cu[0..s] clamped into [0, T],
+ *              entry 0 by 0 and entry batch by T.  A well-formed table is unchanged
+ *              by both; for any other the results are unspecified but every read and
+ *              write stays inside the caller's buffers.
  *   Tensors are those of the calls above with N replaced by T (rows stay global);
  *   block_idx entries are block numbers within the row's own sequence.
  *   Limits: ceil(T / B_k) + batch <= 8192, batch <= 65535.
@@ -202,7 +208,11 @@ msa_status_t msa_sparse_attn_fwd_varlen(const void* q, const void* k, const void
  * them is split across workgroups and merged by log-sum-exp.
  *   q            bf16 [batch, H_q, d_h];  q_idx  bf16 [batch, H_kv, d_idx]
  *   k_cache, v_cache bf16 [T, H_kv, d_h]; k_idx_cache bf16 [T, d_idx]
- *   cu_seqlens   int64 [batch + 1], device memory, cu[0] = 0, cu[s+1] - cu[s] = L_s
+ *   cu_seqlens   int64 [batch + 1], device memory, cu[0] = 0, cu[s+1] - cu[s] = L_s;
+ *                sequence s is read as [clamp(cu[s], 0, T), clamp(cu[s+1], that, T)),
+ *                so a malformed table cannot read outside the caches (results are
+ *                then unspecified)
+ *   T            cached tokens (rows of the three caches), host
  *   max_len      host-side bound on every L_s (sizes the launch and workspace; a
  *                longer sequence is only scored over its first max_len tokens)
  *   block_idx    int32 [batch, H_kv, k]  out (as for msa_index_topk)
@@ -215,7 +225,7 @@ msa_status_t msa_sparse_attn_fwd_varlen(const void* q, const void* k, const void
 size_t msa_decode_workspace(int batch, int H_q, int H_kv, int d_h, int d_idx, int B_k, int k,
                             int64_t max_len);
 msa_status_t msa_decode(const void* q, const void* q_idx, const void* k_cache, const void* v_cache,
-                        const void* k_idx_cache, const int64_t* cu_seqlens, int batch,
+                        const void* k_idx_cache, const int64_t* cu_seqlens, int batch, int64_t T,
                         int64_t max_len, int H_q, int H_kv, int d_h, int d_idx, int B_k, int k,
                         float scale, int32_t* block_idx, float* o, float* lse, void* ws,
                         size_t ws_bytes, void* hip_stream);
@@ -240,8 +250,8 @@ msa_status_t msa_decode(const void* q, const void* q_idx, const void* k_cache, c
 #define MSA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
 msa_status_t msa_decode_noalloc(const void* q, const void* q_idx, const void* k_cache,
                                 const void* v_cache, const void* k_idx_cache,
-                                const int64_t* cu_seqlens, int batch, int64_t max_len, int H_q,
-                                int H_kv, int d_h, int d_idx, int B_k, int k, float scale,
+                                const int64_t* cu_seqlens, int batch, int64_t T, int64_t max_len,
+                                int H_q, int H_kv, int d_h, int d_idx, int B_k, int k, float scale,
                                 int32_t* block_idx, float* o, float* lse, void* hip_stream);
 
 /* ------------------------------------------------------------------ Paged FP8 decode
@@ -253,9 +263,13 @@ msa_status_t msa_decode_noalloc(const void* q, const void* q_idx, const void* k_
  *   k_idx_pages       bf16 [P, B_k, d_idx]       index keys (kept at bf16: they
  *                     decide the selection)
  *   block_table       int32 [batch, max_blocks], device; entries for blocks
- *                     0 .. ceil(L_s / B_k) - 1 must be valid page numbers (not
- *                     checked on the device), the rest are never read
+ *                     0 .. ceil(L_s / B_k) - 1 must be page numbers in [0, P), the
+ *                     rest are never read
+ *   num_pages         P, the pages of the three page arrays (>= 1), host
  *   seqlens           int64 [batch], device: L_s (the new token is position L_s - 1)
+ *   The kernels read L_s clamped into [0, max_blocks * B_k] and every page number
+ *   clamped into [0, P - 1], so malformed tables cannot read outside the buffers
+ *   (results are then unspecified).
  *   max_len           host-side bound on every L_s, as for msa_decode
  * Other arguments and outputs as msa_decode; the workspace size is
  * msa_decode_workspace() of the same shapes.  FP8 values are widened to bf16
@@ -264,8 +278,9 @@ msa_status_t msa_decode_noalloc(const void* q, const void* q_idx, const void* k_
 msa_status_t msa_decode_paged(const void* q, const void* q_idx, const void* k_pages,
                               const void* v_pages, float k_scale, float v_scale,
                               const void* k_idx_pages, const int32_t* block_table,
-                              int64_t max_blocks, const int64_t* seqlens, int batch,
-                              int64_t max_len, int H_q, int H_kv, int d_h, int d_idx, int B_k,
+                              int64_t max_blocks, int64_t num_pages, const int64_t* seqlens,
+                              int batch, int64_t max_len, int H_q, int H_kv, int d_h, int d_idx,
+                              int B_k,
                               int k, float scale, int32_t* block_idx, float* o, float* lse,
                               void* ws, size_t ws_bytes, void* hip_stream);
 

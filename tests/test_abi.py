@@ -108,14 +108,15 @@ def test_decode_rejects_bad_arguments(lib):
     f = 0x10000
 
     def call(batch=4, max_len=1024, H_q=16, H_kv=2, d_h=128, d_idx=64, B_k=128, k=4, ws=f, ws_bytes=1 << 40,
-             cu=f):
-        return raw.msa_decode(f, f, f, f, f, cu, batch, max_len, H_q, H_kv, d_h, d_idx, B_k, k, 0.088, f, f, f,
+             cu=f, T=4096):
+        return raw.msa_decode(f, f, f, f, f, cu, batch, T, max_len, H_q, H_kv, d_h, d_idx, B_k, k, 0.088, f, f, f,
                               ws, ws_bytes, None)
 
     assert call(d_idx=128) == lib.MSA_ERR_UNSUPPORTED
     assert call(H_q=64, H_kv=2) == lib.MSA_ERR_UNSUPPORTED  # G = 32 > 16
     assert call(batch=-1) == lib.MSA_ERR_INVALID_ARG
     assert call(max_len=0) == lib.MSA_ERR_INVALID_ARG
+    assert call(T=-1) == lib.MSA_ERR_INVALID_ARG
     assert call(cu=None) == lib.MSA_ERR_INVALID_ARG
     assert call(cu=f + 4) == lib.MSA_ERR_INVALID_ARG
     assert call(ws_bytes=16) == lib.MSA_ERR_WORKSPACE
@@ -228,15 +229,16 @@ def test_decode_paged_rejects_bad_arguments(lib):
     f = 0x10000
 
     def call(batch=4, max_len=1024, H_q=16, H_kv=2, k=4, ks=0.01, vs=0.01, max_blocks=8, bt=f, lens=f,
-             ws=f, ws_bytes=1 << 40, B_k=128):
-        return raw.msa_decode_paged(f, f, f, f, ks, vs, f, bt, max_blocks, lens, batch, max_len, H_q, H_kv, 128, 64,
-                                    B_k, k, 0.088, f, f, f, ws, ws_bytes, None)
+             ws=f, ws_bytes=1 << 40, B_k=128, num_pages=64):
+        return raw.msa_decode_paged(f, f, f, f, ks, vs, f, bt, max_blocks, num_pages, lens, batch, max_len, H_q,
+                                    H_kv, 128, 64, B_k, k, 0.088, f, f, f, ws, ws_bytes, None)
 
     assert call(B_k=32, max_blocks=32) == lib.MSA_ERR_UNSUPPORTED
 
     assert call(ks=0.0) == lib.MSA_ERR_INVALID_ARG
     assert call(vs=float("inf")) == lib.MSA_ERR_INVALID_ARG
     assert call(max_blocks=7) == lib.MSA_ERR_INVALID_ARG  # ceil(1024 / 128) = 8 blocks per row needed
+    assert call(num_pages=0) == lib.MSA_ERR_INVALID_ARG
     assert call(bt=None) == lib.MSA_ERR_INVALID_ARG
     assert call(lens=f + 4) == lib.MSA_ERR_INVALID_ARG
     assert call(H_q=64, H_kv=2) == lib.MSA_ERR_UNSUPPORTED
@@ -267,9 +269,13 @@ def test_noalloc_decode_rejects_shapes_beyond_its_static_scratch(lib):
     raw = lib.raw()
     f = 0x10000  # never dereferenced: the size check comes before any pointer or device use
     # 512 sequences of 1M tokens need 128 MiB of block scores: above the 32 MiB scratch.
-    st = raw.msa_decode_noalloc(f, f, f, f, f, f, 512, 1 << 20, 64, 8, 128, 64, 128, 16, 0.088, f, f, f, None)
+    st = raw.msa_decode_noalloc(f, f, f, f, f, f, 512, 512 << 20, 1 << 20, 64, 8, 128, 64, 128, 16, 0.088, f, f, f,
+                                None)
     assert st == lib.MSA_ERR_WORKSPACE
     assert "static" in raw.msa_last_error().decode()
-    assert raw.msa_decode_noalloc(f, f, f, f, f, f, 0, 0, 64, 8, 128, 64, 128, 16, 0.088, f, f, f, None) == lib.MSA_OK
-    assert raw.msa_decode_noalloc(f, f, f, f, f, f, 4, 4096, 64, 8, 64, 64, 128, 16, 0.088, f, f, f,
+    assert raw.msa_decode_noalloc(f, f, f, f, f, f, 0, 0, 0, 64, 8, 128, 64, 128, 16, 0.088, f, f, f,
+                                  None) == lib.MSA_OK
+    assert raw.msa_decode_noalloc(f, f, f, f, f, f, 4, 16384, 4096, 64, 8, 64, 64, 128, 16, 0.088, f, f, f,
                                   None) == lib.MSA_ERR_UNSUPPORTED  # d_h = 64
+    assert raw.msa_decode_noalloc(f, f, f, f, f, f, 4, -1, 4096, 64, 8, 128, 64, 128, 16, 0.088, f, f, f,
+                                  None) == lib.MSA_ERR_INVALID_ARG  # T < 0

@@ -43,6 +43,7 @@ def test_noalloc_decode_matches_workspace_decode_twice(msa):
 def test_noalloc_decode_rejects_shapes_beyond_the_scratch(msa):
     raw = msa.raw()
     f = 0x10000  # never dereferenced: the size check fails first
-    st = raw.msa_decode_noalloc(f, f, f, f, f, f, 512, 1 << 20, 64, 8, 128, 64, 128, 16, 0.088, f, f, f, None)
+    st = raw.msa_decode_noalloc(f, f, f, f, f, f, 512, 512 << 20, 1 << 20, 64, 8, 128, 64, 128, 16, 0.088, f, f, f,
+                                None)
     assert st == msa.MSA_ERR_WORKSPACE
     assert "static" in raw.msa_last_error().decode()
