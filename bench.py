@@ -308,6 +308,39 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+CLOCK_HZ = 100e6  # the GPU's constant-rate clock (s_memrealtime)
+
+
+def load_balance(msa, call, max_wg=1024):
+    """Per-workgroup start / end clocks of one persistent-grid launch (the library's
+    clock hook) reduced to: span, mean busy fraction of the grid over the span, the
+    time every workgroup is running (last start to first end), and the tail from the
+    first workgroup to finish to the last."""
+    import torch
+    clk = torch.zeros(2 * max_wg, dtype=torch.int64, device="cuda")
+    torch.cuda.synchronize()
+    msa.msa_set_profile_clock(clk)
+    try:
+        call()
+        torch.cuda.synchronize()
+    finally:
+        msa.msa_set_profile_clock(None)
+    c = clk.view(-1, 2).cpu()
+    c = c[(c[:, 0] != 0) & (c[:, 1] != 0)].double()
+    if c.shape[0] == 0:
+        return None
+    us = lambda ticks: round(float(ticks) / CLOCK_HZ * 1e6, 2)
+    t0, t1 = c[:, 0].min(), c[:, 1].max()
+    span = float(t1 - t0)
+    ends = c[:, 1].sort().values
+    return {"workgroups": int(c.shape[0]), "span_us": us(span),
+            "busy_frac": round(float((c[:, 1] - c[:, 0]).sum()) / (c.shape[0] * span), 4),
+            "all_running_us": us(max(0.0, float(c[:, 1].min() - c[:, 0].max()))),
+            "tail_first_end_to_last_us": us(t1 - ends[0]),
+            "tail_p90_end_to_last_us": us(t1 - ends[int(0.9 * (len(ends) - 1))]),
+            "last_start_us": us(c[:, 0].max() - t0)}
+
+
 def run_prefill(msa, synth, cfg, mode, steps, warmup, with_kl=False, with_bwd=False):
     import torch
     dev = "cuda"
@@ -394,6 +427,8 @@ def run_prefill(msa, synth, cfg, mode, steps, warmup, with_kl=False, with_bwd=Fa
         "block0_fanin_per_group": int(fan[:, 0].float().mean().item()), "max_fanin": int(fan.max().item()),
         "median_fanin": float(fan.float().median().item()),
     }
+    res["phase1_load_balance"] = load_balance(
+        msa, lambda: msa.msa_sparse_attn_fwd(inp.q, inp.k, inp.v, block_idx, B_k=B_k, o=o, lse=lse, workspace=ws))
     del ws
     if with_kl:
         res["kl"] = run_kl(msa, inp, cfg, block_idx, lse, slot_pairs, lists, pairs, steps)
@@ -489,7 +524,7 @@ def run_bwd(msa, inp, cfg, block_idx, o, lse, slot_pairs, pairs, steps):
     flops = 10 * cfg.d_h * pairs
     out = {"ms": round(ms, 4), "tflops": round(flops / (ms / 1e3) / 1e12, 2),
            "mfma_peak_frac": round(flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4), "steps": steps,
-           "workspace_bytes": int(ws.numel())}
+           "workspace_bytes": int(ws.numel()), "main_kernel_load_balance": load_balance(msa, step)}
     del ws, dO, dq, dk, dv
     torch.cuda.empty_cache()
     return out

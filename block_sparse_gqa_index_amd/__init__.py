@@ -45,6 +45,7 @@ _SIGS = {
     "msa_index_block_scores": ([_P, _P, _I64, _I32, _I32, _I32, _P, _P], _I32),
     "msa_topk_from_scores": ([_P, _I64, _I32, _I64, _I32, _I32, _P, _P], _I32),
     "msa_set_profile_events": ([ctypes.POINTER(_P), _I32], _I32),
+    "msa_set_profile_clock": ([_P, _I64], _I32),
     "msa_sparse_kl_fwd_workspace": ([_I64, _I32, _I32, _I32, _I32, _I32, _I32], _SZ),
     "msa_sparse_kl_fwd_workspace_min": ([_I64, _I32, _I32, _I32, _I32, _I32, _I32], _SZ),
     "msa_sparse_kl_fwd": ([_P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _F32, _P, _P, _P, _P, _SZ,
@@ -452,6 +453,18 @@ def msa_set_profile_events(events=None) -> None:
             e.record()
     arr = (_P * len(events))(*[e.cuda_event for e in events])
     _check(_lib.msa_set_profile_events(arr, len(events)), "msa_set_profile_events")
+
+
+def msa_set_profile_clock(clock: torch.Tensor | None = None) -> None:
+    """Per-workgroup start / end clocks (100 MHz) of the persistent-grid kernels of
+    later calls on this thread (phase 1 of msa_sparse_attn_fwd, the backward's main
+    kernel; first query window only) into ``clock`` (int64 on the device, two per
+    workgroup); None clears."""
+    if clock is None:
+        _check(_lib.msa_set_profile_clock(None, 0), "msa_set_profile_clock")
+        return
+    _need(clock, "clock", torch.int64, (clock.numel(),))
+    _check(_lib.msa_set_profile_clock(_ptr(clock), clock.numel()), "msa_set_profile_clock")
 
 
 def raw():

@@ -113,7 +113,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
     const uint16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Drow,
     const int4* __restrict__ items, const int32_t* __restrict__ n_items_ptr, const int32_t* __restrict__ pairs,
     int64_t N, int H_kv, int64_t B, int bk, int nW, int kk, int64_t w0, float scale, float scale_log2,
-    uint16_t* __restrict__ dq_part, float* __restrict__ dkv_part) {
+    uint16_t* __restrict__ dq_part, float* __restrict__ dkv_part, int32_t* __restrict__ ctr,
+    uint64_t* __restrict__ clk) {
   static_assert(G <= 32, "a sub-chunk holds at least two queries");
   constexpr int kQS = kBwdRows / G;  // queries per sub-chunk
   // 3 x 32 KB block tiles + 4 x 16 KB sub-chunk tiles = 160 KB (one workgroup per CU).
@@ -131,19 +132,25 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
   const int h = lane >> 5, l32 = lane & 31;
   const int H_q = H_kv * G;
   const int n_items = *n_items_ptr;
-  const int grid = gridDim.x;
-  const int per_xcd = grid >> 3;
-  const int xcd = blockIdx.x & 7, slot_in_xcd = blockIdx.x >> 3;
-  for (int64_t round = 0;; ++round) {
-    const int64_t item = round * grid + (int64_t)xcd * per_xcd + slot_in_xcd;
-    if (item >= n_items) break;
+  // Items from the per-XCD queues (as in the forward kernels); the next item is
+  // published through the first 8 bytes of the dS tile, which is free from the
+  // item's last barrier until after the next item's first sub-chunk barrier.
+  int64_t* const wg_item = reinterpret_cast<int64_t*>(dSs);
+  ItemQueue queue{ctr, n_items, (int)gridDim.x, (int)gridDim.x >> 3, (int)(blockIdx.x & 7), kItemCounterStride, 0};
+  wg_clock_start(clk);
+  if (tid == 0) publish_item(wg_item, queue.resolve(queue.take()));
+  for (;;) {
+    __syncthreads();  // the item is published; the previous item's LDS reads are done
+    const int64_t item = *wg_item;
+    if (item < 0) break;
+    int ticket = 0;
+    if (tid == 0) ticket = queue.take();  // the next item's ticket, in flight meanwhile
     const int4 it = items[item];
     const int64_t b = it.x, r = it.w;
     const int start = it.y, cnt = it.z;
     int ip[kBwdPairRegs];
 #pragma unroll
     for (int k = 0; k < kBwdPairRegs; ++k) ip[k] = pairs[start + (64 * k + lane < cnt ? 64 * k + lane : cnt - 1)];
-    __syncthreads();  // the previous item's LDS reads are done
     {
       // Threads 0..255 stage K and V rows, threads 256..511 K^T.
       int stid = tid & 255;
@@ -397,7 +404,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
         vpart[key * kDh + 64 * dh + 32 * dt + l32] = dv_acc[dt][v];
       }
     }
+    if (tid == 0) publish_item(wg_item, queue.resolve(ticket));  // read by all after the next barrier
   }
+  wg_clock_end(clk);
 }
 
 // dQ: per (query, head) the sum of its valid slots' partial rows in slot order; 16
@@ -528,7 +537,7 @@ hipError_t launch_bwd_window(const uint16_t* q, const uint16_t* k, const uint16_
                              const float* lse, const float* D, const int32_t* block_idx, int64_t N, int64_t B,
                              int bk, int H_q, int H_kv, int kk, float scale, int64_t w0, int64_t W, int num_cus,
                              float* dq, float* dk, float* dv, uint8_t* ws, const AttnWorkspace& L,
-                             hipStream_t stream) {
+                             hipStream_t stream, uint64_t* clk) {
   const int G = H_q / H_kv;
   const int bsh = bk == 64 ? 6 : 7;
   int32_t* lfirst = reinterpret_cast<int32_t*>(ws + L.lfirst);
@@ -541,6 +550,7 @@ hipError_t launch_bwd_window(const uint16_t* q, const uint16_t* k, const uint16_
   const int32_t* counts = reinterpret_cast<const int32_t*>(ws + L.counts);
   uint16_t* dq_part = reinterpret_cast<uint16_t*>(ws + L.opart);
   float* dkv_part = reinterpret_cast<float*>(ws + L.lpart);
+  int32_t* ctr = reinterpret_cast<int32_t*>(ws + L.ctr);
   int64_t grid = num_cus;
   if (grid > L.max_items) grid = L.max_items;
   grid = ((grid + 7) / 8) * 8;
@@ -550,7 +560,7 @@ hipError_t launch_bwd_window(const uint16_t* q, const uint16_t* k, const uint16_
   case GG:                                                                                                \
     bwd_kernel<GG><<<dim3((unsigned)grid), dim3(kBwdThreads), 0, stream>>>(                                \
         q, k, v, dO, lse, D, items, n_items, pairs, N, H_kv, B, bk, L.nW, kk, w0, scale, scale_log2, dq_part, \
-        dkv_part);                                                                                        \
+        dkv_part, ctr, clk);                                                                              \
     break;
     MSA_BWD_CASE(1)
     MSA_BWD_CASE(2)

@@ -22,6 +22,9 @@ thread_local char g_last_error[512] = "";
 constexpr int kMaxProfileWindows = 1024;
 thread_local hipEvent_t g_phase_events[4 * kMaxProfileWindows] = {};
 thread_local int g_phase_windows = 0;  // windows with events; 0 = hook off
+// Per-workgroup clock buffer of the persistent-grid kernels (msa_set_profile_clock).
+thread_local uint64_t* g_clock = nullptr;
+thread_local int64_t g_clock_slots = 0;
 
 msa_status_t fail(msa_status_t st, const char* fmt, ...) {
   va_list ap;
@@ -189,6 +192,9 @@ static msa_status_t check_attn_shape(int64_t N, int H_q, int H_kv, int d_h, int 
   return MSA_OK;
 }
 
+// The clock buffer when it holds 2 slots for each of up to max_wg workgroups.
+static uint64_t* clock_for(int64_t max_wg) { return g_clock && g_clock_slots >= 2 * max_wg ? g_clock : nullptr; }
+
 // Attention over N tokens with list stride B (blocks), given sequence tables si (si.cu
 // null: one sequence).  The workspace holds the sequence tables (S) and then the
 // per-window buffers.
@@ -206,7 +212,7 @@ static msa_status_t attn_run(const void* q, const void* k, const void* v, const 
     hipError_t e = msa::launch_sparse_attn_window(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), block_idx,
         N, B, si, B_k, H_q, H_kv, k_sel, scale, w0, Wn, cus, o, lse, ws + S.total, L, stream,
-        wi < g_phase_windows ? g_phase_events + 4 * wi : nullptr);
+        wi < g_phase_windows ? g_phase_events + 4 * wi : nullptr, wi == 0 ? clock_for(2 * cus + 8) : nullptr);
     if (e != hipSuccess) return hip_fail(e, "sparse_attn launch");
   }
   return ok();
@@ -465,9 +471,23 @@ msa_status_t msa_sparse_attn_bwd(const void* q, const void* k, const void* v, co
     const int64_t Wn = (N - w0 < W) ? N - w0 : W;
     e = msa::launch_bwd_window(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dO), lse, D, block_idx,
-                               N, B, B_k, H_q, H_kv, k_sel, scale, w0, Wn, cus, dq, dk, dv, w + dbytes, L, stream);
+                               N, B, B_k, H_q, H_kv, k_sel, scale, w0, Wn, cus, dq, dk, dv, w + dbytes, L, stream,
+                               w0 == 0 ? clock_for(cus + 8) : nullptr);
     if (e != hipSuccess) return hip_fail(e, "backward launch");
   }
+  return ok();
+}
+
+msa_status_t msa_set_profile_clock(uint64_t* clock, int64_t slots) {
+  if (slots == 0) {
+    g_clock = nullptr;
+    g_clock_slots = 0;
+    return ok();
+  }
+  if (slots < 0 || !clock || !aligned(clock, 8))
+    return fail(MSA_ERR_INVALID_ARG, "msa_set_profile_clock takes a device buffer of slots >= 1 uint64");
+  g_clock = clock;
+  g_clock_slots = slots;
   return ok();
 }
 

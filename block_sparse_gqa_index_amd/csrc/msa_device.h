@@ -260,6 +260,54 @@ __device__ __forceinline__ void write_selection(int (&cand)[N], int k, int b_loc
   }
 }
 
+// Dynamic item schedule of the persistent-grid kernels (the pages balance their
+// variable work with a persistent grid and a global atomic counter).  Workgroup w runs
+// on XCD w % 8.  The items of XCD x are, in order, items
+//   (t / per) * grid + x * per + t % per,   t = 0, 1, ...   (per = grid / 8),
+// runs of `per` consecutive items, mostly of one list, so that a staged K/V block is
+// re-read from that XCD's L2.  Each XCD hands its items out through its own counter
+// (ctr[x * stride], zeroed before the launch); a workgroup whose XCD has none left
+// takes the next XCD's, and so on, and stops when all eight are exhausted.  Only one
+// thread of a workgroup uses the queue.  take() issues the atomic for a ticket;
+// resolve() turns it into an item (or -1), taking more tickets past an exhausted XCD.
+struct ItemQueue {
+  int32_t* ctr;
+  int64_t n_items;
+  int grid, per, xcd, stride, off;
+  __device__ int take() { return atomicAdd(ctr + ((xcd + off) & 7) * stride, 1); }
+  __device__ int64_t resolve(int t) {
+    for (;;) {
+      const int x = (xcd + off) & 7;
+      const int64_t item = (int64_t)(t / per) * grid + (int64_t)x * per + t % per;
+      if (item < n_items) return item;
+      if (++off == 8) return -1;
+      t = take();
+    }
+  }
+};
+
+// Stores the next item into the workgroup's LDS slot and waits until the store has
+// completed (lgkmcnt(0); vmcnt and expcnt left alone), so that a barrier that follows
+// publishes it to every wave.
+__device__ __forceinline__ void publish_item(int64_t* slot, int64_t item) {
+  *slot = item;
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+}
+
+// Load-balance measurement of the persistent-grid kernels: with clk set, thread 0 of
+// every workgroup stores the constant-rate (100 MHz) clock at its start (slot 0) and,
+// after its last item, at its end (slot 1), in clk[2 * blockIdx.x + slot].  clk is a
+// kernel argument (uniform), so the check costs nothing when it is null.
+__device__ __forceinline__ void wg_clock_start(uint64_t* clk) {
+  if (clk && threadIdx.x == 0) clk[2 * blockIdx.x] = __builtin_amdgcn_s_memrealtime();
+}
+__device__ __forceinline__ void wg_clock_end(uint64_t* clk) {
+  if (clk) {
+    __syncthreads();
+    if (threadIdx.x == 0) clk[2 * blockIdx.x + 1] = __builtin_amdgcn_s_memrealtime();
+  }
+}
+
 // ---------------------------------------------------------------------------------
 // K / V block staging shared by the prefill and decode attention kernels (256
 // threads).

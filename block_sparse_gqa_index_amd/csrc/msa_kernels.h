@@ -15,11 +15,14 @@ constexpr int kBlockKeys = 128;
 // Chunks (of 128 MFMA rows) per work item of the KV-outer kernel.
 constexpr int kItemChunks = 16;
 
+// Distance (in int32) between the eight per-XCD item counters of a workspace.
+constexpr int kItemCounterStride = 64;
+
 // Floats per (query, group, slot) partial of the KL pass.
 constexpr int kKlPart = 8;
 
 struct AttnWorkspace {
-  size_t counts, tsum, cursor, n_items, items, pairs, opart, lpart, lfirst, tcount, total;
+  size_t counts, tsum, cursor, n_items, ctr, items, pairs, opart, lpart, lfirst, tcount, total;
   int64_t max_items;
   int item_q;  // queries per work item
   int64_t WQ;  // queries per q-locality window
@@ -82,7 +85,8 @@ hipError_t launch_sparse_attn_window(const uint16_t* q, const uint16_t* k, const
                                      const int32_t* block_idx, int64_t N, int64_t B, const SeqInfo& si, int bk,
                                      int H_q, int H_kv, int kk, float scale, int64_t w0, int64_t W, int num_cus,
                                      float* o, float* lse, uint8_t* ws, const AttnWorkspace& L, hipStream_t stream,
-                                     const hipEvent_t* events);  // 4 phase events or null
+                                     const hipEvent_t* events,  // 4 phase events or null
+                                     uint64_t* clk);            // per-workgroup clock of phase 1, or null
 
 // KL alignment pass over one query window (single sequence of N tokens): per
 // (query, group) kl and lse_idx.  launch_kl_loss then reduces kl [n] to its mean in
@@ -104,7 +108,7 @@ hipError_t launch_bwd_window(const uint16_t* q, const uint16_t* k, const uint16_
                              const float* lse, const float* D, const int32_t* block_idx, int64_t N, int64_t B,
                              int bk, int H_q, int H_kv, int kk, float scale, int64_t w0, int64_t W, int num_cus,
                              float* dq, float* dk, float* dv, uint8_t* ws, const AttnWorkspace& L,
-                             hipStream_t stream);
+                             hipStream_t stream, uint64_t* clk);  // per-workgroup clock, or null
 
 DecodeWorkspace decode_workspace_layout(int batch, int H_q, int H_kv, int kk, int64_t Bmax);
 hipError_t launch_decode(const uint16_t* q, const uint16_t* q_idx, const uint16_t* k_cache,

@@ -169,9 +169,11 @@ __global__ __launch_bounds__(kScanTile) void inv_scan_write_kernel(const int32_t
                                                                  int32_t* __restrict__ cursor,
                                                                  int4* __restrict__ items,
                                                                  int32_t* __restrict__ n_items,
-                                                                 int32_t* __restrict__ lfirst) {
+                                                                 int32_t* __restrict__ lfirst,
+                                                                 int32_t* __restrict__ ctr) {
   __shared__ int64_t lds[16];
   const int tile = blockIdx.x;
+  if (tile == 0 && threadIdx.x < 8) ctr[threadIdx.x * kItemCounterStride] = 0;  // the item counters
   int64_t pp = 0, ip = 0;
   for (int j = threadIdx.x; j < tile; j += kScanTile) {
     pp += tsum[2 * j];
@@ -441,7 +443,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
     const int4* __restrict__ items, const int32_t* __restrict__ n_items_ptr, const int32_t* __restrict__ pairs,
     int64_t N, SeqInfo si, int H_kv, int64_t B, int nW, int kk, int64_t w0, float scale_log2,
-    uint16_t* __restrict__ Opart, float2* __restrict__ Lpart) {
+    uint16_t* __restrict__ Opart, float2* __restrict__ Lpart, int32_t* __restrict__ ctr,
+    uint64_t* __restrict__ clk) {
   constexpr int kQC = 128 / G;         // gathered queries per chunk
   constexpr int NKT = BK / 32;         // 32-key MFMA tiles per block
   __shared__ __attribute__((aligned(16))) uint8_t Ks[kBk * 256];
@@ -454,14 +457,25 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
   const int H_q = H_kv * G;
   const int n_items = *n_items_ptr;
 
-  // Consecutive items (mostly of one list) go to the workgroups of one XCD, so the
-  // staged K/V block is read from that XCD's L2.
-  const int grid = gridDim.x;
-  const int per_xcd = grid >> 3;
-  const int xcd = blockIdx.x & 7, slot_in_xcd = blockIdx.x >> 3;
-  for (int64_t round = 0;; ++round) {
-    const int64_t item = round * grid + (int64_t)xcd * per_xcd + slot_in_xcd;
-    if (item >= n_items) break;
+  // Items come from the per-XCD queues: consecutive items (mostly of one list) go
+  // to the workgroups of one XCD, so the staged K/V block is read from its L2.
+  // The next item is published through the first 8 bytes of wave 0's staging buffer
+  // (no extra LDS: two workgroups per CU use all of it).  Thread 0 writes it after
+  // wave 0's last use of that buffer for the item; every thread reads it right after
+  // the item's first barrier, and the buffer is next written after the second.
+  // The publishing write is waited for before the barrier explicitly: the compiler
+  // emits no LDS wait ahead of the loop's first barrier, so without it another wave
+  // could read the slot before the write lands.
+  int64_t* const wg_item = reinterpret_cast<int64_t*>(&Ostage[0][0]);
+  ItemQueue queue{ctr, n_items, (int)gridDim.x, (int)gridDim.x >> 3, (int)(blockIdx.x & 7), kItemCounterStride, 0};
+  wg_clock_start(clk);
+  if (tid == 0) publish_item(wg_item, queue.resolve(queue.take()));
+  for (;;) {
+    __syncthreads();  // the item is published; the previous item's LDS reads are done
+    const int64_t item = *wg_item;
+    if (item < 0) break;
+    int ticket = 0;
+    if (tid == 0) ticket = queue.take();  // the next item's ticket, in flight meanwhile
     const int4 it = items[item];
     const int64_t gb = it.x, r = it.w;
     const int start = it.y, cnt = it.z;
@@ -475,7 +489,6 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
     int ip[NR];
 #pragma unroll
     for (int k = 0; k < NR; ++k) ip[k] = pairs[start + (64 * k + lane < cnt ? 64 * k + lane : cnt - 1)];
-    __syncthreads();  // previous item's LDS reads are done
     {
       // Recompute the staging addresses per item rather than keeping ~40 loop-
       // invariant address registers live across the whole kernel.
@@ -711,7 +724,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
       for (int t = 0; t < 8; ++t) prs[t] = prs_n[t];
 
     }
+    if (tid == 0) publish_item(wg_item, queue.resolve(ticket));  // read by all after the next barrier
   }
+  wg_clock_end(clk);
 }
 
 // --------------------------------------------------------------------- phase 2
@@ -940,14 +955,14 @@ struct KlRows {
 // KlRows<G>::NQ queries (16 at G = 1) and the next chunk's operands in flight, which
 // leaves the compiler little slack at two workgroups per CU.  Per variant, chosen
 // from the compiler's resource-usage report so that none spills registers:
-//  - G = 1, and G = 2 with 64-key blocks, run one workgroup per CU (their running
-//    sums do not fit the 256 registers of two);
-//  - G = 4 with 128-key blocks walks its four key tiles in a loop rather than
-//    unrolled (the unrolled form spills at two workgroups per CU).
+//  - G <= 2 runs one workgroup per CU (its running sums do not fit the 256
+//    registers of two);
+//  - G = 4 and G = 8 with 128-key blocks walk their four key tiles in a loop rather
+//    than unrolled (the unrolled form spills at two workgroups per CU).
 template <int G, int BK>
 struct KlRegs {
-  static constexpr int kBlocksPerCU = (G == 1 || (G == 2 && BK == 64)) ? 1 : 2;
-  static constexpr int kTileUnroll = (G == 4 && BK == 128) ? 1 : BK / 32;
+  static constexpr int kBlocksPerCU = G <= 2 ? 1 : 2;
+  static constexpr int kTileUnroll = ((G == 4 || G == 8) && BK == 128) ? 1 : BK / 32;
 };
 
 // BK: keys per block (64 or 128); a 64-key block fills the first half of the
@@ -957,7 +972,7 @@ __global__ __launch_bounds__(kAttnThreads, (KlRegs<G, BK>::kBlocksPerCU)) void k
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp, const uint16_t* __restrict__ q_idx,
     const uint16_t* __restrict__ k_idx, const float* __restrict__ lse, const int4* __restrict__ items,
     const int32_t* __restrict__ n_items_ptr, const int32_t* __restrict__ pairs, int64_t N, int H_kv, int64_t B,
-    int nW, int kk, int64_t w0, float scale_log2, float* __restrict__ part) {
+    int nW, int kk, int64_t w0, float scale_log2, float* __restrict__ part, int32_t* __restrict__ ctr) {
   constexpr int kQC = 128 / G;
   constexpr int GL = KlRows<G>::GL, NQ = KlRows<G>::NQ;
   static_assert(G <= 32, "a query's heads must lie in one wave");
@@ -970,12 +985,18 @@ __global__ __launch_bounds__(kAttnThreads, (KlRegs<G, BK>::kBlocksPerCU)) void k
   const int h = lane >> 5, l32 = lane & 31;
   const int H_q = H_kv * G;
   const int n_items = *n_items_ptr;
-  const int grid = gridDim.x;
-  const int per_xcd = grid >> 3;
-  const int xcd = blockIdx.x & 7, slot_in_xcd = blockIdx.x >> 3;
-  for (int64_t round = 0;; ++round) {
-    const int64_t item = round * grid + (int64_t)xcd * per_xcd + slot_in_xcd;
-    if (item >= n_items) break;
+  // Items from the per-XCD queues, as in the attention kernel; the next item is
+  // published through the first 8 bytes of wave 0's q rows, which are next written
+  // after the item's second barrier.
+  int64_t* const wg_item = reinterpret_cast<int64_t*>(&Qs[0][0]);
+  ItemQueue queue{ctr, n_items, (int)gridDim.x, (int)gridDim.x >> 3, (int)(blockIdx.x & 7), kItemCounterStride, 0};
+  if (tid == 0) publish_item(wg_item, queue.resolve(queue.take()));
+  for (;;) {
+    __syncthreads();  // the item is published; the previous item's LDS reads are done
+    const int64_t item = *wg_item;
+    if (item < 0) break;
+    int ticket = 0;
+    if (tid == 0) ticket = queue.take();  // the next item's ticket, in flight meanwhile
     const int4 it = items[item];
     const int64_t b = it.x, r = it.w;
     const int start = it.y, cnt = it.z;
@@ -984,7 +1005,6 @@ __global__ __launch_bounds__(kAttnThreads, (KlRegs<G, BK>::kBlocksPerCU)) void k
     int ip[NR];
 #pragma unroll
     for (int k = 0; k < NR; ++k) ip[k] = pairs[start + (64 * k + lane < cnt ? 64 * k + lane : cnt - 1)];
-    __syncthreads();  // previous item's LDS reads are done
     {
       int stid = tid;
       asm volatile("" : "+v"(stid));
@@ -1155,6 +1175,7 @@ __global__ __launch_bounds__(kAttnThreads, (KlRegs<G, BK>::kBlocksPerCU)) void k
 #pragma unroll
       for (int t = 0; t < 4; ++t) qi_op[t] = qi_n[t];
     }
+    if (tid == 0) publish_item(wg_item, queue.resolve(ticket));  // read by all after the next barrier
   }
 }
 
@@ -1296,6 +1317,7 @@ AttnWorkspace attn_workspace_layout(int64_t W, int H_q, int H_kv, int kk, int64_
   L.tsum = take(sizeof(int64_t) * 2 * ((lists + kScanTile - 1) / kScanTile));
   L.cursor = take(sizeof(int32_t) * lists);
   L.n_items = take(sizeof(int32_t) * 4);
+  L.ctr = take(sizeof(int32_t) * kItemCounterStride * 8);
   L.items = take(sizeof(int4) * max_items);
   L.pairs = take(sizeof(int32_t) * max_pairs);
   if (parts == kPartsKl) {
@@ -1352,7 +1374,8 @@ hipError_t launch_inverse_index(const int32_t* block_idx, int64_t B, const SeqIn
   inv_tile_sums_kernel<<<dim3(tiles), dim3(kScanTile), 0, stream>>>(counts, lists, L.item_q, tsum);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   inv_scan_write_kernel<<<dim3(tiles), dim3(kScanTile), 0, stream>>>(counts, lists, B, L.nW, L.item_q, tsum, cursor,
-                                                                    items, n_items, lfirst);
+                                                                    items, n_items, lfirst,
+                                                                    reinterpret_cast<int32_t*>(ws + L.ctr));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ordered) {
     inv_tile_base_kernel<<<dim3((unsigned)((lists + 255) / 256)), dim3(256), 0, stream>>>(
@@ -1371,7 +1394,7 @@ hipError_t launch_sparse_attn_window(const uint16_t* q, const uint16_t* k, const
                                      const int32_t* block_idx, int64_t N, int64_t B, const SeqInfo& si, int bk,
                                      int H_q, int H_kv, int kk, float scale, int64_t w0, int64_t W, int num_cus,
                                      float* o, float* lse, uint8_t* ws, const AttnWorkspace& L, hipStream_t stream,
-                                     const hipEvent_t* events) {
+                                     const hipEvent_t* events, uint64_t* clk) {
   const int bsh = bk == 64 ? 6 : 7;
   const int G = H_q / H_kv;
   const int32_t* n_items = reinterpret_cast<const int32_t*>(ws + L.n_items);
@@ -1388,16 +1411,17 @@ hipError_t launch_sparse_attn_window(const uint16_t* q, const uint16_t* k, const
   if (grid > L.max_items) grid = L.max_items;
   grid = ((grid + 7) / 8) * 8;
   const float scale_log2 = scale * kLog2e;
+  int32_t* ctr = reinterpret_cast<int32_t*>(ws + L.ctr);
   if (events && (e = hipEventRecord(events[1], stream)) != hipSuccess) return e;
   switch (G) {
 #define MSA_ATTN_CASE(GG)                                                                            \
   case GG:                                                                                           \
     if (bk == 64)                                                                                    \
       attn_kvouter_kernel<GG, 64><<<dim3((unsigned)grid), dim3(kAttnThreads), 0, stream>>>(          \
-          q, k, v, items, n_items, pairs, N, si, H_kv, B, L.nW, kk, w0, scale_log2, opart, lpart);   \
+          q, k, v, items, n_items, pairs, N, si, H_kv, B, L.nW, kk, w0, scale_log2, opart, lpart, ctr, clk);\
     else                                                                                             \
       attn_kvouter_kernel<GG, 128><<<dim3((unsigned)grid), dim3(kAttnThreads), 0, stream>>>(         \
-          q, k, v, items, n_items, pairs, N, si, H_kv, B, L.nW, kk, w0, scale_log2, opart, lpart);   \
+          q, k, v, items, n_items, pairs, N, si, H_kv, B, L.nW, kk, w0, scale_log2, opart, lpart, ctr, clk);\
     break;
     MSA_ATTN_CASE(1)
     MSA_ATTN_CASE(2)
@@ -1462,6 +1486,7 @@ hipError_t launch_sparse_kl_window(const uint16_t* q, const uint16_t* k, const u
   const int4* items = reinterpret_cast<const int4*>(ws + L.items);
   const int32_t* pairs = reinterpret_cast<const int32_t*>(ws + L.pairs);
   float* part = reinterpret_cast<float*>(ws + L.opart);
+  int32_t* ctr = reinterpret_cast<int32_t*>(ws + L.ctr);
   int64_t grid = (int64_t)num_cus * 2;
   if (grid > L.max_items) grid = L.max_items;
   grid = ((grid + 7) / 8) * 8;
@@ -1471,10 +1496,10 @@ hipError_t launch_sparse_kl_window(const uint16_t* q, const uint16_t* k, const u
   case GG:                                                                                                 \
     if (bk == 64)                                                                                          \
       kl_pair_kernel<GG, 64><<<dim3((unsigned)grid), dim3(kAttnThreads), 0, stream>>>(                     \
-          q, k, q_idx, k_idx, lse, items, n_items, pairs, N, H_kv, B, L.nW, kk, w0, scale_log2, part);     \
+          q, k, q_idx, k_idx, lse, items, n_items, pairs, N, H_kv, B, L.nW, kk, w0, scale_log2, part, ctr);\
     else                                                                                                   \
       kl_pair_kernel<GG, 128><<<dim3((unsigned)grid), dim3(kAttnThreads), 0, stream>>>(                    \
-          q, k, q_idx, k_idx, lse, items, n_items, pairs, N, H_kv, B, L.nW, kk, w0, scale_log2, part);     \
+          q, k, q_idx, k_idx, lse, items, n_items, pairs, N, H_kv, B, L.nW, kk, w0, scale_log2, part, ctr);\
     break;
     MSA_KL_CASE(1)
     MSA_KL_CASE(2)

@@ -314,6 +314,21 @@ msa_status_t msa_topk_from_scores(const float* M, int64_t N, int H_kv, int64_t B
  * is kept).  Host-only; no device work. */
 msa_status_t msa_set_profile_events(void* const* events, int n);
 
+/* msa_set_profile_clock — measurement hook for the load balance of the persistent-grid
+ * kernels (the pages balance variable work with a persistent grid: paper review page,
+ * section 4; here a static item order stands in for their atomic counter).  While set,
+ * the KV-outer phase-1 kernel of the first query window of every later
+ * msa_sparse_attn_fwd / _varlen call on this host thread, and the main kernel of the
+ * first query window of every later msa_sparse_attn_bwd call, store for each workgroup
+ * w the GPU's constant-rate clock (100 MHz) at its start in clock[2w] and after its
+ * last item in clock[2w + 1].  A launch whose grid needs more than `slots` entries
+ * (at most 2 * (2 * CUs + 8)) records nothing.
+ *   clock  device buffer of `slots` uint64, owned by the caller, valid while set.
+ *   slots  its length; 0 clears the hook (clock is then ignored).
+ * Returns MSA_ERR_INVALID_ARG for a negative size or a null / misaligned buffer.
+ * Host-only; no device work. */
+msa_status_t msa_set_profile_clock(uint64_t* clock, int64_t slots);
+
 #ifdef __cplusplus
 }
 #endif

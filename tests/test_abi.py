@@ -123,6 +123,14 @@ def test_decode_rejects_bad_arguments(lib):
     assert call(batch=0) == lib.MSA_OK
 
 
+def test_profile_clock_hook_validates(lib):
+    raw = lib.raw()
+    assert raw.msa_set_profile_clock(None, 4) == lib.MSA_ERR_INVALID_ARG
+    assert raw.msa_set_profile_clock(0x10004, 4) == lib.MSA_ERR_INVALID_ARG  # not 8-byte aligned
+    assert raw.msa_set_profile_clock(0x10000, -2) == lib.MSA_ERR_INVALID_ARG
+    assert raw.msa_set_profile_clock(None, 0) == lib.MSA_OK
+
+
 def test_profile_events_hook_validates(lib):
     raw = lib.raw()
     assert raw.msa_set_profile_events(None, 3) == lib.MSA_ERR_INVALID_ARG
