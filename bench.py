@@ -563,7 +563,33 @@ def run_kl(msa, inp, cfg, block_idx, lse, slot_pairs, lists, pairs, steps):
     flops = 2 * cfg.d_h * pairs + 2 * cfg.d_idx * (pairs // G)
     out = {"ms": round(ms, 4), "algorithmic_bytes": nbytes, "GB_s": round(nbytes / (ms / 1e3) / 1e9, 1),
            "tflops": round(flops / (ms / 1e3) / 1e12, 2), "loss": round(float(loss.item()), 6), "steps": steps}
-    del kws, kl, lse_idx, loss
+    del kws, kl, loss
+    # LSE_idx emitted by the forward (msa_sparse_attn_fwd_lse_idx): its cost over the
+    # plain forward, both timed here on the same inputs and workspace.
+    torch.cuda.empty_cache()
+    ws = torch.empty(msa.msa_sparse_attn_fwd_workspace(N, H_q, H_kv, k, B_k=B_k), dtype=torch.uint8, device=dev)
+    o = torch.empty((N, H_q, cfg.d_h), dtype=torch.float32, device=dev)
+    lse2 = torch.empty((N, H_q), dtype=torch.float32, device=dev)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    t_plain = timed(lambda: msa.msa_sparse_attn_fwd(inp.q, inp.k, inp.v, block_idx, B_k=B_k, o=o, lse=lse2,
+                                                    workspace=ws))
+    t_li = timed(lambda: msa.msa_sparse_attn_fwd_lse_idx(inp.q, inp.k, inp.v, inp.q_idx, inp.k_idx, block_idx,
+                                                         B_k=B_k, o=o, lse=lse2, lse_idx=lse_idx, workspace=ws))
+    out["forward_ms"] = round(t_plain, 4)
+    out["forward_with_lse_idx_ms"] = round(t_li, 4)
+    out["lse_idx_emission_ms"] = round(t_li - t_plain, 4)
+    del ws, o, lse2, lse_idx
     return out
 
 

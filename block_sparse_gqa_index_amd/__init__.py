@@ -37,6 +37,8 @@ _SIGS = {
     "msa_sparse_attn_fwd_workspace_min": ([_I64, _I32, _I32, _I32, _I32, _I32], _SZ),
     "msa_sparse_attn_fwd_windows": ([_I64, _I32, _I32, _I32, _I32, _I32, _SZ], _I64),
     "msa_sparse_attn_fwd": ([_P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _F32, _P, _P, _P, _SZ, _P], _I32),
+    "msa_sparse_attn_fwd_lse_idx": ([_P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _F32, _P, _P,
+                                     _P, _P, _SZ, _P], _I32),
     "msa_decode_workspace": ([_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I64], _SZ),
     "msa_decode": ([_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _F32, _P, _P, _P, _P,
                     _SZ, _P], _I32),
@@ -194,6 +196,42 @@ def msa_sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block
                                     float(scale), _ptr(o), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
                                     _stream(stream)), "msa_sparse_attn_fwd")
     return o, lse
+
+
+def msa_sparse_attn_fwd_lse_idx(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_idx: torch.Tensor,
+                                k_idx: torch.Tensor, block_idx: torch.Tensor, B_k: int = 128,
+                                scale: float | None = None, o: torch.Tensor | None = None,
+                                lse: torch.Tensor | None = None, lse_idx: torch.Tensor | None = None,
+                                workspace: torch.Tensor | None = None, stream=None):
+    """msa_sparse_attn_fwd that also emits LSE_idx [N, H_kv] (the index distribution's
+    log partition over each row's selected tokens).  Returns (o, lse, lse_idx)."""
+    N, H_q, d_h = q.shape
+    H_kv = k.shape[1]
+    kk = block_idx.shape[2]
+    d_idx = q_idx.shape[2]
+    _need(q, "q", torch.bfloat16, (N, H_q, d_h))
+    _need(k, "k", torch.bfloat16, (N, H_kv, d_h))
+    _need(v, "v", torch.bfloat16, (N, H_kv, d_h))
+    _need(q_idx, "q_idx", torch.bfloat16, (N, H_kv, d_idx))
+    _need(k_idx, "k_idx", torch.bfloat16, (N, d_idx))
+    _need(block_idx, "block_idx", torch.int32, (N, H_kv, kk))
+    if scale is None:
+        scale = d_h ** -0.5
+    if o is None:
+        o = torch.empty((N, H_q, d_h), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((N, H_q), dtype=torch.float32, device=q.device)
+    if lse_idx is None:
+        lse_idx = torch.empty((N, H_kv), dtype=torch.float32, device=q.device)
+    _need(o, "o", torch.float32, (N, H_q, d_h))
+    _need(lse, "lse", torch.float32, (N, H_q))
+    _need(lse_idx, "lse_idx", torch.float32, (N, H_kv))
+    ws = _ws(_lib.msa_sparse_attn_fwd_workspace(N, H_q, H_kv, d_h, B_k, kk), q.device, workspace)
+    _check(_lib.msa_sparse_attn_fwd_lse_idx(_ptr(q), _ptr(k), _ptr(v), _ptr(q_idx), _ptr(k_idx), _ptr(block_idx), N,
+                                            H_q, H_kv, d_h, d_idx, B_k, kk, float(scale), _ptr(o), _ptr(lse),
+                                            _ptr(lse_idx), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "msa_sparse_attn_fwd_lse_idx")
+    return o, lse, lse_idx
 
 
 # ----------------------------------------------------------------- Backward

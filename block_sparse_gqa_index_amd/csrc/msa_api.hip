@@ -201,7 +201,8 @@ static uint64_t* clock_for(int64_t max_wg) { return g_clock && g_clock_slots >= 
 static msa_status_t attn_run(const void* q, const void* k, const void* v, const int32_t* block_idx, int64_t N,
                              int64_t B, const msa::SeqInfo& si, const msa::SeqTables& S, int B_k, int H_q, int H_kv,
                              int k_sel, float scale, float* o, float* lse, uint8_t* ws, size_t ws_bytes,
-                             hipStream_t stream) {
+                             hipStream_t stream, const void* q_idx = nullptr, const void* k_idx = nullptr,
+                             float* lse_idx = nullptr) {
   const size_t avail = ws_bytes - S.total;
   const int64_t W = window_for_bytes(N, B, H_q, H_kv, k_sel, avail);
   const msa::AttnWorkspace L = msa::attn_workspace_layout(W, H_q, H_kv, k_sel, B);
@@ -212,7 +213,8 @@ static msa_status_t attn_run(const void* q, const void* k, const void* v, const 
     hipError_t e = msa::launch_sparse_attn_window(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), block_idx,
         N, B, si, B_k, H_q, H_kv, k_sel, scale, w0, Wn, cus, o, lse, ws + S.total, L, stream,
-        wi < g_phase_windows ? g_phase_events + 4 * wi : nullptr, wi == 0 ? clock_for(2 * cus + 8) : nullptr);
+        wi < g_phase_windows ? g_phase_events + 4 * wi : nullptr, wi == 0 ? clock_for(2 * cus + 8) : nullptr,
+        static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx), lse_idx);
     if (e != hipSuccess) return hip_fail(e, "sparse_attn launch");
   }
   return ok();
@@ -267,6 +269,28 @@ msa_status_t msa_sparse_attn_fwd(const void* q, const void* k, const void* v, co
   if (!aligned(ws, 256)) return fail(MSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   return attn_run(q, k, v, block_idx, N, (N + B_k - 1) / B_k, msa::SeqInfo{}, msa::SeqTables{}, B_k, H_q, H_kv, k_sel,
                   scale, o, lse, static_cast<uint8_t*>(ws), ws_bytes, static_cast<hipStream_t>(hip_stream));
+}
+
+msa_status_t msa_sparse_attn_fwd_lse_idx(const void* q, const void* k, const void* v, const void* q_idx,
+                                         const void* k_idx, const int32_t* block_idx, int64_t N, int H_q, int H_kv,
+                                         int d_h, int d_idx, int B_k, int k_sel, float scale, float* o, float* lse,
+                                         float* lse_idx, void* ws, size_t ws_bytes, void* hip_stream) {
+  msa_status_t st = check_attn_shape(N, H_q, H_kv, d_h, B_k, k_sel);
+  if (st != MSA_OK) return st;
+  if (d_idx != msa::kIndexDim) return fail(MSA_ERR_UNSUPPORTED, "d_idx must be %d (got %d)", msa::kIndexDim, d_idx);
+  if (!(scale > 0.f) || scale != scale) return fail(MSA_ERR_INVALID_ARG, "scale must be a positive number");
+  if (N == 0) return ok();
+  if ((st = check_attn_ptrs(q, k, v, block_idx, o, lse, scale)) != MSA_OK) return st;
+  if (!q_idx || !k_idx || !lse_idx) return fail(MSA_ERR_INVALID_ARG, "null pointer");
+  if (!aligned(q_idx, 16) || !aligned(k_idx, 16) || !aligned(lse_idx, 4))
+    return fail(MSA_ERR_INVALID_ARG, "misaligned pointer (q_idx/k_idx need 16 B)");
+  const size_t need = msa_sparse_attn_fwd_workspace_min(N, H_q, H_kv, d_h, B_k, k_sel);
+  if (!ws || ws_bytes < need)
+    return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes is below the minimum %zu", ws ? ws_bytes : 0, need);
+  if (!aligned(ws, 256)) return fail(MSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  return attn_run(q, k, v, block_idx, N, (N + B_k - 1) / B_k, msa::SeqInfo{}, msa::SeqTables{}, B_k, H_q, H_kv, k_sel,
+                  scale, o, lse, static_cast<uint8_t*>(ws), ws_bytes, static_cast<hipStream_t>(hip_stream), q_idx,
+                  k_idx, lse_idx);
 }
 
 // ---------------------------------------------------------------- packed sequences

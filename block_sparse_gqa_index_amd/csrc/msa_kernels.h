@@ -15,14 +15,16 @@ constexpr int kBlockKeys = 128;
 // Chunks (of 128 MFMA rows) per work item of the KV-outer kernel.
 constexpr int kItemChunks = 16;
 
-// Distance (in int32) between the eight per-XCD item counters of a workspace.
+// Distance (in int32) between the per-XCD item counters of a workspace; a workspace
+// holds kItemCounterSets sets of eight (one per persistent launch over its items).
 constexpr int kItemCounterStride = 64;
+constexpr int kItemCounterSets = 2;
 
 // Floats per (query, group, slot) partial of the KL pass.
 constexpr int kKlPart = 8;
 
 struct AttnWorkspace {
-  size_t counts, tsum, cursor, n_items, ctr, items, pairs, opart, lpart, lfirst, tcount, total;
+  size_t counts, tsum, cursor, n_items, ctr, items, pairs, opart, lpart, lidx, lfirst, tcount, total;
   int64_t max_items;
   int item_q;  // queries per work item
   int64_t WQ;  // queries per q-locality window
@@ -86,7 +88,9 @@ hipError_t launch_sparse_attn_window(const uint16_t* q, const uint16_t* k, const
                                      int H_q, int H_kv, int kk, float scale, int64_t w0, int64_t W, int num_cus,
                                      float* o, float* lse, uint8_t* ws, const AttnWorkspace& L, hipStream_t stream,
                                      const hipEvent_t* events,  // 4 phase events or null
-                                     uint64_t* clk);            // per-workgroup clock of phase 1, or null
+                                     uint64_t* clk,             // per-workgroup clock of phase 1, or null
+                                     const uint16_t* q_idx = nullptr, const uint16_t* k_idx = nullptr,
+                                     float* lse_idx = nullptr);  // LSE_idx [N, H_kv] when set
 
 // KL alignment pass over one query window (single sequence of N tokens): per
 // (query, group) kl and lse_idx.  launch_kl_loss then reduces kl [n] to its mean in

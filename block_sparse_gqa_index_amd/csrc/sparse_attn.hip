@@ -173,7 +173,7 @@ __global__ __launch_bounds__(kScanTile) void inv_scan_write_kernel(const int32_t
                                                                  int32_t* __restrict__ ctr) {
   __shared__ int64_t lds[16];
   const int tile = blockIdx.x;
-  if (tile == 0 && threadIdx.x < 8) ctr[threadIdx.x * kItemCounterStride] = 0;  // the item counters
+  if (tile == 0 && threadIdx.x < 8 * kItemCounterSets) ctr[threadIdx.x * kItemCounterStride] = 0;  // item counters
   int64_t pp = 0, ip = 0;
   for (int j = threadIdx.x; j < tile; j += kScanTile) {
     pp += tsum[2 * j];
@@ -1246,6 +1246,132 @@ __global__ __launch_bounds__(256) void kl_mean_kernel(const double* __restrict__
   if (threadIdx.x == 0) loss[0] = (float)(red[0] / (double)n);
 }
 
+// --------------------------------------------------------------------- LSE_idx
+// The index distribution's log partition over the selected tokens (Eq. 9's P^idx
+// normaliser), emitted with the forward as the pages' main pass emits it (paper
+// review, section 5, 4.3): LSE_idx[i][r] = ln sum over the tokens j <= i of the
+// row's selected blocks of exp(S_j), S_j = <q_idx[i][r], k_idx[j]> / sqrt(d_idx).
+// It walks the main pass's lists (items of one (group, block)), so each index-key
+// block is staged once per list; per (query, group, slot) pair it writes the
+// block's base-2 max and sum, and lse_idx_combine_kernel merges a row's slots.
+//
+// Per item: the block's index keys go to LDS in the staged key order (stage_kidx);
+// the pairs are taken 128 at a time, wave w's lanes l32 owning pair 32w + l32 (both
+// lane halves).  S^T = K_idx . q_idx^T on 32x32x16 MFMAs puts 16 keys of the pair
+// in each lane (element v of tile kt is key kt*32 + 16(v/8) + 4((v/4)%2) + v%4 + 8h,
+// as in phase 1), so the max and the sum over keys are in-lane, then across the
+// two lane halves.  The q_idx row of the pair is the B operand (k-slot (h, e) of
+// step t is dim 32h + 8t + e, matching chunk 4h + t of the staged key rows).
+template <int BK>
+__global__ __launch_bounds__(256) void lse_idx_pair_kernel(
+    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, const int4* __restrict__ items,
+    const int32_t* __restrict__ n_items_ptr, const int32_t* __restrict__ pairs, int64_t N, SeqInfo si, int H_kv,
+    int kk, int64_t w0, float2* __restrict__ lidx, int32_t* __restrict__ ctr) {
+  constexpr int NKT = BK / 32;
+  constexpr float kScale2 = 0.125f * kLog2e;  // 1 / sqrt(64), base 2
+  __shared__ __attribute__((aligned(16))) uint8_t KIs[kBk * 128];
+  __shared__ int64_t wg_item;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int n_items = *n_items_ptr;
+  ItemQueue queue{ctr, n_items, (int)gridDim.x, (int)gridDim.x >> 3, (int)(blockIdx.x & 7), kItemCounterStride, 0};
+  if (tid == 0) publish_item(&wg_item, queue.resolve(queue.take()));
+  for (;;) {
+    __syncthreads();  // the item is published; the previous item's LDS reads are done
+    const int64_t item = wg_item;
+    if (item < 0) break;
+    int ticket = 0;
+    if (tid == 0) ticket = queue.take();
+    const int4 it = items[item];
+    const int64_t gb = it.x, r = it.w;
+    const int start = it.y, cnt = it.z;
+    const int s_item = si.cu ? si.seq_blk[gb] : 0;
+    const int64_t b = gb - (si.cu ? si.bstart[s_item] : 0);
+    const int64_t j0 = si.cu ? si.cu[s_item] : 0;
+    const int64_t seqN = si.cu ? si.cu[s_item + 1] - j0 : N;
+    const int64_t tok0 = b * BK;
+    const int nvalid = (seqN - tok0 < BK) ? (int)(seqN - tok0) : BK;
+    stage_kidx(k_idx + (j0 + tok0) * kDidx, nvalid, KIs, tid);
+    __syncthreads();
+
+    const uint8_t* ki_row = KIs + l32 * 128;
+    const int ki_sw = (l32 >> 1) & 7;
+    for (int p0 = 0; p0 < cnt; p0 += 128) {
+      const int pi = p0 + wave * 32 + l32;
+      const int pr = pairs[start + (pi < cnt ? pi : cnt - 1)];
+      const int64_t i_local = pr >> 5;
+      const int64_t i = w0 + i_local;  // global row
+      const uint16_t* src = q_idx + (i * H_kv + r) * kDidx + 32 * h;
+      u32x4_t qb[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) qb[t] = *reinterpret_cast<const u32x4_t*>(src + 8 * t);
+      // Causal limit of this lane's keys: key kt*32 + off + 8h is visible iff off <= lim.
+      const int lim = (int)(i - j0 - tok0) - 8 * h;
+      float m = -__builtin_inff(), l = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) {
+        f32x16_t acc = f32x16_t{};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(ki_row + kt * 32 * 128 + (((4 * h + t) ^ ki_sw) << 4));
+          acc = mfma_32x32x16(as_bf16x8(a), as_bf16x8(qb[t]), acc);
+        }
+        float sv[16];
+        float tm = -__builtin_inff();
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int off = kt * 32 + 16 * (v >> 3) + 4 * ((v >> 2) & 1) + (v & 3);
+          sv[v] = off <= lim ? acc[v] * kScale2 : -__builtin_inff();
+          tm = fmaxf(tm, sv[v]);
+        }
+        const float nm = fmaxf(m, tm);
+        if (nm != -__builtin_inff()) {
+          float add = 0.f;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) add += __builtin_amdgcn_exp2f(sv[v] - nm);
+          l = l * __builtin_amdgcn_exp2f(m - nm) + add;
+          m = nm;
+        }
+      }
+      // The other lane half holds the pair's other keys.
+      const float mo = __shfl_xor(m, 32), lo = __shfl_xor(l, 32);
+      const float M = fmaxf(m, mo);
+      const float L = (m == -__builtin_inff() ? 0.f : l * __builtin_amdgcn_exp2f(m - M)) +
+                      (mo == -__builtin_inff() ? 0.f : lo * __builtin_amdgcn_exp2f(mo - M));
+      if (h == 0 && pi < cnt) lidx[(i_local * H_kv + r) * kk + (pr & 31)] = make_float2(M, L);
+    }
+    if (tid == 0) publish_item(&wg_item, queue.resolve(ticket));
+  }
+}
+
+// LSE_idx[i][r] from the row's valid slots (same validity rule as the combine):
+// ln of sum_s 2^m_s l_s; -inf when no slot is valid.  One thread per (query, group).
+__global__ __launch_bounds__(256) void lse_idx_combine_kernel(const float2* __restrict__ lidx,
+                                                              const int32_t* __restrict__ block_idx, SeqInfo si,
+                                                              int bsh, int64_t w0, int64_t W, int H_kv, int kk,
+                                                              float* __restrict__ lse_idx) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (i_local, r)
+  if (t >= W * H_kv) return;
+  const int64_t i = w0 + t / H_kv;
+  int s_seq;
+  const int64_t i_rel = i - seq_start(si, i, s_seq);
+  const int32_t* sel = block_idx + (i * H_kv + t % H_kv) * kk;
+  float M = -__builtin_inff(), L = 0.f;
+  for (int s = 0; s < kk; ++s) {
+    if (!pair_valid(sel[s], i_rel, bsh)) continue;
+    const float2 ml = lidx[t * kk + s];
+    if (ml.x == -__builtin_inff()) continue;
+    if (ml.x > M) {
+      L = L * __builtin_amdgcn_exp2f(M - ml.x) + ml.y;
+      M = ml.x;
+    } else {
+      L += ml.y * __builtin_amdgcn_exp2f(ml.x - M);
+    }
+  }
+  lse_idx[i * H_kv + t % H_kv] = M == -__builtin_inff() ? -__builtin_inff() : (M + __log2f(L)) * kLn2;
+}
+
 __global__ void fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t val) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += stride) p[e] = val;
@@ -1317,7 +1443,7 @@ AttnWorkspace attn_workspace_layout(int64_t W, int H_q, int H_kv, int kk, int64_
   L.tsum = take(sizeof(int64_t) * 2 * ((lists + kScanTile - 1) / kScanTile));
   L.cursor = take(sizeof(int32_t) * lists);
   L.n_items = take(sizeof(int32_t) * 4);
-  L.ctr = take(sizeof(int32_t) * kItemCounterStride * 8);
+  L.ctr = take(sizeof(int32_t) * kItemCounterStride * 8 * kItemCounterSets);
   L.items = take(sizeof(int4) * max_items);
   L.pairs = take(sizeof(int32_t) * max_pairs);
   if (parts == kPartsKl) {
@@ -1330,6 +1456,7 @@ AttnWorkspace attn_workspace_layout(int64_t W, int H_q, int H_kv, int kk, int64_
     L.opart = take(sizeof(uint16_t) * max_pairs * G * kDh);
     L.lpart = take(sizeof(float2) * max_pairs * G);
   }
+  L.lidx = take(parts == kPartsAttn ? sizeof(float2) * max_pairs : 0);  // LSE_idx per pair
   L.lfirst = take(parts == kPartsBwd ? sizeof(int32_t) * lists : 0);
   // Per-tile list counts (then bases) of the ordered placement: tiles x H_kv x B.
   const int64_t tq = inv_tile_queries(kk);
@@ -1394,7 +1521,8 @@ hipError_t launch_sparse_attn_window(const uint16_t* q, const uint16_t* k, const
                                      const int32_t* block_idx, int64_t N, int64_t B, const SeqInfo& si, int bk,
                                      int H_q, int H_kv, int kk, float scale, int64_t w0, int64_t W, int num_cus,
                                      float* o, float* lse, uint8_t* ws, const AttnWorkspace& L, hipStream_t stream,
-                                     const hipEvent_t* events, uint64_t* clk) {
+                                     const hipEvent_t* events, uint64_t* clk, const uint16_t* q_idx,
+                                     const uint16_t* k_idx, float* lse_idx) {
   const int bsh = bk == 64 ? 6 : 7;
   const int G = H_q / H_kv;
   const int32_t* n_items = reinterpret_cast<const int32_t*>(ws + L.n_items);
@@ -1470,7 +1598,24 @@ hipError_t launch_sparse_attn_window(const uint16_t* q, const uint16_t* k, const
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (events && (e = hipEventRecord(events[3], stream)) != hipSuccess) return e;
-  return hipSuccess;
+  if (!lse_idx) return hipSuccess;
+  // LSE_idx over the same lists (after the events, so that the phase times above
+  // stay those of the plain forward).
+  float2* lidx = reinterpret_cast<float2*>(ws + L.lidx);
+  int32_t* ctr1 = ctr + 8 * kItemCounterStride;  // the second counter set
+  int64_t lgrid = (int64_t)num_cus * 4;
+  if (lgrid > L.max_items) lgrid = L.max_items;
+  lgrid = ((lgrid + 7) / 8) * 8;
+  if (bk == 64)
+    lse_idx_pair_kernel<64><<<dim3((unsigned)lgrid), dim3(256), 0, stream>>>(q_idx, k_idx, items, n_items, pairs, N,
+                                                                             si, H_kv, kk, w0, lidx, ctr1);
+  else
+    lse_idx_pair_kernel<128><<<dim3((unsigned)lgrid), dim3(256), 0, stream>>>(q_idx, k_idx, items, n_items, pairs, N,
+                                                                              si, H_kv, kk, w0, lidx, ctr1);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  lse_idx_combine_kernel<<<dim3((unsigned)((W * H_kv + 255) / 256)), dim3(256), 0, stream>>>(
+      lidx, block_idx, si, bsh, w0, W, H_kv, kk, lse_idx);
+  return hipGetLastError();
 }
 
 hipError_t launch_sparse_kl_window(const uint16_t* q, const uint16_t* k, const uint16_t* q_idx,

@@ -99,6 +99,25 @@ msa_status_t msa_sparse_attn_fwd(const void* q, const void* k, const void* v,
                                  int B_k, int k_sel, float scale, float* o, float* lse, void* ws,
                                  size_t ws_bytes, void* hip_stream);
 
+/* msa_sparse_attn_fwd_lse_idx — msa_sparse_attn_fwd that also emits LSE_idx, the log
+ * partition of the index distribution over each row's selected tokens (Eq. 9's
+ * P^idx; the paper review page, section 5, 4.3, has the main pass emit such LSE
+ * scalars so that the KL term's backward needs no separate forward):
+ *   lse_idx[i][r] = ln sum_{j <= i, j in the row's selected blocks} exp(S_j),
+ *   S_j = <q_idx[i][r], k_idx[j]> / sqrt(d_idx),
+ * -inf for a row with no selected token.  Computed over the forward's own lists
+ * (each index-key block staged once per list), after its combine.
+ *   q_idx  bf16 [N, H_kv, d_idx];  k_idx  bf16 [N, d_idx];  d_idx = 64
+ *   lse_idx fp32 [N, H_kv]  out
+ * Everything else (arguments, outputs, workspace sizes, windows, errors) as
+ * msa_sparse_attn_fwd; o and lse are bit-identical to its results. */
+msa_status_t msa_sparse_attn_fwd_lse_idx(const void* q, const void* k, const void* v,
+                                         const void* q_idx, const void* k_idx,
+                                         const int32_t* block_idx, int64_t N, int H_q, int H_kv,
+                                         int d_h, int d_idx, int B_k, int k_sel, float scale,
+                                         float* o, float* lse, float* lse_idx, void* ws,
+                                         size_t ws_bytes, void* hip_stream);
+
 /* ------------------------------------------------------------------ KL alignment
  * msa_sparse_kl_fwd — Eq. 9-10 (the Index Branch's alignment loss, Algorithm 1
  * step 7) on the selected token set T of each (query, group): the tokens j <= i

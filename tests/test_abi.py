@@ -123,6 +123,22 @@ def test_decode_rejects_bad_arguments(lib):
     assert call(batch=0) == lib.MSA_OK
 
 
+def test_forward_lse_idx_rejects_bad_arguments(lib):
+    raw = lib.raw()
+    f = 0x10000
+
+    def call(N=4096, d_idx=64, qi=f, ki=f, li=f, ws=f, ws_bytes=1 << 40):
+        return raw.msa_sparse_attn_fwd_lse_idx(f, f, f, qi, ki, f, N, 8, 2, 128, d_idx, 128, 8, 0.088, f, f, li,
+                                               ws, ws_bytes, None)
+
+    assert call(d_idx=128) == lib.MSA_ERR_UNSUPPORTED
+    assert call(qi=None) == lib.MSA_ERR_INVALID_ARG
+    assert call(li=None) == lib.MSA_ERR_INVALID_ARG
+    assert call(ki=f + 8) == lib.MSA_ERR_INVALID_ARG  # k_idx needs 16 B
+    assert call(ws_bytes=16) == lib.MSA_ERR_WORKSPACE
+    assert call(N=0) == lib.MSA_OK
+
+
 def test_profile_clock_hook_validates(lib):
     raw = lib.raw()
     assert raw.msa_set_profile_clock(None, 4) == lib.MSA_ERR_INVALID_ARG

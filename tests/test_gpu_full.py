@@ -161,6 +161,14 @@ def test_sparse_kl_128k(msa):
     assert bool(torch.isfinite(kl_all).all()) and float(kl_all.min()) >= -1e-4
     assert abs(float(loss.item()) - float(kl_all.mean())) <= 1e-6 * max(1.0, abs(float(kl_all.mean())))
     print(f"[full] c2 KL: max err {err.max():.2e}, loss {float(loss.item()):.6f}", flush=True)
+    # LSE_idx emitted by the forward itself: the same values on the sampled rows, and
+    # everywhere within fp32 rounding of the KL pass's.
+    _, _, li_fwd = msa.msa_sparse_attn_fwd_lse_idx(inp.q, inp.k, inp.v, inp.q_idx, inp.k_idx, bi, B_k=cfg.B_k)
+    torch.cuda.synchronize()
+    li_f = li_fwd[ridx].cpu().double().numpy()
+    assert np.abs(li_f - li_ref).max() <= 1e-3
+    assert float((li_fwd.double() - lse_idx.double()).abs().max()) <= 1e-4
+    print(f"[full] c2 forward LSE_idx: max err {np.abs(li_f - li_ref).max():.2e}", flush=True)
 
 
 def test_backward_128k(msa):

@@ -126,3 +126,54 @@ def test_sparse_kl_empty(msa):
     lse = torch.empty((0, 8), dtype=torch.float32, device=DEV)
     kl, li, loss = msa.msa_sparse_kl_fwd(q, kv, qi, ki, bi, lse)
     assert kl.shape == (0, 2) and li.shape == (0, 2)
+
+
+def _check_lse_idx(got, li_ref, what, tol=1e-3):
+    got = got.cpu().double().numpy()
+    fin = np.isfinite(li_ref)
+    assert np.array_equal(np.isfinite(got), fin), what
+    assert np.all(got[~fin] == -np.inf), what
+    assert np.abs(got[fin] - li_ref[fin]).max(initial=0) <= tol, (what, np.abs(got[fin] - li_ref[fin]).max())
+
+
+@pytest.mark.parametrize("N,H_q,H_kv,k,B_k", [s + (128,) for s in KL_SHAPES[:8]] + [(2600, 16, 2, 8, 64),
+                                                                                     (700, 8, 1, 16, 64)])
+def test_forward_emits_lse_idx(msa, N, H_q, H_kv, k, B_k):
+    """LSE_idx from the forward (msa_sparse_attn_fwd_lse_idx) against the oracle's, and
+    the forward's o / lse bit-identical to the plain forward."""
+    inp = synth.small_prefill(N=N, H_q=H_q, H_kv=H_kv, k=k, seed=1300 + N, needles=1 if N >= 2000 else 0,
+                              device=DEV, B_k=B_k)
+    bi = msa.msa_index_topk(inp.q_idx, inp.k_idx, k, B_k=B_k)
+    o, lse = msa.msa_sparse_attn_fwd(inp.q, inp.k, inp.v, bi, B_k=B_k)
+    o2, lse2, li = msa.msa_sparse_attn_fwd_lse_idx(inp.q, inp.k, inp.v, inp.q_idx, inp.k_idx, bi, B_k=B_k)
+    _, li_kl, _ = msa.msa_sparse_kl_fwd(inp.q, inp.k, inp.q_idx, inp.k_idx, bi, lse, B_k=B_k)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    _, li_ref = oracle.sparse_kl(inp.q, inp.k, inp.q_idx, inp.k_idx, bi.cpu().numpy(), B_k)
+    _check_lse_idx(li, li_ref, f"N={N} H_q={H_q} H_kv={H_kv} k={k} B_k={B_k}")
+    _check_lse_idx(li, li_kl.cpu().double().numpy(), "against the KL pass", tol=1e-5)
+
+
+def test_forward_lse_idx_arbitrary_block_sets_and_windows(msa):
+    """-1 entries, future blocks and empty rows (-inf), and the minimum workspace's
+    query windows giving the same bits."""
+    N, H_q, H_kv, k = 1500, 8, 2, 5
+    inp = synth.small_prefill(N=N, H_q=H_q, H_kv=H_kv, k=k, seed=1302, device=DEV)
+    g = np.random.default_rng(6)
+    B = (N + 127) // 128
+    bi = np.full((N, H_kv, k), -1, dtype=np.int32)
+    for i in range(N):
+        for r in range(H_kv):
+            c = g.choice(B, size=g.integers(0, k + 1), replace=False)
+            bi[i, r, :len(c)] = c
+    bi[7] = -1
+    bi_d = torch.from_numpy(bi).to(DEV)
+    _, _, li = msa.msa_sparse_attn_fwd_lse_idx(inp.q, inp.k, inp.v, inp.q_idx, inp.k_idx, bi_d)
+    wmin = msa.msa_sparse_attn_fwd_workspace(N, H_q, H_kv, k, minimum=True)
+    ws = torch.empty(wmin, dtype=torch.uint8, device=DEV)
+    _, _, li2 = msa.msa_sparse_attn_fwd_lse_idx(inp.q, inp.k, inp.v, inp.q_idx, inp.k_idx, bi_d, workspace=ws)
+    torch.cuda.synchronize()
+    _, li_ref = oracle.sparse_kl(inp.q, inp.k, inp.q_idx, inp.k_idx, bi, 128)
+    assert np.all(np.isinf(li_ref[7]))
+    _check_lse_idx(li, li_ref, "arbitrary sets")
+    assert torch.equal(li, li2)
