@@ -255,8 +255,9 @@ def write_counter_summary(util_csv: str, fetch_csv: str, write_csv: str, command
     ff, fw = copy_factor(fetch, "FETCH_SIZE"), copy_factor(write, "WRITE_SIZE")
     lines = [
         "# rocprofv3 counters of the library's kernels: 128K prefill (N=131072 H_q=64 H_kv=8 d_h=128",
-        "# B_k=128 k=16, literal inputs), the paged and packed 128K decode (64 sequences) and the",
-        "# split-form Top-k at the pages' table shapes; MI355X, one GPU.  Per kernel: dispatches,",
+        "# B_k=128 k=16, literal inputs) with its KL pass, LSE_idx emission and backward, the paged",
+        "# and packed 128K decode (64 sequences) and the split-form Top-k at the pages' table",
+        "# shapes; MI355X, one GPU.  Per kernel: dispatches,",
         "# mean duration, shader clock (GUI cycles / duration), MFMA busy per SIMD, VALU busy,",
         "# LDS-indexed activity and LDS bank-conflict cycles per CU (fractions of the kernel's",
         "# cycles), and HBM bytes fetched / written per dispatch (calibrated by 1 GiB copies:",
