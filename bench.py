@@ -590,7 +590,16 @@ def run_kl(msa, inp, cfg, block_idx, lse, slot_pairs, lists, pairs, steps):
     out["forward_ms"] = round(t_plain, 4)
     out["forward_with_lse_idx_ms"] = round(t_li, 4)
     out["lse_idx_emission_ms"] = round(t_li - t_plain, 4)
-    del ws, o, lse2, lse_idx
+    del ws, o, lse2
+    # The KL value with that LSE_idx given (no index log partition in the pass).
+    kws = torch.empty(msa.msa_sparse_kl_fwd_workspace(N, H_q, H_kv, k), dtype=torch.uint8, device=dev)
+    kl = torch.empty((N, H_kv), dtype=torch.float32, device=dev)
+    loss = torch.empty((1,), dtype=torch.float32, device=dev)
+    t_given = timed(lambda: msa.msa_sparse_kl_fwd_from_lse_idx(inp.q, inp.k, inp.q_idx, inp.k_idx, block_idx, lse,
+                                                               lse_idx, B_k=B_k, kl=kl, loss=loss, workspace=kws))
+    out["from_lse_idx_ms"] = round(t_given, 4)
+    out["from_lse_idx_loss"] = round(float(loss.item()), 6)
+    del kws, kl, loss, lse_idx
     return out
 
 

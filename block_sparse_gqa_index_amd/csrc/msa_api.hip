@@ -400,18 +400,21 @@ size_t msa_sparse_kl_fwd_workspace_min(int64_t N, int H_q, int H_kv, int d_h, in
   return kl_workspace_bytes(N, H_q, H_kv, k, B_k, true);
 }
 
-msa_status_t msa_sparse_kl_fwd(const void* q, const void* k, const void* q_idx, const void* k_idx,
-                               const int32_t* block_idx, const float* lse, int64_t N, int H_q, int H_kv, int d_h,
-                               int d_idx, int B_k, int k_sel, float scale, float* kl, float* lse_idx, float* loss,
-                               void* ws, size_t ws_bytes, void* hip_stream) {
+// msa_sparse_kl_fwd and msa_sparse_kl_fwd_from_lse_idx: lse_idx_in null computes
+// LSE_idx into lse_idx; otherwise LSE_idx is read from lse_idx_in (lse_idx unused).
+static msa_status_t sparse_kl_run(const void* q, const void* k, const void* q_idx, const void* k_idx,
+                                  const int32_t* block_idx, const float* lse, const float* lse_idx_in, int64_t N,
+                                  int H_q, int H_kv, int d_h, int d_idx, int B_k, int k_sel, float scale, float* kl,
+                                  float* lse_idx, float* loss, void* ws, size_t ws_bytes, void* hip_stream) {
   msa_status_t st = check_kl_shape(N, H_q, H_kv, d_h, d_idx, B_k, k_sel);
   if (st != MSA_OK) return st;
   if (!(scale > 0.f) || scale != scale) return fail(MSA_ERR_INVALID_ARG, "scale must be a positive number");
   if (N == 0) return ok();
-  if (!q || !k || !q_idx || !k_idx || !block_idx || !lse || !kl || !lse_idx || !loss)
+  if (!q || !k || !q_idx || !k_idx || !block_idx || !lse || !kl || !(lse_idx || lse_idx_in) || !loss)
     return fail(MSA_ERR_INVALID_ARG, "null pointer");
+  const void* li = lse_idx_in ? static_cast<const void*>(lse_idx_in) : static_cast<const void*>(lse_idx);
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(q_idx, 16) || !aligned(k_idx, 16) || !aligned(block_idx, 4) ||
-      !aligned(lse, 4) || !aligned(kl, 4) || !aligned(lse_idx, 4) || !aligned(loss, 4))
+      !aligned(lse, 4) || !aligned(kl, 4) || !aligned(li, 4) || !aligned(loss, 4))
     return fail(MSA_ERR_INVALID_ARG, "misaligned pointer (q/k/q_idx/k_idx need 16 B)");
   const size_t need = msa_sparse_kl_fwd_workspace_min(N, H_q, H_kv, d_h, d_idx, B_k, k_sel);
   if (!ws || ws_bytes < need)
@@ -427,13 +430,30 @@ msa_status_t msa_sparse_kl_fwd(const void* q, const void* k, const void* q_idx, 
     const int64_t Wn = (N - w0 < W) ? N - w0 : W;
     hipError_t e = msa::launch_sparse_kl_window(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(q_idx),
-        static_cast<const uint16_t*>(k_idx), lse, block_idx, N, B, B_k, H_q, H_kv, k_sel, scale, w0, Wn, cus, kl, lse_idx,
-        w + kKlLossBytes, L, stream);
+        static_cast<const uint16_t*>(k_idx), lse, block_idx, N, B, B_k, H_q, H_kv, k_sel, scale, w0, Wn, cus,
+        lse_idx_in, kl, lse_idx, w + kKlLossBytes, L, stream);
     if (e != hipSuccess) return hip_fail(e, "sparse_kl launch");
   }
   hipError_t e = msa::launch_kl_loss(kl, N * H_kv, reinterpret_cast<double*>(w), loss, stream);
   if (e != hipSuccess) return hip_fail(e, "kl loss launch");
   return ok();
+}
+
+msa_status_t msa_sparse_kl_fwd(const void* q, const void* k, const void* q_idx, const void* k_idx,
+                               const int32_t* block_idx, const float* lse, int64_t N, int H_q, int H_kv, int d_h,
+                               int d_idx, int B_k, int k_sel, float scale, float* kl, float* lse_idx, float* loss,
+                               void* ws, size_t ws_bytes, void* hip_stream) {
+  return sparse_kl_run(q, k, q_idx, k_idx, block_idx, lse, nullptr, N, H_q, H_kv, d_h, d_idx, B_k, k_sel, scale, kl,
+                       lse_idx, loss, ws, ws_bytes, hip_stream);
+}
+
+msa_status_t msa_sparse_kl_fwd_from_lse_idx(const void* q, const void* k, const void* q_idx, const void* k_idx,
+                                            const int32_t* block_idx, const float* lse, const float* lse_idx,
+                                            int64_t N, int H_q, int H_kv, int d_h, int d_idx, int B_k, int k_sel,
+                                            float scale, float* kl, float* loss, void* ws, size_t ws_bytes,
+                                            void* hip_stream) {
+  return sparse_kl_run(q, k, q_idx, k_idx, block_idx, lse, lse_idx, N, H_q, H_kv, d_h, d_idx, B_k, k_sel, scale, kl,
+                       nullptr, loss, ws, ws_bytes, hip_stream);
 }
 
 // ---------------------------------------------------------------- backward

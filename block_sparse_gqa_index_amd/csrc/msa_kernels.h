@@ -99,7 +99,8 @@ constexpr int kKlLossParts = 256;
 hipError_t launch_sparse_kl_window(const uint16_t* q, const uint16_t* k, const uint16_t* q_idx,
                                    const uint16_t* k_idx, const float* lse, const int32_t* block_idx, int64_t N,
                                    int64_t B, int bk, int H_q, int H_kv, int kk, float scale, int64_t w0, int64_t W,
-                                   int num_cus, float* kl, float* lse_idx, uint8_t* ws, const AttnWorkspace& L,
+                                   int num_cus, const float* lse_idx_in,  // given LSE_idx, or null
+                                   float* kl, float* lse_idx, uint8_t* ws, const AttnWorkspace& L,
                                    hipStream_t stream);
 hipError_t launch_kl_loss(const float* kl, int64_t n, double* partial, float* loss, hipStream_t stream);
 

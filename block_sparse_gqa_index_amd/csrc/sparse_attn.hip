@@ -957,18 +957,21 @@ struct KlRows {
 // from the compiler's resource-usage report so that none spills registers:
 //  - G <= 2 runs one workgroup per CU (its running sums do not fit the 256
 //    registers of two);
-//  - G = 4 and G = 8 with 128-key blocks walk their four key tiles in a loop rather
-//    than unrolled (the unrolled form spills at two workgroups per CU).
-template <int G, int BK>
+//  - G = 4 with 128-key blocks, and G = 8 with 128-key blocks when it keeps the index
+//    log partition (not GIVEN), walk their four key tiles in a loop rather than
+//    unrolled (the unrolled form spills at two workgroups per CU).
+template <int G, int BK, bool GIVEN>
 struct KlRegs {
   static constexpr int kBlocksPerCU = G <= 2 ? 1 : 2;
-  static constexpr int kTileUnroll = ((G == 4 || G == 8) && BK == 128) ? 1 : BK / 32;
+  static constexpr int kTileUnroll = ((G == 4 || (G == 8 && !GIVEN)) && BK == 128) ? 1 : BK / 32;
 };
 
 // BK: keys per block (64 or 128); a 64-key block fills the first half of the
-// staged tiles, and only its two 32-key tiles are computed.
-template <int G, int BK>
-__global__ __launch_bounds__(kAttnThreads, (KlRegs<G, BK>::kBlocksPerCU)) void kl_pair_kernel(
+// staged tiles, and only its two 32-key tiles are computed.  GIVEN: LSE_idx is an
+// input (from msa_sparse_attn_fwd_lse_idx), so the index log partition is not
+// accumulated and a pair's partial is (A, C, Z) alone.
+template <int G, int BK, bool GIVEN>
+__global__ __launch_bounds__(kAttnThreads, (KlRegs<G, BK, GIVEN>::kBlocksPerCU)) void kl_pair_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp, const uint16_t* __restrict__ q_idx,
     const uint16_t* __restrict__ k_idx, const float* __restrict__ lse, const int4* __restrict__ items,
     const int32_t* __restrict__ n_items_ptr, const int32_t* __restrict__ pairs, int64_t N, int H_kv, int64_t B,
@@ -1110,7 +1113,7 @@ __global__ __launch_bounds__(kAttnThreads, (KlRegs<G, BK>::kBlocksPerCU)) void k
         A[qq] = C[qq] = Z[qq] = l[qq] = 0.f;
         mx[qq] = -__builtin_inff();
       }
-#pragma unroll KlRegs<G, BK>::kTileUnroll
+#pragma unroll KlRegs<G, BK, GIVEN>::kTileUnroll
       for (int kt = 0; kt < BK / 32; ++kt) {
         f32x16_t sacc = f32x16_t{}, iacc = f32x16_t{};
 #pragma unroll
@@ -1143,28 +1146,33 @@ __global__ __launch_bounds__(kAttnThreads, (KlRegs<G, BK>::kBlocksPerCU)) void k
           Z[qq] += P;
           C[qq] += pos ? P * S : 0.f;
           A[qq] += pos ? P * (__log2f(P) * kLn2) : 0.f;
-          // running log partition of the index scores
-          const float Sm = in ? S : -__builtin_inff();
-          const float nm = fmaxf(mx[qq], Sm);
-          const float ref = nm == -__builtin_inff() ? 0.f : nm;
-          l[qq] = l[qq] * __builtin_amdgcn_exp2f((mx[qq] - ref) * kLog2e) +
-                  __builtin_amdgcn_exp2f((Sm - ref) * kLog2e);
-          mx[qq] = nm;
+          if constexpr (!GIVEN) {
+            // running log partition of the index scores
+            const float Sm = in ? S : -__builtin_inff();
+            const float nm = fmaxf(mx[qq], Sm);
+            const float ref = nm == -__builtin_inff() ? 0.f : nm;
+            l[qq] = l[qq] * __builtin_amdgcn_exp2f((mx[qq] - ref) * kLog2e) +
+                    __builtin_amdgcn_exp2f((Sm - ref) * kLog2e);
+            mx[qq] = nm;
+          }
         }
       }
       // Sum over the block's keys (the 32 columns of a lane half, 4 tiles each).
 #pragma unroll
       for (int qq = 0; qq < NQ; ++qq) {
         const float a = half_sum(A[qq]), c = half_sum(C[qq]), z = half_sum(Z[qq]);
-        const float M = half_max(mx[qq]);
-        const float ref = M == -__builtin_inff() ? 0.f : M;
-        const float ls = half_sum(l[qq] * __builtin_amdgcn_exp2f((mx[qq] - ref) * kLog2e));
+        float M = 0.f, ls = 0.f;
+        if constexpr (!GIVEN) {
+          M = half_max(mx[qq]);
+          const float ref = M == -__builtin_inff() ? 0.f : M;
+          ls = half_sum(l[qq] * __builtin_amdgcn_exp2f((mx[qq] - ref) * kLog2e));
+        }
         const bool writer = l32 == 0 && (!KlRows<G>::kCross || h == 0);
         if (writer) {
           const int pq = prq[qq];
           float* dst = part + (((int64_t)(pq >> 5) * H_kv + r) * kk + (pq & 31)) * kKlPart;
           *reinterpret_cast<float4*>(dst) = make_float4(a, c, z, M);
-          dst[4] = ls;
+          if constexpr (!GIVEN) dst[4] = ls;
         }
       }
 
@@ -1179,10 +1187,12 @@ __global__ __launch_bounds__(kAttnThreads, (KlRegs<G, BK>::kBlocksPerCU)) void k
   }
 }
 
-// Per (query, group): sum of the valid slots' partials, then KL and LSE_idx.
+// Per (query, group): sum of the valid slots' partials, then KL and LSE_idx (lse_in
+// set: LSE_idx is given, and only KL is written).
 __global__ __launch_bounds__(256) void kl_combine_kernel(const float* __restrict__ part,
                                                          const int32_t* __restrict__ block_idx, int64_t w0,
                                                          int64_t W, int H_kv, int kk, int bsh,
+                                                         const float* __restrict__ lse_in,
                                                          float* __restrict__ kl, float* __restrict__ lse_idx) {
   const int64_t ir = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (ir >= W * H_kv) return;
@@ -1197,7 +1207,7 @@ __global__ __launch_bounds__(256) void kl_combine_kernel(const float* __restrict
     A += a.x;
     C += a.y;
     Z += a.z;
-    if (a.w == -__builtin_inff()) continue;
+    if (lse_in || a.w == -__builtin_inff()) continue;
     if (a.w > M) {
       L = L * __expf(M - a.w) + l;
       M = a.w;
@@ -1206,7 +1216,10 @@ __global__ __launch_bounds__(256) void kl_combine_kernel(const float* __restrict
     }
   }
   const int64_t o = w0 * H_kv + ir;
-  if (M == -__builtin_inff()) {
+  if (lse_in) {
+    const float lse_i = lse_in[o];
+    kl[o] = lse_i == -__builtin_inff() ? 0.f : A - C + lse_i * Z;
+  } else if (M == -__builtin_inff()) {
     kl[o] = 0.f;
     lse_idx[o] = -__builtin_inff();
   } else {
@@ -1621,8 +1634,8 @@ hipError_t launch_sparse_attn_window(const uint16_t* q, const uint16_t* k, const
 hipError_t launch_sparse_kl_window(const uint16_t* q, const uint16_t* k, const uint16_t* q_idx,
                                    const uint16_t* k_idx, const float* lse, const int32_t* block_idx, int64_t N,
                                    int64_t B, int bk, int H_q, int H_kv, int kk, float scale, int64_t w0, int64_t W,
-                                   int num_cus, float* kl, float* lse_idx, uint8_t* ws, const AttnWorkspace& L,
-                                   hipStream_t stream) {
+                                   int num_cus, const float* lse_idx_in, float* kl, float* lse_idx, uint8_t* ws,
+                                   const AttnWorkspace& L, hipStream_t stream) {
   const int G = H_q / H_kv;
   const int bsh = bk == 64 ? 6 : 7;
   hipError_t e = launch_inverse_index(block_idx, B, SeqInfo{}, bsh, H_kv, kk, w0, W, ws, L, stream);
@@ -1637,14 +1650,19 @@ hipError_t launch_sparse_kl_window(const uint16_t* q, const uint16_t* k, const u
   grid = ((grid + 7) / 8) * 8;
   const float scale_log2 = scale * kLog2e;
   switch (G) {
+#define MSA_KL_LAUNCH(GG, BB, GV)                                                                          \
+  kl_pair_kernel<GG, BB, GV><<<dim3((unsigned)grid), dim3(kAttnThreads), 0, stream>>>(                     \
+      q, k, q_idx, k_idx, lse, items, n_items, pairs, N, H_kv, B, L.nW, kk, w0, scale_log2, part, ctr)
 #define MSA_KL_CASE(GG)                                                                                    \
   case GG:                                                                                                 \
-    if (bk == 64)                                                                                          \
-      kl_pair_kernel<GG, 64><<<dim3((unsigned)grid), dim3(kAttnThreads), 0, stream>>>(                     \
-          q, k, q_idx, k_idx, lse, items, n_items, pairs, N, H_kv, B, L.nW, kk, w0, scale_log2, part, ctr);\
+    if (bk == 64 && lse_idx_in)                                                                            \
+      MSA_KL_LAUNCH(GG, 64, true);                                                                         \
+    else if (bk == 64)                                                                                     \
+      MSA_KL_LAUNCH(GG, 64, false);                                                                        \
+    else if (lse_idx_in)                                                                                   \
+      MSA_KL_LAUNCH(GG, 128, true);                                                                        \
     else                                                                                                   \
-      kl_pair_kernel<GG, 128><<<dim3((unsigned)grid), dim3(kAttnThreads), 0, stream>>>(                    \
-          q, k, q_idx, k_idx, lse, items, n_items, pairs, N, H_kv, B, L.nW, kk, w0, scale_log2, part, ctr);\
+      MSA_KL_LAUNCH(GG, 128, false);                                                                       \
     break;
     MSA_KL_CASE(1)
     MSA_KL_CASE(2)
@@ -1653,13 +1671,14 @@ hipError_t launch_sparse_kl_window(const uint16_t* q, const uint16_t* k, const u
     MSA_KL_CASE(16)
     MSA_KL_CASE(32)
 #undef MSA_KL_CASE
+#undef MSA_KL_LAUNCH
     default:
       return hipErrorInvalidValue;
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t rows = W * H_kv;
-  kl_combine_kernel<<<dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream>>>(part, block_idx, w0, W, H_kv,
-                                                                                     kk, bsh, kl, lse_idx);
+  kl_combine_kernel<<<dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream>>>(
+      part, block_idx, w0, W, H_kv, kk, bsh, lse_idx_in, kl, lse_idx);
   return hipGetLastError();
 }
 

@@ -149,6 +149,22 @@ msa_status_t msa_sparse_kl_fwd(const void* q, const void* k, const void* q_idx, 
                                float* kl, float* lse_idx, float* loss, void* ws, size_t ws_bytes,
                                void* hip_stream);
 
+/* msa_sparse_kl_fwd_from_lse_idx — msa_sparse_kl_fwd with LSE_idx given rather than
+ * computed: the forward emits it (msa_sparse_attn_fwd_lse_idx), as the pages' main
+ * pass emits its LSE scalars (paper review page, section 5, 4.3), so the KL value
+ * needs only the teacher terms: kl = sum_j P(j) (ln P(j) - S_j) + LSE_idx, summed
+ * over T (with sum_j P(j) kept exact).
+ *   lse_idx  fp32 [N, H_kv] in: LSE_idx for the same q_idx, k_idx and block_idx
+ *            (-inf marks an empty T: kl = 0 there)
+ * Other arguments, outputs (kl, loss), workspace sizes, limits and errors as
+ * msa_sparse_kl_fwd. */
+msa_status_t msa_sparse_kl_fwd_from_lse_idx(const void* q, const void* k, const void* q_idx,
+                                            const void* k_idx, const int32_t* block_idx,
+                                            const float* lse, const float* lse_idx, int64_t N,
+                                            int H_q, int H_kv, int d_h, int d_idx, int B_k,
+                                            int k_sel, float scale, float* kl, float* loss,
+                                            void* ws, size_t ws_bytes, void* hip_stream);
+
 /* ------------------------------------------------------------------ Backward
  * msa_sparse_attn_bwd — gradients of Eq. 8 with respect to q, k and v for the
  * upstream gradient dO of o, the selection block_idx held fixed (reading notes,

@@ -123,6 +123,23 @@ def test_decode_rejects_bad_arguments(lib):
     assert call(batch=0) == lib.MSA_OK
 
 
+def test_kl_from_lse_idx_rejects_bad_arguments(lib):
+    raw = lib.raw()
+    f = 0x10000
+
+    def call(N=4096, H_q=8, H_kv=2, d_idx=64, li=f, kl=f, ws=f, ws_bytes=1 << 40):
+        return raw.msa_sparse_kl_fwd_from_lse_idx(f, f, f, f, f, f, li, N, H_q, H_kv, 128, d_idx, 128, 8, 0.088, kl,
+                                                  f, ws, ws_bytes, None)
+
+    assert call(d_idx=128) == lib.MSA_ERR_UNSUPPORTED
+    assert call(H_q=128, H_kv=2) == lib.MSA_ERR_UNSUPPORTED  # G = 64 > 32
+    assert call(li=None) == lib.MSA_ERR_INVALID_ARG
+    assert call(li=f + 2) == lib.MSA_ERR_INVALID_ARG
+    assert call(kl=None) == lib.MSA_ERR_INVALID_ARG
+    assert call(ws_bytes=16) == lib.MSA_ERR_WORKSPACE
+    assert call(N=0) == lib.MSA_OK
+
+
 def test_forward_lse_idx_rejects_bad_arguments(lib):
     raw = lib.raw()
     f = 0x10000

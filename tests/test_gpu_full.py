@@ -169,6 +169,15 @@ def test_sparse_kl_128k(msa):
     assert np.abs(li_f - li_ref).max() <= 1e-3
     assert float((li_fwd.double() - lse_idx.double()).abs().max()) <= 1e-4
     print(f"[full] c2 forward LSE_idx: max err {np.abs(li_f - li_ref).max():.2e}", flush=True)
+    # The KL value from that LSE_idx.
+    kl2, loss2 = msa.msa_sparse_kl_fwd_from_lse_idx(inp.q, inp.k, inp.q_idx, inp.k_idx, bi, lse, li_fwd,
+                                                    B_k=cfg.B_k)
+    torch.cuda.synchronize()
+    kl2_s = kl2[ridx].cpu().double().numpy()
+    err2 = np.abs(kl2_s - kl_ref)
+    assert np.all(err2 <= 5e-4 + 2e-3 * np.abs(kl_ref)), err2.max()
+    assert abs(float(loss2.item()) - float(loss.item())) <= 1e-4 * max(1.0, abs(float(loss.item())))
+    print(f"[full] c2 KL from the forward's LSE_idx: max err {err2.max():.2e}", flush=True)
 
 
 def test_backward_128k(msa):

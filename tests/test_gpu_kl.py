@@ -177,3 +177,41 @@ def test_forward_lse_idx_arbitrary_block_sets_and_windows(msa):
     assert np.all(np.isinf(li_ref[7]))
     _check_lse_idx(li, li_ref, "arbitrary sets")
     assert torch.equal(li, li2)
+
+
+@pytest.mark.parametrize("N,H_q,H_kv,k,B_k", [s + (128,) for s in KL_SHAPES] + [(2600, 16, 2, 8, 64),
+                                                                                (700, 8, 1, 16, 64)])
+def test_kl_from_forward_lse_idx(msa, N, H_q, H_kv, k, B_k):
+    """The KL value with LSE_idx given (from the forward) against the oracle, and
+    within fp32 rounding of the pass that computes LSE_idx itself."""
+    inp = synth.small_prefill(N=N, H_q=H_q, H_kv=H_kv, k=k, seed=1400 + N, needles=1 if N >= 2000 else 0,
+                              device=DEV, B_k=B_k)
+    bi = msa.msa_index_topk(inp.q_idx, inp.k_idx, k, B_k=B_k)
+    _, lse, li = msa.msa_sparse_attn_fwd_lse_idx(inp.q, inp.k, inp.v, inp.q_idx, inp.k_idx, bi, B_k=B_k)
+    kl, loss = msa.msa_sparse_kl_fwd_from_lse_idx(inp.q, inp.k, inp.q_idx, inp.k_idx, bi, lse, li, B_k=B_k)
+    kl2, _, loss2 = msa.msa_sparse_kl_fwd(inp.q, inp.k, inp.q_idx, inp.k_idx, bi, lse, B_k=B_k)
+    torch.cuda.synchronize()
+    kl_ref, li_ref = oracle.sparse_kl(inp.q, inp.k, inp.q_idx, inp.k_idx, bi.cpu().numpy(), B_k)
+    _check_kl(kl, li, loss, kl_ref, li_ref, f"from lse_idx N={N} H_q={H_q} H_kv={H_kv} k={k} B_k={B_k}")
+    d = (kl.double() - kl2.double()).abs()
+    assert float(d.max()) <= 1e-4 + 1e-4 * float(kl2.double().abs().max())
+
+
+def test_kl_from_lse_idx_arbitrary_block_sets(msa):
+    """-1 entries, future blocks and empty rows: kl 0 where LSE_idx is -inf."""
+    N, H_q, H_kv, k = 1500, 8, 2, 5
+    inp = synth.small_prefill(N=N, H_q=H_q, H_kv=H_kv, k=k, seed=1402, device=DEV)
+    g = np.random.default_rng(7)
+    B = (N + 127) // 128
+    bi = np.full((N, H_kv, k), -1, dtype=np.int32)
+    for i in range(N):
+        for r in range(H_kv):
+            c = g.choice(B, size=g.integers(0, k + 1), replace=False)
+            bi[i, r, :len(c)] = c
+    bi[7] = -1
+    bi_d = torch.from_numpy(bi).to(DEV)
+    _, lse, li = msa.msa_sparse_attn_fwd_lse_idx(inp.q, inp.k, inp.v, inp.q_idx, inp.k_idx, bi_d)
+    kl, loss = msa.msa_sparse_kl_fwd_from_lse_idx(inp.q, inp.k, inp.q_idx, inp.k_idx, bi_d, lse, li)
+    torch.cuda.synchronize()
+    kl_ref, li_ref = oracle.sparse_kl(inp.q, inp.k, inp.q_idx, inp.k_idx, bi, 128)
+    _check_kl(kl, li, loss, kl_ref, li_ref, "from lse_idx, arbitrary sets")
