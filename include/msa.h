@@ -177,7 +177,8 @@ msa_status_t msa_sparse_kl_fwd_from_lse_idx(const void* q, const void* k, const 
  *   dq         fp32 [N, H_q, d_h]   out
  *   dk, dv     fp32 [N, H_kv, d_h]  out (overwritten, not accumulated into)
  * Limits: G = H_q / H_kv <= 32, and those of msa_sparse_attn_fwd (B_k = 64 or 128).
- * Workspace as for the forward (smaller workspaces run in query windows).  No
+ * Workspace as for the forward (smaller workspaces run in query windows), with a
+ * default size capped at 64 GiB rather than 40 GiB (one window at 128K).  No
  * atomics touch a gradient and each block's rows are listed in (query, slot) order,
  * so all three gradients are bitwise reproducible across reruns with the same
  * workspace size; dq also across workspace sizes, while dk and dv then group their
