@@ -59,6 +59,12 @@ __device__ __forceinline__ u32x4_t pack8(const float* x) {
                  pack_bf16x2(x[6], x[7])};
 }
 
+// dS of a sub-chunk in LDS, key-major: key K (0..127) owns 128 bytes, rows 0..63 as
+// bf16, in 16-byte chunks of 8 rows placed at chunk (R / 8) ^ (K % 8), so that the
+// 8-byte accesses of one instruction (consecutive keys) spread over the banks.  Runs
+// of four rows starting at a multiple of 4 stay inside one chunk.
+__device__ __forceinline__ int bwd_ds_offset(int K, int R) { return K * 128 + ((((R >> 3) ^ K) & 7) << 4) + (R & 7) * 2; }
+
 // Per-row values of a 64-row sub-chunk are kept one row per lane, row R on lane
 // bwd_row_lane(R): bit 2 of R picks the lane half and the other five bits the lane
 // within it.  The S/dP layout needs, in lane half h, rows whose bit 2 is h, so each
@@ -123,7 +129,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t Kt[kDh * 256];   // K^T, keys in natural order
   __shared__ __attribute__((aligned(16))) uint8_t Qs[kBwdRows * 256];   // q rows
   __shared__ __attribute__((aligned(16))) uint8_t dOs[kBwdRows * 256];  // dO rows
-  __shared__ __attribute__((aligned(16))) uint8_t dSs[kBwdRows * 256];  // dS rows (keys in natural order)
+  __shared__ __attribute__((aligned(16))) uint8_t dSs[kBwdRows * 256];  // dS, key-major (bwd_ds_offset)
   __shared__ __attribute__((aligned(16))) uint8_t Px[8 * 2048];         // each wave's P for its partner
 
   const int tid = threadIdx.x;
@@ -275,9 +281,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
       else
         s_dp(std::integral_constant<int, 1>{});
       // The wave's P goes to Px for its partner (wave w's 2 KB at w * 2 KB, operand s2
-      // of lane l at (64 s2 + l) * 16 B); its dS rows go into dSs, row-major with keys
-      // in natural order and chunk kc at kc ^ (row & 15), for dQ and for the partner.
-      // Both areas were last read before the previous sub-chunk's final barrier.
+      // of lane l at (64 s2 + l) * 16 B); its dS goes into dSs key-major: the lane's key
+      // holds the four runs of four consecutive rows of its 16 values, one 8-byte store
+      // each.  Both areas were last read before the previous sub-chunk's final barrier.
       {
         const int lv = lane_v();
         const int h = lv >> 5;
@@ -286,11 +292,11 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
         xp[0] = Pp[0];
         xp[64] = Pp[1];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int rv = dh * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-          const uint32_t w2 = dSp[v >> 3][(v & 7) >> 1];
-          *reinterpret_cast<uint16_t*>(dSs + rv * 256 + ((((koff >> 3) ^ (rv & 15))) << 4) + (koff & 7) * 2) =
-              (uint16_t)((v & 1) ? (w2 >> 16) : (w2 & 0xffffu));
+        for (int g = 0; g < 4; ++g) {
+          const int r0 = dh * 32 + 8 * g + 4 * h;  // values v = 4g .. 4g + 3
+          const u32x4_t& src = dSp[g >> 1];
+          *reinterpret_cast<u32x2_t*>(dSs + bwd_ds_offset(koff, r0)) =
+              (g & 1) ? u32x2_t{src[2], src[3]} : u32x2_t{src[0], src[1]};
         }
       }
       __syncthreads();  // P exchanged, dS complete
@@ -322,20 +328,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
         const u32x4_t* xo = reinterpret_cast<const u32x4_t*>(Px + (wave ^ 4) * 2048) + lv;
         Po[0] = xo[0];
         Po[1] = xo[64];
+        // The partner's dS at this lane's key: k-slots j = 0..3 and 4..7 of step s2 are
+        // the runs of rows rto*32 + 16 s2 + 4h and + 8 (four consecutive rows each).
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            uint32_t hw[2];
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-              const int j = 2 * m + e;
-              const int row = rto * 32 + 8 * (2 * s2 + (j >> 2)) + 4 * h + (j & 3);
-              hw[e] = *reinterpret_cast<const uint16_t*>(dSs + row * 256 + ((((koff >> 3) ^ (row & 15))) << 4) +
-                                                         (koff & 7) * 2);
-            }
-            dSo[s2][m] = hw[0] | (hw[1] << 16);
-          }
+          const int r0 = rto * 32 + 16 * s2 + 4 * h;
+          const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(dSs + bwd_ds_offset(koff, r0));
+          const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(dSs + bwd_ds_offset(koff, r0 + 8));
+          dSo[s2] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
         }
 #pragma unroll
         for (int tile = 0; tile < 2; ++tile) {
@@ -368,12 +368,26 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
         const int h = lv >> 5, l32 = lv & 31;
         const int row = 32 * (wave & 1) + l32;
         const int d = 32 * (wave >> 1) + swap23(l32);
+        // The B operand (8 keys of the lane's dQ row) from the key-major dS by
+        // transposing reads: in each group of 16 lanes, lane L reads rows
+        // Rb + 4(L % 4) .. + 3 of key K0 + L / 4, so lane i receives row Rb + i of keys
+        // K0 .. K0 + 3 (Rb: the group's first row).
+        const int gl = lv & 15;
+        const int rb = 32 * (wave & 1) + (l32 & 16) + 4 * (gl & 3);
+        auto ds_tr = [&](int k0) -> u32x2_t {
+          typedef short v4i16 __attribute__((ext_vector_type(4)));
+          const uint8_t* p = dSs + bwd_ds_offset(k0 + (gl >> 2), rb);
+          const v4i16 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (v4i16 __attribute__((address_space(3)))*)(const_cast<uint8_t*>(p)));
+          return __builtin_bit_cast(u32x2_t, x);
+        };
         f32x16_t qacc = f32x16_t{};
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
           const int kc = 2 * t + h;
           const u32x4_t ak = *reinterpret_cast<const u32x4_t*>(Kt + d * 256 + ((kc ^ (d & 15)) << 4));
-          const u32x4_t bs = *reinterpret_cast<const u32x4_t*>(dSs + row * 256 + ((kc ^ (row & 15)) << 4));
+          const u32x2_t s0 = ds_tr(8 * kc), s1 = ds_tr(8 * kc + 4);
+          const u32x4_t bs = u32x4_t{s0[0], s0[1], s1[0], s1[1]};
           qacc = mfma_32x32x16(as_bf16x8(ak), as_bf16x8(bs), qacc);
         }
         const int pr = __shfl(cur_prv, bwd_row_lane(row));
