@@ -447,37 +447,49 @@ static uint32_t block_key_mask(int64_t N, int bk) {
   return m;
 }
 
+template <int LIST, int CT, int BK>
+static void launch_index_topk_ct(const uint16_t* q_idx, const uint16_t* k_idx, int64_t N, int H_kv, int k,
+                                 int32_t* block_idx, const int64_t* cu, unsigned gy, int64_t T, uint32_t imask,
+                                 hipStream_t stream) {
+  const int64_t grid = (N * H_kv + kIdxWaves * 32 * CT - 1) / (kIdxWaves * 32 * CT);
+  index_topk_kernel<LIST, CT, false, BK><<<dim3((unsigned)grid, gy), dim3(kIdxThreads), 0, stream>>>(
+      q_idx, k_idx, N, H_kv, k, 0, block_idx, nullptr, cu, T, imask);
+}
+
+// Four column tiles per wave halve the staged key reads per column, but at small
+// N * H_kv they leave too few workgroups: with fewer than two per CU the GPU is
+// half idle (each workgroup's sweep is as long as its last query), so two tiles
+// are used there instead (B_k = 64 and k > 16 always use two: four would spill).
 template <int BK>
 static hipError_t launch_index_topk_bk(const uint16_t* q_idx, const uint16_t* k_idx, int64_t N, int H_kv, int k,
-                                       int32_t* block_idx, const int64_t* cu, int batch, int64_t T,
+                                       int32_t* block_idx, const int64_t* cu, int batch, int64_t T, int num_cus,
                                        hipStream_t stream) {
-  const int64_t total = N * H_kv;
   const uint32_t imask = block_key_mask(N, BK);
   const unsigned gy = cu ? (unsigned)batch : 1u;
+  const int64_t wg4 = (N * H_kv + kIdxWaves * 32 * 4 - 1) / (kIdxWaves * 32 * 4) * gy;
+  const bool four = wg4 >= 2 * (int64_t)num_cus;
+  constexpr int CT4 = BK == 128 ? 4 : 2;
   if (k <= 8) {
-    constexpr int CT = BK == 128 ? 4 : 2;  // at B_k = 64 four tiles would spill registers
-    const int64_t grid = (total + kIdxWaves * 32 * CT - 1) / (kIdxWaves * 32 * CT);
-    index_topk_kernel<7, CT, false, BK><<<dim3((unsigned)grid, gy), dim3(kIdxThreads), 0, stream>>>(
-        q_idx, k_idx, N, H_kv, k, 0, block_idx, nullptr, cu, T, imask);
+    if (four)
+      launch_index_topk_ct<7, CT4, BK>(q_idx, k_idx, N, H_kv, k, block_idx, cu, gy, T, imask, stream);
+    else
+      launch_index_topk_ct<7, 2, BK>(q_idx, k_idx, N, H_kv, k, block_idx, cu, gy, T, imask, stream);
   } else if (k <= 16) {
-    constexpr int CT = BK == 128 ? 4 : 2;  // at B_k = 64 four tiles would spill registers
-    const int64_t grid = (total + kIdxWaves * 32 * CT - 1) / (kIdxWaves * 32 * CT);
-    index_topk_kernel<15, CT, false, BK><<<dim3((unsigned)grid, gy), dim3(kIdxThreads), 0, stream>>>(
-        q_idx, k_idx, N, H_kv, k, 0, block_idx, nullptr, cu, T, imask);
+    if (four)
+      launch_index_topk_ct<15, CT4, BK>(q_idx, k_idx, N, H_kv, k, block_idx, cu, gy, T, imask, stream);
+    else
+      launch_index_topk_ct<15, 2, BK>(q_idx, k_idx, N, H_kv, k, block_idx, cu, gy, T, imask, stream);
   } else {
-    constexpr int CT = 2;
-    const int64_t grid = (total + kIdxWaves * 32 * CT - 1) / (kIdxWaves * 32 * CT);
-    index_topk_kernel<31, CT, false, BK><<<dim3((unsigned)grid, gy), dim3(kIdxThreads), 0, stream>>>(
-        q_idx, k_idx, N, H_kv, k, 0, block_idx, nullptr, cu, T, imask);
+    launch_index_topk_ct<31, 2, BK>(q_idx, k_idx, N, H_kv, k, block_idx, cu, gy, T, imask, stream);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_index_topk(const uint16_t* q_idx, const uint16_t* k_idx, int64_t N, int H_kv, int k,
-                             int32_t* block_idx, const int64_t* cu, int batch, int64_t T, int bk,
+                             int32_t* block_idx, const int64_t* cu, int batch, int64_t T, int bk, int num_cus,
                              hipStream_t stream) {
-  if (bk == 64) return launch_index_topk_bk<64>(q_idx, k_idx, N, H_kv, k, block_idx, cu, batch, T, stream);
-  return launch_index_topk_bk<128>(q_idx, k_idx, N, H_kv, k, block_idx, cu, batch, T, stream);
+  if (bk == 64) return launch_index_topk_bk<64>(q_idx, k_idx, N, H_kv, k, block_idx, cu, batch, T, num_cus, stream);
+  return launch_index_topk_bk<128>(q_idx, k_idx, N, H_kv, k, block_idx, cu, batch, T, num_cus, stream);
 }
 
 hipError_t launch_index_block_scores(const uint16_t* q_idx, const uint16_t* k_idx, int64_t N, int H_kv, int bk,

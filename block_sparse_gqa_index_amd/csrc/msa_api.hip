@@ -148,7 +148,8 @@ msa_status_t msa_index_topk(const void* q_idx, const void* k_idx, int64_t N, int
     return fail(MSA_ERR_INVALID_ARG, "misaligned pointer (q_idx/k_idx need 16 B, block_idx 4 B)");
   if (N * H_kv >= ((int64_t)1 << 31)) return fail(MSA_ERR_UNSUPPORTED, "N * H_kv too large");
   hipError_t e = msa::launch_index_topk(static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx),
-                                        N, H_kv, k, block_idx, nullptr, 0, N, B_k, static_cast<hipStream_t>(hip_stream));
+                                        N, H_kv, k, block_idx, nullptr, 0, N, B_k, num_cus(),
+                                        static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_fail(e, "index_topk launch");
   return ok();
 }
@@ -323,7 +324,7 @@ msa_status_t msa_index_topk_varlen(const void* q_idx, const void* k_idx, const i
   if (T * H_kv >= ((int64_t)1 << 31)) return fail(MSA_ERR_UNSUPPORTED, "T * H_kv too large");
   if (batch > 65535) return fail(MSA_ERR_UNSUPPORTED, "batch must be <= 65535");
   hipError_t e = msa::launch_index_topk(static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx),
-                                        max_len, H_kv, k, block_idx, cu_seqlens, batch, T, B_k,
+                                        max_len, H_kv, k, block_idx, cu_seqlens, batch, T, B_k, num_cus(),
                                         static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_fail(e, "index_topk launch");
   return ok();

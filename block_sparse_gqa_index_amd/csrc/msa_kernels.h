@@ -37,7 +37,7 @@ struct DecodeWorkspace {
 
 // bk: keys per block, 64 or 128.
 hipError_t launch_index_topk(const uint16_t* q_idx, const uint16_t* k_idx, int64_t N, int H_kv, int k,
-                             int32_t* block_idx, const int64_t* cu, int batch, int64_t T, int bk,
+                             int32_t* block_idx, const int64_t* cu, int batch, int64_t T, int bk, int num_cus,
                              hipStream_t stream);
 hipError_t launch_index_block_scores(const uint16_t* q_idx, const uint16_t* k_idx, int64_t N, int H_kv, int bk,
                                      float* M, hipStream_t stream);
