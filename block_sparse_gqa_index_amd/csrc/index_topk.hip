@@ -25,29 +25,28 @@ namespace {
 
 constexpr int kIdxWaves = 8;
 constexpr int kIdxThreads = kIdxWaves * kWave;
-constexpr int kIdxLoads = kBk * 8 / kIdxThreads;  // 16-byte chunks of a staged block per thread
 constexpr int kIdxBlocksPerCU = 8 / kIdxWaves;     // two waves per SIMD
 
-// Stage key block b of k_idx into LDS: 128 rows x 8 chunks of 16 B, chunk c of row
-// j stored at chunk position c ^ ((j >> 1) & 7): the 16 rows a 16-lane LDS pass
-// reads then fall on 16 different 16-byte bank groups.
-__device__ __forceinline__ void idx_load_block(const uint16_t* __restrict__ k_idx, int64_t N,
-                                               int64_t b, int tid, uint4 (&r)[kIdxLoads]) {
-#pragma unroll
-  for (int m = 0; m < kIdxLoads; ++m) {
-    const int cidx = tid + kIdxThreads * m;
-    const int key = cidx >> 3, c = cidx & 7;
-    const int64_t j = b * kBk + key;
-    r[m] = j < N ? *reinterpret_cast<const uint4*>(k_idx + j * kDidx + c * 8) : make_uint4(0, 0, 0, 0);
-  }
-}
+// Stage key tile b of k_idx (128 keys) into LDS: 128 rows x 8 chunks of 16 B, chunk c
+// of row j stored at chunk position c ^ ((j >> 1) & 7): the 16 rows a 16-lane LDS
+// pass reads then fall on 16 different 16-byte bank groups.  The 16-byte global ->
+// LDS loads write lane l's 16 bytes at the instruction's LDS base + 16 l (measured on
+// the GPU with an in-bounds probe), so each wave instruction fills 8 rows (1 KB) and
+// a lane fetches the global chunk that belongs at its LDS position.  Keys past the
+// end read the last key (their scores are masked: no query sees them).
+constexpr int kIdxDmaPerWave = 16 / kIdxWaves;  // 1 KB instructions per wave per tile
+constexpr unsigned kWaitVmcnt0 = 0x0F70;        // s_waitcnt vmcnt(0), other counters free
 
-__device__ __forceinline__ void idx_store_block(uint8_t* buf, int tid, const uint4 (&r)[kIdxLoads]) {
+__device__ __forceinline__ void idx_dma_block(const uint16_t* __restrict__ k_idx, int64_t N, int64_t b, int wave,
+                                              int lane, uint8_t* buf) {
 #pragma unroll
-  for (int m = 0; m < kIdxLoads; ++m) {
-    const int cidx = tid + kIdxThreads * m;
-    const int key = cidx >> 3, c = cidx & 7;
-    *reinterpret_cast<uint4*>(buf + key * 128 + ((c ^ ((key >> 1) & 7)) << 4)) = r[m];
+  for (int t = 0; t < kIdxDmaPerWave; ++t) {
+    const int m = wave + kIdxWaves * t;  // rows 8m .. 8m+7 (uniform per wave)
+    const int key = 8 * m + (lane >> 3);
+    const int c = (lane & 7) ^ ((key >> 1) & 7);
+    int64_t j = b * kBk + key;
+    j = j < N ? j : N - 1;
+    __builtin_amdgcn_global_load_lds(k_idx + j * kDidx + c * 8, buf + m * 1024, 16, 0, 0);
   }
 }
 
@@ -205,19 +204,21 @@ __global__ __launch_bounds__(kIdxThreads, kIdxBlocksPerCU) void index_topk_kerne
     }
   }
 
-  uint4 pre[2][kIdxLoads];
-  idx_load_block(k_idx, N, 0, tid, pre[0]);
-  if (b_last >= 1) idx_load_block(k_idx, N, 1, tid, pre[1]);
+  // Key tiles go straight from global memory to LDS (no registers), one step ahead:
+  // tiles b+2, b+3 are loaded into the other buffer pair while b, b+1 are computed.
+  idx_dma_block(k_idx, N, 0, wave, lane, kbuf[0][0]);
+  if (b_last >= 1) idx_dma_block(k_idx, N, 1, wave, lane, kbuf[0][1]);
   int step = 0;
   for (int64_t b = 0; b <= b_last; b += 2, ++step) {
     const bool two = b + 1 <= b_last;
     uint8_t* buf0 = kbuf[step & 1][0];
     uint8_t* buf1 = kbuf[step & 1][1];
-    idx_store_block(buf0, tid, pre[0]);
-    if (two) idx_store_block(buf1, tid, pre[1]);
+    // This wave's loads of the pair have landed; after the barrier everyone's have,
+    // and everyone has finished reading the other pair (the previous step's).
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
-    if (b + 2 <= b_last) idx_load_block(k_idx, N, b + 2, tid, pre[0]);
-    if (b + 3 <= b_last) idx_load_block(k_idx, N, b + 3, tid, pre[1]);
+    if (b + 2 <= b_last) idx_dma_block(k_idx, N, b + 2, wave, lane, kbuf[(step + 1) & 1][0]);
+    if (b + 3 <= b_last) idx_dma_block(k_idx, N, b + 3, wave, lane, kbuf[(step + 1) & 1][1]);
 
     float m0[CT][NS], m1[CT][NS];
     idx_block_max<CT, NS>(buf0, qop, qi, b, b * kBk + (kBk - 1) > i_min_wave, h, l32, m0);
