@@ -107,6 +107,19 @@ __device__ __forceinline__ void idx_block_max(const uint8_t* buf, const uint4 (&
       const int pj = j - 1, pkt = pj / CT, pct = pj % CT;
       idx_tile_reduce<MASK>(acc[pj & 1], qi[pct], b, pkt, h, bmax[pct][pkt / kPerBlock]);
     }
+    // Each MFMA of tile j is followed by a share of tile j-1's reduction, so the
+    // VALU work issues while the matrix unit runs (left to itself the compiler
+    // paired two tiles' MFMAs and then reduced both, with no overlap in the wave).
+    if (ct == 0) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    if (j == 0) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    } else {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, MASK ? 12 : 2, 0);
+      }
+    }
   }
   {
     constexpr int pj = kTiles - 1, pkt = pj / CT, pct = pj % CT;
