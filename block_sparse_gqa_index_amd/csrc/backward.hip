@@ -454,24 +454,17 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
         fetch_rows(cb + kQS);
         fetch_info(cb + kQS);
       }
-      // dV/dK(1).
-#pragma unroll
-      for (int i = 0; i < kDvkAhead; ++i) dvk_load(1, i);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (i + kDvkAhead < 16) dvk_load(1, i + kDvkAhead);
-        dvk_mfma(1, i);
-        __builtin_amdgcn_sched_barrier(0);
-      }
       __syncthreads();  // dS complete
-      // dQ^T = K^T dS^T: rows 32 nt + l32 (MFMA columns), dims 32w + swap23(i) (MFMA
-      // rows), all 128 keys.  The dS^T operand by transposing reads of the key-major
-      // dS: lane L of a group reads rows rb .. rb+3 of key K0 + L / 4, so lane i
-      // receives row (group's first row) + i of keys K0 .. K0+3.
+      // dV/dK(1) and dQ^T = K^T dS^T as one sequence, their MFMAs alternating (each with
+      // its operand reads a few steps ahead), so that neither waits alone on its LDS
+      // reads.  dQ: rows 32 nt + l32 (MFMA columns), dims 32w + swap23(i) (MFMA rows),
+      // all 128 keys; its dS^T operand by transposing reads of the key-major dS: lane L
+      // of a group reads rows rb .. rb+3 of key K0 + L / 4, so lane i receives row
+      // (group's first row) + i of keys K0 .. K0+3.
       {
         constexpr int kDqAhead = 4;
         u32x4_t sop[16];
-        // MFMA i: k-step t = i / 2 of row tile nt = i % 2.
+        // dQ MFMA i: k-step t = i / 2 of row tile nt = i % 2.
         auto load_s = [&](int i) {
           const int t = i >> 1, nt = i & 1;
           const u32x2_t lo = lds_tr8(dSs + 4096 * (t >> 1) + off_dq[t & 1][nt][0]);
@@ -481,15 +474,18 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
         f32x16_t qacc[2];
         qacc[0] = qacc[1] = f32x16_t{};
 #pragma unroll
+        for (int i = 0; i < kDvkAhead; ++i) dvk_load(1, i);
+#pragma unroll
         for (int i = 0; i < kDqAhead; ++i) load_s(i);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
+          if (i + kDvkAhead < 16) dvk_load(1, i + kDvkAhead);
+          dvk_mfma(1, i);
+          __builtin_amdgcn_sched_barrier(0);
           if (i + kDqAhead < 16) load_s(i + kDqAhead);
           qacc[i & 1] = mfma_32x32x16(as_bf16x8(ktop[i >> 1]), as_bf16x8(sop[i]), qacc[i & 1]);
-          if (i + kDqAhead < 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
         // dQ rows (bf16, one per pair and head, scaled): element v of lane (l32, h) in
         // tile nt is row 32 nt + l32, dim 32w + 8h + 16(v / 8) + v % 8.  Rows past the
         // item's end write to a dummy row, so every lane stores and the count of
