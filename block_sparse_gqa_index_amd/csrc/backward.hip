@@ -144,7 +144,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
     uint64_t* __restrict__ clk) {
   static_assert(G <= 32, "a sub-chunk holds at least two queries");
   constexpr int kQS = kBwdRows / G;  // queries per sub-chunk
-  // 2 x 32 KB block rows + 2 x 2 x 16 KB q/dO rows + 16 KB dS = 144 KB.
+  // 2 x 32 KB block rows + 2 x 2 x 16 KB q/dO rows + 16 KB dS + 3 KB of row tables and
+  // the item's pairs: 147 KB (one workgroup per CU).
   __shared__ __attribute__((aligned(16))) uint8_t Ks[kBk * 256];
   __shared__ __attribute__((aligned(16))) uint8_t Vs[kBk * 256];
   __shared__ __attribute__((aligned(16))) uint8_t Qs[2][kBwdRows * 256];
