@@ -17,6 +17,8 @@
 // S^T = K * Q^T and O^T = V^T * P^T on 32x32x16 bf16 MFMAs, with the softmax in
 // fp32 in between.  Every pair owns its partial slot [query][group][slot], so the
 // partials of hot (sink) blocks spread over many workgroups without atomics.
+#include <type_traits>
+
 #include "msa_device.h"
 #include "msa_kernels.h"
 #include "table_clamp.h"
@@ -957,14 +959,23 @@ struct KlRows {
 // from the compiler's resource-usage report so that none spills registers:
 //  - G <= 2 runs one workgroup per CU (its running sums do not fit the 256
 //    registers of two);
-//  - G = 4 with 128-key blocks, and G = 8 with 128-key blocks when it keeps the index
-//    log partition (not GIVEN), walk their four key tiles in a loop rather than
-//    unrolled (the unrolled form spills at two workgroups per CU).
+//  - G = 4 and G = 16, and G = 8 with 128-key blocks when it keeps the index log
+//    partition (not GIVEN), walk their key tiles in a loop rather than unrolled
+//    (the unrolled form spills at two workgroups per CU);
+//  - the key tiles are walked by two copies of the loop, with and without the
+//    causal mask (only a query's own block needs it), except for G = 4 with
+//    128-key blocks and not GIVEN, which spills with both copies.
 template <int G, int BK, bool GIVEN>
 struct KlRegs {
   static constexpr int kBlocksPerCU = G <= 2 ? 1 : 2;
-  static constexpr int kTileUnroll = ((G == 4 || (G == 8 && !GIVEN)) && BK == 128) ? 1 : BK / 32;
+  static constexpr int kTileUnroll = (G == 4 || G == 16 || (G == 8 && !GIVEN && BK == 128)) ? 1 : BK / 32;
+  static constexpr bool kSplitMask = !(G == 4 && BK == 128 && !GIVEN);
 };
+
+// Index score scale 1 / sqrt(d_idx), in natural and base-2 units.
+constexpr float kIdxScale = 0.125f;
+constexpr float kIdxScaleLog2 = kIdxScale * kLog2e;
+static_assert(kDidx == 64, "kIdxScale is 1 / sqrt(64)");
 
 // BK: keys per block (64 or 128); a 64-key block fills the first half of the
 // staged tiles, and only its two 32-key tiles are computed.  GIVEN: LSE_idx is an
@@ -979,6 +990,8 @@ __global__ __launch_bounds__(kAttnThreads, (KlRegs<G, BK, GIVEN>::kBlocksPerCU))
   constexpr int kQC = 128 / G;
   constexpr int GL = KlRows<G>::GL, NQ = KlRows<G>::NQ;
   static_assert(G <= 32, "a query's heads must lie in one wave");
+  static_assert((G & (G - 1)) == 0, "G is a power of two");
+  constexpr float kLog2G = (float)__builtin_ctz(G);
   __shared__ __attribute__((aligned(16))) uint8_t Ks[kBk * 256];
   __shared__ __attribute__((aligned(16))) uint8_t KIs[kBk * 128];
   __shared__ __attribute__((aligned(16))) uint8_t Qs[4][32 * 256];  // per wave: its 32 q rows
@@ -1055,7 +1068,7 @@ __global__ __launch_bounds__(kAttnThreads, (KlRegs<G, BK, GIVEN>::kBlocksPerCU))
       const uint16_t* src = q_idx + (iq * H_kv + r) * kDidx + 32 * hh;
 #pragma unroll
       for (int t = 0; t < 4; ++t) qi[t] = *reinterpret_cast<const u32x4_t*>(src + 8 * t);
-      l2 = lse[iq * H_q + r * G + g] * kLog2e;
+      l2 = fmaf(lse[iq * H_q + r * G + g], kLog2e, kLog2G);  // log2(G): the head mean's 1/G
     };
 
     int cur = chunk_reg(0), cur_n = cur;
@@ -1107,14 +1120,22 @@ __global__ __launch_bounds__(kAttnThreads, (KlRegs<G, BK, GIVEN>::kBlocksPerCU))
         part_blk |= lim[qq] < BK - 1;
       }
       part_blk = __any(part_blk);
+      // Running sums per query over the lane's keys, in the units that cost no
+      // instruction per key: R = <q_idx, k_idx> unscaled (S = R / sqrt(d_idx)), and
+      // base-2 logarithms; the constant factors are applied once per block below.
+      //   Z = sum P,  C = sum P R,  A = sum P log2 P,
+      //   l = sum 2^((R - mx) c), mx = max R, c = log2(e) / sqrt(d_idx).
+      // P log2 P uses max(P, FLT_MIN) in the logarithm, so P = 0 adds 0 without a
+      // select.  l takes one exponential per key: 2^(-|R - mx| c) either scales the
+      // old sum (R above the running max) or is the key's own term.
       float A[NQ], C[NQ], Z[NQ], mx[NQ], l[NQ];
 #pragma unroll
       for (int qq = 0; qq < NQ; ++qq) {
         A[qq] = C[qq] = Z[qq] = l[qq] = 0.f;
         mx[qq] = -__builtin_inff();
       }
-#pragma unroll KlRegs<G, BK, GIVEN>::kTileUnroll
-      for (int kt = 0; kt < BK / 32; ++kt) {
+      auto tile = [&](int kt, auto masked) {
+        constexpr bool MASKED = decltype(masked)::value;
         f32x16_t sacc = f32x16_t{}, iacc = f32x16_t{};
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
@@ -1132,40 +1153,46 @@ __global__ __launch_bounds__(kAttnThreads, (KlRegs<G, BK, GIVEN>::kBlocksPerCU))
         const int koff = kt * 32 + koff0;
 #pragma unroll
         for (int qq = 0; qq < NQ; ++qq) {
-          const bool in = !part_blk || koff <= lim[qq];
-          float ps = 0.f;
+          // Teacher P: the mean over the group's heads (1/G is in l2v).
+          float ps = __builtin_amdgcn_exp2f(fmaf(sacc[qq * GL], scale_log2, -l2v[qq * GL]));
 #pragma unroll
-          for (int e = 0; e < GL; ++e) {
+          for (int e = 1; e < GL; ++e) {
             const int v = qq * GL + e;
             ps += __builtin_amdgcn_exp2f(fmaf(sacc[v], scale_log2, -l2v[v]));
           }
           if constexpr (KlRows<G>::kCross) ps += __shfl_xor(ps, 32);
-          const float P = in ? ps * (1.f / G) : 0.f;
-          const float S = iacc[qq * GL] * 0.125f;  // 1 / sqrt(d_idx)
-          const bool pos = P > 0.f;
+          const bool in = !MASKED || koff <= lim[qq];
+          const float P = in ? ps : 0.f;
+          const float R = iacc[qq * GL];
           Z[qq] += P;
-          C[qq] += pos ? P * S : 0.f;
-          A[qq] += pos ? P * (__log2f(P) * kLn2) : 0.f;
+          C[qq] = fmaf(P, R, C[qq]);
+          A[qq] = fmaf(P, __log2f(fmaxf(P, __FLT_MIN__)), A[qq]);
           if constexpr (!GIVEN) {
-            // running log partition of the index scores
-            const float Sm = in ? S : -__builtin_inff();
-            const float nm = fmaxf(mx[qq], Sm);
-            const float ref = nm == -__builtin_inff() ? 0.f : nm;
-            l[qq] = l[qq] * __builtin_amdgcn_exp2f((mx[qq] - ref) * kLog2e) +
-                    __builtin_amdgcn_exp2f((Sm - ref) * kLog2e);
-            mx[qq] = nm;
+            const float d = in ? R - mx[qq] : -__builtin_inff();
+            const float ex = __builtin_amdgcn_exp2f(-fabsf(d) * kIdxScaleLog2);
+            const bool up = d > 0.f;
+            l[qq] = up ? fmaf(l[qq], ex, 1.f) : l[qq] + ex;
+            mx[qq] = up ? R : mx[qq];
           }
         }
+      };
+      if (!KlRegs<G, BK, GIVEN>::kSplitMask || part_blk) {
+#pragma unroll KlRegs<G, BK, GIVEN>::kTileUnroll
+        for (int kt = 0; kt < BK / 32; ++kt) tile(kt, std::true_type{});
+      } else {
+#pragma unroll KlRegs<G, BK, GIVEN>::kTileUnroll
+        for (int kt = 0; kt < BK / 32; ++kt) tile(kt, std::false_type{});
       }
       // Sum over the block's keys (the 32 columns of a lane half, 4 tiles each).
 #pragma unroll
       for (int qq = 0; qq < NQ; ++qq) {
-        const float a = half_sum(A[qq]), c = half_sum(C[qq]), z = half_sum(Z[qq]);
+        const float a = half_sum(A[qq]) * kLn2, c = half_sum(C[qq]) * kIdxScale, z = half_sum(Z[qq]);
         float M = 0.f, ls = 0.f;
         if constexpr (!GIVEN) {
-          M = half_max(mx[qq]);
-          const float ref = M == -__builtin_inff() ? 0.f : M;
-          ls = half_sum(l[qq] * __builtin_amdgcn_exp2f((mx[qq] - ref) * kLog2e));
+          const float Mr = half_max(mx[qq]);
+          const float ref = Mr == -__builtin_inff() ? 0.f : Mr;
+          ls = half_sum(l[qq] * __builtin_amdgcn_exp2f((mx[qq] - ref) * kIdxScaleLog2));
+          M = Mr * kIdxScale;
         }
         const bool writer = l32 == 0 && (!KlRows<G>::kCross || h == 0);
         if (writer) {
@@ -1281,7 +1308,7 @@ __global__ __launch_bounds__(256) void lse_idx_pair_kernel(
     const int32_t* __restrict__ n_items_ptr, const int32_t* __restrict__ pairs, int64_t N, SeqInfo si, int H_kv,
     int kk, int64_t w0, float2* __restrict__ lidx, int32_t* __restrict__ ctr) {
   constexpr int NKT = BK / 32;
-  constexpr float kScale2 = 0.125f * kLog2e;  // 1 / sqrt(64), base 2
+  constexpr float kScale2 = kIdxScaleLog2;
   __shared__ __attribute__((aligned(16))) uint8_t KIs[kBk * 128];
   __shared__ int64_t wg_item;
   const int tid = threadIdx.x;
