@@ -9,7 +9,7 @@
 //   dV = P^T dO,  dS = P * (dO V^T - D),  dQ = scale dS K,  dK = scale dS^T Q.
 //
 // Work decomposition on gfx950.  The forward's inverse index is rebuilt (in its
-// ordered form): for every (group, block) list, items of at most 256 (query, slot)
+// ordered form): for every (group, block) list, items of at most kBwdItemPairs (query, slot)
 // pairs.  A workgroup of four waves (one per SIMD, with up to 512 registers each)
 // takes items from per-XCD queues, stages the block's K and V rows in LDS once per
 // item and walks the item in sub-chunks of 64 MFMA rows ((64 / G) queries x G
@@ -43,7 +43,7 @@ namespace msa {
 namespace {
 
 constexpr int kBwdRows = 64;  // MFMA rows per sub-chunk
-constexpr int kBwdMaxPairs = 256;  // pairs per item
+constexpr int kBwdMaxPairs = kBwdItemPairs;  // pairs per item
 
 __device__ __forceinline__ u32x4_t pack8(const float* x) {
   return u32x4_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
@@ -221,8 +221,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_kernel(
     const int start = it.y, cnt = it.z;
     // The item's pairs go to LDS with its block (index idx of the item: ipair[idx], idx
     // clamped to cnt - 1).
-    static_assert(kBwdThreads == kBwdMaxPairs, "one pair per thread");
-    ipair[tid] = pairs[start + (tid < cnt ? tid : cnt - 1)];
+    static_assert(kBwdMaxPairs % kBwdThreads == 0, "whole rounds of one pair per thread");
+    for (int j = tid; j < cnt; j += kBwdThreads) ipair[j] = pairs[start + j];
     auto pair_at = [&](int idx) { return ipair[idx < cnt ? idx : cnt - 1]; };
     __syncthreads();  // the item's pairs
     // q and dO rows of the sub-chunk starting at pair cbase: row rho is (pair

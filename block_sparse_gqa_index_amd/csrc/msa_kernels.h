@@ -14,6 +14,11 @@ constexpr int kBlockKeys = 128;
 
 // Chunks (of 128 MFMA rows) per work item of the KV-outer kernel.
 constexpr int kItemChunks = 16;
+// Pairs per backward work item (its pair list sits in LDS).  A longer item writes
+// fewer fp32 dK/dV partial blocks (128 KB each) and stages its K/V block fewer
+// times; measured at 128K: 256 pairs 44.7-45.9 ms, 512 43.3, 1024 42.7-43.5, 2048
+// 42.7-42.9 (longer items lengthen the schedule's tail).
+constexpr int kBwdItemPairs = 1024;
 
 // Distance (in int32) between the per-XCD item counters of a workspace; a workspace
 // holds kItemCounterSets sets of eight (one per persistent launch over its items).

@@ -1471,7 +1471,8 @@ AttnWorkspace attn_workspace_layout(int64_t W, int H_q, int H_kv, int kk, int64_
   // The attention kernel keeps an item's pairs in registers: at most 256 pairs
   // for G >= 4 and 128 otherwise.
   const int max_q = G >= 4 ? 256 : 128;
-  const int item_q = kItemChunks * (128 / G) < max_q ? kItemChunks * (128 / G) : max_q;
+  const int item_fwd = kItemChunks * (128 / G) < max_q ? kItemChunks * (128 / G) : max_q;
+  const int item_q = parts == kPartsBwd ? kBwdItemPairs : item_fwd;
   const int64_t max_items = (max_pairs + item_q - 1) / item_q + lists;
   size_t off = 0;
   auto take = [&](size_t bytes) {
