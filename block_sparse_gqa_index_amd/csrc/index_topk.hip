@@ -303,8 +303,8 @@ __global__ __launch_bounds__(kIdxThreads, kIdxBlocksPerCU) void index_topk_kerne
 // (query, group) row, four rows per workgroup.  Block b < b_loc of the row has the
 // 64-bit key rank_key(score, b): score first, then the lower block.  The k-1 best
 // keys are found without sorting the row:
-//  1. lane l takes blocks l, l + 64, ... (coalesced across the wave; all of the
-//     row's R chunks of 64 stay in registers) and keeps its best key.  The (k-1)-th best of
+//  1. lane l takes blocks l, l + 64, ... (coalesced across the wave; up to 32 chunks
+//     of 64 stay in registers, longer rows are streamed twice) and keeps its best key.  The (k-1)-th best of
 //     the 64 lane bests, t0, is reached by k-1 distinct blocks, so every one of the
 //     row's k-1 best keys is >= t0;
 //  2. the blocks with key >= t0 are compacted into LDS in block order (ballot and
@@ -326,6 +326,74 @@ __device__ __forceinline__ int lane_prefix(uint64_t bal) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
 }
 
+// Step 1's threshold t0: the lane best that exactly kk-1 lane bests exceed
+// (nonzero keys are distinct and at least kk+1 lanes hold one).  s_lb: the wave's
+// 64-entry LDS table.
+__device__ __forceinline__ uint64_t tfs_threshold(uint64_t lbest, uint64_t* s_lb, int lane, int kk) {
+  s_lb[lane] = lbest;
+  wave_lds_sync();
+  int above = 0;
+#pragma unroll 8
+  for (int l = 0; l < 64; ++l) above += s_lb[l] > lbest;
+  const uint64_t who = __ballot(above == kk - 1);
+  const int wl = __builtin_ctzll(who);
+  return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(lbest >> 32), wl) << 32) |
+         (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)lbest, wl);
+}
+
+// Step 3 over C <= kTfsCap candidates s_c[0..C) in block order: keep those that fewer
+// than kk others beat, in candidate order, then the local block bl.
+__device__ __forceinline__ void tfs_write_kept(const uint64_t* s_c, int C, int kk, int lane, int bl,
+                                               int32_t* orow) {
+  int S = 0;
+  for (int m0 = 0; m0 < C; m0 += 64) {
+    const int ci = m0 + lane;
+    const uint64_t key = ci < C ? s_c[ci] : ~0ull;
+    int beat = 0;
+    for (int cj = 0; cj < C; ++cj) beat += s_c[cj] > key;
+    const bool keep = ci < C && beat < kk;
+    const uint64_t bal = __ballot(keep);
+    if (keep) orow[S + lane_prefix(bal)] = rank_key_block(key);
+    S += __popcll(bal);
+  }
+  if (lane == 0) orow[S] = bl;  // S == kk
+}
+
+// The overflow path: kk rounds of wave arg-max, each below the previous round's key
+// (best_below(prev) returns the lane's best key below prev); lane t keeps round t's
+// block, then the kk blocks are placed by their rank.  s_c: the wave's candidate area.
+template <typename F>
+__device__ __forceinline__ void tfs_rounds(F&& best_below, uint64_t* s_c, int kk, int lane, int bl, int32_t* orow) {
+  uint64_t prev = ~0ull;
+  int mine = 0x7fffffff;
+  for (int t = 0; t < kk; ++t) {
+    prev = wave_max_u64(best_below(prev));
+    if (lane == t) mine = rank_key_block(prev);
+  }
+  wave_lds_sync();
+  s_c[lane] = (uint64_t)(uint32_t)mine;
+  wave_lds_sync();
+  if (lane < kk) {
+    int pos = 0;
+    for (int t = 0; t < kk; ++t) pos += (int)s_c[t] < mine;
+    orow[pos] = mine;
+  }
+  if (lane == 0) orow[kk] = bl;
+}
+
+// Rows that select everything or only the local block; true when the row is done.
+__device__ __forceinline__ bool tfs_trivial(int kk, int bl, int k, int lane, int32_t* orow) {
+  if (kk == 0) {
+    if (lane == 0) orow[0] = bl;
+    return true;
+  }
+  if (bl <= kk) {  // every causal block is chosen
+    for (int t = lane; t < k; t += 64) orow[t] = t <= bl ? t : -1;
+    return true;
+  }
+  return false;
+}
+
 template <int R>
 __global__ __launch_bounds__(256) void topk_from_scores_kernel(const float* __restrict__ M, int64_t N,
                                                                 int H_kv, int64_t B, int k, int bk,
@@ -339,14 +407,7 @@ __global__ __launch_bounds__(256) void topk_from_scores_kernel(const float* __re
   const int kk = k - 1;  // blocks chosen besides the local one
   const float* row = M + c * B;
   int32_t* orow = block_idx + c * k;
-  if (kk == 0) {
-    if (lane == 0) orow[0] = bl;
-    return;
-  }
-  if (bl <= kk) {  // every causal block is chosen
-    for (int t = lane; t < k; t += 64) orow[t] = t <= bl ? t : -1;
-    return;
-  }
+  if (tfs_trivial(kk, bl, k, lane, orow)) return;
   const int nch = (bl + 63) >> 6;  // >= 1; kk < bl blocks and kk < 64 lanes hold one
 
   // 1. The row's scores, chunk j in x[j] (nch <= R); each lane's best key.
@@ -368,17 +429,7 @@ __global__ __launch_bounds__(256) void topk_from_scores_kernel(const float* __re
       }
     }
   }
-  // t0: the lane best that exactly kk-1 lane bests exceed (nonzero keys are distinct
-  // and at least kk+1 lanes hold one).
-  s_lbest[w][lane] = lbest;
-  wave_lds_sync();
-  int above = 0;
-#pragma unroll 8
-  for (int l = 0; l < 64; ++l) above += s_lbest[w][l] > lbest;
-  const uint64_t who = __ballot(above == kk - 1);
-  const int wl = __builtin_ctzll(who);
-  const uint64_t t0 = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(lbest >> 32), wl) << 32) |
-                      (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)lbest, wl);
+  const uint64_t t0 = tfs_threshold(lbest, s_lbest[w], lane, kk);
 
   // 2. Candidates (key >= t0) in block order.
   int C = 0;
@@ -397,48 +448,90 @@ __global__ __launch_bounds__(256) void topk_from_scores_kernel(const float* __re
     }
   }
   wave_lds_sync();
-
   if (C <= kTfsCap) {
-    // 3. Keep the candidates that fewer than kk others beat, in block order.
-    int S = 0;
-    for (int m0 = 0; m0 < C; m0 += 64) {
-      const int ci = m0 + lane;
-      const uint64_t key = ci < C ? s_cand[w][ci] : ~0ull;
-      int beat = 0;
-      for (int cj = 0; cj < C; ++cj) beat += s_cand[w][cj] > key;
-      const bool keep = ci < C && beat < kk;
-      const uint64_t bal = __ballot(keep);
-      if (keep) orow[S + lane_prefix(bal)] = rank_key_block(key);
-      S += __popcll(bal);
-    }
-    if (lane == 0) orow[S] = bl;  // S == kk
+    tfs_write_kept(s_cand[w], C, kk, lane, bl, orow);  // 3.
   } else {
-    // kk rounds of wave arg-max, each below the previous round's key; lane t keeps
-    // round t's block, then the kk blocks are placed by their rank.
-    uint64_t prev = ~0ull;
-    int mine = 0x7fffffff;
-    for (int t = 0; t < kk; ++t) {
-      uint64_t best = 0;
+    tfs_rounds(
+        [&](uint64_t prev) {
+          uint64_t best = 0;
 #pragma unroll
-      for (int j = 0; j < R; ++j) {
-        if (j < nch) {
-          const int b = j * 64 + lane;
-          const uint64_t key = b < bl ? rank_key(x[j], b) : 0ull;
-          best = (key < prev && key > best) ? key : best;
+          for (int j = 0; j < R; ++j) {
+            if (j < nch) {
+              const int b = j * 64 + lane;
+              const uint64_t key = b < bl ? rank_key(x[j], b) : 0ull;
+              best = (key < prev && key > best) ? key : best;
+            }
+          }
+          return best;
+        },
+        s_cand[w], kk, lane, bl, orow);
+  }
+}
+
+// Rows of more than 32 chunks: the same three steps, with the row streamed from
+// memory in groups of kTfsGroup chunks instead of held in registers (which at 64 or
+// 128 chunks left two or one waves per SIMD): one sweep for the lane bests, a second
+// for the candidates (mostly re-read from the L2), and for the overflow path one per
+// round.  Measured at 512K rows: 4096 blocks 2.45 -> 1.45-1.52 ms, 8192 blocks (k =
+// 32) 8.78 -> 2.63-2.83 ms, the same selections.
+constexpr int kTfsGroup = 32;
+
+__global__ __launch_bounds__(256) void topk_from_scores_long_kernel(const float* __restrict__ M, int64_t N,
+                                                                     int H_kv, int64_t B, int k, int bk,
+                                                                     int32_t* __restrict__ block_idx) {
+  __shared__ uint64_t s_cand[4][kTfsCap];
+  __shared__ uint64_t s_lbest[4][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t c = (int64_t)blockIdx.x * 4 + w;
+  if (c >= N * H_kv) return;  // whole waves
+  const int bl = (int)((c / H_kv) / bk);
+  const int kk = k - 1;
+  const float* row = M + c * B;
+  int32_t* orow = block_idx + c * k;
+  if (tfs_trivial(kk, bl, k, lane, orow)) return;
+  const int nch = (bl + 63) >> 6;
+
+  // fn(key) for every chunk of the row in block order (lane l: blocks l, l + 64, ...;
+  // a block at or past bl offers key 0).  Each group's loads are issued together.
+  auto sweep = [&](auto&& fn) {
+    for (int g0 = 0; g0 < nch; g0 += kTfsGroup) {
+      float x[kTfsGroup];
+#pragma unroll
+      for (int j = 0; j < kTfsGroup; ++j) {
+        const int b = (g0 + j) * 64 + lane;
+        x[j] = g0 + j < nch ? row[b < bl ? b : 0] : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < kTfsGroup; ++j) {
+        if (g0 + j < nch) {
+          const int b = (g0 + j) * 64 + lane;
+          fn(b < bl ? rank_key(x[j], b) : 0ull);
         }
       }
-      prev = wave_max_u64(best);
-      if (lane == t) mine = rank_key_block(prev);
     }
-    wave_lds_sync();
-    s_cand[w][lane] = (uint64_t)(uint32_t)mine;
-    wave_lds_sync();
-    if (lane < kk) {
-      int pos = 0;
-      for (int t = 0; t < kk; ++t) pos += (int)s_cand[w][t] < mine;
-      orow[pos] = mine;
-    }
-    if (lane == 0) orow[kk] = bl;
+  };
+  uint64_t lbest = 0;
+  sweep([&](uint64_t key) { lbest = key > lbest ? key : lbest; });
+  const uint64_t t0 = tfs_threshold(lbest, s_lbest[w], lane, kk);
+  int C = 0;
+  sweep([&](uint64_t key) {
+    const bool p = key >= t0;
+    const uint64_t bal = __ballot(p);
+    const int pos = C + lane_prefix(bal);
+    if (p && pos < kTfsCap) s_cand[w][pos] = key;
+    C += __popcll(bal);
+  });
+  wave_lds_sync();
+  if (C <= kTfsCap) {
+    tfs_write_kept(s_cand[w], C, kk, lane, bl, orow);
+  } else {
+    tfs_rounds(
+        [&](uint64_t prev) {
+          uint64_t best = 0;
+          sweep([&](uint64_t key) { best = (key < prev && key > best) ? key : best; });
+          return best;
+        },
+        s_cand[w], kk, lane, bl, orow);
   }
 }
 
@@ -535,10 +628,8 @@ hipError_t launch_topk_from_scores(const float* M, int64_t N, int H_kv, int64_t 
     topk_from_scores_kernel<16><<<g, t, 0, stream>>>(M, N, H_kv, B, k, bk, block_idx);
   else if (chunks <= 32)
     topk_from_scores_kernel<32><<<g, t, 0, stream>>>(M, N, H_kv, B, k, bk, block_idx);
-  else if (chunks <= 64)
-    topk_from_scores_kernel<64><<<g, t, 0, stream>>>(M, N, H_kv, B, k, bk, block_idx);
   else
-    topk_from_scores_kernel<128><<<g, t, 0, stream>>>(M, N, H_kv, B, k, bk, block_idx);
+    topk_from_scores_long_kernel<<<g, t, 0, stream>>>(M, N, H_kv, B, k, bk, block_idx);
   return hipGetLastError();
 }
 

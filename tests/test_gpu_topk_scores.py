@@ -1,9 +1,10 @@
 """GPU parity of the split-form selection (msa_topk_from_scores) on long score rows.
 
-Rows here hold 1,000 to 8,191 causal blocks, so the kernel's variants for up to 32
-and 128 register-held chunks of 64 blocks and its fallback for rows with too many
-candidates all run; the oracle checks sampled rows (it takes explicit row
-positions).  Scores are drawn on the device from a seeded generator.
+Rows here hold 1,000 to 8,191 causal blocks, so both kernels (rows of up to 32
+register-held chunks of 64 blocks, and longer rows streamed from memory) and the
+fallback of each for rows with too many candidates run; the oracle checks sampled
+rows (it takes explicit row positions).  Scores are drawn on the device from a
+seeded generator.
 """
 import numpy as np
 import pytest
@@ -47,11 +48,13 @@ def test_long_rows_random(msa, k):
     _check_rows(bi, M, _sample_rows(N, 200, k), k, BK)
 
 
+# 76,000 tokens: up to 19 chunks (register-held rows); 200,000: up to 49 (streamed).
+@pytest.mark.parametrize("N", [76000, 200000])
 @pytest.mark.parametrize("k", [16, 32])
-def test_few_lanes_own_the_best_blocks(msa, k):
+def test_few_lanes_own_the_best_blocks(msa, k, N):
     """Blocks b with b % 64 < k - 2 outscore all others: with k = 32 the rows near the
     end have more than 512 blocks at or above the lane-best bound (the fallback)."""
-    N, H_kv, BK = 76000, 1, 64
+    H_kv, BK = 1, 64
     B = (N + BK - 1) // BK
     g = torch.Generator(device=DEV).manual_seed(6000 + k)
     M = torch.randn((N, H_kv, B), generator=g, device=DEV)
@@ -60,11 +63,14 @@ def test_few_lanes_own_the_best_blocks(msa, k):
     bi = msa.msa_topk_from_scores(M, k, B_k=BK)
     torch.cuda.synchronize()
     _check_rows(bi, M, _sample_rows(N, 200, 60 + k), k, BK)
+    del M
+    torch.cuda.empty_cache()
 
 
-def test_ties_and_neg_inf_long_rows(msa):
+@pytest.mark.parametrize("N", [76000, 200000])
+def test_ties_and_neg_inf_long_rows(msa, N):
     """Scores on a coarse grid (many exact ties) with some -inf entries."""
-    N, H_kv, BK, k = 76000, 1, 64, 32
+    H_kv, BK, k = 1, 64, 32
     B = (N + BK - 1) // BK
     g = torch.Generator(device=DEV).manual_seed(6100)
     M = torch.randint(-4, 5, (N, H_kv, B), generator=g, device=DEV).float() * 0.5
@@ -72,6 +78,8 @@ def test_ties_and_neg_inf_long_rows(msa):
     bi = msa.msa_topk_from_scores(M, k, B_k=BK)
     torch.cuda.synchronize()
     _check_rows(bi, M, _sample_rows(N, 200, 61), k, BK)
+    del M
+    torch.cuda.empty_cache()
 
 
 def test_neg_inf_short_rows(msa):
