@@ -351,8 +351,9 @@ msa_status_t msa_topk_from_scores(const float* M, int64_t N, int H_kv, int64_t B
 msa_status_t msa_set_profile_events(void* const* events, int n);
 
 /* msa_set_profile_clock — measurement hook for the load balance of the persistent-grid
- * kernels (the pages balance variable work with a persistent grid: paper review page,
- * section 4; here a static item order stands in for their atomic counter).  While set,
+ * kernels (the pages balance variable work with a persistent grid and an atomic
+ * counter: paper review page, section 4; here eight per-XCD atomic item counters
+ * play that part).  While set,
  * the KV-outer phase-1 kernel of the first query window of every later
  * msa_sparse_attn_fwd / _varlen call on this host thread, and the main kernel of the
  * first query window of every later msa_sparse_attn_bwd call, store for each workgroup
