@@ -11,7 +11,7 @@
 //
 // Work decomposition on gfx950.  For each (group r, KV block b) the inverse index
 // lists the (query, slot) pairs that chose it.  Lists are cut into fixed items of
-// at most kItemChunks chunks and 256 pairs; a chunk is 128 MFMA rows = (128 / G) gathered queries x G
+// at most 2 * kItemChunks chunks and 512 pairs; a chunk is 128 MFMA rows = (128 / G) gathered queries x G
 // heads (query concatenation).  A workgroup stages the block's K (32 KB) and V^T
 // (32 KB) in LDS once per item, then for each chunk every wave computes 32 rows:
 // S^T = K * Q^T and O^T = V^T * P^T on 32x32x16 bf16 MFMAs, with the softmax in
@@ -376,6 +376,12 @@ constexpr int kAttnThreads = 256;
 // stores.  An item holds at most 64 * kPairRegs<G> pairs.
 template <int G>
 constexpr int kPairRegs = G >= 4 ? 4 : 2;
+// The attention kernel's items are twice as long (32 chunks, 512 pairs at G >= 4): each
+// item stages its K/V block (64 KB) into LDS once, and at 128K the longer items took
+// phase 1 from 12.52-12.56 to 12.31-12.35 ms (32K and B_k = 64 unchanged).
+constexpr int kAttnItemMult = 2;
+template <int G>
+constexpr int kAttnPairRegs = kPairRegs<G> * kAttnItemMult;
 
 // Chunk c covers the item's pairs [c*kQC, (c+1)*kQC); with G >= 4, kQC = 128/G
 // divides 64, so one register holds all of them (pairs past the end are replaced
@@ -415,9 +421,9 @@ __device__ __forceinline__ int item_pair_v(const int (&ip)[NR], int idx) {
 // 1 KB run: its base is uniform (pair read from one lane of the chunk's register
 // `cur` into prs[t]) and the lane only adds lane*16 bytes.  Addresses are formed
 // from the kernel's global pointer, so the loads stay global, not flat.
-template <int G>
+template <int G, int NR>
 __device__ __forceinline__ void gather_q(u32x4_t (&qraw)[8], int (&prs)[8], const uint16_t* __restrict__ q,
-                                         const int (&ip)[kPairRegs<G>], int cur, int cbase, int cnt, int wave,
+                                         const int (&ip)[NR], int cur, int cbase, int cnt, int wave,
                                          int lane, int64_t w0, int H_q, int64_t r) {
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
@@ -487,7 +493,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kvouter_kernel(
     const int64_t j0 = si.cu ? si.cu[s_item] : 0;
     const int64_t seqN = si.cu ? si.cu[s_item + 1] - j0 : N;
 
-    constexpr int NR = kPairRegs<G>;
+    constexpr int NR = kAttnPairRegs<G>;
     int ip[NR];
 #pragma unroll
     for (int k = 0; k < NR; ++k) ip[k] = pairs[start + (64 * k + lane < cnt ? 64 * k + lane : cnt - 1)];
@@ -1468,10 +1474,12 @@ AttnWorkspace attn_workspace_layout(int64_t W, int H_q, int H_kv, int kk, int64_
   const int64_t lists = (int64_t)H_kv * L.nW * B;
   const int64_t max_pairs = W * H_kv * kk;
   const int G = H_q / H_kv;
-  // The attention kernel keeps an item's pairs in registers: at most 256 pairs
-  // for G >= 4 and 128 otherwise.
-  const int max_q = G >= 4 ? 256 : 128;
-  const int item_fwd = kItemChunks * (128 / G) < max_q ? kItemChunks * (128 / G) : max_q;
+  // The attention and KL kernels keep an item's pairs in registers: at most 256
+  // pairs for G >= 4 and 128 otherwise, twice that for the attention.
+  const int mult = parts == kPartsAttn ? kAttnItemMult : 1;
+  const int max_q = (G >= 4 ? 256 : 128) * mult;
+  const int chunks = kItemChunks * mult;
+  const int item_fwd = chunks * (128 / G) < max_q ? chunks * (128 / G) : max_q;
   const int item_q = parts == kPartsBwd ? kBwdItemPairs : item_fwd;
   const int64_t max_items = (max_pairs + item_q - 1) / item_q + lists;
   size_t off = 0;
